@@ -1,0 +1,170 @@
+"""Drafter context injection and block forward (oracle side, fp64).
+
+Injection [P1 "关键创新" Steps 2-3; P2 §2.2; P3 §四; P4 §5.1]: for every new
+context row, concatenate the selected target layers' hidden states (ascending
+layer order), project with fc, apply one RMSNorm (gain gamma_h) to get the
+fused feature g, then for every drafter layer project g with that layer's own
+W_k / W_v, RMS-normalise each k head (gain gamma_k of the layer), apply RoPE at
+the row's absolute position and store (k, v) in the drafter cache.  Hidden
+states themselves are not kept (immediate materialisation, [P3 §四]).
+
+Block forward [P2 §2.1-2.2; P4 §4, §4.1-4.4; P1 "关键创新" Step 3]: the block
+is [anchor | mask x K] embedded with the shared embedding times
+input_embedding_scale at positions C..C+K (C = context length of the request).
+Each Qwen3-style layer: RMSNorm, q/k/v projections, per-head RMSNorm of q and
+k, RoPE, attention of the block queries over [context K/V ; block K/V] with no
+mask inside the block (non-causal, [P4 §5.3 table; P1 training paragraph]),
+output projection + residual, RMSNorm, SwiGLU MLP + residual.  A final
+RMSNorm and the shared LM head give logits for the K mask rows only [P4 §4.3].
+
+Readings (silent points): no biases; RMSNorm y = x / sqrt(mean(x^2) + eps) * g
+with eps = 1e-6; rotate-half RoPE pairing (i, i + d/2) with inv_freq_i =
+theta^(-2i/d); attention scale 1/sqrt(d); q head h uses kv head h // (n_q/n_kv);
+a final RMSNorm precedes the LM head; the fused feature g is shared by all
+layers (one RMSNorm after fc, no per-layer norm on g).
+
+Parity of absolute forward values is unpinned by the pages (no page prints an
+activation or a logit); the pieces are pinned against library routines and the
+invariants listed in tests/test_oracle_drafter.py.
+"""
+from __future__ import annotations
+
+from typing import Dict, List
+
+import numpy as np
+
+
+def as64(t) -> np.ndarray:
+    """Widen a tensor/array (fp32/bf16 torch or numpy) to fp64 numpy exactly."""
+    try:
+        import torch
+        if isinstance(t, torch.Tensor):
+            return t.detach().to(torch.float64).cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(t, dtype=np.float64)
+
+
+def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2, last axis) + eps) * gain."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * gain
+
+
+def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half RoPE on the last axis (size d) of x[..., n, heads, d] with positions pos[n]."""
+    d = x.shape[-1]
+    half = d // 2
+    inv = theta ** (-np.arange(half, dtype=np.float64) * 2.0 / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]        # [n, half]
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, group: int) -> np.ndarray:
+    """q [R, n_q, d]; keys/vals [S, n_kv, d]; softmax(q k^T / sqrt d) v, no mask."""
+    R, nq, d = q.shape
+    out = np.zeros_like(q)
+    for h in range(nq):
+        kv = h // group
+        s = q[:, h, :] @ keys[:, kv, :].T / np.sqrt(d)
+        s = s - s.max(axis=-1, keepdims=True)
+        a = np.exp(s)
+        a /= a.sum(axis=-1, keepdims=True)
+        out[:, h, :] = a @ vals[:, kv, :]
+    return out
+
+
+class DrafterOracle:
+    """fp64 drafter with its own per-slot context K/V cache."""
+
+    def __init__(self, cfg, weights: Dict, pos_offset: int = 0):
+        self.cfg = cfg
+        self.pos_offset = pos_offset          # added to every absolute position (tests only)
+        c = cfg
+        self.embed = as64(weights["embed"])
+        self.lm_head = as64(weights["lm_head"])
+        self.fc = as64(weights["fc"])
+        self.hidden_norm = as64(weights["hidden_norm"])
+        self.final_norm = as64(weights["final_norm"])
+        self.layers = [{k: as64(v) for k, v in lw.items()} for lw in weights["layers"]]
+        self.cache: Dict[int, List] = {}      # slot -> per layer [k (C, n_kv, d), v (C, n_kv, d)]
+        self.d = c.head_dim
+
+    # ---- context ----
+    def ctx_len(self, slot: int) -> int:
+        return 0 if slot not in self.cache else self.cache[slot][0][0].shape[0]
+
+    def reset(self, slot: int):
+        self.cache.pop(slot, None)
+
+    def project_context(self, feats: np.ndarray, pos: np.ndarray):
+        """feats [n, L_t, H_t] -> per layer (k [n, n_kv, d], v [n, n_kv, d]) at positions pos."""
+        c = self.cfg
+        x = as64(feats).reshape(feats.shape[0], -1)           # concat over selected layers
+        g = rms_norm(x @ self.fc.T, self.hidden_norm, c.rms_eps)
+        out = []
+        for lw in self.layers:
+            k = (g @ lw["k_w"].T).reshape(-1, c.n_kv_heads, self.d)
+            v = (g @ lw["v_w"].T).reshape(-1, c.n_kv_heads, self.d)
+            k = rope(rms_norm(k, lw["k_norm"], c.rms_eps), pos, c.rope_theta)
+            out.append((k, v))
+        return out
+
+    def inject(self, slot: int, feats) -> None:
+        """Append rows for `slot` at positions ctx_len..ctx_len+n-1."""
+        n = feats.shape[0]
+        c0 = self.ctx_len(slot)
+        kv = self.project_context(feats, np.arange(c0, c0 + n) + self.pos_offset)
+        if slot not in self.cache:
+            self.cache[slot] = [[k, v] for k, v in kv]
+        else:
+            for l, (k, v) in enumerate(kv):
+                self.cache[slot][l][0] = np.concatenate([self.cache[slot][l][0], k], axis=0)
+                self.cache[slot][l][1] = np.concatenate([self.cache[slot][l][1], v], axis=0)
+
+    # ---- block forward ----
+    def block_hidden(self, slot: int, anchor: int, K: int, single_query: bool = False):
+        """Residual stream after all layers for the R = K+1 block rows.
+
+        single_query=True evaluates each row's attention separately against the
+        same keys (the block-parallel invariant's other side).
+        """
+        c = self.cfg
+        R = K + 1
+        C = self.ctx_len(slot)
+        ids = np.array([anchor] + [c.mask_token_id] * K)
+        X = self.embed[ids] * c.input_embedding_scale
+        pos = np.arange(C, C + R) + self.pos_offset
+        for l, lw in enumerate(self.layers):
+            h = rms_norm(X, lw["in_norm"], c.rms_eps)
+            q = (h @ lw["q_w"].T).reshape(R, c.n_q_heads, self.d)
+            k = (h @ lw["k_w"].T).reshape(R, c.n_kv_heads, self.d)
+            v = (h @ lw["v_w"].T).reshape(R, c.n_kv_heads, self.d)
+            q = rope(rms_norm(q, lw["q_norm"], c.rms_eps), pos, c.rope_theta)
+            k = rope(rms_norm(k, lw["k_norm"], c.rms_eps), pos, c.rope_theta)
+            if C > 0:
+                keys = np.concatenate([self.cache[slot][l][0], k], axis=0)
+                vals = np.concatenate([self.cache[slot][l][1], v], axis=0)
+            else:
+                keys, vals = k, v
+            if single_query:
+                o = np.concatenate([attention(q[i:i + 1], keys, vals, c.group) for i in range(R)], axis=0)
+            else:
+                o = attention(q, keys, vals, c.group)
+            X = X + o.reshape(R, c.q_dim) @ lw["o_w"].T
+            h = rms_norm(X, lw["post_norm"], c.rms_eps)
+            X = X + (silu(h @ lw["gate_w"].T) * (h @ lw["up_w"].T)) @ lw["down_w"].T
+        return X
+
+    def block_logits(self, slot: int, anchor: int, K: int, single_query: bool = False) -> np.ndarray:
+        """Logits [K, V] of the mask rows (block positions 1..K)."""
+        X = self.block_hidden(slot, anchor, K, single_query)
+        z = rms_norm(X[1:], self.final_norm, self.cfg.rms_eps)
+        return z @ self.lm_head.T

@@ -1,0 +1,88 @@
+"""Verification of a drafted block against target logits (oracle side, fp64).
+
+Greedy [P2 §2.3 last paragraph, §4.2; P1 "核心推理伪代码"]: the target's
+per-row argmax post_j (rows j = 0..K) is compared with the drafts shifted by
+one -- draft d_i (block position i) against post_{i-1} -- and the accepted
+length is the product-prefix sum  a = sum_i prod_{k<=i} [d_k == post_{k-1}].
+The step emits d_1..d_a plus post_a (the target's token at the first mismatch,
+or the bonus row when all K match), so it always yields a+1 tokens [P2 §2.1's
+3 accepted + 1 resampled = 4 example; P4 §2: at most K+1 tokens per round].
+
+Rejection sampling [P2 §2.3, §4.2]: with p_j = softmax(t_j / T) and
+q_i = softmax(z_i / T), accept d_i iff u_i < p_{i-1}(d_i) / q_i(d_i); at the
+first rejection draw from the residual max(0, p_{i-1} - q_i) renormalised, or
+from p_{i-1} when that residual is exhausted; when all K are accepted add a
+bonus token drawn from p_K.
+
+Readings: the accept test uses u in [0,1) so p >= q always accepts; the
+residual counts as exhausted when its total mass is below RESIDUAL_EPS (the
+pages say "exhausted or underflowed" without a threshold); draws are
+inverse-CDF in ascending id order with Philox uniforms (purpose 1 for accept
+tests at position i, purpose 2 for the final draw at position i* or K+1).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import philox
+from .select import softmax, inverse_cdf, argmax_with_margin
+
+RESIDUAL_EPS = 2.0 ** -20
+
+
+def verify_greedy(draft_ids, target_logits):
+    """draft_ids [K] (d_1..d_K); target_logits [K+1, V].  Returns dict."""
+    d = np.asarray(draft_ids, dtype=np.int64)
+    t = np.asarray(target_logits, dtype=np.float64)
+    K = d.shape[0]
+    post, margin = zip(*[argmax_with_margin(t[j]) for j in range(K + 1)])
+    post = np.array(post, dtype=np.int64)
+    match = (d == post[:K]).astype(np.int64)
+    a = int(np.cumprod(match).sum())
+    out = list(d[:a]) + [int(post[a])]
+    return {"out_tokens": np.array(out, dtype=np.int64), "out_len": a + 1, "accept_len": a,
+            "post": post, "margins": np.array(margin)}
+
+
+def verify_rejection(draft_ids, draft_logits, target_logits, T, seed, slot, step, uniform_fn=None):
+    """draft_ids [K]; draft_logits [K, V] (row i-1 <-> mask i); target_logits [K+1, V].
+
+    uniform_fn(position, purpose) overrides the Philox uniforms (tests only).
+    """
+    if uniform_fn is None:
+        def uniform_fn(position, purpose):
+            return float(philox.uniform(seed, slot, step, position, purpose))
+    d = np.asarray(draft_ids, dtype=np.int64)
+    K = d.shape[0]
+    if T <= 0:
+        return verify_greedy(d, target_logits)
+    p = softmax(target_logits, T)
+    q = softmax(draft_logits, T)
+    near = np.inf
+    a = 0
+    out = []
+    for i in range(1, K + 1):
+        pi, qi = p[i - 1][d[i - 1]], q[i - 1][d[i - 1]]
+        u = uniform_fn(i, philox.PURPOSE_ACCEPT)
+        near = min(near, abs(u * qi - pi) / max(pi, qi, 1e-300))
+        if u * qi < pi:
+            out.append(int(d[i - 1]))
+            a += 1
+            continue
+        # first rejection at block position i
+        r = np.maximum(p[i - 1] - q[i - 1], 0.0)
+        u2 = uniform_fn(i, philox.PURPOSE_RESAMPLE)
+        rs = r.sum()
+        near = min(near, abs(rs - RESIDUAL_EPS) / RESIDUAL_EPS)
+        w = r if rs >= RESIDUAL_EPS else p[i - 1]
+        c, m2 = inverse_cdf(w, u2)
+        near = min(near, m2)
+        out.append(c)
+        return {"out_tokens": np.array(out, dtype=np.int64), "out_len": a + 1, "accept_len": a,
+                "near_margin": near, "fallback": bool(rs < RESIDUAL_EPS)}
+    u2 = uniform_fn(K + 1, philox.PURPOSE_RESAMPLE)
+    c, m2 = inverse_cdf(p[K], u2)
+    near = min(near, m2)
+    out.append(c)
+    return {"out_tokens": np.array(out, dtype=np.int64), "out_len": K + 1, "accept_len": K,
+            "near_margin": near, "fallback": False}
