@@ -1,0 +1,673 @@
+// Host library: handle, validation, scratch ownership and the launch sequence
+// of the three drafting calls.  No host synchronisation on the drafting path;
+// every device-dependent size is bounded on the host and resolved on the device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "ops.h"
+
+using namespace dfl;
+
+struct dflash_handle {
+  dflash_config cfg{};
+  int esize = 4;
+  int device = 0, num_cus = 256;
+  // borrowed weights
+  const void *embed = nullptr, *lm_head = nullptr, *fc = nullptr, *hidden_norm = nullptr, *final_norm = nullptr;
+  std::vector<dflash_layer_weights> layers;
+  const void** d_k_gains = nullptr;       // device array of per-layer k_norm pointers
+  // cache and state
+  void* cache_k = nullptr;
+  void* cache_vt = nullptr;
+  int64_t ctx_alloc = 0;
+  int32_t* ctx_len = nullptr;
+  int32_t* err = nullptr;
+  float2* rope = nullptr;
+  int n_rope = 0;
+  // draft scratch
+  int maxM = 0, Rpad = 0, QRpad = 0, attn_splits = 1, item_cap = 0, target_wg = 1024, qrt_max = 5;
+  float* X = nullptr;
+  void *hbuf = nullptr, *attn_out = nullptr, *act = nullptr, *qb = nullptr, *kb = nullptr, *vbt = nullptr;
+  float *o_part = nullptr, *m_part = nullptr, *l_part = nullptr;
+  AttnPlan* plan = nullptr;
+  int4* items = nullptr;
+  int32_t *first_item = nullptr, *n_items = nullptr;
+  int32_t* dslots = nullptr;              // validated slot ids of the current draft
+  float* partials = nullptr;
+  size_t partials_elems = 0;
+  // LM head
+  int n_vtiles = 0;
+  float *logits_ws = nullptr, *tmax = nullptr, *tsum = nullptr, *row_max = nullptr, *row_lse = nullptr;
+  int32_t* targ = nullptr;
+  int32_t* tk_ids = nullptr;
+  float* tk_probs = nullptr;
+  // injection
+  int inject_chunk = 0;
+  float* y = nullptr;
+  void* g = nullptr;
+  int32_t *a_rows = nullptr, *row_slot = nullptr, *row_pos = nullptr, *req_off = nullptr, *req_pos = nullptr;
+  // verification
+  int32_t* post = nullptr;
+  float* vstats = nullptr;
+  std::vector<void*> allocs;
+};
+
+namespace {
+
+int alloc(dflash_handle* h, void** p, size_t bytes) {
+  if (bytes == 0) bytes = 256;
+  if (hipMalloc(p, bytes) != hipSuccess) return DFLASH_E_NOMEM;
+  h->allocs.push_back(*p);
+  if (hipMemset(*p, 0, bytes) != hipSuccess) return DFLASH_E_HIP;
+  return DFLASH_OK;
+}
+
+template <typename P>
+int alloc_t(dflash_handle* h, P** p, size_t count, size_t elem) {
+  void* v = nullptr;
+  const int rc = alloc(h, &v, count * elem);
+  *p = (P*)v;
+  return rc;
+}
+
+void free_all(dflash_handle* h) {
+  for (void* p : h->allocs) (void)hipFree(p);
+  h->allocs.clear();
+}
+
+int check_config(const dflash_config& c) {
+  if (c.dtype != DFLASH_F32 && c.dtype != DFLASH_BF16) return DFLASH_E_INVALID;
+  if (c.n_layers < 1 || c.n_layers > 64 || c.hidden <= 0 || c.n_q_heads <= 0 || c.n_kv_heads <= 0 ||
+      c.ffn <= 0 || c.vocab <= 0 || c.n_target_layers < 1 || c.target_hidden <= 0)
+    return DFLASH_E_INVALID;
+  if (c.max_batch < 1 || c.max_ctx < 1 || c.max_k < 1 || c.max_inject_rows < 1 || c.max_top_k < 0 ||
+      c.max_tree < 0)
+    return DFLASH_E_INVALID;
+  if (c.mask_token_id < 0 || c.mask_token_id >= c.vocab) return DFLASH_E_INVALID;
+  if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return DFLASH_E_INVALID;
+  if (c.head_dim != 64 && c.head_dim != 128) return DFLASH_E_UNSUPPORTED;
+  if (c.n_q_heads % c.n_kv_heads) return DFLASH_E_UNSUPPORTED;
+  if (c.hidden % 128 || (c.n_q_heads * c.head_dim) % 128 || (c.n_kv_heads * c.head_dim) % 128)
+    return DFLASH_E_UNSUPPORTED;
+  if (c.ffn % 64 || c.target_hidden % 64) return DFLASH_E_UNSUPPORTED;
+  if (c.n_target_layers > MAX_ASEG) return DFLASH_E_UNSUPPORTED;
+  if (c.max_k > 31) return DFLASH_E_UNSUPPORTED;
+  if (c.max_top_k > 256 || c.max_tree > 256) return DFLASH_E_UNSUPPORTED;
+  if ((int64_t)c.max_batch * (c.max_k + 1) > (1 << 20)) return DFLASH_E_UNSUPPORTED;
+  return DFLASH_OK;
+}
+
+// q-row splits so that one attention work-group holds at most 16*qrt_cap query rows
+int choose_attn_splits(const dflash_config& c, int qrt_cap) {
+  const int g = c.n_q_heads / c.n_kv_heads;
+  for (int s = 1; s <= g; s *= 2) {
+    if (g % s) continue;
+    if ((g / s) * (c.max_k + 1) <= 16 * qrt_cap) return s;
+  }
+  return -1;
+}
+
+GemmArgs gemm_a1(const void* a, int64_t lda, int M, int N, int K) {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a_ptr[0] = a;
+  g.a_ld[0] = lda;
+  g.a_nseg = 1;
+  g.a_segk = K;
+  g.b_nseg = 1;
+  g.splits = 1;
+  return g;
+}
+
+void set_b(GemmArgs& g, std::initializer_list<std::pair<const void*, int>> segs, int64_t ld) {
+  int s = 0, begin = 0;
+  for (auto& p : segs) {
+    g.b_ptr[s] = p.first;
+    g.b_begin[s] = begin;
+    begin += p.second;
+    ++s;
+  }
+  g.b_begin[s] = begin;
+  g.b_nseg = s;
+  g.b_ld = ld;
+}
+
+inline hipStream_t S(void* s) { return (hipStream_t)s; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_str(int st) {
+  switch (st) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_E_INVALID: return "invalid argument";
+    case DFLASH_E_NOMEM: return "out of device memory";
+    case DFLASH_E_CAPACITY: return "capacity exceeded";
+    case DFLASH_E_UNSUPPORTED: return "unsupported shape";
+    case DFLASH_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_handle** out) {
+  if (!cfg || !w || !out) return DFLASH_E_INVALID;
+  *out = nullptr;
+  int rc = check_config(*cfg);
+  if (rc) return rc;
+  const dflash_config& c = *cfg;
+  if (w->n_layers != c.n_layers || !w->layers || !w->embed || !w->lm_head || !w->fc || !w->hidden_norm ||
+      !w->final_norm)
+    return DFLASH_E_INVALID;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const dflash_layer_weights& L = w->layers[l];
+    if (!L.in_norm || !L.q_w || !L.k_w || !L.v_w || !L.o_w || !L.q_norm || !L.k_norm || !L.post_norm ||
+        !L.gate_w || !L.up_w || !L.down_w)
+      return DFLASH_E_INVALID;
+  }
+  const int qrt_cap = (c.dtype == DFLASH_F32 && c.head_dim == 128) ? 3 : 5;
+  const int splits = choose_attn_splits(c, qrt_cap);
+  if (splits < 0) return DFLASH_E_UNSUPPORTED;
+
+  dflash_handle* h = new dflash_handle();
+  h->cfg = c;
+  h->esize = c.dtype == DFLASH_BF16 ? 2 : 4;
+  h->qrt_max = qrt_cap;
+  h->attn_splits = splits;
+  (void)hipGetDevice(&h->device);
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, h->device) == hipSuccess && prop.multiProcessorCount > 0)
+    h->num_cus = prop.multiProcessorCount;
+  h->embed = w->embed;
+  h->lm_head = w->lm_head;
+  h->fc = w->fc;
+  h->hidden_norm = w->hidden_norm;
+  h->final_norm = w->final_norm;
+  h->layers.assign(w->layers, w->layers + c.n_layers);
+
+  const int H = c.hidden, d = c.head_dim, nkv = c.n_kv_heads, g = c.n_q_heads / nkv;
+  const int qdim = c.n_q_heads * d, kvdim = nkv * d;
+  const size_t es = h->esize;
+  const int R = c.max_k + 1;
+  h->maxM = c.max_batch * R;
+  h->Rpad = ((R + 31) / 32) * 32;
+  h->QRpad = ((g * R + 15) / 16) * 16 + 80;
+  h->ctx_alloc = ((int64_t)(c.max_ctx + 63) / 64) * 64 + 64;
+  h->item_cap = c.max_batch + h->target_wg / (nkv * splits) + 8;
+  h->n_vtiles = (c.vocab + 127) / 128;
+  h->inject_chunk = std::min(c.max_inject_rows, 16384);
+
+  const size_t cache_elems = (size_t)c.n_layers * (c.max_batch + 1) * nkv * h->ctx_alloc * d;
+  do {
+    if ((rc = alloc(h, &h->cache_k, cache_elems * es))) break;
+    if ((rc = alloc(h, &h->cache_vt, cache_elems * es))) break;
+    if ((rc = alloc_t(h, &h->ctx_len, c.max_batch + 1, 4))) break;
+    if ((rc = alloc_t(h, &h->err, 1, 4))) break;
+    h->n_rope = (int)h->ctx_alloc;
+    if ((rc = alloc_t(h, &h->rope, (size_t)h->n_rope * (d / 2), sizeof(float2)))) break;
+    void* kg = nullptr;
+    if ((rc = alloc(h, &kg, sizeof(void*) * c.n_layers))) break;
+    h->d_k_gains = (const void**)kg;
+    if ((rc = alloc_t(h, &h->X, (size_t)h->maxM * H, 4))) break;
+    if ((rc = alloc(h, &h->hbuf, (size_t)h->maxM * H * es))) break;
+    if ((rc = alloc(h, &h->attn_out, (size_t)h->maxM * qdim * es))) break;
+    if ((rc = alloc(h, &h->act, (size_t)h->maxM * c.ffn * es))) break;
+    if ((rc = alloc(h, &h->qb, (size_t)c.max_batch * nkv * h->QRpad * d * es))) break;
+    if ((rc = alloc(h, &h->kb, (size_t)c.max_batch * nkv * h->Rpad * d * es))) break;
+    if ((rc = alloc(h, &h->vbt, (size_t)c.max_batch * nkv * h->Rpad * d * es))) break;
+    const size_t prow = (size_t)h->item_cap * nkv * splits * 16 * h->qrt_max;
+    if ((rc = alloc_t(h, &h->o_part, prow * d, 4))) break;
+    if ((rc = alloc_t(h, &h->m_part, prow, 4))) break;
+    if ((rc = alloc_t(h, &h->l_part, prow, 4))) break;
+    if ((rc = alloc_t(h, &h->plan, 1, sizeof(AttnPlan)))) break;
+    if ((rc = alloc_t(h, &h->items, h->item_cap, sizeof(int4)))) break;
+    if ((rc = alloc_t(h, &h->first_item, c.max_batch, 4))) break;
+    if ((rc = alloc_t(h, &h->n_items, c.max_batch, 4))) break;
+    if ((rc = alloc_t(h, &h->dslots, c.max_batch, 4))) break;
+    h->partials_elems = (size_t)(2 * h->num_cus + 8) * 128 * 128;
+    if ((rc = alloc_t(h, &h->partials, h->partials_elems, 4))) break;
+    const size_t lrows = (size_t)c.max_batch * c.max_k;
+    if ((rc = alloc_t(h, &h->logits_ws, lrows * c.vocab, 4))) break;
+    if ((rc = alloc_t(h, &h->tmax, lrows * h->n_vtiles, 4))) break;
+    if ((rc = alloc_t(h, &h->tsum, lrows * h->n_vtiles, 4))) break;
+    if ((rc = alloc_t(h, &h->targ, lrows * h->n_vtiles, 4))) break;
+    if ((rc = alloc_t(h, &h->row_max, lrows, 4))) break;
+    if ((rc = alloc_t(h, &h->row_lse, lrows, 4))) break;
+    const int kc = std::max(1, std::min(c.max_tree, c.vocab));
+    if ((rc = alloc_t(h, &h->tk_ids, lrows * kc, 4))) break;
+    if ((rc = alloc_t(h, &h->tk_probs, lrows * kc, 4))) break;
+    if ((rc = alloc_t(h, &h->y, (size_t)h->inject_chunk * H, 4))) break;
+    if ((rc = alloc(h, &h->g, (size_t)h->inject_chunk * H * es))) break;
+    if ((rc = alloc_t(h, &h->a_rows, c.max_inject_rows, 4))) break;
+    if ((rc = alloc_t(h, &h->row_slot, c.max_inject_rows, 4))) break;
+    if ((rc = alloc_t(h, &h->row_pos, c.max_inject_rows, 4))) break;
+    if ((rc = alloc_t(h, &h->req_off, c.max_batch + 1, 4))) break;
+    if ((rc = alloc_t(h, &h->req_pos, c.max_batch, 4))) break;
+    if ((rc = alloc_t(h, &h->post, (size_t)c.max_batch * R, 4))) break;
+    if ((rc = alloc_t(h, &h->vstats, (size_t)c.max_batch * (2 * c.max_k + 1) * 2, 4))) break;
+  } while (0);
+  if (rc) {
+    free_all(h);
+    delete h;
+    return rc;
+  }
+  std::vector<const void*> kg(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) kg[l] = h->layers[l].k_norm;
+  if (hipMemcpy(h->d_k_gains, kg.data(), sizeof(void*) * c.n_layers, hipMemcpyHostToDevice) != hipSuccess) rc = -5;
+  if (!rc) {
+    launch_rope_table(h->rope, h->n_rope, d, (double)c.rope_theta, nullptr);
+    if (hipDeviceSynchronize() != hipSuccess || hipGetLastError() != hipSuccess) rc = DFLASH_E_HIP;
+  }
+  if (rc) {
+    free_all(h);
+    delete h;
+    return rc;
+  }
+  *out = h;
+  return DFLASH_OK;
+}
+
+int dflash_destroy(dflash_handle* h) {
+  if (!h) return DFLASH_E_INVALID;
+  (void)hipDeviceSynchronize();
+  free_all(h);
+  delete h;
+  return DFLASH_OK;
+}
+
+int dflash_reset_slots(dflash_handle* h, void* stream, int32_t n, const int32_t* slots_dev) {
+  if (!h || n < 0 || (n > 0 && !slots_dev)) return DFLASH_E_INVALID;
+  launch_reset_slots(n, slots_dev, h->ctx_len, h->cfg.max_batch, h->err, S(stream));
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
+                          const int32_t* row_start, const int32_t* row_count, int64_t rows_upper_bound,
+                          const void* const* target_hidden, int64_t row_stride) {
+  if (!h || n_req < 0 || rows_upper_bound < 0) return DFLASH_E_INVALID;
+  if (n_req == 0 || rows_upper_bound == 0) return DFLASH_OK;
+  const dflash_config& c = h->cfg;
+  if (!slots || !row_start || !row_count || !target_hidden) return DFLASH_E_INVALID;
+  if (n_req > c.max_batch || rows_upper_bound > c.max_inject_rows) return DFLASH_E_CAPACITY;
+  if (row_stride < c.target_hidden || row_stride % 8) return DFLASH_E_INVALID;
+  for (int l = 0; l < c.n_target_layers; ++l)
+    if (!target_hidden[l]) return DFLASH_E_INVALID;
+  hipStream_t s = S(stream);
+  const int dt = c.dtype;
+  const int H = c.hidden, kvdim = c.n_kv_heads * c.head_dim;
+  launch_inject_scan(n_req, slots, row_start, row_count, h->ctx_len, c.max_ctx, c.max_batch, rows_upper_bound,
+                     h->req_off, h->req_pos, h->err, s);
+  launch_inject_fill(n_req, rows_upper_bound, slots, row_start, h->req_off, h->req_pos, h->a_rows, h->row_slot,
+                     h->row_pos, s);
+  const int featK = c.n_target_layers * c.target_hidden;
+  for (int64_t c0 = 0; c0 < rows_upper_bound; c0 += h->inject_chunk) {
+    const int rows = (int)std::min<int64_t>(h->inject_chunk, rows_upper_bound - c0);
+    // fc over the concatenated target layers
+    GemmArgs ga = gemm_a1(nullptr, 0, rows, H, featK);
+    for (int l = 0; l < c.n_target_layers; ++l) {
+      ga.a_ptr[l] = target_hidden[l];
+      ga.a_ld[l] = row_stride;
+    }
+    ga.a_nseg = c.n_target_layers;
+    ga.a_segk = c.target_hidden;
+    ga.a_rows = h->a_rows + c0;
+    ga.m_valid = h->req_off + n_req;
+    ga.m_valid_base = (int)c0;
+    set_b(ga, {{h->fc, H}}, featK);
+    EpiStore<float>::Params pf{h->y, H};
+    launch_gemm(dt, EPI_STORE_F32, ga, &pf, plan_gemm(dt, rows, H, featK, h->num_cus), h->partials,
+                h->partials_elems, s);
+    launch_rmsnorm_rows_f32in(dt, rows, H, h->y, h->hidden_norm, h->g, c.rms_eps, s);
+    // per-layer K|V of the fused feature, up to 8 layers per product
+    for (int l0 = 0; l0 < c.n_layers; l0 += MAX_BSEG / 2) {
+      const int nl = std::min(MAX_BSEG / 2, c.n_layers - l0);
+      GemmArgs gk = gemm_a1(h->g, H, rows, 2 * kvdim * nl, H);
+      gk.m_valid = h->req_off + n_req;
+      gk.m_valid_base = (int)c0;
+      for (int i = 0; i < nl; ++i) {
+        gk.b_ptr[2 * i] = h->layers[l0 + i].k_w;
+        gk.b_ptr[2 * i + 1] = h->layers[l0 + i].v_w;
+        gk.b_begin[2 * i] = 2 * i * kvdim;
+        gk.b_begin[2 * i + 1] = (2 * i + 1) * kvdim;
+      }
+      gk.b_begin[2 * nl] = 2 * nl * kvdim;
+      gk.b_nseg = 2 * nl;
+      gk.b_ld = H;
+      EpiKVInject<bf16_t>::Params pk;
+      pk.cache_k = (bf16_t*)h->cache_k;
+      pk.cache_vt = (bf16_t*)h->cache_vt;
+      pk.row_slot = h->row_slot + c0;
+      pk.row_pos = h->row_pos + c0;
+      pk.k_gain = (const bf16_t* const*)(h->d_k_gains + l0);
+      pk.rope = h->rope;
+      pk.n_kv = c.n_kv_heads;
+      pk.d = c.head_dim;
+      pk.kv_dim = kvdim;
+      pk.max_batch = c.max_batch + 1;  // cache slot dimension (one spare slot)
+      pk.ctx_alloc = h->ctx_alloc;
+      pk.eps = c.rms_eps;
+      pk.layer0 = l0;
+      // the parameter block has the same layout for fp32 (pointers only differ in type)
+      launch_gemm(dt, EPI_KVINJECT, gk, &pk, plan_gemm(dt, rows, gk.N, H, h->num_cus), h->partials,
+                  h->partials_elems, s);
+    }
+  }
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+namespace {
+
+int validate_draft(dflash_handle* h, int n_req, const dflash_draft_params* p, const dflash_draft_outputs* o) {
+  const dflash_config& c = h->cfg;
+  if (!p || !o || n_req < 0) return DFLASH_E_INVALID;
+  if (n_req > c.max_batch) return DFLASH_E_CAPACITY;
+  if (p->K < 1 || p->K > c.max_k) return DFLASH_E_CAPACITY;
+  if (p->top_k < 0 || p->top_k > c.max_top_k || p->top_k > c.vocab) return DFLASH_E_CAPACITY;
+  if (p->tree_budget < 0 || p->tree_budget > c.max_tree) return DFLASH_E_CAPACITY;
+  if (!(p->temperature >= 0.f)) return DFLASH_E_INVALID;
+  if (!o->draft_ids) return DFLASH_E_INVALID;
+  if (p->top_k > 0 && (!o->topk_ids || !o->topk_probs)) return DFLASH_E_INVALID;
+  if (p->tree_budget > 0 && (!o->tree_tokens || !o->tree_parents || !o->tree_depth)) return DFLASH_E_INVALID;
+  return DFLASH_OK;
+}
+
+// LM-head statistics are ready; finish rows: stats, draft ids, top-k, tree.
+void select_stage(dflash_handle* h, hipStream_t s, int n_req, const int32_t* slots, const int32_t* anchors,
+                  const float* logits, const dflash_draft_params* p, const dflash_draft_outputs* o) {
+  const dflash_config& c = h->cfg;
+  const int K = p->K, rows = n_req * K, V = c.vocab;
+  const float T = p->temperature;
+  const float inv_t = T > 0.f ? 1.0f / T : 1.0f;
+  launch_row_finalize(rows, h->n_vtiles, h->tmax, h->tsum, h->targ, h->row_max, h->row_lse,
+                      T > 0.f ? nullptr : o->draft_ids, o->row_max, o->row_lse, s);
+  if (T > 0.f)
+    launch_sample(rows, K, slots, p->seed, p->step, inv_t, logits, V, h->n_vtiles, h->tmax, h->tsum, h->row_max,
+                  o->draft_ids, s);
+  const int B = p->tree_budget;
+  const int kc = B > 0 ? std::min(B, V) : 0;
+  if (p->top_k > 0)
+    launch_topk(rows, V, p->top_k, logits, h->tmax, h->n_vtiles, inv_t, h->row_max, h->row_lse, o->topk_ids,
+                o->topk_probs, s);
+  if (B > 0) {
+    const int32_t* ids = o->topk_ids;
+    const float* probs = o->topk_probs;
+    int stride = p->top_k;
+    if (p->top_k < kc) {
+      launch_topk(rows, V, kc, logits, h->tmax, h->n_vtiles, inv_t, h->row_max, h->row_lse, h->tk_ids, h->tk_probs,
+                  s);
+      ids = h->tk_ids;
+      probs = h->tk_probs;
+      stride = kc;
+    }
+    launch_tree(n_req, K, kc, stride, B, probs, ids, anchors, o->tree_tokens, o->tree_parents, o->tree_depth,
+                o->tree_mask, s);
+  }
+}
+
+}  // namespace
+
+int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots_in,
+                       const int32_t* anchor_ids, const dflash_draft_params* p, const dflash_draft_outputs* o) {
+  if (!h) return DFLASH_E_INVALID;
+  int rc = validate_draft(h, n_req, p, o);
+  if (rc) return rc;
+  if (n_req == 0) return DFLASH_OK;
+  if (!slots_in || !anchor_ids) return DFLASH_E_INVALID;
+  const dflash_config& c = h->cfg;
+  hipStream_t s = S(stream);
+  // every later kernel addresses the cache through validated slot ids
+  launch_sanitize_slots(n_req, slots_in, h->dslots, c.max_batch, h->err, s);
+  const int32_t* slots = h->dslots;
+  const int dt = c.dtype;
+  const int K = p->K, R = K + 1, M = n_req * R;
+  const int H = c.hidden, d = c.head_dim, nkv = c.n_kv_heads, g = c.n_q_heads / nkv;
+  const int qdim = c.n_q_heads * d, kvdim = nkv * d, F = c.ffn, V = c.vocab;
+  const int splits = h->attn_splits, gps = g / splits;
+  const int rows_split = gps * R;
+  const int qrt = (rows_split + 15) / 16;
+
+  launch_embed_norm(dt, M, R, anchor_ids, c.mask_token_id, V, h->embed, c.input_embedding_scale, H, h->X,
+                    h->layers[0].in_norm, h->hbuf, c.rms_eps, h->err, s);
+  launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->target_wg, h->item_cap, h->plan, h->items,
+                   h->first_item, h->n_items, h->err, s);
+  const int64_t layer_cache = (int64_t)(c.max_batch + 1) * nkv * h->ctx_alloc * d * h->esize;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const dflash_layer_weights& L = h->layers[l];
+    // q | k | v with head norm + RoPE into the attention layouts
+    {
+      GemmArgs ga = gemm_a1(h->hbuf, H, M, qdim + 2 * kvdim, H);
+      set_b(ga, {{L.q_w, qdim}, {L.k_w, kvdim}, {L.v_w, kvdim}}, H);
+      EpiQKV<bf16_t>::Params pq;
+      pq.qb = (bf16_t*)h->qb;
+      pq.kb = (bf16_t*)h->kb;
+      pq.vbt = (bf16_t*)h->vbt;
+      pq.slots = slots;
+      pq.ctx_len = h->ctx_len;
+      pq.q_gain = (const bf16_t*)L.q_norm;
+      pq.k_gain = (const bf16_t*)L.k_norm;
+      pq.rope = h->rope;
+      pq.R = R;
+      pq.group = g;
+      pq.n_kv = nkv;
+      pq.d = d;
+      pq.q_dim = qdim;
+      pq.kv_dim = kvdim;
+      pq.QRpad = h->QRpad;
+      pq.Rpad = h->Rpad;
+      pq.eps = c.rms_eps;
+      launch_gemm(dt, EPI_QKV, ga, &pq, plan_gemm(dt, M, ga.N, H, h->num_cus), h->partials, h->partials_elems, s);
+    }
+    // attention over [context ; block]
+    {
+      AttnArgs a;
+      a.qb = h->qb;
+      a.cache_k = (const char*)h->cache_k + l * layer_cache;
+      a.cache_vt = (const char*)h->cache_vt + l * layer_cache;
+      a.kb = h->kb;
+      a.vbt = h->vbt;
+      a.slots = slots;
+      a.ctx_len = h->ctx_len;
+      a.plan = h->plan;
+      a.items = h->items;
+      a.o_part = h->o_part;
+      a.m_part = h->m_part;
+      a.l_part = h->l_part;
+      a.n_kv = nkv;
+      a.R = R;
+      a.Rpad = h->Rpad;
+      a.QRpad = h->QRpad;
+      a.rows_per_split = rows_split;
+      a.splits = splits;
+      a.ctx_alloc = h->ctx_alloc;
+      a.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
+      const int gx = std::min(h->item_cap, n_req + h->target_wg / (nkv * splits) + 2);
+      launch_attn(dt, d, qrt, a, dim3(gx, nkv, splits), s);
+      AttnCombineArgs cb;
+      cb.o_part = h->o_part;
+      cb.m_part = h->m_part;
+      cb.l_part = h->l_part;
+      cb.first_item = h->first_item;
+      cb.n_items = h->n_items;
+      cb.out = h->attn_out;
+      cb.n_kv = nkv;
+      cb.group = g;
+      cb.R = R;
+      cb.rows_per_split = rows_split;
+      cb.splits = splits;
+      cb.QRT16 = 16 * qrt;
+      cb.q_dim = qdim;
+      cb.D = d;
+      launch_attn_combine(dt, d, cb, dim3(n_req, nkv, splits), s);
+    }
+    // output projection + residual
+    {
+      GemmArgs ga = gemm_a1(h->attn_out, qdim, M, H, qdim);
+      set_b(ga, {{L.o_w, H}}, qdim);
+      EpiResidualAdd::Params pr{h->X, H};
+      launch_gemm(dt, EPI_RESADD, ga, &pr, plan_gemm(dt, M, H, qdim, h->num_cus), h->partials, h->partials_elems, s);
+    }
+    launch_rmsnorm(dt, M, H, h->X, 0, K, R, L.post_norm, h->hbuf, c.rms_eps, s);
+    // SwiGLU MLP
+    {
+      GemmArgs ga = gemm_a1(h->hbuf, H, M, 2 * F, H);
+      ga.b_ptr[0] = L.gate_w;
+      ga.b_ptr[1] = L.up_w;
+      ga.b_interleave = 1;
+      ga.b_ld = H;
+      EpiSwiGLU<bf16_t>::Params ps{(bf16_t*)h->act, F, F};
+      launch_gemm(dt, EPI_SWIGLU, ga, &ps, plan_gemm(dt, M, 2 * F, H, h->num_cus), h->partials, h->partials_elems,
+                  s);
+      GemmArgs gd = gemm_a1(h->act, F, M, H, F);
+      set_b(gd, {{L.down_w, H}}, F);
+      EpiResidualAdd::Params pr{h->X, H};
+      launch_gemm(dt, EPI_RESADD, gd, &pr, plan_gemm(dt, M, H, F, h->num_cus), h->partials, h->partials_elems, s);
+    }
+    if (l + 1 < c.n_layers)
+      launch_rmsnorm(dt, M, H, h->X, 0, K, R, h->layers[l + 1].in_norm, h->hbuf, c.rms_eps, s);
+  }
+  // final norm on the K mask rows, LM head with streaming statistics
+  const int rows = n_req * K;
+  launch_rmsnorm(dt, rows, H, h->X, 1, K, R, h->final_norm, h->hbuf, c.rms_eps, s);
+  const float T = p->temperature;
+  const bool need_logits = o->logits || T > 0.f || p->top_k > 0 || p->tree_budget > 0;
+  float* logits = o->logits ? o->logits : (need_logits ? h->logits_ws : nullptr);
+  {
+    GemmArgs ga = gemm_a1(h->hbuf, H, rows, V, H);
+    set_b(ga, {{h->lm_head, V}}, H);
+    EpiLMHead::Params pl;
+    pl.logits = logits;
+    pl.ld = V;
+    pl.tile_max = h->tmax;
+    pl.tile_sum = h->tsum;
+    pl.tile_arg = h->targ;
+    pl.n_tiles = h->n_vtiles;
+    pl.inv_temp = T > 0.f ? 1.0f / T : 1.0f;
+    pl.out_mult = c.output_multiplier;
+    pl.softcap = c.logit_softcap;
+    GemmPlan gp = plan_gemm(dt, rows, V, H, h->num_cus);
+    gp.splits = 1;   // statistics are per output tile: no split-K for the vocabulary product
+    launch_gemm(dt, EPI_LMHEAD, ga, &pl, gp, h->partials, h->partials_elems, s);
+  }
+  select_stage(h, s, n_req, slots, anchor_ids, logits, p, o);
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+__global__ void lm_stats_from_logits_kernel(int V, int n_tiles, const float* logits, float inv_temp, float* tmax,
+                                            float* tsum, int32_t* targ) {
+  // one wave per (row, 128-column tile): the same statistics the LM-head epilogue produces
+  const int m = blockIdx.y, t = blockIdx.x, lane = threadIdx.x;
+  float best = -INFINITY;
+  int arg = 0x7fffffff;
+  float s[2];
+  for (int q = 0; q < 2; ++q) {
+    const int n = t * 128 + lane + 64 * q;
+    s[q] = -INFINITY;
+    if (n < V) {
+      s[q] = logits[(int64_t)m * V + n] * inv_temp;
+      if (s[q] > best) { best = s[q]; arg = n; }
+    }
+  }
+  const float mx = wave_max(best);
+  int cand = best == mx ? arg : 0x7fffffff;
+  for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o, 64));
+  float e = 0.f;
+  for (int q = 0; q < 2; ++q)
+    if (t * 128 + lane + 64 * q < V) e += expf(s[q] - mx);
+  e = wave_sum(e);
+  if (lane == 0) {
+    tmax[(int64_t)m * n_tiles + t] = mx;
+    tsum[(int64_t)m * n_tiles + t] = e;
+    targ[(int64_t)m * n_tiles + t] = cand;
+  }
+}
+
+int dflash_select_from_logits(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
+                              const int32_t* anchor_ids, const float* logits, const dflash_draft_params* p,
+                              const dflash_draft_outputs* o) {
+  if (!h) return DFLASH_E_INVALID;
+  int rc = validate_draft(h, n_req, p, o);
+  if (rc) return rc;
+  if (n_req == 0) return DFLASH_OK;
+  if (!slots || !logits) return DFLASH_E_INVALID;
+  hipStream_t s = S(stream);
+  const float T = p->temperature;
+  const int rows = n_req * p->K;
+  dim3 grid(h->n_vtiles, rows);
+  lm_stats_from_logits_kernel<<<grid, 64, 0, s>>>(h->cfg.vocab, h->n_vtiles, logits, T > 0.f ? 1.0f / T : 1.0f,
+                                                   h->tmax, h->tsum, h->targ);
+  select_stage(h, s, n_req, slots, anchor_ids, logits, p, o);
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, const int32_t* slots,
+                  const int32_t* draft_ids, const float* draft_logits, const float* target_logits, float temperature,
+                  uint64_t seed, uint64_t step, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len) {
+  if (!h || n_req < 0) return DFLASH_E_INVALID;
+  if (n_req == 0) return DFLASH_OK;
+  const dflash_config& c = h->cfg;
+  if (n_req > c.max_batch || K < 1 || K > c.max_k) return DFLASH_E_CAPACITY;
+  if (!draft_ids || !target_logits || !out_tokens || !out_len || !accept_len) return DFLASH_E_INVALID;
+  if (!(temperature >= 0.f)) return DFLASH_E_INVALID;
+  hipStream_t s = S(stream);
+  if (temperature == 0.f) {
+    launch_verify_greedy(n_req, K, c.vocab, draft_ids, target_logits, h->post, out_tokens, out_len, accept_len, s);
+  } else {
+    if (!draft_logits || !slots) return DFLASH_E_INVALID;
+    launch_verify_rejection(n_req, K, c.vocab, slots, draft_ids, draft_logits, target_logits, 1.0f / temperature,
+                            seed, step, h->vstats, out_tokens, out_len, accept_len, h->err, s);
+  }
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+int dflash_get_error(dflash_handle* h, void* stream, int32_t* code) {
+  if (!h || !code) return DFLASH_E_INVALID;
+  if (hipStreamSynchronize(S(stream)) != hipSuccess) return DFLASH_E_HIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, h->err, 4, hipMemcpyDeviceToHost) != hipSuccess) return DFLASH_E_HIP;
+  if (hipMemset(h->err, 0, 4) != hipSuccess) return DFLASH_E_HIP;
+  *code = v;
+  return DFLASH_OK;
+}
+
+int dflash_ctx_lens(dflash_handle* h, void* stream, int32_t* out_dev) {
+  if (!h || !out_dev) return DFLASH_E_INVALID;
+  return hipMemcpyAsync(out_dev, h->ctx_len, 4 * h->cfg.max_batch, hipMemcpyDeviceToDevice, S(stream)) == hipSuccess
+             ? DFLASH_OK
+             : DFLASH_E_HIP;
+}
+
+int dflash_copy_cache(dflash_handle* h, void* stream, int32_t layer, int32_t slot, int32_t start, int32_t n,
+                      void* k_out, void* v_out) {
+  if (!h || !k_out || !v_out) return DFLASH_E_INVALID;
+  const dflash_config& c = h->cfg;
+  if (layer < 0 || layer >= c.n_layers || slot < 0 || slot >= c.max_batch || start < 0 || n < 0 ||
+      start + n > c.max_ctx)
+    return DFLASH_E_INVALID;
+  launch_copy_cache(c.dtype, h->cache_k, h->cache_vt, layer, slot, start, n, c.max_batch + 1, c.n_kv_heads, c.head_dim,
+                    h->ctx_alloc, k_out, v_out, S(stream));
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+int dflash_synth_target_logits(void* stream, int32_t n_req, int32_t K, int32_t vocab, const float* draft_logits,
+                               float sigma, uint64_t seed, uint64_t step, float* out) {
+  if (n_req < 0 || K < 1 || vocab < 1 || !draft_logits || !out) return DFLASH_E_INVALID;
+  if (n_req == 0) return DFLASH_OK;
+  launch_synth_target(n_req, K, vocab, draft_logits, sigma, seed, step, out, S(stream));
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+int dflash_philox_uniforms(void* stream, int32_t n, uint64_t seed, uint32_t slot, uint64_t step, uint32_t purpose,
+                           float* out) {
+  if (n < 0 || (n > 0 && !out)) return DFLASH_E_INVALID;
+  launch_philox_fill(n, seed, slot, step, purpose, out, S(stream));
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+}  // extern "C"

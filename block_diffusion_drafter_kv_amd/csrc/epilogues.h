@@ -1,0 +1,237 @@
+// GEMM epilogues.  Each receives a 64-row slab of the output tile staged in LDS
+// (fp32, row stride `ld`) and finishes the fused step that follows the product.
+#pragma once
+#include "common.h"
+
+namespace dfl {
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
+
+// ---- plain store (fp32 or T) ----
+template <typename OutT>
+struct EpiStore {
+  struct Params { OutT* out; int64_t ld; };
+  template <int BN>
+  __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int, int tid) {
+    for (int idx = tid; idx < EPI_ROWS * BN; idx += 256) {
+      const int r = idx / BN, c = idx % BN;
+      const int m = m0 + r, n = n0 + c;
+      if (m < M && n < N) p.out[(int64_t)m * p.ld + n] = from_f32<OutT>(st[r * ld + c]);
+    }
+  }
+};
+
+// ---- residual add into the fp32 stream ----
+struct EpiResidualAdd {
+  struct Params { float* x; int64_t ld; };
+  template <int BN>
+  __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int, int tid) {
+    for (int idx = tid; idx < EPI_ROWS * BN; idx += 256) {
+      const int r = idx / BN, c = idx % BN;
+      const int m = m0 + r, n = n0 + c;
+      if (m < M && n < N) p.x[(int64_t)m * p.ld + n] += st[r * ld + c];
+    }
+  }
+};
+
+// ---- SwiGLU: tile columns [0, BN/2) are gate, [BN/2, BN) the matching up columns ----
+template <typename OutT>
+struct EpiSwiGLU {
+  struct Params { OutT* out; int64_t ld; int F; };
+  template <int BN>
+  __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
+    constexpr int H = BN / 2;
+    for (int idx = tid; idx < EPI_ROWS * H; idx += 256) {
+      const int r = idx / H, c = idx % H;
+      const int m = m0 + r, f = n0 / 2 + c;
+      if (m < M && f < p.F) {
+        const float gt = st[r * ld + c], up = st[r * ld + H + c];
+        p.out[(int64_t)m * p.ld + f] = from_f32<OutT>(silu_f(gt) * up);
+      }
+    }
+  }
+};
+
+// Per-head RMSNorm + rotate-half RoPE of one head held in a staged row.
+// Lanes [0, d/2) of a lane group handle the pairs (i, i + d/2).
+template <typename T>
+__device__ __forceinline__ void norm_rope_pair(float& x1, float& x2, int i, int d, const T* gain, float eps,
+                                               const float2* rope_row) {
+  const float ss = group_sum(x1 * x1 + x2 * x2, d / 2);
+  const float rs = rsqrtf(ss / (float)d + eps);
+  x1 = x1 * rs * to_f32(gain[i]);
+  x2 = x2 * rs * to_f32(gain[i + d / 2]);
+  const float2 cs = rope_row[i];  // (cos, sin)
+  const float y1 = x1 * cs.x - x2 * cs.y;
+  const float y2 = x2 * cs.x + x1 * cs.y;
+  x1 = y1;
+  x2 = y2;
+}
+
+// ---- draft block: q | k | v projections -> head norm + RoPE -> attention layouts ----
+// q rows go to qb[r][kv][i*R + j][d] (q head kv*g + i, block row j), k rows to
+// kb[r][kv][j][d], v rows to vbt[r][kv][d][j] (transposed for the PV product).
+template <typename T>
+struct EpiQKV {
+  struct Params {
+    T* qb; T* kb; T* vbt;
+    const int32_t* slots; const int32_t* ctx_len;
+    const T* q_gain; const T* k_gain;
+    const float2* rope;      // [pos][d/2] (cos, sin)
+    int R, group, n_kv, d, q_dim, kv_dim, QRpad, Rpad;
+    float eps;
+  };
+  template <int BN>
+  __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+    const int half = p.d / 2;
+    const int per = 64 / half;  // items per wave iteration
+    const int sub = lane / half, i = lane % half;
+    const int heads = BN / p.d;
+    const int items = EPI_ROWS * heads;
+    for (int it = wave * per + sub; it < items; it += 4 * per) {
+      const int r = it / heads, hh = it % heads;
+      const int m = m0 + r;
+      if (m >= M) continue;
+      const int req = m / p.R, j = m % p.R;
+      const int nb = n0 + hh * p.d;
+      float x1 = st[r * ld + hh * p.d + i], x2 = st[r * ld + hh * p.d + i + half];
+      if (nb < p.q_dim + p.kv_dim) {
+        const int slot = p.slots[req];
+        const int pos = p.ctx_len[slot] + j;
+        const bool isq = nb < p.q_dim;
+        norm_rope_pair<T>(x1, x2, i, p.d, isq ? p.q_gain : p.k_gain, p.eps, p.rope + (int64_t)pos * half);
+        if (isq) {
+          const int qh = nb / p.d, kv = qh / p.group, gi = qh % p.group;
+          T* dst = p.qb + ((int64_t)(req * p.n_kv + kv) * p.QRpad + gi * p.R + j) * p.d;
+          dst[i] = from_f32<T>(x1);
+          dst[i + half] = from_f32<T>(x2);
+        } else {
+          const int kh = (nb - p.q_dim) / p.d;
+          T* dst = p.kb + ((int64_t)(req * p.n_kv + kh) * p.Rpad + j) * p.d;
+          dst[i] = from_f32<T>(x1);
+          dst[i + half] = from_f32<T>(x2);
+        }
+      } else {
+        const int vh = (nb - p.q_dim - p.kv_dim) / p.d;
+        T* dst = p.vbt + (int64_t)(req * p.n_kv + vh) * p.d * p.Rpad;
+        dst[(int64_t)i * p.Rpad + j] = from_f32<T>(x1);
+        dst[(int64_t)(i + half) * p.Rpad + j] = from_f32<T>(x2);
+      }
+    }
+  }
+};
+
+// ---- context injection: per-layer k|v of the fused feature -> k-norm + RoPE -> cache ----
+// Cache layouts: K [layer][slot][kv][ctx_alloc][d], V^T [layer][slot][kv][d][ctx_alloc].
+template <typename T>
+struct EpiKVInject {
+  struct Params {
+    T* cache_k; T* cache_vt;
+    const int32_t* row_slot; const int32_t* row_pos;   // per GEMM row (global row index)
+    const T* const* k_gain;                              // device array [n_layers] of gains
+    const float2* rope;
+    int n_kv, d, kv_dim, max_batch;
+    int64_t ctx_alloc;
+    float eps;
+    int layer0;                                          // first layer of this product
+  };
+  template <int BN>
+  __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+    const int heads = BN / p.d;
+    for (int hh = 0; hh < heads; ++hh) {
+      const int nb = n0 + hh * p.d;
+      const int layer = nb / (2 * p.kv_dim);
+      const int within = nb % (2 * p.kv_dim);
+      const bool isv = within >= p.kv_dim;
+      const int head = (within % p.kv_dim) / p.d;
+      if (!isv) {
+        const int half = p.d / 2, per = 64 / half;
+        const int sub = lane / half, i = lane % half;
+        for (int r = wave * per + sub; r < EPI_ROWS; r += 4 * per) {
+          const int m = m0 + r;
+          if (m >= M) continue;
+          const int slot = p.row_slot[m];
+          if (slot < 0) continue;
+          const int pos = p.row_pos[m];
+          float x1 = st[r * ld + hh * p.d + i], x2 = st[r * ld + hh * p.d + i + half];
+          norm_rope_pair<T>(x1, x2, i, p.d, p.k_gain[layer], p.eps, p.rope + (int64_t)pos * half);
+          T* dst = p.cache_k + (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.ctx_alloc * p.d +
+                   (int64_t)pos * p.d;
+          dst[i] = from_f32<T>(x1);
+          dst[i + half] = from_f32<T>(x2);
+        }
+      } else {
+        // lanes walk rows (consecutive positions -> coalesced stores), waves walk columns
+        const int r = lane;
+        const int m = m0 + r;
+        int slot = -1, pos = 0;
+        if (m < M) {
+          slot = p.row_slot[m];
+          pos = p.row_pos[m];
+        }
+        if (slot >= 0) {
+          T* base = p.cache_vt + (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.d * p.ctx_alloc + pos;
+          for (int c = wave; c < p.d; c += 4) base[(int64_t)c * p.ctx_alloc] = from_f32<T>(st[r * ld + hh * p.d + c]);
+        }
+      }
+    }
+  }
+};
+
+// ---- LM head: logits (optional store) + per-(row, tile) max / sum-exp / argmax ----
+struct EpiLMHead {
+  struct Params {
+    float* logits;           // [M][ld] or null
+    int64_t ld;
+    float* tile_max;         // [M][n_tiles]   (of z / T)
+    float* tile_sum;         // [M][n_tiles]   sum exp(z/T - tile_max)
+    int32_t* tile_arg;       // [M][n_tiles]
+    int n_tiles;
+    float inv_temp, out_mult, softcap;
+  };
+  template <int BN>
+  __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int tn,
+                               int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int r = wave; r < EPI_ROWS; r += 4) {
+      const int m = m0 + r;
+      if (m >= M) break;
+      float best = -INFINITY;
+      int arg = 0x7fffffff;
+      float zz[BN / 64];
+#pragma unroll
+      for (int q = 0; q < BN / 64; ++q) {
+        const int c = lane + 64 * q, n = n0 + c;
+        float z = st[r * ld + c] * p.out_mult;
+        if (p.softcap > 0.f) z = p.softcap * tanhf(z / p.softcap);
+        zz[q] = z;
+        if (n < N) {
+          if (p.logits) p.logits[(int64_t)m * p.ld + n] = z;
+          const float s = z * p.inv_temp;
+          if (s > best) { best = s; arg = n; }
+        }
+      }
+      const float mx = wave_max(best);
+      int cand = (best == mx) ? arg : 0x7fffffff;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o, 64));
+      float e = 0.f;
+#pragma unroll
+      for (int q = 0; q < BN / 64; ++q) {
+        const int n = n0 + lane + 64 * q;
+        if (n < N) e += expf(zz[q] * p.inv_temp - mx);
+      }
+      e = wave_sum(e);
+      if (lane == 0) {
+        const int64_t o = (int64_t)m * p.n_tiles + tn;
+        p.tile_max[o] = mx;
+        p.tile_sum[o] = e;
+        p.tile_arg[o] = cand;
+      }
+    }
+  }
+};
+
+}  // namespace dfl

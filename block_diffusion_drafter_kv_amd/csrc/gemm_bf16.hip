@@ -1,0 +1,41 @@
+// bf16 GEMM instantiations and the shared tile / split planner.
+#include "gemm_dispatch.h"
+
+namespace dfl {
+
+void gemm_dispatch_bf16(EpiKind kind, int bm, const GemmArgs& g, const void* ep, hipStream_t s) {
+  gemm_dispatch_t<bf16_t>(kind, bm, g, ep, s);
+}
+
+GemmPlan plan_gemm(int dtype, int M, int N, int K, int num_cus) {
+  GemmPlan p;
+  p.bm = M <= 64 ? 64 : 128;
+  p.bn = 128;
+  const int bk = dtype == DT_BF16 ? 64 : 32;
+  const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+  const int kt = K / bk;
+  int sp = 1;
+  // split K while the grid is below two waves of work-groups and each split keeps >= 8 slabs
+  while (tiles * sp * 2 <= 2L * num_cus && kt / (sp * 2) >= 8) sp *= 2;
+  p.splits = sp;
+  return p;
+}
+
+void launch_gemm(int dtype, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan, float* partials,
+                 size_t partials_elems, hipStream_t s) {
+  const int bk = dtype == DT_BF16 ? 64 : 32;
+  g.tiles_m = (g.M + plan.bm - 1) / plan.bm;
+  g.tiles_n = (g.N + plan.bn - 1) / plan.bn;
+  g.Mpad = g.tiles_m * plan.bm;
+  g.Npad = g.tiles_n * plan.bn;
+  int splits = plan.splits;
+  while (splits > 1 && (size_t)splits * g.Mpad * g.Npad > partials_elems) splits /= 2;
+  const int kt = g.K / bk;
+  g.splits = splits;
+  g.k_per_split = ((kt + splits - 1) / splits) * bk;
+  g.partials = partials;
+  if (dtype == DT_BF16) gemm_dispatch_bf16(kind, plan.bm, g, epi_params, s);
+  else gemm_dispatch_f32(kind, plan.bm, g, epi_params, s);
+}
+
+}  // namespace dfl

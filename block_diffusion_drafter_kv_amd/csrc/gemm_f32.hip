@@ -1,0 +1,10 @@
+// fp32 GEMM instantiations (fp32 drafters use v_mfma_f32_16x16x4_f32).
+#include "gemm_dispatch.h"
+
+namespace dfl {
+
+void gemm_dispatch_f32(EpiKind kind, int bm, const GemmArgs& g, const void* ep, hipStream_t s) {
+  gemm_dispatch_t<float>(kind, bm, g, ep, s);
+}
+
+}  // namespace dfl

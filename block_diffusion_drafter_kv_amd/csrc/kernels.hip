@@ -1,0 +1,920 @@
+// Row-wise and selection kernels of the drafter hot path: RoPE table, block
+// embedding, RMSNorm, injection row tables, LM-head row statistics, sampling,
+// top-k, prefix tree, verification.
+#include "ops.h"
+
+namespace dfl {
+
+// ---- block reductions (256 threads) ----
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += red[i];
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// RoPE table: (cos, sin) of pos * theta^(-2i/d), angle formed and reduced in fp64.
+// ---------------------------------------------------------------------------
+__global__ void rope_table_kernel(float2* table, int n_pos, int d, double theta) {
+  const int half = d / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)n_pos * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double inv = pow(theta, -2.0 * (double)i / (double)d);
+  double ang = fmod((double)p * inv, 6.283185307179586476925286766559);
+  table[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+// ---------------------------------------------------------------------------
+// Block embedding [P2 §2.2; P4 §4]: row r*R + j holds the anchor (j = 0) or the
+// mask token (j >= 1), embedded and scaled; then the first layer's RMSNorm.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* anchors, int mask_id, int vocab,
+                                                          const T* embed, float scale, int H, float* X,
+                                                          const T* gain, T* h_out, float eps, int32_t* err) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const int r = m / R, j = m % R;
+  int id = j == 0 ? anchors[r] : mask_id;
+  if (id < 0 || id >= vocab) {
+    if (threadIdx.x == 0) raise_error(err, ERR_BAD_TOKEN);
+    id = 0;
+  }
+  const T* e = embed + (int64_t)id * H;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < H; c += 256) {
+    const float v = to_f32(e[c]) * scale;
+    X[(int64_t)m * H + c] = v;
+    ss += v * v;
+  }
+  ss = block_sum(ss, red);
+  const float rs = rsqrtf(ss / (float)H + eps);
+  for (int c = threadIdx.x; c < H; c += 256)
+    h_out[(int64_t)m * H + c] = from_f32<T>(X[(int64_t)m * H + c] * rs * to_f32(gain[c]));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int H, const float* X, int map_mask, int K, int R,
+                                                       const T* gain, T* h_out, float eps) {
+  __shared__ float red[4];
+  const int o = blockIdx.x;
+  const int src = map_mask ? (o / K) * R + 1 + (o % K) : o;
+  const float* x = X + (int64_t)src * H;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < H; c += 256) ss += x[c] * x[c];
+  ss = block_sum(ss, red);
+  const float rs = rsqrtf(ss / (float)H + eps);
+  for (int c = threadIdx.x; c < H; c += 256) h_out[(int64_t)o * H + c] = from_f32<T>(x[c] * rs * to_f32(gain[c]));
+}
+
+// ---------------------------------------------------------------------------
+// Injection row tables.  Requests are appended in call order; a request whose
+// rows do not fit its slot, or whose slot is invalid, is skipped and flagged.
+// ---------------------------------------------------------------------------
+__global__ void inject_scan_kernel(int n_req, const int32_t* slots, const int32_t* row_count, int32_t* ctx_len,
+                                   int max_ctx, int max_batch, int64_t rows_upper, int32_t* req_off,
+                                   int32_t* req_pos, int32_t* err) {
+  if (threadIdx.x != 0) return;
+  int64_t off = 0;
+  for (int r = 0; r < n_req; ++r) {
+    const int slot = slots[r];
+    int cnt = row_count[r];
+    req_off[r] = (int32_t)off;
+    if (slot < 0 || slot >= max_batch) {
+      raise_error(err, ERR_BAD_SLOT);
+      req_pos[r] = 0;
+      continue;
+    }
+    if (cnt < 0) {
+      raise_error(err, ERR_ROWS);
+      cnt = 0;
+    }
+    const int c0 = ctx_len[slot];
+    if ((int64_t)c0 + cnt > max_ctx) {
+      raise_error(err, ERR_CAPACITY);
+      cnt = 0;
+    }
+    if (off + cnt > rows_upper) {
+      raise_error(err, ERR_ROWS);
+      cnt = 0;
+    }
+    req_pos[r] = c0;
+    ctx_len[slot] = c0 + cnt;
+    off += cnt;
+  }
+  req_off[n_req] = (int32_t)off;
+}
+
+__global__ void inject_fill_kernel(int n_req, int64_t rows_upper, const int32_t* slots, const int32_t* row_start,
+                                   const int32_t* req_off, const int32_t* req_pos, int32_t* a_rows,
+                                   int32_t* row_slot, int32_t* row_pos) {
+  const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= rows_upper) return;
+  if (m >= req_off[n_req]) {
+    a_rows[m] = -1;
+    row_slot[m] = -1;
+    row_pos[m] = 0;
+    return;
+  }
+  int lo = 0, hi = n_req - 1;  // last r with req_off[r] <= m
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (req_off[mid] <= m) lo = mid;
+    else hi = mid - 1;
+  }
+  // skip empty requests that share the same offset
+  while (lo + 1 <= n_req - 1 && req_off[lo + 1] <= m) ++lo;
+  const int i = (int)(m - req_off[lo]);
+  a_rows[m] = row_start[lo] + i;
+  row_slot[m] = slots[lo];
+  row_pos[m] = req_pos[lo] + i;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_f32in_kernel(int H, const float* Y, const T* gain, T* g_out,
+                                                             float eps) {
+  __shared__ float red[4];
+  const int64_t o = blockIdx.x;
+  const float* y = Y + o * H;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < H; c += 256) ss += y[c] * y[c];
+  ss = block_sum(ss, red);
+  const float rs = rsqrtf(ss / (float)H + eps);
+  for (int c = threadIdx.x; c < H; c += 256) g_out[o * H + c] = from_f32<T>(y[c] * rs * to_f32(gain[c]));
+}
+
+// ---------------------------------------------------------------------------
+// LM-head rows: merge tile statistics (fixed tile order).
+// row_max = max z/T, row_lse = log sum exp(z/T - row_max), argmax (lowest id on ties).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void row_finalize_kernel(int n_tiles, const float* tmax, const float* tsum,
+                                                           const int32_t* targ, float* row_max, float* row_lse,
+                                                           int32_t* argmax_out, float* out_row_max,
+                                                           float* out_row_lse) {
+  const int m = blockIdx.x, lane = threadIdx.x;
+  const float* tm = tmax + (int64_t)m * n_tiles;
+  const float* ts = tsum + (int64_t)m * n_tiles;
+  const int32_t* ta = targ + (int64_t)m * n_tiles;
+  float best = -INFINITY;
+  int arg = 0x7fffffff;
+  for (int t = lane; t < n_tiles; t += 64) {
+    const float v = tm[t];
+    if (v > best) { best = v; arg = ta[t]; }   // ascending tiles: first max per lane has the lowest id
+  }
+  const float M = wave_max(best);
+  int cand = best == M ? arg : 0x7fffffff;
+  for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o, 64));
+  // fixed-order sum: each lane a contiguous range, then a tree over lanes
+  const int per = (n_tiles + 63) / 64;
+  float s = 0.f;
+  for (int t = lane * per; t < min(n_tiles, (lane + 1) * per); ++t) s += ts[t] * expf(tm[t] - M);
+  s = wave_sum(s);
+  if (lane == 0) {
+    const float lse = logf(s);
+    row_max[m] = M;
+    row_lse[m] = lse;
+    if (argmax_out) argmax_out[m] = cand;
+    if (out_row_max) out_row_max[m] = M;
+    if (out_row_lse) out_row_lse[m] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Inverse-CDF draft sampling [P2 §2.2 "采样时按分布抽取"]: the smallest id c
+// with sum_{id<=c} exp(z_id/T - M) > u * S, with u = Philox(seed; j+1, slot,
+// step, 0).  The sum runs over the LM-head tile sums (ascending tiles), then
+// inside the selected tile (ascending ids).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_incl_scan(float v, float* sh) {
+  // inclusive scan over 256 threads in thread order
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  float x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  float add = 0.f;
+  for (int i = 0; i < w; ++i) add += sh[i];
+  return x + add;
+}
+
+__global__ __launch_bounds__(256) void sample_kernel(int K, const int32_t* slots, uint64_t seed, uint64_t step,
+                                                      float inv_temp, const float* logits, int V, int n_tiles,
+                                                      const float* tmax, const float* tsum, const float* row_max,
+                                                      int32_t* draft_ids) {
+  __shared__ float sh[8];
+  __shared__ int s_thread;
+  __shared__ int s_tile;
+  __shared__ float s_before;
+  const int m = blockIdx.x;
+  const int r = m / K, j = m % K;
+  const float M = row_max[m];
+  const float u = philox_uniform(seed, (uint32_t)slots[r], step, (uint32_t)(j + 1), PURPOSE_DRAFT);
+  const int per = (n_tiles + 255) / 256;
+  const int t0 = threadIdx.x * per, t1 = min(n_tiles, t0 + per);
+  const float* tm = tmax + (int64_t)m * n_tiles;
+  const float* ts = tsum + (int64_t)m * n_tiles;
+  float w = 0.f;
+  for (int t = t0; t < t1; ++t) w += ts[t] * expf(tm[t] - M);
+  const float incl = block_incl_scan(w, sh);
+  __shared__ float s_total;
+  if (threadIdx.x == 255) s_total = incl;
+  if (threadIdx.x == 0) s_thread = -1;
+  __syncthreads();
+  const float target = u * s_total;
+  const float excl = incl - w;
+  if (excl <= target && target < incl) s_thread = threadIdx.x;  // exactly one thread (ranges are disjoint)
+  __syncthreads();
+  if (threadIdx.x == 0 && s_thread < 0) {
+    // rounding put the target on/after the total: take the last tile with mass
+    int th = 255;
+    s_thread = th;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x == s_thread) {
+    float acc = excl;
+    int tile = -1;
+    float before = excl;
+    int last_nz = -1;
+    float last_before = excl;
+    for (int t = t0; t < t1; ++t) {
+      const float wt = ts[t] * expf(tm[t] - M);
+      if (wt > 0.f) { last_nz = t; last_before = acc; }
+      if (target < acc + wt && tile < 0) { tile = t; before = acc; }
+      acc += wt;
+    }
+    if (tile < 0) {   // fall back to the last tile with mass (at or before this range)
+      int t = last_nz;
+      before = last_before;
+      if (t < 0) {    // scan backwards over all tiles
+        float a2 = 0.f;
+        for (int q = 0; q < n_tiles; ++q) {
+          const float wt = ts[q] * expf(tm[q] - M);
+          if (wt > 0.f) { t = q; before = a2; }
+          a2 += wt;
+        }
+      }
+      tile = t;
+    }
+    s_tile = tile;
+    s_before = before;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int tile = s_tile;
+    const float* z = logits + (int64_t)m * V;
+    const int c0 = tile * 128 + 2 * lane;
+    const float e0 = c0 < V ? expf(z[c0] * inv_temp - M) : 0.f;
+    const float e1 = c0 + 1 < V ? expf(z[c0 + 1] * inv_temp - M) : 0.f;
+    float x = e0 + e1;
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    const float excl2 = s_before + (x - e0 - e1);
+    const float tgt = target;
+    int pick = 0x7fffffff;
+    if (c0 < V && e0 > 0.f && tgt < excl2 + e0) pick = c0;
+    else if (c0 + 1 < V && e1 > 0.f && tgt < excl2 + e0 + e1) pick = c0 + 1;
+    for (int o = 32; o > 0; o >>= 1) pick = min(pick, __shfl_xor(pick, o, 64));
+    if (pick == 0x7fffffff) {   // rounding: last id of the tile with weight
+      int lastp = -1;
+      if (c0 < V && e0 > 0.f) lastp = c0;
+      if (c0 + 1 < V && e1 > 0.f) lastp = c0 + 1;
+      for (int o = 32; o > 0; o >>= 1) lastp = max(lastp, __shfl_xor(lastp, o, 64));
+      pick = lastp < 0 ? tile * 128 : lastp;
+    }
+    if (lane == 0) draft_ids[m] = pick;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k per row [P5 §3.2: softmax over the vocabulary, then top-k]: order by
+// logit descending, ties by lower id.  Candidates are pruned with the LM-head
+// tile maxima (the k largest tile maxima bound the k-th largest logit), then a
+// radix select on 64-bit keys (orderable logit bits, inverted id) finds the
+// exact k-th key; the selected k are sorted with a bitonic network.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f2key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t ckey(float f, int idx) {
+  return ((uint64_t)f2key(f) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+static constexpr int TOPK_CAP = 4096;
+
+// k-th largest (1-based) composite key among n items provided by get(i).
+template <class Get>
+__device__ uint64_t radix_kth(int n, int k, Get get, uint32_t* hist, uint64_t* sh_prefix, int* sh_k) {
+  uint64_t prefix = 0;
+  int krem = k;
+  for (int pass = 7; pass >= 0; --pass) {
+    const int shift = pass * 8;
+    for (int b = threadIdx.x; b < 256; b += blockDim.x) hist[b] = 0;
+    __syncthreads();
+    const uint64_t hmask = pass == 7 ? 0ull : (~0ull << (shift + 8));
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const uint64_t key = get(i);
+      if ((key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shift) & 255], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int cum = 0, b = 255;
+      for (; b > 0; --b) {
+        if (cum + (int)hist[b] >= krem) break;
+        cum += hist[b];
+      }
+      *sh_prefix = prefix | ((uint64_t)b << shift);
+      *sh_k = krem - cum;
+    }
+    __syncthreads();
+    prefix = *sh_prefix;
+    krem = *sh_k;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(int V, int k, const float* logits, const float* tmax, int n_tiles,
+                                                    float inv_temp, const float* row_max, const float* row_lse,
+                                                    int32_t* ids_out, float* probs_out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t sh_prefix;
+  __shared__ int sh_k;
+  __shared__ uint64_t cand[TOPK_CAP];
+  __shared__ int s_n;
+  __shared__ uint64_t sel[512];
+  const int m = blockIdx.x;
+  const float* z = logits + (int64_t)m * V;
+  const float* tm = tmax + (int64_t)m * n_tiles;
+  const int kk = min(k, V);
+  // threshold from the tile maxima (tile max is in z/T units: compare via the same scaling).
+  // With fewer tiles than k the maxima bound nothing: every element is a candidate.
+  uint32_t thr = 0;
+  if (kk <= n_tiles) {
+    const uint64_t tkey = radix_kth(n_tiles, kk, [&](int i) { return ckey(tm[i], i); }, hist, &sh_prefix, &sh_k);
+    thr = (uint32_t)(tkey >> 32);
+  }
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    if (f2key(tm[t]) < thr) continue;
+    const int c = t * 128 + (threadIdx.x & 127);
+    if (threadIdx.x < 128 && c < V) {
+      const float v = z[c] * inv_temp;
+      if (f2key(v) >= thr) {
+        const int slot = atomicAdd(&s_n, 1);
+        if (slot < TOPK_CAP) cand[slot] = ckey(v, c);
+      }
+    }
+  }
+  __syncthreads();
+  const int n = s_n;
+  uint64_t kth;
+  if (n <= TOPK_CAP) {
+    kth = radix_kth(n, kk, [&](int i) { return cand[i]; }, hist, &sh_prefix, &sh_k);
+  } else {
+    kth = radix_kth(V, kk, [&](int i) { return ckey(z[i] * inv_temp, i); }, hist, &sh_prefix, &sh_k);
+  }
+  // gather the k selected keys
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  int P = 1;
+  while (P < kk) P <<= 1;
+  if (n <= TOPK_CAP) {
+    for (int i = threadIdx.x; i < n; i += 256)
+      if (cand[i] >= kth) sel[atomicAdd(&s_n, 1)] = cand[i];
+  } else {
+    for (int i = threadIdx.x; i < V; i += 256) {
+      const uint64_t key = ckey(z[i] * inv_temp, i);
+      if (key >= kth) sel[atomicAdd(&s_n, 1)] = key;
+    }
+  }
+  __syncthreads();
+  for (int i = kk + threadIdx.x; i < P; i += 256) sel[i] = 0;
+  __syncthreads();
+  // bitonic sort, descending
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < P; i += 256) {
+        const int jx = i ^ stride;
+        if (jx > i) {
+          const bool desc = (i & size) == 0;
+          const uint64_t a = sel[i], b = sel[jx];
+          if (desc ? (a < b) : (a > b)) {
+            sel[i] = b;
+            sel[jx] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const float M = row_max[m], L = row_lse[m];
+  for (int i = threadIdx.x; i < kk; i += 256) {
+    const int id = (int)(0xFFFFFFFFu - (uint32_t)(sel[i] & 0xFFFFFFFFull));
+    ids_out[(int64_t)m * k + i] = id;
+    probs_out[(int64_t)m * k + i] = expf(z[id] * inv_temp - M - L);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Best-first top-B prefix tree [P5 §2.3] per request (one wave): the frontier
+// (at most 2B + 1 rank tuples) sits in LDS; each pop is a wave-parallel
+// arg-best under the order (larger fp32 prefix probability, then shallower,
+// then lexicographically smaller rank tuple).  Node 0 is the root (anchor).
+// Mask [P5 §3.3]: node i sees itself, its ancestors and the root.
+// ---------------------------------------------------------------------------
+static constexpr int TREE_MAXB = 256;
+static constexpr int TREE_MAXF = 2 * TREE_MAXB + 2;
+
+__global__ __launch_bounds__(64) void tree_kernel(int L, int Kc, int stride, int B, const float* probs, const int32_t* ids,
+                                                   const int32_t* anchors, int32_t* tokens, int32_t* parents,
+                                                   int32_t* depth_out, uint64_t* mask) {
+  __shared__ float f_p[TREE_MAXF];
+  __shared__ int f_parent[TREE_MAXF], f_rank[TREE_MAXF], f_depth[TREE_MAXF];
+  __shared__ int f_alive[TREE_MAXF];
+  __shared__ int n_parent[TREE_MAXB + 1], n_rank[TREE_MAXB + 1], n_depth[TREE_MAXB + 1];
+  __shared__ float n_p[TREE_MAXB + 1];
+  __shared__ int s_nf;
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const float* pr = probs + (int64_t)r * L * stride;   // position i's candidates at pr[i * stride ..]
+  const int32_t* id = ids + (int64_t)r * L * stride;
+  const int words = (B + 1 + 63) / 64;
+
+  // rank-tuple comparison for exact ties: walk both parent chains (equal depth)
+  auto lex_less = [&](int pa, int ra, int pb, int rb) -> bool {
+    // tuples are (chain(pa), ra) and (chain(pb), rb); compare from the root down
+    int ca[64], cb[64];
+    int da = 0, db = 0;
+    for (int x = pa; x > 0; x = n_parent[x]) ca[da++] = n_rank[x];
+    for (int x = pb; x > 0; x = n_parent[x]) cb[db++] = n_rank[x];
+    for (int i = 1; i <= da; ++i) {
+      const int a = ca[da - i], b = cb[db - i];
+      if (a != b) return a < b;
+    }
+    return ra < rb;
+  };
+  auto better = [&](int a, int b) -> bool {   // frontier entries
+    if (f_p[a] != f_p[b]) return f_p[a] > f_p[b];
+    if (f_depth[a] != f_depth[b]) return f_depth[a] < f_depth[b];
+    return lex_less(f_parent[a], f_rank[a], f_parent[b], f_rank[b]);
+  };
+
+  if (lane == 0) {
+    n_parent[0] = -1; n_rank[0] = 0; n_depth[0] = 0; n_p[0] = 1.f;
+    f_p[0] = pr[0]; f_parent[0] = 0; f_rank[0] = 1; f_depth[0] = 1; f_alive[0] = 1;
+    s_nf = 1;
+  }
+  __syncthreads();
+  int nodes = 0;
+  for (int step = 0; step < B; ++step) {
+    const int nf = s_nf;
+    int best = -1;
+    for (int i = lane; i < nf; i += 64)
+      if (f_alive[i] && (best < 0 || better(i, best))) best = i;
+    for (int o = 32; o > 0; o >>= 1) {
+      const int other = __shfl_xor(best, o, 64);
+      if (other >= 0 && (best < 0 || better(other, best))) best = other;
+    }
+    if (best < 0) break;
+    if (lane == 0) {
+      const int idx = nodes + 1;
+      const int d = f_depth[best], par = f_parent[best], rk = f_rank[best];
+      f_alive[best] = 0;
+      n_parent[idx] = par; n_rank[idx] = rk; n_depth[idx] = d; n_p[idx] = f_p[best];
+      int nf2 = nf;
+      if (rk < Kc) {   // sibling
+        const float pp = d == 1 ? pr[rk] : n_p[par] * pr[(d - 1) * stride + rk];
+        f_p[nf2] = pp; f_parent[nf2] = par; f_rank[nf2] = rk + 1; f_depth[nf2] = d; f_alive[nf2] = 1; ++nf2;
+      }
+      if (d < L) {     // child
+        f_p[nf2] = f_p[best] * pr[d * stride]; f_parent[nf2] = idx; f_rank[nf2] = 1; f_depth[nf2] = d + 1;
+        f_alive[nf2] = 1; ++nf2;
+      }
+      s_nf = nf2;
+    }
+    ++nodes;
+    __syncthreads();
+  }
+  // outputs
+  const int64_t base = (int64_t)r * (B + 1);
+  for (int i = lane; i <= B; i += 64) {
+    if (i == 0) {
+      tokens[base] = anchors ? anchors[r] : -1;
+      parents[base] = -1;
+      depth_out[base] = 0;
+    } else if (i <= nodes) {
+      const int d = n_depth[i];
+      tokens[base + i] = id[(d - 1) * stride + n_rank[i] - 1];
+      parents[base + i] = n_parent[i];
+      depth_out[base + i] = d;
+    } else {
+      tokens[base + i] = -1;
+      parents[base + i] = -1;
+      depth_out[base + i] = -1;
+    }
+  }
+  if (mask) {
+    // row i = row(parent) | bit(i); rows built in node order by lane 0 (parents precede children)
+    if (lane == 0) {
+      uint64_t* mrow0 = mask + base * words;
+      for (int w = 0; w < words; ++w) mrow0[w] = 0;
+      mrow0[0] = 1ull;
+      for (int i = 1; i <= B; ++i) {
+        uint64_t* mr = mask + (base + i) * words;
+        if (i <= nodes) {
+          const uint64_t* mp = mask + (base + n_parent[i]) * words;
+          for (int w = 0; w < words; ++w) mr[w] = mp[w];
+          mr[i / 64] |= 1ull << (i % 64);
+        } else {
+          for (int w = 0; w < words; ++w) mr[w] = 0;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Verification.
+// Greedy [P2 §2.3]: a = sum_i prod_{k<=i} [d_k == argmax t_{k-1}]; emit d_1..d_a, argmax t_a.
+// Rejection [P2 §2.3, §4.2]: accept d_i iff u_i * q_i(d_i) < p_{i-1}(d_i); at the
+// first rejection draw from max(0, p - q) (or p when that mass is below
+// RESIDUAL_EPS); after K acceptances draw the bonus from p_K.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void argmax_rows_kernel(int V, const float* x, int32_t* out) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int64_t m = blockIdx.x;
+  const float* row = x + m * V;
+  float best = -INFINITY;
+  int arg = 0x7fffffff;
+  for (int c = threadIdx.x; c < V; c += 256) {
+    const float v = row[c];
+    if (v > best) { best = v; arg = c; }
+  }
+  const float M = wave_max(best);
+  int cand = best == M ? arg : 0x7fffffff;
+  for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o, 64));
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) { sv[w] = M; si[w] = cand; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = sv[0];
+    int a = si[0];
+    for (int i = 1; i < 4; ++i)
+      if (sv[i] > b || (sv[i] == b && si[i] < a)) { b = sv[i]; a = si[i]; }
+    out[m] = a;
+  }
+}
+
+__global__ void greedy_finish_kernel(int n_req, int K, const int32_t* draft_ids, const int32_t* post,
+                                     int32_t* out_tokens, int32_t* out_len, int32_t* accept_len) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_req) return;
+  const int32_t* d = draft_ids + (int64_t)r * K;
+  const int32_t* p = post + (int64_t)r * (K + 1);
+  int a = 0;
+  while (a < K && d[a] == p[a]) ++a;
+  int32_t* o = out_tokens + (int64_t)r * (K + 1);
+  for (int i = 0; i < a; ++i) o[i] = d[i];
+  o[a] = p[a];
+  for (int i = a + 1; i <= K; ++i) o[i] = -1;
+  out_len[r] = a + 1;
+  accept_len[r] = a;
+}
+
+// per row: (max of z/T, sum exp(z/T - max)); stats row q of request r = q / (2K+1):
+// j = q % (2K+1) <= K is target row j, otherwise draft row j - K - 1.
+__global__ __launch_bounds__(256) void softmax_stats_kernel(int K, int V, const float* target, const float* draft,
+                                                             float inv_temp, float* stats) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  const int64_t r = m / (2 * K + 1), j = m % (2 * K + 1);
+  const float* row = j <= K ? target + (r * (K + 1) + j) * V : draft + (r * K + (j - K - 1)) * V;
+  float mx = -INFINITY;
+  for (int c = threadIdx.x; c < V; c += 256) mx = fmaxf(mx, row[c] * inv_temp);
+  mx = wave_max(mx);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // fixed order: thread-contiguous ranges, then the scan helper's order
+  const int per = (V + 255) / 256;
+  float s = 0.f;
+  for (int c = threadIdx.x * per; c < min(V, (int)(threadIdx.x + 1) * per); ++c) s += expf(row[c] * inv_temp - M);
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) {
+    stats[2 * m] = M;
+    stats[2 * m + 1] = s;
+  }
+}
+
+static constexpr float RESIDUAL_EPS = 9.5367431640625e-07f;  // 2^-20
+
+__global__ __launch_bounds__(256) void rejection_kernel(int K, int V, const int32_t* slots, const int32_t* draft_ids,
+                                                         const float* draft_logits, const float* target,
+                                                         float inv_temp, uint64_t seed, uint64_t step,
+                                                         const float* stats, int32_t* out_tokens, int32_t* out_len,
+                                                         int32_t* accept_len, int32_t* err) {
+  __shared__ float sh[8];
+  __shared__ int s_a, s_stop;
+  __shared__ float s_total;
+  __shared__ int s_thread, s_pick;
+  const int r = blockIdx.x;
+  const uint32_t slot = (uint32_t)slots[r];
+  const float* T0 = target + (int64_t)r * (K + 1) * V;
+  const float* Z0 = draft_logits + (int64_t)r * K * V;
+  const float* ts = stats + (int64_t)r * (2 * K + 1) * 2;   // rows: K+1 target, then K draft
+  const int32_t* d = draft_ids + (int64_t)r * K;
+  if (threadIdx.x == 0) {
+    int a = 0;
+    for (; a < K; ++a) {
+      const int i = a + 1;
+      const int tok = d[a];
+      if (tok < 0 || tok >= V) {   // not a token: reject here (and flag it)
+        raise_error(err, ERR_BAD_TOKEN);
+        break;
+      }
+      const float pm = ts[2 * a], ps = ts[2 * a + 1];
+      const float qm = ts[2 * (K + 1 + a)], qs = ts[2 * (K + 1 + a) + 1];
+      const float p = expf(T0[(int64_t)a * V + tok] * inv_temp - pm) / ps;
+      const float q = expf(Z0[(int64_t)a * V + tok] * inv_temp - qm) / qs;
+      const float u = philox_uniform(seed, slot, step, (uint32_t)i, PURPOSE_ACCEPT);
+      if (!(u * q < p)) break;
+    }
+    s_a = a;
+  }
+  __syncthreads();
+  const int a = s_a;
+  const bool bonus = a == K;
+  const int row = a;   // target row p_a (p_{i*-1} with i* = a+1, or the bonus row K)
+  const float* t = T0 + (int64_t)row * V;
+  const float* z = bonus ? nullptr : Z0 + (int64_t)a * V;
+  const float pm = ts[2 * row], ps = ts[2 * row + 1];
+  const float qm = bonus ? 0.f : ts[2 * (K + 1 + a)], qs = bonus ? 1.f : ts[2 * (K + 1 + a) + 1];
+  const int per = (V + 255) / 256;
+  const int c0 = threadIdx.x * per, c1 = min(V, c0 + per);
+  auto weight = [&](int c, bool use_resid) -> float {
+    const float p = expf(t[c] * inv_temp - pm) / ps;
+    if (!use_resid) return p;
+    const float q = expf(z[c] * inv_temp - qm) / qs;
+    return fmaxf(p - q, 0.f);
+  };
+  bool use_resid = !bonus;
+  float w = 0.f;
+  if (use_resid) {
+    for (int c = c0; c < c1; ++c) w += weight(c, true);
+    float tot = block_incl_scan(w, sh);
+    if (threadIdx.x == 255) s_total = tot;
+    __syncthreads();
+    if (s_total < RESIDUAL_EPS) use_resid = false;   // exhausted / underflowed: sample from p
+    __syncthreads();
+  }
+  if (!use_resid) {
+    w = 0.f;
+    for (int c = c0; c < c1; ++c) w += weight(c, false);
+  }
+  const float incl = block_incl_scan(w, sh);
+  if (threadIdx.x == 255) s_total = incl;
+  if (threadIdx.x == 0) { s_thread = -1; s_pick = -1; }
+  __syncthreads();
+  const float u2 = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_RESAMPLE);
+  const float target_mass = u2 * s_total;
+  const float excl = incl - w;
+  if (excl <= target_mass && target_mass < incl) s_thread = threadIdx.x;
+  __syncthreads();
+  if ((int)threadIdx.x == s_thread) {
+    float acc = excl;
+    for (int c = c0; c < c1; ++c) {
+      const float wc = weight(c, use_resid);
+      if (wc > 0.f && target_mass < acc + wc) { s_pick = c; break; }
+      acc += wc;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int pick = s_pick;
+    if (pick < 0) {   // rounding: last id with weight
+      for (int c = V - 1; c >= 0; --c)
+        if (weight(c, use_resid) > 0.f) { pick = c; break; }
+      if (pick < 0) pick = 0;
+    }
+    int32_t* o = out_tokens + (int64_t)r * (K + 1);
+    for (int i = 0; i < a; ++i) o[i] = d[i];
+    o[a] = pick;
+    for (int i = a + 1; i <= K; ++i) o[i] = -1;
+    out_len[r] = a + 1;
+    accept_len[r] = a;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Synthetic target logits (benchmark stand-in for the target model):
+// row j < K = draft row j + sigma * N(0,1); row K = sigma * N(0,1).
+// ---------------------------------------------------------------------------
+__global__ void synth_target_kernel(int K, int V, const float* draft, float sigma, uint64_t seed, uint64_t step,
+                                    float* out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t rows = (int64_t)gridDim.y;
+  (void)rows;
+  const int rr = blockIdx.y;            // request * (K+1) + j
+  if (idx >= V) return;
+  const int r = rr / (K + 1), j = rr % (K + 1);
+  U4 c{(uint32_t)idx, (uint32_t)rr, (uint32_t)step, PURPOSE_NOISE};
+  const U4 o = philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  const float u1 = ((float)(o.x >> 8) + 1.0f) * (1.0f / 16777216.0f);
+  const float u2 = (float)(o.y >> 8) * (1.0f / 16777216.0f);
+  const float n = sqrtf(-2.0f * logf(u1)) * cosf(6.283185307f * u2);
+  const float base = j < K ? draft[((int64_t)r * K + j) * V + idx] : 0.f;
+  out[(int64_t)rr * V + idx] = base + sigma * n;
+}
+
+template <typename T>
+__global__ void copy_cache_kernel(const T* cache_k, const T* cache_vt, int layer, int slot, int start, int n,
+                                  int max_batch, int n_kv, int d, int64_t ctx_alloc, T* k_out, T* v_out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)n * n_kv * d;
+  if (idx >= total) return;
+  const int e = (int)(idx % d);
+  const int h = (int)((idx / d) % n_kv);
+  const int i = (int)(idx / ((int64_t)d * n_kv));
+  const int64_t head = ((int64_t)layer * max_batch + slot) * n_kv + h;
+  k_out[idx] = cache_k[(head * ctx_alloc + start + i) * d + e];
+  v_out[idx] = cache_vt[(head * d + e) * ctx_alloc + start + i];
+}
+
+__global__ void reset_slots_kernel(int n, const int32_t* slots, int32_t* ctx_len, int max_batch, int32_t* err) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int s = slots[i];
+  if (s < 0 || s >= max_batch) {
+    raise_error(err, ERR_BAD_SLOT);
+    return;
+  }
+  ctx_len[s] = 0;
+}
+
+__global__ void philox_fill_kernel(int n, uint64_t seed, uint32_t slot, uint64_t step, uint32_t purpose, float* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = philox_uniform(seed, slot, step, (uint32_t)i, purpose);
+}
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+void launch_rope_table(float2* table, int n_pos, int d, double theta, hipStream_t s) {
+  const int64_t n = (int64_t)n_pos * (d / 2);
+  rope_table_kernel<<<cdiv(n, 256), 256, 0, s>>>(table, n_pos, d, theta);
+}
+
+void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int mask_id, int vocab, const void* embed,
+                       float scale, int H, float* X, const void* gain, void* h_out, float eps, int32_t* err,
+                       hipStream_t s) {
+  if (dtype == DT_BF16)
+    embed_norm_kernel<bf16_t><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const bf16_t*)embed, scale, H, X,
+                                                      (const bf16_t*)gain, (bf16_t*)h_out, eps, err);
+  else
+    embed_norm_kernel<float><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const float*)embed, scale, H, X,
+                                                     (const float*)gain, (float*)h_out, eps, err);
+}
+
+void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, int K, int R, const void* gain,
+                    void* h_out, float eps, hipStream_t s) {
+  if (n_rows <= 0) return;
+  if (dtype == DT_BF16)
+    rmsnorm_kernel<bf16_t><<<n_rows, 256, 0, s>>>(H, X, map_mask, K, R, (const bf16_t*)gain, (bf16_t*)h_out, eps);
+  else
+    rmsnorm_kernel<float><<<n_rows, 256, 0, s>>>(H, X, map_mask, K, R, (const float*)gain, (float*)h_out, eps);
+}
+
+void launch_inject_scan(int n_req, const int32_t* slots, const int32_t* row_start, const int32_t* row_count,
+                        int32_t* ctx_len, int max_ctx, int max_batch, int64_t rows_upper, int32_t* req_off,
+                        int32_t* req_pos, int32_t* err, hipStream_t s) {
+  (void)row_start;
+  inject_scan_kernel<<<1, 64, 0, s>>>(n_req, slots, row_count, ctx_len, max_ctx, max_batch, rows_upper, req_off,
+                                       req_pos, err);
+}
+
+void launch_inject_fill(int n_req, int64_t rows_upper, const int32_t* slots, const int32_t* row_start,
+                        const int32_t* req_off, const int32_t* req_pos, int32_t* a_rows, int32_t* row_slot,
+                        int32_t* row_pos, hipStream_t s) {
+  if (rows_upper <= 0) return;
+  inject_fill_kernel<<<cdiv(rows_upper, 256), 256, 0, s>>>(n_req, rows_upper, slots, row_start, req_off, req_pos,
+                                                           a_rows, row_slot, row_pos);
+}
+
+void launch_rmsnorm_rows_f32in(int dtype, int n_rows, int H, const float* Y, const void* gain, void* g_out, float eps,
+                               hipStream_t s) {
+  if (n_rows <= 0) return;
+  if (dtype == DT_BF16)
+    rmsnorm_f32in_kernel<bf16_t><<<n_rows, 256, 0, s>>>(H, Y, (const bf16_t*)gain, (bf16_t*)g_out, eps);
+  else
+    rmsnorm_f32in_kernel<float><<<n_rows, 256, 0, s>>>(H, Y, (const float*)gain, (float*)g_out, eps);
+}
+
+void launch_row_finalize(int n_rows, int n_tiles, const float* tmax, const float* tsum, const int32_t* targ,
+                         float* row_max, float* row_lse, int32_t* argmax_out, float* out_row_max, float* out_row_lse,
+                         hipStream_t s) {
+  row_finalize_kernel<<<n_rows, 64, 0, s>>>(n_tiles, tmax, tsum, targ, row_max, row_lse, argmax_out, out_row_max,
+                                             out_row_lse);
+}
+
+void launch_sample(int n_rows, int K, const int32_t* slots, uint64_t seed, uint64_t step, float inv_temp,
+                   const float* logits, int V, int n_tiles, const float* tmax, const float* tsum,
+                   const float* row_max, int32_t* draft_ids, hipStream_t s) {
+  sample_kernel<<<n_rows, 256, 0, s>>>(K, slots, seed, step, inv_temp, logits, V, n_tiles, tmax, tsum, row_max,
+                                        draft_ids);
+}
+
+void launch_topk(int n_rows, int V, int k, const float* logits, const float* tmax, int n_tiles, float inv_temp,
+                 const float* row_max, const float* row_lse, int32_t* ids_out, float* probs_out, hipStream_t s) {
+  topk_kernel<<<n_rows, 256, 0, s>>>(V, k, logits, tmax, n_tiles, inv_temp, row_max, row_lse, ids_out, probs_out);
+}
+
+void launch_tree(int n_req, int L, int Kc, int stride, int B, const float* probs, const int32_t* ids,
+                 const int32_t* anchors, int32_t* tokens, int32_t* parents, int32_t* depth, uint64_t* mask,
+                 hipStream_t s) {
+  tree_kernel<<<n_req, 64, 0, s>>>(L, Kc, stride, B, probs, ids, anchors, tokens, parents, depth, mask);
+}
+
+void launch_verify_greedy(int n_req, int K, int V, const int32_t* draft_ids, const float* target, int32_t* post,
+                          int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, hipStream_t s) {
+  argmax_rows_kernel<<<n_req * (K + 1), 256, 0, s>>>(V, target, post);
+  greedy_finish_kernel<<<cdiv(n_req, 64), 64, 0, s>>>(n_req, K, draft_ids, post, out_tokens, out_len, accept_len);
+}
+
+void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,
+                             const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
+                             uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
+                             int32_t* err, hipStream_t s) {
+  // stats rows per request: K+1 target rows then K draft rows
+  softmax_stats_kernel<<<n_req * (2 * K + 1), 256, 0, s>>>(K, V, target, draft_logits, inv_temp, stats);
+  rejection_kernel<<<n_req, 256, 0, s>>>(K, V, slots, draft_ids, draft_logits, target, inv_temp, seed, step, stats,
+                                          out_tokens, out_len, accept_len, err);
+}
+
+__global__ void sanitize_slots_kernel(int n, const int32_t* in, int32_t* out, int max_batch, int32_t* err) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int s = in[i];
+  if (s < 0 || s >= max_batch) {
+    raise_error(err, ERR_BAD_SLOT);
+    out[i] = max_batch;   // the spare, always-empty slot
+  } else {
+    out[i] = s;
+  }
+}
+
+void launch_sanitize_slots(int n, const int32_t* in, int32_t* out, int max_batch, int32_t* err, hipStream_t s) {
+  if (n <= 0) return;
+  sanitize_slots_kernel<<<cdiv(n, 64), 64, 0, s>>>(n, in, out, max_batch, err);
+}
+
+void launch_synth_target(int n_req, int K, int V, const float* draft_logits, float sigma, uint64_t seed,
+                         uint64_t step, float* out, hipStream_t s) {
+  dim3 grid(cdiv(V, 256), n_req * (K + 1));
+  synth_target_kernel<<<grid, 256, 0, s>>>(K, V, draft_logits, sigma, seed, step, out);
+}
+
+void launch_copy_cache(int dtype, const void* cache_k, const void* cache_vt, int layer, int slot, int start, int n,
+                       int max_batch, int n_kv, int d, int64_t ctx_alloc, void* k_out, void* v_out, hipStream_t s) {
+  const int64_t total = (int64_t)n * n_kv * d;
+  if (total <= 0) return;
+  if (dtype == DT_BF16)
+    copy_cache_kernel<bf16_t><<<cdiv(total, 256), 256, 0, s>>>((const bf16_t*)cache_k, (const bf16_t*)cache_vt, layer,
+                                                                slot, start, n, max_batch, n_kv, d, ctx_alloc,
+                                                                (bf16_t*)k_out, (bf16_t*)v_out);
+  else
+    copy_cache_kernel<float><<<cdiv(total, 256), 256, 0, s>>>((const float*)cache_k, (const float*)cache_vt, layer,
+                                                               slot, start, n, max_batch, n_kv, d, ctx_alloc,
+                                                               (float*)k_out, (float*)v_out);
+}
+
+void launch_reset_slots(int n, const int32_t* slots, int32_t* ctx_len, int max_batch, int32_t* err, hipStream_t s) {
+  if (n <= 0) return;
+  reset_slots_kernel<<<cdiv(n, 64), 64, 0, s>>>(n, slots, ctx_len, max_batch, err);
+}
+
+void launch_philox_fill(int n, uint64_t seed, uint32_t slot, uint64_t step, uint32_t purpose, float* out,
+                        hipStream_t s) {
+  if (n <= 0) return;
+  philox_fill_kernel<<<cdiv(n, 256), 256, 0, s>>>(n, seed, slot, step, purpose, out);
+}
+
+}  // namespace dfl

@@ -1,0 +1,73 @@
+// Internal launch interface between the host library and the kernels.
+#pragma once
+#include "common.h"
+#include "gemm.h"
+#include "epilogues.h"
+#include "attention.h"
+
+namespace dfl {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// ---- GEMM (gemm_inst.hip) ----
+enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_T, EPI_RESADD, EPI_SWIGLU, EPI_QKV, EPI_KVINJECT, EPI_LMHEAD };
+
+struct GemmPlan {
+  int bm = 128, bn = 128, splits = 1;
+};
+// Choose tile/split for an M x N x K product (K multiple of the slab).
+GemmPlan plan_gemm(int dtype, int M, int N, int K, int num_cus);
+// Fill tiles/splits/partials fields of g and launch kernel (+ reduce when split).
+void launch_gemm(int dtype, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan,
+                 float* partials, size_t partials_elems, hipStream_t s);
+
+// ---- attention (attention.hip) ----
+void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, int n_kv, int splits, int target_wg,
+                      int item_cap, AttnPlan* plan, int4* items, int32_t* first_item, int32_t* n_items, int32_t* err,
+                      hipStream_t s);
+void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, dim3 grid, hipStream_t s);
+void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, hipStream_t s);
+
+// ---- elementwise / row kernels (kernels.hip) ----
+void launch_rope_table(float2* table, int n_pos, int d, double theta, hipStream_t s);
+void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int mask_id, int vocab, const void* embed,
+                       float scale, int H, float* X, const void* gain, void* h_out, float eps, int32_t* err,
+                       hipStream_t s);
+// out row o reads X row (map_mask ? (o / K) * R + 1 + o % K : o)
+void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, int K, int R, const void* gain,
+                    void* h_out, float eps, hipStream_t s);
+void launch_inject_scan(int n_req, const int32_t* slots, const int32_t* row_start, const int32_t* row_count,
+                        int32_t* ctx_len, int max_ctx, int max_batch, int64_t rows_upper, int32_t* req_off,
+                        int32_t* req_pos, int32_t* err, hipStream_t s);
+void launch_inject_fill(int n_req, int64_t rows_upper, const int32_t* slots, const int32_t* row_start,
+                        const int32_t* req_off, const int32_t* req_pos, int32_t* a_rows, int32_t* row_slot,
+                        int32_t* row_pos, hipStream_t s);
+void launch_rmsnorm_rows_f32in(int dtype, int n_rows, int H, const float* Y, const void* gain, void* g_out, float eps,
+                               hipStream_t s);
+void launch_row_finalize(int n_rows, int n_tiles, const float* tmax, const float* tsum, const int32_t* targ,
+                         float* row_max, float* row_lse, int32_t* argmax_out, float* out_row_max, float* out_row_lse,
+                         hipStream_t s);
+void launch_sample(int n_rows, int K, const int32_t* slots, uint64_t seed, uint64_t step, float inv_temp,
+                   const float* logits, int V, int n_tiles, const float* tmax, const float* tsum,
+                   const float* row_max, int32_t* draft_ids, hipStream_t s);
+void launch_topk(int n_rows, int V, int k, const float* logits, const float* tmax, int n_tiles, float inv_temp,
+                 const float* row_max, const float* row_lse, int32_t* ids_out, float* probs_out, hipStream_t s);
+void launch_tree(int n_req, int L, int Kc, int stride, int B, const float* probs, const int32_t* ids, const int32_t* anchors,
+                 int32_t* tokens, int32_t* parents, int32_t* depth, uint64_t* mask, hipStream_t s);
+void launch_verify_greedy(int n_req, int K, int V, const int32_t* draft_ids, const float* target, int32_t* post,
+                          int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, hipStream_t s);
+void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,
+                             const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
+                             uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
+                             int32_t* err, hipStream_t s);
+// out[i] = in[i] if in [0, max_batch) else max_batch (a spare empty slot), flagging the error word
+void launch_sanitize_slots(int n, const int32_t* in, int32_t* out, int max_batch, int32_t* err, hipStream_t s);
+void launch_synth_target(int n_req, int K, int V, const float* draft_logits, float sigma, uint64_t seed,
+                         uint64_t step, float* out, hipStream_t s);
+void launch_copy_cache(int dtype, const void* cache_k, const void* cache_vt, int layer, int slot, int start, int n,
+                       int max_batch, int n_kv, int d, int64_t ctx_alloc, void* k_out, void* v_out, hipStream_t s);
+void launch_reset_slots(int n, const int32_t* slots, int32_t* ctx_len, int max_batch, int32_t* err, hipStream_t s);
+void launch_philox_fill(int n, uint64_t seed, uint32_t slot, uint64_t step, uint32_t purpose, float* out,
+                        hipStream_t s);
+
+}  // namespace dfl

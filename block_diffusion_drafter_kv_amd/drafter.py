@@ -1,0 +1,171 @@
+"""Convenience wrapper holding one library handle and its borrowed torch tensors.
+
+PyTorch supplies device memory and the current HIP stream; all computation is
+done by the library's kernels through the C ABI.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import (DFLASH_BF16, DFLASH_F32, dflash_config, dflash_copy_cache, dflash_create, dflash_ctx_lens,
+               dflash_destroy, dflash_draft_block, dflash_draft_outputs, dflash_draft_params, dflash_get_error,
+               dflash_inject_context, dflash_layer_weights, dflash_reset_slots, dflash_select_from_logits,
+               dflash_verify, dflash_weights)
+
+_LAYER_KEYS = ("in_norm", "q_w", "k_w", "v_w", "o_w", "q_norm", "k_norm", "post_norm", "gate_w", "up_w", "down_w")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Drafter:
+    def __init__(self, model, weights: Dict, *, max_batch: int, max_ctx: int, max_k: int, max_inject_rows: int,
+                 max_top_k: int = 0, max_tree: int = 0, output_multiplier: float = 1.0, logit_softcap: float = 0.0):
+        self.model = model
+        self.dtype = torch.float32 if model.dtype == "f32" else torch.bfloat16
+        self._w = weights                       # keep the borrowed tensors alive
+        for k in ("embed", "lm_head", "fc", "hidden_norm", "final_norm"):
+            t = weights[k]
+            if not t.is_cuda or t.dtype != self.dtype or not t.is_contiguous():
+                raise ValueError(f"weight {k}: need a contiguous {self.dtype} CUDA tensor")
+        cfg = dflash_config()
+        cfg.dtype = DFLASH_F32 if model.dtype == "f32" else DFLASH_BF16
+        for f in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "vocab", "n_target_layers",
+                  "target_hidden", "mask_token_id"):
+            setattr(cfg, f, int(getattr(model, f)))
+        cfg.rms_eps = float(model.rms_eps)
+        cfg.rope_theta = float(model.rope_theta)
+        cfg.input_embedding_scale = float(model.input_embedding_scale)
+        cfg.output_multiplier = float(output_multiplier)
+        cfg.logit_softcap = float(logit_softcap)
+        cfg.max_batch, cfg.max_ctx, cfg.max_k = max_batch, max_ctx, max_k
+        cfg.max_inject_rows, cfg.max_top_k, cfg.max_tree = max_inject_rows, max_top_k, max_tree
+        self.cfg = cfg
+        layers = (dflash_layer_weights * model.n_layers)()
+        for l, lw in enumerate(weights["layers"]):
+            for k in _LAYER_KEYS:
+                t = lw[k]
+                if not t.is_cuda or t.dtype != self.dtype or not t.is_contiguous():
+                    raise ValueError(f"layer {l} weight {k}: need a contiguous {self.dtype} CUDA tensor")
+                setattr(layers[l], k, t.data_ptr())
+        self._layers = layers
+        w = dflash_weights()
+        w.embed, w.lm_head, w.fc = _ptr(weights["embed"]), _ptr(weights["lm_head"]), _ptr(weights["fc"])
+        w.hidden_norm, w.final_norm = _ptr(weights["hidden_norm"]), _ptr(weights["final_norm"])
+        w.n_layers = model.n_layers
+        w.layers = layers
+        self._wstruct = w
+        self.handle = dflash_create(cfg, w)
+
+    def close(self):
+        if self.handle is not None:
+            dflash_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- calls ----
+    def reset(self, slots: torch.Tensor):
+        dflash_reset_slots(self.handle, _stream(), slots.numel(), slots.data_ptr())
+
+    def inject(self, slots: torch.Tensor, row_start: torch.Tensor, row_count: torch.Tensor, rows_upper_bound: int,
+               hidden):
+        """hidden: [N, L_t, H_t] tensor, or a list of L_t tensors [N, H_t] sharing one row stride."""
+        tensors = [hidden] if isinstance(hidden, torch.Tensor) else list(hidden)
+        for t in tensors:
+            if not t.is_cuda or t.dtype != self.dtype:
+                raise ValueError(f"hidden states must be {self.dtype} CUDA tensors")
+        for t in (slots, row_start, row_count):
+            if not t.is_cuda or t.dtype != torch.int32:
+                raise ValueError("slots / row_start / row_count must be int32 CUDA tensors")
+        if isinstance(hidden, torch.Tensor):
+            n, lt, ht = hidden.shape
+            if not hidden.is_contiguous():
+                raise ValueError("hidden must be contiguous")
+            es = hidden.element_size()
+            ptrs = [hidden.data_ptr() + l * ht * es for l in range(lt)]
+            stride = lt * ht
+        else:
+            ptrs = [t.data_ptr() for t in hidden]
+            stride = hidden[0].stride(0)
+        dflash_inject_context(self.handle, _stream(), slots.numel(), slots.data_ptr(), row_start.data_ptr(),
+                              row_count.data_ptr(), int(rows_upper_bound), ptrs, stride)
+
+    def _outputs(self, n, K, top_k, tree_budget, logits, want_stats):
+        dev = torch.device("cuda")
+        o = {"draft_ids": torch.empty((n, K), dtype=torch.int32, device=dev)}
+        if top_k:
+            o["topk_ids"] = torch.empty((n, K, top_k), dtype=torch.int32, device=dev)
+            o["topk_probs"] = torch.empty((n, K, top_k), dtype=torch.float32, device=dev)
+        if want_stats:
+            o["row_max"] = torch.empty((n, K), dtype=torch.float32, device=dev)
+            o["row_lse"] = torch.empty((n, K), dtype=torch.float32, device=dev)
+        if logits is not None:
+            o["logits"] = logits
+        if tree_budget:
+            B = tree_budget
+            o["tree_tokens"] = torch.empty((n, B + 1), dtype=torch.int32, device=dev)
+            o["tree_parents"] = torch.empty((n, B + 1), dtype=torch.int32, device=dev)
+            o["tree_depth"] = torch.empty((n, B + 1), dtype=torch.int32, device=dev)
+            o["tree_mask"] = torch.empty((n, B + 1, (B + 64) // 64), dtype=torch.int64, device=dev)
+        s = dflash_draft_outputs()
+        for k, v in o.items():
+            setattr(s, k, v.data_ptr())
+        return o, s
+
+    def draft(self, slots, anchors, K, temperature=0.0, seed=0, step=0, top_k=0, tree_budget=0,
+              want_logits=False, logits_out: Optional[torch.Tensor] = None, want_stats=True):
+        n = slots.numel()
+        if want_logits and logits_out is None:
+            logits_out = torch.empty((n, K, self.model.vocab), dtype=torch.float32, device="cuda")
+        o, s = self._outputs(n, K, top_k, tree_budget, logits_out, want_stats)
+        p = dflash_draft_params(K, float(temperature), seed, step, top_k, tree_budget)
+        dflash_draft_block(self.handle, _stream(), n, slots.data_ptr(), anchors.data_ptr(), p, s)
+        return o
+
+    def select_from_logits(self, slots, anchors, logits, temperature=0.0, seed=0, step=0, top_k=0, tree_budget=0):
+        n, K, _ = logits.shape
+        o, s = self._outputs(n, K, top_k, tree_budget, None, True)
+        p = dflash_draft_params(K, float(temperature), seed, step, top_k, tree_budget)
+        dflash_select_from_logits(self.handle, _stream(), n, slots.data_ptr(),
+                                  anchors.data_ptr() if anchors is not None else None, logits.data_ptr(), p, s)
+        return o
+
+    def verify(self, slots, draft_ids, draft_logits, target_logits, temperature=0.0, seed=0, step=0):
+        n, K = draft_ids.shape
+        dev = torch.device("cuda")
+        out_tokens = torch.empty((n, K + 1), dtype=torch.int32, device=dev)
+        out_len = torch.empty((n,), dtype=torch.int32, device=dev)
+        accept_len = torch.empty((n,), dtype=torch.int32, device=dev)
+        dflash_verify(self.handle, _stream(), n, K, slots.data_ptr(), draft_ids.data_ptr(),
+                      _ptr(draft_logits), target_logits.data_ptr(), float(temperature), seed, step,
+                      out_tokens.data_ptr(), out_len.data_ptr(), accept_len.data_ptr())
+        return {"out_tokens": out_tokens, "out_len": out_len, "accept_len": accept_len}
+
+    # ---- inspection ----
+    def ctx_lens(self) -> torch.Tensor:
+        out = torch.empty(self.cfg.max_batch, dtype=torch.int32, device="cuda")
+        dflash_ctx_lens(self.handle, _stream(), out.data_ptr())
+        return out
+
+    def copy_cache(self, layer, slot, start, n):
+        m = self.model
+        k = torch.empty((n, m.n_kv_heads, m.head_dim), dtype=self.dtype, device="cuda")
+        v = torch.empty_like(k)
+        dflash_copy_cache(self.handle, _stream(), layer, slot, start, n, k.data_ptr(), v.data_ptr())
+        return k, v
+
+    def get_error(self) -> int:
+        return dflash_get_error(self.handle, _stream())

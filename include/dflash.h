@@ -1,0 +1,234 @@
+/*
+ * dflash.h -- C ABI of the MI355X (gfx950) DFlash drafter hot path.
+ *
+ * The library implements the three steps of block-diffusion speculative
+ * drafting with target-feature KV injection, as the following public pages
+ * describe them (cited by key throughout the sources):
+ *
+ *   [P1] "LLM的推理加速-DFlash" (wnma3mz.github.io blog)
+ *   [P2] "一次前向，白赚 4 个 token：DFlash 2 块扩散投机解码技术详解" (forceinjection.github.io)
+ *   [P3] "DFlash：块扩散 + KV 注入，让投机解码的草稿不再串行" (rainlin-top.pages.dev)
+ *   [P4] "【大模型】DFlash：把串行 Draft 变成并行“填空”" (developer.horizon.auto)
+ *   [P5] "DDTree 深度解析:从 Block Diffusion 到 Diffusion Draft Tree" (zhichai.net)
+ *
+ * Conventions shared by every call:
+ *  - Pointers documented "device" are HIP device memory (hipMalloc'ed or a
+ *    torch CUDA tensor's data_ptr()); "host" pointers are ordinary memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on `stream` and returns; none synchronises
+ *    except dflash_get_error and dflash_destroy.  Calls on one handle must be
+ *    ordered on one stream; a handle is not thread-safe.
+ *  - Host-side argument validation runs before anything is enqueued; on a
+ *    negative return value nothing was enqueued.
+ *  - Conditions only the device can see (a slot whose context would overflow,
+ *    an out-of-range slot or token id) never fault: the affected request is
+ *    skipped or clamped and a bit is OR-ed into the handle's sticky error
+ *    word, read (and cleared) by dflash_get_error.
+ *  - Weights are borrowed: the caller keeps them alive and unchanged for the
+ *    handle's lifetime.  The handle owns the drafter KV cache, the per-slot
+ *    context lengths and all scratch memory (allocated in dflash_create).
+ *  - Element type: every weight, the KV cache and GEMM operands use
+ *    cfg.dtype (fp32 or bf16); logits, probabilities and statistics are fp32;
+ *    token ids, lengths and tree indices are int32.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dflash_status {
+  DFLASH_OK = 0,
+  DFLASH_E_INVALID = -1,     /* bad argument (null pointer, size out of range)            */
+  DFLASH_E_NOMEM = -2,       /* device allocation failed in dflash_create                  */
+  DFLASH_E_CAPACITY = -3,    /* request exceeds a limit fixed in dflash_config             */
+  DFLASH_E_UNSUPPORTED = -4, /* shape the kernels do not handle (see dflash_create)        */
+  DFLASH_E_HIP = -5          /* a HIP runtime call failed                                  */
+};
+
+enum dflash_dtype { DFLASH_F32 = 0, DFLASH_BF16 = 1 };
+
+/* Device error word bits (dflash_get_error). */
+enum dflash_device_error {
+  DFLASH_DEV_CAPACITY = 1,   /* an injection would exceed max_ctx: that request's rows were skipped */
+  DFLASH_DEV_BAD_SLOT = 2,   /* a slot id outside [0, max_batch): that request was skipped          */
+  DFLASH_DEV_ROWS = 4,       /* row counts negative or above rows_upper_bound: rows skipped         */
+  DFLASH_DEV_BAD_TOKEN = 8   /* an anchor id outside [0, vocab): id 0 was embedded instead          */
+};
+
+/* Model shape, numerics and capacity, fixed at create time.
+ * Drafter: Qwen3-style decoder layers (GQA attention with per-head q/k
+ * RMSNorm and RoPE, SwiGLU MLP), fed by context K/V projected from the
+ * hidden states of n_target_layers target layers [P1 "关键创新"; P2 §2.2]. */
+typedef struct dflash_config {
+  int32_t dtype;              /* DFLASH_F32 or DFLASH_BF16                                      */
+  int32_t n_layers;           /* drafter decoder layers L_d (1..64)                             */
+  int32_t hidden;             /* H, multiple of 128                                              */
+  int32_t n_q_heads;          /* multiple of n_kv_heads                                           */
+  int32_t n_kv_heads;
+  int32_t head_dim;           /* d: 64 or 128                                                     */
+  int32_t ffn;                /* SwiGLU width F, multiple of 64                                   */
+  int32_t vocab;              /* V (shared embedding and LM head rows)                            */
+  int32_t n_target_layers;    /* L_t (1..8): hidden states concatenated in ascending layer order */
+  int32_t target_hidden;      /* H_t, multiple of 64                                              */
+  int32_t mask_token_id;      /* id embedded at the K mask positions [P2 §2.1; P4 §5.2]          */
+  float rms_eps;              /* RMSNorm epsilon (e.g. 1e-6)                                      */
+  float rope_theta;           /* RoPE base (rotate-half pairing (i, i + d/2))                     */
+  float input_embedding_scale;/* multiplies the shared embedding of the block [P2 §2.2]          */
+  float output_multiplier;    /* logits *= output_multiplier (1 = off) [P2 §2.2]                  */
+  float logit_softcap;        /* > 0: logits = c * tanh(logits / c); 0 = off [P2 §2.2]             */
+  int32_t max_batch;          /* number of request slots                                          */
+  int32_t max_ctx;            /* context positions per slot                                        */
+  int32_t max_k;              /* largest K (masks per block), 1..31                                */
+  int32_t max_inject_rows;    /* largest rows_upper_bound accepted by dflash_inject_context       */
+  int32_t max_top_k;          /* largest top_k of dflash_draft_block (0..256)                      */
+  int32_t max_tree;           /* largest tree_budget (0..256)                                      */
+} dflash_config;
+
+/* Per-layer weights, all [out_features, in_features] row-major, cfg.dtype. */
+typedef struct dflash_layer_weights {
+  const void* in_norm;        /* [H]          pre-attention RMSNorm gain          */
+  const void* q_w;            /* [n_q*d, H]                                       */
+  const void* k_w;            /* [n_kv*d, H]  used for block rows and context     */
+  const void* v_w;            /* [n_kv*d, H]  used for block rows and context     */
+  const void* o_w;            /* [H, n_q*d]                                       */
+  const void* q_norm;         /* [d]          per-head RMSNorm gain of q          */
+  const void* k_norm;         /* [d]          per-head RMSNorm gain of k          */
+  const void* post_norm;      /* [H]          pre-MLP RMSNorm gain                */
+  const void* gate_w;         /* [F, H]                                           */
+  const void* up_w;           /* [F, H]                                           */
+  const void* down_w;         /* [H, F]                                           */
+} dflash_layer_weights;
+
+typedef struct dflash_weights {
+  const void* embed;          /* [V, H] shared with the target [P1 "架构设计"]   */
+  const void* lm_head;        /* [V, H] shared with the target                   */
+  const void* fc;             /* [H, L_t*H_t] fusion of the target features      */
+  const void* hidden_norm;    /* [H] RMSNorm gain after fc                        */
+  const void* final_norm;     /* [H] RMSNorm gain before the LM head              */
+  int32_t n_layers;           /* must equal cfg.n_layers                          */
+  const dflash_layer_weights* layers; /* host array [n_layers] of device pointers */
+} dflash_weights;
+
+typedef struct dflash_handle dflash_handle;
+
+/* Create a handle: validates the shapes, allocates and zeroes the KV cache
+ * (n_layers x max_batch x n_kv_heads x max_ctx positions of K and V), the
+ * per-slot context lengths and the scratch memory.  Returns DFLASH_OK and
+ * *out, or a negative status (nothing allocated). */
+int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_handle** out);
+
+/* Synchronises the device and frees everything the handle owns. */
+int dflash_destroy(dflash_handle* h);
+
+/* Set the context length of the n slots in slots_dev (device int32[n]) to 0. */
+int dflash_reset_slots(dflash_handle* h, void* stream, int32_t n, const int32_t* slots_dev);
+
+/* Context injection [P1 "关键创新" Steps 1-3; P2 §2.2; P3 §四; P4 §5.1, §5.6].
+ * For request r (0 <= r < n_req) take row_count[r] rows starting at row
+ * row_start[r] of every target-layer buffer, concatenate the layers (ascending
+ * order of target_hidden[]), project with fc, RMSNorm (hidden_norm), then for
+ * every drafter layer project with k_w / v_w, RMSNorm each k head (k_norm),
+ * rotate k with RoPE at positions ctx_len[slot]..ctx_len[slot]+count-1, and
+ * write K and V into the slot's cache; ctx_len[slot] += count.
+ *   slots, row_start, row_count : device int32[n_req]; slots may repeat (rows append in order)
+ *   rows_upper_bound            : host bound >= sum(row_count), <= cfg.max_inject_rows
+ *   target_hidden               : host array [n_target_layers] of device pointers; layer l's
+ *                                 rows are target_hidden[l] + row * row_stride (elements)
+ *   row_stride                  : elements between rows (>= target_hidden, multiple of 8) */
+int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
+                          const int32_t* row_start, const int32_t* row_count, int64_t rows_upper_bound,
+                          const void* const* target_hidden, int64_t row_stride);
+
+/* Per-call parameters of a draft. */
+typedef struct dflash_draft_params {
+  int32_t K;                  /* masks per block, 1..max_k; the block has K+1 rows [P4 §4]   */
+  float temperature;          /* 0: greedy argmax; > 0: sample from softmax(z / T)           */
+  uint64_t seed;              /* Philox4x32-10 key                                           */
+  uint64_t step;              /* Philox counter word (low 32 bits used)                      */
+  int32_t top_k;              /* 0 or 1..max_top_k: report the top_k tokens per position     */
+  int32_t tree_budget;        /* 0 or 1..max_tree: build a best-first prefix tree [P5 §2.3]  */
+} dflash_draft_params;
+
+/* Outputs of a draft (device pointers; NULL where optional). */
+typedef struct dflash_draft_outputs {
+  int32_t* draft_ids;         /* [n_req, K] required: d_1..d_K                                  */
+  int32_t* topk_ids;          /* [n_req, K, top_k]   if top_k > 0: logit desc, ties lower id    */
+  float* topk_probs;          /* [n_req, K, top_k]   full-vocabulary softmax(z/T') probability  */
+  float* row_max;             /* [n_req, K] or NULL  max of z/T'                                 */
+  float* row_lse;             /* [n_req, K] or NULL  log sum exp(z/T' - row_max)                 */
+  float* logits;              /* [n_req, K, V] or NULL: z (after output_multiplier / softcap)    */
+  int32_t* tree_tokens;       /* [n_req, B+1] if tree_budget = B > 0; node 0 = anchor            */
+  int32_t* tree_parents;      /* [n_req, B+1] parent node index (-1 for the root / unused)       */
+  int32_t* tree_depth;        /* [n_req, B+1] depth (root 0; -1 unused)                           */
+  uint64_t* tree_mask;        /* [n_req, B+1, ceil((B+1)/64)] bit j of row i: i may attend to j  */
+} dflash_draft_outputs;
+/* T' = temperature if > 0, else 1.  A tree needs top_k >= min(B, V). */
+
+/* One drafter forward over the block [anchor | mask x K] of each request
+ * [P2 §2.1-2.2; P4 §4-4.4]: embedding x input_embedding_scale at positions
+ * C..C+K (C = ctx_len[slot]), n_layers decoder layers whose queries attend to
+ * the slot's context K/V plus the block's own K/V with no mask inside the
+ * block [P4 §5.3], final RMSNorm, LM head on the K mask rows, per-position
+ * softmax, top-k, draft tokens (argmax, or inverse-CDF sampling with
+ * u = Philox(seed; position j, slot, step, 0)), and optionally the prefix tree
+ * and its ancestor-only mask [P5 §2.3, §3.3].  Does not modify the cache.
+ *   slots, anchor_ids : device int32[n_req] (distinct slots in [0, max_batch)) */
+int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
+                       const int32_t* anchor_ids, const dflash_draft_params* params,
+                       const dflash_draft_outputs* out);
+
+/* The selection stage of dflash_draft_block alone, from caller logits
+ * [n_req, K, V] (device fp32): row statistics, top-k, draft tokens, tree. */
+int dflash_select_from_logits(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
+                              const int32_t* anchor_ids, const float* logits,
+                              const dflash_draft_params* params, const dflash_draft_outputs* out);
+
+/* Verification of one drafted block per request [P2 §2.3, §4.2; P1 "验证"].
+ * target_logits [n_req, K+1, V]: row j is the target's distribution after
+ * the anchor and d_1..d_j.  temperature 0: greedy prefix match, emitting
+ * d_1..d_a and the target's argmax of row a.  temperature > 0: rejection
+ * sampling against draft_logits [n_req, K, V] (row i-1 for d_i) with accept
+ * uniforms Philox(seed; i, slot, step, 1) and a residual / bonus draw with
+ * Philox(seed; a+1, slot, step, 2); an exhausted residual (mass < 2^-20)
+ * falls back to p.  Outputs (device): out_tokens [n_req, K+1] (unused -1),
+ * out_len [n_req] = a+1, accept_len [n_req] = a.  Does not touch the cache:
+ * inject the a+1 committed rows next (row_count = out_len on the device). */
+int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, const int32_t* slots,
+                  const int32_t* draft_ids, const float* draft_logits, const float* target_logits,
+                  float temperature, uint64_t seed, uint64_t step, int32_t* out_tokens, int32_t* out_len,
+                  int32_t* accept_len);
+
+/* Synchronise `stream`, return the sticky device error word in *code and clear it. */
+int dflash_get_error(dflash_handle* h, void* stream, int32_t* code);
+
+/* Human-readable name of a status code. */
+const char* dflash_status_str(int status);
+
+/* ---- inspection and benchmark helpers (not part of the drafting path) ---- */
+
+/* Copy ctx_len[0..max_batch) to device int32 buffer out_dev. */
+int dflash_ctx_lens(dflash_handle* h, void* stream, int32_t* out_dev);
+
+/* Copy cache positions [start, start+n) of (layer, slot) as K and V, each
+ * [n, n_kv_heads, head_dim] in cfg.dtype, to device buffers k_out / v_out. */
+int dflash_copy_cache(dflash_handle* h, void* stream, int32_t layer, int32_t slot, int32_t start, int32_t n,
+                      void* k_out, void* v_out);
+
+/* Synthetic target logits for benchmarks and tests (a stand-in for the target
+ * model): out[r, j] = draft_logits[r, j] + sigma * N(0,1) for j < K and
+ * out[r, K] = sigma * N(0,1), normals from Philox (purpose 3) + Box-Muller. */
+int dflash_synth_target_logits(void* stream, int32_t n_req, int32_t K, int32_t vocab, const float* draft_logits,
+                               float sigma, uint64_t seed, uint64_t step, float* out);
+
+/* out[i] = Philox uniform (seed; position i, slot, step, purpose), i < n (device fp32). */
+int dflash_philox_uniforms(void* stream, int32_t n, uint64_t seed, uint32_t slot, uint64_t step, uint32_t purpose,
+                           float* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

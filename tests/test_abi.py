@@ -1,0 +1,55 @@
+"""The C ABI library loads and exports every entry point include/dflash.h declares (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_diffusion_drafter_kv_amd as dk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared()
+    for n in ("dflash_inject_context", "dflash_draft_block", "dflash_verify", "dflash_create", "dflash_destroy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(dk.LIB_PATH):
+        pytest.skip("library not built")
+    lib = ctypes.CDLL(dk.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding wraps each of them under the same name
+    assert sorted(dk.EXPORTS) == _declared()
+    for n in _declared():
+        assert callable(getattr(dk, n))
+
+
+def test_status_strings_and_host_validation_without_gpu():
+    if not os.path.exists(dk.LIB_PATH):
+        pytest.skip("library not built")
+    dk.load()
+    assert dk.dflash_status_str(0) == "ok"
+    assert dk.dflash_status_str(-3) == "capacity exceeded"
+    # invalid configurations are rejected before any device work
+    cfg = dk.dflash_config()
+    w = dk.dflash_weights()
+    h = ctypes.c_void_p()
+    assert dk.load().dflash_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)) == -1
+    cfg.dtype, cfg.n_layers, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads = 1, 1, 256, 4, 2
+    cfg.head_dim, cfg.ffn, cfg.vocab, cfg.n_target_layers, cfg.target_hidden = 96, 512, 1024, 1, 256
+    cfg.mask_token_id, cfg.rms_eps, cfg.rope_theta = 1023, 1e-6, 1e4
+    cfg.max_batch, cfg.max_ctx, cfg.max_k, cfg.max_inject_rows = 1, 16, 4, 16
+    assert dk.load().dflash_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)) == -4   # head_dim 96
+    # null handle / null pointers
+    assert dk.load().dflash_verify(None, None, 1, 4, None, None, None, None, 0.0, 0, 0, None, None, None) == -1
+    assert dk.load().dflash_draft_block(None, None, 1, None, None, None, None) == -1
