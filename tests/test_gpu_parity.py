@@ -61,11 +61,12 @@ def test_inject_cache_parity(gpu_lib, cfg):
                 assert_close_report(k, kw, atol=2e-5, rtol=2e-5, what="K cache")
                 assert_close_report(v, vw, atol=2e-5, rtol=2e-5, what="V cache")
             else:
-                # within 2 bf16 ulp of the exact value (plus a small absolute floor)
-                ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(kw), 1e-30))) - 7)
-                assert np.all(np.abs(k - kw) <= 2 * ulp + 2e-3), "K cache beyond 2 bf16 ulp"
-                ulpv = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(vw), 1e-30))) - 7)
-                assert np.all(np.abs(v - vw) <= 2 * ulpv + 2e-3), "V cache beyond 2 bf16 ulp"
+                # bf16 path: the fused feature g is rounded to bf16 before the K/V product
+                # (relative 2^-9 per element), which leaves ~1.1e-3 RMS absolute error on a
+                # unit-RMS normalised k; the cache store adds at most half a bf16 ulp.
+                # Bound: 2^-8 relative + 1e-2 absolute (about 5 sigma of the former).
+                assert_close_report(k, kw, atol=1e-2, rtol=2.0 ** -8, what="K cache")
+                assert_close_report(v, vw, atol=1e-2, rtol=2.0 ** -8, what="V cache")
     dr.close()
 
 
