@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash drafter hot path on one MI355X.
+
+Workload (default "b32_ragged4k"): a 5-layer Qwen3-8B-shaped bf16 drafter
+(hidden 4096, 32/8 heads, SwiGLU 12288, vocab 151936, 5 x 4096 target
+features), batch 32 with ragged context lengths uniform in [512, 8192]
+(seed 7, mean ~4.3K), K = 16.  One step = the whole hot path over the batch:
+  dflash_inject_context (the out_len committed rows of every request),
+  dflash_draft_block (K+1 rows per request, greedy),
+  dflash_verify (greedy) against synthetic target logits
+  (drafter logits + sigma * N(0,1), generated between draft and verify by a
+  helper kernel that stands in for the target model and is not timed).
+Inputs are synthetic and seeded (weights N(0, 0.02^2) in bf16, target hidden
+states N(0, 1)), resident in HBM before timing starts.
+
+Prints one JSON line (see the keys below).  --gpus N > 1 is not supported: the
+path runs on one GPU (requests shard across GPUs with no exchange).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gpu_weights(cfg, seed):
+    """Seeded N(0, 0.02^2) bf16 weights generated on the GPU (gains 1)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    dt = torch.bfloat16
+    H, F, V = cfg.hidden, cfg.ffn, cfg.vocab
+
+    def n(*shape):
+        return (torch.randn(*shape, generator=g, device="cuda", dtype=torch.float32) * 0.02).to(dt)
+
+    ones = lambda k: torch.ones(k, device="cuda", dtype=dt)
+    w = {"embed": n(V, H), "lm_head": n(V, H), "fc": n(H, cfg.feat_dim), "hidden_norm": ones(H),
+         "final_norm": ones(H), "layers": []}
+    for _ in range(cfg.n_layers):
+        w["layers"].append({"in_norm": ones(H), "q_w": n(cfg.q_dim, H), "k_w": n(cfg.kv_dim, H),
+                            "v_w": n(cfg.kv_dim, H), "o_w": n(H, cfg.q_dim), "q_norm": ones(cfg.head_dim),
+                            "k_norm": ones(cfg.head_dim), "post_norm": ones(H), "gate_w": n(F, H),
+                            "up_w": n(F, H), "down_w": n(H, F)})
+    return w
+
+
+def phase_work(cfg, B, K, sum_ctx):
+    """Algorithmic flops / bytes per launch of each draft phase (one layer for per-layer phases)."""
+    R = K + 1
+    M = B * R
+    H, F, V = cfg.hidden, cfg.ffn, cfg.vocab
+    e = 2
+    per_layer_w = cfg.layer_params() * e
+    return {
+        "qkv": ("mfma", 2.0 * M * H * (cfg.q_dim + 2 * cfg.kv_dim)),
+        "o": ("mfma", 2.0 * M * cfg.q_dim * H),
+        "gate_up": ("mfma", 2.0 * M * H * 2 * F),
+        "down": ("mfma", 2.0 * M * F * H),
+        "lm_head": ("mfma", 2.0 * B * K * H * V),
+        # one launch reads every context K/V element of one layer once (+ the block's own K/V)
+        "attn": ("hbm", float((sum_ctx + B * R) * cfg.kv_dim * 2 * e)),
+        "_weights_bytes": ("hbm", float(per_layer_w * cfg.n_layers + V * H * e)),
+    }
+
+
+def cpu_baseline(cfg, K, ctx, sigma, seconds_budget=25.0):
+    """The oracle, as it stands, on the host: one request's step (inject 5 rows + draft + verify)."""
+    import numpy as np
+    import torch
+
+    from oracle import drafter as od
+    from oracle import verify as ov
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.time()
+    w = gpu_weights(cfg, seed=4321)
+    wc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in w.items() if k != "layers"}
+    wc["layers"] = [{k: v.cpu() for k, v in lw.items()} for lw in w["layers"]]
+    del w
+    torch.cuda.empty_cache()
+    orc = od.DrafterOracle(cfg, wc)
+    del wc
+    rng = np.random.default_rng(0)
+    # a context of `ctx` positions already materialised (random K/V, values do not affect timing)
+    orc.cache[0] = [[rng.standard_normal((ctx, cfg.n_kv_heads, cfg.head_dim)),
+                     rng.standard_normal((ctx, cfg.n_kv_heads, cfg.head_dim))] for _ in range(cfg.n_layers)]
+    setup = time.time() - t0
+    feats = rng.standard_normal((5, cfg.n_target_layers, cfg.target_hidden))
+    times = []
+    t_start = time.time()
+    while True:
+        t1 = time.perf_counter()
+        orc.inject(0, feats)
+        z = orc.block_logits(0, 7, K)
+        t = np.concatenate([z, np.zeros((1, cfg.vocab))]) + sigma * rng.standard_normal((K + 1, cfg.vocab))
+        ov.verify_greedy(z.argmax(axis=1), t)
+        times.append(time.perf_counter() - t1)
+        if time.time() - t_start > seconds_budget or len(times) >= 5:
+            break
+    per = statistics.median(times)
+    return {"value": K / per, "unit": "draft tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} step(s) of one request (ctx {ctx}: inject 5 rows + draft K={K} + greedy "
+                      f"verify) in fp64 NumPy; per-request throughput equals whole-batch throughput of a "
+                      f"sequential CPU run; setup {setup:.1f}s untimed",
+            "seconds_per_request_step": per,
+            "host_cpu": _cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b32_ragged4k")
+    ap.add_argument("--sigma", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the drafter hot path shards by request with no exchange "
+              "between GPUs; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_diffusion_drafter_kv_amd as dk
+    from synth.configs import get_workload
+
+    wl = get_workload(args.workload)
+    cfg = wl.model
+    B, K = wl.batch, wl.K
+    R = K + 1
+    sigma = wl.sigma if args.sigma is None else args.sigma
+    if wl.temperature != 0.0 or wl.tree_budget:
+        print(f"workload {wl.name} is a parity configuration; bench.py times the greedy hot path",
+              file=sys.stderr)
+    dk.load()
+    torch.cuda.set_device(0)
+    ctx = wl.ctx_lengths()
+    total_steps = args.warmup + args.steps + 1
+    max_ctx = max(ctx) + total_steps * R + 64
+    log(f"[bench] workload {wl.name}: B={B} K={K} ctx mean {np.mean(ctx):.0f} (sum {sum(ctx)}), sigma {sigma}")
+
+    t0 = time.time()
+    w = gpu_weights(cfg, seed=1234)
+    dr = dk.Drafter(cfg, w, max_batch=B, max_ctx=max_ctx, max_k=K, max_inject_rows=8192)
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    # prompt injection, untimed (one call per request, rows generated on the GPU)
+    for r, c in enumerate(ctx):
+        for s0 in range(0, c, 8192):
+            n = min(8192, c - s0)
+            rows = torch.randn((n, cfg.n_target_layers, cfg.target_hidden), generator=gen, device="cuda",
+                               dtype=torch.float32).to(torch.bfloat16)
+            dr.inject(i32([r]), i32([0]), i32([n]), n, rows)
+    torch.cuda.synchronize()
+    assert dr.get_error() == 0
+    log(f"[bench] setup (weights + {sum(ctx)} prompt rows injected) {time.time() - t0:.1f}s")
+
+    # per-step inputs: a pool of target hidden rows for the committed positions (N(0,1))
+    pool = torch.randn((B * R, cfg.n_target_layers, cfg.target_hidden), generator=gen, device="cuda",
+                       dtype=torch.float32).to(torch.bfloat16)
+    slots = i32(np.arange(B))
+    row_start = i32(np.arange(B) * R)
+    anchors = i32(np.random.default_rng(3).integers(0, cfg.vocab - 1, B))
+    out_len = i32(np.ones(B))           # the first step commits the anchor row of every request
+    logits = torch.empty((B, K, cfg.vocab), dtype=torch.float32, device="cuda")
+    target = torch.empty((B, R, cfg.vocab), dtype=torch.float32, device="cuda")
+    vout = {"out_tokens": torch.empty((B, R), dtype=torch.int32, device="cuda"), "out_len": out_len,
+            "accept_len": torch.empty((B,), dtype=torch.int32, device="cuda"),
+            "next_anchor": anchors}
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(i, marks=None):
+        e = [ev() for _ in range(6)] if marks is not None else None
+        if e: e[0].record(stream)
+        dr.inject(slots, row_start, vout["out_len"], B * R, pool)
+        if e: e[1].record(stream)
+        if e: e[2].record(stream)
+        o = dr.draft(slots, vout["next_anchor"], K, temperature=0.0, logits_out=logits, want_stats=False)
+        if e: e[3].record(stream)
+        dk.dflash_synth_target_logits(ctypes_stream(), B, K, cfg.vocab, logits.data_ptr(), sigma, 99, i,
+                                      target.data_ptr())
+        if e: e[4].record(stream)
+        dr.verify(slots, o["draft_ids"], None, target, temperature=0.0, out=vout)
+        if e: e[5].record(stream)
+        if marks is not None:
+            marks.append(e)
+
+    def ctypes_stream():
+        import ctypes
+        return ctypes.c_void_p(stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ctx_before = dr.ctx_lens()[:B].sum().item()
+
+    # phase breakdown (separate, untimed pass over 3 steps with per-phase events)
+    dr.profile(True)
+    for i in range(3):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    phases = dr.profile_read()
+    dr.profile(False)
+    ctx_before = dr.ctx_lens()[:B].sum().item()
+
+    # timed region
+    marks = []
+    accepted = []
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + 3 + i, marks)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ctx_after = dr.ctx_lens()[:B].sum().item()
+    assert dr.get_error() == 0
+    inj = [m[0].elapsed_time(m[1]) for m in marks]
+    dra = [m[2].elapsed_time(m[3]) for m in marks]
+    ver = [m[4].elapsed_time(m[5]) for m in marks]
+    per_step = [a + b + c for a, b, c in zip(inj, dra, ver)]
+    ms_step = statistics.mean(per_step)
+    mean_out_len = (ctx_after - ctx_before) / (B * args.steps)   # rows committed per request per step
+
+    # dominant kernel phase and its roofline
+    n_steps_prof = 3
+    sum_ctx_mid = (ctx_before + ctx_after) / 2.0
+    work = phase_work(cfg, B, K, sum_ctx_mid)
+    per_launch = {p: (ms / max(n, 1), n) for p, (ms, n) in phases.items() if n}
+    totals = {p: ms / n_steps_prof for p, (ms, n) in phases.items() if n}
+    dom = max((p for p in totals if p in work), key=lambda p: totals[p])
+    bound, amount = work[dom]
+    avg_ms = per_launch[dom][0]
+    if bound == "mfma":
+        achieved = amount / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_per_launch": amount, "avg_launch_ms": round(avg_ms, 4)}
+    else:
+        achieved = amount / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "algorithmic_per_launch": amount, "avg_launch_ms": round(avg_ms, 4)}
+
+    # whole-step HBM roofline of the draft (algorithmic bytes: weights once + context K/V once per layer)
+    draft_bytes = work["_weights_bytes"][1] + work["attn"][1] * cfg.n_layers
+    draft_ms = statistics.median(dra)
+    result = {
+        "metric": "draft tokens/s (5-layer, K=16, ctx 4K, B=32)",
+        "value": round(B * K / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02^2) bf16 weights, N(0,1) target features, "
+                "target logits = drafter logits + sigma*N(0,1))",
+        "config": {"workload": wl.name, "batch": B, "K": K, "ctx": "uniform[512,8192] seed 7",
+                   "mean_ctx_start": round(sum(ctx) / B, 1), "layers": cfg.n_layers, "hidden": cfg.hidden,
+                   "heads": f"{cfg.n_q_heads}/{cfg.n_kv_heads}x{cfg.head_dim}", "ffn": cfg.ffn,
+                   "vocab": cfg.vocab, "target_features": f"{cfg.n_target_layers}x{cfg.target_hidden}",
+                   "verify": "greedy", "sigma": sigma, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "draft_us_median": round(draft_ms * 1e3, 1),
+        "draft_only_tokens_per_s": round(B * K / (draft_ms * 1e-3), 1),
+        "draft_hbm_roofline_frac": round(draft_bytes / (draft_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "draft_algorithmic_bytes": draft_bytes,
+        "inject_us_median": round(statistics.median(inj) * 1e3, 1),
+        "verify_us_median": round(statistics.median(ver) * 1e3, 1),
+        "cycle_ms_wall_incl_synthetic_target": round(t_wall / args.steps * 1e3, 4),
+        "mean_committed_per_verify": round(mean_out_len, 3),
+        "phase_ms_per_step": {p: round(t, 4) for p, t in sorted(totals.items(), key=lambda x: -x[1])},
+    }
+    dr.close()
+    del w
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(cfg, K, ctx=4096, sigma=sigma)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

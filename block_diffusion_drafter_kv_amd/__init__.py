@@ -68,7 +68,9 @@ _SIGS = {
     "dflash_select_from_logits": ([c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                    POINTER(dflash_draft_params), POINTER(dflash_draft_outputs)], c_int32),
     "dflash_verify": ([c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
-                       c_uint64, c_uint64, c_void_p, c_void_p, c_void_p], c_int32),
+                       c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
+    "dflash_profile": ([c_void_p, c_int32], c_int32),
+    "dflash_profile_read": ([c_void_p, c_int32, POINTER(ctypes.c_double), POINTER(c_int32)], c_int32),
     "dflash_get_error": ([c_void_p, c_void_p, POINTER(c_int32)], c_int32),
     "dflash_status_str": ([c_int32], ctypes.c_char_p),
     "dflash_ctx_lens": ([c_void_p, c_void_p, c_void_p], c_int32),
@@ -138,9 +140,26 @@ def dflash_select_from_logits(h, stream, n_req, slots, anchors, logits, params, 
 
 
 def dflash_verify(h, stream, n_req, K, slots, draft_ids, draft_logits, target_logits, temperature, seed, step,
-                  out_tokens, out_len, accept_len):
+                  out_tokens, out_len, accept_len, next_anchor=None):
     return _call("dflash_verify", h, stream, n_req, K, slots, draft_ids, draft_logits, target_logits, temperature,
-                 seed, step, out_tokens, out_len, accept_len)
+                 seed, step, out_tokens, out_len, accept_len, next_anchor)
+
+
+PHASES = ("inject_prep", "inject_fc", "inject_norm", "inject_kv", "embed", "qkv", "attn", "attn_combine", "o",
+          "norm", "gate_up", "down", "lm_head", "select", "verify")
+
+
+def dflash_profile(h, enable: bool):
+    return _call("dflash_profile", h, 1 if enable else 0)
+
+
+def dflash_profile_read(h):
+    """Accumulated (ms, launches) per phase since the last read, as a dict keyed by phase name."""
+    n = len(PHASES)
+    ms = (ctypes.c_double * n)()
+    cnt = (c_int32 * n)()
+    _call("dflash_profile_read", h, n, ms, cnt)
+    return {p: (ms[i], cnt[i]) for i, p in enumerate(PHASES)}
 
 
 def dflash_get_error(h, stream) -> int:

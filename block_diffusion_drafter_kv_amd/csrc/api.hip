@@ -54,9 +54,45 @@ struct dflash_handle {
   int32_t* post = nullptr;
   float* vstats = nullptr;
   std::vector<void*> allocs;
+  // optional per-phase timing
+  struct Mark { int phase; hipEvent_t a, b; };
+  bool prof = false;
+  std::vector<Mark> marks;
+  std::vector<hipEvent_t> event_pool;
 };
 
 namespace {
+
+// Records a pair of HIP events around a group of launches when timing is enabled.
+struct Phase {
+  dflash_handle* h;
+  hipStream_t s;
+  int phase;
+  hipEvent_t a = nullptr;
+  static hipEvent_t take(dflash_handle* h) {
+    if (!h->event_pool.empty()) {
+      hipEvent_t e = h->event_pool.back();
+      h->event_pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    (void)hipEventCreate(&e);
+    return e;
+  }
+  Phase(dflash_handle* h_, hipStream_t s_, int ph) : h(h_), s(s_), phase(ph) {
+    if (h->prof) {
+      a = take(h);
+      (void)hipEventRecord(a, s);
+    }
+  }
+  ~Phase() {
+    if (h->prof) {
+      hipEvent_t b = take(h);
+      (void)hipEventRecord(b, s);
+      h->marks.push_back({phase, a, b});
+    }
+  }
+};
 
 int alloc(dflash_handle* h, void** p, size_t bytes) {
   if (bytes == 0) bytes = 256;
@@ -302,10 +338,13 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
   hipStream_t s = S(stream);
   const int dt = c.dtype;
   const int H = c.hidden, kvdim = c.n_kv_heads * c.head_dim;
-  launch_inject_scan(n_req, slots, row_start, row_count, h->ctx_len, c.max_ctx, c.max_batch, rows_upper_bound,
-                     h->req_off, h->req_pos, h->err, s);
-  launch_inject_fill(n_req, rows_upper_bound, slots, row_start, h->req_off, h->req_pos, h->a_rows, h->row_slot,
-                     h->row_pos, s);
+  {
+    Phase ph(h, s, DFLASH_PH_INJECT_PREP);
+    launch_inject_scan(n_req, slots, row_start, row_count, h->ctx_len, c.max_ctx, c.max_batch, rows_upper_bound,
+                       h->req_off, h->req_pos, h->err, s);
+    launch_inject_fill(n_req, rows_upper_bound, slots, row_start, h->req_off, h->req_pos, h->a_rows, h->row_slot,
+                       h->row_pos, s);
+  }
   const int featK = c.n_target_layers * c.target_hidden;
   for (int64_t c0 = 0; c0 < rows_upper_bound; c0 += h->inject_chunk) {
     const int rows = (int)std::min<int64_t>(h->inject_chunk, rows_upper_bound - c0);
@@ -322,9 +361,15 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
     ga.m_valid_base = (int)c0;
     set_b(ga, {{h->fc, H}}, featK);
     EpiStore<float>::Params pf{h->y, H};
-    launch_gemm(dt, EPI_STORE_F32, ga, &pf, plan_gemm(dt, rows, H, featK, h->num_cus), h->partials,
-                h->partials_elems, s);
-    launch_rmsnorm_rows_f32in(dt, rows, H, h->y, h->hidden_norm, h->g, c.rms_eps, s);
+    {
+      Phase ph(h, s, DFLASH_PH_INJECT_FC);
+      launch_gemm(dt, EPI_STORE_F32, ga, &pf, plan_gemm(dt, rows, H, featK, h->num_cus), h->partials,
+                  h->partials_elems, s);
+    }
+    {
+      Phase ph(h, s, DFLASH_PH_INJECT_NORM);
+      launch_rmsnorm_rows_f32in(dt, rows, H, h->y, h->hidden_norm, h->g, c.rms_eps, s);
+    }
     // per-layer K|V of the fused feature, up to 8 layers per product
     for (int l0 = 0; l0 < c.n_layers; l0 += MAX_BSEG / 2) {
       const int nl = std::min(MAX_BSEG / 2, c.n_layers - l0);
@@ -355,6 +400,7 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
       pk.eps = c.rms_eps;
       pk.layer0 = l0;
       // the parameter block has the same layout for fp32 (pointers only differ in type)
+      Phase ph(h, s, DFLASH_PH_INJECT_KV);
       launch_gemm(dt, EPI_KVINJECT, gk, &pk, plan_gemm(dt, rows, gk.N, H, h->num_cus), h->partials,
                   h->partials_elems, s);
     }
@@ -385,6 +431,7 @@ void select_stage(dflash_handle* h, hipStream_t s, int n_req, const int32_t* slo
   const int K = p->K, rows = n_req * K, V = c.vocab;
   const float T = p->temperature;
   const float inv_t = T > 0.f ? 1.0f / T : 1.0f;
+  Phase ph(h, s, DFLASH_PH_SELECT);
   launch_row_finalize(rows, h->n_vtiles, h->tmax, h->tsum, h->targ, h->row_max, h->row_lse,
                       T > 0.f ? nullptr : o->draft_ids, o->row_max, o->row_lse, s);
   if (T > 0.f)
@@ -433,10 +480,16 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   const int rows_split = gps * R;
   const int qrt = (rows_split + 15) / 16;
 
-  launch_embed_norm(dt, M, R, anchor_ids, c.mask_token_id, V, h->embed, c.input_embedding_scale, H, h->X,
-                    h->layers[0].in_norm, h->hbuf, c.rms_eps, h->err, s);
-  launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->target_wg, h->item_cap, h->plan, h->items,
-                   h->first_item, h->n_items, h->err, s);
+  {
+    Phase ph(h, s, DFLASH_PH_EMBED);
+    launch_embed_norm(dt, M, R, anchor_ids, c.mask_token_id, V, h->embed, c.input_embedding_scale, H, h->X,
+                      h->layers[0].in_norm, h->hbuf, c.rms_eps, h->err, s);
+  }
+  {
+    Phase ph(h, s, DFLASH_PH_ATTN);
+    launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->target_wg, h->item_cap, h->plan, h->items,
+                     h->first_item, h->n_items, h->err, s);
+  }
   const int64_t layer_cache = (int64_t)(c.max_batch + 1) * nkv * h->ctx_alloc * d * h->esize;
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& L = h->layers[l];
@@ -462,6 +515,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       pq.QRpad = h->QRpad;
       pq.Rpad = h->Rpad;
       pq.eps = c.rms_eps;
+      Phase ph(h, s, DFLASH_PH_QKV);
       launch_gemm(dt, EPI_QKV, ga, &pq, plan_gemm(dt, M, ga.N, H, h->num_cus), h->partials, h->partials_elems, s);
     }
     // attention over [context ; block]
@@ -488,7 +542,10 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       a.ctx_alloc = h->ctx_alloc;
       a.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
       const int gx = std::min(h->item_cap, n_req + h->target_wg / (nkv * splits) + 2);
-      launch_attn(dt, d, qrt, a, dim3(gx, nkv, splits), s);
+      {
+        Phase ph(h, s, DFLASH_PH_ATTN);
+        launch_attn(dt, d, qrt, a, dim3(gx, nkv, splits), s);
+      }
       AttnCombineArgs cb;
       cb.o_part = h->o_part;
       cb.m_part = h->m_part;
@@ -504,6 +561,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       cb.QRT16 = 16 * qrt;
       cb.q_dim = qdim;
       cb.D = d;
+      Phase ph(h, s, DFLASH_PH_ATTN_COMBINE);
       launch_attn_combine(dt, d, cb, dim3(n_req, nkv, splits), s);
     }
     // output projection + residual
@@ -511,9 +569,13 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       GemmArgs ga = gemm_a1(h->attn_out, qdim, M, H, qdim);
       set_b(ga, {{L.o_w, H}}, qdim);
       EpiResidualAdd::Params pr{h->X, H};
+      Phase ph(h, s, DFLASH_PH_O);
       launch_gemm(dt, EPI_RESADD, ga, &pr, plan_gemm(dt, M, H, qdim, h->num_cus), h->partials, h->partials_elems, s);
     }
-    launch_rmsnorm(dt, M, H, h->X, 0, K, R, L.post_norm, h->hbuf, c.rms_eps, s);
+    {
+      Phase ph(h, s, DFLASH_PH_NORM);
+      launch_rmsnorm(dt, M, H, h->X, 0, K, R, L.post_norm, h->hbuf, c.rms_eps, s);
+    }
     // SwiGLU MLP
     {
       GemmArgs ga = gemm_a1(h->hbuf, H, M, 2 * F, H);
@@ -522,19 +584,28 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       ga.b_interleave = 1;
       ga.b_ld = H;
       EpiSwiGLU<bf16_t>::Params ps{(bf16_t*)h->act, F, F};
-      launch_gemm(dt, EPI_SWIGLU, ga, &ps, plan_gemm(dt, M, 2 * F, H, h->num_cus), h->partials, h->partials_elems,
-                  s);
+      {
+        Phase ph(h, s, DFLASH_PH_GATE_UP);
+        launch_gemm(dt, EPI_SWIGLU, ga, &ps, plan_gemm(dt, M, 2 * F, H, h->num_cus), h->partials,
+                    h->partials_elems, s);
+      }
       GemmArgs gd = gemm_a1(h->act, F, M, H, F);
       set_b(gd, {{L.down_w, H}}, F);
       EpiResidualAdd::Params pr{h->X, H};
+      Phase ph(h, s, DFLASH_PH_DOWN);
       launch_gemm(dt, EPI_RESADD, gd, &pr, plan_gemm(dt, M, H, F, h->num_cus), h->partials, h->partials_elems, s);
     }
-    if (l + 1 < c.n_layers)
+    if (l + 1 < c.n_layers) {
+      Phase ph(h, s, DFLASH_PH_NORM);
       launch_rmsnorm(dt, M, H, h->X, 0, K, R, h->layers[l + 1].in_norm, h->hbuf, c.rms_eps, s);
+    }
   }
   // final norm on the K mask rows, LM head with streaming statistics
   const int rows = n_req * K;
-  launch_rmsnorm(dt, rows, H, h->X, 1, K, R, h->final_norm, h->hbuf, c.rms_eps, s);
+  {
+    Phase ph(h, s, DFLASH_PH_NORM);
+    launch_rmsnorm(dt, rows, H, h->X, 1, K, R, h->final_norm, h->hbuf, c.rms_eps, s);
+  }
   const float T = p->temperature;
   const bool need_logits = o->logits || T > 0.f || p->top_k > 0 || p->tree_budget > 0;
   float* logits = o->logits ? o->logits : (need_logits ? h->logits_ws : nullptr);
@@ -553,6 +624,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     pl.softcap = c.logit_softcap;
     GemmPlan gp = plan_gemm(dt, rows, V, H, h->num_cus);
     gp.splits = 1;   // statistics are per output tile: no split-K for the vocabulary product
+    Phase ph(h, s, DFLASH_PH_LM_HEAD);
     launch_gemm(dt, EPI_LMHEAD, ga, &pl, gp, h->partials, h->partials_elems, s);
   }
   select_stage(h, s, n_req, slots, anchor_ids, logits, p, o);
@@ -608,22 +680,52 @@ int dflash_select_from_logits(dflash_handle* h, void* stream, int32_t n_req, con
 
 int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, const int32_t* slots,
                   const int32_t* draft_ids, const float* draft_logits, const float* target_logits, float temperature,
-                  uint64_t seed, uint64_t step, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len) {
+                  uint64_t seed, uint64_t step, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
+                  int32_t* next_anchor) {
   if (!h || n_req < 0) return DFLASH_E_INVALID;
   if (n_req == 0) return DFLASH_OK;
   const dflash_config& c = h->cfg;
   if (n_req > c.max_batch || K < 1 || K > c.max_k) return DFLASH_E_CAPACITY;
   if (!draft_ids || !target_logits || !out_tokens || !out_len || !accept_len) return DFLASH_E_INVALID;
   if (!(temperature >= 0.f)) return DFLASH_E_INVALID;
+  if (temperature > 0.f && (!draft_logits || !slots)) return DFLASH_E_INVALID;
   hipStream_t s = S(stream);
+  Phase ph(h, s, DFLASH_PH_VERIFY);
   if (temperature == 0.f) {
-    launch_verify_greedy(n_req, K, c.vocab, draft_ids, target_logits, h->post, out_tokens, out_len, accept_len, s);
+    launch_verify_greedy(n_req, K, c.vocab, draft_ids, target_logits, h->post, out_tokens, out_len, accept_len,
+                         next_anchor, s);
   } else {
-    if (!draft_logits || !slots) return DFLASH_E_INVALID;
     launch_verify_rejection(n_req, K, c.vocab, slots, draft_ids, draft_logits, target_logits, 1.0f / temperature,
-                            seed, step, h->vstats, out_tokens, out_len, accept_len, h->err, s);
+                            seed, step, h->vstats, out_tokens, out_len, accept_len, next_anchor, h->err, s);
   }
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+int dflash_profile(dflash_handle* h, int32_t enable) {
+  if (!h) return DFLASH_E_INVALID;
+  h->prof = enable != 0;
+  return DFLASH_OK;
+}
+
+int dflash_profile_read(dflash_handle* h, int32_t n, double* ms, int32_t* launches) {
+  if (!h || n < 0) return DFLASH_E_INVALID;
+  std::vector<double> acc(DFLASH_PH_COUNT, 0.0);
+  std::vector<int32_t> cnt(DFLASH_PH_COUNT, 0);
+  int rc = DFLASH_OK;
+  for (auto& m : h->marks) {
+    float t = 0.f;
+    if (hipEventSynchronize(m.b) != hipSuccess || hipEventElapsedTime(&t, m.a, m.b) != hipSuccess) rc = DFLASH_E_HIP;
+    acc[m.phase] += t;
+    cnt[m.phase] += 1;
+    h->event_pool.push_back(m.a);
+    h->event_pool.push_back(m.b);
+  }
+  h->marks.clear();
+  for (int i = 0; i < n && i < DFLASH_PH_COUNT; ++i) {
+    if (ms) ms[i] = acc[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return rc;
 }
 
 int dflash_get_error(dflash_handle* h, void* stream, int32_t* code) {

@@ -581,7 +581,8 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(int V, const float* x,
 }
 
 __global__ void greedy_finish_kernel(int n_req, int K, const int32_t* draft_ids, const int32_t* post,
-                                     int32_t* out_tokens, int32_t* out_len, int32_t* accept_len) {
+                                     int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
+                                     int32_t* next_anchor) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= n_req) return;
   const int32_t* d = draft_ids + (int64_t)r * K;
@@ -594,6 +595,7 @@ __global__ void greedy_finish_kernel(int n_req, int K, const int32_t* draft_ids,
   for (int i = a + 1; i <= K; ++i) o[i] = -1;
   out_len[r] = a + 1;
   accept_len[r] = a;
+  if (next_anchor) next_anchor[r] = p[a];
 }
 
 // per row: (max of z/T, sum exp(z/T - max)); stats row q of request r = q / (2K+1):
@@ -629,7 +631,7 @@ __global__ __launch_bounds__(256) void rejection_kernel(int K, int V, const int3
                                                          const float* draft_logits, const float* target,
                                                          float inv_temp, uint64_t seed, uint64_t step,
                                                          const float* stats, int32_t* out_tokens, int32_t* out_len,
-                                                         int32_t* accept_len, int32_t* err) {
+                                                         int32_t* accept_len, int32_t* next_anchor, int32_t* err) {
   __shared__ float sh[8];
   __shared__ int s_a, s_stop;
   __shared__ float s_total;
@@ -719,6 +721,7 @@ __global__ __launch_bounds__(256) void rejection_kernel(int K, int V, const int3
     for (int i = a + 1; i <= K; ++i) o[i] = -1;
     out_len[r] = a + 1;
     accept_len[r] = a;
+    if (next_anchor) next_anchor[r] = pick;
   }
 }
 
@@ -854,19 +857,21 @@ void launch_tree(int n_req, int L, int Kc, int stride, int B, const float* probs
 }
 
 void launch_verify_greedy(int n_req, int K, int V, const int32_t* draft_ids, const float* target, int32_t* post,
-                          int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, hipStream_t s) {
+                          int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
+                          hipStream_t s) {
   argmax_rows_kernel<<<n_req * (K + 1), 256, 0, s>>>(V, target, post);
-  greedy_finish_kernel<<<cdiv(n_req, 64), 64, 0, s>>>(n_req, K, draft_ids, post, out_tokens, out_len, accept_len);
+  greedy_finish_kernel<<<cdiv(n_req, 64), 64, 0, s>>>(n_req, K, draft_ids, post, out_tokens, out_len, accept_len,
+                                                      next_anchor);
 }
 
 void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,
                              const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
                              uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
-                             int32_t* err, hipStream_t s) {
+                             int32_t* next_anchor, int32_t* err, hipStream_t s) {
   // stats rows per request: K+1 target rows then K draft rows
   softmax_stats_kernel<<<n_req * (2 * K + 1), 256, 0, s>>>(K, V, target, draft_logits, inv_temp, stats);
   rejection_kernel<<<n_req, 256, 0, s>>>(K, V, slots, draft_ids, draft_logits, target, inv_temp, seed, step, stats,
-                                          out_tokens, out_len, accept_len, err);
+                                          out_tokens, out_len, accept_len, next_anchor, err);
 }
 
 __global__ void sanitize_slots_kernel(int n, const int32_t* in, int32_t* out, int max_batch, int32_t* err) {

@@ -55,11 +55,12 @@ void launch_topk(int n_rows, int V, int k, const float* logits, const float* tma
 void launch_tree(int n_req, int L, int Kc, int stride, int B, const float* probs, const int32_t* ids, const int32_t* anchors,
                  int32_t* tokens, int32_t* parents, int32_t* depth, uint64_t* mask, hipStream_t s);
 void launch_verify_greedy(int n_req, int K, int V, const int32_t* draft_ids, const float* target, int32_t* post,
-                          int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, hipStream_t s);
+                          int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
+                          hipStream_t s);
 void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,
                              const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
                              uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
-                             int32_t* err, hipStream_t s);
+                             int32_t* next_anchor, int32_t* err, hipStream_t s);
 // out[i] = in[i] if in [0, max_batch) else max_batch (a spare empty slot), flagging the error word
 void launch_sanitize_slots(int n, const int32_t* in, int32_t* out, int max_batch, int32_t* err, hipStream_t s);
 void launch_synth_target(int n_req, int K, int V, const float* draft_logits, float sigma, uint64_t seed,

@@ -12,8 +12,8 @@ import torch
 
 from . import (DFLASH_BF16, DFLASH_F32, dflash_config, dflash_copy_cache, dflash_create, dflash_ctx_lens,
                dflash_destroy, dflash_draft_block, dflash_draft_outputs, dflash_draft_params, dflash_get_error,
-               dflash_inject_context, dflash_layer_weights, dflash_reset_slots, dflash_select_from_logits,
-               dflash_verify, dflash_weights)
+               dflash_inject_context, dflash_layer_weights, dflash_profile, dflash_profile_read, dflash_reset_slots,
+               dflash_select_from_logits, dflash_verify, dflash_weights)
 
 _LAYER_KEYS = ("in_norm", "q_w", "k_w", "v_w", "o_w", "q_norm", "k_norm", "post_norm", "gate_w", "up_w", "down_w")
 
@@ -143,16 +143,25 @@ class Drafter:
                                   anchors.data_ptr() if anchors is not None else None, logits.data_ptr(), p, s)
         return o
 
-    def verify(self, slots, draft_ids, draft_logits, target_logits, temperature=0.0, seed=0, step=0):
+    def verify(self, slots, draft_ids, draft_logits, target_logits, temperature=0.0, seed=0, step=0, out=None):
         n, K = draft_ids.shape
         dev = torch.device("cuda")
-        out_tokens = torch.empty((n, K + 1), dtype=torch.int32, device=dev)
-        out_len = torch.empty((n,), dtype=torch.int32, device=dev)
-        accept_len = torch.empty((n,), dtype=torch.int32, device=dev)
+        if out is None:
+            out = {"out_tokens": torch.empty((n, K + 1), dtype=torch.int32, device=dev),
+                   "out_len": torch.empty((n,), dtype=torch.int32, device=dev),
+                   "accept_len": torch.empty((n,), dtype=torch.int32, device=dev),
+                   "next_anchor": torch.empty((n,), dtype=torch.int32, device=dev)}
         dflash_verify(self.handle, _stream(), n, K, slots.data_ptr(), draft_ids.data_ptr(),
                       _ptr(draft_logits), target_logits.data_ptr(), float(temperature), seed, step,
-                      out_tokens.data_ptr(), out_len.data_ptr(), accept_len.data_ptr())
-        return {"out_tokens": out_tokens, "out_len": out_len, "accept_len": accept_len}
+                      out["out_tokens"].data_ptr(), out["out_len"].data_ptr(), out["accept_len"].data_ptr(),
+                      _ptr(out.get("next_anchor")))
+        return out
+
+    def profile(self, enable: bool = True):
+        dflash_profile(self.handle, enable)
+
+    def profile_read(self):
+        return dflash_profile_read(self.handle)
 
     # ---- inspection ----
     def ctx_lens(self) -> torch.Tensor:

@@ -200,7 +200,9 @@ int dflash_select_from_logits(dflash_handle* h, void* stream, int32_t n_req, con
 int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, const int32_t* slots,
                   const int32_t* draft_ids, const float* draft_logits, const float* target_logits,
                   float temperature, uint64_t seed, uint64_t step, int32_t* out_tokens, int32_t* out_len,
-                  int32_t* accept_len);
+                  int32_t* accept_len, int32_t* next_anchor);
+/* next_anchor [n_req] (device, or NULL) receives out_tokens[r][out_len[r]-1]: the
+ * token that anchors the next block [P4 §4.2; P1 "核心推理伪代码"]. */
 
 /* Synchronise `stream`, return the sticky device error word in *code and clear it. */
 int dflash_get_error(dflash_handle* h, void* stream, int32_t* code);
@@ -209,6 +211,31 @@ int dflash_get_error(dflash_handle* h, void* stream, int32_t* code);
 const char* dflash_status_str(int status);
 
 /* ---- inspection and benchmark helpers (not part of the drafting path) ---- */
+
+/* Per-phase timing: when enabled, HIP events are recorded on the call's
+ * stream around each group of kernels below; dflash_profile_read synchronises,
+ * writes the accumulated milliseconds and launch counts of the first n phases
+ * since the last read (host arrays, either may be NULL) and resets them. */
+enum dflash_phase {
+  DFLASH_PH_INJECT_PREP = 0, /* row tables                                  */
+  DFLASH_PH_INJECT_FC,       /* fc GEMM over the concatenated target layers */
+  DFLASH_PH_INJECT_NORM,     /* RMSNorm of the fused feature               */
+  DFLASH_PH_INJECT_KV,       /* per-layer K|V GEMM + k-norm/RoPE/cache store */
+  DFLASH_PH_EMBED,           /* block embedding + first RMSNorm             */
+  DFLASH_PH_QKV,             /* q|k|v GEMM + head norm + RoPE               */
+  DFLASH_PH_ATTN,            /* block attention kernel (plan included)      */
+  DFLASH_PH_ATTN_COMBINE,    /* merge of context chunks                     */
+  DFLASH_PH_O,               /* output projection + residual                */
+  DFLASH_PH_NORM,            /* RMSNorms between sub-layers                 */
+  DFLASH_PH_GATE_UP,         /* gate|up GEMM + SwiGLU                       */
+  DFLASH_PH_DOWN,            /* down GEMM + residual                        */
+  DFLASH_PH_LM_HEAD,         /* LM-head GEMM + tile statistics              */
+  DFLASH_PH_SELECT,          /* row statistics, sampling, top-k, tree       */
+  DFLASH_PH_VERIFY,          /* verification                                */
+  DFLASH_PH_COUNT
+};
+int dflash_profile(dflash_handle* h, int32_t enable);
+int dflash_profile_read(dflash_handle* h, int32_t n, double* ms, int32_t* launches);
 
 /* Copy ctx_len[0..max_batch) to device int32 buffer out_dev. */
 int dflash_ctx_lens(dflash_handle* h, void* stream, int32_t* out_dev);

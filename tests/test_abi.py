@@ -51,5 +51,7 @@ def test_status_strings_and_host_validation_without_gpu():
     cfg.max_batch, cfg.max_ctx, cfg.max_k, cfg.max_inject_rows = 1, 16, 4, 16
     assert dk.load().dflash_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)) == -4   # head_dim 96
     # null handle / null pointers
-    assert dk.load().dflash_verify(None, None, 1, 4, None, None, None, None, 0.0, 0, 0, None, None, None) == -1
+    assert dk.load().dflash_verify(None, None, 1, 4, None, None, None, None, 0.0, 0, 0, None, None, None,
+                                   None) == -1
+    assert dk.load().dflash_profile(None, 1) == -1
     assert dk.load().dflash_draft_block(None, None, 1, None, None, None, None) == -1
