@@ -562,7 +562,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       cb.q_dim = qdim;
       cb.D = d;
       Phase ph(h, s, DFLASH_PH_ATTN_COMBINE);
-      launch_attn_combine(dt, d, cb, dim3(n_req, nkv, splits), s);
+      launch_attn_combine(dt, d, cb, dim3(n_req, nkv * splits, (rows_split + 15) / 16), s);
     }
     // output projection + residual
     {

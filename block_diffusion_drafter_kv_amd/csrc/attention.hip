@@ -256,32 +256,49 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   }
 }
 
+// One work-group per (request, kv head and q-row half, block of 16 rows): each
+// thread owns one row and D/16 consecutive head dims and merges the request's
+// chunks in chunk order (max first, then the rescaled sums).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs a) {
-  const int req = blockIdx.x, kv = blockIdx.y, z = blockIdx.z;
+  constexpr int EPT = D / 16;
+  const int req = blockIdx.x;
+  const int kv = blockIdx.y / a.splits, z = blockIdx.y % a.splits;
+  const int row = blockIdx.z * 16 + (threadIdx.x >> 4);
+  const int e0 = (threadIdx.x & 15) * EPT;
+  if (row >= a.rows_per_split) return;
   const int f = a.first_item[req], n = a.n_items[req];
-  const int rows = a.rows_per_split;
-  const int gps = a.group / a.splits;
-  for (int idx = threadIdx.x; idx < rows * D; idx += 256) {
-    const int row = idx / D, e = idx % D;
-    float M = -INFINITY;
-    for (int c = 0; c < n; ++c) {
-      const int64_t b = ((int64_t)(f + c) * a.n_kv + kv) * a.splits + z;
-      M = fmaxf(M, a.m_part[b * a.QRT16 + row]);
+  const int64_t stride_item = (int64_t)a.n_kv * a.splits;         // partial blocks per item
+  const int64_t b0 = ((int64_t)f * a.n_kv + kv) * a.splits + z;
+  float M = -INFINITY;
+  for (int c = 0; c < n; ++c) M = fmaxf(M, a.m_part[(b0 + c * stride_item) * a.QRT16 + row]);
+  float L = 0.f;
+  float O[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) O[i] = 0.f;
+  for (int c = 0; c < n; ++c) {
+    const int64_t b = b0 + c * stride_item;
+    const float m = a.m_part[b * a.QRT16 + row];
+    if (m == -INFINITY) continue;
+    const float w = exp2f(m - M);
+    L += a.l_part[b * a.QRT16 + row] * w;
+    const float4* op = (const float4*)(a.o_part + (b * a.QRT16 + row) * D + e0);
+#pragma unroll
+    for (int i = 0; i < EPT / 4; ++i) {
+      const float4 v = op[i];
+      O[4 * i] += v.x * w;
+      O[4 * i + 1] += v.y * w;
+      O[4 * i + 2] += v.z * w;
+      O[4 * i + 3] += v.w * w;
     }
-    float L = 0.f, O = 0.f;
-    for (int c = 0; c < n; ++c) {
-      const int64_t b = ((int64_t)(f + c) * a.n_kv + kv) * a.splits + z;
-      const float m = a.m_part[b * a.QRT16 + row];
-      if (m == -INFINITY) continue;
-      const float w = exp2f(m - M);
-      L += a.l_part[b * a.QRT16 + row] * w;
-      O += a.o_part[(b * a.QRT16 + row) * D + e] * w;
-    }
-    const int gi = row / a.R, j = row % a.R;
-    const int qh = kv * a.group + z * gps + gi;
-    ((T*)a.out)[((int64_t)req * a.R + j) * a.q_dim + qh * D + e] = from_f32<T>(O / L);
   }
+  const float inv = 1.0f / L;
+  const int gps = a.group / a.splits;
+  const int gi = row / a.R, j = row % a.R;
+  const int qh = kv * a.group + z * gps + gi;
+  T* dst = (T*)a.out + ((int64_t)req * a.R + j) * a.q_dim + qh * D + e0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) dst[i] = from_f32<T>(O[i] * inv);
 }
 
 // ---------------------------------------------------------------------------

@@ -561,9 +561,36 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(int V, const float* x,
   const float* row = x + m * V;
   float best = -INFINITY;
   int arg = 0x7fffffff;
-  for (int c = threadIdx.x; c < V; c += 256) {
-    const float v = row[c];
-    if (v > best) { best = v; arg = c; }
+  if ((V & 3) == 0) {   // 16-byte loads, 4 in flight per thread; ids increase along each thread's walk
+    const float4* r4 = (const float4*)row;
+    const int V4 = V >> 2;
+    int c = threadIdx.x;
+    for (; c + 768 < V4; c += 1024) {
+      float4 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = r4[c + 256 * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int b = 4 * (c + 256 * u);
+        if (q[u].x > best) { best = q[u].x; arg = b; }
+        if (q[u].y > best) { best = q[u].y; arg = b + 1; }
+        if (q[u].z > best) { best = q[u].z; arg = b + 2; }
+        if (q[u].w > best) { best = q[u].w; arg = b + 3; }
+      }
+    }
+    for (; c < V4; c += 256) {
+      const float4 q = r4[c];
+      const int b = 4 * c;
+      if (q.x > best) { best = q.x; arg = b; }
+      if (q.y > best) { best = q.y; arg = b + 1; }
+      if (q.z > best) { best = q.z; arg = b + 2; }
+      if (q.w > best) { best = q.w; arg = b + 3; }
+    }
+  } else {
+    for (int c = threadIdx.x; c < V; c += 256) {
+      const float v = row[c];
+      if (v > best) { best = v; arg = c; }
+    }
   }
   const float M = wave_max(best);
   int cand = best == M ? arg : 0x7fffffff;
