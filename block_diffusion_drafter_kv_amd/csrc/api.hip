@@ -40,7 +40,7 @@ struct dflash_handle {
   float* partials = nullptr;
   size_t partials_elems = 0;
   // LM head
-  int n_vtiles = 0;
+  int n_vtiles = 0, lm_tile = 128;
   float *logits_ws = nullptr, *tmax = nullptr, *tsum = nullptr, *row_max = nullptr, *row_lse = nullptr;
   int32_t* targ = nullptr;
   int32_t* tk_ids = nullptr;
@@ -237,7 +237,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
   h->QRpad = ((g * R + 15) / 16) * 16 + 80;
   h->ctx_alloc = ((int64_t)(c.max_ctx + 63) / 64) * 64 + 64;
   h->item_cap = c.max_batch + h->target_wg / (nkv * splits) + 8;
-  h->n_vtiles = (c.vocab + 127) / 128;
+  h->lm_tile = gemm_bn(c.dtype);
+  h->n_vtiles = (c.vocab + h->lm_tile - 1) / h->lm_tile;
   h->inject_chunk = std::min(c.max_inject_rows, 16384);
 
   const size_t cache_elems = (size_t)c.n_layers * (c.max_batch + 1) * nkv * h->ctx_alloc * d;
@@ -267,7 +268,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc_t(h, &h->first_item, c.max_batch, 4))) break;
     if ((rc = alloc_t(h, &h->n_items, c.max_batch, 4))) break;
     if ((rc = alloc_t(h, &h->dslots, c.max_batch, 4))) break;
-    h->partials_elems = (size_t)(2 * h->num_cus + 8) * 128 * 128;
+    // split-K is used only while tiles * splits <= 2 * CUs: bounded by that many output tiles
+    h->partials_elems = (size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(c.dtype);
     if ((rc = alloc_t(h, &h->partials, h->partials_elems, 4))) break;
     const size_t lrows = (size_t)c.max_batch * c.max_k;
     if ((rc = alloc_t(h, &h->logits_ws, lrows * c.vocab, 4))) break;
@@ -348,6 +350,10 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
   const int featK = c.n_target_layers * c.target_hidden;
   for (int64_t c0 = 0; c0 < rows_upper_bound; c0 += h->inject_chunk) {
     const int rows = (int)std::min<int64_t>(h->inject_chunk, rows_upper_bound - c0);
+    // The true row count is on the device (row tiles past it exit at once).  A
+    // small bound is the per-step case, where usually only the first row tile is
+    // live: size the K split for that tile rather than for the bound.
+    const int plan_rows = rows <= 1024 ? std::min(rows, 64) : rows;
     // fc over the concatenated target layers
     GemmArgs ga = gemm_a1(nullptr, 0, rows, H, featK);
     for (int l = 0; l < c.n_target_layers; ++l) {
@@ -363,12 +369,12 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
     EpiStore<float>::Params pf{h->y, H};
     {
       Phase ph(h, s, DFLASH_PH_INJECT_FC);
-      launch_gemm(dt, EPI_STORE_F32, ga, &pf, plan_gemm(dt, rows, H, featK, h->num_cus), h->partials,
+      launch_gemm(dt, EPI_STORE_F32, ga, &pf, plan_gemm(dt, plan_rows, H, featK, h->num_cus), h->partials,
                   h->partials_elems, s);
     }
     {
       Phase ph(h, s, DFLASH_PH_INJECT_NORM);
-      launch_rmsnorm_rows_f32in(dt, rows, H, h->y, h->hidden_norm, h->g, c.rms_eps, s);
+      launch_rmsnorm(dt, rows, H, h->y, 0, 1, 1, h->hidden_norm, h->g, c.rms_eps, s, h->req_off + n_req, (int)c0);
     }
     // per-layer K|V of the fused feature, up to 8 layers per product
     for (int l0 = 0; l0 < c.n_layers; l0 += MAX_BSEG / 2) {
@@ -401,7 +407,7 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
       pk.layer0 = l0;
       // the parameter block has the same layout for fp32 (pointers only differ in type)
       Phase ph(h, s, DFLASH_PH_INJECT_KV);
-      launch_gemm(dt, EPI_KVINJECT, gk, &pk, plan_gemm(dt, rows, gk.N, H, h->num_cus), h->partials,
+      launch_gemm(dt, EPI_KVINJECT, gk, &pk, plan_gemm(dt, plan_rows, gk.N, H, h->num_cus), h->partials,
                   h->partials_elems, s);
     }
   }
@@ -435,20 +441,20 @@ void select_stage(dflash_handle* h, hipStream_t s, int n_req, const int32_t* slo
   launch_row_finalize(rows, h->n_vtiles, h->tmax, h->tsum, h->targ, h->row_max, h->row_lse,
                       T > 0.f ? nullptr : o->draft_ids, o->row_max, o->row_lse, s);
   if (T > 0.f)
-    launch_sample(rows, K, slots, p->seed, p->step, inv_t, logits, V, h->n_vtiles, h->tmax, h->tsum, h->row_max,
-                  o->draft_ids, s);
+    launch_sample(rows, K, slots, p->seed, p->step, inv_t, logits, V, h->n_vtiles, h->lm_tile, h->tmax, h->tsum,
+                  h->row_max, o->draft_ids, s);
   const int B = p->tree_budget;
   const int kc = B > 0 ? std::min(B, V) : 0;
   if (p->top_k > 0)
-    launch_topk(rows, V, p->top_k, logits, h->tmax, h->n_vtiles, inv_t, h->row_max, h->row_lse, o->topk_ids,
-                o->topk_probs, s);
+    launch_topk(rows, V, p->top_k, logits, h->tmax, h->n_vtiles, h->lm_tile, inv_t, h->row_max, h->row_lse,
+                o->topk_ids, o->topk_probs, s);
   if (B > 0) {
     const int32_t* ids = o->topk_ids;
     const float* probs = o->topk_probs;
     int stride = p->top_k;
     if (p->top_k < kc) {
-      launch_topk(rows, V, kc, logits, h->tmax, h->n_vtiles, inv_t, h->row_max, h->row_lse, h->tk_ids, h->tk_probs,
-                  s);
+      launch_topk(rows, V, kc, logits, h->tmax, h->n_vtiles, h->lm_tile, inv_t, h->row_max, h->row_lse, h->tk_ids,
+                  h->tk_probs, s);
       ids = h->tk_ids;
       probs = h->tk_probs;
       stride = kc;
@@ -622,8 +628,8 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     pl.inv_temp = T > 0.f ? 1.0f / T : 1.0f;
     pl.out_mult = c.output_multiplier;
     pl.softcap = c.logit_softcap;
-    GemmPlan gp = plan_gemm(dt, rows, V, H, h->num_cus);
-    gp.splits = 1;   // statistics are per output tile: no split-K for the vocabulary product
+    GemmPlan gp = plan_gemm(dt, rows, V, H, h->num_cus, /*wide=*/true);
+    gp.splits = 1;   // the vocabulary gives plenty of tiles; statistics are per output tile
     Phase ph(h, s, DFLASH_PH_LM_HEAD);
     launch_gemm(dt, EPI_LMHEAD, ga, &pl, gp, h->partials, h->partials_elems, s);
   }
@@ -631,15 +637,16 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
 
-__global__ void lm_stats_from_logits_kernel(int V, int n_tiles, const float* logits, float inv_temp, float* tmax,
-                                            float* tsum, int32_t* targ) {
-  // one wave per (row, 128-column tile): the same statistics the LM-head epilogue produces
+__global__ void lm_stats_from_logits_kernel(int V, int n_tiles, int tile_w, const float* logits, float inv_temp,
+                                            float* tmax, float* tsum, int32_t* targ) {
+  // one wave per (row, tile_w-column tile): the same statistics the LM-head epilogue produces
   const int m = blockIdx.y, t = blockIdx.x, lane = threadIdx.x;
+  const int per = tile_w / 64;
   float best = -INFINITY;
   int arg = 0x7fffffff;
-  float s[2];
-  for (int q = 0; q < 2; ++q) {
-    const int n = t * 128 + lane + 64 * q;
+  float s[4];
+  for (int q = 0; q < per; ++q) {
+    const int n = t * tile_w + lane + 64 * q;
     s[q] = -INFINITY;
     if (n < V) {
       s[q] = logits[(int64_t)m * V + n] * inv_temp;
@@ -650,8 +657,8 @@ __global__ void lm_stats_from_logits_kernel(int V, int n_tiles, const float* log
   int cand = best == mx ? arg : 0x7fffffff;
   for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o, 64));
   float e = 0.f;
-  for (int q = 0; q < 2; ++q)
-    if (t * 128 + lane + 64 * q < V) e += expf(s[q] - mx);
+  for (int q = 0; q < per; ++q)
+    if (t * tile_w + lane + 64 * q < V) e += expf(s[q] - mx);
   e = wave_sum(e);
   if (lane == 0) {
     tmax[(int64_t)m * n_tiles + t] = mx;
@@ -672,8 +679,11 @@ int dflash_select_from_logits(dflash_handle* h, void* stream, int32_t n_req, con
   const float T = p->temperature;
   const int rows = n_req * p->K;
   dim3 grid(h->n_vtiles, rows);
-  lm_stats_from_logits_kernel<<<grid, 64, 0, s>>>(h->cfg.vocab, h->n_vtiles, logits, T > 0.f ? 1.0f / T : 1.0f,
-                                                   h->tmax, h->tsum, h->targ);
+  {
+    Phase ph(h, s, DFLASH_PH_SELECT);
+    lm_stats_from_logits_kernel<<<grid, 64, 0, s>>>(h->cfg.vocab, h->n_vtiles, h->lm_tile, logits,
+                                                     T > 0.f ? 1.0f / T : 1.0f, h->tmax, h->tsum, h->targ);
+  }
   select_stage(h, s, n_req, slots, anchor_ids, logits, p, o);
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }

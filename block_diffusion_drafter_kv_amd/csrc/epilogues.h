@@ -1,5 +1,6 @@
-// GEMM epilogues.  Each receives a 64-row slab of the output tile staged in LDS
-// (fp32, row stride `ld`) and finishes the fused step that follows the product.
+// GEMM epilogues.  Each receives a slab of ROWS rows of the output tile staged
+// in LDS (fp32, row stride `ld`) and finishes the fused step that follows the
+// product.
 #pragma once
 #include "common.h"
 
@@ -11,9 +12,9 @@ __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x));
 template <typename OutT>
 struct EpiStore {
   struct Params { OutT* out; int64_t ld; };
-  template <int BN>
+  template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int, int tid) {
-    for (int idx = tid; idx < EPI_ROWS * BN; idx += 256) {
+    for (int idx = tid; idx < ROWS * BN; idx += 256) {
       const int r = idx / BN, c = idx % BN;
       const int m = m0 + r, n = n0 + c;
       if (m < M && n < N) p.out[(int64_t)m * p.ld + n] = from_f32<OutT>(st[r * ld + c]);
@@ -24,9 +25,9 @@ struct EpiStore {
 // ---- residual add into the fp32 stream ----
 struct EpiResidualAdd {
   struct Params { float* x; int64_t ld; };
-  template <int BN>
+  template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int, int tid) {
-    for (int idx = tid; idx < EPI_ROWS * BN; idx += 256) {
+    for (int idx = tid; idx < ROWS * BN; idx += 256) {
       const int r = idx / BN, c = idx % BN;
       const int m = m0 + r, n = n0 + c;
       if (m < M && n < N) p.x[(int64_t)m * p.ld + n] += st[r * ld + c];
@@ -38,10 +39,10 @@ struct EpiResidualAdd {
 template <typename OutT>
 struct EpiSwiGLU {
   struct Params { OutT* out; int64_t ld; int F; };
-  template <int BN>
+  template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
     constexpr int H = BN / 2;
-    for (int idx = tid; idx < EPI_ROWS * H; idx += 256) {
+    for (int idx = tid; idx < ROWS * H; idx += 256) {
       const int r = idx / H, c = idx % H;
       const int m = m0 + r, f = n0 / 2 + c;
       if (m < M && f < p.F) {
@@ -81,14 +82,14 @@ struct EpiQKV {
     int R, group, n_kv, d, q_dim, kv_dim, QRpad, Rpad;
     float eps;
   };
-  template <int BN>
+  template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
     const int lane = tid & 63, wave = tid >> 6;
     const int half = p.d / 2;
     const int per = 64 / half;  // items per wave iteration
     const int sub = lane / half, i = lane % half;
     const int heads = BN / p.d;
-    const int items = EPI_ROWS * heads;
+    const int items = ROWS * heads;
     for (int it = wave * per + sub; it < items; it += 4 * per) {
       const int r = it / heads, hh = it % heads;
       const int m = m0 + r;
@@ -136,7 +137,7 @@ struct EpiKVInject {
     float eps;
     int layer0;                                          // first layer of this product
   };
-  template <int BN>
+  template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
     const int lane = tid & 63, wave = tid >> 6;
     const int heads = BN / p.d;
@@ -149,7 +150,7 @@ struct EpiKVInject {
       if (!isv) {
         const int half = p.d / 2, per = 64 / half;
         const int sub = lane / half, i = lane % half;
-        for (int r = wave * per + sub; r < EPI_ROWS; r += 4 * per) {
+        for (int r = wave * per + sub; r < ROWS; r += 4 * per) {
           const int m = m0 + r;
           if (m >= M) continue;
           const int slot = p.row_slot[m];
@@ -157,14 +158,16 @@ struct EpiKVInject {
           const int pos = p.row_pos[m];
           float x1 = st[r * ld + hh * p.d + i], x2 = st[r * ld + hh * p.d + i + half];
           norm_rope_pair<T>(x1, x2, i, p.d, p.k_gain[layer], p.eps, p.rope + (int64_t)pos * half);
-          T* dst = p.cache_k + (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.ctx_alloc * p.d +
+          T* dst = p.cache_k +
+                   (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.ctx_alloc * p.d +
                    (int64_t)pos * p.d;
           dst[i] = from_f32<T>(x1);
           dst[i + half] = from_f32<T>(x2);
         }
       } else {
         // lanes walk rows (consecutive positions -> coalesced stores), waves walk columns
-        const int r = lane;
+        constexpr int RPL = 64 / ROWS;   // columns handled at once by one wave
+        const int r = lane % ROWS;
         const int m = m0 + r;
         int slot = -1, pos = 0;
         if (m < M) {
@@ -172,8 +175,10 @@ struct EpiKVInject {
           pos = p.row_pos[m];
         }
         if (slot >= 0) {
-          T* base = p.cache_vt + (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.d * p.ctx_alloc + pos;
-          for (int c = wave; c < p.d; c += 4) base[(int64_t)c * p.ctx_alloc] = from_f32<T>(st[r * ld + hh * p.d + c]);
+          T* base = p.cache_vt +
+                    (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.d * p.ctx_alloc + pos;
+          for (int c = wave * RPL + lane / ROWS; c < p.d; c += 4 * RPL)
+            base[(int64_t)c * p.ctx_alloc] = from_f32<T>(st[r * ld + hh * p.d + c]);
         }
       }
     }
@@ -191,11 +196,11 @@ struct EpiLMHead {
     int n_tiles;
     float inv_temp, out_mult, softcap;
   };
-  template <int BN>
+  template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int tn,
                                int tid) {
     const int lane = tid & 63, wave = tid >> 6;
-    for (int r = wave; r < EPI_ROWS; r += 4) {
+    for (int r = wave; r < ROWS; r += 4) {
       const int m = m0 + r;
       if (m >= M) break;
       float best = -INFINITY;

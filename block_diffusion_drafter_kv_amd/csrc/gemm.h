@@ -70,8 +70,8 @@ __device__ __forceinline__ const T* b_row_ptr(const GemmArgs& g, int n) {
   return (const T*)g.b_ptr[s] + (int64_t)(n - g.b_begin[s]) * g.b_ld;
 }
 
-// Stage accumulators of rows [pass*64, pass*64+64) of the tile into LDS (fp32, row stride BN+1).
-template <int BM, int BN>
+// Stage accumulators of rows [pass*ROWS, (pass+1)*ROWS) of the tile into LDS (fp32, row stride BN+1).
+template <int BM, int BN, int ROWS = EPI_ROWS>
 __device__ __forceinline__ void stage_acc(float* stage, const f32x4 (&acc)[BM / 32][BN / 32], int wm, int wn,
                                           int lane, int pass) {
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
@@ -80,12 +80,12 @@ __device__ __forceinline__ void stage_acc(float* stage, const f32x4 (&acc)[BM / 
 #pragma unroll
   for (int fi = 0; fi < FM; ++fi) {
     const int row0 = wm * WM + fi * 16;
-    if (row0 < pass * EPI_ROWS || row0 >= (pass + 1) * EPI_ROWS) continue;
+    if (row0 < pass * ROWS || row0 >= (pass + 1) * ROWS) continue;
 #pragma unroll
     for (int fj = 0; fj < FN; ++fj) {
       const int col = wn * WN + fj * 16 + r16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) stage[(row0 - pass * EPI_ROWS + g * 4 + i) * LD + col] = acc[fi][fj][i];
+      for (int i = 0; i < 4; ++i) stage[(row0 - pass * ROWS + g * 4 + i) * LD + col] = acc[fi][fj][i];
     }
   }
 }
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g, const typen
     if (m_base + pass * EPI_ROWS >= g.M) break;
     stage_acc<BM, BN>(stage, acc, wm, wn, lane, pass);
     __syncthreads();
-    Epi::template apply<BN>(ep, stage, BN + 1, m_base + pass * EPI_ROWS, n_base, g.M, g.N, tn, tid);
+    Epi::template apply<BN, EPI_ROWS>(ep, stage, BN + 1, m_base + pass * EPI_ROWS, n_base, g.M, g.N, tn, tid);
     __syncthreads();
   }
 }
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const GemmArgs g, cons
       stage[r * (BN + 1) + c] = s;
     }
     __syncthreads();
-    Epi::template apply<BN>(ep, stage, BN + 1, m0, n_base, g.M, g.N, tn, tid);
+    Epi::template apply<BN, EPI_ROWS>(ep, stage, BN + 1, m0, n_base, g.M, g.N, tn, tid);
     __syncthreads();
   }
 }

@@ -1,0 +1,190 @@
+// Pipelined bf16 MFMA GEMM for gfx950:  C[M, N] = A[M, K] . B[N, K]^T.
+//
+// Same operand addressing, split-K and LDS-staged epilogues as gemm.h, with a
+// deeper memory pipeline: K advances in 128-byte slabs that are copied from
+// global memory straight into a ring of STAGES LDS buffers with 16-byte
+// global_load_lds (no register staging).  Each thread issues its copies for
+// slab k + STAGES - 1 while the MFMAs run on slab k; a per-thread vmcnt wait
+// plus a workgroup barrier publishes a slab.  A raw s_barrier is used (not
+// __syncthreads, whose release fence would drain every outstanding copy).
+//
+// LDS layout of one buffer: A rows [0, BM) then B rows [0, BN), 8 chunks of 16
+// bytes per row with chunk c of row r stored at slot (c ^ (r & 7)); the copy
+// unit writes lane l of a wave to slot (wave base + l), so each lane fetches
+// the global chunk that belongs in its slot.
+#pragma once
+#include "gemm.h"
+
+namespace dfl {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
+
+// 16-byte global -> LDS copy: lane l of the wave lands at lds_wave_base + 16 * l.
+// Issued through inline asm so that the compiler's wait insertion does not treat
+// the copy as an LDS store aliasing every later LDS read (it would drain all
+// copies in flight); ordering is provided by the explicit vmcnt waits and
+// barriers of the ring loop, which contains no other vector-memory operation.
+__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  // M0 carries the LDS base; it is saved and restored around the copy (the
+  // compiler reserves M0), with the one wait state an M0 write needs before an
+  // LDS-DMA instruction reads it.
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(g)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that is also a compiler memory fence (no LDS access moves
+// across it) but, unlike __syncthreads, emits no wait on outstanding copies.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+static constexpr int GEMM2_EPI_ROWS = 32;   // epilogue slab: 32 rows x (BN+1) fp32 fit one ring buffer
+
+template <int BM, int BN, int STAGES, class Epi>
+__global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const typename Epi::Params ep) {
+  typedef bf16_t T;
+  constexpr int BK = 64;
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
+  constexpr int SLOTS = (BM + BN) * 8;
+  constexpr int NA = BM * 8 / 256, NB = BN * 8 / 256, NL = NA + NB;
+  constexpr int ER = GEMM2_EPI_ROWS;
+  static_assert(STAGES >= 2 && STAGES <= 4 && (STAGES - 2) * NL < 64, "stages / vmcnt range");
+  static_assert(ER * (BN + 1) * 4 <= STAGES * SLOTS * 16, "epilogue slab must fit the ring");
+
+  __shared__ uint4 smem[STAGES][SLOTS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int tm = logical % g.tiles_m, tn = logical / g.tiles_m;
+  const int split = blockIdx.y;
+  const int m_base = tm * BM, n_base = tn * BN;
+  if (g.m_valid && m_base >= *g.m_valid - g.m_valid_base) return;
+  const int k_begin = split * g.k_per_split;
+  const int k_end = min(g.K, k_begin + g.k_per_split);
+  const int nk = max(0, (k_end - k_begin) / BK);
+
+  // this thread's copy slots: rows (i*32 + tid/8) of A and B, logical chunk cchunk
+  const int crow = tid >> 3;
+  const int cchunk = (tid & 7) ^ (crow & 7);
+  int64_t a_src[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int m = m_base + i * 32 + crow;
+    int64_t s = 0;                      // rows outside the product read row 0 (discarded)
+    if (m < g.M) {
+      s = g.a_rows ? g.a_rows[m] : m;
+      if (s < 0) s = 0;
+    }
+    a_src[i] = s;
+  }
+  const T* b_src[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const T* p = b_row_ptr<T, BN>(g, n_base + j * 32 + crow);
+    b_src[j] = p ? p : (const T*)g.b_ptr[0];
+  }
+
+  auto issue = [&](int kt, uint4* dst) {
+    const int k0 = k_begin + kt * BK;
+    const int seg = k0 / g.a_segk;
+    const T* abase = (const T*)g.a_ptr[seg];
+    const int64_t ald = g.a_ld[seg];
+    const int kk = k0 - seg * g.a_segk + cchunk * 8;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) copy16_to_lds(abase + a_src[i] * ald + kk, dst + i * 256 + wave * 64);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) copy16_to_lds(b_src[j] + k0 + cchunk * 8, dst + (NA + j) * 256 + wave * 64);
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int grp = lane >> 4, r16 = lane & 15;
+  auto compute = [&](const uint4* buf) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 af[FM], bfr[FN];
+      const int c = s * 4 + grp;
+#pragma unroll
+      for (int fi = 0; fi < FM; ++fi) {
+        const int row = wm * WM + fi * 16 + r16;
+        *(uint4*)&af[fi] = buf[row * 8 + (c ^ (row & 7))];
+      }
+#pragma unroll
+      for (int fj = 0; fj < FN; ++fj) {
+        const int row = wn * WN + fj * 16 + r16;
+        *(uint4*)&bfr[fj] = buf[(BM + row) * 8 + (c ^ (row & 7))];
+      }
+#pragma unroll
+      for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < FN; ++fj) Frag<T>::mma(acc[fi][fj], af[fi], bfr[fj]);
+    }
+  };
+  // ring: slab kt lives in buffer kt % STAGES; up to STAGES - 1 slabs in flight
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nk) issue(p, smem[p]);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = min(STAGES - 2, nk - 1 - kt);   // slabs after kt allowed to stay in flight
+    if constexpr (STAGES == 4) {
+      if (ahead >= 2) wait_vmcnt<2 * NL>();
+      else if (ahead == 1) wait_vmcnt<NL>();
+      else wait_vmcnt<0>();
+    } else if constexpr (STAGES == 3) {
+      if (ahead >= 1) wait_vmcnt<NL>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, smem[(kt + STAGES - 1) % STAGES]);
+    compute(smem[kt % STAGES]);
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  if (g.splits > 1) {
+    float* P = g.partials + (int64_t)split * g.Mpad * g.Npad;
+#pragma unroll
+    for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < FN; ++fj) {
+        const int col = n_base + wn * WN + fj * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = m_base + wm * WM + fi * 16 + grp * 4 + i;
+          P[(int64_t)row * g.Npad + col] = acc[fi][fj][i];
+        }
+      }
+    return;
+  }
+
+  float* stage = (float*)&smem[0][0];
+#pragma unroll
+  for (int pass = 0; pass < BM / ER; ++pass) {
+    if (m_base + pass * ER >= g.M) break;
+    stage_acc<BM, BN, ER>(stage, acc, wm, wn, lane, pass);
+    __syncthreads();
+    Epi::template apply<BN, ER>(ep, stage, BN + 1, m_base + pass * ER, n_base, g.M, g.N, tn, tid);
+    __syncthreads();
+  }
+}
+
+}  // namespace dfl

@@ -3,20 +3,26 @@
 
 namespace dfl {
 
-void gemm_dispatch_bf16(EpiKind kind, int bm, const GemmArgs& g, const void* ep, hipStream_t s) {
-  gemm_dispatch_t<bf16_t>(kind, bm, g, ep, s);
+void gemm_dispatch_bf16(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s) {
+  gemm_dispatch_t<bf16_t>(kind, pl, g, ep, s);
 }
 
-GemmPlan plan_gemm(int dtype, int M, int N, int K, int num_cus) {
+GemmPlan plan_gemm(int dtype, int M, int N, int K, int num_cus, bool wide) {
   GemmPlan p;
   p.bm = M <= 64 ? 64 : 128;
-  p.bn = 128;
+  p.bn = (wide && dtype == DT_BF16) ? 256 : 128;
   const int bk = dtype == DT_BF16 ? 64 : 32;
   const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   const int kt = K / bk;
   int sp = 1;
-  // split K while the grid is below two waves of work-groups and each split keeps >= 8 slabs
-  while (tiles * sp * 2 <= 2L * num_cus && kt / (sp * 2) >= 8) sp *= 2;
+  // Split K for grids far below one work-group per CU (small-M, weight-streaming
+  // products), and in two for long products that leave CUs idle; otherwise the
+  // partial tiles and their reduction cost more than a partly idle grid (measured).
+  if (tiles * 2 < num_cus) {
+    while (tiles * sp * 2 <= 2L * num_cus && kt / (sp * 2) >= 8) sp *= 2;
+  } else if (tiles < num_cus && kt >= 192) {
+    sp = 2;
+  }
   p.splits = sp;
   return p;
 }
@@ -34,8 +40,8 @@ void launch_gemm(int dtype, EpiKind kind, GemmArgs g, const void* epi_params, co
   g.splits = splits;
   g.k_per_split = ((kt + splits - 1) / splits) * bk;
   g.partials = partials;
-  if (dtype == DT_BF16) gemm_dispatch_bf16(kind, plan.bm, g, epi_params, s);
-  else gemm_dispatch_f32(kind, plan.bm, g, epi_params, s);
+  if (dtype == DT_BF16) gemm_dispatch_bf16(kind, plan, g, epi_params, s);
+  else gemm_dispatch_f32(kind, plan, g, epi_params, s);
 }
 
 }  // namespace dfl

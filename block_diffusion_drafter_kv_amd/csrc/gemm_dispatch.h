@@ -1,37 +1,62 @@
-// Host-side dispatch of the GEMM kernel template over (epilogue, tile height).
+// Host-side dispatch of the GEMM kernel templates over (epilogue, tile shape).
+// bf16 products use the pipelined gemm2 kernel; fp32 products use the
+// register-staged kernel of gemm.h.  Tile shapes (measured on MI355X):
+//   bf16, M > 64 : 128 x 128, 2 LDS stages (64 KB: two work-groups per CU)
+//   bf16, M <= 64: 64 x 128, 3 stages
+//   bf16 LM head : 128 x 256 (or 64 x 256), 3 stages (fewer, wider tiles over the vocabulary)
+//   fp32         : 128 x 128 or 64 x 128
 #pragma once
+#include "gemm2.h"
 #include "ops.h"
 
 namespace dfl {
 
-template <typename T, int BM, class Epi>
-static void gemm_go(const GemmArgs& g, const void* ep, hipStream_t s) {
+template <int BM, int BN, int STAGES, class Epi>
+static void gemm2_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   const typename Epi::Params& p = *(const typename Epi::Params*)ep;
   dim3 grid(g.tiles_m * g.tiles_n, g.splits);
-  gemm_kernel<T, BM, 128, Epi><<<grid, 256, 0, s>>>(g, p);
+  gemm2_kernel<BM, BN, STAGES, Epi><<<grid, 256, 0, s>>>(g, p);
+  if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<g.tiles_m * g.tiles_n, 256, 0, s>>>(g, p);
+}
+
+template <int BM, class Epi>
+static void gemm1_go(const GemmArgs& g, const void* ep, hipStream_t s) {
+  const typename Epi::Params& p = *(const typename Epi::Params*)ep;
+  dim3 grid(g.tiles_m * g.tiles_n, g.splits);
+  gemm_kernel<float, BM, 128, Epi><<<grid, 256, 0, s>>>(g, p);
   if (g.splits > 1) gemm_reduce_kernel<BM, 128, Epi><<<g.tiles_m * g.tiles_n, 256, 0, s>>>(g, p);
 }
 
 template <typename T, class Epi>
-static void gemm_bm(int bm, const GemmArgs& g, const void* ep, hipStream_t s) {
-  if (bm == 64) gemm_go<T, 64, Epi>(g, ep, s);
-  else gemm_go<T, 128, Epi>(g, ep, s);
-}
-
-template <typename T>
-static void gemm_dispatch_t(EpiKind kind, int bm, const GemmArgs& g, const void* ep, hipStream_t s) {
-  switch (kind) {
-    case EPI_STORE_F32: gemm_bm<T, EpiStore<float>>(bm, g, ep, s); break;
-    case EPI_STORE_T: gemm_bm<T, EpiStore<T>>(bm, g, ep, s); break;
-    case EPI_RESADD: gemm_bm<T, EpiResidualAdd>(bm, g, ep, s); break;
-    case EPI_SWIGLU: gemm_bm<T, EpiSwiGLU<T>>(bm, g, ep, s); break;
-    case EPI_QKV: gemm_bm<T, EpiQKV<T>>(bm, g, ep, s); break;
-    case EPI_KVINJECT: gemm_bm<T, EpiKVInject<T>>(bm, g, ep, s); break;
-    case EPI_LMHEAD: gemm_bm<T, EpiLMHead>(bm, g, ep, s); break;
+static void gemm_cfg(const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (pl.bn == 256) {
+      if (pl.bm == 64) gemm2_go<64, 256, 3, Epi>(g, ep, s);
+      else gemm2_go<128, 256, 3, Epi>(g, ep, s);
+    } else {
+      if (pl.bm == 64) gemm2_go<64, 128, 3, Epi>(g, ep, s);
+      else gemm2_go<128, 128, 2, Epi>(g, ep, s);
+    }
+  } else {
+    if (pl.bm == 64) gemm1_go<64, Epi>(g, ep, s);
+    else gemm1_go<128, Epi>(g, ep, s);
   }
 }
 
-void gemm_dispatch_bf16(EpiKind kind, int bm, const GemmArgs& g, const void* ep, hipStream_t s);
-void gemm_dispatch_f32(EpiKind kind, int bm, const GemmArgs& g, const void* ep, hipStream_t s);
+template <typename T>
+static void gemm_dispatch_t(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s) {
+  switch (kind) {
+    case EPI_STORE_F32: gemm_cfg<T, EpiStore<float>>(pl, g, ep, s); break;
+    case EPI_STORE_T: gemm_cfg<T, EpiStore<T>>(pl, g, ep, s); break;
+    case EPI_RESADD: gemm_cfg<T, EpiResidualAdd>(pl, g, ep, s); break;
+    case EPI_SWIGLU: gemm_cfg<T, EpiSwiGLU<T>>(pl, g, ep, s); break;
+    case EPI_QKV: gemm_cfg<T, EpiQKV<T>>(pl, g, ep, s); break;
+    case EPI_KVINJECT: gemm_cfg<T, EpiKVInject<T>>(pl, g, ep, s); break;
+    case EPI_LMHEAD: gemm_cfg<T, EpiLMHead>(pl, g, ep, s); break;
+  }
+}
+
+void gemm_dispatch_bf16(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s);
+void gemm_dispatch_f32(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s);
 
 }  // namespace dfl

@@ -3,8 +3,8 @@
 
 namespace dfl {
 
-void gemm_dispatch_f32(EpiKind kind, int bm, const GemmArgs& g, const void* ep, hipStream_t s) {
-  gemm_dispatch_t<float>(kind, bm, g, ep, s);
+void gemm_dispatch_f32(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s) {
+  gemm_dispatch_t<float>(kind, pl, g, ep, s);
 }
 
 }  // namespace dfl

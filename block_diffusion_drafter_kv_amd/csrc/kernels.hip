@@ -59,18 +59,45 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* a
     h_out[(int64_t)m * H + c] = from_f32<T>(X[(int64_t)m * H + c] * rs * to_f32(gain[c]));
 }
 
+// Four values of one row, gain-scaled and stored as one 8- or 16-byte write.
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
+  bf16_t v[4] = {(bf16_t)a, (bf16_t)b, (bf16_t)c, (bf16_t)d};
+  *(uint2*)p = *(const uint2*)v;
+}
+__device__ __forceinline__ float4 load4f(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 load4f(const bf16_t* p) {
+  const uint2 u = *(const uint2*)p;
+  const bf16_t* v = (const bf16_t*)&u;
+  return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+
+// RMSNorm of fp32 rows, one wave per row (H a multiple of 4):
+// out[o] = x * rsqrt(mean(x^2) + eps) * gain, x = X row (map_mask ? (o / K) * R + 1 + o % K : o).
+// Rows at or past (*n_valid - valid_base) are skipped when n_valid is given.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(int H, const float* X, int map_mask, int K, int R,
-                                                       const T* gain, T* h_out, float eps) {
-  __shared__ float red[4];
-  const int o = blockIdx.x;
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int n_rows, int H, const float* X, int map_mask, int K, int R,
+                                                       const T* gain, T* h_out, float eps, const int32_t* n_valid,
+                                                       int valid_base) {
+  const int o = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (o >= n_rows) return;
+  if (n_valid && o >= *n_valid - valid_base) return;
   const int src = map_mask ? (o / K) * R + 1 + (o % K) : o;
   const float* x = X + (int64_t)src * H;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < H; c += 256) ss += x[c] * x[c];
-  ss = block_sum(ss, red);
+  for (int c = lane * 4; c < H; c += 256) {
+    const float4 v = load4f(x + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
   const float rs = rsqrtf(ss / (float)H + eps);
-  for (int c = threadIdx.x; c < H; c += 256) h_out[(int64_t)o * H + c] = from_f32<T>(x[c] * rs * to_f32(gain[c]));
+  T* y = h_out + (int64_t)o * H;
+  for (int c = lane * 4; c < H; c += 256) {
+    const float4 v = load4f(x + c), gn = load4f(gain + c);
+    store4(y + c, v.x * rs * gn.x, v.y * rs * gn.y, v.z * rs * gn.z, v.w * rs * gn.w);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -136,19 +163,6 @@ __global__ void inject_fill_kernel(int n_req, int64_t rows_upper, const int32_t*
   row_pos[m] = req_pos[lo] + i;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_f32in_kernel(int H, const float* Y, const T* gain, T* g_out,
-                                                             float eps) {
-  __shared__ float red[4];
-  const int64_t o = blockIdx.x;
-  const float* y = Y + o * H;
-  float ss = 0.f;
-  for (int c = threadIdx.x; c < H; c += 256) ss += y[c] * y[c];
-  ss = block_sum(ss, red);
-  const float rs = rsqrtf(ss / (float)H + eps);
-  for (int c = threadIdx.x; c < H; c += 256) g_out[o * H + c] = from_f32<T>(y[c] * rs * to_f32(gain[c]));
-}
-
 // ---------------------------------------------------------------------------
 // LM-head rows: merge tile statistics (fixed tile order).
 // row_max = max z/T, row_lse = log sum exp(z/T - row_max), argmax (lowest id on ties).
@@ -209,7 +223,7 @@ __device__ __forceinline__ float block_incl_scan(float v, float* sh) {
 
 __global__ __launch_bounds__(256) void sample_kernel(int K, const int32_t* slots, uint64_t seed, uint64_t step,
                                                       float inv_temp, const float* logits, int V, int n_tiles,
-                                                      const float* tmax, const float* tsum, const float* row_max,
+                                                      int tile_w, const float* tmax, const float* tsum, const float* row_max,
                                                       int32_t* draft_ids) {
   __shared__ float sh[8];
   __shared__ int s_thread;
@@ -270,29 +284,38 @@ __global__ __launch_bounds__(256) void sample_kernel(int K, const int32_t* slots
   }
   __syncthreads();
   if (threadIdx.x < 64) {
+    // inside the chosen tile: lane l owns ids [tile*tile_w + l*epl, +epl), scanned in id order
     const int lane = threadIdx.x;
     const int tile = s_tile;
+    const int epl = tile_w / 64;
     const float* z = logits + (int64_t)m * V;
-    const int c0 = tile * 128 + 2 * lane;
-    const float e0 = c0 < V ? expf(z[c0] * inv_temp - M) : 0.f;
-    const float e1 = c0 + 1 < V ? expf(z[c0 + 1] * inv_temp - M) : 0.f;
-    float x = e0 + e1;
+    const int c0 = tile * tile_w + lane * epl;
+    float e[4];
+    float lsum = 0.f;
+    for (int q = 0; q < epl; ++q) {
+      const int c = c0 + q;
+      e[q] = c < V ? expf(z[c] * inv_temp - M) : 0.f;
+      lsum += e[q];
+    }
+    float x = lsum;
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_up(x, o, 64);
       if (lane >= o) x += y;
     }
-    const float excl2 = s_before + (x - e0 - e1);
+    float acc = s_before + (x - lsum);
     const float tgt = target;
-    int pick = 0x7fffffff;
-    if (c0 < V && e0 > 0.f && tgt < excl2 + e0) pick = c0;
-    else if (c0 + 1 < V && e1 > 0.f && tgt < excl2 + e0 + e1) pick = c0 + 1;
+    int pick = 0x7fffffff, lastp = -1;
+    for (int q = 0; q < epl; ++q) {
+      if (e[q] > 0.f) {
+        if (pick == 0x7fffffff && tgt < acc + e[q]) pick = c0 + q;
+        lastp = c0 + q;
+      }
+      acc += e[q];
+    }
     for (int o = 32; o > 0; o >>= 1) pick = min(pick, __shfl_xor(pick, o, 64));
     if (pick == 0x7fffffff) {   // rounding: last id of the tile with weight
-      int lastp = -1;
-      if (c0 < V && e0 > 0.f) lastp = c0;
-      if (c0 + 1 < V && e1 > 0.f) lastp = c0 + 1;
       for (int o = 32; o > 0; o >>= 1) lastp = max(lastp, __shfl_xor(lastp, o, 64));
-      pick = lastp < 0 ? tile * 128 : lastp;
+      pick = lastp < 0 ? tile * tile_w : lastp;
     }
     if (lane == 0) draft_ids[m] = pick;
   }
@@ -348,7 +371,7 @@ __device__ uint64_t radix_kth(int n, int k, Get get, uint32_t* hist, uint64_t* s
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(int V, int k, const float* logits, const float* tmax, int n_tiles,
-                                                    float inv_temp, const float* row_max, const float* row_lse,
+                                                    int tile_w, float inv_temp, const float* row_max, const float* row_lse,
                                                     int32_t* ids_out, float* probs_out) {
   __shared__ uint32_t hist[256];
   __shared__ uint64_t sh_prefix;
@@ -371,8 +394,8 @@ __global__ __launch_bounds__(256) void topk_kernel(int V, int k, const float* lo
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     if (f2key(tm[t]) < thr) continue;
-    const int c = t * 128 + (threadIdx.x & 127);
-    if (threadIdx.x < 128 && c < V) {
+    const int c = t * tile_w + threadIdx.x;
+    if ((int)threadIdx.x < tile_w && c < V) {
       const float v = z[c] * inv_temp;
       if (f2key(v) >= thr) {
         const int slot = atomicAdd(&s_n, 1);
@@ -825,12 +848,15 @@ void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int
 }
 
 void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, int K, int R, const void* gain,
-                    void* h_out, float eps, hipStream_t s) {
+                    void* h_out, float eps, hipStream_t s, const int32_t* n_valid, int valid_base) {
   if (n_rows <= 0) return;
+  const int grid = cdiv(n_rows, 4);
   if (dtype == DT_BF16)
-    rmsnorm_kernel<bf16_t><<<n_rows, 256, 0, s>>>(H, X, map_mask, K, R, (const bf16_t*)gain, (bf16_t*)h_out, eps);
+    rmsnorm_kernel<bf16_t><<<grid, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, (const bf16_t*)gain, (bf16_t*)h_out,
+                                                 eps, n_valid, valid_base);
   else
-    rmsnorm_kernel<float><<<n_rows, 256, 0, s>>>(H, X, map_mask, K, R, (const float*)gain, (float*)h_out, eps);
+    rmsnorm_kernel<float><<<grid, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, (const float*)gain, (float*)h_out, eps,
+                                                n_valid, valid_base);
 }
 
 void launch_inject_scan(int n_req, const int32_t* slots, const int32_t* row_start, const int32_t* row_count,
@@ -849,15 +875,6 @@ void launch_inject_fill(int n_req, int64_t rows_upper, const int32_t* slots, con
                                                            a_rows, row_slot, row_pos);
 }
 
-void launch_rmsnorm_rows_f32in(int dtype, int n_rows, int H, const float* Y, const void* gain, void* g_out, float eps,
-                               hipStream_t s) {
-  if (n_rows <= 0) return;
-  if (dtype == DT_BF16)
-    rmsnorm_f32in_kernel<bf16_t><<<n_rows, 256, 0, s>>>(H, Y, (const bf16_t*)gain, (bf16_t*)g_out, eps);
-  else
-    rmsnorm_f32in_kernel<float><<<n_rows, 256, 0, s>>>(H, Y, (const float*)gain, (float*)g_out, eps);
-}
-
 void launch_row_finalize(int n_rows, int n_tiles, const float* tmax, const float* tsum, const int32_t* targ,
                          float* row_max, float* row_lse, int32_t* argmax_out, float* out_row_max, float* out_row_lse,
                          hipStream_t s) {
@@ -866,15 +883,17 @@ void launch_row_finalize(int n_rows, int n_tiles, const float* tmax, const float
 }
 
 void launch_sample(int n_rows, int K, const int32_t* slots, uint64_t seed, uint64_t step, float inv_temp,
-                   const float* logits, int V, int n_tiles, const float* tmax, const float* tsum,
+                   const float* logits, int V, int n_tiles, int tile_w, const float* tmax, const float* tsum,
                    const float* row_max, int32_t* draft_ids, hipStream_t s) {
-  sample_kernel<<<n_rows, 256, 0, s>>>(K, slots, seed, step, inv_temp, logits, V, n_tiles, tmax, tsum, row_max,
-                                        draft_ids);
+  sample_kernel<<<n_rows, 256, 0, s>>>(K, slots, seed, step, inv_temp, logits, V, n_tiles, tile_w, tmax, tsum,
+                                        row_max, draft_ids);
 }
 
-void launch_topk(int n_rows, int V, int k, const float* logits, const float* tmax, int n_tiles, float inv_temp,
-                 const float* row_max, const float* row_lse, int32_t* ids_out, float* probs_out, hipStream_t s) {
-  topk_kernel<<<n_rows, 256, 0, s>>>(V, k, logits, tmax, n_tiles, inv_temp, row_max, row_lse, ids_out, probs_out);
+void launch_topk(int n_rows, int V, int k, const float* logits, const float* tmax, int n_tiles, int tile_w,
+                 float inv_temp, const float* row_max, const float* row_lse, int32_t* ids_out, float* probs_out,
+                 hipStream_t s) {
+  topk_kernel<<<n_rows, 256, 0, s>>>(V, k, logits, tmax, n_tiles, tile_w, inv_temp, row_max, row_lse, ids_out,
+                                      probs_out);
 }
 
 void launch_tree(int n_req, int L, int Kc, int stride, int B, const float* probs, const int32_t* ids,

@@ -15,8 +15,12 @@ enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_T, EPI_RESADD, EPI_SWIGLU, EPI_QKV, 
 struct GemmPlan {
   int bm = 128, bn = 128, splits = 1;
 };
-// Choose tile/split for an M x N x K product (K multiple of the slab).
-GemmPlan plan_gemm(int dtype, int M, int N, int K, int num_cus);
+// widest output tile of the GEMM kernels; the LM head uses it, so it is also the
+// column width of the LM-head statistics tiles
+inline int gemm_bn(int dtype) { return dtype == DT_BF16 ? 256 : 128; }
+// Choose tile/split for an M x N x K product (K multiple of the slab); wide = the
+// vocabulary product (widest tiles).
+GemmPlan plan_gemm(int dtype, int M, int N, int K, int num_cus, bool wide = false);
 // Fill tiles/splits/partials fields of g and launch kernel (+ reduce when split).
 void launch_gemm(int dtype, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan,
                  float* partials, size_t partials_elems, hipStream_t s);
@@ -33,25 +37,26 @@ void launch_rope_table(float2* table, int n_pos, int d, double theta, hipStream_
 void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int mask_id, int vocab, const void* embed,
                        float scale, int H, float* X, const void* gain, void* h_out, float eps, int32_t* err,
                        hipStream_t s);
-// out row o reads X row (map_mask ? (o / K) * R + 1 + o % K : o)
+// out row o reads X row (map_mask ? (o / K) * R + 1 + o % K : o); rows at or past
+// (*n_valid - valid_base) are skipped when n_valid is given (device-side row count)
 void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, int K, int R, const void* gain,
-                    void* h_out, float eps, hipStream_t s);
+                    void* h_out, float eps, hipStream_t s, const int32_t* n_valid = nullptr, int valid_base = 0);
 void launch_inject_scan(int n_req, const int32_t* slots, const int32_t* row_start, const int32_t* row_count,
                         int32_t* ctx_len, int max_ctx, int max_batch, int64_t rows_upper, int32_t* req_off,
                         int32_t* req_pos, int32_t* err, hipStream_t s);
 void launch_inject_fill(int n_req, int64_t rows_upper, const int32_t* slots, const int32_t* row_start,
                         const int32_t* req_off, const int32_t* req_pos, int32_t* a_rows, int32_t* row_slot,
                         int32_t* row_pos, hipStream_t s);
-void launch_rmsnorm_rows_f32in(int dtype, int n_rows, int H, const float* Y, const void* gain, void* g_out, float eps,
-                               hipStream_t s);
 void launch_row_finalize(int n_rows, int n_tiles, const float* tmax, const float* tsum, const int32_t* targ,
                          float* row_max, float* row_lse, int32_t* argmax_out, float* out_row_max, float* out_row_lse,
                          hipStream_t s);
+// tile_w: column width of the LM-head statistics tiles (the GEMM's BN)
 void launch_sample(int n_rows, int K, const int32_t* slots, uint64_t seed, uint64_t step, float inv_temp,
-                   const float* logits, int V, int n_tiles, const float* tmax, const float* tsum,
+                   const float* logits, int V, int n_tiles, int tile_w, const float* tmax, const float* tsum,
                    const float* row_max, int32_t* draft_ids, hipStream_t s);
-void launch_topk(int n_rows, int V, int k, const float* logits, const float* tmax, int n_tiles, float inv_temp,
-                 const float* row_max, const float* row_lse, int32_t* ids_out, float* probs_out, hipStream_t s);
+void launch_topk(int n_rows, int V, int k, const float* logits, const float* tmax, int n_tiles, int tile_w,
+                 float inv_temp, const float* row_max, const float* row_lse, int32_t* ids_out, float* probs_out,
+                 hipStream_t s);
 void launch_tree(int n_req, int L, int Kc, int stride, int B, const float* probs, const int32_t* ids, const int32_t* anchors,
                  int32_t* tokens, int32_t* parents, int32_t* depth, uint64_t* mask, hipStream_t s);
 void launch_verify_greedy(int n_req, int K, int V, const int32_t* draft_ids, const float* target, int32_t* post,
