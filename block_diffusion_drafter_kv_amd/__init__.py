@@ -146,7 +146,7 @@ def dflash_verify(h, stream, n_req, K, slots, draft_ids, draft_logits, target_lo
 
 
 PHASES = ("inject_prep", "inject_fc", "inject_norm", "inject_kv", "embed", "qkv", "attn", "attn_combine", "o",
-          "norm", "gate_up", "down", "lm_head", "select", "verify")
+          "norm", "gate_up", "down", "lm_head", "select", "verify", "attn_plan")
 
 
 def dflash_profile(h, enable: bool):

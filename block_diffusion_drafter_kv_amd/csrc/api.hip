@@ -22,7 +22,7 @@ struct dflash_handle {
   const void** d_k_gains = nullptr;       // device array of per-layer k_norm pointers
   // cache and state
   void* cache_k = nullptr;
-  void* cache_vt = nullptr;
+  void* cache_v = nullptr;
   int64_t ctx_alloc = 0;
   int32_t* ctx_len = nullptr;
   int32_t* err = nullptr;
@@ -31,7 +31,7 @@ struct dflash_handle {
   // draft scratch
   int maxM = 0, Rpad = 0, QRpad = 0, attn_splits = 1, item_cap = 0, target_wg = 1024, qrt_max = 5;
   float* X = nullptr;
-  void *hbuf = nullptr, *attn_out = nullptr, *act = nullptr, *qb = nullptr, *kb = nullptr, *vbt = nullptr;
+  void *hbuf = nullptr, *attn_out = nullptr, *act = nullptr, *qb = nullptr, *kb = nullptr, *vb = nullptr;
   float *o_part = nullptr, *m_part = nullptr, *l_part = nullptr;
   AttnPlan* plan = nullptr;
   int4* items = nullptr;
@@ -208,7 +208,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
         !L.gate_w || !L.up_w || !L.down_w)
       return DFLASH_E_INVALID;
   }
-  const int qrt_cap = (c.dtype == DFLASH_F32 && c.head_dim == 128) ? 3 : 5;
+  const int qrt_cap = 5;  // attention work-groups hold at most 5 tiles of 16 query rows
   const int splits = choose_attn_splits(c, qrt_cap);
   if (splits < 0) return DFLASH_E_UNSUPPORTED;
 
@@ -244,7 +244,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
   const size_t cache_elems = (size_t)c.n_layers * (c.max_batch + 1) * nkv * h->ctx_alloc * d;
   do {
     if ((rc = alloc(h, &h->cache_k, cache_elems * es))) break;
-    if ((rc = alloc(h, &h->cache_vt, cache_elems * es))) break;
+    if ((rc = alloc(h, &h->cache_v, cache_elems * es))) break;
     if ((rc = alloc_t(h, &h->ctx_len, c.max_batch + 1, 4))) break;
     if ((rc = alloc_t(h, &h->err, 1, 4))) break;
     h->n_rope = (int)h->ctx_alloc;
@@ -258,7 +258,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc(h, &h->act, (size_t)h->maxM * c.ffn * es))) break;
     if ((rc = alloc(h, &h->qb, (size_t)c.max_batch * nkv * h->QRpad * d * es))) break;
     if ((rc = alloc(h, &h->kb, (size_t)c.max_batch * nkv * h->Rpad * d * es))) break;
-    if ((rc = alloc(h, &h->vbt, (size_t)c.max_batch * nkv * h->Rpad * d * es))) break;
+    if ((rc = alloc(h, &h->vb, (size_t)c.max_batch * nkv * h->Rpad * d * es))) break;
     const size_t prow = (size_t)h->item_cap * nkv * splits * 16 * h->qrt_max;
     if ((rc = alloc_t(h, &h->o_part, prow * d, 4))) break;
     if ((rc = alloc_t(h, &h->m_part, prow, 4))) break;
@@ -393,7 +393,7 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
       gk.b_ld = H;
       EpiKVInject<bf16_t>::Params pk;
       pk.cache_k = (bf16_t*)h->cache_k;
-      pk.cache_vt = (bf16_t*)h->cache_vt;
+      pk.cache_v = (bf16_t*)h->cache_v;
       pk.row_slot = h->row_slot + c0;
       pk.row_pos = h->row_pos + c0;
       pk.k_gain = (const bf16_t* const*)(h->d_k_gains + l0);
@@ -492,7 +492,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
                       h->layers[0].in_norm, h->hbuf, c.rms_eps, h->err, s);
   }
   {
-    Phase ph(h, s, DFLASH_PH_ATTN);
+    Phase ph(h, s, DFLASH_PH_ATTN_PLAN);
     launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->target_wg, h->item_cap, h->plan, h->items,
                      h->first_item, h->n_items, h->err, s);
   }
@@ -506,7 +506,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       EpiQKV<bf16_t>::Params pq;
       pq.qb = (bf16_t*)h->qb;
       pq.kb = (bf16_t*)h->kb;
-      pq.vbt = (bf16_t*)h->vbt;
+      pq.vb = (bf16_t*)h->vb;
       pq.slots = slots;
       pq.ctx_len = h->ctx_len;
       pq.q_gain = (const bf16_t*)L.q_norm;
@@ -529,9 +529,9 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       AttnArgs a;
       a.qb = h->qb;
       a.cache_k = (const char*)h->cache_k + l * layer_cache;
-      a.cache_vt = (const char*)h->cache_vt + l * layer_cache;
+      a.cache_v = (const char*)h->cache_v + l * layer_cache;
       a.kb = h->kb;
-      a.vbt = h->vbt;
+      a.vb = h->vb;
       a.slots = slots;
       a.ctx_len = h->ctx_len;
       a.plan = h->plan;
@@ -762,7 +762,7 @@ int dflash_copy_cache(dflash_handle* h, void* stream, int32_t layer, int32_t slo
   if (layer < 0 || layer >= c.n_layers || slot < 0 || slot >= c.max_batch || start < 0 || n < 0 ||
       start + n > c.max_ctx)
     return DFLASH_E_INVALID;
-  launch_copy_cache(c.dtype, h->cache_k, h->cache_vt, layer, slot, start, n, c.max_batch + 1, c.n_kv_heads, c.head_dim,
+  launch_copy_cache(c.dtype, h->cache_k, h->cache_v, layer, slot, start, n, c.max_batch + 1, c.n_kv_heads, c.head_dim,
                     h->ctx_alloc, k_out, v_out, S(stream));
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }

@@ -5,16 +5,18 @@
 //
 // Work split (decided on the device from the actual context lengths, no host
 // sync): the context keys of each request are cut into chunks of CK keys; one
-// work-group handles (chunk, kv head[, q-row half]) with 4 waves taking a
+// work-group handles (chunk, kv head[, q-row part]) with 4 waves taking a
 // quarter of the chunk each.  Scores are computed transposed, S^T = K Q^T, so
 // that the softmax probabilities land in registers exactly as the B operand of
-// O^T = V^T P^T; K rows and V^T rows (the cache stores V transposed) are read
-// straight from global memory in MFMA operand order.  The key order inside each
-// 32-key group is permuted consistently on both products so no register
-// shuffles are needed.  Waves merge through LDS in a fixed order, and a combine
-// kernel merges the chunks of a request (log-sum-exp rescaling, fixed order).
+// O^T = V^T P^T.  K and V are stored in 32-key blocks in MFMA operand order
+// (kv_layout.h), so every fragment load of a wave is one contiguous 1 KB read;
+// each wave keeps the next two key groups in flight in registers while it
+// computes on the current one.  Waves merge through LDS in a fixed order, and a
+// combine kernel merges the chunks of a request (log-sum-exp rescaling, fixed
+// order).
 #pragma once
 #include "common.h"
+#include "kv_layout.h"
 
 namespace dfl {
 
@@ -25,10 +27,10 @@ struct AttnPlan {          // written by attn_plan_kernel
 
 struct AttnArgs {
   const void* qb;          // [n_req][n_kv][QRpad][D]
-  const void* cache_k;     // layer base: [slot][n_kv][ctx_alloc][D]
-  const void* cache_vt;    // layer base: [slot][n_kv][D][ctx_alloc]
-  const void* kb;          // [n_req][n_kv][Rpad][D]
-  const void* vbt;         // [n_req][n_kv][D][Rpad]
+  const void* cache_k;     // layer base: [slot][n_kv][ctx_alloc * D], 32-key blocks
+  const void* cache_v;     // layer base: [slot][n_kv][ctx_alloc * D], 32-key blocks
+  const void* kb;          // block's own keys   [n_req][n_kv][Rpad * D] (Rpad == 32: one block)
+  const void* vb;          // block's own values [n_req][n_kv][Rpad * D]
   const int32_t* slots;
   const int32_t* ctx_len;
   const AttnPlan* plan;

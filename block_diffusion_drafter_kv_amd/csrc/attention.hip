@@ -1,6 +1,7 @@
 // Block attention kernels: work plan, split-context attention, chunk combine.
 #include "attention.h"
 #include "ops.h"
+#include "lds_dma.h"
 
 namespace dfl {
 
@@ -64,195 +65,164 @@ __device__ __forceinline__ typename Frag<T>::type load_frag8(const T* p) {
   return f;
 }
 
-template <typename T, int D, int QRT>
-__global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
-  constexpr int KSTEPS = D / 32, DT = D / 16, ROWS = QRT * 16;
-  constexpr int CH = (int)sizeof(T) * D / 16;  // 16-byte chunks per q row
-  constexpr int SW = (CH < 16 ? CH : 16) - 1;
-  constexpr int OLD = D + 1;                   // padded row stride of the merge buffer
+// One work-group = (work item, kv head, q-row part) with one wave per 16-row
+// query tile.  The item's keys [kbeg, kend) (and, for a request's last item, the
+// block's own R keys) are streamed in 32-key groups through a ring of S LDS
+// stages by direct global->LDS copies; every wave reads each group from LDS and
+// runs its own online softmax over all of the item's keys, so no cross-wave
+// merge is needed.  Per group: S^T (32 x 16) = K Q^T, scale, mask, softmax
+// update, O^T += V^T P^T.  Copies run S - 1 groups ahead; a group is published
+// by the copying waves' vmcnt wait plus a barrier, which also retires the stage
+// that the next copy overwrites.
+//
+// The running maximum is raised lazily: probabilities are taken relative to a
+// reference m_ref, which only moves (rescaling O and l) when a score exceeds it
+// by more than 2^8 in the exp2 domain; the result is unchanged up to rounding
+// (bf16 rounding of P is relative, and P <= 256 stays far from overflow).
+template <typename T, int D, int QRT, int S>
+__global__ __launch_bounds__(QRT * 64) void attn_kernel(const AttnArgs a) {
+  constexpr int KS = D / 32, DT = D / 16;
+  constexpr int BLK = KV_BLOCK * D;                        // elements of a K (or V) block
+  constexpr int EPC = 16 / (int)sizeof(T);                 // elements per 16-byte copy
+  constexpr int IPG = 2 * BLK / (64 * EPC);                // 1 KB wave copies per group (K, then V)
+  constexpr int CW = QRT >= 4 ? 4 : (QRT >= 2 ? 2 : 1);    // waves that issue copies
+  constexpr int PER = IPG / CW;                            // copies per copying wave per group
+  constexpr int VOFF = IPG / 2 * 64;                       // first uint4 of the V block in a stage
+  constexpr float TAU = 8.f;                               // lazy-rescale threshold (log2 units)
+  static_assert(IPG % CW == 0 && (S - 2) * PER < 64 && S >= 2 && S <= 4, "copy split / vmcnt range");
   typedef typename Frag<T>::type FragT;
-  __shared__ uint4 q_lds[ROWS * CH];
-  __shared__ float o_acc[ROWS * OLD];
-  __shared__ float m_w[4][ROWS], l_w[4][ROWS];
+  __shared__ uint4 ring[S][IPG * 64];
 
   const int item = blockIdx.x, kv = blockIdx.y, z = blockIdx.z;
   if (item >= a.plan->count) return;
   const int4 it = a.items[item];
   const int req = it.x, kbeg = it.y, kend = it.z, is_last = it.w;
   const int slot = a.slots[req];
-  const int ck = a.plan->ck;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, r16 = lane & 15;
 
+  // this wave's 16 query rows as B-operand fragments (row r16, dims 32 s + 8 grp ..)
+  FragT qf[KS];
   {
-    const T* qsrc = (const T*)a.qb + ((int64_t)(req * a.n_kv + kv) * a.QRpad + (int64_t)z * a.rows_per_split) * D;
-    for (int c = tid; c < ROWS * CH; c += 256) {
-      const int row = c / CH, ch = c % CH;
-      q_lds[row * CH + (ch ^ (row & SW))] = ((const uint4*)(qsrc + (int64_t)row * D))[ch];
-    }
+    const T* qrow = (const T*)a.qb +
+                    ((int64_t)(req * a.n_kv + kv) * a.QRpad + (int64_t)z * a.rows_per_split + wave * 16 + r16) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = load_frag8<T>(qrow + s * 32 + grp * 8);
   }
-  __syncthreads();
+  wait_vmcnt<0>();
 
-  f32x4 acc_o[DT][QRT];
-  float m_row[QRT], l_row[QRT];
-#pragma unroll
-  for (int rt = 0; rt < QRT; ++rt) {
-    m_row[rt] = -INFINITY;
-    l_row[rt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc_o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  const int ncache = (kend - kbeg + KV_BLOCK - 1) / KV_BLOCK;
+  const int ng = ncache + (is_last ? 1 : 0);
+  const int64_t head = (int64_t)slot * a.n_kv + kv;
+  const T* kc = (const T*)a.cache_k + head * a.ctx_alloc * D + (int64_t)kbeg * D;
+  const T* vc = (const T*)a.cache_v + head * a.ctx_alloc * D + (int64_t)kbeg * D;
+  const int64_t bh = (int64_t)req * a.n_kv + kv;
+  const T* kblk = (const T*)a.kb + bh * a.Rpad * D;
+  const T* vblk = (const T*)a.vb + bh * a.Rpad * D;
 
-  auto run = [&](const T* kbase, const T* vtbase, int64_t vstride, int s0, int s1) {
-    for (int g0 = s0; g0 < s1; g0 += 32) {
-      FragT kf[2][KSTEPS];
+  auto issue = [&](int gi, int st) {
+    if (wave < CW) {
+      const bool in_cache = gi < ncache;
+      const T* kp = (in_cache ? kc + (int64_t)gi * BLK : kblk) + lane * EPC;
+      const T* vp = (in_cache ? vc + (int64_t)gi * BLK : vblk) + lane * EPC;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int key = g0 + 8 * (r16 >> 2) + 4 * t + (r16 & 3);
-        const T* kp = kbase + (int64_t)key * D + grp * 8;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          if (key < s1) kf[t][s] = load_frag8<T>(kp + s * 32);
-          else kf[t][s] = FragT{};
-        }
+      for (int c = 0; c < PER; ++c) {
+        const int i = wave * PER + c;
+        const T* src = i < IPG / 2 ? kp + i * 64 * EPC : vp + (i - IPG / 2) * 64 * EPC;
+        copy16_to_lds(src, &ring[st][i * 64]);
       }
-      FragT vf[DT];
-      const int kv0 = g0 + grp * 8;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        vf[dt] = load_frag8<T>(vtbase + (int64_t)(dt * 16 + r16) * vstride + kv0);
-        if (kv0 + 8 > s1) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (kv0 + e >= s1) vf[dt][e] = (T)0.f;
-        }
-      }
-      f32x4 sacc[2][QRT];
-#pragma unroll
-      for (int rt = 0; rt < QRT; ++rt) sacc[0][rt] = sacc[1][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-        for (int rt = 0; rt < QRT; ++rt) {
-          const int row = rt * 16 + r16;
-          FragT qf;
-          if constexpr (sizeof(T) == 2) {
-            const int ch = s * 4 + grp;
-            *(uint4*)&qf = q_lds[row * CH + (ch ^ (row & SW))];
-          } else {
-            const int ch = s * 8 + grp * 2;
-            ((uint4*)&qf)[0] = q_lds[row * CH + (ch ^ (row & SW))];
-            ((uint4*)&qf)[1] = q_lds[row * CH + ((ch + 1) ^ (row & SW))];
-          }
-          Frag<T>::mma(sacc[0][rt], kf[0][s], qf);
-          Frag<T>::mma(sacc[1][rt], kf[1][s], qf);
-        }
-      }
-      FragT pf[QRT];
-#pragma unroll
-      for (int rt = 0; rt < QRT; ++rt) {
-        float sv[8];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = g0 + 8 * grp + 4 * t + i;
-            const float v = key < s1 ? sacc[t][rt][i] * a.scale_log2 : -INFINITY;
-            sv[4 * t + i] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m_row[rt], mx);
-        float alpha = 1.f, sum = 0.f;
-        if (mnew != -INFINITY) {
-          alpha = exp2f(m_row[rt] - mnew);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = exp2f(sv[e] - mnew);
-            sv[e] = p;
-            sum += p;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sv[e] = 0.f;
-        }
-        l_row[rt] = l_row[rt] * alpha + sum;
-        m_row[rt] = mnew;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc_o[dt][rt] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[rt][e] = (T)sv[e];
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int rt = 0; rt < QRT; ++rt) Frag<T>::mma(acc_o[dt][rt], vf[dt], pf[rt]);
     }
   };
 
-  const int quarter = ck / 4;
-  {
-    const int wb = kbeg + wave * quarter;
-    const int we = min(kend, wb + quarter);
-    if (wb < we) {
-      const int64_t head = (int64_t)slot * a.n_kv + kv;
-      const T* kbase = (const T*)a.cache_k + head * a.ctx_alloc * D;
-      const T* vtbase = (const T*)a.cache_vt + head * D * a.ctx_alloc;
-      // keys are addressed relative to the segment start so 32-key groups stay aligned
-      run(kbase + (int64_t)wb * D, vtbase + wb, a.ctx_alloc, 0, we - wb);
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_sum = 0.f;
+
+  auto frag_at = [&](const uint4* stage, int f) {  // fragment f (in 64-lane units) of this lane
+    FragT x;
+    if constexpr (sizeof(T) == 2) {
+      *(uint4*)&x = stage[f * 64 + lane];
+    } else {
+      ((uint4*)&x)[0] = stage[2 * (f * 64 + lane)];
+      ((uint4*)&x)[1] = stage[2 * (f * 64 + lane) + 1];
     }
-    if (is_last && wave == 3) {
-      const int64_t bh = (int64_t)req * a.n_kv + kv;
-      run((const T*)a.kb + bh * a.Rpad * D, (const T*)a.vbt + bh * D * a.Rpad, a.Rpad, 0, a.R);
+    return x;
+  };
+
+  auto compute = [&](const uint4* stage, int gi) {
+    const int nvalid = gi < ncache ? min(KV_BLOCK, kend - kbeg - KV_BLOCK * gi) : a.R;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      Frag<T>::mma(s0, frag_at(stage, s), qf[s]);
+      Frag<T>::mma(s1, frag_at(stage, KS + s), qf[s]);
     }
+    // lane holds keys 8*grp + i (s0) and 8*grp + 4 + i (s1) of this group for query row r16
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k0 = 8 * grp + i;
+      sv[i] = k0 < nvalid ? s0[i] * a.scale_log2 : -INFINITY;
+      sv[4 + i] = k0 + 4 < nvalid ? s1[i] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (__any(mx > m_ref + TAU)) {
+      const float mnew = fmaxf(m_ref, mx);
+      const float alpha = mnew > m_ref ? exp2f(m_ref - mnew) : 1.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      l_sum *= alpha;
+      m_ref = mnew;
+    }
+    FragT pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = exp2f(sv[e] - m_ref);
+      l_sum += p;
+      pf[e] = (T)p;
+    }
+    const uint4* vst = stage + VOFF;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      FragT vf = frag_at(vst, dt);
+      if (nvalid < KV_BLOCK) {  // keys past the end hold stale or unwritten data
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (grp * 8 + e >= nvalid) vf[e] = (T)0.f;
+      }
+      Frag<T>::mma(acc[dt], vf, pf);
+    }
+  };
+
+  for (int p = 0; p < S - 1 && p < ng; ++p) issue(p, p);
+  for (int gi = 0; gi < ng; ++gi) {
+    if (wave < CW) {
+      const int ahead = min(S - 2, ng - 1 - gi);  // groups issued after gi that may stay in flight
+      if (S >= 4 && ahead >= 2) wait_vmcnt<(S >= 4 ? 2 * PER : 0)>();
+      else if (S >= 3 && ahead >= 1) wait_vmcnt<(S >= 3 ? PER : 0)>();
+      else wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (gi + S - 1 < ng) issue(gi + S - 1, (gi + S - 1) % S);
+    compute(ring[gi % S], gi);
   }
 
-#pragma unroll
-  for (int rt = 0; rt < QRT; ++rt) {
-    l_row[rt] += __shfl_xor(l_row[rt], 16, 64);
-    l_row[rt] += __shfl_xor(l_row[rt], 32, 64);
-    if (grp == 0) {
-      m_w[wave][rt * 16 + r16] = m_row[rt];
-      l_w[wave][rt * 16 + r16] = l_row[rt];
-    }
-  }
-  __syncthreads();
-  float sc[QRT];
-#pragma unroll
-  for (int rt = 0; rt < QRT; ++rt) {
-    const int row = rt * 16 + r16;
-    const float M = fmaxf(fmaxf(m_w[0][row], m_w[1][row]), fmaxf(m_w[2][row], m_w[3][row]));
-    sc[rt] = (m_row[rt] == -INFINITY) ? 0.f : exp2f(m_row[rt] - M);
-  }
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int rt = 0; rt < QRT; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int idx = (rt * 16 + r16) * OLD + dt * 16 + 4 * grp + i;
-            const float v = acc_o[dt][rt][i] * sc[rt];
-            o_acc[idx] = (w == 0) ? v : o_acc[idx] + v;
-          }
-    }
-    __syncthreads();
-  }
+  // partial result of this item: O (unnormalised, relative to m_ref), m_ref, l
+  l_sum += __shfl_xor(l_sum, 16, 64);
+  l_sum += __shfl_xor(l_sum, 32, 64);
+  const int row = wave * 16 + r16;
   const int64_t base = ((int64_t)item * a.n_kv + kv) * a.splits + z;
-  float* op = a.o_part + base * ROWS * D;
-  for (int idx = tid; idx < ROWS * D; idx += 256) op[idx] = o_acc[(idx / D) * OLD + (idx % D)];
-  for (int row = tid; row < ROWS; row += 256) {
-    float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, m_w[w][row]);
-    float L = 0.f;
-    for (int w = 0; w < 4; ++w)
-      if (m_w[w][row] != -INFINITY) L += l_w[w][row] * exp2f(m_w[w][row] - M);
-    a.m_part[base * ROWS + row] = M;
-    a.l_part[base * ROWS + row] = L;
+  float* op = a.o_part + (base * (QRT * 16) + row) * D + 4 * grp;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + dt * 16) = acc[dt];
+  if (grp == 0) {
+    a.m_part[base * (QRT * 16) + row] = m_ref;
+    a.l_part[base * (QRT * 16) + row] = l_sum;
   }
 }
 
@@ -304,16 +274,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 static void launch_attn_t(const AttnArgs& a, int qrt, dim3 grid, hipStream_t s) {
+  constexpr int S = (sizeof(T) == 4 && D == 128) ? 3 : 4;  // LDS ring stages (16 or 32 KB each)
   switch (qrt) {
-    case 1: attn_kernel<T, D, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: attn_kernel<T, D, 2><<<grid, 256, 0, s>>>(a); break;
-    case 3: attn_kernel<T, D, 3><<<grid, 256, 0, s>>>(a); break;
-    case 4:
-      if constexpr (sizeof(T) == 2 || D == 64) attn_kernel<T, D, 4><<<grid, 256, 0, s>>>(a);
-      break;
-    case 5:
-      if constexpr (sizeof(T) == 2 || D == 64) attn_kernel<T, D, 5><<<grid, 256, 0, s>>>(a);
-      break;
+    case 1: attn_kernel<T, D, 1, S><<<grid, 64, 0, s>>>(a); break;
+    case 2: attn_kernel<T, D, 2, S><<<grid, 128, 0, s>>>(a); break;
+    case 3: attn_kernel<T, D, 3, S><<<grid, 192, 0, s>>>(a); break;
+    case 4: attn_kernel<T, D, 4, S><<<grid, 256, 0, s>>>(a); break;
+    case 5: attn_kernel<T, D, 5, S><<<grid, 320, 0, s>>>(a); break;
   }
 }
 

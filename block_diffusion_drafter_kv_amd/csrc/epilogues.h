@@ -3,6 +3,7 @@
 // product.
 #pragma once
 #include "common.h"
+#include "kv_layout.h"
 
 namespace dfl {
 
@@ -71,11 +72,12 @@ __device__ __forceinline__ void norm_rope_pair(float& x1, float& x2, int i, int 
 
 // ---- draft block: q | k | v projections -> head norm + RoPE -> attention layouts ----
 // q rows go to qb[r][kv][i*R + j][d] (q head kv*g + i, block row j), k rows to
-// kb[r][kv][j][d], v rows to vbt[r][kv][d][j] (transposed for the PV product).
+// kb[r][kv][Rpad * d] and v rows to vb[r][kv][Rpad * d], in the 32-key block
+// order of the cache (kv_layout.h).
 template <typename T>
 struct EpiQKV {
   struct Params {
-    T* qb; T* kb; T* vbt;
+    T* qb; T* kb; T* vb;
     const int32_t* slots; const int32_t* ctx_len;
     const T* q_gain; const T* k_gain;
     const float2* rope;      // [pos][d/2] (cos, sin)
@@ -109,26 +111,26 @@ struct EpiQKV {
           dst[i + half] = from_f32<T>(x2);
         } else {
           const int kh = (nb - p.q_dim) / p.d;
-          T* dst = p.kb + ((int64_t)(req * p.n_kv + kh) * p.Rpad + j) * p.d;
-          dst[i] = from_f32<T>(x1);
-          dst[i + half] = from_f32<T>(x2);
+          T* dst = p.kb + (int64_t)(req * p.n_kv + kh) * p.Rpad * p.d;
+          dst[k_off(j, i, p.d)] = from_f32<T>(x1);
+          dst[k_off(j, i + half, p.d)] = from_f32<T>(x2);
         }
       } else {
         const int vh = (nb - p.q_dim - p.kv_dim) / p.d;
-        T* dst = p.vbt + (int64_t)(req * p.n_kv + vh) * p.d * p.Rpad;
-        dst[(int64_t)i * p.Rpad + j] = from_f32<T>(x1);
-        dst[(int64_t)(i + half) * p.Rpad + j] = from_f32<T>(x2);
+        T* dst = p.vb + (int64_t)(req * p.n_kv + vh) * p.Rpad * p.d;
+        dst[v_off(j, i, p.d)] = from_f32<T>(x1);
+        dst[v_off(j, i + half, p.d)] = from_f32<T>(x2);
       }
     }
   }
 };
 
 // ---- context injection: per-layer k|v of the fused feature -> k-norm + RoPE -> cache ----
-// Cache layouts: K [layer][slot][kv][ctx_alloc][d], V^T [layer][slot][kv][d][ctx_alloc].
+// Cache: K and V [layer][slot][kv][ctx_alloc * d], positions in 32-key blocks (kv_layout.h).
 template <typename T>
 struct EpiKVInject {
   struct Params {
-    T* cache_k; T* cache_vt;
+    T* cache_k; T* cache_v;
     const int32_t* row_slot; const int32_t* row_pos;   // per GEMM row (global row index)
     const T* const* k_gain;                              // device array [n_layers] of gains
     const float2* rope;
@@ -159,10 +161,9 @@ struct EpiKVInject {
           float x1 = st[r * ld + hh * p.d + i], x2 = st[r * ld + hh * p.d + i + half];
           norm_rope_pair<T>(x1, x2, i, p.d, p.k_gain[layer], p.eps, p.rope + (int64_t)pos * half);
           T* dst = p.cache_k +
-                   (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.ctx_alloc * p.d +
-                   (int64_t)pos * p.d;
-          dst[i] = from_f32<T>(x1);
-          dst[i + half] = from_f32<T>(x2);
+                   (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.ctx_alloc * p.d;
+          dst[k_off(pos, i, p.d)] = from_f32<T>(x1);
+          dst[k_off(pos, i + half, p.d)] = from_f32<T>(x2);
         }
       } else {
         // lanes walk rows (consecutive positions -> coalesced stores), waves walk columns
@@ -175,10 +176,10 @@ struct EpiKVInject {
           pos = p.row_pos[m];
         }
         if (slot >= 0) {
-          T* base = p.cache_vt +
-                    (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.d * p.ctx_alloc + pos;
+          T* base = p.cache_v +
+                    (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.ctx_alloc * p.d;
           for (int c = wave * RPL + lane / ROWS; c < p.d; c += 4 * RPL)
-            base[(int64_t)c * p.ctx_alloc] = from_f32<T>(st[r * ld + hh * p.d + c]);
+            base[v_off(pos, c, p.d)] = from_f32<T>(st[r * ld + hh * p.d + c]);
         }
       }
     }

@@ -797,7 +797,7 @@ __global__ void synth_target_kernel(int K, int V, const float* draft, float sigm
 }
 
 template <typename T>
-__global__ void copy_cache_kernel(const T* cache_k, const T* cache_vt, int layer, int slot, int start, int n,
+__global__ void copy_cache_kernel(const T* cache_k, const T* cache_v, int layer, int slot, int start, int n,
                                   int max_batch, int n_kv, int d, int64_t ctx_alloc, T* k_out, T* v_out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)n * n_kv * d;
@@ -806,8 +806,8 @@ __global__ void copy_cache_kernel(const T* cache_k, const T* cache_vt, int layer
   const int h = (int)((idx / d) % n_kv);
   const int i = (int)(idx / ((int64_t)d * n_kv));
   const int64_t head = ((int64_t)layer * max_batch + slot) * n_kv + h;
-  k_out[idx] = cache_k[(head * ctx_alloc + start + i) * d + e];
-  v_out[idx] = cache_vt[(head * d + e) * ctx_alloc + start + i];
+  k_out[idx] = cache_k[head * ctx_alloc * d + k_off(start + i, e, d)];
+  v_out[idx] = cache_v[head * ctx_alloc * d + v_off(start + i, e, d)];
 }
 
 __global__ void reset_slots_kernel(int n, const int32_t* slots, int32_t* ctx_len, int max_batch, int32_t* err) {
@@ -943,16 +943,16 @@ void launch_synth_target(int n_req, int K, int V, const float* draft_logits, flo
   synth_target_kernel<<<grid, 256, 0, s>>>(K, V, draft_logits, sigma, seed, step, out);
 }
 
-void launch_copy_cache(int dtype, const void* cache_k, const void* cache_vt, int layer, int slot, int start, int n,
+void launch_copy_cache(int dtype, const void* cache_k, const void* cache_v, int layer, int slot, int start, int n,
                        int max_batch, int n_kv, int d, int64_t ctx_alloc, void* k_out, void* v_out, hipStream_t s) {
   const int64_t total = (int64_t)n * n_kv * d;
   if (total <= 0) return;
   if (dtype == DT_BF16)
-    copy_cache_kernel<bf16_t><<<cdiv(total, 256), 256, 0, s>>>((const bf16_t*)cache_k, (const bf16_t*)cache_vt, layer,
+    copy_cache_kernel<bf16_t><<<cdiv(total, 256), 256, 0, s>>>((const bf16_t*)cache_k, (const bf16_t*)cache_v, layer,
                                                                 slot, start, n, max_batch, n_kv, d, ctx_alloc,
                                                                 (bf16_t*)k_out, (bf16_t*)v_out);
   else
-    copy_cache_kernel<float><<<cdiv(total, 256), 256, 0, s>>>((const float*)cache_k, (const float*)cache_vt, layer,
+    copy_cache_kernel<float><<<cdiv(total, 256), 256, 0, s>>>((const float*)cache_k, (const float*)cache_v, layer,
                                                                slot, start, n, max_batch, n_kv, d, ctx_alloc,
                                                                (float*)k_out, (float*)v_out);
 }

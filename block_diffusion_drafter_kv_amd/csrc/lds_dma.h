@@ -1,0 +1,40 @@
+// Direct global -> LDS copies and the waits / barrier that order them.
+#pragma once
+#include "common.h"
+
+namespace dfl {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
+
+// 16-byte global -> LDS copy: lane l of the wave lands at lds_wave_base + 16 * l.
+// Issued through inline asm so that the compiler's wait insertion does not treat
+// the copy as an LDS store aliasing every later LDS read (it would drain all
+// copies in flight); ordering is provided by the explicit vmcnt waits and
+// barriers of the ring loop, which contains no other vector-memory operation.
+__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  // M0 carries the LDS base; it is saved and restored around the copy (the
+  // compiler reserves M0), with the one wait state an M0 write needs before an
+  // LDS-DMA instruction reads it.
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(g)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that is also a compiler memory fence (no LDS access moves
+// across it) but, unlike __syncthreads, emits no wait on outstanding copies.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+}  // namespace dfl

@@ -70,7 +70,7 @@ void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, cons
 void launch_sanitize_slots(int n, const int32_t* in, int32_t* out, int max_batch, int32_t* err, hipStream_t s);
 void launch_synth_target(int n_req, int K, int V, const float* draft_logits, float sigma, uint64_t seed,
                          uint64_t step, float* out, hipStream_t s);
-void launch_copy_cache(int dtype, const void* cache_k, const void* cache_vt, int layer, int slot, int start, int n,
+void launch_copy_cache(int dtype, const void* cache_k, const void* cache_v, int layer, int slot, int start, int n,
                        int max_batch, int n_kv, int d, int64_t ctx_alloc, void* k_out, void* v_out, hipStream_t s);
 void launch_reset_slots(int n, const int32_t* slots, int32_t* ctx_len, int max_batch, int32_t* err, hipStream_t s);
 void launch_philox_fill(int n, uint64_t seed, uint32_t slot, uint64_t step, uint32_t purpose, float* out,

@@ -223,7 +223,7 @@ enum dflash_phase {
   DFLASH_PH_INJECT_KV,       /* per-layer K|V GEMM + k-norm/RoPE/cache store */
   DFLASH_PH_EMBED,           /* block embedding + first RMSNorm             */
   DFLASH_PH_QKV,             /* q|k|v GEMM + head norm + RoPE               */
-  DFLASH_PH_ATTN,            /* block attention kernel (plan included)      */
+  DFLASH_PH_ATTN,            /* block attention kernel                      */
   DFLASH_PH_ATTN_COMBINE,    /* merge of context chunks                     */
   DFLASH_PH_O,               /* output projection + residual                */
   DFLASH_PH_NORM,            /* RMSNorms between sub-layers                 */
@@ -232,6 +232,7 @@ enum dflash_phase {
   DFLASH_PH_LM_HEAD,         /* LM-head GEMM + tile statistics              */
   DFLASH_PH_SELECT,          /* row statistics, sampling, top-k, tree       */
   DFLASH_PH_VERIFY,          /* verification                                */
+  DFLASH_PH_ATTN_PLAN,       /* context-chunk work list of the attention    */
   DFLASH_PH_COUNT
 };
 int dflash_profile(dflash_handle* h, int32_t enable);
