@@ -29,13 +29,12 @@ struct dflash_handle {
   float2* rope = nullptr;
   int n_rope = 0;
   // draft scratch
-  int maxM = 0, Rpad = 0, QRpad = 0, attn_splits = 1, item_cap = 0, target_wg = 1024, qrt_max = 5;
+  int maxM = 0, Rpad = 0, QRpad = 0, attn_splits = 1, attn_wg = 0, piece_cap = 0, qrt_max = 5;
   float* X = nullptr;
   void *hbuf = nullptr, *attn_out = nullptr, *act = nullptr, *qb = nullptr, *kb = nullptr, *vb = nullptr;
   float *o_part = nullptr, *m_part = nullptr, *l_part = nullptr;
   AttnPlan* plan = nullptr;
-  int4* items = nullptr;
-  int32_t *first_item = nullptr, *n_items = nullptr;
+  int32_t *seg_start = nullptr, *chunk_base = nullptr;
   int32_t* dslots = nullptr;              // validated slot ids of the current draft
   float* partials = nullptr;
   size_t partials_elems = 0;
@@ -62,6 +61,10 @@ struct dflash_handle {
 };
 
 namespace {
+
+constexpr int kAttnMinGroups = 8;   // fewest 32-key groups per attention work-group range
+constexpr int kAttnChunkMin = 16;   // chunk of a segment: at least 16 groups (512 keys) ...
+constexpr int kAttnChunkMax = 16;   // ... and at most 16 chunks per segment
 
 // Records a pair of HIP events around a group of launches when timing is enabled.
 struct Phase {
@@ -236,7 +239,10 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
   h->Rpad = ((R + 31) / 32) * 32;
   h->QRpad = ((g * R + 15) / 16) * 16 + 80;
   h->ctx_alloc = ((int64_t)(c.max_ctx + 63) / 64) * 64 + 64;
-  h->item_cap = c.max_batch + h->target_wg / (nkv * splits) + 8;
+  // attention: two work-groups per CU (80 KB LDS ring each); at most kAttnChunkMax
+  // partial records (chunks) per segment
+  h->attn_wg = 2 * h->num_cus;
+  h->piece_cap = c.max_batch * nkv * splits * kAttnChunkMax;
   h->lm_tile = gemm_bn(c.dtype);
   h->n_vtiles = (c.vocab + h->lm_tile - 1) / h->lm_tile;
   h->inject_chunk = std::min(c.max_inject_rows, 16384);
@@ -259,14 +265,13 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc(h, &h->qb, (size_t)c.max_batch * nkv * h->QRpad * d * es))) break;
     if ((rc = alloc(h, &h->kb, (size_t)c.max_batch * nkv * h->Rpad * d * es))) break;
     if ((rc = alloc(h, &h->vb, (size_t)c.max_batch * nkv * h->Rpad * d * es))) break;
-    const size_t prow = (size_t)h->item_cap * nkv * splits * 16 * h->qrt_max;
+    const size_t prow = (size_t)h->piece_cap * 16 * h->qrt_max;
     if ((rc = alloc_t(h, &h->o_part, prow * d, 4))) break;
     if ((rc = alloc_t(h, &h->m_part, prow, 4))) break;
     if ((rc = alloc_t(h, &h->l_part, prow, 4))) break;
     if ((rc = alloc_t(h, &h->plan, 1, sizeof(AttnPlan)))) break;
-    if ((rc = alloc_t(h, &h->items, h->item_cap, sizeof(int4)))) break;
-    if ((rc = alloc_t(h, &h->first_item, c.max_batch, 4))) break;
-    if ((rc = alloc_t(h, &h->n_items, c.max_batch, 4))) break;
+    if ((rc = alloc_t(h, &h->seg_start, (size_t)c.max_batch * nkv * splits + 1, 4))) break;
+    if ((rc = alloc_t(h, &h->chunk_base, (size_t)c.max_batch * nkv * splits, 4))) break;
     if ((rc = alloc_t(h, &h->dslots, c.max_batch, 4))) break;
     // split-K is used only while tiles * splits <= 2 * CUs: bounded by that many output tiles
     h->partials_elems = (size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(c.dtype);
@@ -493,8 +498,8 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   }
   {
     Phase ph(h, s, DFLASH_PH_ATTN_PLAN);
-    launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->target_wg, h->item_cap, h->plan, h->items,
-                     h->first_item, h->n_items, h->err, s);
+    launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->attn_wg, kAttnMinGroups, kAttnChunkMin,
+                     kAttnChunkMax, h->plan, h->seg_start, h->chunk_base, s);
   }
   const int64_t layer_cache = (int64_t)(c.max_batch + 1) * nkv * h->ctx_alloc * d * h->esize;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -535,7 +540,11 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       a.slots = slots;
       a.ctx_len = h->ctx_len;
       a.plan = h->plan;
-      a.items = h->items;
+      a.seg_start = h->seg_start;
+      a.chunk_base = h->chunk_base;
+      a.n_seg = n_req * nkv * splits;
+      a.chunk_min = kAttnChunkMin;
+      a.chunk_max = kAttnChunkMax;
       a.o_part = h->o_part;
       a.m_part = h->m_part;
       a.l_part = h->l_part;
@@ -547,17 +556,16 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       a.splits = splits;
       a.ctx_alloc = h->ctx_alloc;
       a.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
-      const int gx = std::min(h->item_cap, n_req + h->target_wg / (nkv * splits) + 2);
       {
         Phase ph(h, s, DFLASH_PH_ATTN);
-        launch_attn(dt, d, qrt, a, dim3(gx, nkv, splits), s);
+        launch_attn(dt, d, qrt, a, h->attn_wg, s);
       }
       AttnCombineArgs cb;
       cb.o_part = h->o_part;
       cb.m_part = h->m_part;
       cb.l_part = h->l_part;
-      cb.first_item = h->first_item;
-      cb.n_items = h->n_items;
+      cb.seg_start = h->seg_start;
+      cb.chunk_base = h->chunk_base;
       cb.out = h->attn_out;
       cb.n_kv = nkv;
       cb.group = g;
@@ -567,6 +575,8 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       cb.QRT16 = 16 * qrt;
       cb.q_dim = qdim;
       cb.D = d;
+      cb.chunk_min = kAttnChunkMin;
+      cb.chunk_max = kAttnChunkMax;
       Phase ph(h, s, DFLASH_PH_ATTN_COMBINE);
       launch_attn_combine(dt, d, cb, dim3(n_req, nkv * splits, (rows_split + 15) / 16), s);
     }

@@ -3,17 +3,22 @@
 // "关键创新" Step 3]).  Few queries (g*(K+1) per kv head) against a long context:
 // the kernel streams K and V exactly once per (request, kv head) from HBM.
 //
-// Work split (decided on the device from the actual context lengths, no host
-// sync): the context keys of each request are cut into chunks of CK keys; one
-// work-group handles (chunk, kv head[, q-row part]) with 4 waves taking a
-// quarter of the chunk each.  Scores are computed transposed, S^T = K Q^T, so
-// that the softmax probabilities land in registers exactly as the B operand of
-// O^T = V^T P^T.  K and V are stored in 32-key blocks in MFMA operand order
-// (kv_layout.h), so every fragment load of a wave is one contiguous 1 KB read;
-// each wave keeps the next two key groups in flight in registers while it
-// computes on the current one.  Waves merge through LDS in a fixed order, and a
-// combine kernel merges the chunks of a request (log-sum-exp rescaling, fixed
-// order).
+// Work split, decided on the device from the actual context lengths (no host
+// sync).  A segment is one (request, kv head, q-row part); its keys form
+// ceil(C/32) cache groups of 32 keys plus one group holding the block's own
+// R <= 32 keys.  Each segment is cut into chunks of cg = max(chunk_min,
+// ceil(groups / chunk_max)) groups; a chunk's partial result (unnormalised O,
+// running max, sum) depends on that request alone, so results do not depend on
+// the rest of the batch.  The groups of all segments are laid end to end and
+// cut into equal ranges, each snapped forward to a chunk start, one range per
+// work-group, so every work-group streams about the same number of bytes
+// whatever the mix of context lengths.  A combine kernel merges the chunks of
+// each segment in order.
+//
+// Inside a work-group, one wave per 16-row query tile.  K and V are stored in
+// 32-key blocks in MFMA operand order (kv_layout.h) and copied straight into a
+// ring of LDS stages; scores are computed transposed, S^T = K Q^T, so that the
+// softmax probabilities land in registers as the B operand of O^T = V^T P^T.
 #pragma once
 #include "common.h"
 #include "kv_layout.h"
@@ -21,8 +26,9 @@
 namespace dfl {
 
 struct AttnPlan {          // written by attn_plan_kernel
-  int32_t count;           // number of work items
-  int32_t ck;              // chunk size (keys)
+  int32_t total;           // 32-key groups over all segments
+  int32_t per_wg;          // groups per work-group range
+  int32_t n_wg;            // work-groups with a non-empty range
 };
 
 struct AttnArgs {
@@ -34,20 +40,29 @@ struct AttnArgs {
   const int32_t* slots;
   const int32_t* ctx_len;
   const AttnPlan* plan;
-  const int4* items;       // (req, key_begin, key_end, is_last)
-  float* o_part;           // [item][n_kv][splits][QRT*16][D]
-  float* m_part;           // [item][n_kv][splits][QRT*16]
-  float* l_part;
-  int n_kv, R, Rpad, QRpad, rows_per_split, splits;
+  const int32_t* seg_start;   // [n_seg + 1] first group of each segment (segment s = (r*n_kv + kv)*splits + z)
+  const int32_t* chunk_base;  // [n_seg] first partial-result record (chunk) of each segment
+  float* o_part;              // [chunk][QRT*16][D]
+  float* m_part;              // [chunk][QRT*16]   running max (exp2 domain)
+  float* l_part;              // [chunk][QRT*16]   sum of exp2(s - m)
+  int n_seg, n_kv, R, Rpad, QRpad, rows_per_split, splits;
+  int chunk_min, chunk_max;   // chunk size rule (groups), see above
   int64_t ctx_alloc;
   float scale_log2;        // log2(e) / sqrt(D)
 };
 
 struct AttnCombineArgs {
   const float* o_part; const float* m_part; const float* l_part;
-  const int32_t* first_item; const int32_t* n_items;
+  const int32_t* seg_start; const int32_t* chunk_base;
   void* out;               // [n_req*R][q_dim] activations (T)
   int n_kv, group, R, rows_per_split, splits, QRT16, q_dim, D;
+  int chunk_min, chunk_max;
 };
+
+// groups per chunk of a segment of `len` groups
+__host__ __device__ __forceinline__ int attn_chunk_groups(int len, int chunk_min, int chunk_max) {
+  const int c = (len + chunk_max - 1) / chunk_max;
+  return c > chunk_min ? c : chunk_min;
+}
 
 }  // namespace dfl

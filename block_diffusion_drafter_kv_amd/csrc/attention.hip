@@ -1,55 +1,72 @@
-// Block attention kernels: work plan, split-context attention, chunk combine.
+// Block attention kernels: balanced work plan, streamed attention, partial combine.
+#include <type_traits>
+
 #include "attention.h"
-#include "ops.h"
 #include "lds_dma.h"
+#include "ops.h"
 
 namespace dfl {
 
 // ---------------------------------------------------------------------------
-// Plan: choose the chunk size from the real context lengths and list the work
-// items (request, first key, end key, last-chunk flag).  One work-group.
+// Plan (one work-group): group counts per segment -> seg_start (exclusive scan),
+// the equal range length per_wg, and the first partial record (chunk) of each
+// segment.
 // ---------------------------------------------------------------------------
+__device__ int block_exclusive_scan(int v, int* buf, int* carry) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  const int excl = *carry + buf[tid] - v;
+  __syncthreads();
+  if (tid == 255) *carry += buf[255];
+  __syncthreads();
+  return excl;
+}
+
 __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* slots, const int32_t* ctx_len, int n_req,
-                                                         int n_kv, int splits, int target_wg, int item_cap,
-                                                         AttnPlan* plan, int4* items, int32_t* first_item,
-                                                         int32_t* n_items, int32_t* err) {
-  __shared__ long long s_total;
-  __shared__ int s_ck;
-  if (threadIdx.x == 0) s_total = 0;
+                                                         int n_kv, int splits, int n_wg_max, int min_per_wg,
+                                                         int chunk_min, int chunk_max, AttnPlan* plan,
+                                                         int32_t* seg_start, int32_t* chunk_base) {
+  __shared__ int buf[256];
+  __shared__ int carry;
+  const int tid = threadIdx.x;
+  const int per_req = n_kv * splits, n_seg = n_req * per_req;
+  if (tid == 0) carry = 0;
   __syncthreads();
-  long long part = 0;
-  for (int r = threadIdx.x; r < n_req; r += blockDim.x) part += ctx_len[slots[r]];
-  atomicAdd((unsigned long long*)&s_total, (unsigned long long)part);
+  for (int b = 0; b < n_seg; b += 256) {
+    const int s = b + tid;
+    int cnt = 0;
+    if (s < n_seg) cnt = (ctx_len[slots[s / per_req]] + KV_BLOCK - 1) / KV_BLOCK + 1;
+    const int st = block_exclusive_scan(cnt, buf, &carry);
+    if (s < n_seg) seg_start[s] = st;
+  }
+  const int total = carry;
+  const int per_wg = max(min_per_wg, (total + n_wg_max - 1) / max(n_wg_max, 1));
   __syncthreads();
-  if (threadIdx.x == 0) {
-    long long want = (s_total * n_kv * splits + target_wg - 1) / target_wg;
-    long long ck = ((want + 127) / 128) * 128;
-    if (ck < 256) ck = 256;
-    s_ck = (int)ck;
-    int pos = 0;
-    for (int r = 0; r < n_req; ++r) {
-      const int C = ctx_len[slots[r]];
-      const int n = C > 0 ? (C + (int)ck - 1) / (int)ck : 1;
-      first_item[r] = pos;
-      n_items[r] = n;
-      pos += n;
-    }
-    if (pos > item_cap) {  // cannot happen with the host-side capacity; keep the grid safe
-      raise_error(err, ERR_ROWS);
-      pos = item_cap;
-    }
-    plan->count = pos;
-    plan->ck = (int)ck;
+  if (tid == 0) {
+    seg_start[n_seg] = total;
+    plan->total = total;
+    plan->per_wg = per_wg;
+    plan->n_wg = (total + per_wg - 1) / per_wg;
+    carry = 0;
   }
   __syncthreads();
-  const int ck = s_ck;
-  for (int r = threadIdx.x; r < n_req; r += blockDim.x) {
-    const int C = ctx_len[slots[r]];
-    const int f = first_item[r], n = n_items[r];
-    for (int c = 0; c < n; ++c) {
-      if (f + c >= item_cap) break;
-      items[f + c] = make_int4(r, c * ck, min(C, (c + 1) * ck), c == n - 1 ? 1 : 0);
+  for (int b = 0; b < n_seg; b += 256) {
+    const int s = b + tid;
+    int cnt = 0;
+    if (s < n_seg) {
+      const int len = seg_start[s + 1] - seg_start[s];
+      const int cg = attn_chunk_groups(len, chunk_min, chunk_max);
+      cnt = (len + cg - 1) / cg;
     }
+    const int cb = block_exclusive_scan(cnt, buf, &carry);
+    if (s < n_seg) chunk_base[s] = cb;
   }
 }
 
@@ -65,67 +82,121 @@ __device__ __forceinline__ typename Frag<T>::type load_frag8(const T* p) {
   return f;
 }
 
-// One work-group = (work item, kv head, q-row part) with one wave per 16-row
-// query tile.  The item's keys [kbeg, kend) (and, for a request's last item, the
-// block's own R keys) are streamed in 32-key groups through a ring of S LDS
-// stages by direct global->LDS copies; every wave reads each group from LDS and
-// runs its own online softmax over all of the item's keys, so no cross-wave
-// merge is needed.  Per group: S^T (32 x 16) = K Q^T, scale, mask, softmax
-// update, O^T += V^T P^T.  Copies run S - 1 groups ahead; a group is published
-// by the copying waves' vmcnt wait plus a barrier, which also retires the stage
-// that the next copy overwrites.
+// s_waitcnt vmcnt(allowed * PER), allowed clamped to [0, MAXA] (a smaller count only waits longer)
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_groups(int allowed) {
+  if constexpr (MAXA > 0) {
+    if (allowed >= MAXA) {
+      wait_vmcnt<MAXA * PER>();
+      return;
+    }
+    wait_groups<PER, MAXA - 1>(allowed);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// One segment (request r, kv head, q-row part z) as seen by a work-group.
+template <typename T>
+struct AttnSeg {
+  const T* kc;   // cache K of (slot, head), group 0
+  const T* vc;
+  const T* kb;   // the block's own K / V group
+  const T* vb;
+  int start, len, ncache, C, cg;   // cg: groups per chunk
+  int64_t qrow;  // this lane's query row in qb (in rows of D elements)
+};
+
+// Streamed attention.  Work-group w takes the chunks that start in groups
+// [w*per_wg, (w+1)*per_wg) of the global group order; one wave per 16-row query
+// tile of the segment's rows.
+// Copying waves move each group (K block then V block, 1 KB per wave copy) into
+// a ring of S LDS stages, S - 2 groups ahead of the compute; a step computes one
+// or two groups of the same segment after the copying waves' vmcnt wait and a
+// barrier, which also retires the stages the next copies overwrite.
 //
-// The running maximum is raised lazily: probabilities are taken relative to a
-// reference m_ref, which only moves (rescaling O and l) when a score exceeds it
-// by more than 2^8 in the exp2 domain; the result is unchanged up to rounding
-// (bf16 rounding of P is relative, and P <= 256 stays far from overflow).
+// Per group and tile: S^T (32 x 16) = K Q^T (MFMA, K from LDS, Q in registers),
+// running max over the lane's 8 keys and the 4 lane groups, P = exp2(scale*s -
+// m) rounded to the operand type, O^T += V^T P^T.  The reference max moves
+// lazily: only when a score exceeds it by more than 8 in the exp2 domain are O
+// and l rescaled, so P <= 2^8; the result is the same up to rounding (rounding
+// of P is relative).  Keys past a segment's end are masked out of the scores
+// and their values zeroed (stale cache contents must not turn 0 * x into NaN).
+//
+// Register budget: three waves per SIMD (<= 168 VGPRs) so that two 5-wave
+// work-groups share a CU.
 template <typename T, int D, int QRT, int S>
-__global__ __launch_bounds__(QRT * 64) void attn_kernel(const AttnArgs a) {
-  constexpr int KS = D / 32, DT = D / 16;
+__global__ __launch_bounds__(QRT * 64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && QRT == 5 ? 3 : 1)))
+void attn_kernel(const AttnArgs a) {
+  constexpr int KS = D / 32, DT = D / 16, ROWS = QRT * 16;
   constexpr int BLK = KV_BLOCK * D;                        // elements of a K (or V) block
   constexpr int EPC = 16 / (int)sizeof(T);                 // elements per 16-byte copy
   constexpr int IPG = 2 * BLK / (64 * EPC);                // 1 KB wave copies per group (K, then V)
   constexpr int CW = QRT >= 4 ? 4 : (QRT >= 2 ? 2 : 1);    // waves that issue copies
   constexpr int PER = IPG / CW;                            // copies per copying wave per group
   constexpr int VOFF = IPG / 2 * 64;                       // first uint4 of the V block in a stage
-  constexpr float TAU = 8.f;                               // lazy-rescale threshold (log2 units)
-  static_assert(IPG % CW == 0 && (S - 2) * PER < 64 && S >= 2 && S <= 4, "copy split / vmcnt range");
+  constexpr int MAXA = (S - 1) * PER < 64 ? S - 1 : 63 / PER;  // groups a wait may leave in flight
+  static_assert(IPG % CW == 0 && PER < 64 && S >= 4 && S <= 8, "copy split / vmcnt range");
   typedef typename Frag<T>::type FragT;
   __shared__ uint4 ring[S][IPG * 64];
 
-  const int item = blockIdx.x, kv = blockIdx.y, z = blockIdx.z;
-  if (item >= a.plan->count) return;
-  const int4 it = a.items[item];
-  const int req = it.x, kbeg = it.y, kend = it.z, is_last = it.w;
-  const int slot = a.slots[req];
-
+  const int w = blockIdx.x;
+  const int per_wg = a.plan->per_wg, total = a.plan->total;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, r16 = lane & 15;
 
-  // this wave's 16 query rows as B-operand fragments (row r16, dims 32 s + 8 grp ..)
-  FragT qf[KS];
-  {
-    const T* qrow = (const T*)a.qb +
-                    ((int64_t)(req * a.n_kv + kv) * a.QRpad + (int64_t)z * a.rows_per_split + wave * 16 + r16) * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = load_frag8<T>(qrow + s * 32 + grp * 8);
-  }
-  wait_vmcnt<0>();
+  // segment holding group x: the last s with seg_start[s] <= x
+  auto find_seg = [&](int x) {
+    int lo = 0, hi = a.n_seg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.seg_start[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  // first chunk start at or after group x
+  auto chunk_start = [&](int x) {
+    if (x >= total) return total;
+    const int s = find_seg(x);
+    const int b = a.seg_start[s], e = a.seg_start[s + 1];
+    const int cg = attn_chunk_groups(e - b, a.chunk_min, a.chunk_max);
+    return min(e, b + (x - b + cg - 1) / cg * cg);
+  };
+  const int g0 = chunk_start(min(w * per_wg, total));
+  const int g1 = chunk_start(min((w + 1) * per_wg, total));
+  if (g0 >= g1) return;
 
-  const int ncache = (kend - kbeg + KV_BLOCK - 1) / KV_BLOCK;
-  const int ng = ncache + (is_last ? 1 : 0);
-  const int64_t head = (int64_t)slot * a.n_kv + kv;
-  const T* kc = (const T*)a.cache_k + head * a.ctx_alloc * D + (int64_t)kbeg * D;
-  const T* vc = (const T*)a.cache_v + head * a.ctx_alloc * D + (int64_t)kbeg * D;
-  const int64_t bh = (int64_t)req * a.n_kv + kv;
-  const T* kblk = (const T*)a.kb + bh * a.Rpad * D;
-  const T* vblk = (const T*)a.vb + bh * a.Rpad * D;
+  auto decode = [&](int s, AttnSeg<T>& d) {
+    const int per_req = a.n_kv * a.splits;
+    const int r = s / per_req, rem = s - r * per_req, kv = rem / a.splits, z = rem - kv * a.splits;
+    const int slot = a.slots[r];
+    d.C = a.ctx_len[slot];
+    d.ncache = (d.C + KV_BLOCK - 1) / KV_BLOCK;
+    d.start = a.seg_start[s];
+    d.len = a.seg_start[s + 1] - d.start;
+    d.cg = attn_chunk_groups(d.len, a.chunk_min, a.chunk_max);
+    const int64_t head = (int64_t)slot * a.n_kv + kv;
+    d.kc = (const T*)a.cache_k + head * a.ctx_alloc * D;
+    d.vc = (const T*)a.cache_v + head * a.ctx_alloc * D;
+    const int64_t bh = (int64_t)r * a.n_kv + kv;
+    d.kb = (const T*)a.kb + bh * a.Rpad * D;
+    d.vb = (const T*)a.vb + bh * a.Rpad * D;
+    d.qrow = bh * a.QRpad + (int64_t)z * a.rows_per_split + wave * 16 + r16;
+  };
 
-  auto issue = [&](int gi, int st) {
+  const int s0 = find_seg(g0);
+
+  // copy cursor
+  AttnSeg<T> is;
+  decode(s0, is);
+  int is_s = s0, is_l = g0 - is.start, issued = g0, is_stage = 0;
+  auto issue = [&]() {
     if (wave < CW) {
-      const bool in_cache = gi < ncache;
-      const T* kp = (in_cache ? kc + (int64_t)gi * BLK : kblk) + lane * EPC;
-      const T* vp = (in_cache ? vc + (int64_t)gi * BLK : vblk) + lane * EPC;
+      const int st = is_stage;
+      const bool in_cache = is_l < is.ncache;
+      const T* kp = (in_cache ? is.kc + (int64_t)is_l * BLK : is.kb) + lane * EPC;
+      const T* vp = (in_cache ? is.vc + (int64_t)is_l * BLK : is.vb) + lane * EPC;
 #pragma unroll
       for (int c = 0; c < PER; ++c) {
         const int i = wave * PER + c;
@@ -133,12 +204,37 @@ __global__ __launch_bounds__(QRT * 64) void attn_kernel(const AttnArgs a) {
         copy16_to_lds(src, &ring[st][i * 64]);
       }
     }
+    ++issued;
+    if (++is_stage == S) is_stage = 0;
+    if (++is_l == is.len && issued < g1) {
+      ++is_s;
+      decode(is_s, is);
+      is_l = 0;
+    }
   };
 
-  f32x4 acc[DT];
+  // compute cursor
+  AttnSeg<T> cs = is;
+  int cs_s = s0, cl = g0 - cs.start;
+  FragT qf[KS];
+  auto load_q = [&]() {
+    const T* q = (const T*)a.qb + cs.qrow * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_sum = 0.f;
+    for (int s = 0; s < KS; ++s) qf[s] = load_frag8<T>(q + s * 32 + grp * 8);
+  };
+  load_q();
+
+  f32x4 acc[DT];
+  const float c = a.scale_log2, thr = 8.f / a.scale_log2;
+  float m_ref, nmc, l_sum;
+  auto reset = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref = -INFINITY;
+    nmc = 0.f;
+    l_sum = 0.f;
+  };
+  reset();
 
   auto frag_at = [&](const uint4* stage, int f) {  // fragment f (in 64-lane units) of this lane
     FragT x;
@@ -151,84 +247,133 @@ __global__ __launch_bounds__(QRT * 64) void attn_kernel(const AttnArgs a) {
     return x;
   };
 
-  auto compute = [&](const uint4* stage, int gi) {
-    const int nvalid = gi < ncache ? min(KV_BLOCK, kend - kbeg - KV_BLOCK * gi) : a.R;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](auto ngc, int stage) {
+    constexpr int NG = decltype(ngc)::value;
+    const uint4* st[NG];
+    int nval[NG];
+    f32x4 sc[NG][2];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      Frag<T>::mma(s0, frag_at(stage, s), qf[s]);
-      Frag<T>::mma(s1, frag_at(stage, KS + s), qf[s]);
+    for (int g = 0; g < NG; ++g) {
+      st[g] = ring[stage + g < S ? stage + g : stage + g - S];
+      const int lg = cl + g;
+      nval[g] = lg < cs.ncache ? min(KV_BLOCK, cs.C - KV_BLOCK * lg) : a.R;
+      sc[g][0] = sc[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // lane holds keys 8*grp + i (s0) and 8*grp + 4 + i (s1) of this group for query row r16
-    float sv[8];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        Frag<T>::mma(sc[g][0], frag_at(st[g], s), qf[s]);
+        Frag<T>::mma(sc[g][1], frag_at(st[g], KS + s), qf[s]);
+      }
+    // lane holds keys 8*grp + i (sc[.][0]) and 8*grp + 4 + i (sc[.][1]) of each group, query row r16
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      if (nval[g] < KV_BLOCK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (8 * grp + i >= nval[g]) sc[g][0][i] = -INFINITY;
+          if (8 * grp + 4 + i >= nval[g]) sc[g][1][i] = -INFINITY;
+        }
+      }
+    // lane-local max; the row max over the 4 lane groups is only formed when some
+    // score passes the reference by more than the threshold (the rare rescale)
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k0 = 8 * grp + i;
-      sv[i] = k0 < nvalid ? s0[i] * a.scale_log2 : -INFINITY;
-      sv[4 + i] = k0 + 4 < nvalid ? s1[i] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (__any(mx > m_ref + TAU)) {
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(sc[g][0][i], sc[g][1][i]));
+    if (__any(mx > m_ref + thr)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mnew = fmaxf(m_ref, mx);
-      const float alpha = mnew > m_ref ? exp2f(m_ref - mnew) : 1.f;
+      const float alpha = mnew > m_ref ? __builtin_amdgcn_exp2f((m_ref - mnew) * c) : 1.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
       l_sum *= alpha;
       m_ref = mnew;
+      nmc = -mnew * c;
     }
-    FragT pf;
+    FragT pf[NG];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = exp2f(sv[e] - m_ref);
-      l_sum += p;
-      pf[e] = (T)p;
-    }
-    const uint4* vst = stage + VOFF;
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      FragT vf = frag_at(vst, dt);
-      if (nvalid < KV_BLOCK) {  // keys past the end hold stale or unwritten data
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (grp * 8 + e >= nvalid) vf[e] = (T)0.f;
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[g][t][i], c, nmc));
+          l_sum += p;
+          pf[g][4 * t + i] = (T)p;
+        }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      FragT vf[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vf[dt] = frag_at(st[g] + VOFF, dt);
+      if (nval[g] < KV_BLOCK) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (grp * 8 + e >= nval[g]) vf[dt][e] = (T)0.f;
       }
-      Frag<T>::mma(acc[dt], vf, pf);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) Frag<T>::mma(acc[dt], vf[dt], pf[g]);
     }
   };
 
-  for (int p = 0; p < S - 1 && p < ng; ++p) issue(p, p);
-  for (int gi = 0; gi < ng; ++gi) {
-    if (wave < CW) {
-      const int ahead = min(S - 2, ng - 1 - gi);  // groups issued after gi that may stay in flight
-      if (S >= 4 && ahead >= 2) wait_vmcnt<(S >= 4 ? 2 * PER : 0)>();
-      else if (S >= 3 && ahead >= 1) wait_vmcnt<(S >= 3 ? PER : 0)>();
-      else wait_vmcnt<0>();
-    }
-    lds_barrier();
-    if (gi + S - 1 < ng) issue(gi + S - 1, (gi + S - 1) % S);
-    compute(ring[gi % S], gi);
-  }
-
-  // partial result of this item: O (unnormalised, relative to m_ref), m_ref, l
-  l_sum += __shfl_xor(l_sum, 16, 64);
-  l_sum += __shfl_xor(l_sum, 32, 64);
-  const int row = wave * 16 + r16;
-  const int64_t base = ((int64_t)item * a.n_kv + kv) * a.splits + z;
-  float* op = a.o_part + (base * (QRT * 16) + row) * D + 4 * grp;
+  // partial record of chunk `ck` of segment cs_s: O rows of this wave, max (exp2 domain), sum
+  auto flush = [&](int ck) {
+    float l = l_sum;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int64_t piece = a.chunk_base[cs_s] + ck;
+    const int row = wave * 16 + r16;
+    if (row >= a.rows_per_split) return;  // padding rows of the last tile are never combined
+    float* op = a.o_part + (piece * ROWS + row) * D + 4 * grp;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + dt * 16) = acc[dt];
-  if (grp == 0) {
-    a.m_part[base * (QRT * 16) + row] = m_ref;
-    a.l_part[base * (QRT * 16) + row] = l_sum;
+    for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + dt * 16) = acc[dt];
+    if (grp == 0) {
+      a.m_part[piece * ROWS + row] = m_ref * c;
+      a.l_part[piece * ROWS + row] = l;
+    }
+  };
+
+  while (issued < min(g1, g0 + S - 2)) issue();
+  int stage = 0;                                   // ring stage of group gi
+  int ck = cl / cs.cg;                             // chunk being computed (segment-local index)
+  int cend = min(cs.len, (ck + 1) * cs.cg);        // its end (segment-local group)
+  for (int gi = g0; gi < g1;) {
+    const int n = cl + 1 < cend ? 2 : 1;
+    if (wave < CW) wait_groups<PER, MAXA>(issued - (gi + n));
+    lds_barrier();
+    while (issued < min(g1, gi + S)) issue();
+    if (n == 2) compute(std::integral_constant<int, 2>{}, stage);
+    else compute(std::integral_constant<int, 1>{}, stage);
+    stage += n;
+    if (stage >= S) stage -= S;
+    gi += n;
+    cl += n;
+    if (cl == cend) {  // chunk done (ranges end on chunk starts, so never mid-chunk)
+      flush(ck);
+      reset();
+      ++ck;
+      cend = min(cs.len, cend + cs.cg);
+    }
+    if (cl == cs.len && gi < g1) {  // next segment: its pointers and query rows
+      ++cs_s;
+      decode(cs_s, cs);
+      cl = 0;
+      ck = 0;
+      cend = min(cs.len, cs.cg);
+      load_q();
+    }
   }
 }
 
-// One work-group per (request, kv head and q-row half, block of 16 rows): each
-// thread owns one row and D/16 consecutive head dims and merges the request's
-// chunks in chunk order (max first, then the rescaled sums).
+// One work-group per (request, kv head and q-row part, block of 16 rows): each
+// thread owns one row and D/16 consecutive head dims and merges the segment's
+// chunk records in order (max first, then the rescaled sums).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs a) {
   constexpr int EPT = D / 16;
@@ -237,29 +382,31 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs
   const int row = blockIdx.z * 16 + (threadIdx.x >> 4);
   const int e0 = (threadIdx.x & 15) * EPT;
   if (row >= a.rows_per_split) return;
-  const int f = a.first_item[req], n = a.n_items[req];
-  const int64_t stride_item = (int64_t)a.n_kv * a.splits;         // partial blocks per item
-  const int64_t b0 = ((int64_t)f * a.n_kv + kv) * a.splits + z;
+  const int seg = (req * a.n_kv + kv) * a.splits + z;
+  const int len = a.seg_start[seg + 1] - a.seg_start[seg];
+  const int cg = attn_chunk_groups(len, a.chunk_min, a.chunk_max);
+  const int n = (len + cg - 1) / cg;
+  const int64_t p0 = a.chunk_base[seg];
   float M = -INFINITY;
-  for (int c = 0; c < n; ++c) M = fmaxf(M, a.m_part[(b0 + c * stride_item) * a.QRT16 + row]);
+  for (int c = 0; c < n; ++c) M = fmaxf(M, a.m_part[(p0 + c) * a.QRT16 + row]);
   float L = 0.f;
   float O[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; ++i) O[i] = 0.f;
   for (int c = 0; c < n; ++c) {
-    const int64_t b = b0 + c * stride_item;
+    const int64_t b = p0 + c;
     const float m = a.m_part[b * a.QRT16 + row];
     if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
-    L += a.l_part[b * a.QRT16 + row] * w;
+    const float wgt = exp2f(m - M);
+    L += a.l_part[b * a.QRT16 + row] * wgt;
     const float4* op = (const float4*)(a.o_part + (b * a.QRT16 + row) * D + e0);
 #pragma unroll
     for (int i = 0; i < EPT / 4; ++i) {
       const float4 v = op[i];
-      O[4 * i] += v.x * w;
-      O[4 * i + 1] += v.y * w;
-      O[4 * i + 2] += v.z * w;
-      O[4 * i + 3] += v.w * w;
+      O[4 * i] += v.x * wgt;
+      O[4 * i + 1] += v.y * wgt;
+      O[4 * i + 2] += v.z * wgt;
+      O[4 * i + 3] += v.w * wgt;
     }
   }
   const float inv = 1.0f / L;
@@ -273,8 +420,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs
 
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-static void launch_attn_t(const AttnArgs& a, int qrt, dim3 grid, hipStream_t s) {
-  constexpr int S = (sizeof(T) == 4 && D == 128) ? 3 : 4;  // LDS ring stages (16 or 32 KB each)
+static void launch_attn_t(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
+  constexpr int S = (sizeof(T) == 4 && D == 128) ? 4 : 5;  // LDS ring stages (16 or 32 KB each)
   switch (qrt) {
     case 1: attn_kernel<T, D, 1, S><<<grid, 64, 0, s>>>(a); break;
     case 2: attn_kernel<T, D, 2, S><<<grid, 128, 0, s>>>(a); break;
@@ -284,14 +431,14 @@ static void launch_attn_t(const AttnArgs& a, int qrt, dim3 grid, hipStream_t s) 
   }
 }
 
-void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, int n_kv, int splits, int target_wg,
-                      int item_cap, AttnPlan* plan, int4* items, int32_t* first_item, int32_t* n_items, int32_t* err,
-                      hipStream_t s) {
-  attn_plan_kernel<<<1, 256, 0, s>>>(slots, ctx_len, n_req, n_kv, splits, target_wg, item_cap, plan, items,
-                                      first_item, n_items, err);
+void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, int n_kv, int splits, int n_wg_max,
+                      int min_per_wg, int chunk_min, int chunk_max, AttnPlan* plan, int32_t* seg_start,
+                      int32_t* chunk_base, hipStream_t s) {
+  attn_plan_kernel<<<1, 256, 0, s>>>(slots, ctx_len, n_req, n_kv, splits, n_wg_max, min_per_wg, chunk_min, chunk_max,
+                                      plan, seg_start, chunk_base);
 }
 
-void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, dim3 grid, hipStream_t s) {
+void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStream_t s) {
   if (dtype == DT_BF16) {
     if (D == 128) launch_attn_t<bf16_t, 128>(a, qrt, grid, s);
     else launch_attn_t<bf16_t, 64>(a, qrt, grid, s);

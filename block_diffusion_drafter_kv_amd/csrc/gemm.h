@@ -254,14 +254,38 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const GemmArgs g, cons
   for (int pass = 0; pass < BM / EPI_ROWS; ++pass) {
     const int m0 = m_base + pass * EPI_ROWS;
     if (m0 >= g.M) break;
-    for (int idx = tid; idx < EPI_ROWS * BN; idx += 256) {
-      const int r = idx / BN, c = idx % BN;
-      float s = 0.f;
-      if (m0 + r < g.M) {
-        const float* P = g.partials + (int64_t)(m0 + r) * g.Npad + n_base + c;
-        for (int sp = 0; sp < g.splits; ++sp) s += P[(int64_t)sp * g.Mpad * g.Npad];
+    // 16-byte loads, all of one split in flight at once; sums taken in split order
+    constexpr int C4 = BN / 4, NV = EPI_ROWS * C4 / 256;
+    static_assert(EPI_ROWS * C4 % 256 == 0, "reduce tiling");
+    const int64_t split_stride = (int64_t)g.Mpad * g.Npad;
+    float4 acc[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < g.splits; ++sp) {
+      float4 v[NV];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int idx = tid + j * 256, r = idx / C4, c4 = idx % C4;
+        v[j] = m0 + r < g.M ? *(const float4*)(g.partials + sp * split_stride + (int64_t)(m0 + r) * g.Npad + n_base +
+                                               4 * c4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      stage[r * (BN + 1) + c] = s;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        acc[j].x += v[j].x;
+        acc[j].y += v[j].y;
+        acc[j].z += v[j].z;
+        acc[j].w += v[j].w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int idx = tid + j * 256, r = idx / C4, c4 = idx % C4;
+      float* d = stage + r * (BN + 1) + 4 * c4;
+      d[0] = acc[j].x;
+      d[1] = acc[j].y;
+      d[2] = acc[j].z;
+      d[3] = acc[j].w;
     }
     __syncthreads();
     Epi::template apply<BN, EPI_ROWS>(ep, stage, BN + 1, m0, n_base, g.M, g.N, tn, tid);

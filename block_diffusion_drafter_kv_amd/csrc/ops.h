@@ -26,10 +26,12 @@ void launch_gemm(int dtype, EpiKind kind, GemmArgs g, const void* epi_params, co
                  float* partials, size_t partials_elems, hipStream_t s);
 
 // ---- attention (attention.hip) ----
-void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, int n_kv, int splits, int target_wg,
-                      int item_cap, AttnPlan* plan, int4* items, int32_t* first_item, int32_t* n_items, int32_t* err,
-                      hipStream_t s);
-void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, dim3 grid, hipStream_t s);
+// attention work plan: per-segment group starts, equal group ranges for up to
+// n_wg_max work-groups (at least min_per_wg groups each), per-segment chunk bases
+void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, int n_kv, int splits, int n_wg_max,
+                      int min_per_wg, int chunk_min, int chunk_max, AttnPlan* plan, int32_t* seg_start,
+                      int32_t* chunk_base, hipStream_t s);
+void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStream_t s);
 void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, hipStream_t s);
 
 // ---- elementwise / row kernels (kernels.hip) ----
