@@ -137,6 +137,14 @@ int check_config(const dflash_config& c) {
   if (c.max_k > 31) return DFLASH_E_UNSUPPORTED;
   if (c.max_top_k > 256 || c.max_tree > 256) return DFLASH_E_UNSUPPORTED;
   if ((int64_t)c.max_batch * (c.max_k + 1) > (1 << 20)) return DFLASH_E_UNSUPPORTED;
+  // the bf16 GEMM addresses each operand with 32-bit byte offsets from a base
+  const int64_t es = c.dtype == DFLASH_BF16 ? 2 : 4, lim = (int64_t)1 << 32;
+  const int64_t widest = std::max<int64_t>(c.ffn, std::max<int64_t>(c.hidden, (int64_t)c.n_q_heads * c.head_dim));
+  if ((int64_t)c.vocab * c.hidden * es >= lim || (int64_t)c.ffn * c.hidden * es >= lim ||
+      (int64_t)c.hidden * c.n_target_layers * c.target_hidden * es >= lim ||
+      (int64_t)c.n_q_heads * c.head_dim * c.hidden * es >= lim ||
+      (int64_t)c.max_batch * (c.max_k + 1) * widest * es >= lim)
+    return DFLASH_E_UNSUPPORTED;
   return DFLASH_OK;
 }
 
@@ -349,8 +357,10 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
     Phase ph(h, s, DFLASH_PH_INJECT_PREP);
     launch_inject_scan(n_req, slots, row_start, row_count, h->ctx_len, c.max_ctx, c.max_batch, rows_upper_bound,
                        h->req_off, h->req_pos, h->err, s);
-    launch_inject_fill(n_req, rows_upper_bound, slots, row_start, h->req_off, h->req_pos, h->a_rows, h->row_slot,
-                       h->row_pos, s);
+    // rows are addressed with 32-bit byte offsets from each layer's base pointer
+    const int64_t max_row = (((int64_t)1 << 32) - (int64_t)c.target_hidden * h->esize) / (row_stride * h->esize);
+    launch_inject_fill(n_req, rows_upper_bound, slots, row_start, h->req_off, h->req_pos, max_row, h->a_rows,
+                       h->row_slot, h->row_pos, h->err, s);
   }
   const int featK = c.n_target_layers * c.target_hidden;
   for (int64_t c0 = 0; c0 < rows_upper_bound; c0 += h->inject_chunk) {

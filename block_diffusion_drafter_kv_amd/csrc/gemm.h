@@ -28,7 +28,7 @@ static constexpr int MAX_BSEG = 16;
 struct GemmArgs {
   int M, N, K;
   const void* a_ptr[MAX_ASEG];
-  int64_t a_ld[MAX_ASEG];
+  int64_t a_ld[MAX_ASEG];       // the bf16 kernel requires one stride for all segments (a_ld[0])
   int a_nseg, a_segk;          // K = a_nseg * a_segk; segment s covers k in [s*a_segk, (s+1)*a_segk)
   const int32_t* a_rows;       // optional gather: source row for output row m (<0: zero row)
   const int32_t* m_valid;      // optional device row count: tiles at or past (*m_valid - m_valid_base) exit

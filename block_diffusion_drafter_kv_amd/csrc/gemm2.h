@@ -33,7 +33,8 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
 
   __shared__ uint4 smem[STAGES][SLOTS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int wm = wave & 1, wn = wave >> 1;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = logical % g.tiles_m, tn = logical / g.tiles_m;
@@ -44,10 +45,13 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
   const int k_end = min(g.K, k_begin + g.k_per_split);
   const int nk = max(0, (k_end - k_begin) / BK);
 
-  // this thread's copy slots: rows (i*32 + tid/8) of A and B, logical chunk cchunk
+  // this thread's copy slots: rows (i*32 + tid/8) of A and B, logical chunk cchunk.
+  // Every copy instruction of a wave covers 8 consecutive rows of one operand, so
+  // it takes a wave-uniform base (SGPRs) plus a per-lane 32-bit byte offset that
+  // stays fixed for the whole K loop; only the bases advance per slab.
   const int crow = tid >> 3;
   const int cchunk = (tid & 7) ^ (crow & 7);
-  int64_t a_src[NA];
+  uint32_t a_off[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int m = m_base + i * 32 + crow;
@@ -56,25 +60,34 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
       s = g.a_rows ? g.a_rows[m] : m;
       if (s < 0) s = 0;
     }
-    a_src[i] = s;
+    a_off[i] = (uint32_t)(s * g.a_ld[0] * (int64_t)sizeof(T)) + cchunk * 16;
   }
-  const T* b_src[NB];
+  const char* b_base[NB];
+  uint32_t b_off[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const T* p = b_row_ptr<T, BN>(g, n_base + j * 32 + crow);
-    b_src[j] = p ? p : (const T*)g.b_ptr[0];
+    const int r0 = n_base + j * 32 + wave * 8;          // first row of this wave's block (uniform)
+    const T* p0 = b_row_ptr<T, BN>(g, r0);
+    const bool valid = p0 && r0 + (lane >> 3) < g.N;    // blocks never straddle a segment boundary
+    b_base[j] = (const char*)(p0 ? p0 : (const T*)g.b_ptr[0]);
+    b_off[j] = (uint32_t)((valid ? (lane >> 3) : 0) * g.b_ld * (int64_t)sizeof(T)) + cchunk * 16;
   }
 
+  // A-segment cursor of the next slab to issue (slabs are issued in K order)
+  int a_seg = k_begin / g.a_segk, a_kk = k_begin - a_seg * g.a_segk;
   auto issue = [&](int kt, uint4* dst) {
     const int k0 = k_begin + kt * BK;
-    const int seg = k0 / g.a_segk;
-    const T* abase = (const T*)g.a_ptr[seg];
-    const int64_t ald = g.a_ld[seg];
-    const int kk = k0 - seg * g.a_segk + cchunk * 8;
+    const char* abase = (const char*)g.a_ptr[a_seg] + (int64_t)a_kk * sizeof(T);
 #pragma unroll
-    for (int i = 0; i < NA; ++i) copy16_to_lds(abase + a_src[i] * ald + kk, dst + i * 256 + wave * 64);
+    for (int i = 0; i < NA; ++i) copy16_to_lds_sv(abase, a_off[i], dst + i * 256 + wave * 64);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) copy16_to_lds(b_src[j] + k0 + cchunk * 8, dst + (NA + j) * 256 + wave * 64);
+    for (int j = 0; j < NB; ++j)
+      copy16_to_lds_sv(b_base[j] + (int64_t)k0 * sizeof(T), b_off[j], dst + (NA + j) * 256 + wave * 64);
+    a_kk += BK;
+    if (a_kk == g.a_segk) {
+      ++a_seg;
+      a_kk = 0;
+    }
   };
 
   f32x4 acc[FM][FN];

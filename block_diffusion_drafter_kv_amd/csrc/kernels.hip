@@ -139,8 +139,8 @@ __global__ void inject_scan_kernel(int n_req, const int32_t* slots, const int32_
 }
 
 __global__ void inject_fill_kernel(int n_req, int64_t rows_upper, const int32_t* slots, const int32_t* row_start,
-                                   const int32_t* req_off, const int32_t* req_pos, int32_t* a_rows,
-                                   int32_t* row_slot, int32_t* row_pos) {
+                                   const int32_t* req_off, const int32_t* req_pos, int64_t max_row, int32_t* a_rows,
+                                   int32_t* row_slot, int32_t* row_pos, int32_t* err) {
   const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (m >= rows_upper) return;
   if (m >= req_off[n_req]) {
@@ -158,7 +158,15 @@ __global__ void inject_fill_kernel(int n_req, int64_t rows_upper, const int32_t*
   // skip empty requests that share the same offset
   while (lo + 1 <= n_req - 1 && req_off[lo + 1] <= m) ++lo;
   const int i = (int)(m - req_off[lo]);
-  a_rows[m] = row_start[lo] + i;
+  const int64_t src = (int64_t)row_start[lo] + i;
+  if (src < 0 || src >= max_row) {  // not addressable: skip the row (its slot is left as it was)
+    raise_error(err, ERR_ROWS);
+    a_rows[m] = -1;
+    row_slot[m] = -1;
+    row_pos[m] = 0;
+    return;
+  }
+  a_rows[m] = (int32_t)src;
   row_slot[m] = slots[lo];
   row_pos[m] = req_pos[lo] + i;
 }
@@ -868,11 +876,11 @@ void launch_inject_scan(int n_req, const int32_t* slots, const int32_t* row_star
 }
 
 void launch_inject_fill(int n_req, int64_t rows_upper, const int32_t* slots, const int32_t* row_start,
-                        const int32_t* req_off, const int32_t* req_pos, int32_t* a_rows, int32_t* row_slot,
-                        int32_t* row_pos, hipStream_t s) {
+                        const int32_t* req_off, const int32_t* req_pos, int64_t max_row, int32_t* a_rows,
+                        int32_t* row_slot, int32_t* row_pos, int32_t* err, hipStream_t s) {
   if (rows_upper <= 0) return;
   inject_fill_kernel<<<cdiv(rows_upper, 256), 256, 0, s>>>(n_req, rows_upper, slots, row_start, req_off, req_pos,
-                                                           a_rows, row_slot, row_pos);
+                                                           max_row, a_rows, row_slot, row_pos, err);
 }
 
 void launch_row_finalize(int n_rows, int n_tiles, const float* tmax, const float* tsum, const int32_t* targ,

@@ -26,6 +26,19 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_wave_base
       : "memory");
 }
 
+// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte
+// offset (global_load_lds with saddr): no per-copy 64-bit address arithmetic.
+__device__ __forceinline__ void copy16_to_lds_sv(const void* sbase, uint32_t voff, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
 // s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

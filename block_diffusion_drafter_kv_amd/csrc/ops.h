@@ -46,9 +46,11 @@ void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, 
 void launch_inject_scan(int n_req, const int32_t* slots, const int32_t* row_start, const int32_t* row_count,
                         int32_t* ctx_len, int max_ctx, int max_batch, int64_t rows_upper, int32_t* req_off,
                         int32_t* req_pos, int32_t* err, hipStream_t s);
+// gemm row table of an injection; source rows at or past max_row (not addressable
+// with 32-bit byte offsets) are skipped and flag the error word
 void launch_inject_fill(int n_req, int64_t rows_upper, const int32_t* slots, const int32_t* row_start,
-                        const int32_t* req_off, const int32_t* req_pos, int32_t* a_rows, int32_t* row_slot,
-                        int32_t* row_pos, hipStream_t s);
+                        const int32_t* req_off, const int32_t* req_pos, int64_t max_row, int32_t* a_rows,
+                        int32_t* row_slot, int32_t* row_pos, int32_t* err, hipStream_t s);
 void launch_row_finalize(int n_rows, int n_tiles, const float* tmax, const float* tsum, const int32_t* targ,
                          float* row_max, float* row_lse, int32_t* argmax_out, float* out_row_max, float* out_row_lse,
                          hipStream_t s);
