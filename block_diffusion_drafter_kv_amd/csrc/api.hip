@@ -357,10 +357,9 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
     Phase ph(h, s, DFLASH_PH_INJECT_PREP);
     launch_inject_scan(n_req, slots, row_start, row_count, h->ctx_len, c.max_ctx, c.max_batch, rows_upper_bound,
                        h->req_off, h->req_pos, h->err, s);
-    // rows are addressed with 32-bit byte offsets from each layer's base pointer
-    const int64_t max_row = (((int64_t)1 << 32) - (int64_t)c.target_hidden * h->esize) / (row_stride * h->esize);
-    launch_inject_fill(n_req, rows_upper_bound, slots, row_start, h->req_off, h->req_pos, max_row, h->a_rows,
-                       h->row_slot, h->row_pos, h->err, s);
+    // source rows are int32 indices into the caller's buffers
+    launch_inject_fill(n_req, rows_upper_bound, slots, row_start, h->req_off, h->req_pos, (int64_t)INT32_MAX,
+                       h->a_rows, h->row_slot, h->row_pos, h->err, s);
   }
   const int featK = c.n_target_layers * c.target_hidden;
   for (int64_t c0 = 0; c0 < rows_upper_bound; c0 += h->inject_chunk) {
@@ -378,6 +377,7 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
     ga.a_nseg = c.n_target_layers;
     ga.a_segk = c.target_hidden;
     ga.a_rows = h->a_rows + c0;
+    ga.a_wide = 1;  // the caller's hidden-state buffers may exceed 4 GiB
     ga.m_valid = h->req_off + n_req;
     ga.m_valid_base = (int)c0;
     set_b(ga, {{h->fc, H}}, featK);

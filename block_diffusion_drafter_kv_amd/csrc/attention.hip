@@ -116,12 +116,14 @@ struct AttnSeg {
 // barrier, which also retires the stages the next copies overwrite.
 //
 // Per group and tile: S^T (32 x 16) = K Q^T (MFMA, K from LDS, Q in registers),
-// running max over the lane's 8 keys and the 4 lane groups, P = exp2(scale*s -
-// m) rounded to the operand type, O^T += V^T P^T.  The reference max moves
-// lazily: only when a score exceeds it by more than 8 in the exp2 domain are O
-// and l rescaled, so P <= 2^8; the result is the same up to rounding (rounding
-// of P is relative).  Keys past a segment's end are masked out of the scores
-// and their values zeroed (stale cache contents must not turn 0 * x into NaN).
+// P = exp2(scale*s - m) rounded to the operand type, O^T += V^T P^T, with l the
+// sum of the unrounded P.  The reference m is an integer in the exp2 domain and
+// moves lazily: only when a scaled score passes it by more than 8 is it raised
+// (to the ceiling of the row max) and O, l rescaled by an exact power of two, so
+// P <= 2^8 and the rounding of P to the operand type does not depend on where
+// the reference sits (a power-of-two shift leaves the significand alone).  Keys
+// past a segment's end are masked out of the scores and their values zeroed
+// (stale cache contents must not turn 0 * x into NaN).
 //
 // Register budget: three waves per SIMD (<= 168 VGPRs) so that two 5-wave
 // work-groups share a CU.
@@ -136,6 +138,7 @@ void attn_kernel(const AttnArgs a) {
   constexpr int PER = IPG / CW;                            // copies per copying wave per group
   constexpr int VOFF = IPG / 2 * 64;                       // first uint4 of the V block in a stage
   constexpr int MAXA = (S - 1) * PER < 64 ? S - 1 : 63 / PER;  // groups a wait may leave in flight
+  constexpr float TAU = 8.f;                               // lazy-rescale threshold (exp2 units)
   static_assert(IPG % CW == 0 && PER < 64 && S >= 4 && S <= 8, "copy split / vmcnt range");
   typedef typename Frag<T>::type FragT;
   __shared__ uint4 ring[S][IPG * 64];
@@ -225,13 +228,12 @@ void attn_kernel(const AttnArgs a) {
   load_q();
 
   f32x4 acc[DT];
-  const float c = a.scale_log2, thr = 8.f / a.scale_log2;
-  float m_ref, nmc, l_sum;
+  const float c = a.scale_log2;
+  float m_ref, l_sum;   // m_ref: integer reference in the exp2 domain of the scaled scores
   auto reset = [&]() {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_ref = -INFINITY;
-    nmc = 0.f;
     l_sum = 0.f;
   };
   reset();
@@ -283,16 +285,16 @@ void attn_kernel(const AttnArgs a) {
     for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(sc[g][0][i], sc[g][1][i]));
-    if (__any(mx > m_ref + thr)) {
+    mx *= c;
+    if (__any(mx > m_ref + TAU)) {
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m_ref, mx);
-      const float alpha = mnew > m_ref ? __builtin_amdgcn_exp2f((m_ref - mnew) * c) : 1.f;
+      const float mnew = fmaxf(m_ref, ceilf(mx));
+      const float alpha = mnew > m_ref ? __builtin_amdgcn_exp2f(m_ref - mnew) : 1.f;   // a power of two
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
       l_sum *= alpha;
       m_ref = mnew;
-      nmc = -mnew * c;
     }
     FragT pf[NG];
 #pragma unroll
@@ -301,7 +303,7 @@ void attn_kernel(const AttnArgs a) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[g][t][i], c, nmc));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[g][t][i], c, -m_ref));
           l_sum += p;
           pf[g][4 * t + i] = (T)p;
         }
@@ -334,7 +336,7 @@ void attn_kernel(const AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + dt * 16) = acc[dt];
     if (grp == 0) {
-      a.m_part[piece * ROWS + row] = m_ref * c;
+      a.m_part[piece * ROWS + row] = m_ref;
       a.l_part[piece * ROWS + row] = l;
     }
   };

@@ -38,6 +38,7 @@ struct GemmArgs {
   int b_nseg;
   int64_t b_ld;
   int b_interleave;            // 1: tile t's rows [0,BN/2) = gate rows t*BN/2.., [BN/2,BN) = up rows
+  int a_wide;                  // 1: A rows need 64-bit byte offsets (caller buffers of 4 GiB or more)
   int splits;
   int k_per_split;             // multiple of the K slab
   float* partials;             // [splits][Mpad][Npad]
@@ -49,8 +50,13 @@ template <typename T> struct GemmTraits;
 template <> struct GemmTraits<bf16_t> { static constexpr int BK = 64; static constexpr int VEC = 8; };
 template <> struct GemmTraits<float> { static constexpr int BK = 32; static constexpr int VEC = 4; };
 
+// Grid of a tiled product: rounded up to a multiple of the 8 XCDs so that the
+// remap below applies (work-groups past the tile count exit at once).
+__host__ __device__ __forceinline__ int gemm_grid(int tiles) { return (tiles + 7) & ~7; }
+
 __device__ __forceinline__ int xcd_remap(int b, int G) {
-  // consecutive logical tiles land on the same XCD (8 XCDs, round-robin dispatch)
+  // consecutive logical tiles land on the same XCD (8 XCDs, round-robin dispatch),
+  // so the row tiles that share a weight tile share that XCD's L2
   if ((G & 7) != 0) return b;
   return (b & 7) * (G >> 3) + (b >> 3);
 }
@@ -104,6 +110,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g, const typen
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  if (logical >= g.tiles_m * g.tiles_n) return;
   const int tm = logical % g.tiles_m, tn = logical / g.tiles_m;
   const int split = blockIdx.y;
   const int m_base = tm * BM, n_base = tn * BN;

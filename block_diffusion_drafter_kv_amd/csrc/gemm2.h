@@ -13,6 +13,7 @@
 // unit writes lane l of a wave to slot (wave base + l), so each lane fetches
 // the global chunk that belongs in its slot.
 #pragma once
+#include <type_traits>
 #include "gemm.h"
 #include "lds_dma.h"
 
@@ -20,23 +21,34 @@ namespace dfl {
 
 static constexpr int GEMM2_EPI_ROWS = 32;   // epilogue slab: 32 rows x (BN+1) fp32 fit one ring buffer
 
-template <int BM, int BN, int STAGES, class Epi>
+// SA / SB: ring depths of the A (activation) and B (weight) slabs.  Either both
+// rings have the same depth, or A is double-buffered and B runs deeper: weight
+// slabs come from HBM with a longer latency than the L2-resident activations.
+//
+// A64: A rows are addressed with per-lane 64-bit byte offsets (one 64-bit add per
+// copy) instead of 32-bit offsets from a wave-uniform base, for A buffers of
+// 4 GiB or more (the injection's caller-provided hidden states).
+template <int BM, int BN, int SA, int SB, class Epi, bool A64 = false>
 __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const typename Epi::Params ep) {
   typedef bf16_t T;
   constexpr int BK = 64;
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
-  constexpr int SLOTS = (BM + BN) * 8;
   constexpr int NA = BM * 8 / 256, NB = BN * 8 / 256, NL = NA + NB;
   constexpr int ER = GEMM2_EPI_ROWS;
-  static_assert(STAGES >= 2 && STAGES <= 4 && (STAGES - 2) * NL < 64, "stages / vmcnt range");
-  static_assert(ER * (BN + 1) * 4 <= STAGES * SLOTS * 16, "epilogue slab must fit the ring");
+  static_assert(SA >= 2 && SB >= 2 && SA <= 4 && SB <= 4 && (SA == SB || SA == 2), "ring depths");
+  static_assert((SA - 2) * NL < 64 && NB * (SB - 1) < 64, "vmcnt range");
+  static_assert(ER * (BN + 1) * 4 <= (SA * BM + SB * BN) * 8 * 16, "epilogue slab must fit the rings");
 
-  __shared__ uint4 smem[STAGES][SLOTS];
+  // one LDS block: A ring [SA][BM rows] then B ring [SB][BN rows], 8 chunks per row
+  __shared__ uint4 smem[(SA * BM + SB * BN) * 8];
+  auto smemA = [&](int st) { return smem + st * (BM * 8); };
+  auto smemB = [&](int st) { return smem + SA * BM * 8 + st * (BN * 8); };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int wm = wave & 1, wn = wave >> 1;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  if (logical >= g.tiles_m * g.tiles_n) return;
   const int tm = logical % g.tiles_m, tn = logical / g.tiles_m;
   const int split = blockIdx.y;
   const int m_base = tm * BM, n_base = tn * BN;
@@ -51,7 +63,8 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
   // stays fixed for the whole K loop; only the bases advance per slab.
   const int crow = tid >> 3;
   const int cchunk = (tid & 7) ^ (crow & 7);
-  uint32_t a_off[NA];
+  typedef typename std::conditional<A64, int64_t, uint32_t>::type AOff;
+  AOff a_off[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int m = m_base + i * 32 + crow;
@@ -60,7 +73,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
       s = g.a_rows ? g.a_rows[m] : m;
       if (s < 0) s = 0;
     }
-    a_off[i] = (uint32_t)(s * g.a_ld[0] * (int64_t)sizeof(T)) + cchunk * 16;
+    a_off[i] = (AOff)(s * g.a_ld[0] * (int64_t)sizeof(T) + cchunk * 16);
   }
   const char* b_base[NB];
   uint32_t b_off[NB];
@@ -73,21 +86,26 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
     b_off[j] = (uint32_t)((valid ? (lane >> 3) : 0) * g.b_ld * (int64_t)sizeof(T)) + cchunk * 16;
   }
 
-  // A-segment cursor of the next slab to issue (slabs are issued in K order)
+  // A-segment cursor of the next slab to issue (A slabs are issued in K order)
   int a_seg = k_begin / g.a_segk, a_kk = k_begin - a_seg * g.a_segk;
-  auto issue = [&](int kt, uint4* dst) {
-    const int k0 = k_begin + kt * BK;
+  auto issue_a = [&](uint4* dst) {
     const char* abase = (const char*)g.a_ptr[a_seg] + (int64_t)a_kk * sizeof(T);
 #pragma unroll
-    for (int i = 0; i < NA; ++i) copy16_to_lds_sv(abase, a_off[i], dst + i * 256 + wave * 64);
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      copy16_to_lds_sv(b_base[j] + (int64_t)k0 * sizeof(T), b_off[j], dst + (NA + j) * 256 + wave * 64);
+    for (int i = 0; i < NA; ++i) {
+      if constexpr (A64) copy16_to_lds(abase + a_off[i], dst + i * 256 + wave * 64);
+      else copy16_to_lds_sv(abase, a_off[i], dst + i * 256 + wave * 64);
+    }
     a_kk += BK;
     if (a_kk == g.a_segk) {
       ++a_seg;
       a_kk = 0;
     }
+  };
+  auto issue_b = [&](int kt, uint4* dst) {
+    const int k0 = k_begin + kt * BK;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      copy16_to_lds_sv(b_base[j] + (int64_t)k0 * sizeof(T), b_off[j], dst + j * 256 + wave * 64);
   };
 
   f32x4 acc[FM][FN];
@@ -97,7 +115,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int grp = lane >> 4, r16 = lane & 15;
-  auto compute = [&](const uint4* buf) {
+  auto compute = [&](const uint4* bufA, const uint4* bufB) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       bf16x8 af[FM], bfr[FN];
@@ -105,12 +123,12 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
 #pragma unroll
       for (int fi = 0; fi < FM; ++fi) {
         const int row = wm * WM + fi * 16 + r16;
-        *(uint4*)&af[fi] = buf[row * 8 + (c ^ (row & 7))];
+        *(uint4*)&af[fi] = bufA[row * 8 + (c ^ (row & 7))];
       }
 #pragma unroll
       for (int fj = 0; fj < FN; ++fj) {
         const int row = wn * WN + fj * 16 + r16;
-        *(uint4*)&bfr[fj] = buf[(BM + row) * 8 + (c ^ (row & 7))];
+        *(uint4*)&bfr[fj] = bufB[row * 8 + (c ^ (row & 7))];
       }
 #pragma unroll
       for (int fi = 0; fi < FM; ++fi)
@@ -118,25 +136,38 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
         for (int fj = 0; fj < FN; ++fj) Frag<T>::mma(acc[fi][fj], af[fi], bfr[fj]);
     }
   };
-  // ring: slab kt lives in buffer kt % STAGES; up to STAGES - 1 slabs in flight
+  // rings: slab kt lives in A stage kt % SA and B stage kt % SB.  Issue order:
+  // prologue p = 0 .. max(SA, SB) - 2 gives [A(p) if p < SA-1][B(p) if p < SB-1];
+  // iteration kt (after its barrier) gives [A(kt+SA-1)][B(kt+SB-1)] when in range.
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < nk) issue(p, smem[p]);
+  for (int p = 0; p < (SA > SB ? SA : SB) - 1; ++p) {
+    if (p < SA - 1 && p < nk) issue_a(smemA(p));
+    if (p < SB - 1 && p < nk) issue_b(p, smemB(p));
+  }
   for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = min(STAGES - 2, nk - 1 - kt);   // slabs after kt allowed to stay in flight
-    if constexpr (STAGES == 4) {
-      if (ahead >= 2) wait_vmcnt<2 * NL>();
-      else if (ahead == 1) wait_vmcnt<NL>();
-      else wait_vmcnt<0>();
-    } else if constexpr (STAGES == 3) {
-      if (ahead >= 1) wait_vmcnt<NL>();
-      else wait_vmcnt<0>();
+    // wait until A(kt) and B(kt) have landed: count the copies issued after them
+    if constexpr (SA == SB) {
+      const int ahead = min(SA - 2, nk - 1 - kt);   // slabs after kt allowed to stay in flight
+      if constexpr (SA == 4) {
+        if (ahead >= 2) wait_vmcnt<2 * NL>();
+        else if (ahead == 1) wait_vmcnt<NL>();
+        else wait_vmcnt<0>();
+      } else if constexpr (SA == 3) {
+        if (ahead >= 1) wait_vmcnt<NL>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
     } else {
-      wait_vmcnt<0>();
+      // SA == 2: A(kt) was issued last (iteration kt-1), followed only by B(kt+SB-2)
+      // (at kt = 0 this also waits for B(1..SB-2): conservative)
+      if (kt + SB - 2 < nk) wait_vmcnt<NB>();
+      else wait_vmcnt<0>();
     }
     lds_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, smem[(kt + STAGES - 1) % STAGES]);
-    compute(smem[kt % STAGES]);
+    if (kt + SA - 1 < nk) issue_a(smemA((kt + SA - 1) % SA));
+    if (kt + SB - 1 < nk) issue_b(kt + SB - 1, smemB((kt + SB - 1) % SB));
+    compute(smemA(kt % SA), smemB(kt % SB));
   }
   wait_vmcnt<0>();
   lds_barrier();
@@ -157,7 +188,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
     return;
   }
 
-  float* stage = (float*)&smem[0][0];
+  float* stage = (float*)smem;
 #pragma unroll
   for (int pass = 0; pass < BM / ER; ++pass) {
     if (m_base + pass * ER >= g.M) break;

@@ -11,18 +11,26 @@
 
 namespace dfl {
 
-template <int BM, int BN, int STAGES, class Epi>
+template <int BM, int BN, int SA, int SB, class Epi>
 static void gemm2_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   const typename Epi::Params& p = *(const typename Epi::Params*)ep;
-  dim3 grid(g.tiles_m * g.tiles_n, g.splits);
-  gemm2_kernel<BM, BN, STAGES, Epi><<<grid, 256, 0, s>>>(g, p);
+  dim3 grid(gemm_grid(g.tiles_m * g.tiles_n), g.splits);
+  // 64-bit A offsets only where a caller's buffer may exceed 4 GiB (injection fc)
+  if constexpr (std::is_same<Epi, EpiStore<float>>::value) {
+    if (g.a_wide) {
+      gemm2_kernel<BM, BN, SA, SB, Epi, true><<<grid, 256, 0, s>>>(g, p);
+      if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<g.tiles_m * g.tiles_n, 256, 0, s>>>(g, p);
+      return;
+    }
+  }
+  gemm2_kernel<BM, BN, SA, SB, Epi><<<grid, 256, 0, s>>>(g, p);
   if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<g.tiles_m * g.tiles_n, 256, 0, s>>>(g, p);
 }
 
 template <int BM, class Epi>
 static void gemm1_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   const typename Epi::Params& p = *(const typename Epi::Params*)ep;
-  dim3 grid(g.tiles_m * g.tiles_n, g.splits);
+  dim3 grid(gemm_grid(g.tiles_m * g.tiles_n), g.splits);
   gemm_kernel<float, BM, 128, Epi><<<grid, 256, 0, s>>>(g, p);
   if (g.splits > 1) gemm_reduce_kernel<BM, 128, Epi><<<g.tiles_m * g.tiles_n, 256, 0, s>>>(g, p);
 }
@@ -31,11 +39,11 @@ template <typename T, class Epi>
 static void gemm_cfg(const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     if (pl.bn == 256) {
-      if (pl.bm == 64) gemm2_go<64, 256, 3, Epi>(g, ep, s);
-      else gemm2_go<128, 256, 3, Epi>(g, ep, s);
+      if (pl.bm == 64) gemm2_go<64, 256, 3, 3, Epi>(g, ep, s);
+      else gemm2_go<128, 256, 3, 3, Epi>(g, ep, s);
     } else {
-      if (pl.bm == 64) gemm2_go<64, 128, 3, Epi>(g, ep, s);
-      else gemm2_go<128, 128, 2, Epi>(g, ep, s);
+      if (pl.bm == 64) gemm2_go<64, 128, 3, 3, Epi>(g, ep, s);
+      else gemm2_go<128, 128, 2, 2, Epi>(g, ep, s);
     }
   } else {
     if (pl.bm == 64) gemm1_go<64, Epi>(g, ep, s);
