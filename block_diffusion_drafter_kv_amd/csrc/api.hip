@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <vector>
 
@@ -19,6 +20,14 @@ struct dflash_handle {
   // borrowed weights
   const void *embed = nullptr, *lm_head = nullptr, *fc = nullptr, *hidden_norm = nullptr, *final_norm = nullptr;
   std::vector<dflash_layer_weights> layers;
+  // matrices as the products read them: the caller's (fp32 drafter) or the
+  // handle's fp16 copies scaled by 2^wscale_log2 (bf16 drafter)
+  struct Mats { const void *q, *k, *v, *o, *gate, *up, *down; };
+  std::vector<Mats> mats;
+  const void* lm = nullptr;
+  int op = OP_F32, op_fc = OP_F32;  // operand type of the products / of the fc product
+  int wscale_log2 = 0;
+  float out_scale = 1.f;            // 2^-wscale_log2: undoes the weight scale in every epilogue
   const void** d_k_gains = nullptr;       // device array of per-layer k_norm pointers
   // cache and state
   void* cache_k = nullptr;
@@ -170,6 +179,7 @@ GemmArgs gemm_a1(const void* a, int64_t lda, int M, int N, int K) {
   g.a_segk = K;
   g.b_nseg = 1;
   g.splits = 1;
+  g.out_scale = 1.f;
   return g;
 }
 
@@ -187,6 +197,68 @@ void set_b(GemmArgs& g, std::initializer_list<std::pair<const void*, int>> segs,
 }
 
 inline hipStream_t S(void* s) { return (hipStream_t)s; }
+
+// The matrices every product reads.  fp32 drafter: the caller's.  bf16 drafter:
+// fp16 copies of q/k/v/o/gate/up/down of every layer and of the LM head, all
+// scaled by one power of two 2^s chosen from the largest |w| so that the largest
+// scaled weight lies in [2^14, 2^15).  A bf16 value has 8 significant bits, so
+// w * 2^s is exact in fp16 whenever it is at least 2^-14, which holds for every
+// |w| of at least 2^-28 times the largest; smaller weights round to fp16's
+// subnormal grid (absolute error at most 2^(-25-s)).  The
+// epilogues multiply the products by 2^-s (exact).
+int prepare_weights(dflash_handle* h) {
+  const dflash_config& c = h->cfg;
+  h->mats.resize(c.n_layers);
+  if (c.dtype != DFLASH_BF16) {
+    for (int l = 0; l < c.n_layers; ++l) {
+      const dflash_layer_weights& L = h->layers[l];
+      h->mats[l] = {L.q_w, L.k_w, L.v_w, L.o_w, L.gate_w, L.up_w, L.down_w};
+    }
+    h->lm = h->lm_head;
+    return DFLASH_OK;
+  }
+  const int64_t H = c.hidden, qdim = (int64_t)c.n_q_heads * c.head_dim, kvdim = (int64_t)c.n_kv_heads * c.head_dim;
+  const int64_t F = c.ffn, V = c.vocab;
+  struct Job { const void* src; int64_t n; const void** dst; };
+  std::vector<Job> jobs;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const dflash_layer_weights& L = h->layers[l];
+    dflash_handle::Mats& m = h->mats[l];
+    jobs.push_back({L.q_w, qdim * H, &m.q});
+    jobs.push_back({L.k_w, kvdim * H, &m.k});
+    jobs.push_back({L.v_w, kvdim * H, &m.v});
+    jobs.push_back({L.o_w, H * qdim, &m.o});
+    jobs.push_back({L.gate_w, F * H, &m.gate});
+    jobs.push_back({L.up_w, F * H, &m.up});
+    jobs.push_back({L.down_w, H * F, &m.down});
+  }
+  jobs.push_back({h->lm_head, V * H, &h->lm});
+  uint32_t* d_max = nullptr;
+  int rc = alloc_t(h, &d_max, 1, 4);
+  if (rc) return rc;
+  for (auto& j : jobs) launch_absmax_bf16(j.src, j.n, d_max, nullptr);
+  uint32_t bits = 0;
+  if (hipMemcpy(&bits, d_max, 4, hipMemcpyDeviceToHost) != hipSuccess) return DFLASH_E_HIP;
+  float amax;
+  std::memcpy(&amax, &bits, 4);
+  if (!(amax <= 3.0e38f)) return DFLASH_E_INVALID;   // Inf or NaN among the weights
+  int s = 0;
+  if (amax > 0.f) {
+    int e;
+    std::frexp(amax, &e);     // amax in [2^(e-1), 2^e)
+    s = 15 - e;               // amax * 2^s in [2^14, 2^15)
+  }
+  h->wscale_log2 = s;
+  h->out_scale = std::ldexp(1.0f, -s);
+  const float scale = std::ldexp(1.0f, s);
+  for (auto& j : jobs) {
+    void* dst = nullptr;
+    if ((rc = alloc(h, &dst, (size_t)j.n * 2))) return rc;
+    launch_convert_bf16_f16(j.src, j.n, scale, dst, nullptr);
+    *j.dst = dst;
+  }
+  return DFLASH_OK;
+}
 
 }  // namespace
 
@@ -251,7 +323,9 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
   // partial records (chunks) per segment
   h->attn_wg = 2 * h->num_cus;
   h->piece_cap = c.max_batch * nkv * splits * kAttnChunkMax;
-  h->lm_tile = gemm_bn(c.dtype);
+  h->op = c.dtype == DFLASH_BF16 ? OP_F16 : OP_F32;
+  h->op_fc = c.dtype == DFLASH_BF16 ? OP_BF16 : OP_F32;
+  h->lm_tile = gemm_bn(h->op);
   h->n_vtiles = (c.vocab + h->lm_tile - 1) / h->lm_tile;
   h->inject_chunk = std::min(c.max_inject_rows, 16384);
 
@@ -282,7 +356,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc_t(h, &h->chunk_base, (size_t)c.max_batch * nkv * splits, 4))) break;
     if ((rc = alloc_t(h, &h->dslots, c.max_batch, 4))) break;
     // split-K is used only while tiles * splits <= 2 * CUs: bounded by that many output tiles
-    h->partials_elems = (size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(c.dtype);
+    h->partials_elems = (size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(h->op);
     if ((rc = alloc_t(h, &h->partials, h->partials_elems, 4))) break;
     const size_t lrows = (size_t)c.max_batch * c.max_k;
     if ((rc = alloc_t(h, &h->logits_ws, lrows * c.vocab, 4))) break;
@@ -309,9 +383,11 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     delete h;
     return rc;
   }
+  if (!rc) rc = prepare_weights(h);
   std::vector<const void*> kg(c.n_layers);
   for (int l = 0; l < c.n_layers; ++l) kg[l] = h->layers[l].k_norm;
-  if (hipMemcpy(h->d_k_gains, kg.data(), sizeof(void*) * c.n_layers, hipMemcpyHostToDevice) != hipSuccess) rc = -5;
+  if (!rc && hipMemcpy(h->d_k_gains, kg.data(), sizeof(void*) * c.n_layers, hipMemcpyHostToDevice) != hipSuccess)
+    rc = DFLASH_E_HIP;
   if (!rc) {
     launch_rope_table(h->rope, h->n_rope, d, (double)c.rope_theta, nullptr);
     if (hipDeviceSynchronize() != hipSuccess || hipGetLastError() != hipSuccess) rc = DFLASH_E_HIP;
@@ -384,8 +460,8 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
     EpiStore<float>::Params pf{h->y, H};
     {
       Phase ph(h, s, DFLASH_PH_INJECT_FC);
-      launch_gemm(dt, EPI_STORE_F32, ga, &pf, plan_gemm(dt, plan_rows, H, featK, h->num_cus), h->partials,
-                  h->partials_elems, s);
+      launch_gemm(h->op_fc, EPI_STORE_F32, ga, &pf, plan_gemm(h->op_fc, plan_rows, H, featK, h->num_cus),
+                  h->partials, h->partials_elems, s);
     }
     {
       Phase ph(h, s, DFLASH_PH_INJECT_NORM);
@@ -395,20 +471,21 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
     for (int l0 = 0; l0 < c.n_layers; l0 += MAX_BSEG / 2) {
       const int nl = std::min(MAX_BSEG / 2, c.n_layers - l0);
       GemmArgs gk = gemm_a1(h->g, H, rows, 2 * kvdim * nl, H);
+      gk.out_scale = h->out_scale;
       gk.m_valid = h->req_off + n_req;
       gk.m_valid_base = (int)c0;
       for (int i = 0; i < nl; ++i) {
-        gk.b_ptr[2 * i] = h->layers[l0 + i].k_w;
-        gk.b_ptr[2 * i + 1] = h->layers[l0 + i].v_w;
+        gk.b_ptr[2 * i] = h->mats[l0 + i].k;
+        gk.b_ptr[2 * i + 1] = h->mats[l0 + i].v;
         gk.b_begin[2 * i] = 2 * i * kvdim;
         gk.b_begin[2 * i + 1] = (2 * i + 1) * kvdim;
       }
       gk.b_begin[2 * nl] = 2 * nl * kvdim;
       gk.b_nseg = 2 * nl;
       gk.b_ld = H;
-      EpiKVInject<bf16_t>::Params pk;
-      pk.cache_k = (bf16_t*)h->cache_k;
-      pk.cache_v = (bf16_t*)h->cache_v;
+      EpiKVInject<f16_t>::Params pk;
+      pk.cache_k = (f16_t*)h->cache_k;
+      pk.cache_v = (f16_t*)h->cache_v;
       pk.row_slot = h->row_slot + c0;
       pk.row_pos = h->row_pos + c0;
       pk.k_gain = (const bf16_t* const*)(h->d_k_gains + l0);
@@ -422,7 +499,7 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
       pk.layer0 = l0;
       // the parameter block has the same layout for fp32 (pointers only differ in type)
       Phase ph(h, s, DFLASH_PH_INJECT_KV);
-      launch_gemm(dt, EPI_KVINJECT, gk, &pk, plan_gemm(dt, plan_rows, gk.N, H, h->num_cus), h->partials,
+      launch_gemm(h->op, EPI_KVINJECT, gk, &pk, plan_gemm(h->op, plan_rows, gk.N, H, h->num_cus), h->partials,
                   h->partials_elems, s);
     }
   }
@@ -514,14 +591,16 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   const int64_t layer_cache = (int64_t)(c.max_batch + 1) * nkv * h->ctx_alloc * d * h->esize;
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& L = h->layers[l];
+    const dflash_handle::Mats& W = h->mats[l];
     // q | k | v with head norm + RoPE into the attention layouts
     {
       GemmArgs ga = gemm_a1(h->hbuf, H, M, qdim + 2 * kvdim, H);
-      set_b(ga, {{L.q_w, qdim}, {L.k_w, kvdim}, {L.v_w, kvdim}}, H);
-      EpiQKV<bf16_t>::Params pq;
-      pq.qb = (bf16_t*)h->qb;
-      pq.kb = (bf16_t*)h->kb;
-      pq.vb = (bf16_t*)h->vb;
+      ga.out_scale = h->out_scale;
+      set_b(ga, {{W.q, qdim}, {W.k, kvdim}, {W.v, kvdim}}, H);
+      EpiQKV<f16_t>::Params pq;
+      pq.qb = (f16_t*)h->qb;
+      pq.kb = (f16_t*)h->kb;
+      pq.vb = (f16_t*)h->vb;
       pq.slots = slots;
       pq.ctx_len = h->ctx_len;
       pq.q_gain = (const bf16_t*)L.q_norm;
@@ -537,7 +616,8 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       pq.Rpad = h->Rpad;
       pq.eps = c.rms_eps;
       Phase ph(h, s, DFLASH_PH_QKV);
-      launch_gemm(dt, EPI_QKV, ga, &pq, plan_gemm(dt, M, ga.N, H, h->num_cus), h->partials, h->partials_elems, s);
+      launch_gemm(h->op, EPI_QKV, ga, &pq, plan_gemm(h->op, M, ga.N, H, h->num_cus), h->partials, h->partials_elems,
+                  s);
     }
     // attention over [context ; block]
     {
@@ -593,10 +673,12 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     // output projection + residual
     {
       GemmArgs ga = gemm_a1(h->attn_out, qdim, M, H, qdim);
-      set_b(ga, {{L.o_w, H}}, qdim);
+      ga.out_scale = h->out_scale;
+      set_b(ga, {{W.o, H}}, qdim);
       EpiResidualAdd::Params pr{h->X, H};
       Phase ph(h, s, DFLASH_PH_O);
-      launch_gemm(dt, EPI_RESADD, ga, &pr, plan_gemm(dt, M, H, qdim, h->num_cus), h->partials, h->partials_elems, s);
+      launch_gemm(h->op, EPI_RESADD, ga, &pr, plan_gemm(h->op, M, H, qdim, h->num_cus), h->partials,
+                  h->partials_elems, s);
     }
     {
       Phase ph(h, s, DFLASH_PH_NORM);
@@ -605,21 +687,24 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     // SwiGLU MLP
     {
       GemmArgs ga = gemm_a1(h->hbuf, H, M, 2 * F, H);
-      ga.b_ptr[0] = L.gate_w;
-      ga.b_ptr[1] = L.up_w;
+      ga.out_scale = h->out_scale;
+      ga.b_ptr[0] = W.gate;
+      ga.b_ptr[1] = W.up;
       ga.b_interleave = 1;
       ga.b_ld = H;
-      EpiSwiGLU<bf16_t>::Params ps{(bf16_t*)h->act, F, F};
+      EpiSwiGLU<f16_t>::Params ps{(f16_t*)h->act, F, F};
       {
         Phase ph(h, s, DFLASH_PH_GATE_UP);
-        launch_gemm(dt, EPI_SWIGLU, ga, &ps, plan_gemm(dt, M, 2 * F, H, h->num_cus), h->partials,
+        launch_gemm(h->op, EPI_SWIGLU, ga, &ps, plan_gemm(h->op, M, 2 * F, H, h->num_cus), h->partials,
                     h->partials_elems, s);
       }
       GemmArgs gd = gemm_a1(h->act, F, M, H, F);
-      set_b(gd, {{L.down_w, H}}, F);
+      gd.out_scale = h->out_scale;
+      set_b(gd, {{W.down, H}}, F);
       EpiResidualAdd::Params pr{h->X, H};
       Phase ph(h, s, DFLASH_PH_DOWN);
-      launch_gemm(dt, EPI_RESADD, gd, &pr, plan_gemm(dt, M, H, F, h->num_cus), h->partials, h->partials_elems, s);
+      launch_gemm(h->op, EPI_RESADD, gd, &pr, plan_gemm(h->op, M, H, F, h->num_cus), h->partials,
+                  h->partials_elems, s);
     }
     if (l + 1 < c.n_layers) {
       Phase ph(h, s, DFLASH_PH_NORM);
@@ -637,7 +722,8 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   float* logits = o->logits ? o->logits : (need_logits ? h->logits_ws : nullptr);
   {
     GemmArgs ga = gemm_a1(h->hbuf, H, rows, V, H);
-    set_b(ga, {{h->lm_head, V}}, H);
+    ga.out_scale = h->out_scale;
+    set_b(ga, {{h->lm, V}}, H);
     EpiLMHead::Params pl;
     pl.logits = logits;
     pl.ld = V;
@@ -648,10 +734,10 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     pl.inv_temp = T > 0.f ? 1.0f / T : 1.0f;
     pl.out_mult = c.output_multiplier;
     pl.softcap = c.logit_softcap;
-    GemmPlan gp = plan_gemm(dt, rows, V, H, h->num_cus, /*wide=*/true);
+    GemmPlan gp = plan_gemm(h->op, rows, V, H, h->num_cus, /*wide=*/true);
     gp.splits = 1;   // the vocabulary gives plenty of tiles; statistics are per output tile
     Phase ph(h, s, DFLASH_PH_LM_HEAD);
-    launch_gemm(dt, EPI_LMHEAD, ga, &pl, gp, h->partials, h->partials_elems, s);
+    launch_gemm(h->op, EPI_LMHEAD, ga, &pl, gp, h->partials, h->partials_elems, s);
   }
   select_stage(h, s, n_req, slots, anchor_ids, logits, p, o);
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;

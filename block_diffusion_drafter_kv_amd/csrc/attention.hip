@@ -442,8 +442,8 @@ void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, i
 
 void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStream_t s) {
   if (dtype == DT_BF16) {
-    if (D == 128) launch_attn_t<bf16_t, 128>(a, qrt, grid, s);
-    else launch_attn_t<bf16_t, 64>(a, qrt, grid, s);
+    if (D == 128) launch_attn_t<f16_t, 128>(a, qrt, grid, s);
+    else launch_attn_t<f16_t, 64>(a, qrt, grid, s);
   } else {
     if (D == 128) launch_attn_t<float, 128>(a, qrt, grid, s);
     else launch_attn_t<float, 64>(a, qrt, grid, s);
@@ -452,8 +452,8 @@ void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStre
 
 void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, hipStream_t s) {
   if (dtype == DT_BF16) {
-    if (D == 128) attn_combine_kernel<bf16_t, 128><<<grid, 256, 0, s>>>(a);
-    else attn_combine_kernel<bf16_t, 64><<<grid, 256, 0, s>>>(a);
+    if (D == 128) attn_combine_kernel<f16_t, 128><<<grid, 256, 0, s>>>(a);
+    else attn_combine_kernel<f16_t, 64><<<grid, 256, 0, s>>>(a);
   } else {
     if (D == 128) attn_combine_kernel<float, 128><<<grid, 256, 0, s>>>(a);
     else attn_combine_kernel<float, 64><<<grid, 256, 0, s>>>(a);

@@ -1,9 +1,14 @@
 // Shared device helpers for the DFlash drafter kernels (gfx950 / CDNA4).
 //
-// Element types: the drafter computes either in fp32 (weights, activations and
-// KV cache in fp32) or in bf16 (weights, GEMM operands and KV cache in bf16,
-// fp32 accumulation, fp32 residual stream).  Matrix products use MFMA:
-// v_mfma_f32_16x16x32_bf16 for bf16 and v_mfma_f32_16x16x4_f32 for fp32.
+// Element types.  An fp32 drafter computes in fp32 throughout (weights,
+// activations, KV cache; v_mfma_f32_16x16x4_f32).  A bf16 drafter (weights and
+// target hidden states given in bf16) multiplies fp16 operands with fp32
+// accumulation (v_mfma_f32_16x16x32_f16, the bf16 rate on CDNA4): its weight
+// matrices are converted once, exactly, to fp16 scaled by a power of two; its
+// activations, block q/k/v, attention weights and KV cache are fp16 (three more
+// significand bits than bf16 at the same size); the residual stream stays fp32.
+// Only the fc product, whose two operands both arrive in bf16, runs on
+// v_mfma_f32_16x16x32_bf16.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -13,6 +18,8 @@ namespace dfl {
 typedef __bf16 bf16_t;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16_t;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
@@ -21,9 +28,16 @@ static constexpr int EPI_ROWS = 64;  // rows staged per GEMM epilogue pass
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16_t x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return (bf16_t)x; }
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) { return (f16_t)x; }
+
+// Storage type of the weights read elementwise (norm gains, embedding) by a
+// kernel whose operand type is C: the caller's bf16 for an fp16-operand drafter.
+template <typename C> struct WeightOf { typedef C type; };
+template <> struct WeightOf<f16_t> { typedef bf16_t type; };
 
 // ---- MFMA fragments: one lane holds 8 consecutive k-values of one row ----
 // For a 16x16 output tile with k = 32 per step, lane l supplies row (l % 16) of
@@ -34,6 +48,12 @@ template <> struct Frag<bf16_t> {
   typedef bf16x8 type;
   __device__ __forceinline__ static void mma(f32x4& c, const bf16x8& a, const bf16x8& b) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Frag<f16_t> {
+  typedef f16x8 type;
+  __device__ __forceinline__ static void mma(f32x4& c, const f16x8& a, const f16x8& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
 };
 template <> struct Frag<float> {
@@ -48,6 +68,7 @@ template <> struct Frag<float> {
 // 16-byte vector of T
 template <typename T> struct Vec16;
 template <> struct Vec16<bf16_t> { typedef bf16x8 type; static constexpr int N = 8; };
+template <> struct Vec16<f16_t> { typedef f16x8 type; static constexpr int N = 8; };
 template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4; };
 
 // ---- wave reductions ----

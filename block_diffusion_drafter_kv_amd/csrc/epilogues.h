@@ -55,9 +55,9 @@ struct EpiSwiGLU {
 };
 
 // Per-head RMSNorm + rotate-half RoPE of one head held in a staged row.
-// Lanes [0, d/2) of a lane group handle the pairs (i, i + d/2).
-template <typename T>
-__device__ __forceinline__ void norm_rope_pair(float& x1, float& x2, int i, int d, const T* gain, float eps,
+// Lanes [0, d/2) of a lane group handle the pairs (i, i + d/2).  G: gain storage type.
+template <typename G>
+__device__ __forceinline__ void norm_rope_pair(float& x1, float& x2, int i, int d, const G* gain, float eps,
                                                const float2* rope_row) {
   const float ss = group_sum(x1 * x1 + x2 * x2, d / 2);
   const float rs = rsqrtf(ss / (float)d + eps);
@@ -76,10 +76,11 @@ __device__ __forceinline__ void norm_rope_pair(float& x1, float& x2, int i, int 
 // order of the cache (kv_layout.h).
 template <typename T>
 struct EpiQKV {
+  typedef typename WeightOf<T>::type W;
   struct Params {
     T* qb; T* kb; T* vb;
     const int32_t* slots; const int32_t* ctx_len;
-    const T* q_gain; const T* k_gain;
+    const W* q_gain; const W* k_gain;
     const float2* rope;      // [pos][d/2] (cos, sin)
     int R, group, n_kv, d, q_dim, kv_dim, QRpad, Rpad;
     float eps;
@@ -103,7 +104,7 @@ struct EpiQKV {
         const int slot = p.slots[req];
         const int pos = p.ctx_len[slot] + j;
         const bool isq = nb < p.q_dim;
-        norm_rope_pair<T>(x1, x2, i, p.d, isq ? p.q_gain : p.k_gain, p.eps, p.rope + (int64_t)pos * half);
+        norm_rope_pair<W>(x1, x2, i, p.d, isq ? p.q_gain : p.k_gain, p.eps, p.rope + (int64_t)pos * half);
         if (isq) {
           const int qh = nb / p.d, kv = qh / p.group, gi = qh % p.group;
           T* dst = p.qb + ((int64_t)(req * p.n_kv + kv) * p.QRpad + gi * p.R + j) * p.d;
@@ -129,10 +130,11 @@ struct EpiQKV {
 // Cache: K and V [layer][slot][kv][ctx_alloc * d], positions in 32-key blocks (kv_layout.h).
 template <typename T>
 struct EpiKVInject {
+  typedef typename WeightOf<T>::type W;
   struct Params {
     T* cache_k; T* cache_v;
     const int32_t* row_slot; const int32_t* row_pos;   // per GEMM row (global row index)
-    const T* const* k_gain;                              // device array [n_layers] of gains
+    const W* const* k_gain;                              // device array [n_layers] of gains
     const float2* rope;
     int n_kv, d, kv_dim, max_batch;
     int64_t ctx_alloc;
@@ -159,7 +161,7 @@ struct EpiKVInject {
           if (slot < 0) continue;
           const int pos = p.row_pos[m];
           float x1 = st[r * ld + hh * p.d + i], x2 = st[r * ld + hh * p.d + i + half];
-          norm_rope_pair<T>(x1, x2, i, p.d, p.k_gain[layer], p.eps, p.rope + (int64_t)pos * half);
+          norm_rope_pair<W>(x1, x2, i, p.d, p.k_gain[layer], p.eps, p.rope + (int64_t)pos * half);
           T* dst = p.cache_k +
                    (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.ctx_alloc * p.d;
           dst[k_off(pos, i, p.d)] = from_f32<T>(x1);

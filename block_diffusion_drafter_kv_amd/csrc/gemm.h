@@ -39,6 +39,7 @@ struct GemmArgs {
   int64_t b_ld;
   int b_interleave;            // 1: tile t's rows [0,BN/2) = gate rows t*BN/2.., [BN/2,BN) = up rows
   int a_wide;                  // 1: A rows need 64-bit byte offsets (caller buffers of 4 GiB or more)
+  float out_scale;             // products are multiplied by this (a power of two undoing the weight scale)
   int splits;
   int k_per_split;             // multiple of the K slab
   float* partials;             // [splits][Mpad][Npad]
@@ -48,6 +49,7 @@ struct GemmArgs {
 
 template <typename T> struct GemmTraits;
 template <> struct GemmTraits<bf16_t> { static constexpr int BK = 64; static constexpr int VEC = 8; };
+template <> struct GemmTraits<f16_t> { static constexpr int BK = 64; static constexpr int VEC = 8; };
 template <> struct GemmTraits<float> { static constexpr int BK = 32; static constexpr int VEC = 4; };
 
 // Grid of a tiled product: rounded up to a multiple of the 8 XCDs so that the
@@ -76,10 +78,11 @@ __device__ __forceinline__ const T* b_row_ptr(const GemmArgs& g, int n) {
   return (const T*)g.b_ptr[s] + (int64_t)(n - g.b_begin[s]) * g.b_ld;
 }
 
-// Stage accumulators of rows [pass*ROWS, (pass+1)*ROWS) of the tile into LDS (fp32, row stride BN+1).
+// Stage accumulators of rows [pass*ROWS, (pass+1)*ROWS) of the tile into LDS (fp32, row stride BN+1),
+// multiplied by the product's output scale (a power of two: exact).
 template <int BM, int BN, int ROWS = EPI_ROWS>
 __device__ __forceinline__ void stage_acc(float* stage, const f32x4 (&acc)[BM / 32][BN / 32], int wm, int wn,
-                                          int lane, int pass) {
+                                          int lane, int pass, float scale) {
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
   constexpr int LD = BN + 1;
   const int g = lane >> 4, r16 = lane & 15;
@@ -91,7 +94,7 @@ __device__ __forceinline__ void stage_acc(float* stage, const f32x4 (&acc)[BM / 
     for (int fj = 0; fj < FN; ++fj) {
       const int col = wn * WN + fj * 16 + r16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) stage[(row0 - pass * ROWS + g * 4 + i) * LD + col] = acc[fi][fj][i];
+      for (int i = 0; i < 4; ++i) stage[(row0 - pass * ROWS + g * 4 + i) * LD + col] = acc[fi][fj][i] * scale;
     }
   }
 }
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g, const typen
 #pragma unroll
   for (int pass = 0; pass < BM / EPI_ROWS; ++pass) {
     if (m_base + pass * EPI_ROWS >= g.M) break;
-    stage_acc<BM, BN>(stage, acc, wm, wn, lane, pass);
+    stage_acc<BM, BN>(stage, acc, wm, wn, lane, pass, g.out_scale);
     __syncthreads();
     Epi::template apply<BN, EPI_ROWS>(ep, stage, BN + 1, m_base + pass * EPI_ROWS, n_base, g.M, g.N, tn, tid);
     __syncthreads();
@@ -289,10 +292,10 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const GemmArgs g, cons
     for (int j = 0; j < NV; ++j) {
       const int idx = tid + j * 256, r = idx / C4, c4 = idx % C4;
       float* d = stage + r * (BN + 1) + 4 * c4;
-      d[0] = acc[j].x;
-      d[1] = acc[j].y;
-      d[2] = acc[j].z;
-      d[3] = acc[j].w;
+      d[0] = acc[j].x * g.out_scale;
+      d[1] = acc[j].y * g.out_scale;
+      d[2] = acc[j].z * g.out_scale;
+      d[3] = acc[j].w * g.out_scale;
     }
     __syncthreads();
     Epi::template apply<BN, EPI_ROWS>(ep, stage, BN + 1, m0, n_base, g.M, g.N, tn, tid);

@@ -1,4 +1,4 @@
-// Pipelined bf16 MFMA GEMM for gfx950:  C[M, N] = A[M, K] . B[N, K]^T.
+// Pipelined 16-bit (fp16 or bf16 operands) MFMA GEMM for gfx950:  C[M, N] = A[M, K] . B[N, K]^T.
 //
 // Same operand addressing, split-K and LDS-staged epilogues as gemm.h, with a
 // deeper memory pipeline: K advances in 128-byte slabs that are copied from
@@ -28,9 +28,10 @@ static constexpr int GEMM2_EPI_ROWS = 32;   // epilogue slab: 32 rows x (BN+1) f
 // A64: A rows are addressed with per-lane 64-bit byte offsets (one 64-bit add per
 // copy) instead of 32-bit offsets from a wave-uniform base, for A buffers of
 // 4 GiB or more (the injection's caller-provided hidden states).
-template <int BM, int BN, int SA, int SB, class Epi, bool A64 = false>
+template <typename T, int BM, int BN, int SA, int SB, class Epi, bool A64 = false>
 __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const typename Epi::Params ep) {
-  typedef bf16_t T;
+  static_assert(sizeof(T) == 2, "16-bit operands");
+  typedef typename Frag<T>::type FragT;
   constexpr int BK = 64;
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
   constexpr int NA = BM * 8 / 256, NB = BN * 8 / 256, NL = NA + NB;
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
   auto compute = [&](const uint4* bufA, const uint4* bufB) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8 af[FM], bfr[FN];
+      FragT af[FM], bfr[FN];
       const int c = s * 4 + grp;
 #pragma unroll
       for (int fi = 0; fi < FM; ++fi) {
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
 #pragma unroll
   for (int pass = 0; pass < BM / ER; ++pass) {
     if (m_base + pass * ER >= g.M) break;
-    stage_acc<BM, BN, ER>(stage, acc, wm, wn, lane, pass);
+    stage_acc<BM, BN, ER>(stage, acc, wm, wn, lane, pass, g.out_scale);
     __syncthreads();
     Epi::template apply<BN, ER>(ep, stage, BN + 1, m_base + pass * ER, n_base, g.M, g.N, tn, tid);
     __syncthreads();

@@ -1,23 +1,24 @@
-// bf16 GEMM instantiations and the shared tile / split planner.
+// bf16 GEMM instantiation (the fc product: caller's bf16 hidden states times the
+// bf16 fc weight, fp32 output), the shared tile / split planner and the launcher.
 #include "gemm_dispatch.h"
 
 namespace dfl {
 
 void gemm_dispatch_bf16(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s) {
-  gemm_dispatch_t<bf16_t>(kind, pl, g, ep, s);
+  if (kind == EPI_STORE_F32) gemm_cfg<bf16_t, EpiStore<float>>(pl, g, ep, s);
 }
 
-GemmPlan plan_gemm(int dtype, int M, int N, int K, int num_cus, bool wide) {
+GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide) {
   GemmPlan p;
-  p.bn = (wide && dtype == DT_BF16) ? 256 : 128;
+  const bool w16 = op != OP_F32;
+  p.bn = (wide && w16) ? 256 : 128;
   p.bm = M <= 64 ? 64 : 128;
-  // bf16: 64-row tiles (3 LDS stages, two work-groups per CU) whenever 128-row
+  // 16-bit: 64-row tiles (3 LDS stages, two work-groups per CU) whenever 128-row
   // tiles would leave fewer than two work-groups per CU (measured on the draft's
   // 544-row products: O 66 -> 45 us, down 175 -> 116 us, QKV 69 -> 56 us)
-  if (dtype == DT_BF16 && !wide && p.bm == 128 &&
-      (long)((M + 127) / 128) * ((N + p.bn - 1) / p.bn) < 2L * num_cus)
+  if (w16 && !wide && p.bm == 128 && (long)((M + 127) / 128) * ((N + p.bn - 1) / p.bn) < 2L * num_cus)
     p.bm = 64;
-  const int bk = dtype == DT_BF16 ? 64 : 32;
+  const int bk = w16 ? 64 : 32;
   const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   const int kt = K / bk;
   int sp = 1;
@@ -33,9 +34,9 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int num_cus, bool wide) {
   return p;
 }
 
-void launch_gemm(int dtype, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan, float* partials,
+void launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan, float* partials,
                  size_t partials_elems, hipStream_t s) {
-  const int bk = dtype == DT_BF16 ? 64 : 32;
+  const int bk = op != OP_F32 ? 64 : 32;
   g.tiles_m = (g.M + plan.bm - 1) / plan.bm;
   g.tiles_n = (g.N + plan.bn - 1) / plan.bn;
   g.Mpad = g.tiles_m * plan.bm;
@@ -46,7 +47,8 @@ void launch_gemm(int dtype, EpiKind kind, GemmArgs g, const void* epi_params, co
   g.splits = splits;
   g.k_per_split = ((kt + splits - 1) / splits) * bk;
   g.partials = partials;
-  if (dtype == DT_BF16) gemm_dispatch_bf16(kind, plan, g, epi_params, s);
+  if (op == OP_F16) gemm_dispatch_f16(kind, plan, g, epi_params, s);
+  else if (op == OP_BF16) gemm_dispatch_bf16(kind, plan, g, epi_params, s);
   else gemm_dispatch_f32(kind, plan, g, epi_params, s);
 }
 

@@ -1,29 +1,31 @@
-// Host-side dispatch of the GEMM kernel templates over (epilogue, tile shape).
-// bf16 products use the pipelined gemm2 kernel; fp32 products use the
-// register-staged kernel of gemm.h.  Tile shapes (measured on MI355X):
-//   bf16, M > 64 : 128 x 128, 2 LDS stages (64 KB: two work-groups per CU)
-//   bf16, M <= 64: 64 x 128, 3 stages
-//   bf16 LM head : 128 x 256 (or 64 x 256), 3 stages (fewer, wider tiles over the vocabulary)
-//   fp32         : 128 x 128 or 64 x 128
+// Host-side dispatch of the GEMM kernel templates over (operand type, epilogue,
+// tile shape).  16-bit products (fp16, or bf16 for the fc) use the pipelined
+// gemm2 kernel; fp32 products use the register-staged kernel of gemm.h.  Tile
+// shapes (measured on MI355X):
+//   16-bit, M > 64 : 128 x 128, 2 LDS stages (64 KB: two work-groups per CU)
+//   16-bit, M <= 64: 64 x 128, 3 stages
+//   16-bit LM head : 128 x 256 (or 64 x 256), 3 stages (fewer, wider tiles over the vocabulary)
+//   fp32           : 128 x 128 or 64 x 128
 #pragma once
 #include "gemm2.h"
 #include "ops.h"
 
 namespace dfl {
 
-template <int BM, int BN, int SA, int SB, class Epi>
+template <typename T, int BM, int BN, int SA, int SB, class Epi>
 static void gemm2_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   const typename Epi::Params& p = *(const typename Epi::Params*)ep;
   dim3 grid(gemm_grid(g.tiles_m * g.tiles_n), g.splits);
-  // 64-bit A offsets only where a caller's buffer may exceed 4 GiB (injection fc)
-  if constexpr (std::is_same<Epi, EpiStore<float>>::value) {
+  // 64-bit A offsets only where a caller's buffer may exceed 4 GiB (the injection
+  // fc over the caller's bf16 hidden states)
+  if constexpr (std::is_same<T, bf16_t>::value) {
     if (g.a_wide) {
-      gemm2_kernel<BM, BN, SA, SB, Epi, true><<<grid, 256, 0, s>>>(g, p);
+      gemm2_kernel<T, BM, BN, SA, SB, Epi, true><<<grid, 256, 0, s>>>(g, p);
       if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<g.tiles_m * g.tiles_n, 256, 0, s>>>(g, p);
       return;
     }
   }
-  gemm2_kernel<BM, BN, SA, SB, Epi><<<grid, 256, 0, s>>>(g, p);
+  gemm2_kernel<T, BM, BN, SA, SB, Epi><<<grid, 256, 0, s>>>(g, p);
   if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<g.tiles_m * g.tiles_n, 256, 0, s>>>(g, p);
 }
 
@@ -39,11 +41,11 @@ template <typename T, class Epi>
 static void gemm_cfg(const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     if (pl.bn == 256) {
-      if (pl.bm == 64) gemm2_go<64, 256, 3, 3, Epi>(g, ep, s);
-      else gemm2_go<128, 256, 3, 3, Epi>(g, ep, s);
+      if (pl.bm == 64) gemm2_go<T, 64, 256, 3, 3, Epi>(g, ep, s);
+      else gemm2_go<T, 128, 256, 3, 3, Epi>(g, ep, s);
     } else {
-      if (pl.bm == 64) gemm2_go<64, 128, 3, 3, Epi>(g, ep, s);
-      else gemm2_go<128, 128, 2, 2, Epi>(g, ep, s);
+      if (pl.bm == 64) gemm2_go<T, 64, 128, 3, 3, Epi>(g, ep, s);
+      else gemm2_go<T, 128, 128, 2, 2, Epi>(g, ep, s);
     }
   } else {
     if (pl.bm == 64) gemm1_go<64, Epi>(g, ep, s);
@@ -65,6 +67,7 @@ static void gemm_dispatch_t(EpiKind kind, const GemmPlan& pl, const GemmArgs& g,
 }
 
 void gemm_dispatch_bf16(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s);
+void gemm_dispatch_f16(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s);
 void gemm_dispatch_f32(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s);
 
 }  // namespace dfl

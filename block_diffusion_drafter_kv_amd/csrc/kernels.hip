@@ -1,6 +1,8 @@
 // Row-wise and selection kernels of the drafter hot path: RoPE table, block
 // embedding, RMSNorm, injection row tables, LM-head row statistics, sampling,
 // top-k, prefix tree, verification.
+#include <algorithm>
+
 #include "ops.h"
 
 namespace dfl {
@@ -34,10 +36,11 @@ __global__ void rope_table_kernel(float2* table, int n_pos, int d, double theta)
 // Block embedding [P2 §2.2; P4 §4]: row r*R + j holds the anchor (j = 0) or the
 // mask token (j >= 1), embedded and scaled; then the first layer's RMSNorm.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename C>
 __global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* anchors, int mask_id, int vocab,
-                                                          const T* embed, float scale, int H, float* X,
-                                                          const T* gain, T* h_out, float eps, int32_t* err) {
+                                                          const typename WeightOf<C>::type* embed, float scale, int H,
+                                                          float* X, const typename WeightOf<C>::type* gain, C* h_out,
+                                                          float eps, int32_t* err) {
   __shared__ float red[4];
   const int m = blockIdx.x;
   const int r = m / R, j = m % R;
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* a
     if (threadIdx.x == 0) raise_error(err, ERR_BAD_TOKEN);
     id = 0;
   }
-  const T* e = embed + (int64_t)id * H;
+  const auto* e = embed + (int64_t)id * H;
   float ss = 0.f;
   for (int c = threadIdx.x; c < H; c += 256) {
     const float v = to_f32(e[c]) * scale;
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* a
   ss = block_sum(ss, red);
   const float rs = rsqrtf(ss / (float)H + eps);
   for (int c = threadIdx.x; c < H; c += 256)
-    h_out[(int64_t)m * H + c] = from_f32<T>(X[(int64_t)m * H + c] * rs * to_f32(gain[c]));
+    h_out[(int64_t)m * H + c] = from_f32<C>(X[(int64_t)m * H + c] * rs * to_f32(gain[c]));
 }
 
 // Four values of one row, gain-scaled and stored as one 8- or 16-byte write.
@@ -65,6 +68,10 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 }
 __device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
   bf16_t v[4] = {(bf16_t)a, (bf16_t)b, (bf16_t)c, (bf16_t)d};
+  *(uint2*)p = *(const uint2*)v;
+}
+__device__ __forceinline__ void store4(f16_t* p, float a, float b, float c, float d) {
+  f16_t v[4] = {(f16_t)a, (f16_t)b, (f16_t)c, (f16_t)d};
   *(uint2*)p = *(const uint2*)v;
 }
 __device__ __forceinline__ float4 load4f(const float* p) { return *(const float4*)p; }
@@ -77,10 +84,10 @@ __device__ __forceinline__ float4 load4f(const bf16_t* p) {
 // RMSNorm of fp32 rows, one wave per row (H a multiple of 4):
 // out[o] = x * rsqrt(mean(x^2) + eps) * gain, x = X row (map_mask ? (o / K) * R + 1 + o % K : o).
 // Rows at or past (*n_valid - valid_base) are skipped when n_valid is given.
-template <typename T>
+template <typename C>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int n_rows, int H, const float* X, int map_mask, int K, int R,
-                                                       const T* gain, T* h_out, float eps, const int32_t* n_valid,
-                                                       int valid_base) {
+                                                       const typename WeightOf<C>::type* gain, C* h_out, float eps,
+                                                       const int32_t* n_valid, int valid_base) {
   const int o = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (o >= n_rows) return;
   if (n_valid && o >= *n_valid - valid_base) return;
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int n_rows, int H, const f
   }
   ss = wave_sum(ss);
   const float rs = rsqrtf(ss / (float)H + eps);
-  T* y = h_out + (int64_t)o * H;
+  C* y = h_out + (int64_t)o * H;
   for (int c = lane * 4; c < H; c += 256) {
     const float4 v = load4f(x + c), gn = load4f(gain + c);
     store4(y + c, v.x * rs * gn.x, v.y * rs * gn.y, v.z * rs * gn.z, v.w * rs * gn.w);
@@ -829,6 +836,26 @@ __global__ void reset_slots_kernel(int n, const int32_t* slots, int32_t* ctx_len
   ctx_len[s] = 0;
 }
 
+// ---------------------------------------------------------------------------
+// Weight conversion of a bf16 drafter (once, at handle creation).  absmax: the
+// largest |w| as its fp32 bit pattern (for non-negative floats the integer order
+// is the numeric order; Inf / NaN patterns sort above every finite value).
+// convert: w * 2^s rounded to fp16; a bf16 value has 8 significant bits, so the
+// result is exact whenever w * 2^s lies in fp16's normal range.
+// ---------------------------------------------------------------------------
+__global__ void absmax_bf16_kernel(const bf16_t* w, int64_t n, uint32_t* out) {
+  uint32_t best = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    best = max(best, __float_as_uint(fabsf((float)w[i])));
+  for (int o = 32; o > 0; o >>= 1) best = max(best, (uint32_t)__shfl_xor((int)best, o, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, best);
+}
+
+__global__ void convert_bf16_f16_kernel(const bf16_t* w, int64_t n, float scale, f16_t* out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = (f16_t)((float)w[i] * scale);
+}
+
 __global__ void philox_fill_kernel(int n, uint64_t seed, uint32_t slot, uint64_t step, uint32_t purpose, float* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) out[i] = philox_uniform(seed, slot, step, (uint32_t)i, purpose);
@@ -848,8 +875,8 @@ void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int
                        float scale, int H, float* X, const void* gain, void* h_out, float eps, int32_t* err,
                        hipStream_t s) {
   if (dtype == DT_BF16)
-    embed_norm_kernel<bf16_t><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const bf16_t*)embed, scale, H, X,
-                                                      (const bf16_t*)gain, (bf16_t*)h_out, eps, err);
+    embed_norm_kernel<f16_t><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const bf16_t*)embed, scale, H, X,
+                                                     (const bf16_t*)gain, (f16_t*)h_out, eps, err);
   else
     embed_norm_kernel<float><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const float*)embed, scale, H, X,
                                                      (const float*)gain, (float*)h_out, eps, err);
@@ -860,8 +887,8 @@ void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, 
   if (n_rows <= 0) return;
   const int grid = cdiv(n_rows, 4);
   if (dtype == DT_BF16)
-    rmsnorm_kernel<bf16_t><<<grid, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, (const bf16_t*)gain, (bf16_t*)h_out,
-                                                 eps, n_valid, valid_base);
+    rmsnorm_kernel<f16_t><<<grid, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, (const bf16_t*)gain, (f16_t*)h_out, eps,
+                                                n_valid, valid_base);
   else
     rmsnorm_kernel<float><<<grid, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, (const float*)gain, (float*)h_out, eps,
                                                 n_valid, valid_base);
@@ -956,13 +983,24 @@ void launch_copy_cache(int dtype, const void* cache_k, const void* cache_v, int 
   const int64_t total = (int64_t)n * n_kv * d;
   if (total <= 0) return;
   if (dtype == DT_BF16)
-    copy_cache_kernel<bf16_t><<<cdiv(total, 256), 256, 0, s>>>((const bf16_t*)cache_k, (const bf16_t*)cache_v, layer,
-                                                                slot, start, n, max_batch, n_kv, d, ctx_alloc,
-                                                                (bf16_t*)k_out, (bf16_t*)v_out);
+    copy_cache_kernel<f16_t><<<cdiv(total, 256), 256, 0, s>>>((const f16_t*)cache_k, (const f16_t*)cache_v, layer,
+                                                               slot, start, n, max_batch, n_kv, d, ctx_alloc,
+                                                               (f16_t*)k_out, (f16_t*)v_out);
   else
     copy_cache_kernel<float><<<cdiv(total, 256), 256, 0, s>>>((const float*)cache_k, (const float*)cache_v, layer,
                                                                slot, start, n, max_batch, n_kv, d, ctx_alloc,
                                                                (float*)k_out, (float*)v_out);
+}
+
+void launch_absmax_bf16(const void* w, int64_t n, uint32_t* out, hipStream_t s) {
+  if (n <= 0) return;
+  absmax_bf16_kernel<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 4096), 256, 0, s>>>((const bf16_t*)w, n, out);
+}
+
+void launch_convert_bf16_f16(const void* w, int64_t n, float scale, void* out, hipStream_t s) {
+  if (n <= 0) return;
+  convert_bf16_f16_kernel<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 65536), 256, 0, s>>>((const bf16_t*)w, n, scale,
+                                                                                           (f16_t*)out);
 }
 
 void launch_reset_slots(int n, const int32_t* slots, int32_t* ctx_len, int max_batch, int32_t* err, hipStream_t s) {

@@ -7,7 +7,10 @@
 
 namespace dfl {
 
+// drafter element type (dflash_config.dtype): fp32, or bf16 inputs with fp16 operands
 enum { DT_F32 = 0, DT_BF16 = 1 };
+// operand type of one matrix product
+enum OpType { OP_F32 = 0, OP_BF16 = 1, OP_F16 = 2 };
 
 // ---- GEMM (gemm_inst.hip) ----
 enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_T, EPI_RESADD, EPI_SWIGLU, EPI_QKV, EPI_KVINJECT, EPI_LMHEAD };
@@ -17,12 +20,13 @@ struct GemmPlan {
 };
 // widest output tile of the GEMM kernels; the LM head uses it, so it is also the
 // column width of the LM-head statistics tiles
-inline int gemm_bn(int dtype) { return dtype == DT_BF16 ? 256 : 128; }
+inline int gemm_bn(int op) { return op != OP_F32 ? 256 : 128; }
 // Choose tile/split for an M x N x K product (K multiple of the slab); wide = the
 // vocabulary product (widest tiles).
-GemmPlan plan_gemm(int dtype, int M, int N, int K, int num_cus, bool wide = false);
+GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide = false);
 // Fill tiles/splits/partials fields of g and launch kernel (+ reduce when split).
-void launch_gemm(int dtype, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan,
+// op: operand type; OP_BF16 supports only EPI_STORE_F32 (the fc product).
+void launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan,
                  float* partials, size_t partials_elems, hipStream_t s);
 
 // ---- attention (attention.hip) ----
@@ -77,6 +81,10 @@ void launch_synth_target(int n_req, int K, int V, const float* draft_logits, flo
 void launch_copy_cache(int dtype, const void* cache_k, const void* cache_v, int layer, int slot, int start, int n,
                        int max_batch, int n_kv, int d, int64_t ctx_alloc, void* k_out, void* v_out, hipStream_t s);
 void launch_reset_slots(int n, const int32_t* slots, int32_t* ctx_len, int max_batch, int32_t* err, hipStream_t s);
+// bf16 drafter weights: *out = max over w of the fp32 bit pattern of |w| (atomic max;
+// *out must start at 0), and out = fp16(w * scale)
+void launch_absmax_bf16(const void* w, int64_t n, uint32_t* out, hipStream_t s);
+void launch_convert_bf16_f16(const void* w, int64_t n, float scale, void* out, hipStream_t s);
 void launch_philox_fill(int n, uint64_t seed, uint32_t slot, uint64_t step, uint32_t purpose, float* out,
                         hipStream_t s);
 

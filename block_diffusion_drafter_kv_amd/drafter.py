@@ -171,7 +171,9 @@ class Drafter:
 
     def copy_cache(self, layer, slot, start, n):
         m = self.model
-        k = torch.empty((n, m.n_kv_heads, m.head_dim), dtype=self.dtype, device="cuda")
+        # cache element type: fp32, or fp16 for a bf16 drafter (fp16 operands)
+        ct = torch.float32 if self.dtype == torch.float32 else torch.float16
+        k = torch.empty((n, m.n_kv_heads, m.head_dim), dtype=ct, device="cuda")
         v = torch.empty_like(k)
         dflash_copy_cache(self.handle, _stream(), layer, slot, start, n, k.data_ptr(), v.data_ptr())
         return k, v

@@ -26,10 +26,18 @@
  *    word, read (and cleared) by dflash_get_error.
  *  - Weights are borrowed: the caller keeps them alive and unchanged for the
  *    handle's lifetime.  The handle owns the drafter KV cache, the per-slot
- *    context lengths and all scratch memory (allocated in dflash_create).
- *  - Element type: every weight, the KV cache and GEMM operands use
- *    cfg.dtype (fp32 or bf16); logits, probabilities and statistics are fp32;
- *    token ids, lengths and tree indices are int32.
+ *    context lengths and all scratch memory (allocated in dflash_create), and
+ *    for a bf16 drafter its own fp16 copies of the weight matrices (below).
+ *  - Element types.  cfg.dtype = DFLASH_F32: weights, target hidden states,
+ *    activations and KV cache are fp32.  cfg.dtype = DFLASH_BF16: weights and
+ *    target hidden states are bf16; every matrix product except the fc takes
+ *    fp16 operands with fp32 accumulation, so dflash_create converts q/k/v/o/
+ *    gate/up/down of every layer and the LM head once into fp16 copies scaled
+ *    by one power of two (exact for every weight of at least 2^-28 times the
+ *    largest |w|; the products are scaled back exactly), and the KV cache and
+ *    activations are fp16.  The fc product multiplies the given bf16 operands.
+ *    The residual stream is fp32 in both.  Logits, probabilities and
+ *    statistics are fp32; token ids, lengths and tree indices are int32.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -88,7 +96,10 @@ typedef struct dflash_config {
   int32_t max_tree;           /* largest tree_budget (0..256)                                      */
 } dflash_config;
 
-/* Per-layer weights, all [out_features, in_features] row-major, cfg.dtype. */
+/* Per-layer weights, all [out_features, in_features] row-major, cfg.dtype.
+ * Matrices and norm gains are read at create time (a bf16 drafter converts the
+ * matrices into its own fp16 copies then); the gains, embedding and fc are
+ * read again on every call. */
 typedef struct dflash_layer_weights {
   const void* in_norm;        /* [H]          pre-attention RMSNorm gain          */
   const void* q_w;            /* [n_q*d, H]                                       */
@@ -117,8 +128,10 @@ typedef struct dflash_handle dflash_handle;
 
 /* Create a handle: validates the shapes, allocates and zeroes the KV cache
  * (n_layers x max_batch x n_kv_heads x max_ctx positions of K and V), the
- * per-slot context lengths and the scratch memory.  Returns DFLASH_OK and
- * *out, or a negative status (nothing allocated). */
+ * per-slot context lengths and the scratch memory, and (bf16 drafter) makes the
+ * fp16 weight copies; synchronises the device.  Returns DFLASH_OK and *out, or
+ * a negative status (nothing allocated): DFLASH_E_INVALID also when a weight
+ * matrix holds Inf or NaN. */
 int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_handle** out);
 
 /* Synchronises the device and frees everything the handle owns. */
@@ -242,7 +255,8 @@ int dflash_profile_read(dflash_handle* h, int32_t n, double* ms, int32_t* launch
 int dflash_ctx_lens(dflash_handle* h, void* stream, int32_t* out_dev);
 
 /* Copy cache positions [start, start+n) of (layer, slot) as K and V, each
- * [n, n_kv_heads, head_dim] in cfg.dtype, to device buffers k_out / v_out. */
+ * [n, n_kv_heads, head_dim] in the cache element type (fp32, or fp16 for a
+ * bf16 drafter), to device buffers k_out / v_out. */
 int dflash_copy_cache(dflash_handle* h, void* stream, int32_t layer, int32_t slot, int32_t start, int32_t n,
                       void* k_out, void* v_out);
 

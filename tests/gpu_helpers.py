@@ -36,10 +36,6 @@ def inject_both(drafter, oracle, cfg, slots, counts, pos0, seed=2024):
             oracle.inject(s, r)
 
 
-def bf16_round(x: np.ndarray) -> np.ndarray:
-    return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
-
-
 def assert_close_report(got, want, atol, rtol=0.0, what=""):
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)

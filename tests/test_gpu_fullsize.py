@@ -1,0 +1,333 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py uses.
+
+The oracle cannot run every request of a full workload in seconds, so each test
+checks outputs it can compute one by one:
+  * KV cache rows at sampled positions (a row's K/V depend on that row only);
+  * the full draft logits of sampled requests (whole-request oracle forward);
+  * the other requests through properties that hold at any size (a request's
+    logits do not depend on the rest of the batch);
+  * selection, tree and verification at full vocabulary and batch from the same
+    fp32 logits fed to both sides (seeded CPU logits, no GPU output as input).
+Weights and hidden rows come from the seeded generators of ``synth``; rows of
+requests the oracle does not follow are drawn on the GPU with torch's generator.
+
+The oracle is the exact fp64 forward.  The library's bf16 drafters take fp16
+operands (11 significant bits) with fp32 accumulation; at 5 full-width layers
+their logits stay within the 2e-2 tolerance of the exact forward (bf16 operands,
+8 significant bits, would not: about 0.09 from the rounding of activations).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import drafter as od
+from oracle import select as osel
+from oracle import tree as otree
+from oracle import verify as over
+from synth import gen
+from synth.configs import get_workload
+
+from gpu_helpers import assert_close_report, to_cuda
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_TOL = 2e-2            # bf16 inputs, fp16 operands, fp32 accumulation
+# fp16 rounding of the fused feature (2.8e-4 RMS relative) and of the stored value
+# (at most 2^-11 relative): 3e-3 absolute is 8 sigma on unit-RMS k and v
+CACHE_ATOL, CACHE_RTOL = 3e-3, 2.0 ** -10
+
+
+def _dev(a, dtype=torch.int32):
+    return torch.tensor(np.asarray(a), dtype=dtype, device="cuda")
+
+
+def _build(cfg, *, max_batch, max_ctx, max_k=16, max_inject_rows=16384, max_top_k=0, max_tree=0, gains="ones"):
+    import block_diffusion_drafter_kv_amd as dk
+    w = gen.weights(cfg, seed=1234, gains=gains)
+    dr = dk.Drafter(cfg, to_cuda(w), max_batch=max_batch, max_ctx=max_ctx, max_k=max_k,
+                    max_inject_rows=max_inject_rows, max_top_k=max_top_k, max_tree=max_tree)
+    return dr, w
+
+
+def _gpu_rows(cfg, n, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return torch.randn((n, cfg.n_target_layers, cfg.target_hidden), generator=g, device="cuda",
+                       dtype=torch.float32).to(torch.bfloat16)
+
+
+def _inject_prompts(dr, cfg, ctx, oracle_slots, chunk=8192):
+    """bench.py's prompt injection (one call per request, chunks of 8192 rows).  Requests in
+    oracle_slots get rows from gen.hidden_rows (CPU, kept for the oracle); the others get
+    GPU-drawn rows.  Returns {slot: cpu rows}."""
+    keep = {}
+    for r, c in enumerate(ctx):
+        rows_cpu = gen.hidden_rows(cfg, r, 0, c) if r in oracle_slots else None
+        if rows_cpu is not None:
+            keep[r] = rows_cpu
+        for s0 in range(0, c, chunk):
+            n = min(chunk, c - s0)
+            rows = rows_cpu[s0:s0 + n].cuda() if rows_cpu is not None else _gpu_rows(cfg, n, 7000 + r * 97 + s0)
+            dr.inject(_dev([r]), _dev([0]), _dev([n]), n, rows.contiguous())
+    torch.cuda.synchronize()
+    assert dr.get_error() == 0
+    return keep
+
+
+def _check_cache_rows(dr, orc, cfg, slot, rows_cpu, positions):
+    """Cache rows at `positions` of `slot` against the oracle's row-local projection."""
+    pos = np.asarray(sorted(positions))
+    kv = orc.project_context(rows_cpu[pos], pos)
+    for layer in range(cfg.n_layers):
+        kw, vw = kv[layer]
+        for i, p in enumerate(pos):
+            k, v = dr.copy_cache(layer, slot, int(p), 1)
+            assert_close_report(k.float().cpu().numpy()[0], kw[i], CACHE_ATOL, CACHE_RTOL, f"K l{layer} p{p}")
+            assert_close_report(v.float().cpu().numpy()[0], vw[i], CACHE_ATOL, CACHE_RTOL, f"V l{layer} p{p}")
+
+
+def _check_logits(logits, ids, want, what):
+    assert_close_report(logits, want, LOGIT_TOL, what=what)
+    for j in range(want.shape[0]):
+        top, margin = osel.argmax_with_margin(want[j])
+        if margin > 2 * LOGIT_TOL:
+            assert ids[j] == top, f"{what} pos {j}"
+        else:
+            assert want[j][ids[j]] >= want[j].max() - 2 * LOGIT_TOL
+
+
+def test_full_b1_ctx2k(gpu_lib):
+    """Batch 1, context 2048, K = 16: the whole request against the oracle."""
+    wl = get_workload("b1_ctx2k")
+    cfg, K = wl.model, wl.K
+    dr, w = _build(cfg, max_batch=1, max_ctx=wl.ctx + 64, gains="random")
+    rows = _inject_prompts(dr, cfg, [wl.ctx], {0})[0]
+    orc = od.DrafterOracle(cfg, w)
+    del w
+    orc.inject(0, rows)
+    rng = np.random.default_rng(1)
+    _check_cache_rows(dr, orc, cfg, 0, rows, list(rng.choice(wl.ctx, 24, replace=False)) + [0, wl.ctx - 1])
+    anchor = int(gen.anchor_ids(cfg, 1, seed=5)[0])
+    o = dr.draft(_dev([0]), _dev([anchor]), K, temperature=0.0, want_logits=True)
+    torch.cuda.synchronize()
+    want = orc.block_logits(0, anchor, K)
+    _check_logits(o["logits"][0].cpu().numpy(), o["draft_ids"][0].cpu().numpy(), want, "b1 logits")
+    dr.close()
+
+
+def test_full_b32_ragged_bench_config(gpu_lib):
+    """The bench workload: batch 32, contexts U[512, 8192], K = 16, greedy."""
+    wl = get_workload("b32_ragged4k")
+    cfg, K, B = wl.model, wl.K, wl.batch
+    ctx = wl.ctx_lengths()
+    order = np.argsort(ctx)
+    sampled = [int(order[0]), int(order[1])]            # the two shortest contexts (full oracle forward)
+    dr, w = _build(cfg, max_batch=B, max_ctx=max(ctx) + 64, max_inject_rows=8192)
+    rows = _inject_prompts(dr, cfg, ctx, set(sampled))
+    orc = od.DrafterOracle(cfg, w)
+    del w
+    anchors = gen.anchor_ids(cfg, B, seed=3)
+    o = dr.draft(_dev(np.arange(B)), _dev(anchors), K, temperature=0.0, want_logits=True)
+    torch.cuda.synchronize()
+    assert dr.get_error() == 0
+    logits = o["logits"].cpu().numpy()
+    ids = o["draft_ids"].cpu().numpy()
+    for r in sampled:
+        orc.inject(r, rows[r])
+        _check_cache_rows(dr, orc, cfg, r, rows[r], [0, 1, ctx[r] // 2, ctx[r] - 1])
+        want = orc.block_logits(r, int(anchors[r]), K)
+        _check_logits(logits[r], ids[r], want, f"b32 req {r} (ctx {ctx[r]})")
+        orc.reset(r)
+    # other requests: a batch-1 draft of the request alone gives the same logits.  The two
+    # calls split the products' K sums differently (the split depends on the row count), so
+    # they agree to the arithmetic's rounding, not bit for bit: within the logit tolerance,
+    # with equal greedy ids wherever the batch-1 margin exceeds twice of it.
+    for r in (int(order[-1]), int(order[B // 2])):
+        one = dr.draft(_dev([r]), _dev(anchors[r:r + 1]), K, temperature=0.0, want_logits=True)
+        torch.cuda.synchronize()
+        z1 = one["logits"][0].cpu().numpy()
+        _check_logits(logits[r], ids[r], z1.astype(np.float64), f"batch composition, req {r}")
+    dr.close()
+
+
+@pytest.mark.timeout(900)
+def test_full_b4_ctx32k_rejection(gpu_lib):
+    """Batch 4 with 32768-row prompts injected in one call, then a T = 1 draft and
+    rejection verification (Philox seed 99)."""
+    wl = get_workload("b4_ctx32k")
+    cfg, K, B, C = wl.model, wl.K, wl.batch, wl.ctx
+    dr, w = _build(cfg, max_batch=B, max_ctx=C + 64, max_inject_rows=B * C)
+    rows0 = gen.hidden_rows(cfg, 0, 0, C)
+    others = _gpu_rows(cfg, (B - 1) * C, 99)
+    allrows = torch.cat([rows0.cuda(), others], dim=0).contiguous()
+    dr.inject(_dev(np.arange(B)), _dev(np.arange(B) * C), _dev([C] * B), B * C, allrows)
+    torch.cuda.synchronize()
+    assert dr.get_error() == 0
+    assert list(dr.ctx_lens().cpu().numpy()[:B]) == [C] * B
+    orc = od.DrafterOracle(cfg, w)
+    del w
+    rng = np.random.default_rng(2)
+    for r in range(B):      # sampled cache rows of every request (first, last and random positions)
+        pos = [0, C - 1] + list(rng.choice(C, 6, replace=False))
+        src = rows0 if r == 0 else allrows[r * C:(r + 1) * C][np.sort(pos)].cpu()
+        if r == 0:
+            _check_cache_rows(dr, orc, cfg, 0, rows0, pos)
+        else:
+            sub = {p: i for i, p in enumerate(np.sort(pos))}
+            kv = orc.project_context(src, np.sort(pos))
+            for layer in range(cfg.n_layers):
+                for p, i in sub.items():
+                    k, v = dr.copy_cache(layer, r, int(p), 1)
+                    assert_close_report(k.float().cpu().numpy()[0], kv[layer][0][i], CACHE_ATOL, CACHE_RTOL,
+                                        f"K r{r} l{layer} p{p}")
+                    assert_close_report(v.float().cpu().numpy()[0], kv[layer][1][i], CACHE_ATOL, CACHE_RTOL,
+                                        f"V r{r} l{layer} p{p}")
+    del allrows, others
+    # request 0: full 32K-context forward against the oracle
+    orc.inject(0, rows0)
+    anchors = gen.anchor_ids(cfg, B, seed=4)
+    o = dr.draft(_dev(np.arange(B)), _dev(anchors), K, temperature=1.0, seed=wl.philox_seed, step=0,
+                 want_logits=True)
+    torch.cuda.synchronize()
+    want = orc.block_logits(0, int(anchors[0]), K)
+    assert_close_report(o["logits"][0].cpu().numpy(), want, LOGIT_TOL, what="32K logits")
+    # T = 1 draws of the fused LM-head path equal the stand-alone selection from the same logits
+    # (the draws themselves are pinned against the oracle in test_full_topk_tree_b64)
+    sel = dr.select_from_logits(_dev(np.arange(B)), _dev(anchors), o["logits"], temperature=1.0,
+                                seed=wl.philox_seed, step=0)
+    torch.cuda.synchronize()
+    assert torch.equal(sel["draft_ids"], o["draft_ids"])
+    dr.close()
+
+
+def test_full_verify_greedy_b32(gpu_lib):
+    """Greedy verification at the bench shapes (B = 32, K = 16, V = 151936)."""
+    wl = get_workload("b32_ragged4k")
+    cfg, K, B, V = wl.model, wl.K, wl.batch, wl.model.vocab
+    import block_diffusion_drafter_kv_amd as dk
+    dr = dk.Drafter(cfg, _idle_weights(cfg), max_batch=B, max_ctx=64, max_k=K, max_inject_rows=64)
+    t = gen.logits_like((B, K + 1, V), 2.0, 31, "target").numpy()
+    post = t.argmax(axis=2)
+    rng = np.random.default_rng(7)
+    acc = rng.integers(0, K + 1, B)                      # accepted prefix length per request
+    d = rng.integers(0, V, (B, K)).astype(np.int32)
+    for i in range(B):
+        d[i, :acc[i]] = post[i, :acc[i]]
+        if acc[i] < K and d[i, acc[i]] == post[i, acc[i]]:
+            d[i, acc[i]] = (post[i, acc[i]] + 1) % V
+    r = dr.verify(_dev(np.arange(B)), _dev(d), None, torch.tensor(t, device="cuda"), temperature=0.0)
+    torch.cuda.synchronize()
+    for i in range(B):
+        want = over.verify_greedy(d[i], t[i])
+        L = want["out_len"]
+        assert r["out_len"][i].item() == L == acc[i] + 1
+        assert list(r["out_tokens"][i].cpu().numpy()[:L]) == list(want["out_tokens"])
+    dr.close()
+
+
+def test_full_verify_rejection_b4(gpu_lib):
+    """Rejection verification at T = 1 at the long-context workload's shapes (B = 4, K = 16)."""
+    wl = get_workload("b4_ctx32k")
+    cfg, K, B, V = wl.model, wl.K, wl.batch, wl.model.vocab
+    import block_diffusion_drafter_kv_amd as dk
+    dr = dk.Drafter(cfg, _idle_weights(cfg), max_batch=B, max_ctx=64, max_k=K, max_inject_rows=64)
+    z = gen.logits_like((B, K, V), 2.0, 41, "draft").numpy()
+    t = np.concatenate([z, np.zeros((B, 1, V), np.float32)], axis=1) + \
+        gen.logits_like((B, K + 1, V), wl.sigma, 42, "noise").numpy()
+    checked = 0
+    for step in range(3):
+        d = np.stack([osel.select_block(z[i], 1.0, 0, wl.philox_seed, i, step)["draft_ids"] for i in range(B)])
+        r = dr.verify(_dev(np.arange(B)), _dev(d), torch.tensor(z, device="cuda"), torch.tensor(t, device="cuda"),
+                      temperature=1.0, seed=wl.philox_seed, step=step)
+        torch.cuda.synchronize()
+        for i in range(B):
+            w = over.verify_rejection(d[i], z[i], t[i], 1.0, wl.philox_seed, i, step)
+            if w["near_margin"] < 1e-5:
+                continue
+            checked += 1
+            L = w["out_len"]
+            assert r["out_len"][i].item() == L
+            assert list(r["out_tokens"][i].cpu().numpy()[:L]) == list(w["out_tokens"])
+    assert checked >= 3 * B - 1
+    dr.close()
+
+
+def test_full_topk_tree_b64(gpu_lib):
+    """Per-position top-64 and the best-first B = 64 prefix tree at the larger drafter's
+    shapes (batch 64, K = 16, V = 151936), from the same fp32 logits on both sides."""
+    wl = get_workload("b64_tree")
+    cfg, K, B, V = wl.model, wl.K, wl.batch, wl.model.vocab
+    import block_diffusion_drafter_kv_amd as dk
+    dr = dk.Drafter(cfg, _idle_weights(cfg), max_batch=B, max_ctx=64, max_k=K, max_inject_rows=64,
+                    max_top_k=wl.top_k, max_tree=wl.tree_budget)
+    z = gen.logits_like((B, K, V), 3.0, 51, "marginals").numpy()
+    anchors = gen.anchor_ids(cfg, B, seed=6)
+    o = dr.select_from_logits(_dev(np.arange(B)), _dev(anchors), torch.tensor(z, device="cuda"), temperature=1.0,
+                              seed=1, step=0, top_k=wl.top_k, tree_budget=wl.tree_budget)
+    torch.cuda.synchronize()
+    tk_ids = o["topk_ids"].cpu().numpy()
+    tk_p = o["topk_probs"].cpu().numpy()
+    draws = o["draft_ids"].cpu().numpy()
+    for i in range(B):
+        q = osel.softmax(z[i], 1.0)
+        sel = osel.select_block(z[i], 1.0, 0, 1, i, 0)       # T = 1 draws: Philox seed 1, slot i, step 0
+        for j in range(K):
+            if sel["margins"][j] > 1e-5:
+                assert draws[i, j] == sel["draft_ids"][j], f"draw req {i} pos {j}"
+        ids = np.stack([osel.topk(z[i][j], wl.top_k) for j in range(K)])
+        assert np.array_equal(tk_ids[i], ids), f"top-k req {i}"
+        assert_close_report(tk_p[i], np.take_along_axis(q, ids, axis=1), 1e-6, 1e-4, f"top-k probs req {i}")
+        Bt = wl.tree_budget
+        probs = np.take_along_axis(q, ids[:, :min(Bt, V)], axis=1)
+        tok, par, dep, pri = otree.build_tree(probs, ids[:, :min(Bt, V)], Bt)
+        gp = o["tree_parents"][i].cpu().numpy()
+        gaps = np.abs(np.diff(np.sort(pri)))
+        if gaps.size == 0 or gaps.min() > 1e-5 * pri.max():
+            assert np.array_equal(o["tree_tokens"][i].cpu().numpy()[1:], tok[1:]), f"tree req {i}"
+            assert np.array_equal(gp, par) and np.array_equal(o["tree_depth"][i].cpu().numpy(), dep)
+        bits = o["tree_mask"][i].cpu().numpy().view(np.uint64)
+        assert np.array_equal(otree.mask_bits(otree.ancestor_mask(gp)), bits)
+    dr.close()
+
+
+@pytest.mark.timeout(900)
+def test_full_b64_larger_drafter_forward(gpu_lib):
+    """The larger drafter (hidden 5120, 64/8 heads, two q-row parts per kv head) at batch 64,
+    context 8192: sampled cache rows and one request's full forward against the oracle."""
+    wl = get_workload("b64_tree")
+    cfg, K, B, C = wl.model, wl.K, wl.batch, wl.ctx
+    dr, w = _build(cfg, max_batch=B, max_ctx=C + 64, max_top_k=wl.top_k, max_tree=wl.tree_budget)
+    rows = _inject_prompts(dr, cfg, [C] * B, {0})
+    orc = od.DrafterOracle(cfg, w)
+    del w
+    orc.inject(0, rows[0])
+    _check_cache_rows(dr, orc, cfg, 0, rows[0], [0, 1, 4097, C - 1])
+    anchors = gen.anchor_ids(cfg, B, seed=8)
+    o = dr.draft(_dev(np.arange(B)), _dev(anchors), K, temperature=1.0, seed=1, step=0, top_k=wl.top_k,
+                 tree_budget=wl.tree_budget, want_logits=True)
+    torch.cuda.synchronize()
+    assert dr.get_error() == 0
+    want = orc.block_logits(0, int(anchors[0]), K)
+    assert_close_report(o["logits"][0].cpu().numpy(), want, LOGIT_TOL, what="b64 req 0 logits")
+    # the tree outputs are well formed for every request: root = anchor, parents precede children
+    par = o["tree_parents"].cpu().numpy()
+    dep = o["tree_depth"].cpu().numpy()
+    assert (o["tree_tokens"][:, 0].cpu().numpy() == anchors).all()
+    for i in range(B):
+        assert par[i, 0] == -1 and all(0 <= par[i, n] < n for n in range(1, wl.tree_budget + 1))
+        assert all(dep[i, n] == dep[i, par[i, n]] + 1 for n in range(1, wl.tree_budget + 1))
+    dr.close()
+
+
+def _idle_weights(cfg):
+    """Valid device weights for a handle that only runs selection / verification (never
+    read): zero tensors of the right shapes, one set shared by all layers."""
+    dt = torch.bfloat16
+    z = lambda *s: torch.zeros(*s, dtype=dt, device="cuda")
+    H, F = cfg.hidden, cfg.ffn
+    w = {"embed": z(cfg.vocab, H), "lm_head": z(cfg.vocab, H), "fc": z(H, cfg.feat_dim), "hidden_norm": z(H),
+         "final_norm": z(H), "layers": []}
+    lw = {"in_norm": z(H), "q_w": z(cfg.q_dim, H), "k_w": z(cfg.kv_dim, H), "v_w": z(cfg.kv_dim, H),
+          "o_w": z(H, cfg.q_dim), "q_norm": z(cfg.head_dim), "k_norm": z(cfg.head_dim), "post_norm": z(H),
+          "gate_w": z(F, H), "up_w": z(F, H), "down_w": z(H, F)}
+    w["layers"] = [lw] * cfg.n_layers
+    return w

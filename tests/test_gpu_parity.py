@@ -1,7 +1,8 @@
 """GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
 
-Tolerances: bf16 logits 2e-2 absolute on N(0,1)-scale values; fp32 logits
-1e-4; K/V cache within 2 bf16 ulp (bf16) or 1e-5 relative (fp32).  Discrete
+Tolerances: logits of a bf16 drafter (fp16 operands, fp32 accumulation) 2e-2
+absolute on N(0,1)-scale values; fp32 logits 1e-4; K/V cache of a bf16 drafter
+within the fp16 rounding bound derived below, fp32 within 2e-5.  Discrete
 outputs are compared exactly where the oracle's own decision margin exceeds
 what the kernel's rounding can move, and checked for validity otherwise.
 """
@@ -16,7 +17,7 @@ from oracle import verify as over
 from synth import gen
 from synth.configs import TINY, QWEN3_8B_SHAPED, scaled_model
 
-from gpu_helpers import assert_close_report, bf16_round, inject_both, make_pair
+from gpu_helpers import assert_close_report, inject_both, make_pair
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +27,14 @@ SMALL_BF16 = scaled_model(QWEN3_8B_SHAPED, n_layers=2, hidden=256, n_q_heads=4, 
 # grouped heads that need two q-row halves per kv head at K = 16 (g = 8), head_dim 64
 GQA8_BF16 = scaled_model(QWEN3_8B_SHAPED, n_layers=1, hidden=256, n_q_heads=16, n_kv_heads=2, head_dim=64,
                          ffn=256, vocab=777, n_target_layers=3, target_hidden=128, mask_token_id=776)
+
+
+# K/V cache of a bf16 drafter.  The fused feature g enters the K/V product as an
+# fp16 operand (relative rounding error uniform in +-2^-11, RMS 2^-11/sqrt(3) =
+# 2.8e-4), so k (unit RMS after its norm) and v (RMS ~1.3 here) carry about 2.8e-4
+# and 3.7e-4 RMS absolute error; the fp16 store adds at most 2^-11 relative.
+# Bound: 3e-3 absolute (8 sigma) + 2^-10 relative.
+CACHE_ATOL_F16, CACHE_RTOL_F16 = 3e-3, 2.0 ** -10
 
 
 def _dev(a, dtype=torch.int32):
@@ -61,12 +70,8 @@ def test_inject_cache_parity(gpu_lib, cfg):
                 assert_close_report(k, kw, atol=2e-5, rtol=2e-5, what="K cache")
                 assert_close_report(v, vw, atol=2e-5, rtol=2e-5, what="V cache")
             else:
-                # bf16 path: the fused feature g is rounded to bf16 before the K/V product
-                # (relative 2^-9 per element), which leaves ~1.1e-3 RMS absolute error on a
-                # unit-RMS normalised k; the cache store adds at most half a bf16 ulp.
-                # Bound: 2^-8 relative + 1e-2 absolute (about 5 sigma of the former).
-                assert_close_report(k, kw, atol=1e-2, rtol=2.0 ** -8, what="K cache")
-                assert_close_report(v, vw, atol=1e-2, rtol=2.0 ** -8, what="V cache")
+                assert_close_report(k, kw, atol=CACHE_ATOL_F16, rtol=CACHE_RTOL_F16, what="K cache")
+                assert_close_report(v, vw, atol=CACHE_ATOL_F16, rtol=CACHE_RTOL_F16, what="V cache")
     dr.close()
 
 
@@ -129,8 +134,11 @@ def test_incremental_equals_from_scratch_gpu(gpu_lib):
     for layer in range(cfg.n_layers):
         ka, va = a.copy_cache(layer, 0, 0, 600)
         kb, vb = b.copy_cache(layer, 0, 0, 600)
-        assert_close_report(kb.float().cpu().numpy(), ka.float().cpu().numpy(), atol=2e-2, what="K incremental")
-        assert_close_report(vb.float().cpu().numpy(), va.float().cpu().numpy(), atol=2e-2, what="V incremental")
+        # same arithmetic per row; only the products' split of K may differ with the call's row count
+        assert_close_report(kb.float().cpu().numpy(), ka.float().cpu().numpy(), atol=1e-3, rtol=2.0 ** -10,
+                            what="K incremental")
+        assert_close_report(vb.float().cpu().numpy(), va.float().cpu().numpy(), atol=1e-3, rtol=2.0 ** -10,
+                            what="V incremental")
     a.close()
     b.close()
 
