@@ -11,12 +11,27 @@ void gemm_dispatch_bf16(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, con
 GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide) {
   GemmPlan p;
   const bool w16 = op != OP_F32;
-  p.bn = (wide && w16) ? 256 : 128;
+  p.bn = 128;
   p.bm = M <= 64 ? 64 : 128;
+  if (w16 && wide) {
+    // the vocabulary product: 128 x 128 tiles with a 3-deep weight ring (measured
+    // on the 512 x 151936 x 4096 LM head: 743 us, against 1023 us for 128 x 256)
+    p.bm = 128;
+    p.sb = 3;
+    return p;
+  }
+  if (w16 && K >= 8192 && M > 64 && M <= 1024) {
+    // long products over few rows (the MLP down projection): 128 x 128, 3-deep
+    // weight ring, K split in four (544 x 4096 x 12288: 101 us, against 120 us
+    // for 64 x 128 tiles without a split)
+    p.sb = 3;
+    p.splits = 4;
+    return p;
+  }
   // 16-bit: 64-row tiles (3 LDS stages, two work-groups per CU) whenever 128-row
   // tiles would leave fewer than two work-groups per CU (measured on the draft's
   // 544-row products: O 66 -> 45 us, down 175 -> 116 us, QKV 69 -> 56 us)
-  if (w16 && !wide && p.bm == 128 && (long)((M + 127) / 128) * ((N + p.bn - 1) / p.bn) < 2L * num_cus)
+  if (w16 && p.bm == 128 && (long)((M + 127) / 128) * ((N + p.bn - 1) / p.bn) < 2L * num_cus)
     p.bm = 64;
   const int bk = w16 ? 64 : 32;
   const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);

@@ -4,7 +4,7 @@
 // shapes (measured on MI355X):
 //   16-bit, M > 64 : 128 x 128, 2 LDS stages (64 KB: two work-groups per CU)
 //   16-bit, M <= 64: 64 x 128, 3 stages
-//   16-bit LM head : 128 x 256 (or 64 x 256), 3 stages (fewer, wider tiles over the vocabulary)
+//   16-bit LM head and long-K products: 128 x 128, A 2 stages, B 3 stages
 //   fp32           : 128 x 128 or 64 x 128
 #pragma once
 #include "gemm2.h"
@@ -40,13 +40,9 @@ static void gemm1_go(const GemmArgs& g, const void* ep, hipStream_t s) {
 template <typename T, class Epi>
 static void gemm_cfg(const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (pl.bn == 256) {
-      if (pl.bm == 64) gemm2_go<T, 64, 256, 3, 3, Epi>(g, ep, s);
-      else gemm2_go<T, 128, 256, 3, 3, Epi>(g, ep, s);
-    } else {
-      if (pl.bm == 64) gemm2_go<T, 64, 128, 3, 3, Epi>(g, ep, s);
-      else gemm2_go<T, 128, 128, 2, 2, Epi>(g, ep, s);
-    }
+    if (pl.bm == 64) gemm2_go<T, 64, 128, 3, 3, Epi>(g, ep, s);
+    else if (pl.sb == 3) gemm2_go<T, 128, 128, 2, 3, Epi>(g, ep, s);
+    else gemm2_go<T, 128, 128, 2, 2, Epi>(g, ep, s);
   } else {
     if (pl.bm == 64) gemm1_go<64, Epi>(g, ep, s);
     else gemm1_go<128, Epi>(g, ep, s);
