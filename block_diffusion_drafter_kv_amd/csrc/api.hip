@@ -44,6 +44,7 @@ struct dflash_handle {
   float *o_part = nullptr, *m_part = nullptr, *l_part = nullptr;
   AttnPlan* plan = nullptr;
   int32_t *seg_start = nullptr, *chunk_base = nullptr;
+  int4 *seg_desc = nullptr, *wg_range = nullptr;
   int32_t* dslots = nullptr;              // validated slot ids of the current draft
   float* partials = nullptr;
   size_t partials_elems = 0;
@@ -319,9 +320,10 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
   h->Rpad = ((R + 31) / 32) * 32;
   h->QRpad = ((g * R + 15) / 16) * 16 + 80;
   h->ctx_alloc = ((int64_t)(c.max_ctx + 63) / 64) * 64 + 64;
-  // attention: two work-groups per CU (80 KB LDS ring each); at most kAttnChunkMax
-  // partial records (chunks) per segment
-  h->attn_wg = 2 * h->num_cus;
+  // attention work-groups: one producer / consumer work-group per CU for 16-bit
+  // K/V (128 KB LDS ring), two per CU for fp32; at most kAttnChunkMax partial
+  // records (chunks) per segment
+  h->attn_wg = (c.dtype == DFLASH_BF16 ? 1 : 2) * h->num_cus;
   h->piece_cap = c.max_batch * nkv * splits * kAttnChunkMax;
   h->op = c.dtype == DFLASH_BF16 ? OP_F16 : OP_F32;
   h->op_fc = c.dtype == DFLASH_BF16 ? OP_BF16 : OP_F32;
@@ -354,6 +356,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc_t(h, &h->plan, 1, sizeof(AttnPlan)))) break;
     if ((rc = alloc_t(h, &h->seg_start, (size_t)c.max_batch * nkv * splits + 1, 4))) break;
     if ((rc = alloc_t(h, &h->chunk_base, (size_t)c.max_batch * nkv * splits, 4))) break;
+    if ((rc = alloc_t(h, &h->seg_desc, (size_t)c.max_batch * nkv * splits, 16))) break;
+    if ((rc = alloc_t(h, &h->wg_range, (size_t)h->attn_wg, 16))) break;
     if ((rc = alloc_t(h, &h->dslots, c.max_batch, 4))) break;
     // split-K is used only while tiles * splits <= 2 * CUs: bounded by that many output tiles
     // split-K partials: grids of at most 2 * CUs tiles, or a four-way split of the
@@ -589,7 +593,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   {
     Phase ph(h, s, DFLASH_PH_ATTN_PLAN);
     launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->attn_wg, kAttnMinGroups, kAttnChunkMin,
-                     kAttnChunkMax, h->plan, h->seg_start, h->chunk_base, s);
+                     kAttnChunkMax, h->plan, h->seg_start, h->chunk_base, h->seg_desc, h->wg_range, s);
   }
   const int64_t layer_cache = (int64_t)(c.max_batch + 1) * nkv * h->ctx_alloc * d * h->esize;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -635,6 +639,8 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       a.plan = h->plan;
       a.seg_start = h->seg_start;
       a.chunk_base = h->chunk_base;
+      a.seg_desc = h->seg_desc;
+      a.wg_range = h->wg_range;
       a.n_seg = n_req * nkv * splits;
       a.chunk_min = kAttnChunkMin;
       a.chunk_max = kAttnChunkMax;

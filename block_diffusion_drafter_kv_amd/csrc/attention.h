@@ -42,6 +42,8 @@ struct AttnArgs {
   const AttnPlan* plan;
   const int32_t* seg_start;   // [n_seg + 1] first group of each segment (segment s = (r*n_kv + kv)*splits + z)
   const int32_t* chunk_base;  // [n_seg] first partial-result record (chunk) of each segment
+  const int4* seg_desc;       // [n_seg] (slot, context length, first group, group count)
+  const int4* wg_range;       // [work-groups] (first group, end group, segment of the first group, -)
   float* o_part;              // [chunk][QRT*16][D]
   float* m_part;              // [chunk][QRT*16]   running max (exp2 domain)
   float* l_part;              // [chunk][QRT*16]   sum of exp2(s - m)

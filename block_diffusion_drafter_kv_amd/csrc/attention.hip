@@ -32,7 +32,8 @@ __device__ int block_exclusive_scan(int v, int* buf, int* carry) {
 __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* slots, const int32_t* ctx_len, int n_req,
                                                          int n_kv, int splits, int n_wg_max, int min_per_wg,
                                                          int chunk_min, int chunk_max, AttnPlan* plan,
-                                                         int32_t* seg_start, int32_t* chunk_base) {
+                                                         int32_t* seg_start, int32_t* chunk_base, int4* seg_desc,
+                                                         int4* wg_range) {
   __shared__ int buf[256];
   __shared__ int carry;
   const int tid = threadIdx.x;
@@ -67,6 +68,31 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* slots, co
     }
     const int cb = block_exclusive_scan(cnt, buf, &carry);
     if (s < n_seg) chunk_base[s] = cb;
+  }
+  // per-segment descriptors and per-work-group ranges, so that an attention
+  // work-group starts with two loads instead of dependent searches
+  for (int s = tid; s < n_seg; s += 256)
+    seg_desc[s] = make_int4(slots[s / per_req], ctx_len[slots[s / per_req]], seg_start[s], seg_start[s + 1] - seg_start[s]);
+  auto find_seg = [&](int x) {   // last s with seg_start[s] <= x
+    int lo = 0, hi = n_seg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seg_start[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  auto chunk_start = [&](int x) {   // first chunk start at or after group x
+    if (x >= total) return total;
+    const int sg = find_seg(x);
+    const int b = seg_start[sg], e = seg_start[sg + 1];
+    const int cg = attn_chunk_groups(e - b, chunk_min, chunk_max);
+    return min(e, b + (x - b + cg - 1) / cg * cg);
+  };
+  for (int w = tid; w < n_wg_max; w += 256) {
+    const int g0 = chunk_start(min(w * per_wg, total));
+    const int g1 = chunk_start(min((w + 1) * per_wg, total));
+    wg_range[w] = make_int4(g0, g1, g0 < total ? find_seg(g0) : 0, 0);
   }
 }
 
@@ -143,41 +169,21 @@ void attn_kernel(const AttnArgs a) {
   typedef typename Frag<T>::type FragT;
   __shared__ uint4 ring[S][IPG * 64];
 
-  const int w = blockIdx.x;
-  const int per_wg = a.plan->per_wg, total = a.plan->total;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, r16 = lane & 15;
-
-  // segment holding group x: the last s with seg_start[s] <= x
-  auto find_seg = [&](int x) {
-    int lo = 0, hi = a.n_seg - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.seg_start[mid] <= x) lo = mid;
-      else hi = mid - 1;
-    }
-    return lo;
-  };
-  // first chunk start at or after group x
-  auto chunk_start = [&](int x) {
-    if (x >= total) return total;
-    const int s = find_seg(x);
-    const int b = a.seg_start[s], e = a.seg_start[s + 1];
-    const int cg = attn_chunk_groups(e - b, a.chunk_min, a.chunk_max);
-    return min(e, b + (x - b + cg - 1) / cg * cg);
-  };
-  const int g0 = chunk_start(min(w * per_wg, total));
-  const int g1 = chunk_start(min((w + 1) * per_wg, total));
+  const int4 rg = a.wg_range[blockIdx.x];   // (first group, end group, first segment), from the plan
+  const int g0 = rg.x, g1 = rg.y;
   if (g0 >= g1) return;
 
   auto decode = [&](int s, AttnSeg<T>& d) {
     const int per_req = a.n_kv * a.splits;
     const int r = s / per_req, rem = s - r * per_req, kv = rem / a.splits, z = rem - kv * a.splits;
-    const int slot = a.slots[r];
-    d.C = a.ctx_len[slot];
+    const int4 sd = a.seg_desc[s];   // (slot, context length, first group, group count)
+    const int slot = sd.x;
+    d.C = sd.y;
     d.ncache = (d.C + KV_BLOCK - 1) / KV_BLOCK;
-    d.start = a.seg_start[s];
-    d.len = a.seg_start[s + 1] - d.start;
+    d.start = sd.z;
+    d.len = sd.w;
     d.cg = attn_chunk_groups(d.len, a.chunk_min, a.chunk_max);
     const int64_t head = (int64_t)slot * a.n_kv + kv;
     d.kc = (const T*)a.cache_k + head * a.ctx_alloc * D;
@@ -188,7 +194,7 @@ void attn_kernel(const AttnArgs a) {
     d.qrow = bh * a.QRpad + (int64_t)z * a.rows_per_split + wave * 16 + r16;
   };
 
-  const int s0 = find_seg(g0);
+  const int s0 = rg.z;
 
   // copy cursor
   AttnSeg<T> is;
@@ -373,6 +379,238 @@ void attn_kernel(const AttnArgs a) {
   }
 }
 
+// Streamed attention, producer / consumer.  Work-group w takes the group range
+// wg_range[w] of the plan.  The last NP waves only copy: between them they keep
+// S-1 groups of K/V in flight into the LDS ring, so that the issue of the copies
+// (about 10 bytes per clock per wave at most on gfx950, and stalling while the
+// memory system is saturated) overlaps the arithmetic.  The NW-NP other waves
+// split the segment's QRT query tiles (wave v: tiles [v*TW, min(QRT, (v+1)*TW)),
+// TW = ceil(QRT/(NW-NP))); a consumer keeps
+// the group's K and V fragments in registers across its tiles and its tiles' Q
+// fragments in registers across the whole segment.  One barrier per group
+// publishes the group and frees the ring stage of the previous one.  Per group and tile: S^T (32 x 16) = K Q^T, P = exp2(scale*s
+// - m) with the lazy integer reference m (as in attn_kernel), O^T += V^T P^T.
+template <typename T, int D, int QRT, int NW, int NP, int S>
+__global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
+  constexpr int KS = D / 32, DT = D / 16, ROWS = QRT * 16;
+  constexpr int NC = NW - NP;                              // consumer waves
+  constexpr int TW = (QRT + NC - 1) / NC;
+  constexpr int BLK = KV_BLOCK * D;                        // elements of a K (or V) block
+  constexpr int EPC = 16 / (int)sizeof(T);                 // elements per 16-byte copy
+  constexpr int IPG = 2 * BLK / (64 * EPC);                // 1 KB wave copies per group (K, then V)
+  constexpr int PER = IPG / NP;                            // copies per producer wave per group
+  constexpr int VOFF = IPG / 2 * 64;                       // first uint4 of the V block in a stage
+  constexpr int MAXA = (S - 1) * PER < 64 ? S - 1 : 63 / PER;
+  constexpr float TAU = 8.f;
+  static_assert(sizeof(T) == 2 && NW > NP && IPG % NP == 0 && S >= 2 && S <= 9, "shape");
+  typedef typename Frag<T>::type FragT;
+  __shared__ uint4 ring[S][IPG * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane >> 4, r16 = lane & 15;
+  const bool producer = wave >= NC;
+  const int t0 = wave * TW, nt = producer ? 0 : min(TW, QRT - t0);
+  const int4 rg = a.wg_range[blockIdx.x];
+  const int g0 = rg.x, g1 = rg.y;
+  if (g0 >= g1) return;
+
+  struct Seg {
+    const T* kc; const T* vc; const T* kb; const T* vb;
+    int start, len, ncache, C, cg;
+    int64_t q0;
+  };
+  auto decode = [&](int s, Seg& d) {
+    const int per_req = a.n_kv * a.splits;
+    const int r = s / per_req, rem = s - r * per_req, kv = rem / a.splits, z = rem - kv * a.splits;
+    const int4 sd = a.seg_desc[s];
+    const int slot = sd.x;
+    d.C = sd.y;
+    d.ncache = (d.C + KV_BLOCK - 1) / KV_BLOCK;
+    d.start = sd.z;
+    d.len = sd.w;
+    d.cg = attn_chunk_groups(d.len, a.chunk_min, a.chunk_max);
+    const int64_t head = (int64_t)slot * a.n_kv + kv;
+    d.kc = (const T*)a.cache_k + head * a.ctx_alloc * D;
+    d.vc = (const T*)a.cache_v + head * a.ctx_alloc * D;
+    const int64_t bh = (int64_t)r * a.n_kv + kv;
+    d.kb = (const T*)a.kb + bh * a.Rpad * D;
+    d.vb = (const T*)a.vb + bh * a.Rpad * D;
+    d.q0 = bh * a.QRpad + (int64_t)z * a.rows_per_split;
+  };
+
+  // ---- copy cursor (producer)
+  const int s0 = rg.z;
+  Seg is;
+  decode(s0, is);
+  int is_s = s0, is_l = g0 - is.start, issued = g0, is_stage = 0;
+  auto issue = [&]() {
+    const bool in_cache = is_l < is.ncache;
+    const T* kp = (in_cache ? is.kc + (int64_t)is_l * BLK : is.kb) + lane * EPC;
+    const T* vp = (in_cache ? is.vc + (int64_t)is_l * BLK : is.vb) + lane * EPC;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      const int i = (wave - NC) * PER + c;
+      const T* src = i < IPG / 2 ? kp + i * 64 * EPC : vp + (i - IPG / 2) * 64 * EPC;
+      copy16_to_lds(src, &ring[is_stage][i * 64]);
+    }
+    ++issued;
+    if (++is_stage == S) is_stage = 0;
+    if (++is_l == is.len && issued < g1) {
+      ++is_s;
+      decode(is_s, is);
+      is_l = 0;
+    }
+  };
+
+  // ---- compute cursor
+  Seg cs = is;
+  int cs_s = s0, cl = g0 - cs.start;
+  FragT qf[TW][KS];
+  auto load_q = [&]() {
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      const int row = (t0 + t) * 16 + r16;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (t < nt && row < a.rows_per_split)
+          *(uint4*)&qf[t][s] = *(const uint4*)((const T*)a.qb + (cs.q0 + row) * D + s * 32 + grp * 8);
+        else
+          *(uint4*)&qf[t][s] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  load_q();
+
+  f32x4 acc[TW][DT];
+  float m_ref[TW], l_sum[TW];
+  const float c = a.scale_log2;
+  auto reset = [&]() {
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_ref[t] = -INFINITY;
+      l_sum[t] = 0.f;
+    }
+  };
+  reset();
+
+  auto compute = [&](int stage) {
+    const uint4* st = ring[stage];
+    const int nval = cl < cs.ncache ? min(KV_BLOCK, cs.C - KV_BLOCK * cl) : a.R;
+    FragT kf[2 * KS], vf[DT];
+#pragma unroll
+    for (int f = 0; f < 2 * KS; ++f) *(uint4*)&kf[f] = st[f * 64 + lane];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *(uint4*)&vf[dt] = st[VOFF + dt * 64 + lane];
+    if (nval < KV_BLOCK) {   // stale cache contents past the end must not turn 0 * x into NaN
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (grp * 8 + e >= nval) vf[dt][e] = (T)0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      if (t >= nt) break;
+      f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        Frag<T>::mma(sc0, kf[s], qf[t][s]);
+        Frag<T>::mma(sc1, kf[KS + s], qf[t][s]);
+      }
+      // lane holds keys 8*grp + i (sc0) and 8*grp + 4 + i (sc1), query row r16 of the tile
+      if (nval < KV_BLOCK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (8 * grp + i >= nval) sc0[i] = -INFINITY;
+          if (8 * grp + 4 + i >= nval) sc1[i] = -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(sc0[i], sc1[i]));
+      mx *= c;
+      if (__any(mx > m_ref[t] + TAU)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m_ref[t], ceilf(mx));
+        const float alpha = mnew > m_ref[t] ? __builtin_amdgcn_exp2f(m_ref[t] - mnew) : 1.f;   // a power of two
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[t][dt] *= alpha;
+        l_sum[t] *= alpha;
+        m_ref[t] = mnew;
+      }
+      FragT pf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc0[i], c, -m_ref[t]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc1[i], c, -m_ref[t]));
+        l_sum[t] += p0 + p1;
+        pf[i] = (T)p0;
+        pf[4 + i] = (T)p1;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) Frag<T>::mma(acc[t][dt], vf[dt], pf);
+    }
+  };
+
+  auto flush = [&](int ck) {
+    const int64_t piece = a.chunk_base[cs_s] + ck;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      if (t >= nt) break;
+      float l = l_sum[t];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      const int row = (t0 + t) * 16 + r16;
+      if (row < a.rows_per_split) {
+        float* op = a.o_part + (piece * ROWS + row) * D + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + dt * 16) = acc[t][dt];
+        if (grp == 0) {
+          a.m_part[piece * ROWS + row] = m_ref[t];
+          a.l_part[piece * ROWS + row] = l;
+        }
+      }
+    }
+  };
+
+  if (producer) {
+    while (issued < min(g1, g0 + S - 1)) issue();
+    for (int gi = g0; gi < g1; ++gi) {
+      wait_groups<PER, MAXA>(issued - (gi + 1));   // group gi has landed
+      lds_barrier();                                // publish it; stage (gi-1) % S is free
+      if (issued < g1) issue();                     // group gi + S - 1 into that stage
+    }
+    return;
+  }
+  int stage = 0;                                   // ring stage of group gi
+  int ck = cl / cs.cg;
+  int cend = min(cs.len, (ck + 1) * cs.cg);
+  for (int gi = g0; gi < g1; ++gi) {
+    lds_barrier();
+    compute(stage);
+    if (++stage == S) stage = 0;
+    ++cl;
+    if (cl == cend) {   // ranges end on chunk starts, so a chunk never straddles work-groups
+      flush(ck);
+      reset();
+      ++ck;
+      cend = min(cs.len, cend + cs.cg);
+    }
+    if (cl == cs.len && gi + 1 < g1) {
+      ++cs_s;
+      decode(cs_s, cs);
+      cl = 0;
+      ck = 0;
+      cend = min(cs.len, cs.cg);
+      load_q();
+    }
+  }
+}
+
 // One work-group per (request, kv head and q-row part, block of 16 rows): each
 // thread owns one row and D/16 consecutive head dims and merges the segment's
 // chunk records in order (max first, then the rescaled sums).
@@ -433,17 +671,31 @@ static void launch_attn_t(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
   }
 }
 
+// 16-bit K/V: one consumer wave per query tile and four producer waves, an
+// 8-stage ring (128 KB at d = 128), one work-group per CU.
+template <int D>
+static void launch_attn_pc(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
+  constexpr int NP = 4, S = 8;
+  switch (qrt) {
+    case 1: attn_pc_kernel<f16_t, D, 1, 1 + NP, NP, S><<<grid, 64 * (1 + NP), 0, s>>>(a); break;
+    case 2: attn_pc_kernel<f16_t, D, 2, 2 + NP, NP, S><<<grid, 64 * (2 + NP), 0, s>>>(a); break;
+    case 3: attn_pc_kernel<f16_t, D, 3, 3 + NP, NP, S><<<grid, 64 * (3 + NP), 0, s>>>(a); break;
+    case 4: attn_pc_kernel<f16_t, D, 4, 4 + NP, NP, S><<<grid, 64 * (4 + NP), 0, s>>>(a); break;
+    case 5: attn_pc_kernel<f16_t, D, 5, 5 + NP, NP, S><<<grid, 64 * (5 + NP), 0, s>>>(a); break;
+  }
+}
+
 void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, int n_kv, int splits, int n_wg_max,
                       int min_per_wg, int chunk_min, int chunk_max, AttnPlan* plan, int32_t* seg_start,
-                      int32_t* chunk_base, hipStream_t s) {
+                      int32_t* chunk_base, int4* seg_desc, int4* wg_range, hipStream_t s) {
   attn_plan_kernel<<<1, 256, 0, s>>>(slots, ctx_len, n_req, n_kv, splits, n_wg_max, min_per_wg, chunk_min, chunk_max,
-                                      plan, seg_start, chunk_base);
+                                      plan, seg_start, chunk_base, seg_desc, wg_range);
 }
 
 void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStream_t s) {
   if (dtype == DT_BF16) {
-    if (D == 128) launch_attn_t<f16_t, 128>(a, qrt, grid, s);
-    else launch_attn_t<f16_t, 64>(a, qrt, grid, s);
+    if (D == 128) launch_attn_pc<128>(a, qrt, grid, s);
+    else launch_attn_pc<64>(a, qrt, grid, s);
   } else {
     if (D == 128) launch_attn_t<float, 128>(a, qrt, grid, s);
     else launch_attn_t<float, 64>(a, qrt, grid, s);

@@ -35,7 +35,7 @@ void launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const
 // n_wg_max work-groups (at least min_per_wg groups each), per-segment chunk bases
 void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, int n_kv, int splits, int n_wg_max,
                       int min_per_wg, int chunk_min, int chunk_max, AttnPlan* plan, int32_t* seg_start,
-                      int32_t* chunk_base, hipStream_t s);
+                      int32_t* chunk_base, int4* seg_desc, int4* wg_range, hipStream_t s);
 void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStream_t s);
 void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, hipStream_t s);
 
