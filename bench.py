@@ -136,6 +136,49 @@ def _cpu_model():
     return "unknown"
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = os.path.join(ROOT, "block_diffusion_drafter_kv_amd", "csrc")
+
+
+def kernel_source_hash():
+    """SHA-256 over the HIP sources, so that recorded counter traffic is only used for the code it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(phase, workload):
+    """HBM bytes per launch of a phase's kernel from the FETCH_SIZE / WRITE_SIZE counter runs (profiles/traffic.json,
+    calibrated against a plain device copy), or None when absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(phase)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def copy_calibration():
+    """A plain device-to-device copy of a known size, for calibrating FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,7 +187,12 @@ def main():
     ap.add_argument("--workload", default="b32_ragged4k")
     ap.add_argument("--sigma", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the drafter hot path shards by request with no exchange "
               "between GPUs; run it with --gpus 1.", file=sys.stderr)
@@ -266,12 +314,12 @@ def main():
     if bound == "mfma":
         achieved = amount / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_16B_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_16B_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_16B_TFLOPS, 4), "traffic": recorded_traffic(dom, wl.name),
                 "algorithmic_per_launch": amount, "avg_launch_ms": round(avg_ms, 4)}
     else:
         achieved = amount / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(dom, wl.name),
                 "algorithmic_per_launch": amount, "avg_launch_ms": round(avg_ms, 4)}
 
     # whole-step HBM roofline of the draft (algorithmic bytes: weights once + context K/V once per layer)
