@@ -252,7 +252,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g, const typen
   }
 }
 
-// Sum split-K partials in split order and run the epilogue on each 64-row pass.
+// Sum split-K partials in split order and run the epilogue on one 64-row pass of
+// a tile: work-group (tile, pass) = (blockIdx.x, blockIdx.y), so the reduction
+// of a small grid still spreads over many CUs.
 template <int BM, int BN, class Epi>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const GemmArgs g, const typename Epi::Params ep) {
   __shared__ float stage[EPI_ROWS * (BN + 1)];
@@ -261,46 +263,56 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const GemmArgs g, cons
   const int tm = logical % g.tiles_m, tn = logical / g.tiles_m;
   const int m_base = tm * BM, n_base = tn * BN;
   if (g.m_valid && m_base >= *g.m_valid - g.m_valid_base) return;
-  for (int pass = 0; pass < BM / EPI_ROWS; ++pass) {
-    const int m0 = m_base + pass * EPI_ROWS;
-    if (m0 >= g.M) break;
-    // 16-byte loads, all of one split in flight at once; sums taken in split order
-    constexpr int C4 = BN / 4, NV = EPI_ROWS * C4 / 256;
-    static_assert(EPI_ROWS * C4 % 256 == 0, "reduce tiling");
-    const int64_t split_stride = (int64_t)g.Mpad * g.Npad;
-    float4 acc[NV];
+  const int m0 = m_base + blockIdx.y * EPI_ROWS;
+  if (m0 >= g.M) return;
+  // 16-byte loads, two splits in flight at once; sums taken in split order
+  constexpr int C4 = BN / 4, NV = EPI_ROWS * C4 / 256;
+  static_assert(EPI_ROWS * C4 % 256 == 0, "reduce tiling");
+  const int64_t split_stride = (int64_t)g.Mpad * g.Npad;
+  float4 acc[NV];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < g.splits; ++sp) {
-      float4 v[NV];
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int idx = tid + j * 256, r = idx / C4, c4 = idx % C4;
-        v[j] = m0 + r < g.M ? *(const float4*)(g.partials + sp * split_stride + (int64_t)(m0 + r) * g.Npad + n_base +
-                                               4 * c4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        acc[j].x += v[j].x;
-        acc[j].y += v[j].y;
-        acc[j].z += v[j].z;
-        acc[j].w += v[j].w;
-      }
-    }
+  for (int j = 0; j < NV; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto load = [&](int sp, float4 (&v)[NV]) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int idx = tid + j * 256, r = idx / C4, c4 = idx % C4;
-      float* d = stage + r * (BN + 1) + 4 * c4;
-      d[0] = acc[j].x * g.out_scale;
-      d[1] = acc[j].y * g.out_scale;
-      d[2] = acc[j].z * g.out_scale;
-      d[3] = acc[j].w * g.out_scale;
+      v[j] = m0 + r < g.M ? *(const float4*)(g.partials + sp * split_stride + (int64_t)(m0 + r) * g.Npad + n_base + 4 * c4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
-    Epi::template apply<BN, EPI_ROWS>(ep, stage, BN + 1, m0, n_base, g.M, g.N, tn, tid);
-    __syncthreads();
+  };
+  auto add = [&](const float4 (&v)[NV]) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      acc[j].x += v[j].x;
+      acc[j].y += v[j].y;
+      acc[j].z += v[j].z;
+      acc[j].w += v[j].w;
+    }
+  };
+  int sp = 0;
+  for (; sp + 1 < g.splits; sp += 2) {
+    float4 v0[NV], v1[NV];
+    load(sp, v0);
+    load(sp + 1, v1);
+    add(v0);
+    add(v1);
   }
+  if (sp < g.splits) {
+    float4 v0[NV];
+    load(sp, v0);
+    add(v0);
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int idx = tid + j * 256, r = idx / C4, c4 = idx % C4;
+    float* d = stage + r * (BN + 1) + 4 * c4;
+    d[0] = acc[j].x * g.out_scale;
+    d[1] = acc[j].y * g.out_scale;
+    d[2] = acc[j].z * g.out_scale;
+    d[3] = acc[j].w * g.out_scale;
+  }
+  __syncthreads();
+  Epi::template apply<BN, EPI_ROWS>(ep, stage, BN + 1, m0, n_base, g.M, g.N, tn, tid);
 }
 
 }  // namespace dfl

@@ -21,12 +21,12 @@ static void gemm2_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (g.a_wide) {
       gemm2_kernel<T, BM, BN, SA, SB, Epi, true><<<grid, 256, 0, s>>>(g, p);
-      if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<g.tiles_m * g.tiles_n, 256, 0, s>>>(g, p);
+      if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<dim3(g.tiles_m * g.tiles_n, BM / EPI_ROWS), 256, 0, s>>>(g, p);
       return;
     }
   }
   gemm2_kernel<T, BM, BN, SA, SB, Epi><<<grid, 256, 0, s>>>(g, p);
-  if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<g.tiles_m * g.tiles_n, 256, 0, s>>>(g, p);
+  if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<dim3(g.tiles_m * g.tiles_n, BM / EPI_ROWS), 256, 0, s>>>(g, p);
 }
 
 template <int BM, class Epi>
@@ -34,7 +34,7 @@ static void gemm1_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   const typename Epi::Params& p = *(const typename Epi::Params*)ep;
   dim3 grid(gemm_grid(g.tiles_m * g.tiles_n), g.splits);
   gemm_kernel<float, BM, 128, Epi><<<grid, 256, 0, s>>>(g, p);
-  if (g.splits > 1) gemm_reduce_kernel<BM, 128, Epi><<<g.tiles_m * g.tiles_n, 256, 0, s>>>(g, p);
+  if (g.splits > 1) gemm_reduce_kernel<BM, 128, Epi><<<dim3(g.tiles_m * g.tiles_n, BM / EPI_ROWS), 256, 0, s>>>(g, p);
 }
 
 template <typename T, class Epi>
