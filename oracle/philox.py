@@ -12,7 +12,8 @@ sampler and the verifier draw their uniforms here):
     key     = (seed & 0xffffffff, seed >> 32)
     counter = (position, slot, step & 0xffffffff, purpose)
     u       = (out0 >> 8) * 2**-24          (exact in fp32 and fp64, in [0, 1))
-purpose 0 = draft sampling, 1 = accept test, 2 = residual / bonus sample.
+purpose 0 = draft sampling, 1 = accept test, 2 = residual / bonus sample,
+3 = synthetic target noise (benchmark only), 4 = draft-tree verifier walk.
 
 Pinned by the published known-answer vectors (tests/golden/philox4x32_10_kat.txt).
 """
@@ -29,6 +30,7 @@ MASK = 0xFFFFFFFF
 PURPOSE_DRAFT = 0
 PURPOSE_ACCEPT = 1
 PURPOSE_RESAMPLE = 2
+PURPOSE_TREE_WALK = 4
 
 
 def philox4x32(c0, c1, c2, c3, k0, k1, rounds: int = 10):

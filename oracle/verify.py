@@ -19,6 +19,19 @@ residual counts as exhausted when its total mass is below RESIDUAL_EPS (the
 pages say "exhausted or underflowed" without a threshold); draws are
 inverse-CDF in ascending id order with Philox uniforms (purpose 1 for accept
 tests at position i, purpose 2 for the final draw at position i* or K+1).
+
+Draft-tree verifier walk [P5 §3.5 "验证流程(Verifier Walk)"]: starting at the
+root of a draft tree (the bonus / anchor token, node 0), the target's own
+decoding rule picks the next token from the target's distribution at the
+current node; if one of the node's children carries that token the walk moves
+to it and continues, otherwise it stops, and the picked token becomes the new
+bonus token.  Readings: the target row of node u is its distribution after the
+path root..u (the tree evaluated under the ancestor-only mask [P5 §3.3]);
+greedy picks the argmax (lowest id on ties); with T > 0 the pick is an
+inverse-CDF draw from softmax(t_u / T) in ascending id order with the uniform
+Philox(seed; depth(u) + 1, slot, step, purpose 4), one per walk step.  The
+emitted sequence is then always a draw from the target itself, whatever the
+tree.
 """
 from __future__ import annotations
 
@@ -86,3 +99,46 @@ def verify_rejection(draft_ids, draft_logits, target_logits, T, seed, slot, step
     out.append(c)
     return {"out_tokens": np.array(out, dtype=np.int64), "out_len": K + 1, "accept_len": K,
             "near_margin": near, "fallback": False}
+
+
+def verify_tree_walk(tree_tokens, tree_parents, target_logits, T, seed=0, slot=0, step=0, uniform_fn=None):
+    """Verifier walk down a draft tree (see the module docstring).
+
+    tree_tokens / tree_parents [n_nodes] (node 0 = root, parent -1; unused
+    nodes have parent -1 too); target_logits [n_nodes, V], row u = the target's
+    distribution after the path root..u.  uniform_fn(position, purpose)
+    overrides the Philox uniforms (tests only).
+
+    Returns dict: out_tokens (accepted tokens, then the stopping token),
+    path (node indices of the accepted path, root first), out_len = a + 1,
+    accept_len = a, near_margin (smallest decision margin along the walk).
+    """
+    if uniform_fn is None:
+        def uniform_fn(position, purpose):
+            return float(philox.uniform(seed, slot, step, position, purpose))
+    tok = np.asarray(tree_tokens, dtype=np.int64)
+    par = np.asarray(tree_parents, dtype=np.int64)
+    t = np.asarray(target_logits, dtype=np.float64)
+    n = tok.shape[0]
+    children = {}
+    for c in range(1, n):
+        if par[c] >= 0:
+            children.setdefault(int(par[c]), {})
+            assert int(tok[c]) not in children[int(par[c])], "siblings must carry distinct tokens"
+            children[int(par[c])][int(tok[c])] = c
+    u_node, depth, out, path, near = 0, 0, [], [0], np.inf
+    while True:
+        if T <= 0:
+            pick, m = argmax_with_margin(t[u_node])
+        else:
+            pick, m = inverse_cdf(softmax(t[u_node], T), uniform_fn(depth + 1, philox.PURPOSE_TREE_WALK))
+        near = min(near, m)
+        out.append(pick)
+        nxt = children.get(u_node, {}).get(pick)
+        if nxt is None:
+            break
+        u_node, depth = nxt, depth + 1
+        path.append(nxt)
+    a = len(out) - 1
+    return {"out_tokens": np.array(out, dtype=np.int64), "path": np.array(path, dtype=np.int64),
+            "out_len": a + 1, "accept_len": a, "near_margin": near}
