@@ -69,6 +69,10 @@ _SIGS = {
                                    POINTER(dflash_draft_params), POINTER(dflash_draft_outputs)], c_int32),
     "dflash_verify": ([c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
                        c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
+    "dflash_verify_tree": ([c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                            c_float, c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
+    "dflash_inject_tree_path": ([c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int64,
+                                 POINTER(c_void_p), c_int64], c_int32),
     "dflash_profile": ([c_void_p, c_int32], c_int32),
     "dflash_profile_read": ([c_void_p, c_int32, POINTER(ctypes.c_double), POINTER(c_int32)], c_int32),
     "dflash_get_error": ([c_void_p, c_void_p, POINTER(c_int32)], c_int32),
@@ -143,6 +147,19 @@ def dflash_verify(h, stream, n_req, K, slots, draft_ids, draft_logits, target_lo
                   out_tokens, out_len, accept_len, next_anchor=None):
     return _call("dflash_verify", h, stream, n_req, K, slots, draft_ids, draft_logits, target_logits, temperature,
                  seed, step, out_tokens, out_len, accept_len, next_anchor)
+
+
+def dflash_verify_tree(h, stream, n_req, K, n_nodes, slots, tree_tokens, tree_parents, target_logits, temperature,
+                       seed, step, out_tokens, out_len, accept_len, next_anchor=None, path_nodes=None):
+    return _call("dflash_verify_tree", h, stream, n_req, K, n_nodes, slots, tree_tokens, tree_parents, target_logits,
+                 temperature, seed, step, out_tokens, out_len, accept_len, next_anchor, path_nodes)
+
+
+def dflash_inject_tree_path(h, stream, n_req, slots, path_nodes, path_len, max_path, tree_stride, rows_upper_bound,
+                            layer_ptrs, row_stride):
+    arr = (c_void_p * len(layer_ptrs))(*layer_ptrs)
+    return _call("dflash_inject_tree_path", h, stream, n_req, slots, path_nodes, path_len, max_path, tree_stride,
+                 rows_upper_bound, arr, row_stride)
 
 
 PHASES = ("inject_prep", "inject_fc", "inject_norm", "inject_kv", "embed", "qkv", "attn", "attn_combine", "o",

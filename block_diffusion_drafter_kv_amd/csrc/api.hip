@@ -382,7 +382,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc_t(h, &h->row_pos, c.max_inject_rows, 4))) break;
     if ((rc = alloc_t(h, &h->req_off, c.max_batch + 1, 4))) break;
     if ((rc = alloc_t(h, &h->req_pos, c.max_batch, 4))) break;
-    if ((rc = alloc_t(h, &h->post, (size_t)c.max_batch * R, 4))) break;
+    if ((rc = alloc_t(h, &h->post, (size_t)c.max_batch * std::max(R, c.max_tree + 1), 4))) break;
     if ((rc = alloc_t(h, &h->vstats, (size_t)c.max_batch * (2 * c.max_k + 1) * 2, 4))) break;
   } while (0);
   if (rc) {
@@ -422,28 +422,29 @@ int dflash_reset_slots(dflash_handle* h, void* stream, int32_t n, const int32_t*
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
 
-int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
-                          const int32_t* row_start, const int32_t* row_count, int64_t rows_upper_bound,
-                          const void* const* target_hidden, int64_t row_stride) {
-  if (!h || n_req < 0 || rows_upper_bound < 0) return DFLASH_E_INVALID;
-  if (n_req == 0 || rows_upper_bound == 0) return DFLASH_OK;
+}  // extern "C"
+
+namespace {
+
+// Common checks of the injection entry points.
+int validate_inject(dflash_handle* h, int n_req, const int32_t* slots, const int32_t* row_count,
+                    int64_t rows_upper_bound, const void* const* target_hidden, int64_t row_stride) {
   const dflash_config& c = h->cfg;
-  if (!slots || !row_start || !row_count || !target_hidden) return DFLASH_E_INVALID;
+  if (!slots || !row_count || !target_hidden) return DFLASH_E_INVALID;
   if (n_req > c.max_batch || rows_upper_bound > c.max_inject_rows) return DFLASH_E_CAPACITY;
   if (row_stride < c.target_hidden || row_stride % 8) return DFLASH_E_INVALID;
   for (int l = 0; l < c.n_target_layers; ++l)
     if (!target_hidden[l]) return DFLASH_E_INVALID;
-  hipStream_t s = S(stream);
+  return DFLASH_OK;
+}
+
+// The products of an injection once its row tables (a_rows, row_slot, row_pos,
+// req_off) are on the device: fc, RMSNorm, per-layer K|V with k-norm + RoPE into the cache.
+int inject_rows(dflash_handle* h, hipStream_t s, int n_req, int64_t rows_upper_bound, const void* const* target_hidden,
+                int64_t row_stride) {
+  const dflash_config& c = h->cfg;
   const int dt = c.dtype;
   const int H = c.hidden, kvdim = c.n_kv_heads * c.head_dim;
-  {
-    Phase ph(h, s, DFLASH_PH_INJECT_PREP);
-    launch_inject_scan(n_req, slots, row_start, row_count, h->ctx_len, c.max_ctx, c.max_batch, rows_upper_bound,
-                       h->req_off, h->req_pos, h->err, s);
-    // source rows are int32 indices into the caller's buffers
-    launch_inject_fill(n_req, rows_upper_bound, slots, row_start, h->req_off, h->req_pos, (int64_t)INT32_MAX,
-                       h->a_rows, h->row_slot, h->row_pos, h->err, s);
-  }
   const int featK = c.n_target_layers * c.target_hidden;
   for (int64_t c0 = 0; c0 < rows_upper_bound; c0 += h->inject_chunk) {
     const int rows = (int)std::min<int64_t>(h->inject_chunk, rows_upper_bound - c0);
@@ -513,6 +514,55 @@ int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const i
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+int dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
+                          const int32_t* row_start, const int32_t* row_count, int64_t rows_upper_bound,
+                          const void* const* target_hidden, int64_t row_stride) {
+  if (!h || n_req < 0 || rows_upper_bound < 0) return DFLASH_E_INVALID;
+  if (n_req == 0 || rows_upper_bound == 0) return DFLASH_OK;
+  if (!row_start) return DFLASH_E_INVALID;
+  int rc = validate_inject(h, n_req, slots, row_count, rows_upper_bound, target_hidden, row_stride);
+  if (rc) return rc;
+  const dflash_config& c = h->cfg;
+  hipStream_t s = S(stream);
+  {
+    Phase ph(h, s, DFLASH_PH_INJECT_PREP);
+    launch_inject_scan(n_req, slots, row_start, row_count, h->ctx_len, c.max_ctx, c.max_batch, rows_upper_bound,
+                       h->req_off, h->req_pos, h->err, s);
+    // source rows are int32 indices into the caller's buffers
+    launch_inject_fill(n_req, rows_upper_bound, slots, row_start, nullptr, 0, 0, h->req_off, h->req_pos,
+                       (int64_t)INT32_MAX, h->a_rows, h->row_slot, h->row_pos, h->err, s);
+  }
+  return inject_rows(h, s, n_req, rows_upper_bound, target_hidden, row_stride);
+}
+
+int dflash_inject_tree_path(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
+                            const int32_t* path_nodes, const int32_t* path_len, int32_t max_path,
+                            int32_t tree_stride, int64_t rows_upper_bound, const void* const* target_hidden,
+                            int64_t row_stride) {
+  if (!h || n_req < 0 || rows_upper_bound < 0 || max_path < 1 || tree_stride < 1) return DFLASH_E_INVALID;
+  if (n_req == 0 || rows_upper_bound == 0) return DFLASH_OK;
+  if (!path_nodes) return DFLASH_E_INVALID;
+  int rc = validate_inject(h, n_req, slots, path_len, rows_upper_bound, target_hidden, row_stride);
+  if (rc) return rc;
+  if ((int64_t)n_req * tree_stride > (int64_t)INT32_MAX) return DFLASH_E_UNSUPPORTED;
+  const dflash_config& c = h->cfg;
+  hipStream_t s = S(stream);
+  {
+    Phase ph(h, s, DFLASH_PH_INJECT_PREP);
+    launch_inject_scan(n_req, slots, nullptr, path_len, h->ctx_len, c.max_ctx, c.max_batch, rows_upper_bound,
+                       h->req_off, h->req_pos, h->err, s);
+    launch_inject_fill(n_req, rows_upper_bound, slots, nullptr, path_nodes, max_path, tree_stride, h->req_off,
+                       h->req_pos, (int64_t)INT32_MAX, h->a_rows, h->row_slot, h->row_pos, h->err, s);
+  }
+  return inject_rows(h, s, n_req, rows_upper_bound, target_hidden, row_stride);
+}
+
+}  // extern "C"
+
 namespace {
 
 int validate_draft(dflash_handle* h, int n_req, const dflash_draft_params* p, const dflash_draft_outputs* o) {
@@ -564,6 +614,8 @@ void select_stage(dflash_handle* h, hipStream_t s, int n_req, const int32_t* slo
 }
 
 }  // namespace
+
+extern "C" {
 
 int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots_in,
                        const int32_t* anchor_ids, const dflash_draft_params* p, const dflash_draft_outputs* o) {
@@ -823,6 +875,27 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
     launch_verify_rejection(n_req, K, c.vocab, slots, draft_ids, draft_logits, target_logits, 1.0f / temperature,
                             seed, step, h->vstats, out_tokens, out_len, accept_len, next_anchor, h->err, s);
   }
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+int dflash_verify_tree(dflash_handle* h, void* stream, int32_t n_req, int32_t K, int32_t n_nodes,
+                       const int32_t* slots, const int32_t* tree_tokens, const int32_t* tree_parents,
+                       const float* target_logits, float temperature, uint64_t seed, uint64_t step,
+                       int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
+                       int32_t* path_nodes) {
+  if (!h || n_req < 0) return DFLASH_E_INVALID;
+  if (n_req == 0) return DFLASH_OK;
+  const dflash_config& c = h->cfg;
+  if (n_req > c.max_batch || K < 1 || K > c.max_k || n_nodes < 1 || n_nodes > c.max_tree + 1)
+    return DFLASH_E_CAPACITY;
+  if (!tree_tokens || !tree_parents || !target_logits || !out_tokens || !out_len || !accept_len)
+    return DFLASH_E_INVALID;
+  if (!(temperature >= 0.f)) return DFLASH_E_INVALID;
+  if (temperature > 0.f && !slots) return DFLASH_E_INVALID;
+  hipStream_t s = S(stream);
+  Phase ph(h, s, DFLASH_PH_VERIFY);
+  launch_verify_tree(n_req, n_nodes, K + 1, c.vocab, slots, tree_tokens, tree_parents, target_logits, temperature,
+                     seed, step, h->post, out_tokens, out_len, accept_len, next_anchor, path_nodes, h->err, s);
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
 

@@ -114,7 +114,7 @@ __device__ __forceinline__ float philox_uniform(uint64_t seed, uint32_t slot, ui
   return (float)(o.x >> 8) * (1.0f / 16777216.0f);
 }
 
-enum : uint32_t { PURPOSE_DRAFT = 0, PURPOSE_ACCEPT = 1, PURPOSE_RESAMPLE = 2, PURPOSE_NOISE = 3 };
+enum : uint32_t { PURPOSE_DRAFT = 0, PURPOSE_ACCEPT = 1, PURPOSE_RESAMPLE = 2, PURPOSE_NOISE = 3, PURPOSE_TREE_WALK = 4 };
 
 // device error word bits
 enum : int32_t { ERR_CAPACITY = 1, ERR_BAD_SLOT = 2, ERR_ROWS = 4, ERR_BAD_TOKEN = 8 };

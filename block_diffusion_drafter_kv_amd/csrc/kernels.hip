@@ -145,7 +145,11 @@ __global__ void inject_scan_kernel(int n_req, const int32_t* slots, const int32_
   req_off[n_req] = (int32_t)off;
 }
 
+// Source row of new row i of request r: row_start[r] + i, or, for a tree path,
+// r * tree_stride + path_nodes[r * max_path + i] (a node index of that request's
+// block of tree_stride rows; a node outside [0, tree_stride) is skipped and flagged).
 __global__ void inject_fill_kernel(int n_req, int64_t rows_upper, const int32_t* slots, const int32_t* row_start,
+                                   const int32_t* path_nodes, int max_path, int tree_stride,
                                    const int32_t* req_off, const int32_t* req_pos, int64_t max_row, int32_t* a_rows,
                                    int32_t* row_slot, int32_t* row_pos, int32_t* err) {
   const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -165,7 +169,13 @@ __global__ void inject_fill_kernel(int n_req, int64_t rows_upper, const int32_t*
   // skip empty requests that share the same offset
   while (lo + 1 <= n_req - 1 && req_off[lo + 1] <= m) ++lo;
   const int i = (int)(m - req_off[lo]);
-  const int64_t src = (int64_t)row_start[lo] + i;
+  int64_t src;
+  if (path_nodes) {
+    const int node = i < max_path ? path_nodes[(int64_t)lo * max_path + i] : -1;
+    src = node >= 0 && node < tree_stride ? (int64_t)lo * tree_stride + node : -1;
+  } else {
+    src = (int64_t)row_start[lo] + i;
+  }
   if (src < 0 || src >= max_row) {  // not addressable: skip the row (its slot is left as it was)
     raise_error(err, ERR_ROWS);
     a_rows[m] = -1;
@@ -791,6 +801,139 @@ __global__ __launch_bounds__(256) void rejection_kernel(int K, int V, const int3
 }
 
 // ---------------------------------------------------------------------------
+// Draft-tree verifier walk [P5 §3.5]: from the root (node 0) the target's own
+// decoding rule picks a token from the target row of the current node; the walk
+// moves to the child carrying that token, if any, and otherwise stops with the
+// pick as the new bonus token.  Greedy picks the row argmax (lowest id on ties);
+// T > 0 draws by inverse CDF in ascending id order with u = Philox(seed;
+// depth + 1, slot, step, 4).  Children have larger indices than their parent
+// (the builder numbers nodes in pop order), so a child search starts past it.
+// out_tokens / path rows hold max_out entries (unused -1).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tree_child(const int32_t* tok, const int32_t* par, int n_nodes, int node, int pick) {
+  for (int c = node + 1; c < n_nodes; ++c)
+    if (par[c] == node && tok[c] == pick) return c;
+  return -1;
+}
+
+__global__ void tree_walk_greedy_kernel(int n_req, int n_nodes, int max_out, const int32_t* tokens,
+                                        const int32_t* parents, const int32_t* post, int32_t* out_tokens,
+                                        int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
+                                        int32_t* path_out, int32_t* err) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_req) return;
+  const int32_t* tok = tokens + (int64_t)r * n_nodes;
+  const int32_t* par = parents + (int64_t)r * n_nodes;
+  const int32_t* pr = post + (int64_t)r * n_nodes;
+  int32_t* o = out_tokens + (int64_t)r * max_out;
+  int32_t* pth = path_out ? path_out + (int64_t)r * max_out : nullptr;
+  int node = 0, a = 0;
+  if (pth) pth[0] = 0;
+  for (;;) {
+    const int pick = pr[node];
+    o[a] = pick;
+    const int nxt = tree_child(tok, par, n_nodes, node, pick);
+    if (nxt < 0) break;
+    if (a + 1 >= max_out) {   // deeper than the output rows allow: stop here
+      raise_error(err, ERR_ROWS);
+      break;
+    }
+    node = nxt;
+    ++a;
+    if (pth) pth[a] = nxt;
+  }
+  for (int i = a + 1; i < max_out; ++i) {
+    o[i] = -1;
+    if (pth) pth[i] = -1;
+  }
+  out_len[r] = a + 1;
+  accept_len[r] = a;
+  if (next_anchor) next_anchor[r] = o[a];
+}
+
+__global__ __launch_bounds__(256) void tree_walk_sample_kernel(int n_nodes, int max_out, int V, const int32_t* slots,
+                                                                const int32_t* tokens, const int32_t* parents,
+                                                                const float* target, float inv_temp, uint64_t seed,
+                                                                uint64_t step, int32_t* out_tokens, int32_t* out_len,
+                                                                int32_t* accept_len, int32_t* next_anchor,
+                                                                int32_t* path_out, int32_t* err) {
+  __shared__ float sh[8];
+  __shared__ float s_total;
+  __shared__ int s_thread, s_pick, s_next;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const uint32_t slot = (uint32_t)slots[r];
+  const int32_t* tok = tokens + (int64_t)r * n_nodes;
+  const int32_t* par = parents + (int64_t)r * n_nodes;
+  int32_t* o = out_tokens + (int64_t)r * max_out;
+  int32_t* pth = path_out ? path_out + (int64_t)r * max_out : nullptr;
+  const int per = (V + 255) / 256;
+  const int c0 = tid * per, c1 = min(V, c0 + per);
+  int node = 0, a = 0;
+  if (pth && tid == 0) pth[0] = 0;
+  for (;;) {
+    const float* t = target + ((int64_t)r * n_nodes + node) * V;
+    float mx = -INFINITY;
+    for (int c = tid; c < V; c += 256) mx = fmaxf(mx, t[c] * inv_temp);
+    mx = wave_max(mx);
+    __syncthreads();
+    if ((tid & 63) == 0) sh[tid >> 6] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+    float w = 0.f;
+    for (int c = c0; c < c1; ++c) w += expf(t[c] * inv_temp - M);
+    const float incl = block_incl_scan(w, sh);
+    if (tid == 255) s_total = incl;
+    if (tid == 0) { s_thread = -1; s_pick = -1; }
+    __syncthreads();
+    const float u = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_TREE_WALK);
+    const float target_mass = u * s_total;
+    const float excl = incl - w;
+    if (excl <= target_mass && target_mass < incl) s_thread = tid;
+    __syncthreads();
+    if (tid == s_thread) {
+      float acc = excl;
+      for (int c = c0; c < c1; ++c) {
+        const float wc = expf(t[c] * inv_temp - M);
+        if (wc > 0.f && target_mass < acc + wc) { s_pick = c; break; }
+        acc += wc;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int pick = s_pick;
+      if (pick < 0) {   // rounding put u*S on the total: last id with weight
+        for (int c = V - 1; c >= 0; --c)
+          if (expf(t[c] * inv_temp - M) > 0.f) { pick = c; break; }
+        if (pick < 0) pick = 0;
+      }
+      o[a] = pick;
+      int nxt = tree_child(tok, par, n_nodes, node, pick);
+      if (nxt >= 0 && a + 1 >= max_out) {
+        raise_error(err, ERR_ROWS);
+        nxt = -1;
+      }
+      s_next = nxt;
+    }
+    __syncthreads();
+    const int nxt = s_next;
+    __syncthreads();
+    if (nxt < 0) break;
+    node = nxt;
+    ++a;
+    if (pth && tid == 0) pth[a] = nxt;
+  }
+  if (tid == 0) {
+    for (int i = a + 1; i < max_out; ++i) {
+      o[i] = -1;
+      if (pth) pth[i] = -1;
+    }
+    out_len[r] = a + 1;
+    accept_len[r] = a;
+    if (next_anchor) next_anchor[r] = o[a];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Synthetic target logits (benchmark stand-in for the target model):
 // row j < K = draft row j + sigma * N(0,1); row K = sigma * N(0,1).
 // ---------------------------------------------------------------------------
@@ -903,11 +1046,13 @@ void launch_inject_scan(int n_req, const int32_t* slots, const int32_t* row_star
 }
 
 void launch_inject_fill(int n_req, int64_t rows_upper, const int32_t* slots, const int32_t* row_start,
-                        const int32_t* req_off, const int32_t* req_pos, int64_t max_row, int32_t* a_rows,
-                        int32_t* row_slot, int32_t* row_pos, int32_t* err, hipStream_t s) {
+                        const int32_t* path_nodes, int max_path, int tree_stride, const int32_t* req_off,
+                        const int32_t* req_pos, int64_t max_row, int32_t* a_rows, int32_t* row_slot,
+                        int32_t* row_pos, int32_t* err, hipStream_t s) {
   if (rows_upper <= 0) return;
-  inject_fill_kernel<<<cdiv(rows_upper, 256), 256, 0, s>>>(n_req, rows_upper, slots, row_start, req_off, req_pos,
-                                                           max_row, a_rows, row_slot, row_pos, err);
+  inject_fill_kernel<<<cdiv(rows_upper, 256), 256, 0, s>>>(n_req, rows_upper, slots, row_start, path_nodes, max_path,
+                                                           tree_stride, req_off, req_pos, max_row, a_rows, row_slot,
+                                                           row_pos, err);
 }
 
 void launch_row_finalize(int n_rows, int n_tiles, const float* tmax, const float* tsum, const int32_t* targ,
@@ -943,6 +1088,21 @@ void launch_verify_greedy(int n_req, int K, int V, const int32_t* draft_ids, con
   argmax_rows_kernel<<<n_req * (K + 1), 256, 0, s>>>(V, target, post);
   greedy_finish_kernel<<<cdiv(n_req, 64), 64, 0, s>>>(n_req, K, draft_ids, post, out_tokens, out_len, accept_len,
                                                       next_anchor);
+}
+
+void launch_verify_tree(int n_req, int n_nodes, int max_out, int V, const int32_t* slots, const int32_t* tokens,
+                        const int32_t* parents, const float* target, float temperature, uint64_t seed, uint64_t step,
+                        int32_t* post, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
+                        int32_t* next_anchor, int32_t* path_out, int32_t* err, hipStream_t s) {
+  if (temperature == 0.f) {
+    argmax_rows_kernel<<<n_req * n_nodes, 256, 0, s>>>(V, target, post);
+    tree_walk_greedy_kernel<<<cdiv(n_req, 64), 64, 0, s>>>(n_req, n_nodes, max_out, tokens, parents, post, out_tokens,
+                                                         out_len, accept_len, next_anchor, path_out, err);
+  } else {
+    tree_walk_sample_kernel<<<n_req, 256, 0, s>>>(n_nodes, max_out, V, slots, tokens, parents, target,
+                                                  1.0f / temperature, seed, step, out_tokens, out_len, accept_len,
+                                                  next_anchor, path_out, err);
+  }
 }
 
 void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,

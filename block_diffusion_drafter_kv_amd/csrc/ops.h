@@ -54,8 +54,9 @@ void launch_inject_scan(int n_req, const int32_t* slots, const int32_t* row_star
 // gemm row table of an injection; source rows at or past max_row (not addressable
 // with 32-bit byte offsets) are skipped and flag the error word
 void launch_inject_fill(int n_req, int64_t rows_upper, const int32_t* slots, const int32_t* row_start,
-                        const int32_t* req_off, const int32_t* req_pos, int64_t max_row, int32_t* a_rows,
-                        int32_t* row_slot, int32_t* row_pos, int32_t* err, hipStream_t s);
+                        const int32_t* path_nodes, int max_path, int tree_stride, const int32_t* req_off,
+                        const int32_t* req_pos, int64_t max_row, int32_t* a_rows, int32_t* row_slot,
+                        int32_t* row_pos, int32_t* err, hipStream_t s);
 void launch_row_finalize(int n_rows, int n_tiles, const float* tmax, const float* tsum, const int32_t* targ,
                          float* row_max, float* row_lse, int32_t* argmax_out, float* out_row_max, float* out_row_lse,
                          hipStream_t s);
@@ -71,6 +72,11 @@ void launch_tree(int n_req, int L, int Kc, int stride, int B, const float* probs
 void launch_verify_greedy(int n_req, int K, int V, const int32_t* draft_ids, const float* target, int32_t* post,
                           int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
                           hipStream_t s);
+// draft-tree verifier walk: greedy (row argmax of every node, then the walk) or sampled
+void launch_verify_tree(int n_req, int n_nodes, int max_out, int V, const int32_t* slots, const int32_t* tokens,
+                        const int32_t* parents, const float* target, float temperature, uint64_t seed, uint64_t step,
+                        int32_t* post, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
+                        int32_t* next_anchor, int32_t* path_out, int32_t* err, hipStream_t s);
 void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,
                              const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
                              uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,

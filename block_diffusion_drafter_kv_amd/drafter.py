@@ -13,7 +13,8 @@ import torch
 from . import (DFLASH_BF16, DFLASH_F32, dflash_config, dflash_copy_cache, dflash_create, dflash_ctx_lens,
                dflash_destroy, dflash_draft_block, dflash_draft_outputs, dflash_draft_params, dflash_get_error,
                dflash_inject_context, dflash_layer_weights, dflash_profile, dflash_profile_read, dflash_reset_slots,
-               dflash_select_from_logits, dflash_verify, dflash_weights)
+               dflash_select_from_logits, dflash_verify, dflash_verify_tree, dflash_inject_tree_path,
+               dflash_weights)
 
 _LAYER_KEYS = ("in_norm", "q_w", "k_w", "v_w", "o_w", "q_norm", "k_norm", "post_norm", "gate_w", "up_w", "down_w")
 
@@ -156,6 +157,46 @@ class Drafter:
                       out["out_tokens"].data_ptr(), out["out_len"].data_ptr(), out["accept_len"].data_ptr(),
                       _ptr(out.get("next_anchor")))
         return out
+
+    def verify_tree(self, slots, K, tree_tokens, tree_parents, target_logits, temperature=0.0, seed=0, step=0,
+                    out=None):
+        """Verifier walk down each request's draft tree (dflash_verify_tree)."""
+        n, n_nodes = tree_tokens.shape
+        for t in (tree_tokens, tree_parents):
+            if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous() or t.shape != (n, n_nodes):
+                raise ValueError("tree_tokens / tree_parents must be contiguous int32 CUDA tensors [n, B+1]")
+        if target_logits.shape != (n, n_nodes, self.model.vocab) or target_logits.dtype != torch.float32 \
+                or not target_logits.is_contiguous():
+            raise ValueError("target_logits must be contiguous fp32 [n, B+1, vocab]")
+        dev = torch.device("cuda")
+        if out is None:
+            out = {"out_tokens": torch.empty((n, K + 1), dtype=torch.int32, device=dev),
+                   "out_len": torch.empty((n,), dtype=torch.int32, device=dev),
+                   "accept_len": torch.empty((n,), dtype=torch.int32, device=dev),
+                   "next_anchor": torch.empty((n,), dtype=torch.int32, device=dev),
+                   "path_nodes": torch.empty((n, K + 1), dtype=torch.int32, device=dev)}
+        dflash_verify_tree(self.handle, _stream(), n, K, n_nodes, _ptr(slots), tree_tokens.data_ptr(),
+                           tree_parents.data_ptr(), target_logits.data_ptr(), float(temperature), seed, step,
+                           out["out_tokens"].data_ptr(), out["out_len"].data_ptr(), out["accept_len"].data_ptr(),
+                           _ptr(out.get("next_anchor")), _ptr(out.get("path_nodes")))
+        return out
+
+    def inject_tree_path(self, slots, path_nodes, path_len, tree_stride, rows_upper_bound, hidden):
+        """Inject the accepted path rows: row i of request r is hidden row r * tree_stride + path_nodes[r, i]
+        (hidden: [n * tree_stride, n_target_layers, target_hidden] contiguous)."""
+        for t in (slots, path_nodes, path_len):
+            if not t.is_cuda or t.dtype != torch.int32:
+                raise ValueError("slots / path_nodes / path_len must be int32 CUDA tensors")
+        if not path_nodes.is_contiguous() or path_nodes.dim() != 2:
+            raise ValueError("path_nodes must be a contiguous [n, max_path] tensor")
+        if not hidden.is_contiguous() or hidden.dim() != 3:
+            raise ValueError("hidden must be contiguous [rows, n_target_layers, target_hidden]")
+        _, lt, ht = hidden.shape
+        es = hidden.element_size()
+        ptrs = [hidden.data_ptr() + l * ht * es for l in range(lt)]
+        dflash_inject_tree_path(self.handle, _stream(), slots.numel(), slots.data_ptr(), path_nodes.data_ptr(),
+                                path_len.data_ptr(), path_nodes.shape[1], int(tree_stride), int(rows_upper_bound),
+                                ptrs, lt * ht)
 
     def profile(self, enable: bool = True):
         dflash_profile(self.handle, enable)

@@ -217,6 +217,46 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
 /* next_anchor [n_req] (device, or NULL) receives out_tokens[r][out_len[r]-1]: the
  * token that anchors the next block [P4 §4.2; P1 "核心推理伪代码"]. */
 
+/* Verifier walk down a draft tree [P5 §3.5 "验证流程(Verifier Walk)"] (one
+ * tree per request, as dflash_draft_block builds it: node 0 = root / anchor,
+ * nodes numbered so that a parent precedes its children, siblings carrying
+ * distinct tokens).  From the root, the target's own decoding rule picks the
+ * next token from target_logits row u (the target's distribution after the
+ * path root..u, i.e. the tree evaluated under its ancestor-only mask
+ * [P5 §3.3]); the walk moves to the child of u carrying that token, if any, and
+ * otherwise stops with the pick as the new bonus token.  temperature 0: row
+ * argmax (lowest id on ties); > 0: inverse-CDF draw from softmax(t_u / T) in
+ * ascending id order with u = Philox(seed; depth(u) + 1, slot, step, 4).
+ *   n_nodes        : B + 1 (1 .. cfg.max_tree + 1); K: the draft's K (tree depth <= K)
+ *   tree_tokens, tree_parents : device int32 [n_req, n_nodes] (parent -1: root or unused)
+ *   target_logits  : device fp32 [n_req, n_nodes, V]
+ * Outputs (device): out_tokens [n_req, K+1] (accepted tokens, then the bonus;
+ * unused -1), out_len [n_req] = a + 1, accept_len [n_req] = a, next_anchor
+ * [n_req] (or NULL) = the bonus, path_nodes [n_req, K+1] (or NULL) = node
+ * indices of the accepted path, root first (unused -1).  A walk deeper than K
+ * stops there and sets DFLASH_DEV_ROWS in the error word.
+ * Does not touch the cache: inject the path's a + 1 rows next
+ * (dflash_inject_tree_path with path_len = out_len). */
+int dflash_verify_tree(dflash_handle* h, void* stream, int32_t n_req, int32_t K, int32_t n_nodes,
+                       const int32_t* slots, const int32_t* tree_tokens, const int32_t* tree_parents,
+                       const float* target_logits, float temperature, uint64_t seed, uint64_t step,
+                       int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
+                       int32_t* path_nodes);
+
+/* Injection of the rows of an accepted tree path [P5 §3.4-3.5; P3 §四]: the
+ * same computation as dflash_inject_context, with request r's i-th new row
+ * (i < path_len[r]) read from row r * tree_stride + path_nodes[r * max_path + i]
+ * of target_hidden (the target's hidden states in tree order, tree_stride rows
+ * per request).  A node index outside [0, tree_stride) sets DFLASH_DEV_ROWS in
+ * the error word and leaves that row's cache entry unwritten (the slot's
+ * context length still advances by path_len, as for any injected row).
+ *   path_nodes : device int32 [n_req, max_path]; path_len: device int32 [n_req]
+ *   rows_upper_bound : host bound >= sum(path_len), <= cfg.max_inject_rows */
+int dflash_inject_tree_path(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
+                            const int32_t* path_nodes, const int32_t* path_len, int32_t max_path,
+                            int32_t tree_stride, int64_t rows_upper_bound, const void* const* target_hidden,
+                            int64_t row_stride);
+
 /* Synchronise `stream`, return the sticky device error word in *code and clear it. */
 int dflash_get_error(dflash_handle* h, void* stream, int32_t* code);
 

@@ -289,6 +289,71 @@ def test_full_topk_tree_b64(gpu_lib):
     dr.close()
 
 
+def _tree_target_rows(tok, par, V, seed, follow=0.8, bump=6.0, scale=1.0):
+    """Target rows of one request's tree nodes: scale * N(0,1) plus a bump on a child's token (or a random one)."""
+    rng = np.random.default_rng(seed)
+    nn = tok.shape[0]
+    t = rng.standard_normal((nn, V), dtype=np.float32) * np.float32(scale)
+    for u in range(nn):
+        kids = [int(tok[c]) for c in range(nn) if par[c] == u]
+        if kids and rng.random() < follow:
+            t[u, kids[0] if rng.random() < 2 / 3 else kids[rng.integers(0, len(kids))]] += bump
+        else:
+            t[u, int(rng.integers(0, V))] += bump
+    return t
+
+
+def test_full_tree_walk_b64(gpu_lib):
+    """Verifier walk over best-first B = 64 trees at batch 64, K = 16, V = 151936 (greedy and
+    T = 1), against the oracle walk on the same trees and fp32 target rows."""
+    wl = get_workload("b64_tree")
+    cfg, K, B, V = wl.model, wl.K, wl.batch, wl.model.vocab
+    Bt = wl.tree_budget
+    import block_diffusion_drafter_kv_amd as dk
+    dr = dk.Drafter(cfg, _idle_weights(cfg), max_batch=B, max_ctx=64, max_k=K, max_inject_rows=64,
+                    max_top_k=wl.top_k, max_tree=Bt)
+    # peaked marginals (N(0,1) plus 12.5 on one token per position): the best-first trees then hold
+    # a deep spine beside bushy first levels, so walks of several accepted nodes occur
+    z = gen.logits_like((B, K, V), 1.0, 52, "marginals").numpy()
+    rng = np.random.default_rng(53)
+    z[np.arange(B)[:, None], np.arange(K)[None, :], rng.integers(0, V, (B, K))] += 12.5
+    o = dr.select_from_logits(_dev(np.arange(B)), _dev(gen.anchor_ids(cfg, B, seed=7)),
+                              torch.tensor(z, device="cuda"), temperature=1.0, seed=1, step=0, top_k=wl.top_k,
+                              tree_budget=Bt)
+    torch.cuda.synchronize()
+    del z
+    tok = o["tree_tokens"].cpu().numpy()
+    par = o["tree_parents"].cpu().numpy()
+    # greedy on N(0,1) rows with a bump of 6; sampling on peaked rows (3 * N(0,1) + 14), where a T = 1
+    # draw lands on one of a few hundred tokens and most draws sit clear of fp32 rounding
+    rows = {0.0: dict(bump=6.0, scale=1.0), 1.0: dict(bump=14.0, scale=3.0)}
+    slots = _dev(np.arange(B))
+    res = {}
+    for T, kw in rows.items():
+        t = torch.empty((B, Bt + 1, V), dtype=torch.float32, device="cuda")
+        for r in range(B):
+            t[r] = torch.from_numpy(_tree_target_rows(tok[r], par[r], V, 1000 + r, **kw))
+        res[T] = dr.verify_tree(slots, K, o["tree_tokens"], o["tree_parents"], t, temperature=T, seed=4, step=3)
+        torch.cuda.synchronize()
+        del t
+    checked, deep = {0.0: 0, 1.0: 0}, 0
+    for r in range(B):
+        for T, kw in rows.items():
+            tr = _tree_target_rows(tok[r], par[r], V, 1000 + r, **kw)
+            w = over.verify_tree_walk(tok[r], par[r], tr, T, seed=4, slot=r, step=3)
+            if w["near_margin"] < 1e-5:
+                continue
+            checked[T] += 1
+            L = w["out_len"]
+            assert res[T]["out_len"][r].item() == L, f"T {T} req {r}"
+            assert list(res[T]["out_tokens"][r].cpu().numpy()[:L]) == list(w["out_tokens"])
+            assert list(res[T]["path_nodes"][r].cpu().numpy()[:L]) == list(w["path"])
+            deep += w["accept_len"] >= 3
+    assert checked[0.0] == B and checked[1.0] >= B // 2 and deep >= 8, (checked, deep)
+    assert dr.get_error() == 0
+    dr.close()
+
+
 @pytest.mark.timeout(900)
 def test_full_b64_larger_drafter_forward(gpu_lib):
     """The larger drafter (hidden 5120, 64/8 heads, two q-row parts per kv head) at batch 64,
