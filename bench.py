@@ -179,6 +179,95 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
+def idle_weights(cfg):
+    """Zero bf16 weights of the right shapes, one set shared by all layers: a handle that only
+    runs selection and verification needs valid weight pointers it never reads."""
+    import torch
+    z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16, device="cuda")
+    H, F = cfg.hidden, cfg.ffn
+    lw = {"in_norm": z(H), "q_w": z(cfg.q_dim, H), "k_w": z(cfg.kv_dim, H), "v_w": z(cfg.kv_dim, H),
+          "o_w": z(H, cfg.q_dim), "q_norm": z(cfg.head_dim), "k_norm": z(cfg.head_dim), "post_norm": z(H),
+          "gate_w": z(F, H), "up_w": z(F, H), "down_w": z(H, F)}
+    return {"embed": z(cfg.vocab, H), "lm_head": z(cfg.vocab, H), "fc": z(H, cfg.feat_dim), "hidden_norm": z(H),
+            "final_norm": z(H), "layers": [lw] * cfg.n_layers}
+
+
+def tree_verify_measure(reps=20):
+    """dflash_verify_tree at the batch-64 tree shape (64 requests, 65-node best-first trees from
+    top-64 marginals, K = 16, V = 151936), greedy and T = 1.
+
+    Trees: the library's builder over peaked synthetic marginals (N(0,1) plus 12.5 on one token per
+    position), which gives a deep spine beside bushy first levels.  Target rows: scale * N(0,1) plus a
+    bump on one token per node (a child's token with probability 0.8, the first-popped child two times
+    in three; else a random token), scale 1 / bump 6 for greedy, 3 / 20 for sampling.  The walk reads
+    one fp32 row per visited node (out_len rows per request); algorithmic bytes = rows read * V * 4.
+    """
+    import numpy as np
+    import torch
+
+    import block_diffusion_drafter_kv_amd as dk
+    from synth.configs import get_workload
+
+    wl = get_workload("b64_tree")
+    cfg, B, K, V, Bt = wl.model, wl.batch, wl.K, wl.model.vocab, wl.tree_budget
+    nn = Bt + 1
+    dr = dk.Drafter(cfg, idle_weights(cfg), max_batch=B, max_ctx=64, max_k=K, max_inject_rows=64,
+                    max_top_k=wl.top_k, max_tree=Bt)
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(52)
+    z = torch.randn((B, K, V), generator=g, device="cuda")
+    hot = torch.randint(0, V, (B, K, 1), generator=g, device="cuda")
+    z.scatter_add_(2, hot, torch.full((B, K, 1), 12.5, device="cuda"))
+    slots = i32(np.arange(B))
+    o = dr.select_from_logits(slots, i32(np.arange(B) + 7), z, temperature=1.0, seed=1, step=0, top_k=wl.top_k,
+                              tree_budget=Bt)
+    del z
+    tok, par = o["tree_tokens"].cpu().numpy(), o["tree_parents"].cpu().numpy()
+    rng = np.random.default_rng(53)
+    bump_tok = np.empty((B, nn), np.int64)
+    for r in range(B):
+        for u in range(nn):
+            kids = [int(tok[r, c]) for c in range(nn) if par[r, c] == u]
+            if kids and rng.random() < 0.8:
+                bump_tok[r, u] = kids[0] if rng.random() < 2 / 3 else kids[rng.integers(0, len(kids))]
+            else:
+                bump_tok[r, u] = rng.integers(0, V)
+    idx = torch.tensor(bump_tok, device="cuda")[..., None]
+    stream = torch.cuda.current_stream()
+    out = {}
+    for T, scale, bump in ((0.0, 1.0, 6.0), (1.0, 3.0, 20.0)):
+        t = torch.randn((B, nn, V), generator=g, device="cuda") * scale
+        t.scatter_add_(2, idx, torch.full((B, nn, 1), bump, device="cuda"))
+        marks, lens, res = [], [], None
+        for i in range(reps + 3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            res = dr.verify_tree(slots, K, o["tree_tokens"], o["tree_parents"], t, temperature=T, seed=4, step=i,
+                                 out=res)
+            e1.record(stream)
+            marks.append((e0, e1))
+            lens.append(res["out_len"].clone())
+        torch.cuda.synchronize()
+        assert dr.get_error() == 0
+        us = [a.elapsed_time(b) * 1e3 for a, b in marks[3:]]
+        ls = [x.cpu().numpy() for x in lens[3:]]
+        med = statistics.median(us)
+        rows = float(np.mean([x.sum() for x in ls]))
+        deepest = float(np.mean([x.max() for x in ls]))
+        nbytes = rows * V * 4
+        out["greedy" if T == 0.0 else "t1"] = {
+            "us_median": round(med, 1), "rows_read_per_call": round(rows, 1),
+            "mean_out_len": round(rows / B, 3), "deepest_walk_rows": round(deepest, 2),
+            "algorithmic_bytes": round(nbytes), "achieved_GBs": round(nbytes / (med * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "us_per_row_of_deepest_walk": round(med / deepest, 2)}
+        del t
+    dr.close()
+    torch.cuda.empty_cache()
+    return {"workload": "b64_tree", "batch": B, "nodes": nn, "K": K, "vocab": V, "reps": reps,
+            "target_rows_bytes_if_all_read": B * nn * V * 4, **out}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +276,7 @@ def main():
     ap.add_argument("--workload", default="b32_ragged4k")
     ap.add_argument("--sigma", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tree", action="store_true", help="skip the tree verifier walk measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -358,6 +448,9 @@ def main():
     dr.close()
     del w
     torch.cuda.empty_cache()
+    if not args.no_tree:
+        log("[bench] tree verify walk (batch 64, 65-node trees) ...")
+        result["tree_verify"] = tree_verify_measure()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(cfg, K, ctx=4096, sigma=sigma)

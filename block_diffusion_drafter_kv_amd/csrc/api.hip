@@ -382,7 +382,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc_t(h, &h->row_pos, c.max_inject_rows, 4))) break;
     if ((rc = alloc_t(h, &h->req_off, c.max_batch + 1, 4))) break;
     if ((rc = alloc_t(h, &h->req_pos, c.max_batch, 4))) break;
-    if ((rc = alloc_t(h, &h->post, (size_t)c.max_batch * std::max(R, c.max_tree + 1), 4))) break;
+    if ((rc = alloc_t(h, &h->post, (size_t)c.max_batch * R, 4))) break;
     if ((rc = alloc_t(h, &h->vstats, (size_t)c.max_batch * (2 * c.max_k + 1) * 2, 4))) break;
   } while (0);
   if (rc) {
@@ -892,10 +892,11 @@ int dflash_verify_tree(dflash_handle* h, void* stream, int32_t n_req, int32_t K,
     return DFLASH_E_INVALID;
   if (!(temperature >= 0.f)) return DFLASH_E_INVALID;
   if (temperature > 0.f && !slots) return DFLASH_E_INVALID;
+  if (temperature > 0.f && (int64_t)tree_walk_segments(c.vocab) * 8 > 65536) return DFLASH_E_CAPACITY;
   hipStream_t s = S(stream);
   Phase ph(h, s, DFLASH_PH_VERIFY);
   launch_verify_tree(n_req, n_nodes, K + 1, c.vocab, slots, tree_tokens, tree_parents, target_logits, temperature,
-                     seed, step, h->post, out_tokens, out_len, accept_len, next_anchor, path_nodes, h->err, s);
+                     seed, step, out_tokens, out_len, accept_len, next_anchor, path_nodes, h->err, s);
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
 

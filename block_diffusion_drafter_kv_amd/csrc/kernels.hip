@@ -806,117 +806,211 @@ __global__ __launch_bounds__(256) void rejection_kernel(int K, int V, const int3
 // moves to the child carrying that token, if any, and otherwise stops with the
 // pick as the new bonus token.  Greedy picks the row argmax (lowest id on ties);
 // T > 0 draws by inverse CDF in ascending id order with u = Philox(seed;
-// depth + 1, slot, step, 4).  Children have larger indices than their parent
-// (the builder numbers nodes in pop order), so a child search starts past it.
-// out_tokens / path rows hold max_out entries (unused -1).
+// depth + 1, slot, step, 4).  out_tokens / path rows hold max_out entries
+// (unused -1); a walk that would pass max_out rows stops there and flags ERR_ROWS,
+// which also bounds the walk on malformed (cyclic) parent arrays.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int tree_child(const int32_t* tok, const int32_t* par, int n_nodes, int node, int pick) {
-  for (int c = node + 1; c < n_nodes; ++c)
-    if (par[c] == node && tok[c] == pick) return c;
-  return -1;
+// One work-group of 1024 threads walks one request's tree and reads only the
+// rows of the nodes it visits.  A row is swept in tiles of 4096 ids: thread t
+// holds ids 4096 * tile + 4t .. 4t + 3, so wave w covers the 256-id segment
+// (tile, w), and segments taken in (tile, wave) order run in ascending id order.
+// Greedy keeps a running (max, lowest id) per thread.  Sampling stores per
+// segment (its max m_s, sum of exp(x - m_s)) in LDS during the one sweep; the
+// block then scans the segment masses rescaled to the row max, finds the
+// segment where u * S falls, and one wave rescans those 256 ids for the id.
+constexpr int WALK_THREADS = 1024, WALK_TILE = 4 * WALK_THREADS, WALK_WAVES = WALK_THREADS / 64;
+constexpr int WALK_BATCH = 12;   // tiles whose loads are in flight together (192 KB per work-group)
+
+__device__ __forceinline__ float4 walk_load(const float* row, int V, int base, bool vec) {
+  if (vec && base + 3 < V) return *(const float4*)(row + base);
+  float4 q;
+  q.x = base < V ? row[base] : -INFINITY;
+  q.y = base + 1 < V ? row[base + 1] : -INFINITY;
+  q.z = base + 2 < V ? row[base + 2] : -INFINITY;
+  q.w = base + 3 < V ? row[base + 3] : -INFINITY;
+  return q;
 }
 
-__global__ void tree_walk_greedy_kernel(int n_req, int n_nodes, int max_out, const int32_t* tokens,
-                                        const int32_t* parents, const int32_t* post, int32_t* out_tokens,
-                                        int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
-                                        int32_t* path_out, int32_t* err) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n_req) return;
-  const int32_t* tok = tokens + (int64_t)r * n_nodes;
-  const int32_t* par = parents + (int64_t)r * n_nodes;
-  const int32_t* pr = post + (int64_t)r * n_nodes;
-  int32_t* o = out_tokens + (int64_t)r * max_out;
-  int32_t* pth = path_out ? path_out + (int64_t)r * max_out : nullptr;
-  int node = 0, a = 0;
-  if (pth) pth[0] = 0;
-  for (;;) {
-    const int pick = pr[node];
-    o[a] = pick;
-    const int nxt = tree_child(tok, par, n_nodes, node, pick);
-    if (nxt < 0) break;
-    if (a + 1 >= max_out) {   // deeper than the output rows allow: stop here
-      raise_error(err, ERR_ROWS);
-      break;
-    }
-    node = nxt;
-    ++a;
-    if (pth) pth[a] = nxt;
-  }
-  for (int i = a + 1; i < max_out; ++i) {
-    o[i] = -1;
-    if (pth) pth[i] = -1;
-  }
-  out_len[r] = a + 1;
-  accept_len[r] = a;
-  if (next_anchor) next_anchor[r] = o[a];
-}
-
-__global__ __launch_bounds__(256) void tree_walk_sample_kernel(int n_nodes, int max_out, int V, const int32_t* slots,
-                                                                const int32_t* tokens, const int32_t* parents,
-                                                                const float* target, float inv_temp, uint64_t seed,
-                                                                uint64_t step, int32_t* out_tokens, int32_t* out_len,
-                                                                int32_t* accept_len, int32_t* next_anchor,
-                                                                int32_t* path_out, int32_t* err) {
-  __shared__ float sh[8];
-  __shared__ float s_total;
-  __shared__ int s_thread, s_pick, s_next;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const uint32_t slot = (uint32_t)slots[r];
+template <bool SAMPLE>
+__global__ __launch_bounds__(WALK_THREADS) void tree_walk_kernel(int n_nodes, int max_out, int V, const int32_t* slots,
+                                                                 const int32_t* tokens, const int32_t* parents,
+                                                                 const float* target, float inv_temp, uint64_t seed,
+                                                                 uint64_t step, int32_t* out_tokens, int32_t* out_len,
+                                                                 int32_t* accept_len, int32_t* next_anchor,
+                                                                 int32_t* path_out, int32_t* err) {
+  extern __shared__ float2 seg[];   // SAMPLE only: [n_tiles * 16] (segment max, segment sum)
+  __shared__ float red_v[WALK_WAVES];
+  __shared__ int red_i[WALK_WAVES];
+  __shared__ float s_total, s_before;
+  __shared__ int s_seg, s_pick, s_child;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int32_t* tok = tokens + (int64_t)r * n_nodes;
   const int32_t* par = parents + (int64_t)r * n_nodes;
   int32_t* o = out_tokens + (int64_t)r * max_out;
   int32_t* pth = path_out ? path_out + (int64_t)r * max_out : nullptr;
-  const int per = (V + 255) / 256;
-  const int c0 = tid * per, c1 = min(V, c0 + per);
+  const uint32_t slot = SAMPLE ? (uint32_t)slots[r] : 0u;
+  const bool vec = (V & 3) == 0;
+  const int n_tiles = (V + WALK_TILE - 1) / WALK_TILE;
+  const int n_seg = n_tiles * WALK_WAVES;
   int node = 0, a = 0;
   if (pth && tid == 0) pth[0] = 0;
   for (;;) {
-    const float* t = target + ((int64_t)r * n_nodes + node) * V;
-    float mx = -INFINITY;
-    for (int c = tid; c < V; c += 256) mx = fmaxf(mx, t[c] * inv_temp);
-    mx = wave_max(mx);
-    __syncthreads();
-    if ((tid & 63) == 0) sh[tid >> 6] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-    float w = 0.f;
-    for (int c = c0; c < c1; ++c) w += expf(t[c] * inv_temp - M);
-    const float incl = block_incl_scan(w, sh);
-    if (tid == 255) s_total = incl;
-    if (tid == 0) { s_thread = -1; s_pick = -1; }
-    __syncthreads();
-    const float u = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_TREE_WALK);
-    const float target_mass = u * s_total;
-    const float excl = incl - w;
-    if (excl <= target_mass && target_mass < incl) s_thread = tid;
-    __syncthreads();
-    if (tid == s_thread) {
-      float acc = excl;
-      for (int c = c0; c < c1; ++c) {
-        const float wc = expf(t[c] * inv_temp - M);
-        if (wc > 0.f && target_mass < acc + wc) { s_pick = c; break; }
-        acc += wc;
+    const float* row = target + ((int64_t)r * n_nodes + node) * V;
+    float best = -INFINITY;
+    int arg = 0x7fffffff;
+    for (int t0 = 0; t0 < n_tiles; t0 += WALK_BATCH) {
+      float4 q[WALK_BATCH];
+#pragma unroll
+      for (int u = 0; u < WALK_BATCH; ++u)
+        q[u] = t0 + u < n_tiles ? walk_load(row, V, (t0 + u) * WALK_TILE + 4 * tid, vec)
+                                : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+#pragma unroll
+      for (int u = 0; u < WALK_BATCH; ++u) {
+        if (t0 + u >= n_tiles) break;
+        if (!SAMPLE) {
+          const int b = (t0 + u) * WALK_TILE + 4 * tid;
+          if (q[u].x > best) { best = q[u].x; arg = b; }
+          if (q[u].y > best) { best = q[u].y; arg = b + 1; }
+          if (q[u].z > best) { best = q[u].z; arg = b + 2; }
+          if (q[u].w > best) { best = q[u].w; arg = b + 3; }
+        } else {
+          const float x0 = q[u].x * inv_temp, x1 = q[u].y * inv_temp, x2 = q[u].z * inv_temp, x3 = q[u].w * inv_temp;
+          const float m = wave_max(fmaxf(fmaxf(x0, x1), fmaxf(x2, x3)));
+          float e = 0.f;
+          if (m > -INFINITY) e = expf(x0 - m) + expf(x1 - m) + expf(x2 - m) + expf(x3 - m);
+          e = wave_sum(e);
+          if (lane == 0) seg[(t0 + u) * WALK_WAVES + wv] = make_float2(m, e);
+        }
       }
     }
-    __syncthreads();
-    if (tid == 0) {
-      int pick = s_pick;
-      if (pick < 0) {   // rounding put u*S on the total: last id with weight
-        for (int c = V - 1; c >= 0; --c)
-          if (expf(t[c] * inv_temp - M) > 0.f) { pick = c; break; }
-        if (pick < 0) pick = 0;
+    int pick;
+    if (!SAMPLE) {
+      const float wm = wave_max(best);
+      int cand = best == wm ? arg : 0x7fffffff;
+      for (int off = 32; off > 0; off >>= 1) cand = min(cand, __shfl_xor(cand, off, 64));
+      if (lane == 0) { red_v[wv] = wm; red_i[wv] = cand; }
+      __syncthreads();
+      if (tid == 0) {
+        float bv = red_v[0];
+        int bi = red_i[0];
+        for (int i = 1; i < WALK_WAVES; ++i)
+          if (red_v[i] > bv || (red_v[i] == bv && red_i[i] < bi)) { bv = red_v[i]; bi = red_i[i]; }
+        s_pick = bi < V ? bi : 0;   // a row of NaN / -inf only: id 0
+        s_child = 0x7fffffff;
       }
-      o[a] = pick;
-      int nxt = tree_child(tok, par, n_nodes, node, pick);
-      if (nxt >= 0 && a + 1 >= max_out) {
-        raise_error(err, ERR_ROWS);
-        nxt = -1;
+      __syncthreads();
+      pick = s_pick;
+    } else {
+      __syncthreads();   // segment table complete
+      // row max, then each thread's consecutive segments' mass at that max, scanned in thread order
+      const int per = (n_seg + WALK_THREADS - 1) / WALK_THREADS;
+      const int g0 = tid * per, g1 = min(n_seg, g0 + per);
+      float mx = -INFINITY;
+      for (int g = g0; g < g1; ++g) mx = fmaxf(mx, seg[g].x);
+      mx = wave_max(mx);
+      if (lane == 0) red_v[wv] = mx;
+      __syncthreads();
+      float M = red_v[0];
+      for (int i = 1; i < WALK_WAVES; ++i) M = fmaxf(M, red_v[i]);
+      float w = 0.f;
+      for (int g = g0; g < g1; ++g) {
+        const float2 sg = seg[g];
+        if (sg.x > -INFINITY) w += sg.y * expf(sg.x - M);
       }
-      s_next = nxt;
+      float x = w;
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      float xp = __shfl_up(x, 1, 64);
+      if (lane == 0) xp = 0.f;
+      __syncthreads();   // red_v reads done
+      if (lane == 63) red_v[wv] = x;
+      if (tid == 0) s_seg = -1;
+      __syncthreads();
+      float off_w = 0.f;
+      for (int i = 0; i < wv; ++i) off_w += red_v[i];
+      // [excl, incl) of neighbouring threads share their end points exactly, so
+      // at most one thread's range holds u * S
+      const float incl = off_w + x, excl = off_w + xp;
+      if (tid == WALK_THREADS - 1) s_total = incl;
+      if (tid == 0) s_child = 0x7fffffff;
+      __syncthreads();
+      const float u = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_TREE_WALK);
+      const float tm = u * s_total;
+      if (w > 0.f && excl <= tm && tm < incl) {
+        float acc = excl;
+        int gs = -1;
+        for (int g = g0; g < g1; ++g) {
+          const float2 sg = seg[g];
+          const float wg = sg.x > -INFINITY ? sg.y * expf(sg.x - M) : 0.f;
+          if (wg > 0.f) { gs = g; s_before = acc; if (tm < acc + wg) break; }
+          acc += wg;
+        }
+        s_seg = gs;
+      }
+      __syncthreads();
+      if (tid == 0 && s_seg < 0) {   // rounding put u * S at or past the total: the last segment with mass
+        float acc = 0.f;
+        for (int g = 0; g < n_seg; ++g) {
+          const float2 sg = seg[g];
+          const float wg = sg.x > -INFINITY ? sg.y * expf(sg.x - M) : 0.f;
+          if (wg > 0.f) { s_seg = g; s_before = acc; }
+          acc += wg;
+        }
+        if (s_seg < 0) s_seg = 0;
+      }
+      __syncthreads();
+      if (wv == 0) {   // rescan the chosen 256-id segment in ascending id order
+        const int gsel = s_seg;
+        const int base = (gsel / WALK_WAVES) * WALK_TILE + (gsel % WALK_WAVES) * 256 + 4 * lane;
+        const float4 q = walk_load(row, V, base, vec);
+        const float e0 = expf(q.x * inv_temp - M), e1 = expf(q.y * inv_temp - M), e2 = expf(q.z * inv_temp - M),
+                    e3 = expf(q.w * inv_temp - M);
+        const float ws = e0 + e1 + e2 + e3;
+        float li = ws;
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(li, off, 64);
+          if (lane >= off) li += y;
+        }
+        float lp = __shfl_up(li, 1, 64);
+        if (lane == 0) lp = 0.f;
+        const float before = s_before;
+        int last = -1;   // this lane's last id with weight
+        if (ws > 0.f) last = e3 > 0.f ? base + 3 : e2 > 0.f ? base + 2 : e1 > 0.f ? base + 1 : base;
+        int found = -1;
+        float acc = before + lp;
+        if (ws > 0.f && acc <= tm && tm < before + li) {
+          const float ev[4] = {e0, e1, e2, e3};
+          found = last;   // rounding inside the lane: its last id with weight
+          for (int k = 0; k < 4; ++k) {
+            if (ev[k] > 0.f && tm < acc + ev[k]) { found = base + k; break; }
+            acc += ev[k];
+          }
+        }
+        // the lane whose range holds u * S; else the last id of the segment with weight
+        int fmin = found < 0 ? 0x7fffffff : found;
+        int lmax = last;
+        for (int off = 32; off > 0; off >>= 1) {
+          fmin = min(fmin, __shfl_xor(fmin, off, 64));
+          lmax = max(lmax, __shfl_xor(lmax, off, 64));
+        }
+        if (lane == 0) s_pick = fmin != 0x7fffffff ? fmin : (lmax >= 0 ? lmax : 0);
+      }
+      __syncthreads();
+      pick = s_pick;
     }
+    // the child of `node` carrying `pick`, searched by all threads (siblings carry distinct tokens;
+    // the lowest index wins should a malformed tree repeat one)
+    for (int c = 1 + tid; c < n_nodes; c += WALK_THREADS)
+      if (par[c] == node && tok[c] == pick) atomicMin(&s_child, c);
+    if (tid == 0) o[a] = pick;
     __syncthreads();
-    const int nxt = s_next;
-    __syncthreads();
+    int nxt = s_child == 0x7fffffff ? -1 : s_child;
+    if (nxt >= 0 && a + 1 >= max_out) {   // deeper than the output rows allow: stop here
+      if (tid == 0) raise_error(err, ERR_ROWS);
+      nxt = -1;
+    }
     if (nxt < 0) break;
     node = nxt;
     ++a;
@@ -1092,18 +1186,21 @@ void launch_verify_greedy(int n_req, int K, int V, const int32_t* draft_ids, con
 
 void launch_verify_tree(int n_req, int n_nodes, int max_out, int V, const int32_t* slots, const int32_t* tokens,
                         const int32_t* parents, const float* target, float temperature, uint64_t seed, uint64_t step,
-                        int32_t* post, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
-                        int32_t* next_anchor, int32_t* path_out, int32_t* err, hipStream_t s) {
+                        int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
+                        int32_t* path_out, int32_t* err, hipStream_t s) {
   if (temperature == 0.f) {
-    argmax_rows_kernel<<<n_req * n_nodes, 256, 0, s>>>(V, target, post);
-    tree_walk_greedy_kernel<<<cdiv(n_req, 64), 64, 0, s>>>(n_req, n_nodes, max_out, tokens, parents, post, out_tokens,
-                                                         out_len, accept_len, next_anchor, path_out, err);
+    tree_walk_kernel<false><<<n_req, WALK_THREADS, 0, s>>>(n_nodes, max_out, V, slots, tokens, parents, target, 1.f,
+                                                           seed, step, out_tokens, out_len, accept_len, next_anchor,
+                                                           path_out, err);
   } else {
-    tree_walk_sample_kernel<<<n_req, 256, 0, s>>>(n_nodes, max_out, V, slots, tokens, parents, target,
-                                                  1.0f / temperature, seed, step, out_tokens, out_len, accept_len,
-                                                  next_anchor, path_out, err);
+    const size_t lds = (size_t)tree_walk_segments(V) * sizeof(float2);
+    tree_walk_kernel<true><<<n_req, WALK_THREADS, lds, s>>>(n_nodes, max_out, V, slots, tokens, parents, target,
+                                                            1.0f / temperature, seed, step, out_tokens, out_len,
+                                                            accept_len, next_anchor, path_out, err);
   }
 }
+
+int tree_walk_segments(int V) { return (V + WALK_TILE - 1) / WALK_TILE * WALK_WAVES; }
 
 void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,
                              const float* draft_logits, const float* target, float inv_temp, uint64_t seed,

@@ -75,8 +75,10 @@ void launch_verify_greedy(int n_req, int K, int V, const int32_t* draft_ids, con
 // draft-tree verifier walk: greedy (row argmax of every node, then the walk) or sampled
 void launch_verify_tree(int n_req, int n_nodes, int max_out, int V, const int32_t* slots, const int32_t* tokens,
                         const int32_t* parents, const float* target, float temperature, uint64_t seed, uint64_t step,
-                        int32_t* post, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
-                        int32_t* next_anchor, int32_t* path_out, int32_t* err, hipStream_t s);
+                        int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
+                        int32_t* path_out, int32_t* err, hipStream_t s);
+// LDS segments (8 bytes each) the sampling tree walk keeps for a vocabulary of V ids.
+int tree_walk_segments(int V);
 void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,
                              const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
                              uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,

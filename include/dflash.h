@@ -219,8 +219,7 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
 
 /* Verifier walk down a draft tree [P5 §3.5 "验证流程(Verifier Walk)"] (one
  * tree per request, as dflash_draft_block builds it: node 0 = root / anchor,
- * nodes numbered so that a parent precedes its children, siblings carrying
- * distinct tokens).  From the root, the target's own decoding rule picks the
+ * siblings carrying distinct tokens).  From the root, the target's own decoding rule picks the
  * next token from target_logits row u (the target's distribution after the
  * path root..u, i.e. the tree evaluated under its ancestor-only mask
  * [P5 §3.3]); the walk moves to the child of u carrying that token, if any, and
@@ -234,7 +233,9 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
  * unused -1), out_len [n_req] = a + 1, accept_len [n_req] = a, next_anchor
  * [n_req] (or NULL) = the bonus, path_nodes [n_req, K+1] (or NULL) = node
  * indices of the accepted path, root first (unused -1).  A walk deeper than K
- * stops there and sets DFLASH_DEV_ROWS in the error word.
+ * stops there and sets DFLASH_DEV_ROWS in the error word.  Only the rows of
+ * the visited nodes are read (one work-group per request).  temperature > 0
+ * needs V <= 2^21 (else DFLASH_E_CAPACITY).
  * Does not touch the cache: inject the path's a + 1 rows next
  * (dflash_inject_tree_path with path_len = out_len). */
 int dflash_verify_tree(dflash_handle* h, void* stream, int32_t n_req, int32_t K, int32_t n_nodes,

@@ -104,6 +104,36 @@ def test_verify_tree_sampling_parity(gpu_lib, T):
     dr.close()
 
 
+@pytest.mark.parametrize("V", [1001, 9001, 12288], ids=["v1001", "v9001", "v12288"])
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_verify_tree_vocab_shapes(gpu_lib, V, T):
+    """Vocabularies that are not a multiple of 4 (scalar loads), span several 4096-id tiles with a
+    ragged last tile, or end exactly on a tile boundary."""
+    cfg = scaled_model(SMALL_BF16, vocab=V, mask_token_id=V - 1)
+    K, n, B = 5, 4, 24
+    dr, _, _ = make_pair(cfg, max_batch=4, max_ctx=64, max_k=8, max_top_k=32, max_tree=32)
+    tt, tp = _trees(dr, n, K, V, B, seed=61)
+    tok, par = tt.cpu().numpy(), tp.cpu().numpy()
+    t = _target_for(tok, par, V, seed=62, bump=6.0 if T == 0.0 else 12.0)
+    slots = [3, 1, 0, 2]
+    checked = 0
+    for step in range(3):
+        r = dr.verify_tree(_dev(slots), K, tt, tp, torch.tensor(t, device="cuda"), temperature=T, seed=5, step=step)
+        torch.cuda.synchronize()
+        for i in range(n):
+            w = over.verify_tree_walk(tok[i], par[i], t[i], T, seed=5, slot=slots[i], step=step)
+            if w["near_margin"] < 1e-5:
+                continue
+            checked += 1
+            L = w["out_len"]
+            assert r["out_len"][i].item() == L, f"step {step} req {i}"
+            assert list(r["out_tokens"][i].cpu().numpy()[:L]) == list(w["out_tokens"])
+            assert list(r["path_nodes"][i].cpu().numpy()[:L]) == list(w["path"])
+    assert checked >= n * 3 // 2   # a draw that lands in the noise tail often sits within 1e-5 of a boundary
+    assert dr.get_error() == 0
+    dr.close()
+
+
 def test_chain_tree_walk_equals_linear_verify_gpu(gpu_lib):
     """A chain tree is one drafted path: the greedy walk must reproduce dflash_verify's greedy result."""
     cfg = SMALL_BF16
