@@ -192,6 +192,64 @@ def idle_weights(cfg):
             "final_norm": z(H), "layers": [lw] * cfg.n_layers}
 
 
+def inject_prompt_measure(w, reps=3):
+    """dflash_inject_context at the long-context shape: 4 requests x 32768-row prompts in one call
+    (131072 rows of 5 x 4096 bf16 target features, N(0,1)), into an emptied cache each time.
+
+    Algorithmic work per call: fc 2 * N * (L_t * H_t) * H flops, the 5-layer K/V product
+    2 * N * H * (L_d * 2 * kv_dim) flops; the per-phase times come from the library's events.
+    """
+    import numpy as np
+    import torch
+
+    import block_diffusion_drafter_kv_amd as dk
+    from synth.configs import get_workload
+
+    wl = get_workload("b4_ctx32k")
+    cfg, B, C = wl.model, wl.batch, wl.ctx
+    N = B * C
+    dr = dk.Drafter(cfg, w, max_batch=B, max_ctx=C + 64, max_k=wl.K, max_inject_rows=N)
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    rows = torch.empty((N, cfg.n_target_layers, cfg.target_hidden), dtype=torch.bfloat16, device="cuda")
+    for s0 in range(0, N, 8192):
+        rows[s0:s0 + 8192] = torch.randn((8192, cfg.n_target_layers, cfg.target_hidden), generator=g,
+                                         device="cuda").to(torch.bfloat16)
+    slots, starts, counts = i32(np.arange(B)), i32(np.arange(B) * C), i32(np.full(B, C))
+    stream = torch.cuda.current_stream()
+    totals, phase_acc = [], {}
+    for i in range(reps + 1):
+        dr.reset(slots)
+        if i > 0:
+            dr.profile(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dr.inject(slots, starts, counts, N, rows)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i > 0:
+            for ph, (ms, n) in dr.profile_read().items():
+                phase_acc.setdefault(ph, []).append(ms)
+            dr.profile(False)
+            totals.append(e0.elapsed_time(e1))
+    assert dr.get_error() == 0
+    dr.close()
+    del rows
+    torch.cuda.empty_cache()
+    fc_flops = 2.0 * N * cfg.feat_dim * cfg.hidden
+    kv_flops = 2.0 * N * cfg.hidden * cfg.n_layers * 2 * cfg.kv_dim
+    ph = {k: statistics.median(v) for k, v in phase_acc.items()}
+    fc_ms, kv_ms, tot = ph.get("inject_fc", float("nan")), ph.get("inject_kv", float("nan")), statistics.median(totals)
+    return {"workload": wl.name, "rows": N, "features": cfg.feat_dim, "reps": reps,
+            "ms_per_call": round(tot, 3), "phase_ms": {k: round(v, 3) for k, v in sorted(ph.items())},
+            "fc": {"flops": fc_flops, "tflops": round(fc_flops / (fc_ms * 1e-3) / 1e12, 1),
+                   "mfma_frac": round(fc_flops / (fc_ms * 1e-3) / 1e12 / PEAK_16B_TFLOPS, 4)},
+            "kv": {"flops": kv_flops, "tflops": round(kv_flops / (kv_ms * 1e-3) / 1e12, 1),
+                   "mfma_frac": round(kv_flops / (kv_ms * 1e-3) / 1e12 / PEAK_16B_TFLOPS, 4)},
+            "gemm_mfma_frac": round((fc_flops + kv_flops) / ((fc_ms + kv_ms) * 1e-3) / 1e12 / PEAK_16B_TFLOPS, 4),
+            "call_mfma_frac": round((fc_flops + kv_flops) / (tot * 1e-3) / 1e12 / PEAK_16B_TFLOPS, 4)}
+
+
 def tree_verify_measure(reps=20):
     """dflash_verify_tree at the batch-64 tree shape (64 requests, 65-node best-first trees from
     top-64 marginals, K = 16, V = 151936), greedy and T = 1.
@@ -277,6 +335,7 @@ def main():
     ap.add_argument("--sigma", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tree", action="store_true", help="skip the tree verifier walk measurement")
+    ap.add_argument("--no-inject", action="store_true", help="skip the long-prompt injection measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -446,6 +505,10 @@ def main():
         "phase_ms_per_step": {p: round(t, 4) for p, t in sorted(totals.items(), key=lambda x: -x[1])},
     }
     dr.close()
+    torch.cuda.empty_cache()
+    if not args.no_inject:
+        log("[bench] prompt injection (4 x 32768 rows, one call) ...")
+        result["inject_prompt"] = inject_prompt_measure(w)
     del w
     torch.cuda.empty_cache()
     if not args.no_tree:

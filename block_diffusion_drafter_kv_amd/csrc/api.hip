@@ -468,7 +468,7 @@ int inject_rows(dflash_handle* h, hipStream_t s, int n_req, int64_t rows_upper_b
     EpiStore<float>::Params pf{h->y, H};
     {
       Phase ph(h, s, DFLASH_PH_INJECT_FC);
-      launch_gemm(h->op_fc, EPI_STORE_F32, ga, &pf, plan_gemm(h->op_fc, plan_rows, H, featK, h->num_cus),
+      launch_gemm(h->op_fc, EPI_STORE_F32, ga, &pf, plan_gemm(h->op_fc, plan_rows, H, featK, h->num_cus, false, true),
                   h->partials, h->partials_elems, s);
     }
     {
@@ -507,7 +507,7 @@ int inject_rows(dflash_handle* h, hipStream_t s, int n_req, int64_t rows_upper_b
       pk.layer0 = l0;
       // the parameter block has the same layout for fp32 (pointers only differ in type)
       Phase ph(h, s, DFLASH_PH_INJECT_KV);
-      launch_gemm(h->op, EPI_KVINJECT, gk, &pk, plan_gemm(h->op, plan_rows, gk.N, H, h->num_cus), h->partials,
+      launch_gemm(h->op, EPI_KVINJECT, gk, &pk, plan_gemm(h->op, plan_rows, gk.N, H, h->num_cus, false, true), h->partials,
                   h->partials_elems, s);
     }
   }
@@ -795,7 +795,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     pl.inv_temp = T > 0.f ? 1.0f / T : 1.0f;
     pl.out_mult = c.output_multiplier;
     pl.softcap = c.logit_softcap;
-    GemmPlan gp = plan_gemm(h->op, rows, V, H, h->num_cus, /*wide=*/true);
+    GemmPlan gp = plan_gemm(h->op, rows, V, H, h->num_cus, /*wide=*/true, /*big_ok=*/true);
     gp.splits = 1;   // the vocabulary gives plenty of tiles; statistics are per output tile
     Phase ph(h, s, DFLASH_PH_LM_HEAD);
     launch_gemm(h->op, EPI_LMHEAD, ga, &pl, gp, h->partials, h->partials_elems, s);

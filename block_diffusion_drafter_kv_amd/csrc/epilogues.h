@@ -188,7 +188,10 @@ struct EpiKVInject {
   }
 };
 
-// ---- LM head: logits (optional store) + per-(row, tile) max / sum-exp / argmax ----
+// ---- LM head: logits (optional store) + per-(row, 128-column tile) max / sum-exp / argmax ----
+// The statistics tile is 128 columns whatever the GEMM tile: a BN-wide GEMM tile
+// tn writes statistics tiles tn * BN/128 .. +BN/128-1.
+constexpr int LM_STAT_TILE = 128;
 struct EpiLMHead {
   struct Params {
     float* logits;           // [M][ld] or null
@@ -202,16 +205,18 @@ struct EpiLMHead {
   template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int tn,
                                int tid) {
+    static_assert(BN % LM_STAT_TILE == 0, "GEMM tile of whole statistics tiles");
     const int lane = tid & 63, wave = tid >> 6;
-    for (int r = wave; r < ROWS; r += 4) {
+    for (int it = wave; it < ROWS * (BN / LM_STAT_TILE); it += 4) {
+      const int r = it % ROWS, hs = it / ROWS;   // row, statistics tile inside the GEMM tile
       const int m = m0 + r;
-      if (m >= M) break;
+      if (m >= M) continue;
       float best = -INFINITY;
       int arg = 0x7fffffff;
-      float zz[BN / 64];
+      float zz[LM_STAT_TILE / 64];
 #pragma unroll
-      for (int q = 0; q < BN / 64; ++q) {
-        const int c = lane + 64 * q, n = n0 + c;
+      for (int q = 0; q < LM_STAT_TILE / 64; ++q) {
+        const int c = hs * LM_STAT_TILE + lane + 64 * q, n = n0 + c;
         float z = st[r * ld + c] * p.out_mult;
         if (p.softcap > 0.f) z = p.softcap * tanhf(z / p.softcap);
         zz[q] = z;
@@ -227,13 +232,14 @@ struct EpiLMHead {
       for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o, 64));
       float e = 0.f;
 #pragma unroll
-      for (int q = 0; q < BN / 64; ++q) {
-        const int n = n0 + lane + 64 * q;
+      for (int q = 0; q < LM_STAT_TILE / 64; ++q) {
+        const int n = n0 + hs * LM_STAT_TILE + lane + 64 * q;
         if (n < N) e += expf(zz[q] * p.inv_temp - mx);
       }
       e = wave_sum(e);
-      if (lane == 0) {
-        const int64_t o = (int64_t)m * p.n_tiles + tn;
+      const int t = tn * (BN / LM_STAT_TILE) + hs;
+      if (lane == 0 && t < p.n_tiles) {
+        const int64_t o = (int64_t)m * p.n_tiles + t;
         p.tile_max[o] = mx;
         p.tile_sum[o] = e;
         p.tile_arg[o] = cand;

@@ -8,11 +8,20 @@ void gemm_dispatch_bf16(EpiKind kind, const GemmPlan& pl, const GemmArgs& g, con
   if (kind == EPI_STORE_F32) gemm_cfg<bf16_t, EpiStore<float>>(pl, g, ep, s);
 }
 
-GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide) {
+GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide, bool big_ok) {
   GemmPlan p;
   const bool w16 = op != OP_F32;
   p.bn = 128;
   p.bm = M <= 64 ? 64 : 128;
+  // 256 x 256 tiles (one 8-wave work-group per CU) once the grid still holds at
+  // least one tile per CU: the injection's fc and K|V products over thousands of
+  // rows and the vocabulary product over >= 256 rows (measured: fc 16384 x 4096
+  // x 20480 and the 512 x 151936 x 4096 LM head, against 128 x 128 tiles)
+  if (w16 && big_ok && M >= 256 && (wide || M >= 2048) &&
+      (long)((M + 255) / 256) * ((N + 255) / 256) >= num_cus) {
+    p.bm = p.bn = 256;
+    return p;
+  }
   if (w16 && wide) {
     // the vocabulary product: 128 x 128 tiles with a 3-deep weight ring (measured
     // on the 512 x 151936 x 4096 LM head: 743 us, against 1023 us for 128 x 256)

@@ -6,11 +6,34 @@
 //   16-bit, M <= 64: 64 x 128, 3 stages
 //   16-bit LM head and long-K products: 128 x 128, A 2 stages, B 3 stages
 //   fp32           : 128 x 128 or 64 x 128
+//   16-bit, many rows (injection fc and K|V) and the vocabulary product: 256 x 256
+//   (gemm256.h), for the epilogues listed in Gemm256Epi
 #pragma once
 #include "gemm2.h"
+#include "gemm256.h"
 #include "ops.h"
 
 namespace dfl {
+
+// Epilogues the 256 x 256 kernel is instantiated for (the products planned onto it)
+template <class Epi> struct Gemm256Epi { static constexpr bool value = false; };
+template <> struct Gemm256Epi<EpiStore<float>> { static constexpr bool value = true; };
+template <> struct Gemm256Epi<EpiKVInject<f16_t>> { static constexpr bool value = true; };
+template <> struct Gemm256Epi<EpiKVInject<bf16_t>> { static constexpr bool value = true; };
+template <> struct Gemm256Epi<EpiLMHead> { static constexpr bool value = true; };
+
+template <typename T, class Epi>
+static void gemm256_go(const GemmArgs& g, const void* ep, hipStream_t s) {
+  const typename Epi::Params& p = *(const typename Epi::Params*)ep;
+  dim3 grid(gemm_grid(g.tiles_m * g.tiles_n), 1);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (g.a_wide) {
+      gemm256_kernel<T, Epi, true><<<grid, GEMM256_THREADS, 0, s>>>(g, p);
+      return;
+    }
+  }
+  gemm256_kernel<T, Epi><<<grid, GEMM256_THREADS, 0, s>>>(g, p);
+}
 
 template <typename T, int BM, int BN, int SA, int SB, class Epi>
 static void gemm2_go(const GemmArgs& g, const void* ep, hipStream_t s) {
@@ -40,6 +63,12 @@ static void gemm1_go(const GemmArgs& g, const void* ep, hipStream_t s) {
 template <typename T, class Epi>
 static void gemm_cfg(const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
+    if constexpr (Gemm256Epi<Epi>::value) {
+      if (pl.bm == 256) {
+        gemm256_go<T, Epi>(g, ep, s);
+        return;
+      }
+    }
     if (pl.bm == 64) gemm2_go<T, 64, 128, 3, 3, Epi>(g, ep, s);
     else if (pl.sb == 3) gemm2_go<T, 128, 128, 2, 3, Epi>(g, ep, s);
     else gemm2_go<T, 128, 128, 2, 2, Epi>(g, ep, s);

@@ -39,12 +39,39 @@ __device__ __forceinline__ void copy16_to_lds_sv(const void* sbase, uint32_t vof
       : "memory");
 }
 
+// The same two copies without a memory clobber, for loops whose barriers
+// (lds_barrier, which clobbers memory) already order every copy against the LDS
+// reads of its stage: the clobber would make the compiler reload kernel
+// arguments after each copy and wait for all outstanding LDS reads first.
+// Volatile asm statements keep their order among themselves.
+__device__ __forceinline__ void copy16_to_lds_nc(const void* g, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(g));
+}
+__device__ __forceinline__ void copy16_to_lds_sv_nc(const void* sbase, uint32_t voff, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(sbase));
+}
+
 // s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// s_waitcnt lgkmcnt(0) leaving the other counters unconstrained
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Workgroup barrier that is also a compiler memory fence (no LDS access moves
 // across it) but, unlike __syncthreads, emits no wait on outstanding copies.

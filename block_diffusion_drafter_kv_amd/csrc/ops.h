@@ -24,7 +24,9 @@ struct GemmPlan {
 inline int gemm_bn(int) { return 128; }
 // Choose tile/split for an M x N x K product (K multiple of the slab); wide = the
 // vocabulary product (widest tiles).
-GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide = false);
+// big_ok: the product's epilogue has a 256 x 256 instantiation (fc store, K|V
+// injection, LM head).
+GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide = false, bool big_ok = false);
 // Fill tiles/splits/partials fields of g and launch kernel (+ reduce when split).
 // op: operand type; OP_BF16 supports only EPI_STORE_F32 (the fc product).
 void launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan,
