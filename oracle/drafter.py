@@ -23,6 +23,19 @@ theta^(-2i/d); attention scale 1/sqrt(d); q head h uses kv head h // (n_q/n_kv);
 a final RMSNorm precedes the LM head; the fused feature g is shared by all
 layers (one RMSNorm after fc, no per-layer norm on g).
 
+DFlash 2 dynamic convolution [P2 §3.2.3 "设计：双抽头动态深度卷积"], when the
+layer carries conv weights: a two-tap depthwise convolution over the block's
+rows, y_t = k_{t,0} * x_t + k_{t,1} * x_{t-1}, where each tap's kernel is a
+learned per-channel base plus a correction projected linearly from x_t and
+shared by every group of conv_group channels; the row before the anchor is zero
+(block-local, zero padding).  Readings: the layer holds two convolutions,
+attention_conv and mlp_conv; each acts on its sub-layer's input, i.e. on the
+RMS-normalised rows that feed the q/k/v projections and the gate/up
+projections respectively (the pages place them in the layer's "prepare" and
+"finish" halves); the correction projection has no bias, its output rows
+[0, H/G) correct tap 0 and rows [H/G, 2H/G) tap 1, channel c using group c // G;
+context rows are untouched (their K/V come from the fused target feature).
+
 Parity of absolute forward values is unpinned by the pages (no page prints an
 activation or a logit); the pieces are pinned against library routines and the
 invariants listed in tests/test_oracle_drafter.py.
@@ -79,6 +92,22 @@ def attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, group: int) -> 
         a /= a.sum(axis=-1, keepdims=True)
         out[:, h, :] = a @ vals[:, kv, :]
     return out
+
+
+def dynamic_conv(x: np.ndarray, base: np.ndarray, proj: np.ndarray, group: int) -> np.ndarray:
+    """Two-tap dynamic depthwise conv over the rows of one block, x [R, H] (row 0 = anchor).
+
+    base [2, H] per-channel kernels of the taps; proj [2*H/group, H] projects each
+    row to its per-group kernel corrections (tap 0 groups first, then tap 1).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    R, H = x.shape
+    ng = H // group
+    corr = x @ np.asarray(proj, dtype=np.float64).T                    # [R, 2 * ng]
+    k0 = base[0][None, :] + np.repeat(corr[:, :ng], group, axis=1)
+    k1 = base[1][None, :] + np.repeat(corr[:, ng:], group, axis=1)
+    prev = np.concatenate([np.zeros((1, H)), x[:-1]], axis=0)           # zero row before the anchor
+    return k0 * x + k1 * prev
 
 
 class DrafterOracle:
@@ -144,6 +173,8 @@ class DrafterOracle:
         pos = np.arange(C, C + R) + self.pos_offset
         for l, lw in enumerate(self.layers):
             h = rms_norm(X, lw["in_norm"], c.rms_eps)
+            if "attn_conv_base" in lw:
+                h = dynamic_conv(h, lw["attn_conv_base"], lw["attn_conv_proj"], c.conv_group)
             q = (h @ lw["q_w"].T).reshape(R, c.n_q_heads, self.d)
             k = (h @ lw["k_w"].T).reshape(R, c.n_kv_heads, self.d)
             v = (h @ lw["v_w"].T).reshape(R, c.n_kv_heads, self.d)
@@ -160,11 +191,17 @@ class DrafterOracle:
                 o = attention(q, keys, vals, c.group)
             X = X + o.reshape(R, c.q_dim) @ lw["o_w"].T
             h = rms_norm(X, lw["post_norm"], c.rms_eps)
+            if "mlp_conv_base" in lw:
+                h = dynamic_conv(h, lw["mlp_conv_base"], lw["mlp_conv_proj"], c.conv_group)
             X = X + (silu(h @ lw["gate_w"].T) * (h @ lw["up_w"].T)) @ lw["down_w"].T
         return X
 
     def block_logits(self, slot: int, anchor: int, K: int, single_query: bool = False) -> np.ndarray:
         """Logits [K, V] of the mask rows (block positions 1..K)."""
+        return self.block_final(slot, anchor, K, single_query)[0]
+
+    def block_final(self, slot: int, anchor: int, K: int, single_query: bool = False):
+        """(logits [K, V], final-normalised hidden rows [K, H]) of the mask rows."""
         X = self.block_hidden(slot, anchor, K, single_query)
-        z = rms_norm(X[1:], self.final_norm, self.cfg.rms_eps)
-        return z @ self.lm_head.T
+        h = rms_norm(X[1:], self.final_norm, self.cfg.rms_eps)
+        return h @ self.lm_head.T, h

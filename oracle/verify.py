@@ -32,6 +32,16 @@ inverse-CDF draw from softmax(t_u / T) in ascending id order with the uniform
 Philox(seed; depth(u) + 1, slot, step, purpose 4), one per walk step.  The
 emitted sequence is then always a draw from the target itself, whatever the
 tree.
+
+Subset-q rejection sampling [P2 §3.1.3, §4.2]: when the draft came from the
+DFlash 2 selector, the drafter's distribution at position i is given as C
+candidate ids and their probabilities (a distribution over that subset).  It is
+projected back onto token ids -- q_full(v) = the summed probability of the
+candidates carrying id v (zero outside the subset) -- and the usual test runs
+with q_full: accept d_i iff u_i * q_full(d_i) < p_{i-1}(d_i); at the first
+rejection draw from max(0, p_{i-1} - q_full) renormalised (p_{i-1} when that
+mass is below RESIDUAL_EPS); after K acceptances the bonus comes from p_K.
+Same Philox purposes and readings as the full-vocabulary test above.
 """
 from __future__ import annotations
 
@@ -142,3 +152,54 @@ def verify_tree_walk(tree_tokens, tree_parents, target_logits, T, seed=0, slot=0
     a = len(out) - 1
     return {"out_tokens": np.array(out, dtype=np.int64), "path": np.array(path, dtype=np.int64),
             "out_len": a + 1, "accept_len": a, "near_margin": near}
+
+
+def subset_to_full(cand_ids, cand_probs, V):
+    """q_full [K, V]: each row's candidate probabilities summed onto their token ids."""
+    cand_ids = np.asarray(cand_ids, dtype=np.int64)
+    cand_probs = np.asarray(cand_probs, dtype=np.float64)
+    K = cand_ids.shape[0]
+    q = np.zeros((K, V))
+    for i in range(K):
+        np.add.at(q[i], cand_ids[i], cand_probs[i])
+    return q
+
+
+def verify_rejection_subset(draft_ids, cand_ids, cand_probs, target_logits, T, seed, slot, step, uniform_fn=None):
+    """Rejection verification of a selector draft (see the module docstring).
+
+    draft_ids [K]; cand_ids / cand_probs [K, C]; target_logits [K+1, V].
+    """
+    if uniform_fn is None:
+        def uniform_fn(position, purpose):
+            return float(philox.uniform(seed, slot, step, position, purpose))
+    d = np.asarray(draft_ids, dtype=np.int64)
+    K = d.shape[0]
+    t = np.asarray(target_logits, dtype=np.float64)
+    if T <= 0:
+        return verify_greedy(d, t)
+    p = softmax(t, T)
+    q = subset_to_full(cand_ids, cand_probs, t.shape[1])
+    near = np.inf
+    out = []
+    for i in range(1, K + 1):
+        pi, qi = p[i - 1][d[i - 1]], q[i - 1][d[i - 1]]
+        u = uniform_fn(i, philox.PURPOSE_ACCEPT)
+        near = min(near, abs(u * qi - pi) / max(pi, qi, 1e-300))
+        if u * qi < pi:
+            out.append(int(d[i - 1]))
+            continue
+        r = np.maximum(p[i - 1] - q[i - 1], 0.0)
+        u2 = uniform_fn(i, philox.PURPOSE_RESAMPLE)
+        rs = r.sum()
+        near = min(near, abs(rs - RESIDUAL_EPS) / RESIDUAL_EPS)
+        c, m2 = inverse_cdf(r if rs >= RESIDUAL_EPS else p[i - 1], u2)
+        near = min(near, m2)
+        out.append(c)
+        return {"out_tokens": np.array(out, dtype=np.int64), "out_len": i, "accept_len": i - 1,
+                "near_margin": near, "fallback": bool(rs < RESIDUAL_EPS)}
+    c, m2 = inverse_cdf(p[K], uniform_fn(K + 1, philox.PURPOSE_RESAMPLE))
+    near = min(near, m2)
+    out.append(c)
+    return {"out_tokens": np.array(out, dtype=np.int64), "out_len": K + 1, "accept_len": K,
+            "near_margin": near, "fallback": False}

@@ -28,6 +28,9 @@ class DrafterConfig:
     rope_theta: float = 1e6
     input_embedding_scale: float = 1.0
     target_layer_ids: Tuple[int, ...] = ()
+    conv_group: int = 0        # DFlash 2 dynamic conv: channels per kernel-correction group (0 = no conv)
+    sel_rank: int = 0          # DFlash 2 path selector: codebook rank (0 = no selector)
+    sel_cands: int = 16        # candidates per position kept by the selector
 
     @property
     def q_dim(self) -> int:

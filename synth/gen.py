@@ -105,6 +105,46 @@ def weights(cfg: DrafterConfig, seed: int = 1234, gains: str = "ones",
     return w
 
 
+def dflash2_weights(cfg: DrafterConfig, seed: int = 4321, conv_base_std: float = 0.3, conv_proj_std: float = 0.02,
+                    codebook_std: float = 0.2, sel_hidden_std: float = 0.02) -> Dict[str, object]:
+    """Weights of the DFlash 2 modules, in the model dtype, as CPU tensors.
+
+    Per layer (when cfg.conv_group > 0): attn_conv_base / mlp_conv_base [2, H]
+    (tap 0 drawn around 1, tap 1 around 0), attn_conv_proj / mlp_conv_proj
+    [2 * H / conv_group, H].  Shared (when cfg.sel_rank > 0): sel_pred and sel_succ
+    [V, rank] codebooks, sel_hidden [rank, H].  Returns {"layers": [...], ...} to
+    merge into the dict of `weights`.
+    """
+    dt = cfg.dtype
+    H, V = cfg.hidden, cfg.vocab
+    out: Dict[str, object] = {"layers": [{} for _ in range(cfg.n_layers)]}
+    if cfg.conv_group > 0:
+        G = cfg.conv_group
+        for l in range(cfg.n_layers):
+            for name in ("attn", "mlp"):
+                base = normal((2, H), conv_base_std, "f32", seed, l, name, "conv_base")
+                base[0] += 1.0
+                out["layers"][l][f"{name}_conv_base"] = base.to(torch_dtype(dt))
+                out["layers"][l][f"{name}_conv_proj"] = normal((2 * H // G, H), conv_proj_std, dt, seed, l, name,
+                                                               "conv_proj")
+    if cfg.sel_rank > 0:
+        r = cfg.sel_rank
+        out["sel_pred"] = normal((V, r), codebook_std, dt, seed, "sel_pred")
+        out["sel_succ"] = normal((V, r), codebook_std, dt, seed, "sel_succ")
+        out["sel_hidden"] = normal((r, H), sel_hidden_std, dt, seed, "sel_hidden")
+    return out
+
+
+def merge_weights(w: Dict[str, object], extra: Dict[str, object]) -> Dict[str, object]:
+    """w with the entries of dflash2_weights(...) added (per-layer dicts merged)."""
+    out = dict(w)
+    out["layers"] = [dict(a, **b) for a, b in zip(w["layers"], extra["layers"])]
+    for k, v in extra.items():
+        if k != "layers":
+            out[k] = v
+    return out
+
+
 def hidden_rows(cfg: DrafterConfig, slot: int, pos0: int, n: int, seed: int = 2024) -> torch.Tensor:
     """Target hidden states for positions [pos0, pos0+n) of request `slot`.
 
