@@ -250,6 +250,69 @@ def inject_prompt_measure(w, reps=3):
             "call_mfma_frac": round((fc_flops + kv_flops) / (tot * 1e-3) / 1e12 / PEAK_16B_TFLOPS, 4)}
 
 
+def dflash2_measure(w, ctx, steps=10, warmup=2):
+    """Draft steps of the same batch-32 workload with the DFlash 2 modules on: dynamic
+    convolutions in every layer (group 16) and the path selector (16 candidates, rank 256),
+    greedy.  Reports the draft time, the two modules' per-step time from the library's events and
+    the overhead against the plain draft; the selector's walk is one work-group per request."""
+    import numpy as np
+    import torch
+
+    import block_diffusion_drafter_kv_amd as dk
+    from synth import gen
+    from synth.configs import get_workload, scaled_model
+
+    wl = get_workload("b32_ragged4k")
+    cfg = scaled_model(wl.model, conv_group=16, sel_rank=256, sel_cands=16)
+    B, K = wl.batch, wl.K
+    extra = gen.dflash2_weights(cfg, seed=77)
+    dev = lambda t: t.cuda()
+    w2 = dict(w)
+    w2["layers"] = [dict(a, **{k: dev(v) for k, v in b.items()}) for a, b in zip(w["layers"], extra["layers"])]
+    for k in ("sel_pred", "sel_succ", "sel_hidden"):
+        w2[k] = dev(extra[k])
+    dr = dk.Drafter(cfg, w2, max_batch=B, max_ctx=max(ctx) + 64, max_k=K, max_inject_rows=8192)
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(2024)
+    for r, c in enumerate(ctx):
+        for s0 in range(0, c, 8192):
+            n = min(8192, c - s0)
+            rows = torch.randn((n, cfg.n_target_layers, cfg.target_hidden), generator=g, device="cuda",
+                               dtype=torch.float32).to(torch.bfloat16)
+            dr.inject(i32([r]), i32([0]), i32([n]), n, rows)
+    slots = i32(np.arange(B))
+    anchors = i32(np.random.default_rng(3).integers(0, cfg.vocab - 1, B))
+    stream = torch.cuda.current_stream()
+    logits = torch.empty((B, K, cfg.vocab), dtype=torch.float32, device="cuda")   # as the plain draft above
+    for _ in range(warmup):
+        dr.draft(slots, anchors, K, want_stats=False, logits_out=logits)
+    torch.cuda.synchronize()
+    marks = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dr.draft(slots, anchors, K, want_stats=False, logits_out=logits)
+        e1.record(stream)
+        marks.append((e0, e1))
+    torch.cuda.synchronize()
+    # per-phase breakdown in a separate pass (the events between phases cost time of their own)
+    dr.profile(True)
+    for _ in range(steps):
+        dr.draft(slots, anchors, K, want_stats=False, logits_out=logits)
+    torch.cuda.synchronize()
+    ph = dr.profile_read()
+    dr.profile(False)
+    assert dr.get_error() == 0
+    dr.close()
+    torch.cuda.empty_cache()
+    us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in marks)
+    per_step = {k: round(v[0] / steps, 4) for k, v in ph.items() if v[1]}
+    return {"workload": wl.name, "conv_group": 16, "sel_rank": 256, "sel_cands": 16, "steps": steps,
+            "draft_us_median": round(us, 1), "draft_tokens_per_s": round(B * K / (us * 1e-6), 1),
+            "conv_ms_per_step": per_step.get("conv"), "selector_ms_per_step": per_step.get("selector"),
+            "phase_ms_per_step": dict(sorted(per_step.items(), key=lambda x: -x[1]))}
+
+
 def tree_verify_measure(reps=20):
     """dflash_verify_tree at the batch-64 tree shape (64 requests, 65-node best-first trees from
     top-64 marginals, K = 16, V = 151936), greedy and T = 1.
@@ -336,6 +399,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tree", action="store_true", help="skip the tree verifier walk measurement")
     ap.add_argument("--no-inject", action="store_true", help="skip the long-prompt injection measurement")
+    ap.add_argument("--no-dflash2", action="store_true", help="skip the DFlash 2 modules measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -509,6 +573,11 @@ def main():
     if not args.no_inject:
         log("[bench] prompt injection (4 x 32768 rows, one call) ...")
         result["inject_prompt"] = inject_prompt_measure(w)
+    if not args.no_dflash2:
+        log("[bench] DFlash 2 modules (conv + selector) on the same workload ...")
+        d2 = dflash2_measure(w, ctx)
+        d2["overhead_vs_plain_draft"] = round(d2["draft_us_median"] / (draft_ms * 1e3) - 1.0, 4)
+        result["dflash2"] = d2
     del w
     torch.cuda.empty_cache()
     if not args.no_tree:

@@ -33,17 +33,19 @@ class dflash_config(ctypes.Structure):
                 ("rms_eps", c_float), ("rope_theta", c_float), ("input_embedding_scale", c_float),
                 ("output_multiplier", c_float), ("logit_softcap", c_float), ("max_batch", c_int32),
                 ("max_ctx", c_int32), ("max_k", c_int32), ("max_inject_rows", c_int32), ("max_top_k", c_int32),
-                ("max_tree", c_int32)]
+                ("max_tree", c_int32), ("conv_group", c_int32), ("sel_rank", c_int32), ("sel_cands", c_int32)]
 
 
 class dflash_layer_weights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("in_norm", "q_w", "k_w", "v_w", "o_w", "q_norm", "k_norm", "post_norm",
-                                        "gate_w", "up_w", "down_w")]
+                                        "gate_w", "up_w", "down_w", "attn_conv_base", "attn_conv_proj",
+                                        "mlp_conv_base", "mlp_conv_proj")]
 
 
 class dflash_weights(ctypes.Structure):
     _fields_ = [("embed", c_void_p), ("lm_head", c_void_p), ("fc", c_void_p), ("hidden_norm", c_void_p),
-                ("final_norm", c_void_p), ("n_layers", c_int32), ("layers", POINTER(dflash_layer_weights))]
+                ("final_norm", c_void_p), ("n_layers", c_int32), ("layers", POINTER(dflash_layer_weights)),
+                ("sel_pred", c_void_p), ("sel_succ", c_void_p), ("sel_hidden", c_void_p)]
 
 
 class dflash_draft_params(ctypes.Structure):
@@ -54,7 +56,8 @@ class dflash_draft_params(ctypes.Structure):
 class dflash_draft_outputs(ctypes.Structure):
     _fields_ = [("draft_ids", c_void_p), ("topk_ids", c_void_p), ("topk_probs", c_void_p), ("row_max", c_void_p),
                 ("row_lse", c_void_p), ("logits", c_void_p), ("tree_tokens", c_void_p), ("tree_parents", c_void_p),
-                ("tree_depth", c_void_p), ("tree_mask", c_void_p)]
+                ("tree_depth", c_void_p), ("tree_mask", c_void_p), ("cand_ids", c_void_p),
+                ("cand_probs", c_void_p), ("hidden", c_void_p)]
 
 
 _SIGS = {
@@ -73,6 +76,10 @@ _SIGS = {
                             c_float, c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
     "dflash_inject_tree_path": ([c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int64,
                                  POINTER(c_void_p), c_int64], c_int32),
+    "dflash_select_path": ([c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
+                            c_uint64, c_uint64, c_void_p, c_void_p, c_void_p], c_int32),
+    "dflash_verify_subset": ([c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_float, c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
     "dflash_profile": ([c_void_p, c_int32], c_int32),
     "dflash_profile_read": ([c_void_p, c_int32, POINTER(ctypes.c_double), POINTER(c_int32)], c_int32),
     "dflash_get_error": ([c_void_p, c_void_p, POINTER(c_int32)], c_int32),
@@ -162,8 +169,20 @@ def dflash_inject_tree_path(h, stream, n_req, slots, path_nodes, path_len, max_p
                  rows_upper_bound, arr, row_stride)
 
 
+def dflash_select_path(h, stream, n_req, K, slots, anchors, logits, hidden, temperature, seed, step, draft_ids,
+                       cand_ids, cand_probs):
+    return _call("dflash_select_path", h, stream, n_req, K, slots, anchors, logits, hidden, temperature, seed, step,
+                 draft_ids, cand_ids, cand_probs)
+
+
+def dflash_verify_subset(h, stream, n_req, K, C, slots, draft_ids, cand_ids, cand_probs, target_logits, temperature,
+                         seed, step, out_tokens, out_len, accept_len, next_anchor=None):
+    return _call("dflash_verify_subset", h, stream, n_req, K, C, slots, draft_ids, cand_ids, cand_probs,
+                 target_logits, temperature, seed, step, out_tokens, out_len, accept_len, next_anchor)
+
+
 PHASES = ("inject_prep", "inject_fc", "inject_norm", "inject_kv", "embed", "qkv", "attn", "attn_combine", "o",
-          "norm", "gate_up", "down", "lm_head", "select", "verify", "attn_plan")
+          "norm", "gate_up", "down", "lm_head", "select", "verify", "attn_plan", "conv", "selector")
 
 
 def dflash_profile(h, enable: bool):

@@ -18,11 +18,12 @@ struct dflash_handle {
   int esize = 4;
   int device = 0, num_cus = 256;
   // borrowed weights
+  const void* sel_hidden_src = nullptr;   // caller's W_H
   const void *embed = nullptr, *lm_head = nullptr, *fc = nullptr, *hidden_norm = nullptr, *final_norm = nullptr;
   std::vector<dflash_layer_weights> layers;
   // matrices as the products read them: the caller's (fp32 drafter) or the
   // handle's fp16 copies scaled by 2^wscale_log2 (bf16 drafter)
-  struct Mats { const void *q, *k, *v, *o, *gate, *up, *down; };
+  struct Mats { const void *q, *k, *v, *o, *gate, *up, *down, *conv_a, *conv_m; };
   std::vector<Mats> mats;
   const void* lm = nullptr;
   int op = OP_F32, op_fc = OP_F32;  // operand type of the products / of the fc product
@@ -59,6 +60,14 @@ struct dflash_handle {
   float* y = nullptr;
   void* g = nullptr;
   int32_t *a_rows = nullptr, *row_slot = nullptr, *row_pos = nullptr, *req_off = nullptr, *req_pos = nullptr;
+  // DFlash 2 modules
+  void* hbuf2 = nullptr;                  // convolved sub-layer input
+  float* cbuf = nullptr;                  // kernel corrections [maxM, 2H/G]
+  const void* sel_h = nullptr;            // W_H (fp16 copy for a bf16 drafter)
+  const void *sel_pred = nullptr, *sel_succ = nullptr;
+  float *sel_gate = nullptr, *sel_cprob = nullptr, *sel_probs_ws = nullptr, *sel_table = nullptr;
+  int32_t *sel_cand = nullptr, *sel_ids_ws = nullptr;
+  void* sel_hin = nullptr;                // caller hidden rows in the operand type
   // verification
   int32_t* post = nullptr;
   float* vstats = nullptr;
@@ -146,6 +155,11 @@ int check_config(const dflash_config& c) {
   if (c.n_target_layers > MAX_ASEG) return DFLASH_E_UNSUPPORTED;
   if (c.max_k > 31) return DFLASH_E_UNSUPPORTED;
   if (c.max_top_k > 256 || c.max_tree > 256) return DFLASH_E_UNSUPPORTED;
+  if (c.conv_group < 0 || c.sel_rank < 0) return DFLASH_E_INVALID;
+  if (c.conv_group > 0 && (c.conv_group % 4 || c.hidden % c.conv_group || (2 * c.hidden / c.conv_group) % 8))
+    return DFLASH_E_UNSUPPORTED;
+  if (c.sel_rank > 0 && (c.sel_rank > 4096 || c.sel_cands < 1 || c.sel_cands > 64 || c.sel_cands > c.vocab))
+    return DFLASH_E_UNSUPPORTED;
   if ((int64_t)c.max_batch * (c.max_k + 1) > (1 << 20)) return DFLASH_E_UNSUPPORTED;
   // the bf16 GEMM addresses each operand with 32-bit byte offsets from a base
   const int64_t es = c.dtype == DFLASH_BF16 ? 2 : 4, lim = (int64_t)1 << 32;
@@ -213,9 +227,10 @@ int prepare_weights(dflash_handle* h) {
   if (c.dtype != DFLASH_BF16) {
     for (int l = 0; l < c.n_layers; ++l) {
       const dflash_layer_weights& L = h->layers[l];
-      h->mats[l] = {L.q_w, L.k_w, L.v_w, L.o_w, L.gate_w, L.up_w, L.down_w};
+      h->mats[l] = {L.q_w, L.k_w, L.v_w, L.o_w, L.gate_w, L.up_w, L.down_w, L.attn_conv_proj, L.mlp_conv_proj};
     }
     h->lm = h->lm_head;
+    h->sel_h = h->sel_hidden_src;
     return DFLASH_OK;
   }
   const int64_t H = c.hidden, qdim = (int64_t)c.n_q_heads * c.head_dim, kvdim = (int64_t)c.n_kv_heads * c.head_dim;
@@ -232,8 +247,14 @@ int prepare_weights(dflash_handle* h) {
     jobs.push_back({L.gate_w, F * H, &m.gate});
     jobs.push_back({L.up_w, F * H, &m.up});
     jobs.push_back({L.down_w, H * F, &m.down});
+    m.conv_a = m.conv_m = nullptr;
+    if (c.conv_group > 0) {
+      jobs.push_back({L.attn_conv_proj, 2 * H / c.conv_group * H, &m.conv_a});
+      jobs.push_back({L.mlp_conv_proj, 2 * H / c.conv_group * H, &m.conv_m});
+    }
   }
   jobs.push_back({h->lm_head, V * H, &h->lm});
+  if (c.sel_rank > 0) jobs.push_back({h->sel_hidden_src, (int64_t)c.sel_rank * H, &h->sel_h});
   uint32_t* d_max = nullptr;
   int rc = alloc_t(h, &d_max, 1, 4);
   if (rc) return rc;
@@ -291,7 +312,10 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if (!L.in_norm || !L.q_w || !L.k_w || !L.v_w || !L.o_w || !L.q_norm || !L.k_norm || !L.post_norm ||
         !L.gate_w || !L.up_w || !L.down_w)
       return DFLASH_E_INVALID;
+    if (c.conv_group > 0 && (!L.attn_conv_base || !L.attn_conv_proj || !L.mlp_conv_base || !L.mlp_conv_proj))
+      return DFLASH_E_INVALID;
   }
+  if (c.sel_rank > 0 && (!w->sel_pred || !w->sel_succ || !w->sel_hidden)) return DFLASH_E_INVALID;
   const int qrt_cap = 5;  // attention work-groups hold at most 5 tiles of 16 query rows
   const int splits = choose_attn_splits(c, qrt_cap);
   if (splits < 0) return DFLASH_E_UNSUPPORTED;
@@ -311,6 +335,11 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
   h->hidden_norm = w->hidden_norm;
   h->final_norm = w->final_norm;
   h->layers.assign(w->layers, w->layers + c.n_layers);
+  if (c.sel_rank > 0) {
+    h->sel_pred = w->sel_pred;
+    h->sel_succ = w->sel_succ;
+    h->sel_hidden_src = w->sel_hidden;
+  }
 
   const int H = c.hidden, d = c.head_dim, nkv = c.n_kv_heads, g = c.n_q_heads / nkv;
   const int qdim = c.n_q_heads * d, kvdim = nkv * d;
@@ -374,6 +403,20 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc_t(h, &h->row_lse, lrows, 4))) break;
     const int kc = std::max(1, std::min(c.max_tree, c.vocab));
     if ((rc = alloc_t(h, &h->tk_ids, lrows * kc, 4))) break;
+    if (c.conv_group > 0) {
+      if ((rc = alloc(h, &h->hbuf2, (size_t)h->maxM * H * es))) break;
+      if ((rc = alloc_t(h, &h->cbuf, (size_t)h->maxM * 2 * (H / c.conv_group), 4))) break;
+    }
+    if (c.sel_rank > 0) {
+      const size_t C = c.sel_cands;
+      if ((rc = alloc_t(h, &h->sel_gate, lrows * c.sel_rank, 4))) break;
+      if ((rc = alloc_t(h, &h->sel_cand, lrows * C, 4))) break;
+      if ((rc = alloc_t(h, &h->sel_cprob, lrows * C, 4))) break;
+      if ((rc = alloc_t(h, &h->sel_ids_ws, lrows * C, 4))) break;
+      if ((rc = alloc_t(h, &h->sel_probs_ws, lrows * C, 4))) break;
+      if ((rc = alloc_t(h, &h->sel_table, lrows * C * C, 4))) break;
+      if ((rc = alloc(h, &h->sel_hin, lrows * H * es))) break;
+    }
     if ((rc = alloc_t(h, &h->tk_probs, lrows * kc, 4))) break;
     if ((rc = alloc_t(h, &h->y, (size_t)h->inject_chunk * H, 4))) break;
     if ((rc = alloc(h, &h->g, (size_t)h->inject_chunk * H * es))) break;
@@ -565,6 +608,43 @@ int dflash_inject_tree_path(dflash_handle* h, void* stream, int32_t n_req, const
 
 namespace {
 
+// DFlash 2 [P2 §3.2.3]: hbuf2 = dynamic conv of the block rows in hbuf; the
+// per-row kernel corrections come from one product with the layer's proj.
+void conv_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj, const void* base, const void* gain) {
+  const dflash_config& c = h->cfg;
+  const int H = c.hidden, nc = 2 * (H / c.conv_group);
+  Phase ph(h, s, DFLASH_PH_CONV);
+  GemmArgs ga = gemm_a1(h->hbuf, H, M, nc, H);
+  ga.out_scale = h->out_scale;
+  set_b(ga, {{proj, nc}}, H);
+  EpiStore<float>::Params pc{h->cbuf, nc};
+  launch_gemm(h->op, EPI_STORE_F32, ga, &pc, plan_gemm(h->op, M, nc, H, h->num_cus), h->partials, h->partials_elems,
+              s);
+  launch_dyn_conv(c.dtype, M, R, H, c.conv_group, h->X, gain, c.rms_eps, h->cbuf, base, h->hbuf2, s);
+}
+
+// DFlash 2 path selector [P2 §3.1.2-3.1.3] over rows n_req*K whose logits and
+// final-normalised hidden rows (operand type, [rows, H]) are given; row
+// statistics (row_max / row_lse) must be current.
+void selector_stage(dflash_handle* h, hipStream_t s, int n_req, int K, const int32_t* slots, const int32_t* anchors,
+                    const float* logits, const void* hidden, float T, uint64_t seed, uint64_t step, int32_t* draft_ids,
+                    int32_t* cand_ids, float* cand_probs) {
+  const dflash_config& c = h->cfg;
+  const int rows = n_req * K, H = c.hidden, C = c.sel_cands, r = c.sel_rank;
+  Phase ph(h, s, DFLASH_PH_SELECTOR);
+  launch_topk(rows, c.vocab, C, logits, h->tmax, h->n_vtiles, h->lm_tile, T > 0.f ? 1.0f / T : 1.0f, h->row_max,
+              h->row_lse, h->sel_cand, h->sel_cprob, s);
+  GemmArgs ga = gemm_a1(hidden, H, rows, r, H);
+  ga.out_scale = h->out_scale;
+  set_b(ga, {{h->sel_h, r}}, H);
+  EpiStore<float>::Params pg{h->sel_gate, r};
+  launch_gemm(h->op, EPI_STORE_F32, ga, &pg, plan_gemm(h->op, rows, r, H, h->num_cus), h->partials,
+              h->partials_elems, s);
+  launch_sel_walk(c.dtype, n_req, K, C, r, c.vocab, slots, anchors, logits, h->sel_cand, h->sel_gate, h->sel_pred,
+                  h->sel_succ, T, seed, step, h->sel_table, draft_ids, cand_ids ? cand_ids : h->sel_ids_ws,
+                  cand_probs ? cand_probs : h->sel_probs_ws, h->err, s);
+}
+
 int validate_draft(dflash_handle* h, int n_req, const dflash_draft_params* p, const dflash_draft_outputs* o) {
   const dflash_config& c = h->cfg;
   if (!p || !o || n_req < 0) return DFLASH_E_INVALID;
@@ -651,9 +731,15 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& L = h->layers[l];
     const dflash_handle::Mats& W = h->mats[l];
+    // DFlash 2: dynamic convolution of the attention sub-layer's input
+    const void* attn_in = h->hbuf;
+    if (c.conv_group > 0) {
+      conv_stage(h, s, M, R, W.conv_a, L.attn_conv_base, L.in_norm);
+      attn_in = h->hbuf2;
+    }
     // q | k | v with head norm + RoPE into the attention layouts
     {
-      GemmArgs ga = gemm_a1(h->hbuf, H, M, qdim + 2 * kvdim, H);
+      GemmArgs ga = gemm_a1(attn_in, H, M, qdim + 2 * kvdim, H);
       ga.out_scale = h->out_scale;
       set_b(ga, {{W.q, qdim}, {W.k, kvdim}, {W.v, kvdim}}, H);
       EpiQKV<f16_t>::Params pq;
@@ -745,9 +831,15 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       Phase ph(h, s, DFLASH_PH_NORM);
       launch_rmsnorm(dt, M, H, h->X, 0, K, R, L.post_norm, h->hbuf, c.rms_eps, s);
     }
+    // DFlash 2: dynamic convolution of the MLP sub-layer's input
+    const void* mlp_in = h->hbuf;
+    if (c.conv_group > 0) {
+      conv_stage(h, s, M, R, W.conv_m, L.mlp_conv_base, L.post_norm);
+      mlp_in = h->hbuf2;
+    }
     // SwiGLU MLP
     {
-      GemmArgs ga = gemm_a1(h->hbuf, H, M, 2 * F, H);
+      GemmArgs ga = gemm_a1(mlp_in, H, M, 2 * F, H);
       ga.out_scale = h->out_scale;
       ga.b_ptr[0] = W.gate;
       ga.b_ptr[1] = W.up;
@@ -779,7 +871,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     launch_rmsnorm(dt, rows, H, h->X, 1, K, R, h->final_norm, h->hbuf, c.rms_eps, s);
   }
   const float T = p->temperature;
-  const bool need_logits = o->logits || T > 0.f || p->top_k > 0 || p->tree_budget > 0;
+  const bool need_logits = o->logits || T > 0.f || p->top_k > 0 || p->tree_budget > 0 || c.sel_rank > 0;
   float* logits = o->logits ? o->logits : (need_logits ? h->logits_ws : nullptr);
   {
     GemmArgs ga = gemm_a1(h->hbuf, H, rows, V, H);
@@ -801,6 +893,10 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     launch_gemm(h->op, EPI_LMHEAD, ga, &pl, gp, h->partials, h->partials_elems, s);
   }
   select_stage(h, s, n_req, slots, anchor_ids, logits, p, o);
+  if (c.sel_rank > 0)
+    selector_stage(h, s, n_req, K, slots, anchor_ids, logits, h->hbuf, T, p->seed, p->step, o->draft_ids, o->cand_ids,
+                   o->cand_probs);
+  if (o->hidden) launch_to_f32(c.dtype, (int64_t)rows * H, h->hbuf, o->hidden, s);
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
 
@@ -897,6 +993,63 @@ int dflash_verify_tree(dflash_handle* h, void* stream, int32_t n_req, int32_t K,
   Phase ph(h, s, DFLASH_PH_VERIFY);
   launch_verify_tree(n_req, n_nodes, K + 1, c.vocab, slots, tree_tokens, tree_parents, target_logits, temperature,
                      seed, step, out_tokens, out_len, accept_len, next_anchor, path_nodes, h->err, s);
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+int dflash_select_path(dflash_handle* h, void* stream, int32_t n_req, int32_t K, const int32_t* slots,
+                       const int32_t* anchor_ids, const float* logits, const float* hidden, float temperature,
+                       uint64_t seed, uint64_t step, int32_t* draft_ids, int32_t* cand_ids, float* cand_probs) {
+  if (!h || n_req < 0) return DFLASH_E_INVALID;
+  const dflash_config& c = h->cfg;
+  if (c.sel_rank <= 0) return DFLASH_E_INVALID;
+  if (n_req == 0) return DFLASH_OK;
+  if (n_req > c.max_batch || K < 1 || K > c.max_k) return DFLASH_E_CAPACITY;
+  if (!slots || !anchor_ids || !logits || !hidden || !draft_ids || !cand_ids || !cand_probs) return DFLASH_E_INVALID;
+  if (!(temperature >= 0.f)) return DFLASH_E_INVALID;
+  hipStream_t s = S(stream);
+  const int rows = n_req * K;
+  dflash_draft_params p{};
+  p.K = K;
+  p.temperature = temperature;
+  p.seed = seed;
+  p.step = step;
+  dflash_draft_outputs o{};
+  o.draft_ids = draft_ids;
+  {
+    Phase ph(h, s, DFLASH_PH_SELECT);
+    lm_stats_from_logits_kernel<<<dim3(h->n_vtiles, rows), 64, 0, s>>>(c.vocab, h->n_vtiles, h->lm_tile, logits,
+                                                                        temperature > 0.f ? 1.0f / temperature : 1.0f,
+                                                                        h->tmax, h->tsum, h->targ);
+  }
+  select_stage(h, s, n_req, slots, anchor_ids, logits, &p, &o);
+  launch_from_f32(c.dtype, (int64_t)rows * c.hidden, hidden, h->sel_hin, s);
+  selector_stage(h, s, n_req, K, slots, anchor_ids, logits, h->sel_hin, temperature, seed, step, draft_ids, cand_ids,
+                 cand_probs);
+  return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+}
+
+int dflash_verify_subset(dflash_handle* h, void* stream, int32_t n_req, int32_t K, int32_t C, const int32_t* slots,
+                         const int32_t* draft_ids, const int32_t* cand_ids, const float* cand_probs,
+                         const float* target_logits, float temperature, uint64_t seed, uint64_t step,
+                         int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor) {
+  if (!h || n_req < 0) return DFLASH_E_INVALID;
+  if (n_req == 0) return DFLASH_OK;
+  const dflash_config& c = h->cfg;
+  if (n_req > c.max_batch || K < 1 || K > c.max_k) return DFLASH_E_CAPACITY;
+  if (C < 1 || C > 64) return DFLASH_E_CAPACITY;
+  if (!draft_ids || !target_logits || !out_tokens || !out_len || !accept_len) return DFLASH_E_INVALID;
+  if (!(temperature >= 0.f)) return DFLASH_E_INVALID;
+  hipStream_t s = S(stream);
+  Phase ph(h, s, DFLASH_PH_VERIFY);
+  if (temperature == 0.f) {
+    launch_verify_greedy(n_req, K, c.vocab, draft_ids, target_logits, h->post, out_tokens, out_len, accept_len,
+                         next_anchor, s);
+  } else {
+    if (!slots || !cand_ids || !cand_probs) return DFLASH_E_INVALID;
+    launch_verify_subset(n_req, K, C, c.vocab, slots, draft_ids, cand_ids, cand_probs, target_logits,
+                         1.0f / temperature, seed, step, h->vstats, out_tokens, out_len, accept_len, next_anchor,
+                         h->err, s);
+  }
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
 

@@ -362,6 +362,7 @@ __device__ __forceinline__ uint64_t ckey(float f, int idx) {
 }
 
 static constexpr int TOPK_CAP = 4096;
+static constexpr int TOPK_TILE_CAP = 512;   // listed candidate tiles (more: scan all tiles)
 
 // k-th largest (1-based) composite key among n items provided by get(i).
 template <class Get>
@@ -415,10 +416,22 @@ __global__ __launch_bounds__(256) void topk_kernel(int V, int k, const float* lo
     const uint64_t tkey = radix_kth(n_tiles, kk, [&](int i) { return ckey(tm[i], i); }, hist, &sh_prefix, &sh_k);
     thr = (uint32_t)(tkey >> 32);
   }
-  if (threadIdx.x == 0) s_n = 0;
+  // tiles whose maximum reaches the threshold, listed in parallel (ascending order is not needed:
+  // the selection below is by key), then their elements scanned one tile per pass
+  __shared__ int tiles[TOPK_TILE_CAP];
+  __shared__ int s_nt;
+  if (threadIdx.x == 0) { s_n = 0; s_nt = 0; }
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    if (f2key(tm[t]) < thr) continue;
+  for (int t = threadIdx.x; t < n_tiles; t += 256)
+    if (f2key(tm[t]) >= thr) {
+      const int q = atomicAdd(&s_nt, 1);
+      if (q < TOPK_TILE_CAP) tiles[q] = t;
+    }
+  __syncthreads();
+  const int nt = s_nt;
+  for (int q = 0; q < (nt <= TOPK_TILE_CAP ? nt : n_tiles); ++q) {
+    const int t = nt <= TOPK_TILE_CAP ? tiles[q] : q;
+    if (nt > TOPK_TILE_CAP && f2key(tm[t]) < thr) continue;
     const int c = t * tile_w + threadIdx.x;
     if ((int)threadIdx.x < tile_w && c < V) {
       const float v = z[c] * inv_temp;
@@ -472,6 +485,82 @@ __global__ __launch_bounds__(256) void topk_kernel(int V, int k, const float* lo
   }
   const float M = row_max[m], L = row_lse[m];
   for (int i = threadIdx.x; i < kk; i += 256) {
+    const int id = (int)(0xFFFFFFFFu - (uint32_t)(sel[i] & 0xFFFFFFFFull));
+    ids_out[(int64_t)m * k + i] = id;
+    probs_out[(int64_t)m * k + i] = expf(z[id] * inv_temp - M - L);
+  }
+}
+
+// Small k (<= 64): k rounds of a block-wide maximum, each over the keys below
+// the previous round's -- first over the tile maxima (the k-th largest tile
+// maximum bounds the k-th largest logit from below), then over the logits of
+// the tiles whose maximum reaches it.  Same keys, order and probabilities as
+// topk_kernel; no sort and no serial histogram scans.
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    v = y > v ? y : v;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  uint64_t m = sh[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = sh[i] > m ? sh[i] : m;
+  return m;
+}
+
+constexpr int TOPK_SMALL_K = 64, TOPK_SMALL_TILES = 2048;
+
+__global__ __launch_bounds__(256) void topk_small_kernel(int V, int k, const float* logits, const float* tmax,
+                                                          int n_tiles, int tile_w, float inv_temp,
+                                                          const float* row_max, const float* row_lse,
+                                                          int32_t* ids_out, float* probs_out) {
+  __shared__ uint64_t red[4];
+  __shared__ int tiles[TOPK_SMALL_TILES];
+  __shared__ int s_nt;
+  __shared__ uint64_t sel[TOPK_SMALL_K];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float* z = logits + (int64_t)m * V;
+  const float* tm = tmax + (int64_t)m * n_tiles;
+  const int kk = min(k, V);
+  // the kk-th largest tile maximum (all tiles when there are no more than kk)
+  uint32_t thr = 0;
+  if (kk < n_tiles) {
+    uint64_t prev = ~0ull;
+    for (int i = 0; i < kk; ++i) {
+      uint64_t best = 0;
+      for (int t = tid; t < n_tiles; t += 256) {
+        const uint64_t key = ckey(tm[t], t);
+        if (key < prev && key > best) best = key;
+      }
+      prev = block_max_u64(best, red);
+    }
+    thr = (uint32_t)(prev >> 32);
+  }
+  if (tid == 0) s_nt = 0;
+  __syncthreads();
+  for (int t = tid; t < n_tiles; t += 256)
+    if (f2key(tm[t]) >= thr) tiles[atomicAdd(&s_nt, 1)] = t;
+  __syncthreads();
+  const int ne = s_nt * tile_w;
+  uint64_t prev = ~0ull;
+  for (int i = 0; i < kk; ++i) {
+    uint64_t best = 0;
+    for (int e = tid; e < ne; e += 256) {
+      const int c = tiles[e / tile_w] * tile_w + e % tile_w;
+      if (c < V) {
+        const uint64_t key = ckey(z[c] * inv_temp, c);
+        if (key < prev && key > best) best = key;
+      }
+    }
+    prev = block_max_u64(best, red);
+    if (tid == 0) sel[i] = prev;
+  }
+  __syncthreads();
+  const float M = row_max[m], L = row_lse[m];
+  for (int i = tid; i < kk; i += 256) {
     const int id = (int)(0xFFFFFFFFu - (uint32_t)(sel[i] & 0xFFFFFFFFull));
     ids_out[(int64_t)m * k + i] = id;
     probs_out[(int64_t)m * k + i] = expf(z[id] * inv_temp - M - L);
@@ -673,13 +762,14 @@ __global__ void greedy_finish_kernel(int n_req, int K, const int32_t* draft_ids,
   if (next_anchor) next_anchor[r] = p[a];
 }
 
-// per row: (max of z/T, sum exp(z/T - max)); stats row q of request r = q / (2K+1):
-// j = q % (2K+1) <= K is target row j, otherwise draft row j - K - 1.
-__global__ __launch_bounds__(256) void softmax_stats_kernel(int K, int V, const float* target, const float* draft,
-                                                             float inv_temp, float* stats) {
+// per row: (max of z/T, sum exp(z/T - max)); stats row q of request r = q / nrow
+// (nrow = 2K+1, or K+1 for target rows only): j = q % nrow <= K is target row j,
+// otherwise draft row j - K - 1.
+__global__ __launch_bounds__(256) void softmax_stats_kernel(int K, int nrow, int V, const float* target,
+                                                             const float* draft, float inv_temp, float* stats) {
   __shared__ float red[4];
   const int64_t m = blockIdx.x;
-  const int64_t r = m / (2 * K + 1), j = m % (2 * K + 1);
+  const int64_t r = m / nrow, j = m % nrow;
   const float* row = j <= K ? target + (r * (K + 1) + j) * V : draft + (r * K + (j - K - 1)) * V;
   float mx = -INFINITY;
   for (int c = threadIdx.x; c < V; c += 256) mx = fmaxf(mx, row[c] * inv_temp);
@@ -797,6 +887,324 @@ __global__ __launch_bounds__(256) void rejection_kernel(int K, int V, const int3
     out_len[r] = a + 1;
     accept_len[r] = a;
     if (next_anchor) next_anchor[r] = pick;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Subset-q rejection [P2 §3.1.3, §4.2]: the draft at position i carries C
+// candidate ids with a distribution over them (the DFlash 2 selector's);
+// q_full(v) = the summed probability of the candidates with id v (0 outside).
+// Accept d_i iff u * q_full(d_i) < p_{i-1}(d_i); at the first rejection draw
+// from max(0, p - q_full) (p alone when that mass is below RESIDUAL_EPS), after
+// K acceptances the bonus from p_K.  The residual equals p away from the
+// candidates, so each thread sums p over its id range and corrects the few
+// candidates inside it, found in an id-sorted copy of the candidate list.
+// ---------------------------------------------------------------------------
+constexpr int SUBSET_MAX_C = 64;
+
+__global__ __launch_bounds__(256) void rejection_subset_kernel(int K, int C, int V, const int32_t* slots,
+                                                                const int32_t* draft_ids, const int32_t* cand_ids,
+                                                                const float* cand_probs, const float* target,
+                                                                float inv_temp, uint64_t seed, uint64_t step,
+                                                                const float* stats, int32_t* out_tokens,
+                                                                int32_t* out_len, int32_t* accept_len,
+                                                                int32_t* next_anchor, int32_t* err) {
+  __shared__ float sh[8];
+  __shared__ int s_a, s_nc, s_thread, s_pick;
+  __shared__ float s_total;
+  __shared__ int sc_id[SUBSET_MAX_C];
+  __shared__ float sc_q[SUBSET_MAX_C];
+  const int r = blockIdx.x;
+  const uint32_t slot = (uint32_t)slots[r];
+  const float* T0 = target + (int64_t)r * (K + 1) * V;
+  const float* ts = stats + (int64_t)r * (K + 1) * 2;
+  const int32_t* d = draft_ids + (int64_t)r * K;
+  if (threadIdx.x == 0) {
+    int a = 0;
+    for (; a < K; ++a) {
+      const int tok = d[a];
+      if (tok < 0 || tok >= V) {   // not a token: reject here (and flag it)
+        raise_error(err, ERR_BAD_TOKEN);
+        break;
+      }
+      const float p = expf(T0[(int64_t)a * V + tok] * inv_temp - ts[2 * a]) / ts[2 * a + 1];
+      float q = 0.f;
+      for (int j = 0; j < C; ++j)
+        if (cand_ids[((int64_t)r * K + a) * C + j] == tok) q += cand_probs[((int64_t)r * K + a) * C + j];
+      const float u = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_ACCEPT);
+      if (!(u * q < p)) break;
+    }
+    s_a = a;
+    // candidates of the rejected position, sorted by id, equal ids merged
+    int n = 0;
+    if (a < K) {
+      for (int j = 0; j < C; ++j) {
+        const int id = cand_ids[((int64_t)r * K + a) * C + j];
+        const float q = cand_probs[((int64_t)r * K + a) * C + j];
+        if (id < 0 || id >= V) continue;
+        int pos = n;
+        while (pos > 0 && sc_id[pos - 1] > id) {
+          sc_id[pos] = sc_id[pos - 1];
+          sc_q[pos] = sc_q[pos - 1];
+          --pos;
+        }
+        if (pos > 0 && sc_id[pos - 1] == id) {   // merge (shift back what was moved)
+          sc_q[pos - 1] += q;
+          for (int k = pos; k < n; ++k) {
+            sc_id[k] = sc_id[k + 1];
+            sc_q[k] = sc_q[k + 1];
+          }
+          continue;
+        }
+        sc_id[pos] = id;
+        sc_q[pos] = q;
+        ++n;
+      }
+    }
+    s_nc = n;
+  }
+  __syncthreads();
+  const int a = s_a, nc = s_nc;
+  const bool bonus = a == K;
+  const float* t = T0 + (int64_t)a * V;
+  const float pm = ts[2 * a], ps = ts[2 * a + 1];
+  const int per = (V + 255) / 256;
+  const int c0 = threadIdx.x * per, c1 = min(V, c0 + per);
+  // first candidate at or after c0
+  int first = 0;
+  while (first < nc && sc_id[first] < c0) ++first;
+  auto pw = [&](int c) { return expf(t[c] * inv_temp - pm) / ps; };
+  // weight of id c given the candidate cursor k (advanced past ids below c)
+  auto weight = [&](int c, int& k, bool resid) -> float {
+    const float p = pw(c);
+    if (!resid) return p;
+    while (k < nc && sc_id[k] < c) ++k;
+    return (k < nc && sc_id[k] == c) ? fmaxf(p - sc_q[k], 0.f) : p;
+  };
+  bool use_resid = !bonus;
+  float w = 0.f;
+  if (use_resid) {
+    int k = first;
+    for (int c = c0; c < c1; ++c) w += weight(c, k, true);
+    const float tot = block_incl_scan(w, sh);
+    if (threadIdx.x == 255) s_total = tot;
+    __syncthreads();
+    if (s_total < RESIDUAL_EPS) use_resid = false;   // exhausted / underflowed: draw from p
+    __syncthreads();
+  }
+  if (!use_resid) {
+    w = 0.f;
+    for (int c = c0; c < c1; ++c) w += pw(c);
+  }
+  const float incl = block_incl_scan(w, sh);
+  if (threadIdx.x == 255) s_total = incl;
+  if (threadIdx.x == 0) { s_thread = -1; s_pick = -1; }
+  __syncthreads();
+  const float u2 = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_RESAMPLE);
+  const float target_mass = u2 * s_total;
+  const float excl = incl - w;
+  if (excl <= target_mass && target_mass < incl) s_thread = threadIdx.x;
+  __syncthreads();
+  if ((int)threadIdx.x == s_thread) {
+    float acc = excl;
+    int k = first;
+    for (int c = c0; c < c1; ++c) {
+      const float wc = weight(c, k, use_resid);
+      if (wc > 0.f && target_mass < acc + wc) { s_pick = c; break; }
+      acc += wc;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int pick = s_pick;
+    if (pick < 0) {   // rounding: the last id with weight
+      int k = 0;
+      for (int c = 0; c < V; ++c)
+        if (weight(c, k, use_resid) > 0.f) pick = c;
+      if (pick < 0) pick = 0;
+    }
+    int32_t* o = out_tokens + (int64_t)r * (K + 1);
+    for (int i = 0; i < a; ++i) o[i] = d[i];
+    o[a] = pick;
+    for (int i = a + 1; i <= K; ++i) o[i] = -1;
+    out_len[r] = a + 1;
+    accept_len[r] = a;
+    if (next_anchor) next_anchor[r] = pick;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// DFlash 2 dynamic convolution [P2 §3.2.3]: y_t = k_{t,0} x_t + k_{t,1} x_{t-1}
+// over the R rows of each request's block (x_{-1} = 0), per channel c with
+// k_{t,j}[c] = base_j[c] + corr[t][j * H/G + c/G]; corr = x . proj^T comes from
+// the GEMM before (on the operand-type copy of x).  x is the sub-layer's RMSNorm
+// of the fp32 residual X, recomputed here in fp32 for rows t and t-1 so that y
+// is rounded to the operand type once.  One work-group per row.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void dyn_conv_kernel(int M, int R, int H, int G, const float* X,
+                                                        const typename WeightOf<T>::type* gain, float eps,
+                                                        const float* corr, const typename WeightOf<T>::type* base,
+                                                        T* y) {
+  // one wave per row, four rows per work-group (as the RMSNorm kernel)
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (m >= M) return;
+  const bool first = m % R == 0;
+  const int ng = H / G;
+  const float* xr = X + (int64_t)m * H;
+  const float* xp = xr - H;
+  float ss = 0.f, sp = 0.f;
+  // unrolled so that several rows' loads are in flight per wave (one wave per row is latency-bound)
+#pragma unroll 8
+  for (int c = lane * 4; c < H; c += 256) {
+    const float4 v = load4f(xr + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    if (!first) {
+      const float4 u = load4f(xp + c);
+      sp += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
+    }
+  }
+  const float rs = rsqrtf(wave_sum(ss) / (float)H + eps);
+  const float rp = first ? 0.f : rsqrtf(wave_sum(sp) / (float)H + eps);
+  const float* cr = corr + (int64_t)m * 2 * ng;
+#pragma unroll 4
+  for (int c = lane * 4; c < H; c += 256) {   // G is a multiple of 4: the four channels share a group
+    const float4 v = load4f(xr + c), g = load4f(gain + c), b0 = load4f(base + c), b1 = load4f(base + H + c);
+    const float4 u = first ? make_float4(0.f, 0.f, 0.f, 0.f) : load4f(xp + c);
+    const float c0 = cr[c / G], c1 = cr[ng + c / G];
+    store4(y + (int64_t)m * H + c, (b0.x + c0) * v.x * rs * g.x + (b1.x + c1) * u.x * rp * g.x,
+           (b0.y + c0) * v.y * rs * g.y + (b1.y + c1) * u.y * rp * g.y,
+           (b0.z + c0) * v.z * rs * g.z + (b1.z + c1) * u.z * rp * g.z,
+           (b0.w + c0) * v.w * rs * g.w + (b1.w + c1) * u.w * rp * g.w);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// DFlash 2 path selector [P2 §3.1.2-3.1.3].  Candidates of mask position t are
+// the top-C ids of its logits (top-k order); candidate b following predecessor a
+// scores S_t(a, b) = z_t(b) + sum_i A[a][i] * gate_t[i] * B[b][i], gate = H(h_t).
+// As the pages lay it out, every pair score is computed first, in parallel, into
+// a table -- predecessors of position 0: the anchor; of position t >= 1: the C
+// candidates of t-1 -- and only the walk over the table is sequential.
+// ---------------------------------------------------------------------------
+constexpr int SEL_RC = 120;   // rank chunk staged in LDS per pass (C = 64: 2 x 64 x 121 x 4 B < 64 KB)
+constexpr int SEL_LD = SEL_RC + 1;   // padded row stride: the C successor rows fall in distinct banks
+
+// table[r][t][i][j] = S_t(pred_i, cand_tj); grid (K, n_req), 256 threads.
+template <typename W>
+__global__ __launch_bounds__(256) void sel_table_kernel(int K, int C, int rank, int V, const int32_t* anchors,
+                                                         const float* logits, const int32_t* cand, const float* gate,
+                                                         const W* A, const W* B, float* table, int32_t* err) {
+  extern __shared__ float st_lds[];          // [C][SEL_LD] gated predecessor codes, [C][SEL_LD] successor codes
+  float* ap = st_lds;
+  float* bs = st_lds + C * SEL_LD;
+  const int t = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int64_t row = (int64_t)r * K + t;
+  const int np = t == 0 ? 1 : C;             // predecessors
+  const int pairs = np * C;
+  constexpr int PPT = 16;                    // pairs per thread (C <= 64 -> at most 4096 pairs)
+  float acc[PPT];
+#pragma unroll
+  for (int q = 0; q < PPT; ++q) acc[q] = 0.f;
+  for (int k0 = 0; k0 < rank; k0 += SEL_RC) {
+    const int kn = min(SEL_RC, rank - k0);
+    __syncthreads();
+    for (int e = tid; e < np * SEL_RC; e += 256) {
+      const int i = e / SEL_RC, k = e % SEL_RC;
+      float v = 0.f;
+      if (k < kn) {
+        int a;
+        if (t == 0) {
+          a = anchors[r];
+          if (a < 0 || a >= V) a = 0;
+        } else {
+          a = cand[(row - 1) * C + i];
+        }
+        v = to_f32(A[(int64_t)a * rank + k0 + k]) * gate[row * rank + k0 + k];
+      }
+      ap[i * SEL_LD + k] = v;
+    }
+    for (int e = tid; e < C * SEL_RC; e += 256) {
+      const int j = e / SEL_RC, k = e % SEL_RC;
+      bs[j * SEL_LD + k] = k < kn ? to_f32(B[(int64_t)cand[row * C + j] * rank + k0 + k]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      const int pidx = tid + q * 256;
+      if (pidx < pairs) {
+        const float* x = ap + (pidx / C) * SEL_LD;
+        const float* y = bs + (pidx % C) * SEL_LD;
+        float sum = 0.f;
+        for (int k = 0; k < kn; ++k) sum += x[k] * y[k];
+        acc[q] += sum;
+      }
+    }
+  }
+  if (t == 0 && tid == 0 && (anchors[r] < 0 || anchors[r] >= V)) raise_error(err, ERR_BAD_TOKEN);
+#pragma unroll
+  for (int q = 0; q < PPT; ++q) {
+    const int pidx = tid + q * 256;
+    if (pidx < pairs) {
+      const int j = pidx % C;
+      table[(row * C + pidx / C) * C + j] = logits[row * V + cand[row * C + j]] + acc[q];
+    }
+  }
+}
+
+// The walk over the table, one wave per request, lane j <-> candidate j.  Greedy:
+// the highest score, lowest id on ties.  T > 0: softmax(S / T) over the
+// candidates and an inverse-CDF draw in candidate order with u = Philox(seed;
+// t+1, slot, step, 0); neighbouring lanes' prefix ranges share end points exactly.
+__global__ __launch_bounds__(64) void sel_walk_kernel(int K, int C, const int32_t* slots, const int32_t* cand,
+                                                       const float* table, float inv_temp, uint64_t seed,
+                                                       uint64_t step, int32_t* draft_ids, int32_t* cand_out,
+                                                       float* probs_out) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const bool on = lane < C;
+  int pidx = 0;                              // index of the predecessor among its candidates (anchor: 0)
+  for (int t = 0; t < K; ++t) {
+    const int64_t row = (int64_t)r * K + t;
+    const int id = on ? cand[row * C + lane] : 0x7fffffff;
+    const float sc = on ? table[(row * C + pidx) * C + lane] : -INFINITY;
+    int pick;
+    float pr;
+    if (inv_temp == 0.f) {
+      const float mx = wave_max(sc);
+      int best = (on && sc == mx) ? id : 0x7fffffff;
+      for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o, 64));
+      const unsigned long long hit = __ballot(on && id == best);
+      pick = hit ? __ffsll((long long)hit) - 1 : 0;
+      pr = lane == pick ? 1.f : 0.f;
+    } else {
+      const float mx = wave_max(sc);
+      const float e = on ? expf((sc - mx) * inv_temp) : 0.f;
+      float incl = e;
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      float excl = __shfl_up(incl, 1, 64);
+      if (lane == 0) excl = 0.f;
+      const float tot = __shfl(incl, 63, 64);
+      const float u = philox_uniform(seed, (uint32_t)slots[r], step, (uint32_t)(t + 1), PURPOSE_DRAFT);
+      const float tm = u * tot;
+      const unsigned long long hit = __ballot(on && e > 0.f && excl <= tm && tm < incl);
+      if (hit) {
+        pick = __ffsll((long long)hit) - 1;
+      } else {   // rounding put u * S on the total: the last candidate with weight
+        const unsigned long long nz = __ballot(on && e > 0.f);
+        pick = nz ? 63 - __clzll((long long)nz) : 0;
+      }
+      pr = e / tot;
+    }
+    if (on) {
+      probs_out[row * C + lane] = pr;
+      cand_out[row * C + lane] = id;
+    }
+    const int tok = __shfl(id, pick, 64);
+    if (lane == 0) draft_ids[row] = tok;
+    pidx = pick;
   }
 }
 
@@ -1166,8 +1574,12 @@ void launch_sample(int n_rows, int K, const int32_t* slots, uint64_t seed, uint6
 void launch_topk(int n_rows, int V, int k, const float* logits, const float* tmax, int n_tiles, int tile_w,
                  float inv_temp, const float* row_max, const float* row_lse, int32_t* ids_out, float* probs_out,
                  hipStream_t s) {
-  topk_kernel<<<n_rows, 256, 0, s>>>(V, k, logits, tmax, n_tiles, tile_w, inv_temp, row_max, row_lse, ids_out,
-                                      probs_out);
+  if (k <= TOPK_SMALL_K && n_tiles <= TOPK_SMALL_TILES)
+    topk_small_kernel<<<n_rows, 256, 0, s>>>(V, k, logits, tmax, n_tiles, tile_w, inv_temp, row_max, row_lse,
+                                              ids_out, probs_out);
+  else
+    topk_kernel<<<n_rows, 256, 0, s>>>(V, k, logits, tmax, n_tiles, tile_w, inv_temp, row_max, row_lse, ids_out,
+                                        probs_out);
 }
 
 void launch_tree(int n_req, int L, int Kc, int stride, int B, const float* probs, const int32_t* ids,
@@ -1207,9 +1619,70 @@ void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, cons
                              uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
                              int32_t* next_anchor, int32_t* err, hipStream_t s) {
   // stats rows per request: K+1 target rows then K draft rows
-  softmax_stats_kernel<<<n_req * (2 * K + 1), 256, 0, s>>>(K, V, target, draft_logits, inv_temp, stats);
+  softmax_stats_kernel<<<n_req * (2 * K + 1), 256, 0, s>>>(K, 2 * K + 1, V, target, draft_logits, inv_temp, stats);
   rejection_kernel<<<n_req, 256, 0, s>>>(K, V, slots, draft_ids, draft_logits, target, inv_temp, seed, step, stats,
                                           out_tokens, out_len, accept_len, next_anchor, err);
+}
+
+void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, const int32_t* draft_ids,
+                          const int32_t* cand_ids, const float* cand_probs, const float* target, float inv_temp,
+                          uint64_t seed, uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len,
+                          int32_t* accept_len, int32_t* next_anchor, int32_t* err, hipStream_t s) {
+  softmax_stats_kernel<<<n_req * (K + 1), 256, 0, s>>>(K, K + 1, V, target, nullptr, inv_temp, stats);
+  rejection_subset_kernel<<<n_req, 256, 0, s>>>(K, C, V, slots, draft_ids, cand_ids, cand_probs, target, inv_temp,
+                                                 seed, step, stats, out_tokens, out_len, accept_len, next_anchor,
+                                                 err);
+}
+
+void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const void* gain, float eps,
+                     const float* corr, const void* base, void* y, hipStream_t s) {
+  if (dtype == DT_BF16)
+    dyn_conv_kernel<f16_t><<<cdiv(M, 4), 256, 0, s>>>(M, R, H, G, X, (const bf16_t*)gain, eps, corr,
+                                                       (const bf16_t*)base, (f16_t*)y);
+  else
+    dyn_conv_kernel<float><<<cdiv(M, 4), 256, 0, s>>>(M, R, H, G, X, (const float*)gain, eps, corr,
+                                                       (const float*)base, (float*)y);
+}
+
+void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const int32_t* slots,
+                     const int32_t* anchors, const float* logits, const int32_t* cand, const float* gate,
+                     const void* A, const void* B, float temperature, uint64_t seed, uint64_t step, float* table,
+                     int32_t* draft_ids, int32_t* cand_out, float* probs_out, int32_t* err, hipStream_t s) {
+  const size_t lds = (size_t)2 * C * SEL_LD * sizeof(float);
+  const dim3 grid(K, n_req);
+  if (dtype == DT_BF16)
+    sel_table_kernel<bf16_t><<<grid, 256, lds, s>>>(K, C, rank, V, anchors, logits, cand, gate, (const bf16_t*)A,
+                                                    (const bf16_t*)B, table, err);
+  else
+    sel_table_kernel<float><<<grid, 256, lds, s>>>(K, C, rank, V, anchors, logits, cand, gate, (const float*)A,
+                                                   (const float*)B, table, err);
+  sel_walk_kernel<<<n_req, 64, 0, s>>>(K, C, slots, cand, table, temperature > 0.f ? 1.0f / temperature : 0.f, seed,
+                                       step, draft_ids, cand_out, probs_out);
+}
+
+template <typename T>
+__global__ void to_f32_kernel(int64_t n, const T* src, float* dst) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = to_f32(src[i]);
+}
+template <typename T>
+__global__ void from_f32_kernel(int64_t n, const float* src, T* dst) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = from_f32<T>(src[i]);
+}
+
+void launch_to_f32(int dtype, int64_t n, const void* src, float* dst, hipStream_t s) {
+  const int grid = (int)std::min<int64_t>(4096, (n + 255) / 256);
+  if (n <= 0) return;
+  if (dtype == DT_BF16) to_f32_kernel<f16_t><<<grid, 256, 0, s>>>(n, (const f16_t*)src, dst);
+  else to_f32_kernel<float><<<grid, 256, 0, s>>>(n, (const float*)src, dst);
+}
+
+void launch_from_f32(int dtype, int64_t n, const float* src, void* dst, hipStream_t s) {
+  const int grid = (int)std::min<int64_t>(4096, (n + 255) / 256);
+  if (n <= 0) return;
+  if (dtype == DT_BF16) from_f32_kernel<f16_t><<<grid, 256, 0, s>>>(n, src, (f16_t*)dst);
+  else from_f32_kernel<float><<<grid, 256, 0, s>>>(n, src, (float*)dst);
 }
 
 __global__ void sanitize_slots_kernel(int n, const int32_t* in, int32_t* out, int max_batch, int32_t* err) {

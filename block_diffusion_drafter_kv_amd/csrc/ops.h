@@ -81,6 +81,25 @@ void launch_verify_tree(int n_req, int n_nodes, int max_out, int V, const int32_
                         int32_t* path_out, int32_t* err, hipStream_t s);
 // LDS segments (8 bytes each) the sampling tree walk keeps for a vocabulary of V ids.
 int tree_walk_segments(int V);
+// DFlash 2: rejection against candidate-subset draft distributions (C <= 64)
+void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, const int32_t* draft_ids,
+                          const int32_t* cand_ids, const float* cand_probs, const float* target, float inv_temp,
+                          uint64_t seed, uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len,
+                          int32_t* accept_len, int32_t* next_anchor, int32_t* err, hipStream_t s);
+// DFlash 2: y = dynamic two-tap conv of x = RMSNorm(X; gain) [M, H] (blocks of R rows) with kernel
+// corrections corr [M, 2H/G]
+void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const void* gain, float eps,
+                     const float* corr, const void* base, void* y, hipStream_t s);
+// DFlash 2: selector pair-score table (scratch [n_req*K, C, C]) and walk over cand [n_req*K, C] with
+// gate [n_req*K, rank] and codebooks A, B [V, rank]
+void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const int32_t* slots,
+                     const int32_t* anchors, const float* logits, const int32_t* cand, const float* gate,
+                     const void* A, const void* B, float temperature, uint64_t seed, uint64_t step, float* table,
+                     int32_t* draft_ids, int32_t* cand_out, float* probs_out, int32_t* err, hipStream_t s);
+// fp32 copy of n 16-bit (fp16) or fp32 values
+void launch_to_f32(int dtype, int64_t n, const void* src, float* dst, hipStream_t s);
+// n fp32 values rounded to the activation type (fp16 for a bf16 drafter)
+void launch_from_f32(int dtype, int64_t n, const float* src, void* dst, hipStream_t s);
 void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,
                              const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
                              uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,

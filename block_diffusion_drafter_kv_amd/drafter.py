@@ -14,9 +14,11 @@ from . import (DFLASH_BF16, DFLASH_F32, dflash_config, dflash_copy_cache, dflash
                dflash_destroy, dflash_draft_block, dflash_draft_outputs, dflash_draft_params, dflash_get_error,
                dflash_inject_context, dflash_layer_weights, dflash_profile, dflash_profile_read, dflash_reset_slots,
                dflash_select_from_logits, dflash_verify, dflash_verify_tree, dflash_inject_tree_path,
-               dflash_weights)
+               dflash_weights, dflash_select_path, dflash_verify_subset)
 
 _LAYER_KEYS = ("in_norm", "q_w", "k_w", "v_w", "o_w", "q_norm", "k_norm", "post_norm", "gate_w", "up_w", "down_w")
+_CONV_KEYS = ("attn_conv_base", "attn_conv_proj", "mlp_conv_base", "mlp_conv_proj")
+_SEL_KEYS = ("sel_pred", "sel_succ", "sel_hidden")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -49,10 +51,13 @@ class Drafter:
         cfg.logit_softcap = float(logit_softcap)
         cfg.max_batch, cfg.max_ctx, cfg.max_k = max_batch, max_ctx, max_k
         cfg.max_inject_rows, cfg.max_top_k, cfg.max_tree = max_inject_rows, max_top_k, max_tree
+        cfg.conv_group = int(getattr(model, "conv_group", 0))
+        cfg.sel_rank = int(getattr(model, "sel_rank", 0))
+        cfg.sel_cands = int(getattr(model, "sel_cands", 16)) if cfg.sel_rank else 0
         self.cfg = cfg
         layers = (dflash_layer_weights * model.n_layers)()
         for l, lw in enumerate(weights["layers"]):
-            for k in _LAYER_KEYS:
+            for k in _LAYER_KEYS + (_CONV_KEYS if cfg.conv_group else ()):
                 t = lw[k]
                 if not t.is_cuda or t.dtype != self.dtype or not t.is_contiguous():
                     raise ValueError(f"layer {l} weight {k}: need a contiguous {self.dtype} CUDA tensor")
@@ -63,6 +68,12 @@ class Drafter:
         w.hidden_norm, w.final_norm = _ptr(weights["hidden_norm"]), _ptr(weights["final_norm"])
         w.n_layers = model.n_layers
         w.layers = layers
+        if cfg.sel_rank:
+            for k in _SEL_KEYS:
+                t = weights[k]
+                if not t.is_cuda or t.dtype != self.dtype or not t.is_contiguous():
+                    raise ValueError(f"weight {k}: need a contiguous {self.dtype} CUDA tensor")
+                setattr(w, k, t.data_ptr())
         self._wstruct = w
         self.handle = dflash_create(cfg, w)
 
@@ -104,9 +115,15 @@ class Drafter:
         dflash_inject_context(self.handle, _stream(), slots.numel(), slots.data_ptr(), row_start.data_ptr(),
                               row_count.data_ptr(), int(rows_upper_bound), ptrs, stride)
 
-    def _outputs(self, n, K, top_k, tree_budget, logits, want_stats):
+    def _outputs(self, n, K, top_k, tree_budget, logits, want_stats, want_hidden=False):
         dev = torch.device("cuda")
         o = {"draft_ids": torch.empty((n, K), dtype=torch.int32, device=dev)}
+        if self.cfg.sel_rank:
+            C = self.cfg.sel_cands
+            o["cand_ids"] = torch.empty((n, K, C), dtype=torch.int32, device=dev)
+            o["cand_probs"] = torch.empty((n, K, C), dtype=torch.float32, device=dev)
+        if want_hidden:
+            o["hidden"] = torch.empty((n, K, self.model.hidden), dtype=torch.float32, device=dev)
         if top_k:
             o["topk_ids"] = torch.empty((n, K, top_k), dtype=torch.int32, device=dev)
             o["topk_probs"] = torch.empty((n, K, top_k), dtype=torch.float32, device=dev)
@@ -127,11 +144,11 @@ class Drafter:
         return o, s
 
     def draft(self, slots, anchors, K, temperature=0.0, seed=0, step=0, top_k=0, tree_budget=0,
-              want_logits=False, logits_out: Optional[torch.Tensor] = None, want_stats=True):
+              want_logits=False, logits_out: Optional[torch.Tensor] = None, want_stats=True, want_hidden=False):
         n = slots.numel()
         if want_logits and logits_out is None:
             logits_out = torch.empty((n, K, self.model.vocab), dtype=torch.float32, device="cuda")
-        o, s = self._outputs(n, K, top_k, tree_budget, logits_out, want_stats)
+        o, s = self._outputs(n, K, top_k, tree_budget, logits_out, want_stats, want_hidden)
         p = dflash_draft_params(K, float(temperature), seed, step, top_k, tree_budget)
         dflash_draft_block(self.handle, _stream(), n, slots.data_ptr(), anchors.data_ptr(), p, s)
         return o
@@ -156,6 +173,39 @@ class Drafter:
                       _ptr(draft_logits), target_logits.data_ptr(), float(temperature), seed, step,
                       out["out_tokens"].data_ptr(), out["out_len"].data_ptr(), out["accept_len"].data_ptr(),
                       _ptr(out.get("next_anchor")))
+        return out
+
+    def select_path(self, slots, anchors, logits, hidden, temperature=0.0, seed=0, step=0):
+        """DFlash 2 path selector alone (dflash_select_path) from fp32 logits [n, K, V] and hidden [n, K, H]."""
+        n, K, _ = logits.shape
+        for t in (logits, hidden):
+            if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError("logits / hidden must be contiguous fp32 CUDA tensors")
+        C = self.cfg.sel_cands
+        dev = torch.device("cuda")
+        o = {"draft_ids": torch.empty((n, K), dtype=torch.int32, device=dev),
+             "cand_ids": torch.empty((n, K, C), dtype=torch.int32, device=dev),
+             "cand_probs": torch.empty((n, K, C), dtype=torch.float32, device=dev)}
+        dflash_select_path(self.handle, _stream(), n, K, slots.data_ptr(), anchors.data_ptr(), logits.data_ptr(),
+                           hidden.data_ptr(), float(temperature), seed, step, o["draft_ids"].data_ptr(),
+                           o["cand_ids"].data_ptr(), o["cand_probs"].data_ptr())
+        return o
+
+    def verify_subset(self, slots, draft_ids, cand_ids, cand_probs, target_logits, temperature=0.0, seed=0, step=0,
+                      out=None):
+        """Rejection verification against candidate-subset draft distributions (dflash_verify_subset)."""
+        n, K = draft_ids.shape
+        C = cand_ids.shape[-1]
+        dev = torch.device("cuda")
+        if out is None:
+            out = {"out_tokens": torch.empty((n, K + 1), dtype=torch.int32, device=dev),
+                   "out_len": torch.empty((n,), dtype=torch.int32, device=dev),
+                   "accept_len": torch.empty((n,), dtype=torch.int32, device=dev),
+                   "next_anchor": torch.empty((n,), dtype=torch.int32, device=dev)}
+        dflash_verify_subset(self.handle, _stream(), n, K, C, _ptr(slots), draft_ids.data_ptr(), _ptr(cand_ids),
+                             _ptr(cand_probs), target_logits.data_ptr(), float(temperature), seed, step,
+                             out["out_tokens"].data_ptr(), out["out_len"].data_ptr(), out["accept_len"].data_ptr(),
+                             _ptr(out.get("next_anchor")))
         return out
 
     def verify_tree(self, slots, K, tree_tokens, tree_parents, target_logits, temperature=0.0, seed=0, step=0,

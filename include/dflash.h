@@ -94,6 +94,13 @@ typedef struct dflash_config {
   int32_t max_inject_rows;    /* largest rows_upper_bound accepted by dflash_inject_context       */
   int32_t max_top_k;          /* largest top_k of dflash_draft_block (0..256)                      */
   int32_t max_tree;           /* largest tree_budget (0..256)                                      */
+  /* DFlash 2 modules [P2 §3.1-3.2]; all zero = DFlash 1. */
+  int32_t conv_group;         /* > 0: each layer applies two-tap dynamic depthwise convolutions to its
+                                 attention and MLP sub-layer inputs; channels per kernel-correction
+                                 group (a multiple of 4 dividing hidden, 2*hidden/conv_group a multiple
+                                 of 8); 0 = off                                                        */
+  int32_t sel_rank;           /* > 0: path selector with codebooks of this rank (1..4096); 0 = off   */
+  int32_t sel_cands;          /* selector candidates per position (1..64, <= vocab) when sel_rank > 0 */
 } dflash_config;
 
 /* Per-layer weights, all [out_features, in_features] row-major, cfg.dtype.
@@ -112,6 +119,14 @@ typedef struct dflash_layer_weights {
   const void* gate_w;         /* [F, H]                                           */
   const void* up_w;           /* [F, H]                                           */
   const void* down_w;         /* [H, F]                                           */
+  /* DFlash 2 dynamic convolutions (read when cfg.conv_group > 0, else ignored) [P2 §3.2.3]:
+   * y_t = k_t0 * x_t + k_t1 * x_{t-1} over the block rows (x_{-1} = 0), with
+   * k_tj[c] = base[j][c] + (x_t . proj^T)[j * H/G + c/G].  attn_* acts on the
+   * RMS-normalised input of q/k/v, mlp_* on that of gate/up. */
+  const void* attn_conv_base; /* [2, H]        per-channel kernels of the two taps (current, previous) */
+  const void* attn_conv_proj; /* [2*H/G, H]    kernel corrections: rows [0,H/G) tap 0, [H/G,2H/G) tap 1 */
+  const void* mlp_conv_base;  /* [2, H]                                           */
+  const void* mlp_conv_proj;  /* [2*H/G, H]                                       */
 } dflash_layer_weights;
 
 typedef struct dflash_weights {
@@ -122,6 +137,11 @@ typedef struct dflash_weights {
   const void* final_norm;     /* [H] RMSNorm gain before the LM head              */
   int32_t n_layers;           /* must equal cfg.n_layers                          */
   const dflash_layer_weights* layers; /* host array [n_layers] of device pointers */
+  /* DFlash 2 path selector (read when cfg.sel_rank > 0) [P2 §3.1.2]:
+   * S_t(a, b) = z_t(b) + <A(a) * (W_H h_t), B(b)>. */
+  const void* sel_pred;       /* [V, rank] predecessor codebook A                 */
+  const void* sel_succ;       /* [V, rank] successor codebook B                   */
+  const void* sel_hidden;     /* [rank, H] W_H, applied to the final-normalised hidden state */
 } dflash_weights;
 
 typedef struct dflash_handle dflash_handle;
@@ -178,6 +198,10 @@ typedef struct dflash_draft_outputs {
   int32_t* tree_parents;      /* [n_req, B+1] parent node index (-1 for the root / unused)       */
   int32_t* tree_depth;        /* [n_req, B+1] depth (root 0; -1 unused)                           */
   uint64_t* tree_mask;        /* [n_req, B+1, ceil((B+1)/64)] bit j of row i: i may attend to j  */
+  /* selector (cfg.sel_rank > 0): the walk's candidates and its distribution over them */
+  int32_t* cand_ids;          /* [n_req, K, sel_cands] or NULL: top-sel_cands ids (logit desc, id asc) */
+  float* cand_probs;          /* [n_req, K, sel_cands] or NULL: softmax(S/T) (one-hot when T = 0)       */
+  float* hidden;              /* [n_req, K, H] or NULL: final-normalised hidden rows of the masks (fp32) */
 } dflash_draft_outputs;
 /* T' = temperature if > 0, else 1.  A tree needs top_k >= min(B, V). */
 
@@ -194,11 +218,29 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
                        const int32_t* anchor_ids, const dflash_draft_params* params,
                        const dflash_draft_outputs* out);
 
+/* With cfg.sel_rank > 0, dflash_draft_block's draft tokens come from the DFlash 2
+ * path selector [P2 §3.1.2-3.1.3]: per mask position t (0-based) the top
+ * sel_cands ids of the logits are the candidates, scored S_t(a, b) = z_t(b) +
+ * <A(a) * (W_H h_t), B(b)> with a the anchor (t = 0) or the token picked at t-1
+ * and h_t the final-normalised hidden row; temperature 0 picks the best score
+ * (lowest id on ties), T > 0 draws from softmax(S/T) over the candidates by
+ * inverse CDF in candidate order with u = Philox(seed; t+1, slot, step, 0).
+ * cand_ids / cand_probs then feed dflash_verify_subset. */
+
 /* The selection stage of dflash_draft_block alone, from caller logits
  * [n_req, K, V] (device fp32): row statistics, top-k, draft tokens, tree. */
 int dflash_select_from_logits(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
                               const int32_t* anchor_ids, const float* logits,
                               const dflash_draft_params* params, const dflash_draft_outputs* out);
+
+/* The DFlash 2 path selector alone, from caller logits [n_req, K, V] and
+ * final-normalised hidden rows [n_req, K, H] (device fp32; a bf16 drafter rounds
+ * the hidden rows to fp16 before the W_H product): writes draft_ids [n_req, K],
+ * cand_ids and cand_probs [n_req, K, sel_cands].  Needs cfg.sel_rank > 0
+ * (else DFLASH_E_INVALID). */
+int dflash_select_path(dflash_handle* h, void* stream, int32_t n_req, int32_t K, const int32_t* slots,
+                       const int32_t* anchor_ids, const float* logits, const float* hidden, float temperature,
+                       uint64_t seed, uint64_t step, int32_t* draft_ids, int32_t* cand_ids, float* cand_probs);
 
 /* Verification of one drafted block per request [P2 §2.3, §4.2; P1 "验证"].
  * target_logits [n_req, K+1, V]: row j is the target's distribution after
@@ -216,6 +258,20 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
                   int32_t* accept_len, int32_t* next_anchor);
 /* next_anchor [n_req] (device, or NULL) receives out_tokens[r][out_len[r]-1]: the
  * token that anchors the next block [P4 §4.2; P1 "核心推理伪代码"]. */
+
+/* Rejection verification of a selector draft [P2 §3.1.3, §4.2]: the drafter's
+ * distribution at position i is given over C candidates (cand_ids / cand_probs
+ * [n_req, K, C], device; C <= 64), projected onto token ids (q_full(v) = summed
+ * probability of the candidates with id v, 0 elsewhere); accept d_i iff
+ * u * q_full(d_i) < p_{i-1}(d_i) with u = Philox(seed; i, slot, step, 1); at the
+ * first rejection draw from max(0, p - q_full) renormalised (from p when that
+ * mass is below 2^-20) with Philox(seed; i, slot, step, 2); after K acceptances
+ * the bonus from p_K.  temperature 0: the greedy prefix match of dflash_verify.
+ * Outputs as dflash_verify. */
+int dflash_verify_subset(dflash_handle* h, void* stream, int32_t n_req, int32_t K, int32_t C, const int32_t* slots,
+                         const int32_t* draft_ids, const int32_t* cand_ids, const float* cand_probs,
+                         const float* target_logits, float temperature, uint64_t seed, uint64_t step,
+                         int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor);
 
 /* Verifier walk down a draft tree [P5 §3.5 "验证流程(Verifier Walk)"] (one
  * tree per request, as dflash_draft_block builds it: node 0 = root / anchor,
@@ -287,6 +343,8 @@ enum dflash_phase {
   DFLASH_PH_SELECT,          /* row statistics, sampling, top-k, tree       */
   DFLASH_PH_VERIFY,          /* verification                                */
   DFLASH_PH_ATTN_PLAN,       /* context-chunk work list of the attention    */
+  DFLASH_PH_CONV,            /* DFlash 2 kernel-correction GEMMs + dynamic convolutions */
+  DFLASH_PH_SELECTOR,        /* DFlash 2 candidates, W_H product and walk   */
   DFLASH_PH_COUNT
 };
 int dflash_profile(dflash_handle* h, int32_t enable);

@@ -105,9 +105,14 @@ def weights(cfg: DrafterConfig, seed: int = 1234, gains: str = "ones",
     return w
 
 
-def dflash2_weights(cfg: DrafterConfig, seed: int = 4321, conv_base_std: float = 0.3, conv_proj_std: float = 0.02,
+def dflash2_weights(cfg: DrafterConfig, seed: int = 4321, conv_base_std: float = 0.3, conv_proj_std: float = 0.002,
                     codebook_std: float = 0.2, sel_hidden_std: float = 0.02) -> Dict[str, object]:
     """Weights of the DFlash 2 modules, in the model dtype, as CPU tensors.
+
+    The pages describe the convolution's kernel as a learned base plus a small
+    correction derived from the hidden state: the correction projection is drawn
+    at std 0.002, so that on unit-RMS rows at hidden 4096 a correction has std
+    about 0.13 against base taps around 1 and 0 (std 0.3).
 
     Per layer (when cfg.conv_group > 0): attn_conv_base / mlp_conv_base [2, H]
     (tap 0 drawn around 1, tap 1 around 0), attn_conv_proj / mlp_conv_proj

@@ -396,3 +396,72 @@ def _idle_weights(cfg):
           "gate_w": z(F, H), "up_w": z(F, H), "down_w": z(H, F)}
     w["layers"] = [lw] * cfg.n_layers
     return w
+
+
+def test_full_dflash2_qwen_shape(gpu_lib):
+    """DFlash 2 modules at the Qwen3-8B shape (5 layers, hidden 4096, V = 151936) with the pages'
+    selector sizes (16 candidates, rank 256) and conv group 16: one request's logits against the
+    oracle forward at ctx 1024, the selector walk (greedy and T = 1) against the oracle walk on the
+    GPU's own logits and hidden rows for a batch of 8, and subset-q verification at full vocabulary."""
+    from oracle import selector as osl
+    from synth.configs import QWEN3_8B_SHAPED, scaled_model
+    cfg = scaled_model(QWEN3_8B_SHAPED, conv_group=16, sel_rank=256, sel_cands=16)
+    B, K, C = 8, 16, cfg.sel_cands
+    w = gen.merge_weights(gen.weights(cfg, seed=1234), gen.dflash2_weights(cfg, seed=1235))
+    import block_diffusion_drafter_kv_amd as dk
+    dr = dk.Drafter(cfg, to_cuda(w), max_batch=B, max_ctx=2048, max_k=K, max_inject_rows=8192)
+    ctx = [1024, 300, 777, 64, 1500, 12, 900, 400]
+    rows = []
+    for r, c in enumerate(ctx):
+        x = gen.hidden_rows(cfg, r, 0, c)
+        rows.append(x)
+        dr.inject(_dev([r]), _dev([0]), _dev([c]), c, x.cuda().contiguous())
+    anchors = gen.anchor_ids(cfg, B, seed=21)
+    W_H = w["sel_hidden"].float().numpy().astype(np.float64)
+    A = w["sel_pred"].float().numpy().astype(np.float64)
+    Bc = w["sel_succ"].float().numpy().astype(np.float64)
+    for T in (0.0, 1.0):
+        o = dr.draft(_dev(np.arange(B)), _dev(anchors), K, temperature=T, seed=3, step=1, want_logits=True,
+                     want_hidden=True)
+        torch.cuda.synchronize()
+        z = o["logits"].cpu().numpy().astype(np.float64)
+        hid = o["hidden"].cpu().numpy().astype(np.float64)
+        if T == 0.0:
+            orc = od.DrafterOracle(cfg, w)
+            orc.inject(0, rows[0])
+            zw = orc.block_logits(0, int(anchors[0]), K)
+            assert_close_report(z[0], zw, atol=2e-2, what="DFlash 2 logits, request 0")
+            del orc
+        checked = 0
+        for r in range(B):
+            ref = osl.selector_walk(z[r], hid[r], int(anchors[r]), W_H, A, Bc, C, T, seed=3, slot=r, step=1)
+            assert (o["cand_ids"][r].cpu().numpy() == ref["cand_ids"]).all()
+            if ref["margin"] < (1e-4 if T == 0 else 1e-5):
+                continue
+            checked += 1
+            assert list(o["draft_ids"][r].cpu().numpy()) == list(ref["draft_ids"]), f"T {T} req {r}"
+        assert checked >= B - 2
+        if T == 1.0:
+            # subset-q verification of these drafts at full vocabulary against target rows near the drafter's
+            t = torch.empty((B, K + 1, cfg.vocab), dtype=torch.float32, device="cuda")
+            t[:, :K] = o["logits"] + 0.5 * torch.randn((B, K, cfg.vocab), generator=torch.Generator(device="cuda")
+                                                       .manual_seed(5), device="cuda")
+            t[:, K] = torch.randn((B, cfg.vocab), device="cuda")
+            v = dr.verify_subset(_dev(np.arange(B)), o["draft_ids"], o["cand_ids"], o["cand_probs"], t,
+                                 temperature=1.0, seed=8, step=2)
+            torch.cuda.synchronize()
+            tn = t.cpu().numpy()
+            ok = 0
+            for r in range(B):
+                ref = over.verify_rejection_subset(o["draft_ids"][r].cpu().numpy(), o["cand_ids"][r].cpu().numpy(),
+                                                   o["cand_probs"][r].cpu().numpy().astype(np.float64), tn[r], 1.0,
+                                                   8, r, 2)
+                if ref["near_margin"] < 1e-5:
+                    continue
+                ok += 1
+                L = ref["out_len"]
+                assert v["out_len"][r].item() == L
+                assert list(v["out_tokens"][r].cpu().numpy()[:L]) == list(ref["out_tokens"])
+            assert ok >= B // 2
+    assert dr.get_error() == 0
+    dr.close()
