@@ -36,6 +36,13 @@ projections respectively (the pages place them in the layer's "prepare" and
 [0, H/G) correct tap 0 and rows [H/G, 2H/G) tap 1, channel c using group c // G;
 context rows are untouched (their K/V come from the fused target feature).
 
+Variants [P2 §2.2 "注意力" / "输出端"; P4 §5.2]: a causal-in-block flag (block
+row i attends to the context and to block rows j <= i; the pages disagree on the
+block-internal mask, non-causal is the default); the logits' output multiplier
+and softcap z -> c * tanh(z / c) applied in that order; a mask-embedding
+override, a trained vector that replaces the embedding row of mask_token_id at
+the mask positions (the input_embedding_scale still applies to it).
+
 Parity of absolute forward values is unpinned by the pages (no page prints an
 activation or a logit); the pieces are pinned against library routines and the
 invariants listed in tests/test_oracle_drafter.py.
@@ -80,13 +87,21 @@ def silu(x):
     return x / (1.0 + np.exp(-x))
 
 
-def attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, group: int) -> np.ndarray:
-    """q [R, n_q, d]; keys/vals [S, n_kv, d]; softmax(q k^T / sqrt d) v, no mask."""
+def attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, group: int, causal_from=None) -> np.ndarray:
+    """q [R, n_q, d]; keys/vals [S, n_kv, d]; softmax(q k^T / sqrt d) v.
+
+    causal_from = (C, rows): the last keys are the block's, key C + j is hidden
+    from query row i when j > rows[i] (block-internal causal mask); None: no mask.
+    """
     R, nq, d = q.shape
     out = np.zeros_like(q)
     for h in range(nq):
         kv = h // group
         s = q[:, h, :] @ keys[:, kv, :].T / np.sqrt(d)
+        if causal_from is not None:
+            C, rows = causal_from
+            for i in range(R):
+                s[i, C + rows[i] + 1:] = -np.inf
         s = s - s.max(axis=-1, keepdims=True)
         a = np.exp(s)
         a /= a.sum(axis=-1, keepdims=True)
@@ -113,8 +128,12 @@ def dynamic_conv(x: np.ndarray, base: np.ndarray, proj: np.ndarray, group: int) 
 class DrafterOracle:
     """fp64 drafter with its own per-slot context K/V cache."""
 
-    def __init__(self, cfg, weights: Dict, pos_offset: int = 0):
+    def __init__(self, cfg, weights: Dict, pos_offset: int = 0, output_multiplier: float = 1.0,
+                 logit_softcap: float = 0.0):
         self.cfg = cfg
+        self.output_multiplier = float(output_multiplier)
+        self.logit_softcap = float(logit_softcap)
+        self.mask_embedding = as64(weights["mask_embedding"]) if "mask_embedding" in weights else None
         self.pos_offset = pos_offset          # added to every absolute position (tests only)
         c = cfg
         self.embed = as64(weights["embed"])
@@ -170,6 +189,8 @@ class DrafterOracle:
         C = self.ctx_len(slot)
         ids = np.array([anchor] + [c.mask_token_id] * K)
         X = self.embed[ids] * c.input_embedding_scale
+        if self.mask_embedding is not None:
+            X[1:] = self.mask_embedding * c.input_embedding_scale
         pos = np.arange(C, C + R) + self.pos_offset
         for l, lw in enumerate(self.layers):
             h = rms_norm(X, lw["in_norm"], c.rms_eps)
@@ -185,10 +206,12 @@ class DrafterOracle:
                 vals = np.concatenate([self.cache[slot][l][1], v], axis=0)
             else:
                 keys, vals = k, v
+            causal = getattr(c, "causal_block", False)
             if single_query:
-                o = np.concatenate([attention(q[i:i + 1], keys, vals, c.group) for i in range(R)], axis=0)
+                o = np.concatenate([attention(q[i:i + 1], keys, vals, c.group,
+                                             (C, [i]) if causal else None) for i in range(R)], axis=0)
             else:
-                o = attention(q, keys, vals, c.group)
+                o = attention(q, keys, vals, c.group, (C, list(range(R))) if causal else None)
             X = X + o.reshape(R, c.q_dim) @ lw["o_w"].T
             h = rms_norm(X, lw["post_norm"], c.rms_eps)
             if "mlp_conv_base" in lw:
@@ -204,4 +227,7 @@ class DrafterOracle:
         """(logits [K, V], final-normalised hidden rows [K, H]) of the mask rows."""
         X = self.block_hidden(slot, anchor, K, single_query)
         h = rms_norm(X[1:], self.final_norm, self.cfg.rms_eps)
-        return h @ self.lm_head.T, h
+        z = (h @ self.lm_head.T) * self.output_multiplier
+        if self.logit_softcap > 0:
+            z = self.logit_softcap * np.tanh(z / self.logit_softcap)
+        return z, h

@@ -12,6 +12,15 @@ Readings where the pages are silent:
   * sampling is inverse-CDF in ascending token-id order with one Philox
     uniform u: the smallest id c with  sum_{id<=c} q(id) > u.
 
+Symmetric truncation [P2 §3.3: top-k / top-p act on both the draft's and the
+target's distributions]: truncate(p, top_k, top_p) keeps the top_k ids in
+top-k order (probability descending, id ascending), renormalises them, then
+keeps the shortest prefix of that order whose cumulative renormalised
+probability reaches top_p (the token that crosses is kept), and renormalises
+again.  Readings: top-p acts on the top-k-renormalised distribution (the common
+top-k-then-top-p convention; top_k = 0 means no top-k cut); the truncated draw
+is the inverse CDF in ascending id order over the kept ids.
+
 Every decision also returns a *margin*: how far the decision is from flipping
 (in units of the quantity compared).  Tests accept a different GPU result only
 when this margin is below the kernel's rounding bound.
@@ -74,7 +83,28 @@ def inverse_cdf(w: np.ndarray, u: float):
     return c, margin
 
 
-def select_block(z: np.ndarray, T: float, top_k: int, seed: int, slot: int, step: int):
+def truncate(p: np.ndarray, top_k: int = 0, top_p: float = 1.0):
+    """Truncated, renormalised copy of the distribution p (1-D); also the kept ids
+    (in top-k order) and the top-p decision margin (distance of the cumulative
+    sums next to the cut from top_p; inf when top-p is off)."""
+    p = np.asarray(p, dtype=np.float64)
+    order = topk(p, p.shape[0])
+    keep = order[:top_k] if top_k > 0 else order
+    margin = np.inf
+    if top_p < 1.0:
+        cum = np.cumsum(p[keep]) / p[keep].sum()
+        n = int(np.searchsorted(cum, top_p, side="left")) + 1      # shortest prefix with cum >= top_p
+        n = min(n, keep.shape[0])
+        lo = cum[n - 2] if n >= 2 else 0.0
+        margin = min(abs(cum[n - 1] - top_p), abs(top_p - lo))
+        keep = keep[:n]
+    out = np.zeros_like(p)
+    out[keep] = p[keep]
+    return out / out.sum(), keep, margin
+
+
+def select_block(z: np.ndarray, T: float, top_k: int, seed: int, slot: int, step: int, trunc_k: int = 0,
+                 trunc_p: float = 1.0):
     """Draft outputs for one request: z is [K, V] logits for mask positions 1..K.
 
     Returns dict with draft_ids [K], margins [K], topk_ids [K, top_k],
@@ -91,7 +121,12 @@ def select_block(z: np.ndarray, T: float, top_k: int, seed: int, slot: int, step
             draft[j], margin[j] = argmax_with_margin(z[j])
         else:
             u = float(philox.uniform(seed, slot, step, j + 1, philox.PURPOSE_DRAFT))
-            draft[j], margin[j] = inverse_cdf(q[j], u)
+            qj = q[j]
+            mt = np.inf
+            if trunc_k > 0 or trunc_p < 1.0:
+                qj, _, mt = truncate(q[j], trunc_k, trunc_p)
+            draft[j], margin[j] = inverse_cdf(qj, u)
+            margin[j] = min(margin[j], mt)
     out = {"draft_ids": draft, "margins": margin, "row_max": m, "row_lse": lse, "probs": q}
     if top_k > 0:
         tid = np.stack([topk(z[j], top_k) for j in range(K)])

@@ -48,7 +48,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import philox
-from .select import softmax, inverse_cdf, argmax_with_margin
+from .select import softmax, inverse_cdf, argmax_with_margin, truncate
 
 RESIDUAL_EPS = 2.0 ** -20
 
@@ -67,10 +67,24 @@ def verify_greedy(draft_ids, target_logits):
             "post": post, "margins": np.array(margin)}
 
 
-def verify_rejection(draft_ids, draft_logits, target_logits, T, seed, slot, step, uniform_fn=None):
+def _truncated_rows(probs, trunc_k, trunc_p):
+    """Row-wise truncate(); also the smallest top-p margin over the rows."""
+    if trunc_k <= 0 and trunc_p >= 1.0:
+        return probs, np.inf
+    rows, margin = [], np.inf
+    for row in probs:
+        t, _, m = truncate(row, trunc_k, trunc_p)
+        rows.append(t)
+        margin = min(margin, m)
+    return np.stack(rows), margin
+
+
+def verify_rejection(draft_ids, draft_logits, target_logits, T, seed, slot, step, uniform_fn=None, trunc_k=0,
+                     trunc_p=1.0):
     """draft_ids [K]; draft_logits [K, V] (row i-1 <-> mask i); target_logits [K+1, V].
 
     uniform_fn(position, purpose) overrides the Philox uniforms (tests only).
+    trunc_k / trunc_p: the symmetric top-k / top-p truncation of p and q (select.truncate).
     """
     if uniform_fn is None:
         def uniform_fn(position, purpose):
@@ -79,9 +93,9 @@ def verify_rejection(draft_ids, draft_logits, target_logits, T, seed, slot, step
     K = d.shape[0]
     if T <= 0:
         return verify_greedy(d, target_logits)
-    p = softmax(target_logits, T)
-    q = softmax(draft_logits, T)
-    near = np.inf
+    p, mp = _truncated_rows(softmax(target_logits, T), trunc_k, trunc_p)
+    q, mq = _truncated_rows(softmax(draft_logits, T), trunc_k, trunc_p)
+    near = min(mp, mq)
     a = 0
     out = []
     for i in range(1, K + 1):
@@ -165,10 +179,12 @@ def subset_to_full(cand_ids, cand_probs, V):
     return q
 
 
-def verify_rejection_subset(draft_ids, cand_ids, cand_probs, target_logits, T, seed, slot, step, uniform_fn=None):
+def verify_rejection_subset(draft_ids, cand_ids, cand_probs, target_logits, T, seed, slot, step, uniform_fn=None,
+                            trunc_k=0, trunc_p=1.0):
     """Rejection verification of a selector draft (see the module docstring).
 
     draft_ids [K]; cand_ids / cand_probs [K, C]; target_logits [K+1, V].
+    trunc_k / trunc_p truncate the target's p (the selector's q is its own subset law).
     """
     if uniform_fn is None:
         def uniform_fn(position, purpose):
@@ -178,9 +194,8 @@ def verify_rejection_subset(draft_ids, cand_ids, cand_probs, target_logits, T, s
     t = np.asarray(target_logits, dtype=np.float64)
     if T <= 0:
         return verify_greedy(d, t)
-    p = softmax(t, T)
+    p, near = _truncated_rows(softmax(t, T), trunc_k, trunc_p)
     q = subset_to_full(cand_ids, cand_probs, t.shape[1])
-    near = np.inf
     out = []
     for i in range(1, K + 1):
         pi, qi = p[i - 1][d[i - 1]], q[i - 1][d[i - 1]]

@@ -31,6 +31,7 @@ class DrafterConfig:
     conv_group: int = 0        # DFlash 2 dynamic conv: channels per kernel-correction group (0 = no conv)
     sel_rank: int = 0          # DFlash 2 path selector: codebook rank (0 = no selector)
     sel_cands: int = 16        # candidates per position kept by the selector
+    causal_block: bool = False  # block rows attend to the context and to block rows up to their own
 
     @property
     def q_dim(self) -> int:
