@@ -33,7 +33,8 @@ class dflash_config(ctypes.Structure):
                 ("rms_eps", c_float), ("rope_theta", c_float), ("input_embedding_scale", c_float),
                 ("output_multiplier", c_float), ("logit_softcap", c_float), ("max_batch", c_int32),
                 ("max_ctx", c_int32), ("max_k", c_int32), ("max_inject_rows", c_int32), ("max_top_k", c_int32),
-                ("max_tree", c_int32), ("conv_group", c_int32), ("sel_rank", c_int32), ("sel_cands", c_int32)]
+                ("max_tree", c_int32), ("conv_group", c_int32), ("sel_rank", c_int32), ("sel_cands", c_int32),
+                ("causal_block", c_int32)]
 
 
 class dflash_layer_weights(ctypes.Structure):
@@ -45,7 +46,8 @@ class dflash_layer_weights(ctypes.Structure):
 class dflash_weights(ctypes.Structure):
     _fields_ = [("embed", c_void_p), ("lm_head", c_void_p), ("fc", c_void_p), ("hidden_norm", c_void_p),
                 ("final_norm", c_void_p), ("n_layers", c_int32), ("layers", POINTER(dflash_layer_weights)),
-                ("sel_pred", c_void_p), ("sel_succ", c_void_p), ("sel_hidden", c_void_p)]
+                ("sel_pred", c_void_p), ("sel_succ", c_void_p), ("sel_hidden", c_void_p),
+                ("mask_embedding", c_void_p)]
 
 
 class dflash_draft_params(ctypes.Structure):
@@ -80,6 +82,7 @@ _SIGS = {
                             c_uint64, c_uint64, c_void_p, c_void_p, c_void_p], c_int32),
     "dflash_verify_subset": ([c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_float, c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
+    "dflash_set_sampling": ([c_void_p, c_int32, c_float], c_int32),
     "dflash_profile": ([c_void_p, c_int32], c_int32),
     "dflash_profile_read": ([c_void_p, c_int32, POINTER(ctypes.c_double), POINTER(c_int32)], c_int32),
     "dflash_get_error": ([c_void_p, c_void_p, POINTER(c_int32)], c_int32),
@@ -179,6 +182,10 @@ def dflash_verify_subset(h, stream, n_req, K, C, slots, draft_ids, cand_ids, can
                          seed, step, out_tokens, out_len, accept_len, next_anchor=None):
     return _call("dflash_verify_subset", h, stream, n_req, K, C, slots, draft_ids, cand_ids, cand_probs,
                  target_logits, temperature, seed, step, out_tokens, out_len, accept_len, next_anchor)
+
+
+def dflash_set_sampling(h, top_k, top_p):
+    return _call("dflash_set_sampling", h, int(top_k), float(top_p))
 
 
 PHASES = ("inject_prep", "inject_fc", "inject_norm", "inject_kv", "embed", "qkv", "attn", "attn_combine", "o",

@@ -19,6 +19,7 @@ struct dflash_handle {
   int device = 0, num_cus = 256;
   // borrowed weights
   const void* sel_hidden_src = nullptr;   // caller's W_H
+  const void* mask_emb = nullptr;         // caller's mask-embedding override (or null)
   const void *embed = nullptr, *lm_head = nullptr, *fc = nullptr, *hidden_norm = nullptr, *final_norm = nullptr;
   std::vector<dflash_layer_weights> layers;
   // matrices as the products read them: the caller's (fp32 drafter) or the
@@ -68,6 +69,13 @@ struct dflash_handle {
   float *sel_gate = nullptr, *sel_cprob = nullptr, *sel_probs_ws = nullptr, *sel_table = nullptr;
   int32_t *sel_cand = nullptr, *sel_ids_ws = nullptr;
   void* sel_hin = nullptr;                // caller hidden rows in the operand type
+  // symmetric sampling truncation (dflash_set_sampling)
+  int trunc_k = 0;
+  float trunc_p = 1.f;
+  float *vt_max = nullptr, *vt_sum = nullptr, *vrow_max = nullptr, *vrow_lse = nullptr;
+  int32_t* vt_arg = nullptr;
+  int32_t *tr_ids = nullptr, *kp_ids = nullptr;
+  float *tr_probs = nullptr, *kp_probs = nullptr;
   // verification
   int32_t* post = nullptr;
   float* vstats = nullptr;
@@ -155,7 +163,7 @@ int check_config(const dflash_config& c) {
   if (c.n_target_layers > MAX_ASEG) return DFLASH_E_UNSUPPORTED;
   if (c.max_k > 31) return DFLASH_E_UNSUPPORTED;
   if (c.max_top_k > 256 || c.max_tree > 256) return DFLASH_E_UNSUPPORTED;
-  if (c.conv_group < 0 || c.sel_rank < 0) return DFLASH_E_INVALID;
+  if (c.conv_group < 0 || c.sel_rank < 0 || c.causal_block < 0 || c.causal_block > 1) return DFLASH_E_INVALID;
   if (c.conv_group > 0 && (c.conv_group % 4 || c.hidden % c.conv_group || (2 * c.hidden / c.conv_group) % 8))
     return DFLASH_E_UNSUPPORTED;
   if (c.sel_rank > 0 && (c.sel_rank > 4096 || c.sel_cands < 1 || c.sel_cands > 64 || c.sel_cands > c.vocab))
@@ -335,6 +343,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
   h->hidden_norm = w->hidden_norm;
   h->final_norm = w->final_norm;
   h->layers.assign(w->layers, w->layers + c.n_layers);
+  h->mask_emb = w->mask_embedding;
   if (c.sel_rank > 0) {
     h->sel_pred = w->sel_pred;
     h->sel_succ = w->sel_succ;
@@ -403,6 +412,18 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc_t(h, &h->row_lse, lrows, 4))) break;
     const int kc = std::max(1, std::min(c.max_tree, c.vocab));
     if ((rc = alloc_t(h, &h->tk_ids, lrows * kc, 4))) break;
+    {   // truncation scratch: rows of a verification (K+1 target and K draft rows per request)
+      const size_t vrows = (size_t)c.max_batch * (2 * c.max_k + 1);
+      if ((rc = alloc_t(h, &h->vt_max, vrows * h->n_vtiles, 4))) break;
+      if ((rc = alloc_t(h, &h->vt_sum, vrows * h->n_vtiles, 4))) break;
+      if ((rc = alloc_t(h, &h->vt_arg, vrows * h->n_vtiles, 4))) break;
+      if ((rc = alloc_t(h, &h->vrow_max, vrows, 4))) break;
+      if ((rc = alloc_t(h, &h->vrow_lse, vrows, 4))) break;
+      if ((rc = alloc_t(h, &h->tr_ids, vrows * 64, 4))) break;
+      if ((rc = alloc_t(h, &h->tr_probs, vrows * 64, 4))) break;
+      if ((rc = alloc_t(h, &h->kp_ids, vrows * 64, 4))) break;
+      if ((rc = alloc_t(h, &h->kp_probs, vrows * 64, 4))) break;
+    }
     if (c.conv_group > 0) {
       if ((rc = alloc(h, &h->hbuf2, (size_t)h->maxM * H * es))) break;
       if ((rc = alloc_t(h, &h->cbuf, (size_t)h->maxM * 2 * (H / c.conv_group), 4))) break;
@@ -669,9 +690,15 @@ void select_stage(dflash_handle* h, hipStream_t s, int n_req, const int32_t* slo
   Phase ph(h, s, DFLASH_PH_SELECT);
   launch_row_finalize(rows, h->n_vtiles, h->tmax, h->tsum, h->targ, h->row_max, h->row_lse,
                       T > 0.f ? nullptr : o->draft_ids, o->row_max, o->row_lse, s);
-  if (T > 0.f)
+  if (T > 0.f && h->trunc_k > 0) {   // symmetric truncation: draw from the truncated rows
+    launch_topk(rows, V, h->trunc_k, logits, h->tmax, h->n_vtiles, h->lm_tile, inv_t, h->row_max, h->row_lse,
+                h->tr_ids, h->tr_probs, s);
+    launch_trunc_rows(rows, h->trunc_k, h->trunc_p, h->tr_ids, h->tr_probs, h->kp_ids, h->kp_probs, s);
+    launch_sparse_sample(rows, K, h->trunc_k, slots, p->seed, p->step, h->kp_ids, h->kp_probs, o->draft_ids, s);
+  } else if (T > 0.f) {
     launch_sample(rows, K, slots, p->seed, p->step, inv_t, logits, V, h->n_vtiles, h->lm_tile, h->tmax, h->tsum,
                   h->row_max, o->draft_ids, s);
+  }
   const int B = p->tree_budget;
   const int kc = B > 0 ? std::min(B, V) : 0;
   if (p->top_k > 0)
@@ -719,7 +746,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
 
   {
     Phase ph(h, s, DFLASH_PH_EMBED);
-    launch_embed_norm(dt, M, R, anchor_ids, c.mask_token_id, V, h->embed, c.input_embedding_scale, H, h->X,
+    launch_embed_norm(dt, M, R, anchor_ids, c.mask_token_id, V, h->embed, h->mask_emb, c.input_embedding_scale, H, h->X,
                       h->layers[0].in_norm, h->hbuf, c.rms_eps, h->err, s);
   }
   {
@@ -793,6 +820,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       a.splits = splits;
       a.ctx_alloc = h->ctx_alloc;
       a.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
+      a.causal = c.causal_block ? 1 : 0;
       {
         Phase ph(h, s, DFLASH_PH_ATTN);
         launch_attn(dt, d, qrt, a, h->attn_wg, s);
@@ -951,6 +979,39 @@ int dflash_select_from_logits(dflash_handle* h, void* stream, int32_t n_req, con
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+// Truncated rows of `rows` logits rows (scratch rows [row0, row0 + rows)): statistics,
+// top-k, then top-p; kept ids / probabilities land in kp_ids / kp_probs at row0.
+void truncate_rows(dflash_handle* h, hipStream_t s, int row0, int rows, const float* logits, float T) {
+  const int V = h->cfg.vocab, nt = h->n_vtiles;
+  const float inv_t = 1.0f / T;
+  const int64_t o = (int64_t)row0 * nt;
+  lm_stats_from_logits_kernel<<<dim3(nt, rows), 64, 0, s>>>(V, nt, h->lm_tile, logits, inv_t, h->vt_max + o,
+                                                             h->vt_sum + o, h->vt_arg + o);
+  launch_row_finalize(rows, nt, h->vt_max + o, h->vt_sum + o, h->vt_arg + o, h->vrow_max + row0, h->vrow_lse + row0,
+                      nullptr, nullptr, nullptr, s);
+  launch_topk(rows, V, h->trunc_k, logits, h->vt_max + o, nt, h->lm_tile, inv_t, h->vrow_max + row0,
+              h->vrow_lse + row0, h->tr_ids + (int64_t)row0 * h->trunc_k, h->tr_probs + (int64_t)row0 * h->trunc_k, s);
+  launch_trunc_rows(rows, h->trunc_k, h->trunc_p, h->tr_ids + (int64_t)row0 * h->trunc_k,
+                    h->tr_probs + (int64_t)row0 * h->trunc_k, h->kp_ids + (int64_t)row0 * h->trunc_k,
+                    h->kp_probs + (int64_t)row0 * h->trunc_k, s);
+}
+}  // namespace
+
+extern "C" {
+
+int dflash_set_sampling(dflash_handle* h, int32_t top_k, float top_p) {
+  if (!h) return DFLASH_E_INVALID;
+  if (top_k < 0 || top_k > 64 || !(top_p > 0.f && top_p <= 1.f)) return DFLASH_E_INVALID;
+  if (top_k == 0 && top_p < 1.f) return DFLASH_E_UNSUPPORTED;   // top-p is applied within a top-k set
+  if (top_k > h->cfg.vocab) return DFLASH_E_CAPACITY;
+  h->trunc_k = top_k;
+  h->trunc_p = top_p;
+  return DFLASH_OK;
+}
+
 int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, const int32_t* slots,
                   const int32_t* draft_ids, const float* draft_logits, const float* target_logits, float temperature,
                   uint64_t seed, uint64_t step, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
@@ -967,6 +1028,15 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
   if (temperature == 0.f) {
     launch_verify_greedy(n_req, K, c.vocab, draft_ids, target_logits, h->post, out_tokens, out_len, accept_len,
                          next_anchor, s);
+  } else if (h->trunc_k > 0) {
+    // target rows [0, n(K+1)) and draft rows after them, each truncated
+    const int nt = n_req * (K + 1), nd = n_req * K;
+    truncate_rows(h, s, 0, nt, target_logits, temperature);
+    truncate_rows(h, s, nt, nd, draft_logits, temperature);
+    const int tk = h->trunc_k;
+    launch_verify_sparse(n_req, K, tk, tk, slots, draft_ids, h->kp_ids, h->kp_probs, h->kp_ids + (int64_t)nt * tk,
+                         h->kp_probs + (int64_t)nt * tk, seed, step, out_tokens, out_len, accept_len, next_anchor,
+                         h->err, s);
   } else {
     launch_verify_rejection(n_req, K, c.vocab, slots, draft_ids, draft_logits, target_logits, 1.0f / temperature,
                             seed, step, h->vstats, out_tokens, out_len, accept_len, next_anchor, h->err, s);
@@ -1046,6 +1116,12 @@ int dflash_verify_subset(dflash_handle* h, void* stream, int32_t n_req, int32_t 
                          next_anchor, s);
   } else {
     if (!slots || !cand_ids || !cand_probs) return DFLASH_E_INVALID;
+    if (h->trunc_k > 0) {   // the target's p truncated; q is the selector's own subset law
+      truncate_rows(h, s, 0, n_req * (K + 1), target_logits, temperature);
+      launch_verify_sparse(n_req, K, h->trunc_k, C, slots, draft_ids, h->kp_ids, h->kp_probs, cand_ids, cand_probs,
+                           seed, step, out_tokens, out_len, accept_len, next_anchor, h->err, s);
+      return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
+    }
     launch_verify_subset(n_req, K, C, c.vocab, slots, draft_ids, cand_ids, cand_probs, target_logits,
                          1.0f / temperature, seed, step, h->vstats, out_tokens, out_len, accept_len, next_anchor,
                          h->err, s);

@@ -51,6 +51,7 @@ struct AttnArgs {
   int chunk_min, chunk_max;   // chunk size rule (groups), see above
   int64_t ctx_alloc;
   float scale_log2;        // log2(e) / sqrt(D)
+  int causal;              // 1: block row j sees block keys 0..j only (context keys always)
 };
 
 struct AttnCombineArgs {

@@ -276,7 +276,7 @@ void attn_kernel(const AttnArgs a) {
       }
     // lane holds keys 8*grp + i (sc[.][0]) and 8*grp + 4 + i (sc[.][1]) of each group, query row r16
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int g = 0; g < NG; ++g) {
       if (nval[g] < KV_BLOCK) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -284,6 +284,15 @@ void attn_kernel(const AttnArgs a) {
           if (8 * grp + 4 + i >= nval[g]) sc[g][1][i] = -INFINITY;
         }
       }
+      if (a.causal && cl + g >= cs.ncache) {   // the block's own keys: key j visible to block rows >= j
+        const int jrow = (wave * 16 + r16) % a.R;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (8 * grp + i > jrow) sc[g][0][i] = -INFINITY;
+          if (8 * grp + 4 + i > jrow) sc[g][1][i] = -INFINITY;
+        }
+      }
+    }
     // lane-local max; the row max over the 4 lane groups is only formed when some
     // score passes the reference by more than the threshold (the rare rescale)
     float mx = -INFINITY;
@@ -526,6 +535,14 @@ __global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
         for (int i = 0; i < 4; ++i) {
           if (8 * grp + i >= nval) sc0[i] = -INFINITY;
           if (8 * grp + 4 + i >= nval) sc1[i] = -INFINITY;
+        }
+      }
+      if (a.causal && cl >= cs.ncache) {   // the block's own keys: key j visible to block rows >= j
+        const int jrow = ((t0 + t) * 16 + r16) % a.R;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (8 * grp + i > jrow) sc0[i] = -INFINITY;
+          if (8 * grp + 4 + i > jrow) sc1[i] = -INFINITY;
         }
       }
       float mx = -INFINITY;

@@ -38,7 +38,8 @@ __global__ void rope_table_kernel(float2* table, int n_pos, int d, double theta)
 // ---------------------------------------------------------------------------
 template <typename C>
 __global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* anchors, int mask_id, int vocab,
-                                                          const typename WeightOf<C>::type* embed, float scale, int H,
+                                                          const typename WeightOf<C>::type* embed,
+                                                          const typename WeightOf<C>::type* mask_emb, float scale, int H,
                                                           float* X, const typename WeightOf<C>::type* gain, C* h_out,
                                                           float eps, int32_t* err) {
   __shared__ float red[4];
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* a
     if (threadIdx.x == 0) raise_error(err, ERR_BAD_TOKEN);
     id = 0;
   }
-  const auto* e = embed + (int64_t)id * H;
+  const auto* e = (j > 0 && mask_emb) ? mask_emb : embed + (int64_t)id * H;
   float ss = 0.f;
   for (int c = threadIdx.x; c < H; c += 256) {
     const float v = to_f32(e[c]) * scale;
@@ -1034,6 +1035,159 @@ __global__ __launch_bounds__(256) void rejection_subset_kernel(int K, int C, int
 }
 
 // ---------------------------------------------------------------------------
+// Symmetric top-k / top-p truncation [P2 §3.3]: a distribution is cut to its
+// top-k ids (probability descending, id ascending), renormalised, cut again to
+// the shortest prefix of that order whose cumulative probability reaches top_p
+// (the crossing id kept), and renormalised.  Sets are at most 64 ids, one lane
+// per id; ids out of the set are written -1 with probability 0.
+// ---------------------------------------------------------------------------
+constexpr int TRUNC_MAX_K = 64;
+
+__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// one wave per row: ids_in / probs_in [rows][k] in top-k order with full-vocabulary probabilities
+__global__ __launch_bounds__(64) void trunc_rows_kernel(int k, float top_p, const int32_t* ids_in,
+                                                         const float* probs_in, int32_t* ids_out, float* probs_out) {
+  const int64_t m = blockIdx.x;
+  const int lane = threadIdx.x;
+  const bool on = lane < k;
+  const int id = on ? ids_in[m * k + lane] : -1;
+  const float p = on ? probs_in[m * k + lane] : 0.f;
+  const float r = p / wave_sum(p);
+  const float incl = wave_incl_scan(r, lane);
+  float excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.f;
+  const bool keep = on && (top_p >= 1.f || excl < top_p);
+  const float z = wave_sum(keep ? r : 0.f);
+  if (on) {
+    ids_out[m * k + lane] = keep ? id : -1;
+    probs_out[m * k + lane] = keep ? r / z : 0.f;
+  }
+}
+
+// Inverse-CDF draw in ascending id order over a lane set (ids < 0 unused):
+// every lane's rank by id places the set in id order in LDS, then a prefix scan
+// in that order (neighbouring ranges share end points exactly).  Returns the id
+// (wave-uniform); falls back to the last id with weight.
+__device__ int sparse_draw(int id, float w, float u, int lane, float* sp, int* si) {
+  const bool on = id >= 0;
+  int rank = 0;
+  for (int l = 0; l < 64; ++l) {
+    const int o = __shfl(id, l, 64);
+    rank += (o >= 0 && o < id) ? 1 : 0;
+  }
+  sp[lane] = 0.f;
+  si[lane] = -1;
+  __syncthreads();
+  if (on) {
+    sp[rank] = w;
+    si[rank] = id;
+  }
+  __syncthreads();
+  const float ws = sp[lane];
+  const int is = si[lane];
+  const float incl = wave_incl_scan(ws, lane);
+  float excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.f;
+  const float tm = u * __shfl(incl, 63, 64);
+  const unsigned long long hit = __ballot(is >= 0 && ws > 0.f && excl <= tm && tm < incl);
+  int pick;
+  if (hit) {
+    pick = __ffsll((long long)hit) - 1;
+  } else {
+    const unsigned long long nz = __ballot(is >= 0 && ws > 0.f);
+    pick = nz ? 63 - __clzll((long long)nz) : 0;
+  }
+  const int out = __shfl(is, pick, 64);
+  __syncthreads();
+  return out < 0 ? 0 : out;
+}
+
+// drafts from truncated rows: row j of request r draws with Philox(seed; j+1, slot, step, 0)
+__global__ __launch_bounds__(64) void sparse_sample_kernel(int K, int k, const int32_t* slots, uint64_t seed,
+                                                            uint64_t step, const int32_t* ids, const float* probs,
+                                                            int32_t* draft_ids) {
+  __shared__ float sp[64];
+  __shared__ int si[64];
+  const int64_t m = blockIdx.x;
+  const int r = (int)(m / K), j = (int)(m % K), lane = threadIdx.x;
+  const int id = lane < k ? ids[m * k + lane] : -1;
+  const float w = lane < k ? probs[m * k + lane] : 0.f;
+  const float u = philox_uniform(seed, (uint32_t)slots[r], step, (uint32_t)(j + 1), PURPOSE_DRAFT);
+  const int pick = sparse_draw(id, w, u, lane, sp, si);
+  if (lane == 0) draft_ids[m] = pick;
+}
+
+// Rejection against sparse distributions, one wave per request: p rows (target,
+// truncated) [n][K+1][kp], q rows (draft: truncated, or the selector's subset)
+// [n][K][kq]; ids < 0 unused, equal ids in q summed.  Same test, residual,
+// fallback and Philox uniforms as rejection_kernel.
+__global__ __launch_bounds__(64) void rejection_sparse_kernel(int K, int kp, int kq, const int32_t* slots,
+                                                               const int32_t* draft_ids, const int32_t* p_ids,
+                                                               const float* p_probs, const int32_t* q_ids,
+                                                               const float* q_probs, uint64_t seed, uint64_t step,
+                                                               int32_t* out_tokens, int32_t* out_len,
+                                                               int32_t* accept_len, int32_t* next_anchor,
+                                                               int32_t* err) {
+  __shared__ float sp[64];
+  __shared__ int si[64];
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const uint32_t slot = (uint32_t)slots[r];
+  const int32_t* d = draft_ids + (int64_t)r * K;
+  auto p_at = [&](int row, int tok) {   // p_row(tok), wave-uniform
+    const int64_t b = ((int64_t)r * (K + 1) + row) * kp;
+    const float v = (lane < kp && p_ids[b + lane] == tok) ? p_probs[b + lane] : 0.f;
+    return wave_sum(v);
+  };
+  auto q_at = [&](int row, int tok) {
+    const int64_t b = ((int64_t)r * K + row) * kq;
+    const float v = (lane < kq && q_ids[b + lane] == tok) ? q_probs[b + lane] : 0.f;
+    return wave_sum(v);
+  };
+  int a = 0;
+  for (; a < K; ++a) {
+    const int tok = d[a];
+    if (tok < 0) {
+      if (lane == 0) raise_error(err, ERR_BAD_TOKEN);
+      break;
+    }
+    const float pt = p_at(a, tok), qt = q_at(a, tok);
+    const float u = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_ACCEPT);
+    if (!(u * qt < pt)) break;
+  }
+  // draw at row a: the residual max(0, p - q) (p alone when it is exhausted), or the bonus from p_K
+  const int64_t pb = ((int64_t)r * (K + 1) + a) * kp;
+  const int id = lane < kp ? p_ids[pb + lane] : -1;
+  const float pv = (lane < kp && id >= 0) ? p_probs[pb + lane] : 0.f;
+  float w = pv;
+  if (a < K) {
+    float qv = 0.f;
+    const int64_t qb = ((int64_t)r * K + a) * kq;
+    for (int l = 0; l < kq; ++l) {
+      const int qi = q_ids[qb + l];
+      if (qi == id && id >= 0) qv += q_probs[qb + l];
+    }
+    w = fmaxf(pv - qv, 0.f);
+    if (wave_sum(w) < RESIDUAL_EPS) w = pv;   // exhausted / underflowed: draw from p
+  }
+  const float u2 = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_RESAMPLE);
+  const int pick = sparse_draw(id, w, u2, lane, sp, si);
+  int32_t* o = out_tokens + (int64_t)r * (K + 1);
+  for (int i = lane; i <= K; i += 64) o[i] = i < a ? d[i] : (i == a ? pick : -1);
+  if (lane == 0) {
+    out_len[r] = a + 1;
+    accept_len[r] = a;
+    if (next_anchor) next_anchor[r] = pick;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // DFlash 2 dynamic convolution [P2 §3.2.3]: y_t = k_{t,0} x_t + k_{t,1} x_{t-1}
 // over the R rows of each request's block (x_{-1} = 0), per channel c with
 // k_{t,j}[c] = base_j[c] + corr[t][j * H/G + c/G]; corr = x . proj^T comes from
@@ -1517,14 +1671,16 @@ void launch_rope_table(float2* table, int n_pos, int d, double theta, hipStream_
 }
 
 void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int mask_id, int vocab, const void* embed,
-                       float scale, int H, float* X, const void* gain, void* h_out, float eps, int32_t* err,
-                       hipStream_t s) {
+                       const void* mask_emb, float scale, int H, float* X, const void* gain, void* h_out, float eps,
+                       int32_t* err, hipStream_t s) {
   if (dtype == DT_BF16)
-    embed_norm_kernel<f16_t><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const bf16_t*)embed, scale, H, X,
-                                                     (const bf16_t*)gain, (f16_t*)h_out, eps, err);
+    embed_norm_kernel<f16_t><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const bf16_t*)embed,
+                                                     (const bf16_t*)mask_emb, scale, H, X, (const bf16_t*)gain,
+                                                     (f16_t*)h_out, eps, err);
   else
-    embed_norm_kernel<float><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const float*)embed, scale, H, X,
-                                                     (const float*)gain, (float*)h_out, eps, err);
+    embed_norm_kernel<float><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const float*)embed,
+                                                     (const float*)mask_emb, scale, H, X, (const float*)gain,
+                                                     (float*)h_out, eps, err);
 }
 
 void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, int K, int R, const void* gain,
@@ -1658,6 +1814,24 @@ void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const 
                                                    (const float*)B, table, err);
   sel_walk_kernel<<<n_req, 64, 0, s>>>(K, C, slots, cand, table, temperature > 0.f ? 1.0f / temperature : 0.f, seed,
                                        step, draft_ids, cand_out, probs_out);
+}
+
+void launch_trunc_rows(int rows, int k, float top_p, const int32_t* ids_in, const float* probs_in,
+                       int32_t* ids_out, float* probs_out, hipStream_t s) {
+  if (rows > 0) trunc_rows_kernel<<<rows, 64, 0, s>>>(k, top_p, ids_in, probs_in, ids_out, probs_out);
+}
+
+void launch_sparse_sample(int rows, int K, int k, const int32_t* slots, uint64_t seed, uint64_t step,
+                          const int32_t* ids, const float* probs, int32_t* draft_ids, hipStream_t s) {
+  if (rows > 0) sparse_sample_kernel<<<rows, 64, 0, s>>>(K, k, slots, seed, step, ids, probs, draft_ids);
+}
+
+void launch_verify_sparse(int n_req, int K, int kp, int kq, const int32_t* slots, const int32_t* draft_ids,
+                          const int32_t* p_ids, const float* p_probs, const int32_t* q_ids, const float* q_probs,
+                          uint64_t seed, uint64_t step, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
+                          int32_t* next_anchor, int32_t* err, hipStream_t s) {
+  rejection_sparse_kernel<<<n_req, 64, 0, s>>>(K, kp, kq, slots, draft_ids, p_ids, p_probs, q_ids, q_probs, seed,
+                                                step, out_tokens, out_len, accept_len, next_anchor, err);
 }
 
 template <typename T>

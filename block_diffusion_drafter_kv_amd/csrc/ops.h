@@ -44,8 +44,8 @@ void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, 
 // ---- elementwise / row kernels (kernels.hip) ----
 void launch_rope_table(float2* table, int n_pos, int d, double theta, hipStream_t s);
 void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int mask_id, int vocab, const void* embed,
-                       float scale, int H, float* X, const void* gain, void* h_out, float eps, int32_t* err,
-                       hipStream_t s);
+                       const void* mask_emb, float scale, int H, float* X, const void* gain, void* h_out, float eps,
+                       int32_t* err, hipStream_t s);
 // out row o reads X row (map_mask ? (o / K) * R + 1 + o % K : o); rows at or past
 // (*n_valid - valid_base) are skipped when n_valid is given (device-side row count)
 void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, int K, int R, const void* gain,
@@ -96,6 +96,18 @@ void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const 
                      const int32_t* anchors, const float* logits, const int32_t* cand, const float* gate,
                      const void* A, const void* B, float temperature, uint64_t seed, uint64_t step, float* table,
                      int32_t* draft_ids, int32_t* cand_out, float* probs_out, int32_t* err, hipStream_t s);
+// symmetric top-k / top-p truncation: rows of top-k (ids, full-vocabulary probabilities), k <= 64 ->
+// kept ids (-1 elsewhere) and renormalised probabilities
+void launch_trunc_rows(int rows, int k, float top_p, const int32_t* ids_in, const float* probs_in,
+                       int32_t* ids_out, float* probs_out, hipStream_t s);
+// draft tokens drawn from truncated rows (row j of request r: Philox(seed; j+1, slot, step, 0))
+void launch_sparse_sample(int rows, int K, int k, const int32_t* slots, uint64_t seed, uint64_t step,
+                          const int32_t* ids, const float* probs, int32_t* draft_ids, hipStream_t s);
+// rejection with sparse p rows [n][K+1][kp] and q rows [n][K][kq]
+void launch_verify_sparse(int n_req, int K, int kp, int kq, const int32_t* slots, const int32_t* draft_ids,
+                          const int32_t* p_ids, const float* p_probs, const int32_t* q_ids, const float* q_probs,
+                          uint64_t seed, uint64_t step, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
+                          int32_t* next_anchor, int32_t* err, hipStream_t s);
 // fp32 copy of n 16-bit (fp16) or fp32 values
 void launch_to_f32(int dtype, int64_t n, const void* src, float* dst, hipStream_t s);
 // n fp32 values rounded to the activation type (fp16 for a bf16 drafter)

@@ -14,7 +14,7 @@ from . import (DFLASH_BF16, DFLASH_F32, dflash_config, dflash_copy_cache, dflash
                dflash_destroy, dflash_draft_block, dflash_draft_outputs, dflash_draft_params, dflash_get_error,
                dflash_inject_context, dflash_layer_weights, dflash_profile, dflash_profile_read, dflash_reset_slots,
                dflash_select_from_logits, dflash_verify, dflash_verify_tree, dflash_inject_tree_path,
-               dflash_weights, dflash_select_path, dflash_verify_subset)
+               dflash_weights, dflash_select_path, dflash_verify_subset, dflash_set_sampling)
 
 _LAYER_KEYS = ("in_norm", "q_w", "k_w", "v_w", "o_w", "q_norm", "k_norm", "post_norm", "gate_w", "up_w", "down_w")
 _CONV_KEYS = ("attn_conv_base", "attn_conv_proj", "mlp_conv_base", "mlp_conv_proj")
@@ -54,6 +54,7 @@ class Drafter:
         cfg.conv_group = int(getattr(model, "conv_group", 0))
         cfg.sel_rank = int(getattr(model, "sel_rank", 0))
         cfg.sel_cands = int(getattr(model, "sel_cands", 16)) if cfg.sel_rank else 0
+        cfg.causal_block = 1 if getattr(model, "causal_block", False) else 0
         self.cfg = cfg
         layers = (dflash_layer_weights * model.n_layers)()
         for l, lw in enumerate(weights["layers"]):
@@ -68,6 +69,11 @@ class Drafter:
         w.hidden_norm, w.final_norm = _ptr(weights["hidden_norm"]), _ptr(weights["final_norm"])
         w.n_layers = model.n_layers
         w.layers = layers
+        if "mask_embedding" in weights:
+            t = weights["mask_embedding"]
+            if not t.is_cuda or t.dtype != self.dtype or not t.is_contiguous() or t.shape != (model.hidden,):
+                raise ValueError(f"mask_embedding: need a contiguous {self.dtype} CUDA tensor [hidden]")
+            w.mask_embedding = t.data_ptr()
         if cfg.sel_rank:
             for k in _SEL_KEYS:
                 t = weights[k]
@@ -174,6 +180,10 @@ class Drafter:
                       out["out_tokens"].data_ptr(), out["out_len"].data_ptr(), out["accept_len"].data_ptr(),
                       _ptr(out.get("next_anchor")))
         return out
+
+    def set_sampling(self, top_k=0, top_p=1.0):
+        """Symmetric top-k / top-p truncation of later sampled drafts and verifications (dflash_set_sampling)."""
+        dflash_set_sampling(self.handle, top_k, top_p)
 
     def select_path(self, slots, anchors, logits, hidden, temperature=0.0, seed=0, step=0):
         """DFlash 2 path selector alone (dflash_select_path) from fp32 logits [n, K, V] and hidden [n, K, H]."""

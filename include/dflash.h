@@ -101,6 +101,9 @@ typedef struct dflash_config {
                                  of 8); 0 = off                                                        */
   int32_t sel_rank;           /* > 0: path selector with codebooks of this rank (1..4096); 0 = off   */
   int32_t sel_cands;          /* selector candidates per position (1..64, <= vocab) when sel_rank > 0 */
+  int32_t causal_block;       /* 1: block row j attends to the context and to block rows 0..j only
+                                 (the pages differ on the block-internal mask [P2 §2.2 vs P4 §5.3]);
+                                 0: no mask inside the block (default)                               */
 } dflash_config;
 
 /* Per-layer weights, all [out_features, in_features] row-major, cfg.dtype.
@@ -142,6 +145,8 @@ typedef struct dflash_weights {
   const void* sel_pred;       /* [V, rank] predecessor codebook A                 */
   const void* sel_succ;       /* [V, rank] successor codebook B                   */
   const void* sel_hidden;     /* [rank, H] W_H, applied to the final-normalised hidden state */
+  const void* mask_embedding; /* [H] or NULL: trained vector embedded at the mask positions in place of
+                                 the embedding row of mask_token_id (times input_embedding_scale) [P4 §5.2] */
 } dflash_weights;
 
 typedef struct dflash_handle dflash_handle;
@@ -241,6 +246,16 @@ int dflash_select_from_logits(dflash_handle* h, void* stream, int32_t n_req, con
 int dflash_select_path(dflash_handle* h, void* stream, int32_t n_req, int32_t K, const int32_t* slots,
                        const int32_t* anchor_ids, const float* logits, const float* hidden, float temperature,
                        uint64_t seed, uint64_t step, int32_t* draft_ids, int32_t* cand_ids, float* cand_probs);
+
+/* Symmetric sampling truncation [P2 §3.3]: from this call on, every draw at
+ * temperature > 0 uses distributions cut to their top_k ids (probability
+ * descending, id ascending), renormalised, then to the shortest prefix of that
+ * order whose cumulative probability reaches top_p (the crossing id kept), and
+ * renormalised: the draft's sampling (not the selector's walk), and in
+ * dflash_verify both p and q, in dflash_verify_subset p.  Truncated draws are
+ * inverse CDFs in ascending id order.  top_k 0 = off (the default); 1..64;
+ * top_p in (0, 1] (1 = off) needs top_k >= 1 (else DFLASH_E_UNSUPPORTED). */
+int dflash_set_sampling(dflash_handle* h, int32_t top_k, float top_p);
 
 /* Verification of one drafted block per request [P2 §2.3, §4.2; P1 "验证"].
  * target_logits [n_req, K+1, V]: row j is the target's distribution after
