@@ -313,6 +313,88 @@ def dflash2_measure(w, ctx, steps=10, warmup=2):
             "phase_ms_per_step": dict(sorted(per_step.items(), key=lambda x: -x[1]))}
 
 
+def _timed(fn, steps, warmup=2):
+    """Median microseconds of fn() over `steps` calls on torch's current stream (after `warmup`)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    marks = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        marks.append((e0, e1))
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) * 1e3 for a, b in marks)
+
+
+def variants_measure(w, ctx, steps=10):
+    """The sampling and attention variants on the batch-32 workload: the draft with the
+    causal-in-block mask against the plain (non-causal) draft; sampled drafting (T = 1) and
+    rejection verification (T = 1, K = 16, V = 151936) without and with symmetric truncation
+    (top_k 50, top_p 0.9).  Verification bytes: one read of the K+1 target and K draft fp32 rows
+    per request."""
+    import numpy as np
+    import torch
+
+    import block_diffusion_drafter_kv_amd as dk
+    from synth.configs import get_workload, scaled_model
+
+    wl = get_workload("b32_ragged4k")
+    B, K, V = wl.batch, wl.K, wl.model.vocab
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    out = {"workload": wl.name, "steps": steps}
+    slots = i32(np.arange(B))
+    anchors = i32(np.random.default_rng(3).integers(0, V - 1, B))
+    logits = torch.empty((B, K, V), dtype=torch.float32, device="cuda")
+    for causal in (False, True):
+        cfg = scaled_model(wl.model, causal_block=causal)
+        dr = dk.Drafter(cfg, w, max_batch=B, max_ctx=max(ctx) + 64, max_k=K, max_inject_rows=8192)
+        g = torch.Generator(device="cuda").manual_seed(2024)
+        for r, c in enumerate(ctx):
+            for s0 in range(0, c, 8192):
+                n = min(8192, c - s0)
+                rows = torch.randn((n, cfg.n_target_layers, cfg.target_hidden), generator=g, device="cuda",
+                                   dtype=torch.float32).to(torch.bfloat16)
+                dr.inject(i32([r]), i32([0]), i32([n]), n, rows)
+        us = _timed(lambda: dr.draft(slots, anchors, K, want_stats=False, logits_out=logits), steps)
+        out["draft_causal_us" if causal else "draft_plain_us"] = round(us, 1)
+        if causal:
+            dr.close()
+            break
+        # sampled drafting and verification on this drafter's logits (drafts drawn under each mode)
+        dr.draft(slots, anchors, K, want_stats=False, logits_out=logits)
+        gt = torch.Generator(device="cuda").manual_seed(7)
+        target = torch.cat([logits, torch.zeros((B, 1, V), device="cuda")], dim=1)
+        target += torch.randn(target.shape, generator=gt, device="cuda") * 0.5
+        vb = (B * (2 * K + 1) * V * 4)
+        for name, (tk, tp) in (("plain", (0, 1.0)), ("trunc_k50_p0.9", (50, 0.9))):
+            dr.set_sampling(tk, tp)
+            d_ids = dr.draft(slots, anchors, K, temperature=1.0, seed=1, step=0, want_stats=False,
+                             logits_out=logits)["draft_ids"].clone()
+            res = {}
+            res["draft_t1_us"] = round(_timed(lambda: dr.draft(slots, anchors, K, temperature=1.0, seed=1, step=0,
+                                                                want_stats=False, logits_out=logits), steps), 1)
+            vo = dr.verify(slots, d_ids, logits, target, temperature=1.0, seed=2, step=0)
+            us = _timed(lambda: dr.verify(slots, d_ids, logits, target, temperature=1.0, seed=2, step=0, out=vo),
+                        steps)
+            res["verify_t1_us"] = round(us, 1)
+            res["verify_algorithmic_bytes"] = vb
+            res["verify_hbm_frac"] = round(vb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+            res["mean_committed"] = round(float(vo["out_len"].float().mean().item()), 3)
+            out[name] = res
+        dr.set_sampling(0, 1.0)
+        assert dr.get_error() == 0
+        dr.close()
+        del target
+    torch.cuda.empty_cache()
+    out["causal_overhead_vs_plain"] = round(out["draft_causal_us"] / out["draft_plain_us"] - 1.0, 4)
+    return out
+
+
 def tree_verify_measure(reps=20):
     """dflash_verify_tree at the batch-64 tree shape (64 requests, 65-node best-first trees from
     top-64 marginals, K = 16, V = 151936), greedy and T = 1.
@@ -400,6 +482,8 @@ def main():
     ap.add_argument("--no-tree", action="store_true", help="skip the tree verifier walk measurement")
     ap.add_argument("--no-inject", action="store_true", help="skip the long-prompt injection measurement")
     ap.add_argument("--no-dflash2", action="store_true", help="skip the DFlash 2 modules measurement")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the causal-mask / sampled / truncated draft and verify measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -578,6 +662,9 @@ def main():
         d2 = dflash2_measure(w, ctx)
         d2["overhead_vs_plain_draft"] = round(d2["draft_us_median"] / (draft_ms * 1e3) - 1.0, 4)
         result["dflash2"] = d2
+    if not args.no_variants:
+        log("[bench] sampling and attention variants on the same workload ...")
+        result["variants"] = variants_measure(w, ctx)
     del w
     torch.cuda.empty_cache()
     if not args.no_tree:

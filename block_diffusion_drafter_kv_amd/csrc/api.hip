@@ -79,6 +79,8 @@ struct dflash_handle {
   // verification
   int32_t* post = nullptr;
   float* vstats = nullptr;
+  int32_t* vacc = nullptr;     // accepted count per request (T > 0 verification)
+  float* vchunks = nullptr;    // chunk sums of p and of the residual
   std::vector<void*> allocs;
   // optional per-phase timing
   struct Mark { int phase; hipEvent_t a, b; };
@@ -448,6 +450,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc_t(h, &h->req_pos, c.max_batch, 4))) break;
     if ((rc = alloc_t(h, &h->post, (size_t)c.max_batch * R, 4))) break;
     if ((rc = alloc_t(h, &h->vstats, (size_t)c.max_batch * (2 * c.max_k + 1) * 2, 4))) break;
+    if ((rc = alloc_t(h, &h->vacc, (size_t)c.max_batch, 4))) break;
+    if ((rc = alloc_t(h, &h->vchunks, (size_t)2 * c.max_batch * draw_chunks(c.vocab), 4))) break;
   } while (0);
   if (rc) {
     free_all(h);
@@ -988,10 +992,9 @@ void truncate_rows(dflash_handle* h, hipStream_t s, int row0, int rows, const fl
   const int V = h->cfg.vocab, nt = h->n_vtiles;
   const float inv_t = 1.0f / T;
   const int64_t o = (int64_t)row0 * nt;
-  lm_stats_from_logits_kernel<<<dim3(nt, rows), 64, 0, s>>>(V, nt, h->lm_tile, logits, inv_t, h->vt_max + o,
-                                                             h->vt_sum + o, h->vt_arg + o);
-  launch_row_finalize(rows, nt, h->vt_max + o, h->vt_sum + o, h->vt_arg + o, h->vrow_max + row0, h->vrow_lse + row0,
-                      nullptr, nullptr, nullptr, s);
+  // one pass: row max / log-sum and the 128-id tile maxima (the LM head's tile width)
+  launch_row_stats(rows, V, logits, inv_t, h->vt_max + o, nt, h->vrow_max + row0, h->vrow_lse + row0, 1, 1 << 30,
+                   1 << 30, 0, 1, s);
   launch_topk(rows, V, h->trunc_k, logits, h->vt_max + o, nt, h->lm_tile, inv_t, h->vrow_max + row0,
               h->vrow_lse + row0, h->tr_ids + (int64_t)row0 * h->trunc_k, h->tr_probs + (int64_t)row0 * h->trunc_k, s);
   launch_trunc_rows(rows, h->trunc_k, h->trunc_p, h->tr_ids + (int64_t)row0 * h->trunc_k,
@@ -1023,6 +1026,7 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
   if (!draft_ids || !target_logits || !out_tokens || !out_len || !accept_len) return DFLASH_E_INVALID;
   if (!(temperature >= 0.f)) return DFLASH_E_INVALID;
   if (temperature > 0.f && (!draft_logits || !slots)) return DFLASH_E_INVALID;
+  if (temperature > 0.f && !draw_vocab_ok(c.vocab)) return DFLASH_E_CAPACITY;
   hipStream_t s = S(stream);
   Phase ph(h, s, DFLASH_PH_VERIFY);
   if (temperature == 0.f) {
@@ -1039,7 +1043,8 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
                          h->err, s);
   } else {
     launch_verify_rejection(n_req, K, c.vocab, slots, draft_ids, draft_logits, target_logits, 1.0f / temperature,
-                            seed, step, h->vstats, out_tokens, out_len, accept_len, next_anchor, h->err, s);
+                            seed, step, h->vstats, h->vacc, h->vchunks, out_tokens, out_len, accept_len,
+                            next_anchor, h->err, s);
   }
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
@@ -1116,6 +1121,7 @@ int dflash_verify_subset(dflash_handle* h, void* stream, int32_t n_req, int32_t 
                          next_anchor, s);
   } else {
     if (!slots || !cand_ids || !cand_probs) return DFLASH_E_INVALID;
+    if (!draw_vocab_ok(c.vocab)) return DFLASH_E_CAPACITY;
     if (h->trunc_k > 0) {   // the target's p truncated; q is the selector's own subset law
       truncate_rows(h, s, 0, n_req * (K + 1), target_logits, temperature);
       launch_verify_sparse(n_req, K, h->trunc_k, C, slots, draft_ids, h->kp_ids, h->kp_probs, cand_ids, cand_probs,
@@ -1123,8 +1129,8 @@ int dflash_verify_subset(dflash_handle* h, void* stream, int32_t n_req, int32_t 
       return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
     }
     launch_verify_subset(n_req, K, C, c.vocab, slots, draft_ids, cand_ids, cand_probs, target_logits,
-                         1.0f / temperature, seed, step, h->vstats, out_tokens, out_len, accept_len, next_anchor,
-                         h->err, s);
+                         1.0f / temperature, seed, step, h->vstats, h->vacc, h->vchunks, out_tokens, out_len,
+                         accept_len, next_anchor, h->err, s);
   }
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }

@@ -492,11 +492,14 @@ __global__ __launch_bounds__(256) void topk_kernel(int V, int k, const float* lo
   }
 }
 
-// Small k (<= 64): k rounds of a block-wide maximum, each over the keys below
-// the previous round's -- first over the tile maxima (the k-th largest tile
-// maximum bounds the k-th largest logit from below), then over the logits of
-// the tiles whose maximum reaches it.  Same keys, order and probabilities as
-// topk_kernel; no sort and no serial histogram scans.
+// Small k (<= 64).  The k-th largest tile maximum (a radix select over the
+// maxima's order keys) bounds the k-th largest logit from below, so the top k
+// lie among the logits at or above it in the tiles whose maximum reaches it;
+// those are gathered into LDS (at least k of them, usually a few more) and each
+// is placed by its rank among them (the keys are distinct: they carry the id).
+// More than TOPK_RANK_CAP gathered (heavy ties) falls back to k rounds of
+// block maxima over the same tiles.  Same keys, order and probabilities as
+// topk_kernel.
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
   for (int o = 32; o > 0; o >>= 1) {
     const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
@@ -512,52 +515,113 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
   return m;
 }
 
-constexpr int TOPK_SMALL_K = 64, TOPK_SMALL_TILES = 2048;
+// k-th largest of n 32-bit keys (1 <= k <= n): four 8-bit digit passes, each a
+// shared histogram of the keys that match the digits found so far, searched by
+// one wave from the top bucket down (four buckets per lane, integer scan).
+template <class Get>
+__device__ uint32_t radix_kth32(int n, int k, Get get, uint32_t* hist, uint32_t* sh_prefix, int* sh_k) {
+  uint32_t prefix = 0;
+  int krem = k;
+  const int lane = threadIdx.x & 63;
+  for (int pass = 3; pass >= 0; --pass) {
+    const int shift = pass * 8;
+    for (int b = threadIdx.x; b < 256; b += blockDim.x) hist[b] = 0;
+    __syncthreads();
+    const uint32_t hmask = pass == 3 ? 0u : (~0u << (shift + 8));
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const uint32_t key = get(i);
+      if ((key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shift) & 255], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int b0 = 255 - 4 * lane;   // buckets b0, b0-1, b0-2, b0-3 (descending)
+      int c[4], ls = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { c[q] = (int)hist[b0 - q]; ls += c[q]; }
+      int incl = ls;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const int excl = incl - ls;
+      if (excl < krem && krem <= incl) {
+        int cum = excl, q = 0;
+        for (; q < 3; ++q) {
+          if (cum + c[q] >= krem) break;
+          cum += c[q];
+        }
+        *sh_prefix = prefix | ((uint32_t)(b0 - q) << shift);
+        *sh_k = krem - cum;
+      }
+    }
+    __syncthreads();
+    prefix = *sh_prefix;
+    krem = *sh_k;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+constexpr int TOPK_SMALL_K = 64, TOPK_SMALL_TILES = 2048, TOPK_RANK_CAP = 1024;
 
 __global__ __launch_bounds__(256) void topk_small_kernel(int V, int k, const float* logits, const float* tmax,
                                                           int n_tiles, int tile_w, float inv_temp,
                                                           const float* row_max, const float* row_lse,
                                                           int32_t* ids_out, float* probs_out) {
   __shared__ uint64_t red[4];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_pref;
+  __shared__ int s_kr;
   __shared__ int tiles[TOPK_SMALL_TILES];
-  __shared__ int s_nt;
+  __shared__ int s_nt, s_nc;
+  __shared__ uint64_t cand[TOPK_RANK_CAP];
   __shared__ uint64_t sel[TOPK_SMALL_K];
   const int m = blockIdx.x, tid = threadIdx.x;
   const float* z = logits + (int64_t)m * V;
   const float* tm = tmax + (int64_t)m * n_tiles;
   const int kk = min(k, V);
-  // the kk-th largest tile maximum (all tiles when there are no more than kk)
+  // the kk-th largest tile maximum (no bound when there are no more tiles than kk)
   uint32_t thr = 0;
-  if (kk < n_tiles) {
-    uint64_t prev = ~0ull;
-    for (int i = 0; i < kk; ++i) {
-      uint64_t best = 0;
-      for (int t = tid; t < n_tiles; t += 256) {
-        const uint64_t key = ckey(tm[t], t);
-        if (key < prev && key > best) best = key;
-      }
-      prev = block_max_u64(best, red);
-    }
-    thr = (uint32_t)(prev >> 32);
-  }
-  if (tid == 0) s_nt = 0;
+  if (kk < n_tiles) thr = radix_kth32(n_tiles, kk, [&](int i) { return f2key(tm[i]); }, hist, &s_pref, &s_kr);
+  if (tid == 0) { s_nt = 0; s_nc = 0; }
   __syncthreads();
   for (int t = tid; t < n_tiles; t += 256)
     if (f2key(tm[t]) >= thr) tiles[atomicAdd(&s_nt, 1)] = t;
   __syncthreads();
   const int ne = s_nt * tile_w;
-  uint64_t prev = ~0ull;
-  for (int i = 0; i < kk; ++i) {
-    uint64_t best = 0;
-    for (int e = tid; e < ne; e += 256) {
-      const int c = tiles[e / tile_w] * tile_w + e % tile_w;
-      if (c < V) {
-        const uint64_t key = ckey(z[c] * inv_temp, c);
-        if (key < prev && key > best) best = key;
+  for (int e = tid; e < ne; e += 256) {
+    const int c = tiles[e / tile_w] * tile_w + e % tile_w;
+    if (c < V) {
+      const float v = z[c] * inv_temp;
+      if (f2key(v) >= thr) {
+        const int q = atomicAdd(&s_nc, 1);
+        if (q < TOPK_RANK_CAP) cand[q] = ckey(v, c);
       }
     }
-    prev = block_max_u64(best, red);
-    if (tid == 0) sel[i] = prev;
+  }
+  __syncthreads();
+  const int nc = s_nc;
+  if (nc <= TOPK_RANK_CAP) {
+    for (int i = tid; i < nc; i += 256) {
+      const uint64_t key = cand[i];
+      int rank = 0;
+      for (int j = 0; j < nc; ++j) rank += cand[j] > key ? 1 : 0;
+      if (rank < kk) sel[rank] = key;
+    }
+  } else {
+    uint64_t prev = ~0ull;
+    for (int i = 0; i < kk; ++i) {
+      uint64_t best = 0;
+      for (int e = tid; e < ne; e += 256) {
+        const int c = tiles[e / tile_w] * tile_w + e % tile_w;
+        if (c < V) {
+          const uint64_t key = ckey(z[c] * inv_temp, c);
+          if (key < prev && key > best) best = key;
+        }
+      }
+      prev = block_max_u64(best, red);
+      if (tid == 0) sel[i] = prev;
+    }
   }
   __syncthreads();
   const float M = row_max[m], L = row_lse[m];
@@ -763,199 +827,378 @@ __global__ void greedy_finish_kernel(int n_req, int K, const int32_t* draft_ids,
   if (next_anchor) next_anchor[r] = p[a];
 }
 
-// per row: (max of z/T, sum exp(z/T - max)); stats row q of request r = q / nrow
-// (nrow = 2K+1, or K+1 for target rows only): j = q % nrow <= K is target row j,
-// otherwise draft row j - K - 1.
-__global__ __launch_bounds__(256) void softmax_stats_kernel(int K, int nrow, int V, const float* target,
-                                                             const float* draft, float inv_temp, float* stats) {
-  __shared__ float red[4];
-  const int64_t m = blockIdx.x;
-  const int64_t r = m / nrow, j = m % nrow;
-  const float* row = j <= K ? target + (r * (K + 1) + j) * V : draft + (r * K + (j - K - 1)) * V;
-  float mx = -INFINITY;
-  for (int c = threadIdx.x; c < V; c += 256) mx = fmaxf(mx, row[c] * inv_temp);
-  mx = wave_max(mx);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[w] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // fixed order: thread-contiguous ranges, then the scan helper's order
-  const int per = (V + 255) / 256;
-  float s = 0.f;
-  for (int c = threadIdx.x * per; c < min(V, (int)(threadIdx.x + 1) * per); ++c) s += expf(row[c] * inv_temp - M);
-  s = block_sum(s, red);
-  if (threadIdx.x == 0) {
-    stats[2 * m] = M;
-    stats[2 * m + 1] = s;
+// ---------------------------------------------------------------------------
+// Row statistics of fp32 logits rows for verification and truncation, one
+// 256-thread block per row in one coalesced pass: M = max z/T and S = sum
+// exp(z/T - M) (online, per lane, then combined), and optionally the maximum of
+// z/T over each 128-id tile (the pruning bound of the top-k kernels).  Lane l
+// of a wave reads ids 4l..4l+3 of a 256-id unit (one 16-byte load when `vec`),
+// so lanes 0-31 cover one tile and lanes 32-63 the next.  Row m's results go to
+// o = (m / per) * group + off + m % per: out_max[o * os] and out_b[o * os]
+// (S, or log S with want_log).
+// ---------------------------------------------------------------------------
+constexpr int RS_TILE = 128;
+
+// e^x as 2^(x log2 e) on the hardware's base-2 exponential (v_exp_f32): a few
+// ulp for the x <= 0 the sums here take (larger relative error only where the
+// result is far below the terms that dominate a sum); 0 for x = -inf.
+__device__ __forceinline__ float exp_sum_term(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
+__device__ __forceinline__ void load4_row(const float* row, int c0, int V, bool vec, float x[4]) {
+  if (vec && c0 + 3 < V) {
+    const float4 v = *(const float4*)(row + c0);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = c0 + q < V ? row[c0 + q] : -INFINITY;
   }
+}
+
+template <bool TILES, bool VEC>
+__global__ __launch_bounds__(256) void row_stats_kernel(int V, const float* x, float inv_temp, float* tmax, int n_tiles,
+                                                        float* out_max, float* out_b, int os, int per, int group,
+                                                        int off, int want_log) {
+  __shared__ float sm[4], ss[4];
+  const int64_t m = blockIdx.x;
+  const float* row = x + m * V;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int units = (V + 255) / 256;
+  float lm = -INFINITY, ls = 0.f;
+  // four units per wave and pass: their loads are issued together (bytes in flight)
+  for (int u0 = w; u0 < units; u0 += 16) {
+    float v[4][4];
+    if (VEC && (u0 + 13) * 256 <= V) {   // the pass lies inside the row: plain 16-byte loads
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 q = *(const float4*)(row + (u0 + 4 * j) * 256 + 4 * lane);
+        v[j][0] = q.x; v[j][1] = q.y; v[j][2] = q.z; v[j][3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c0 = (u0 + 4 * j) * 256 + 4 * lane;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[j][q] = c0 + q < V ? row[c0 + q] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = u0 + 4 * j;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[j][q] *= inv_temp;   // -inf (past the row) stays -inf
+        mx = fmaxf(mx, v[j][q]);
+      }
+      if (TILES) {
+        float tm = mx;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 64));
+        const int t = 2 * u + (lane >> 5);
+        if ((lane & 31) == 0 && t < n_tiles) tmax[m * n_tiles + t] = tm;
+      }
+      if (mx > -INFINITY) {
+        const float nm = fmaxf(lm, mx);
+        float acc = ls * exp_sum_term(lm - nm);     // lm = -inf with ls = 0 gives 0
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc += exp_sum_term(v[j][q] - nm);
+        lm = nm;
+        ls = acc;
+      }
+    }
+  }
+  const float wm = wave_max(lm);
+  const float wsum = wave_sum(wm > -INFINITY && lm > -INFINITY ? ls * exp_sum_term(lm - wm) : 0.f);
+  if (lane == 0) { sm[w] = wm; ss[w] = wsum; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    float S = 0.f;
+    for (int i = 0; i < 4; ++i) S += sm[i] > -INFINITY ? ss[i] * expf(sm[i] - M) : 0.f;
+    const int64_t o = (m / per) * group + off + m % per;
+    out_max[o * os] = M;
+    out_b[o * os] = want_log ? logf(S) : S;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Inverse-CDF draw over ids [0, V) in ascending order by one 256-thread block,
+// for weights given four ids at a time: wf(c0, e) fills e[0..3] with the
+// weights of ids c0..c0+3 (0 beyond V).  Sums of 256-id chunks (coalesced, one
+// wave per chunk) go to LDS; one wave scans them in lane-contiguous ranges to
+// the chunk where the cumulative mass first exceeds u * total, then scans that
+// chunk's ids.  Neighbouring ranges share their end points, so exactly one
+// range holds the target; should rounding leave it past the last weight, the
+// last id with weight in the chosen range is taken.
+// ---------------------------------------------------------------------------
+constexpr int DRAW_CHUNK = 256;
+
+template <class WF>
+__device__ __forceinline__ void chunk_sums(int V, WF wf, float* csum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
+  // four chunks per wave and pass, their loads issued together
+  for (int c0 = w; c0 < nch; c0 += 16) {
+    float e[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wf((c0 + 4 * j) * DRAW_CHUNK + 4 * lane, e[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float t = wave_sum((e[j][0] + e[j][1]) + (e[j][2] + e[j][3]));
+      if (lane == 0 && c0 + 4 * j < nch) csum[c0 + 4 * j] = t;
+    }
+  }
+}
+
+// total of the chunk sums (wave 0 computes, every thread gets it)
+__device__ __forceinline__ float chunk_total(int V, const float* csum, float* sh) {
+  const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
+  if (threadIdx.x < 64) {
+    float t = 0.f;
+    for (int c = threadIdx.x; c < nch; c += 64) t += csum[c];
+    t = wave_sum(t);
+    if (threadIdx.x == 0) sh[0] = t;
+  }
+  __syncthreads();
+  const float t = sh[0];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ float wave_incl_scan_f(float v, int lane) {
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+template <class WF>
+__device__ int chunk_draw(int V, float u, WF wf, const float* csum, float* sh, int* si) {
+  const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    // level 1: the chunk
+    const int per = (nch + 63) / 64;
+    const int c0 = lane * per, c1 = min(nch, c0 + per);
+    float ls = 0.f;
+    for (int c = c0; c < c1; ++c) ls += csum[c];
+    const float incl = wave_incl_scan_f(ls, lane);
+    float excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.f;
+    const float target = u * __shfl(incl, 63, 64);
+    const unsigned long long hit = __ballot(ls > 0.f && excl <= target && target < incl);
+    const unsigned long long nz = __ballot(ls > 0.f);
+    const int owner = hit ? __ffsll((long long)hit) - 1 : (nz ? 63 - __clzll((long long)nz) : -1);
+    if (lane == owner) {
+      float acc = excl, before = excl, lastb = excl;
+      int ch = -1, last = -1;
+      for (int c = c0; c < c1; ++c) {
+        const float wc = csum[c];
+        if (wc > 0.f) {
+          last = c;
+          lastb = acc;
+          if (hit && ch < 0 && target < acc + wc) { ch = c; before = acc; }
+        }
+        acc += wc;
+      }
+      if (ch < 0) { ch = last; before = lastb; }
+      si[0] = ch;
+      sh[0] = before;
+      sh[1] = target;
+    }
+    if (owner < 0 && lane == 0) si[0] = -1;
+  }
+  __syncthreads();
+  const int ch = si[0];
+  const float before = sh[0], target = sh[1];
+  __syncthreads();
+  if (ch < 0) return 0;   // no weight anywhere
+  if (threadIdx.x < 64) {
+    // level 2: the id inside the chunk (lane l holds ids 4l..4l+3, ascending with l)
+    const int c0 = ch * DRAW_CHUNK + 4 * lane;
+    float e[4];
+    wf(c0, e);
+    const float ls = ((e[0] + e[1]) + e[2]) + e[3];
+    const float incl = before + wave_incl_scan_f(ls, lane);
+    float excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = before;
+    const unsigned long long hit = __ballot(ls > 0.f && excl <= target && target < incl);
+    const unsigned long long nz = __ballot(ls > 0.f);
+    const int owner = hit ? __ffsll((long long)hit) - 1 : (nz ? 63 - __clzll((long long)nz) : -1);
+    if (lane == owner) {
+      float acc = excl;
+      int pick = -1, last = -1;
+      for (int q = 0; q < 4; ++q) {
+        if (e[q] > 0.f) {
+          last = c0 + q;
+          if (hit && pick < 0 && target < acc + e[q]) pick = c0 + q;
+        }
+        acc += e[q];
+      }
+      si[1] = pick >= 0 ? pick : last;
+    }
+    if (owner < 0 && lane == 0) si[1] = ch * DRAW_CHUNK;
+  }
+  __syncthreads();
+  const int pick = si[1];
+  __syncthreads();
+  return pick;
 }
 
 static constexpr float RESIDUAL_EPS = 9.5367431640625e-07f;  // 2^-20
 
-__global__ __launch_bounds__(256) void rejection_kernel(int K, int V, const int32_t* slots, const int32_t* draft_ids,
-                                                         const float* draft_logits, const float* target,
-                                                         float inv_temp, uint64_t seed, uint64_t step,
-                                                         const float* stats, int32_t* out_tokens, int32_t* out_len,
-                                                         int32_t* accept_len, int32_t* next_anchor, int32_t* err) {
-  __shared__ float sh[8];
-  __shared__ int s_a, s_stop;
-  __shared__ float s_total;
-  __shared__ int s_thread, s_pick;
-  const int r = blockIdx.x;
-  const uint32_t slot = (uint32_t)slots[r];
-  const float* T0 = target + (int64_t)r * (K + 1) * V;
-  const float* Z0 = draft_logits + (int64_t)r * K * V;
-  const float* ts = stats + (int64_t)r * (2 * K + 1) * 2;   // rows: K+1 target, then K draft
-  const int32_t* d = draft_ids + (int64_t)r * K;
-  if (threadIdx.x == 0) {
-    int a = 0;
-    for (; a < K; ++a) {
-      const int i = a + 1;
-      const int tok = d[a];
-      if (tok < 0 || tok >= V) {   // not a token: reject here (and flag it)
-        raise_error(err, ERR_BAD_TOKEN);
-        break;
-      }
-      const float pm = ts[2 * a], ps = ts[2 * a + 1];
-      const float qm = ts[2 * (K + 1 + a)], qs = ts[2 * (K + 1 + a) + 1];
-      const float p = expf(T0[(int64_t)a * V + tok] * inv_temp - pm) / ps;
-      const float q = expf(Z0[(int64_t)a * V + tok] * inv_temp - qm) / qs;
-      const float u = philox_uniform(seed, slot, step, (uint32_t)i, PURPOSE_ACCEPT);
-      if (!(u * q < p)) break;
-    }
-    s_a = a;
-  }
-  __syncthreads();
-  const int a = s_a;
-  const bool bonus = a == K;
-  const int row = a;   // target row p_a (p_{i*-1} with i* = a+1, or the bonus row K)
-  const float* t = T0 + (int64_t)row * V;
-  const float* z = bonus ? nullptr : Z0 + (int64_t)a * V;
-  const float pm = ts[2 * row], ps = ts[2 * row + 1];
-  const float qm = bonus ? 0.f : ts[2 * (K + 1 + a)], qs = bonus ? 1.f : ts[2 * (K + 1 + a) + 1];
-  const int per = (V + 255) / 256;
-  const int c0 = threadIdx.x * per, c1 = min(V, c0 + per);
-  auto weight = [&](int c, bool use_resid) -> float {
-    const float p = expf(t[c] * inv_temp - pm) / ps;
-    if (!use_resid) return p;
-    const float q = expf(z[c] * inv_temp - qm) / qs;
-    return fmaxf(p - q, 0.f);
-  };
-  bool use_resid = !bonus;
-  float w = 0.f;
-  if (use_resid) {
-    for (int c = c0; c < c1; ++c) w += weight(c, true);
-    float tot = block_incl_scan(w, sh);
-    if (threadIdx.x == 255) s_total = tot;
-    __syncthreads();
-    if (s_total < RESIDUAL_EPS) use_resid = false;   // exhausted / underflowed: sample from p
-    __syncthreads();
-  }
-  if (!use_resid) {
-    w = 0.f;
-    for (int c = c0; c < c1; ++c) w += weight(c, false);
-  }
-  const float incl = block_incl_scan(w, sh);
-  if (threadIdx.x == 255) s_total = incl;
-  if (threadIdx.x == 0) { s_thread = -1; s_pick = -1; }
-  __syncthreads();
-  const float u2 = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_RESAMPLE);
-  const float target_mass = u2 * s_total;
-  const float excl = incl - w;
-  if (excl <= target_mass && target_mass < incl) s_thread = threadIdx.x;
-  __syncthreads();
-  if ((int)threadIdx.x == s_thread) {
-    float acc = excl;
-    for (int c = c0; c < c1; ++c) {
-      const float wc = weight(c, use_resid);
-      if (wc > 0.f && target_mass < acc + wc) { s_pick = c; break; }
-      acc += wc;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int pick = s_pick;
-    if (pick < 0) {   // rounding: last id with weight
-      for (int c = V - 1; c >= 0; --c)
-        if (weight(c, use_resid) > 0.f) { pick = c; break; }
-      if (pick < 0) pick = 0;
-    }
-    int32_t* o = out_tokens + (int64_t)r * (K + 1);
-    for (int i = 0; i < a; ++i) o[i] = d[i];
-    o[a] = pick;
-    for (int i = a + 1; i <= K; ++i) o[i] = -1;
-    out_len[r] = a + 1;
-    accept_len[r] = a;
-    if (next_anchor) next_anchor[r] = pick;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Subset-q rejection [P2 §3.1.3, §4.2]: the draft at position i carries C
-// candidate ids with a distribution over them (the DFlash 2 selector's);
-// q_full(v) = the summed probability of the candidates with id v (0 outside).
-// Accept d_i iff u * q_full(d_i) < p_{i-1}(d_i); at the first rejection draw
-// from max(0, p - q_full) (p alone when that mass is below RESIDUAL_EPS), after
-// K acceptances the bonus from p_K.  The residual equals p away from the
-// candidates, so each thread sums p over its id range and corrects the few
-// candidates inside it, found in an id-sorted copy of the candidate list.
+// Rejection verification at temperature T > 0 [P2 §2.3, §4.2; P1 "验证"], in
+// three steps so that the residual's pass over the vocabulary spreads over the
+// GPU instead of one work-group per request:
+//  1. verify_accept_kernel, one wave per request: lane i tests draft position
+//     i+1 (accept iff u * q(d_i) < p(d_i), Philox(seed; i+1, slot, step, 1));
+//     the first failure (or K) is the number accepted, a.
+//  2. resid_chunks_kernel, a grid of work-groups per request: sums of p and of
+//     the residual max(0, p - q) over 256-id chunks of row a (p alone after K
+//     acceptances).
+//  3. verify_draw_kernel, one work-group per request: the inverse-CDF draw
+//     (Philox(seed; a+1, slot, step, 2)) from the residual, from p when its mass
+//     is below RESIDUAL_EPS, or from the bonus row p_K.
+// Two forms of q: dense (the drafter's logits: q = softmax(z / T)) and subset
+// [P2 §3.1.3]: the selector's C candidates with a distribution over them,
+// q_full(v) = the summed probability of the candidates with id v (0 outside);
+// there the residual is p away from the candidates and p - min(p, q) at them,
+// so the chunk sums of p are corrected at the few candidates, in id order.
+// Statistics rows per request: K+1 target rows, then (dense) K draft rows.
 // ---------------------------------------------------------------------------
 constexpr int SUBSET_MAX_C = 64;
 
-__global__ __launch_bounds__(256) void rejection_subset_kernel(int K, int C, int V, const int32_t* slots,
-                                                                const int32_t* draft_ids, const int32_t* cand_ids,
-                                                                const float* cand_probs, const float* target,
-                                                                float inv_temp, uint64_t seed, uint64_t step,
-                                                                const float* stats, int32_t* out_tokens,
-                                                                int32_t* out_len, int32_t* accept_len,
-                                                                int32_t* next_anchor, int32_t* err) {
-  __shared__ float sh[8];
-  __shared__ int s_a, s_nc, s_thread, s_pick;
-  __shared__ float s_total;
+__global__ __launch_bounds__(64) void verify_accept_kernel(int K, int V, int subset, const int32_t* slots,
+                                                            const int32_t* draft_ids, const float* draft_logits,
+                                                            const float* target, float inv_temp,
+                                                            const float* stats, int C, const int32_t* cand_ids,
+                                                            const float* cand_probs, uint64_t seed, uint64_t step,
+                                                            int32_t* acc_out, int32_t* err) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const int nrow = subset ? K + 1 : 2 * K + 1;
+  const float* ts = stats + (int64_t)r * nrow * 2;
+  bool fail = false, bad = false;
+  if (lane < K) {
+    const int tok = draft_ids[(int64_t)r * K + lane];
+    bad = tok < 0 || tok >= V;
+    if (bad) {
+      fail = true;
+    } else {
+      const float p = expf(target[((int64_t)r * (K + 1) + lane) * V + tok] * inv_temp - ts[2 * lane]) /
+                      ts[2 * lane + 1];
+      float q = 0.f;
+      if (subset) {
+        const int64_t b = ((int64_t)r * K + lane) * C;
+        for (int j = 0; j < C; ++j)
+          if (cand_ids[b + j] == tok) q += cand_probs[b + j];
+      } else {
+        const int sr = K + 1 + lane;
+        q = expf(draft_logits[((int64_t)r * K + lane) * V + tok] * inv_temp - ts[2 * sr]) / ts[2 * sr + 1];
+      }
+      const float u = philox_uniform(seed, (uint32_t)slots[r], step, (uint32_t)(lane + 1), PURPOSE_ACCEPT);
+      fail = !(u * q < p);
+    }
+  }
+  const unsigned long long f = __ballot(fail);
+  const int a = f ? __ffsll((long long)f) - 1 : K;
+  if (lane == a && bad) raise_error(err, ERR_BAD_TOKEN);   // not a token: rejected here, flagged
+  if (lane == 0) acc_out[r] = a;
+}
+
+// chunk sums of row a: csp = p, csr = max(0, p - q) (dense q, a < K); grid (G, n_req)
+__global__ __launch_bounds__(256) void resid_chunks_kernel(int K, int V, int dense, const float* draft_logits,
+                                                            const float* target, float inv_temp,
+                                                            const float* stats, int vec, const int32_t* acc,
+                                                            int per_wg, float* csp, float* csr) {
+  const int r = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
+  const int a = acc[r];
+  const bool resid = dense && a < K;
+  const int nrow = dense ? 2 * K + 1 : K + 1;
+  const float* ts = stats + (int64_t)r * nrow * 2;
+  const float* t = target + ((int64_t)r * (K + 1) + a) * V;
+  const float* z = draft_logits + ((int64_t)r * K + (resid ? a : 0)) * V;
+  const float pm = ts[2 * a], ips = 1.0f / ts[2 * a + 1];
+  const float qm = resid ? ts[2 * (K + 1 + a)] : 0.f, iqs = resid ? 1.0f / ts[2 * (K + 1 + a) + 1] : 1.f;
+  const bool vv = vec != 0;
+  const int ch0 = blockIdx.x * per_wg, ch1 = min(nch, ch0 + per_wg);
+  float* op = csp + (int64_t)r * nch;
+  float* orr = csr + (int64_t)r * nch;
+  for (int c0 = ch0 + w; c0 < ch1; c0 += 16) {
+    float x[4][4], y[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      load4_row(t, (c0 + 4 * j) * DRAW_CHUNK + 4 * lane, V, vv, x[j]);
+      if (resid) load4_row(z, (c0 + 4 * j) * DRAW_CHUNK + 4 * lane, V, vv, y[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cb = (c0 + 4 * j) * DRAW_CHUNK + 4 * lane;
+      float sp = 0.f, sr = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (cb + q < V) {
+          const float pv = exp_sum_term(x[j][q] * inv_temp - pm) * ips;
+          sp += pv;
+          if (resid) sr += fmaxf(pv - exp_sum_term(y[j][q] * inv_temp - qm) * iqs, 0.f);
+        }
+      }
+      sp = wave_sum(sp);
+      if (resid) sr = wave_sum(sr);
+      if (lane == 0 && c0 + 4 * j < ch1) {
+        op[c0 + 4 * j] = sp;
+        if (resid) orr[c0 + 4 * j] = sr;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void verify_draw_kernel(int K, int V, int subset, const int32_t* slots,
+                                                           const int32_t* draft_ids, const float* draft_logits,
+                                                           const float* target, float inv_temp,
+                                                           const float* stats, int vec, int C,
+                                                           const int32_t* cand_ids, const float* cand_probs,
+                                                           const int32_t* acc, const float* csp, const float* csr,
+                                                           uint64_t seed, uint64_t step, int32_t* out_tokens,
+                                                           int32_t* out_len, int32_t* accept_len,
+                                                           int32_t* next_anchor) {
+  extern __shared__ float csum[];
+  __shared__ float sh[4];
+  __shared__ int si[2];
+  __shared__ int s_nc;
   __shared__ int sc_id[SUBSET_MAX_C];
   __shared__ float sc_q[SUBSET_MAX_C];
   const int r = blockIdx.x;
-  const uint32_t slot = (uint32_t)slots[r];
-  const float* T0 = target + (int64_t)r * (K + 1) * V;
-  const float* ts = stats + (int64_t)r * (K + 1) * 2;
-  const int32_t* d = draft_ids + (int64_t)r * K;
-  if (threadIdx.x == 0) {
-    int a = 0;
-    for (; a < K; ++a) {
-      const int tok = d[a];
-      if (tok < 0 || tok >= V) {   // not a token: reject here (and flag it)
-        raise_error(err, ERR_BAD_TOKEN);
-        break;
-      }
-      const float p = expf(T0[(int64_t)a * V + tok] * inv_temp - ts[2 * a]) / ts[2 * a + 1];
-      float q = 0.f;
-      for (int j = 0; j < C; ++j)
-        if (cand_ids[((int64_t)r * K + a) * C + j] == tok) q += cand_probs[((int64_t)r * K + a) * C + j];
-      const float u = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_ACCEPT);
-      if (!(u * q < p)) break;
-    }
-    s_a = a;
+  const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
+  const int a = acc[r];
+  const bool bonus = a == K;
+  const int nrow = subset ? K + 1 : 2 * K + 1;
+  const float* ts = stats + (int64_t)r * nrow * 2;
+  const float* t = target + ((int64_t)r * (K + 1) + a) * V;
+  const float* z = draft_logits ? draft_logits + ((int64_t)r * K + (bonus ? 0 : a)) * V : nullptr;
+  const float pm = ts[2 * a], ips = 1.0f / ts[2 * a + 1];
+  const float qm = !subset && !bonus ? ts[2 * (K + 1 + a)] : 0.f;
+  const float iqs = !subset && !bonus ? 1.0f / ts[2 * (K + 1 + a) + 1] : 1.f;
+  const bool vv = vec != 0;
+  if (subset && threadIdx.x == 0) {
     // candidates of the rejected position, sorted by id, equal ids merged
     int n = 0;
-    if (a < K) {
+    if (!bonus) {
+      const int64_t b = ((int64_t)r * K + a) * C;
       for (int j = 0; j < C; ++j) {
-        const int id = cand_ids[((int64_t)r * K + a) * C + j];
-        const float q = cand_probs[((int64_t)r * K + a) * C + j];
+        const int id = cand_ids[b + j];
+        const float q = cand_probs[b + j];
         if (id < 0 || id >= V) continue;
         int pos = n;
-        while (pos > 0 && sc_id[pos - 1] > id) {
-          sc_id[pos] = sc_id[pos - 1];
-          sc_q[pos] = sc_q[pos - 1];
-          --pos;
-        }
-        if (pos > 0 && sc_id[pos - 1] == id) {   // merge (shift back what was moved)
+        while (pos > 0 && sc_id[pos - 1] > id) --pos;
+        if (pos > 0 && sc_id[pos - 1] == id) {
           sc_q[pos - 1] += q;
-          for (int k = pos; k < n; ++k) {
-            sc_id[k] = sc_id[k + 1];
-            sc_q[k] = sc_q[k + 1];
-          }
           continue;
+        }
+        for (int k = n; k > pos; --k) {
+          sc_id[k] = sc_id[k - 1];
+          sc_q[k] = sc_q[k - 1];
         }
         sc_id[pos] = id;
         sc_q[pos] = q;
@@ -964,70 +1207,56 @@ __global__ __launch_bounds__(256) void rejection_subset_kernel(int K, int C, int
     }
     s_nc = n;
   }
+  const float* src = !bonus && !subset ? csr : csp;
+  for (int c = threadIdx.x; c < nch; c += 256) csum[c] = src[(int64_t)r * nch + c];
   __syncthreads();
-  const int a = s_a, nc = s_nc;
-  const bool bonus = a == K;
-  const float* t = T0 + (int64_t)a * V;
-  const float pm = ts[2 * a], ps = ts[2 * a + 1];
-  const int per = (V + 255) / 256;
-  const int c0 = threadIdx.x * per, c1 = min(V, c0 + per);
-  // first candidate at or after c0
-  int first = 0;
-  while (first < nc && sc_id[first] < c0) ++first;
-  auto pw = [&](int c) { return expf(t[c] * inv_temp - pm) / ps; };
-  // weight of id c given the candidate cursor k (advanced past ids below c)
-  auto weight = [&](int c, int& k, bool resid) -> float {
-    const float p = pw(c);
-    if (!resid) return p;
-    while (k < nc && sc_id[k] < c) ++k;
-    return (k < nc && sc_id[k] == c) ? fmaxf(p - sc_q[k], 0.f) : p;
+  const int nc = subset ? s_nc : 0;
+  auto wp = [&](int c0, float* e) {
+    float x[4];
+    load4_row(t, c0, V, vv, x);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) e[q] = c0 + q < V ? exp_sum_term(x[q] * inv_temp - pm) * ips : 0.f;
+  };
+  auto wr = [&](int c0, float* e) {   // the residual of ids c0..c0+3
+    wp(c0, e);
+    if (subset) {
+      for (int k = 0; k < nc; ++k) {
+        const int j = sc_id[k] - c0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (j == q) e[q] = fmaxf(e[q] - sc_q[k], 0.f);
+      }
+    } else {
+      float y[4];
+      load4_row(z, c0, V, vv, y);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (c0 + q < V) e[q] = fmaxf(e[q] - exp_sum_term(y[q] * inv_temp - qm) * iqs, 0.f);
+    }
   };
   bool use_resid = !bonus;
-  float w = 0.f;
   if (use_resid) {
-    int k = first;
-    for (int c = c0; c < c1; ++c) w += weight(c, k, true);
-    const float tot = block_incl_scan(w, sh);
-    if (threadIdx.x == 255) s_total = tot;
+    if (subset && threadIdx.x == 0) {   // p - min(p, q) at each candidate, in id order
+      for (int k = 0; k < nc; ++k) {
+        const int id = sc_id[k];
+        const float pv = exp_sum_term(t[id] * inv_temp - pm) * ips;
+        const int ch = id / DRAW_CHUNK;
+        csum[ch] = fmaxf(csum[ch] - fminf(pv, sc_q[k]), 0.f);
+      }
+    }
     __syncthreads();
-    if (s_total < RESIDUAL_EPS) use_resid = false;   // exhausted / underflowed: draw from p
-    __syncthreads();
-  }
-  if (!use_resid) {
-    w = 0.f;
-    for (int c = c0; c < c1; ++c) w += pw(c);
-  }
-  const float incl = block_incl_scan(w, sh);
-  if (threadIdx.x == 255) s_total = incl;
-  if (threadIdx.x == 0) { s_thread = -1; s_pick = -1; }
-  __syncthreads();
-  const float u2 = philox_uniform(seed, slot, step, (uint32_t)(a + 1), PURPOSE_RESAMPLE);
-  const float target_mass = u2 * s_total;
-  const float excl = incl - w;
-  if (excl <= target_mass && target_mass < incl) s_thread = threadIdx.x;
-  __syncthreads();
-  if ((int)threadIdx.x == s_thread) {
-    float acc = excl;
-    int k = first;
-    for (int c = c0; c < c1; ++c) {
-      const float wc = weight(c, k, use_resid);
-      if (wc > 0.f && target_mass < acc + wc) { s_pick = c; break; }
-      acc += wc;
+    if (chunk_total(V, csum, sh) < RESIDUAL_EPS) {   // exhausted / underflowed: draw from p
+      use_resid = false;
+      for (int c = threadIdx.x; c < nch; c += 256) csum[c] = csp[(int64_t)r * nch + c];
+      __syncthreads();
     }
   }
-  __syncthreads();
+  const float u2 = philox_uniform(seed, (uint32_t)slots[r], step, (uint32_t)(a + 1), PURPOSE_RESAMPLE);
+  const int pick = use_resid ? chunk_draw(V, u2, wr, csum, sh, si) : chunk_draw(V, u2, wp, csum, sh, si);
+  const int32_t* d = draft_ids + (int64_t)r * K;
+  int32_t* o = out_tokens + (int64_t)r * (K + 1);
+  for (int i = threadIdx.x; i <= K; i += 256) o[i] = i < a ? d[i] : (i == a ? pick : -1);
   if (threadIdx.x == 0) {
-    int pick = s_pick;
-    if (pick < 0) {   // rounding: the last id with weight
-      int k = 0;
-      for (int c = 0; c < V; ++c)
-        if (weight(c, k, use_resid) > 0.f) pick = c;
-      if (pick < 0) pick = 0;
-    }
-    int32_t* o = out_tokens + (int64_t)r * (K + 1);
-    for (int i = 0; i < a; ++i) o[i] = d[i];
-    o[a] = pick;
-    for (int i = a + 1; i <= K; ++i) o[i] = -1;
     out_len[r] = a + 1;
     accept_len[r] = a;
     if (next_anchor) next_anchor[r] = pick;
@@ -1770,24 +1999,66 @@ void launch_verify_tree(int n_req, int n_nodes, int max_out, int V, const int32_
 
 int tree_walk_segments(int V) { return (V + WALK_TILE - 1) / WALK_TILE * WALK_WAVES; }
 
+static inline int rows_vec_ok(int V, const float* p) { return (V & 3) == 0 && ((uintptr_t)p & 15) == 0; }
+static inline size_t draw_lds_bytes(int V) { return (size_t)((V + DRAW_CHUNK - 1) / DRAW_CHUNK) * sizeof(float); }
+int draw_vocab_ok(int V) { return draw_lds_bytes(V) <= 32768; }
+int draw_chunks(int V) { return (V + DRAW_CHUNK - 1) / DRAW_CHUNK; }
+static constexpr int RESID_CHUNKS_PER_WG = 32;
+
+void launch_row_stats(int rows, int V, const float* x, float inv_temp, float* tmax, int n_tiles, float* out_max,
+                      float* out_b, int os, int per, int group, int off, int want_log, hipStream_t s) {
+  if (rows <= 0) return;
+  const bool vec = rows_vec_ok(V, x);
+  auto go = [&](auto kern) {
+    kern<<<rows, 256, 0, s>>>(V, x, inv_temp, tmax, n_tiles, out_max, out_b, os, per, group, off, want_log);
+  };
+  if (tmax) {
+    if (vec) go(row_stats_kernel<true, true>);
+    else go(row_stats_kernel<true, false>);
+  } else {
+    if (vec) go(row_stats_kernel<false, true>);
+    else go(row_stats_kernel<false, false>);
+  }
+}
+
 void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,
                              const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
-                             uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
-                             int32_t* next_anchor, int32_t* err, hipStream_t s) {
+                             uint64_t step, float* stats, int32_t* acc, float* chunks, int32_t* out_tokens,
+                             int32_t* out_len, int32_t* accept_len, int32_t* next_anchor, int32_t* err,
+                             hipStream_t s) {
   // stats rows per request: K+1 target rows then K draft rows
-  softmax_stats_kernel<<<n_req * (2 * K + 1), 256, 0, s>>>(K, 2 * K + 1, V, target, draft_logits, inv_temp, stats);
-  rejection_kernel<<<n_req, 256, 0, s>>>(K, V, slots, draft_ids, draft_logits, target, inv_temp, seed, step, stats,
-                                          out_tokens, out_len, accept_len, next_anchor, err);
+  const int vec = rows_vec_ok(V, target) && rows_vec_ok(V, draft_logits);
+  const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
+  launch_row_stats(n_req * (K + 1), V, target, inv_temp, nullptr, 0, stats, stats + 1, 2, K + 1, 2 * K + 1, 0, 0, s);
+  launch_row_stats(n_req * K, V, draft_logits, inv_temp, nullptr, 0, stats, stats + 1, 2, K, 2 * K + 1, K + 1, 0, s);
+  verify_accept_kernel<<<n_req, 64, 0, s>>>(K, V, 0, slots, draft_ids, draft_logits, target, inv_temp, stats, 0,
+                                            nullptr, nullptr, seed, step, acc, err);
+  const int per_wg = RESID_CHUNKS_PER_WG;
+  float* csp = chunks;
+  float* csr = chunks + (int64_t)n_req * nch;
+  resid_chunks_kernel<<<dim3(cdiv(nch, per_wg), n_req), 256, 0, s>>>(K, V, 1, draft_logits, target, inv_temp, stats,
+                                                                     vec, acc, per_wg, csp, csr);
+  verify_draw_kernel<<<n_req, 256, draw_lds_bytes(V), s>>>(K, V, 0, slots, draft_ids, draft_logits, target, inv_temp,
+                                                           stats, vec, 0, nullptr, nullptr, acc, csp, csr, seed, step,
+                                                           out_tokens, out_len, accept_len, next_anchor);
 }
 
 void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, const int32_t* draft_ids,
                           const int32_t* cand_ids, const float* cand_probs, const float* target, float inv_temp,
-                          uint64_t seed, uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len,
-                          int32_t* accept_len, int32_t* next_anchor, int32_t* err, hipStream_t s) {
-  softmax_stats_kernel<<<n_req * (K + 1), 256, 0, s>>>(K, K + 1, V, target, nullptr, inv_temp, stats);
-  rejection_subset_kernel<<<n_req, 256, 0, s>>>(K, C, V, slots, draft_ids, cand_ids, cand_probs, target, inv_temp,
-                                                 seed, step, stats, out_tokens, out_len, accept_len, next_anchor,
-                                                 err);
+                          uint64_t seed, uint64_t step, float* stats, int32_t* acc, float* chunks,
+                          int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
+                          int32_t* err, hipStream_t s) {
+  const int vec = rows_vec_ok(V, target);
+  const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
+  launch_row_stats(n_req * (K + 1), V, target, inv_temp, nullptr, 0, stats, stats + 1, 2, 1 << 30, 1 << 30, 0, 0, s);
+  verify_accept_kernel<<<n_req, 64, 0, s>>>(K, V, 1, slots, draft_ids, nullptr, target, inv_temp, stats, C, cand_ids,
+                                            cand_probs, seed, step, acc, err);
+  const int per_wg = RESID_CHUNKS_PER_WG;
+  resid_chunks_kernel<<<dim3(cdiv(nch, per_wg), n_req), 256, 0, s>>>(K, V, 0, nullptr, target, inv_temp, stats, vec,
+                                                                     acc, per_wg, chunks, chunks);
+  verify_draw_kernel<<<n_req, 256, draw_lds_bytes(V), s>>>(K, V, 1, slots, draft_ids, nullptr, target, inv_temp,
+                                                           stats, vec, C, cand_ids, cand_probs, acc, chunks, chunks,
+                                                           seed, step, out_tokens, out_len, accept_len, next_anchor);
 }
 
 void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const void* gain, float eps,

@@ -82,10 +82,20 @@ void launch_verify_tree(int n_req, int n_nodes, int max_out, int V, const int32_
 // LDS segments (8 bytes each) the sampling tree walk keeps for a vocabulary of V ids.
 int tree_walk_segments(int V);
 // DFlash 2: rejection against candidate-subset draft distributions (C <= 64)
+// Row statistics of fp32 rows (max z/T and sum exp(z/T - max), or its log), with
+// optional per-128-id tile maxima; row m lands at (m / per) * group + off + m % per.
+void launch_row_stats(int rows, int V, const float* x, float inv_temp, float* tmax, int n_tiles, float* out_max,
+                      float* out_b, int os, int per, int group, int off, int want_log, hipStream_t s);
+// whether the verification draws' LDS chunk table fits for this vocabulary
+int draw_vocab_ok(int V);
+// number of 256-id chunks of the verification draws (chunk-sum scratch: 2 * n_req * chunks floats)
+int draw_chunks(int V);
+// stats [n_req * (K+1) * 2], acc [n_req], chunks [n_req * draw_chunks(V)] floats
 void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, const int32_t* draft_ids,
                           const int32_t* cand_ids, const float* cand_probs, const float* target, float inv_temp,
-                          uint64_t seed, uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len,
-                          int32_t* accept_len, int32_t* next_anchor, int32_t* err, hipStream_t s);
+                          uint64_t seed, uint64_t step, float* stats, int32_t* acc, float* chunks,
+                          int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
+                          int32_t* err, hipStream_t s);
 // DFlash 2: y = dynamic two-tap conv of x = RMSNorm(X; gain) [M, H] (blocks of R rows) with kernel
 // corrections corr [M, 2H/G]
 void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const void* gain, float eps,
@@ -112,10 +122,12 @@ void launch_verify_sparse(int n_req, int K, int kp, int kq, const int32_t* slots
 void launch_to_f32(int dtype, int64_t n, const void* src, float* dst, hipStream_t s);
 // n fp32 values rounded to the activation type (fp16 for a bf16 drafter)
 void launch_from_f32(int dtype, int64_t n, const float* src, void* dst, hipStream_t s);
+// stats [n_req * (2K+1) * 2], acc [n_req], chunks [2 * n_req * draw_chunks(V)] floats
 void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, const int32_t* draft_ids,
                              const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
-                             uint64_t step, float* stats, int32_t* out_tokens, int32_t* out_len, int32_t* accept_len,
-                             int32_t* next_anchor, int32_t* err, hipStream_t s);
+                             uint64_t step, float* stats, int32_t* acc, float* chunks, int32_t* out_tokens,
+                             int32_t* out_len, int32_t* accept_len, int32_t* next_anchor, int32_t* err,
+                             hipStream_t s);
 // out[i] = in[i] if in [0, max_batch) else max_batch (a spare empty slot), flagging the error word
 void launch_sanitize_slots(int n, const int32_t* in, int32_t* out, int max_batch, int32_t* err, hipStream_t s);
 void launch_synth_target(int n_req, int K, int V, const float* draft_logits, float sigma, uint64_t seed,

@@ -465,3 +465,62 @@ def test_full_dflash2_qwen_shape(gpu_lib):
             assert ok >= B // 2
     assert dr.get_error() == 0
     dr.close()
+
+
+def test_full_variants_qwen_shape(gpu_lib):
+    """Sampling and attention variants at the Qwen3-8B shape (5 layers, hidden 4096, V = 151936):
+    the causal-in-block mask (one request's K = 16 logits against the oracle forward at ctx 1024),
+    sampled drafts of a batch of 8 under top_k 50 / top_p 0.9 against the oracle's truncated draw
+    on the GPU's own logits, and rejection verification with truncated p and q at full vocabulary."""
+    from synth.configs import QWEN3_8B_SHAPED, scaled_model
+    cfg = scaled_model(QWEN3_8B_SHAPED, causal_block=True)
+    B, K, T, tk, tp = 8, 16, 0.8, 50, 0.9
+    w = gen.weights(cfg, seed=1234)
+    import block_diffusion_drafter_kv_amd as dk
+    dr = dk.Drafter(cfg, to_cuda(w), max_batch=B, max_ctx=2048, max_k=K, max_inject_rows=8192)
+    ctx = [1024, 300, 777, 64, 1500, 12, 900, 400]
+    rows0 = None
+    for r, c in enumerate(ctx):
+        x = gen.hidden_rows(cfg, r, 0, c)
+        rows0 = x if r == 0 else rows0
+        dr.inject(_dev([r]), _dev([0]), _dev([c]), c, x.cuda().contiguous())
+    anchors = gen.anchor_ids(cfg, B, seed=21)
+    o = dr.draft(_dev(np.arange(B)), _dev(anchors), K, want_logits=True)
+    torch.cuda.synchronize()
+    orc = od.DrafterOracle(cfg, w)
+    orc.inject(0, rows0)
+    assert_close_report(o["logits"][0].cpu().numpy(), orc.block_logits(0, int(anchors[0]), K), atol=2e-2,
+                        what="causal logits, request 0")
+    del orc
+    dr.set_sampling(tk, tp)
+    o = dr.draft(_dev(np.arange(B)), _dev(anchors), K, temperature=T, seed=3, step=1, want_logits=True)
+    torch.cuda.synchronize()
+    z = o["logits"].cpu().numpy().astype(np.float64)
+    ids = o["draft_ids"].cpu().numpy()
+    checked = 0
+    for r in range(B):
+        ref = osel.select_block(z[r], T, 0, seed=3, slot=r, step=1, trunc_k=tk, trunc_p=tp)
+        for j in range(K):
+            if ref["margins"][j] > 1e-5:
+                checked += 1
+                assert ids[r, j] == ref["draft_ids"][j], f"req {r} pos {j}"
+    assert checked >= B * K - 4
+    t = torch.empty((B, K + 1, cfg.vocab), dtype=torch.float32, device="cuda")
+    t[:, :K] = o["logits"] + 0.3 * torch.randn((B, K, cfg.vocab), generator=torch.Generator(device="cuda")
+                                               .manual_seed(5), device="cuda")
+    t[:, K] = o["logits"][:, K - 1]
+    v = dr.verify(_dev(np.arange(B)), o["draft_ids"], o["logits"], t, temperature=T, seed=8, step=2)
+    torch.cuda.synchronize()
+    tn = t.cpu().numpy()
+    ok = 0
+    for r in range(B):
+        ref = over.verify_rejection(ids[r], z[r], tn[r], T, 8, r, 2, trunc_k=tk, trunc_p=tp)
+        if ref["near_margin"] < 1e-5:
+            continue
+        ok += 1
+        L = ref["out_len"]
+        assert v["out_len"][r].item() == L, f"req {r}"
+        assert list(v["out_tokens"][r].cpu().numpy()[:L]) == list(ref["out_tokens"])
+    assert ok >= B - 2
+    assert dr.get_error() == 0
+    dr.close()
