@@ -333,7 +333,8 @@ def _timed(fn, steps, warmup=2):
 
 def variants_measure(w, ctx, steps=10):
     """The sampling and attention variants on the batch-32 workload: the draft with the
-    causal-in-block mask against the plain (non-causal) draft; sampled drafting (T = 1) and
+    causal-in-block mask, and with a paged cache (256-position pages scattered over the pool by
+    a shuffled table), against the plain draft; sampled drafting (T = 1) and
     rejection verification (T = 1, K = 16, V = 151936) without and with symmetric truncation
     (top_k 50, top_p 0.9).  Verification bytes: one read of the K+1 target and K draft fp32 rows
     per request."""
@@ -350,9 +351,19 @@ def variants_measure(w, ctx, steps=10):
     slots = i32(np.arange(B))
     anchors = i32(np.random.default_rng(3).integers(0, V - 1, B))
     logits = torch.empty((B, K, V), dtype=torch.float32, device="cuda")
-    for causal in (False, True):
+    page = 256
+    for mode in ("plain", "causal", "paged"):
+        causal = mode == "causal"
         cfg = scaled_model(wl.model, causal_block=causal)
-        dr = dk.Drafter(cfg, w, max_batch=B, max_ctx=max(ctx) + 64, max_k=K, max_inject_rows=8192)
+        mctx = max(ctx) + 64
+        kw = {}
+        if mode == "paged":   # 256-position pages, each request's pages scattered over the pool
+            per_slot = -(-mctx // page)
+            kw = {"page_size": page, "num_pages": B * per_slot}
+        dr = dk.Drafter(cfg, w, max_batch=B, max_ctx=mctx, max_k=K, max_inject_rows=8192, **kw)
+        if mode == "paged":
+            perm = np.random.default_rng(11).permutation(B * per_slot).astype(np.int32)
+            dr.set_page_table(torch.tensor(perm.reshape(B, per_slot), device="cuda"))
         g = torch.Generator(device="cuda").manual_seed(2024)
         for r, c in enumerate(ctx):
             for s0 in range(0, c, 8192):
@@ -361,10 +372,11 @@ def variants_measure(w, ctx, steps=10):
                                    dtype=torch.float32).to(torch.bfloat16)
                 dr.inject(i32([r]), i32([0]), i32([n]), n, rows)
         us = _timed(lambda: dr.draft(slots, anchors, K, want_stats=False, logits_out=logits), steps)
-        out["draft_causal_us" if causal else "draft_plain_us"] = round(us, 1)
-        if causal:
+        out[f"draft_{mode}_us"] = round(us, 1)
+        if mode != "plain":
+            assert dr.get_error() == 0
             dr.close()
-            break
+            continue
         # sampled drafting and verification on this drafter's logits (drafts drawn under each mode)
         dr.draft(slots, anchors, K, want_stats=False, logits_out=logits)
         gt = torch.Generator(device="cuda").manual_seed(7)
@@ -392,6 +404,8 @@ def variants_measure(w, ctx, steps=10):
         del target
     torch.cuda.empty_cache()
     out["causal_overhead_vs_plain"] = round(out["draft_causal_us"] / out["draft_plain_us"] - 1.0, 4)
+    out["paged_overhead_vs_plain"] = round(out["draft_paged_us"] / out["draft_plain_us"] - 1.0, 4)
+    out["page_size"] = page
     return out
 
 

@@ -34,7 +34,7 @@ class dflash_config(ctypes.Structure):
                 ("output_multiplier", c_float), ("logit_softcap", c_float), ("max_batch", c_int32),
                 ("max_ctx", c_int32), ("max_k", c_int32), ("max_inject_rows", c_int32), ("max_top_k", c_int32),
                 ("max_tree", c_int32), ("conv_group", c_int32), ("sel_rank", c_int32), ("sel_cands", c_int32),
-                ("causal_block", c_int32)]
+                ("causal_block", c_int32), ("page_size", c_int32), ("num_pages", c_int32)]
 
 
 class dflash_layer_weights(ctypes.Structure):
@@ -83,6 +83,7 @@ _SIGS = {
     "dflash_verify_subset": ([c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_float, c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
     "dflash_set_sampling": ([c_void_p, c_int32, c_float], c_int32),
+    "dflash_set_page_table": ([c_void_p, c_void_p], c_int32),
     "dflash_profile": ([c_void_p, c_int32], c_int32),
     "dflash_profile_read": ([c_void_p, c_int32, POINTER(ctypes.c_double), POINTER(c_int32)], c_int32),
     "dflash_get_error": ([c_void_p, c_void_p, POINTER(c_int32)], c_int32),
@@ -182,6 +183,10 @@ def dflash_verify_subset(h, stream, n_req, K, C, slots, draft_ids, cand_ids, can
                          seed, step, out_tokens, out_len, accept_len, next_anchor=None):
     return _call("dflash_verify_subset", h, stream, n_req, K, C, slots, draft_ids, cand_ids, cand_probs,
                  target_logits, temperature, seed, step, out_tokens, out_len, accept_len, next_anchor)
+
+
+def dflash_set_page_table(h, table_ptr):
+    return _call("dflash_set_page_table", h, table_ptr)
 
 
 def dflash_set_sampling(h, top_k, top_p):

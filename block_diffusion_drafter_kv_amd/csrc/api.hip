@@ -35,6 +35,20 @@ struct dflash_handle {
   void* cache_k = nullptr;
   void* cache_v = nullptr;
   int64_t ctx_alloc = 0;
+  // paged cache (cfg.page_size > 0): the caller's page table and its geometry
+  const int32_t* page_table = nullptr;
+  int pages_per_slot = 0;
+  int64_t page_elems = 0;   // elements of one page (all layers and kv heads)
+  KvPages pages() const {
+    KvPages p;
+    p.table = cfg.page_size > 0 ? page_table : nullptr;
+    p.per_slot = pages_per_slot;
+    p.page_size = cfg.page_size;
+    p.n_pages = cfg.num_pages;
+    p.table_rows = cfg.max_batch;
+    p.page_elems = page_elems;
+    return p;
+  }
   int32_t* ctx_len = nullptr;
   int32_t* err = nullptr;
   float2* rope = nullptr;
@@ -166,6 +180,8 @@ int check_config(const dflash_config& c) {
   if (c.max_k > 31) return DFLASH_E_UNSUPPORTED;
   if (c.max_top_k > 256 || c.max_tree > 256) return DFLASH_E_UNSUPPORTED;
   if (c.conv_group < 0 || c.sel_rank < 0 || c.causal_block < 0 || c.causal_block > 1) return DFLASH_E_INVALID;
+  if (c.page_size < 0 || (c.page_size > 0 && c.num_pages < 1)) return DFLASH_E_INVALID;
+  if (c.page_size > 0 && (c.page_size % 32 || c.page_size > 8192)) return DFLASH_E_UNSUPPORTED;
   if (c.conv_group > 0 && (c.conv_group % 4 || c.hidden % c.conv_group || (2 * c.hidden / c.conv_group) % 8))
     return DFLASH_E_UNSUPPORTED;
   if (c.sel_rank > 0 && (c.sel_rank > 4096 || c.sel_cands < 1 || c.sel_cands > 64 || c.sel_cands > c.vocab))
@@ -371,7 +387,12 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
   h->n_vtiles = (c.vocab + h->lm_tile - 1) / h->lm_tile;
   h->inject_chunk = std::min(c.max_inject_rows, 16384);
 
-  const size_t cache_elems = (size_t)c.n_layers * (c.max_batch + 1) * nkv * h->ctx_alloc * d;
+  if (c.page_size > 0) {
+    h->pages_per_slot = (c.max_ctx + c.page_size - 1) / c.page_size;
+    h->page_elems = (int64_t)c.n_layers * nkv * c.page_size * d;
+  }
+  const size_t cache_elems = c.page_size > 0 ? (size_t)c.num_pages * h->page_elems
+                                             : (size_t)c.n_layers * (c.max_batch + 1) * nkv * h->ctx_alloc * d;
   do {
     if ((rc = alloc(h, &h->cache_k, cache_elems * es))) break;
     if ((rc = alloc(h, &h->cache_v, cache_elems * es))) break;
@@ -501,6 +522,7 @@ int validate_inject(dflash_handle* h, int n_req, const int32_t* slots, const int
   if (!slots || !row_count || !target_hidden) return DFLASH_E_INVALID;
   if (n_req > c.max_batch || rows_upper_bound > c.max_inject_rows) return DFLASH_E_CAPACITY;
   if (row_stride < c.target_hidden || row_stride % 8) return DFLASH_E_INVALID;
+  if (c.page_size > 0 && !h->page_table) return DFLASH_E_INVALID;
   for (int l = 0; l < c.n_target_layers; ++l)
     if (!target_hidden[l]) return DFLASH_E_INVALID;
   return DFLASH_OK;
@@ -573,6 +595,8 @@ int inject_rows(dflash_handle* h, hipStream_t s, int n_req, int64_t rows_upper_b
       pk.ctx_alloc = h->ctx_alloc;
       pk.eps = c.rms_eps;
       pk.layer0 = l0;
+      pk.pages = h->pages();
+      pk.err = h->err;
       // the parameter block has the same layout for fp32 (pointers only differ in type)
       Phase ph(h, s, DFLASH_PH_INJECT_KV);
       launch_gemm(h->op, EPI_KVINJECT, gk, &pk, plan_gemm(h->op, plan_rows, gk.N, H, h->num_cus, false, true), h->partials,
@@ -674,6 +698,7 @@ int validate_draft(dflash_handle* h, int n_req, const dflash_draft_params* p, co
   const dflash_config& c = h->cfg;
   if (!p || !o || n_req < 0) return DFLASH_E_INVALID;
   if (n_req > c.max_batch) return DFLASH_E_CAPACITY;
+  if (c.page_size > 0 && !h->page_table) return DFLASH_E_INVALID;
   if (p->K < 1 || p->K > c.max_k) return DFLASH_E_CAPACITY;
   if (p->top_k < 0 || p->top_k > c.max_top_k || p->top_k > c.vocab) return DFLASH_E_CAPACITY;
   if (p->tree_budget < 0 || p->tree_budget > c.max_tree) return DFLASH_E_CAPACITY;
@@ -757,6 +782,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     Phase ph(h, s, DFLASH_PH_ATTN_PLAN);
     launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->attn_wg, kAttnMinGroups, kAttnChunkMin,
                      kAttnChunkMax, h->plan, h->seg_start, h->chunk_base, h->seg_desc, h->wg_range, s);
+    launch_page_check(n_req, slots, h->ctx_len, c.max_batch, h->pages(), h->err, s);
   }
   const int64_t layer_cache = (int64_t)(c.max_batch + 1) * nkv * h->ctx_alloc * d * h->esize;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -799,8 +825,16 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     {
       AttnArgs a;
       a.qb = h->qb;
-      a.cache_k = (const char*)h->cache_k + l * layer_cache;
-      a.cache_v = (const char*)h->cache_v + l * layer_cache;
+      // contiguous: the layer's region; paged: the layer's part of page 0
+      const int64_t lofs = c.page_size > 0 ? (int64_t)l * nkv * c.page_size * d * h->esize : l * layer_cache;
+      a.cache_k = (const char*)h->cache_k + lofs;
+      a.cache_v = (const char*)h->cache_v + lofs;
+      a.page_table = h->pages().table;
+      a.pages_per_slot = h->pages_per_slot;
+      a.gpp = c.page_size / 32;
+      a.n_pages = c.num_pages;
+      a.table_rows = c.max_batch;
+      a.page_elems = h->page_elems;
       a.kb = h->kb;
       a.vb = h->vb;
       a.slots = slots;
@@ -1005,6 +1039,13 @@ void truncate_rows(dflash_handle* h, hipStream_t s, int row0, int rows, const fl
 
 extern "C" {
 
+int dflash_set_page_table(dflash_handle* h, const int32_t* table) {
+  if (!h) return DFLASH_E_INVALID;
+  if (h->cfg.page_size == 0) return DFLASH_E_UNSUPPORTED;
+  h->page_table = table;
+  return DFLASH_OK;
+}
+
 int dflash_set_sampling(dflash_handle* h, int32_t top_k, float top_p) {
   if (!h) return DFLASH_E_INVALID;
   if (top_k < 0 || top_k > 64 || !(top_p > 0.f && top_p <= 1.f)) return DFLASH_E_INVALID;
@@ -1186,8 +1227,9 @@ int dflash_copy_cache(dflash_handle* h, void* stream, int32_t layer, int32_t slo
   if (layer < 0 || layer >= c.n_layers || slot < 0 || slot >= c.max_batch || start < 0 || n < 0 ||
       start + n > c.max_ctx)
     return DFLASH_E_INVALID;
+  if (c.page_size > 0 && !h->page_table) return DFLASH_E_INVALID;
   launch_copy_cache(c.dtype, h->cache_k, h->cache_v, layer, slot, start, n, c.max_batch + 1, c.n_kv_heads, c.head_dim,
-                    h->ctx_alloc, k_out, v_out, S(stream));
+                    h->ctx_alloc, h->pages(), k_out, v_out, S(stream));
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
 

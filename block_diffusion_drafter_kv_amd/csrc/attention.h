@@ -52,6 +52,11 @@ struct AttnArgs {
   int64_t ctx_alloc;
   float scale_log2;        // log2(e) / sqrt(D)
   int causal;              // 1: block row j sees block keys 0..j only (context keys always)
+  // paged cache (page_table null: contiguous); cache_k / cache_v then point at the
+  // layer's part of page 0 and a kv head's part of a page is page_size * D elements
+  const int32_t* page_table;   // [table_rows][pages_per_slot]
+  int pages_per_slot, gpp, n_pages, table_rows;   // gpp: 32-key groups per page
+  int64_t page_elems;
 };
 
 struct AttnCombineArgs {

@@ -125,13 +125,65 @@ __device__ __forceinline__ void wait_groups(int allowed) {
 // One segment (request r, kv head, q-row part z) as seen by a work-group.
 template <typename T>
 struct AttnSeg {
-  const T* kc;   // cache K of (slot, head), group 0
+  const T* kc;   // cache K of (slot, head), group 0 (contiguous storage)
   const T* vc;
   const T* kb;   // the block's own K / V group
   const T* vb;
   int start, len, ncache, C, cg;   // cg: groups per chunk
+  int slot, kv;
   int64_t qrow;  // this lane's query row in qb (in rows of D elements)
 };
+
+// K / V of context group g (32 keys) of (slot, kv head): contiguous, or through
+// the page table (an unmapped page reads page 0; the draft's page check flags
+// it).  A copy wave keeps the current page's id and loads the next page's id
+// when it enters a page, so the table read is off the copy issue's path.
+struct PageCursor {
+  int g, gin;                 // last group looked up (-1: none) and its index inside its page
+  int pi, page, npi, npage;   // current page index and id; prefetched next index (-1: none) and id
+};
+__device__ __forceinline__ void page_cursor_reset(PageCursor& pc) {
+  pc.g = -1;
+  pc.gin = 0;
+  pc.pi = -1;
+  pc.npi = -1;
+  pc.page = pc.npage = 0;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void ctx_group_ptrs(const AttnArgs& a, PageCursor& pc, const T* kc, const T* vc, int slot,
+                                               int kv, int g, int ncache, const T** kp, const T** vp) {
+  constexpr int BLK = KV_BLOCK * D;
+  if (!a.page_table) {
+    *kp = kc + (int64_t)g * BLK;
+    *vp = vc + (int64_t)g * BLK;
+    return;
+  }
+  // groups are visited in order inside a segment: step the in-page index, divide only on a jump
+  int pi;
+  if (g == pc.g + 1 && pc.g >= 0) {
+    pi = pc.pi;
+    if (++pc.gin == a.gpp) {
+      pc.gin = 0;
+      ++pi;
+    }
+  } else {
+    pi = g / a.gpp;
+    pc.gin = g - pi * a.gpp;
+  }
+  pc.g = g;
+  if (pi != pc.pi) {
+    const int32_t* row = a.page_table + (int64_t)(slot < a.table_rows ? slot : 0) * a.pages_per_slot;
+    pc.page = pi == pc.npi ? pc.npage : row[pi];
+    pc.pi = pi;
+    pc.npi = (pi + 1) * a.gpp < ncache ? pi + 1 : -1;
+    if (pc.npi >= 0) pc.npage = row[pc.npi];
+  }
+  const int page = slot < a.table_rows && (unsigned)pc.page < (unsigned)a.n_pages ? pc.page : 0;
+  const int64_t off = page * a.page_elems + ((int64_t)kv * a.gpp + pc.gin) * BLK;
+  *kp = (const T*)a.cache_k + off;
+  *vp = (const T*)a.cache_v + off;
+}
 
 // Streamed attention.  Work-group w takes the chunks that start in groups
 // [w*per_wg, (w+1)*per_wg) of the global group order; one wave per 16-row query
@@ -185,6 +237,8 @@ void attn_kernel(const AttnArgs a) {
     d.start = sd.z;
     d.len = sd.w;
     d.cg = attn_chunk_groups(d.len, a.chunk_min, a.chunk_max);
+    d.slot = slot;
+    d.kv = kv;
     const int64_t head = (int64_t)slot * a.n_kv + kv;
     d.kc = (const T*)a.cache_k + head * a.ctx_alloc * D;
     d.vc = (const T*)a.cache_v + head * a.ctx_alloc * D;
@@ -200,12 +254,17 @@ void attn_kernel(const AttnArgs a) {
   AttnSeg<T> is;
   decode(s0, is);
   int is_s = s0, is_l = g0 - is.start, issued = g0, is_stage = 0;
+  PageCursor pcur;
+  page_cursor_reset(pcur);
   auto issue = [&]() {
     if (wave < CW) {
       const int st = is_stage;
       const bool in_cache = is_l < is.ncache;
-      const T* kp = (in_cache ? is.kc + (int64_t)is_l * BLK : is.kb) + lane * EPC;
-      const T* vp = (in_cache ? is.vc + (int64_t)is_l * BLK : is.vb) + lane * EPC;
+      const T* kp = is.kb;
+      const T* vp = is.vb;
+      if (in_cache) ctx_group_ptrs<T, D>(a, pcur, is.kc, is.vc, is.slot, is.kv, is_l, is.ncache, &kp, &vp);
+      kp += lane * EPC;
+      vp += lane * EPC;
 #pragma unroll
       for (int c = 0; c < PER; ++c) {
         const int i = wave * PER + c;
@@ -219,6 +278,7 @@ void attn_kernel(const AttnArgs a) {
       ++is_s;
       decode(is_s, is);
       is_l = 0;
+      page_cursor_reset(pcur);
     }
   };
 
@@ -426,7 +486,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
 
   struct Seg {
     const T* kc; const T* vc; const T* kb; const T* vb;
-    int start, len, ncache, C, cg;
+    int start, len, ncache, C, cg, slot, kv;
     int64_t q0;
   };
   auto decode = [&](int s, Seg& d) {
@@ -439,6 +499,8 @@ __global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
     d.start = sd.z;
     d.len = sd.w;
     d.cg = attn_chunk_groups(d.len, a.chunk_min, a.chunk_max);
+    d.slot = slot;
+    d.kv = kv;
     const int64_t head = (int64_t)slot * a.n_kv + kv;
     d.kc = (const T*)a.cache_k + head * a.ctx_alloc * D;
     d.vc = (const T*)a.cache_v + head * a.ctx_alloc * D;
@@ -453,10 +515,15 @@ __global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
   Seg is;
   decode(s0, is);
   int is_s = s0, is_l = g0 - is.start, issued = g0, is_stage = 0;
+  PageCursor pcur;
+  page_cursor_reset(pcur);
   auto issue = [&]() {
     const bool in_cache = is_l < is.ncache;
-    const T* kp = (in_cache ? is.kc + (int64_t)is_l * BLK : is.kb) + lane * EPC;
-    const T* vp = (in_cache ? is.vc + (int64_t)is_l * BLK : is.vb) + lane * EPC;
+    const T* kp = is.kb;
+    const T* vp = is.vb;
+    if (in_cache) ctx_group_ptrs<T, D>(a, pcur, is.kc, is.vc, is.slot, is.kv, is_l, is.ncache, &kp, &vp);
+    kp += lane * EPC;
+    vp += lane * EPC;
 #pragma unroll
     for (int c = 0; c < PER; ++c) {
       const int i = (wave - NC) * PER + c;
@@ -469,6 +536,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
       ++is_s;
       decode(is_s, is);
       is_l = 0;
+      page_cursor_reset(pcur);
     }
   };
 

@@ -117,7 +117,7 @@ __device__ __forceinline__ float philox_uniform(uint64_t seed, uint32_t slot, ui
 enum : uint32_t { PURPOSE_DRAFT = 0, PURPOSE_ACCEPT = 1, PURPOSE_RESAMPLE = 2, PURPOSE_NOISE = 3, PURPOSE_TREE_WALK = 4 };
 
 // device error word bits
-enum : int32_t { ERR_CAPACITY = 1, ERR_BAD_SLOT = 2, ERR_ROWS = 4, ERR_BAD_TOKEN = 8 };
+enum : int32_t { ERR_CAPACITY = 1, ERR_BAD_SLOT = 2, ERR_ROWS = 4, ERR_BAD_TOKEN = 8, ERR_PAGE = 16 };
 
 __device__ __forceinline__ void raise_error(int32_t* err, int32_t bit) {
   if (err) atomicOr(err, bit);

@@ -140,6 +140,8 @@ struct EpiKVInject {
     int64_t ctx_alloc;
     float eps;
     int layer0;                                          // first layer of this product
+    KvPages pages;                                       // paged storage (table null: contiguous)
+    int32_t* err;                                        // device error word (unmapped pages)
   };
   template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
@@ -160,12 +162,18 @@ struct EpiKVInject {
           const int slot = p.row_slot[m];
           if (slot < 0) continue;
           const int pos = p.row_pos[m];
+          int64_t hb;
+          int pin;
+          if (!kv_locate(p.pages, p.ctx_alloc * p.d, p.max_batch, p.n_kv, p.d, p.layer0 + layer, slot, head, pos,
+                         &hb, &pin)) {
+            if (i == 0) raise_error(p.err, ERR_PAGE);
+            continue;
+          }
           float x1 = st[r * ld + hh * p.d + i], x2 = st[r * ld + hh * p.d + i + half];
           norm_rope_pair<W>(x1, x2, i, p.d, p.k_gain[layer], p.eps, p.rope + (int64_t)pos * half);
-          T* dst = p.cache_k +
-                   (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.ctx_alloc * p.d;
-          dst[k_off(pos, i, p.d)] = from_f32<T>(x1);
-          dst[k_off(pos, i + half, p.d)] = from_f32<T>(x2);
+          T* dst = p.cache_k + hb;
+          dst[k_off(pin, i, p.d)] = from_f32<T>(x1);
+          dst[k_off(pin, i + half, p.d)] = from_f32<T>(x2);
         }
       } else {
         // lanes walk rows (consecutive positions -> coalesced stores), waves walk columns
@@ -177,11 +185,16 @@ struct EpiKVInject {
           slot = p.row_slot[m];
           pos = p.row_pos[m];
         }
+        int64_t hb = 0;
+        int pin = 0;
+        if (slot >= 0 &&
+            !kv_locate(p.pages, p.ctx_alloc * p.d, p.max_batch, p.n_kv, p.d, p.layer0 + layer, slot, head, pos, &hb,
+                       &pin))
+          slot = -1;   // unmapped: flagged by the K half
         if (slot >= 0) {
-          T* base = p.cache_v +
-                    (((int64_t)(p.layer0 + layer) * p.max_batch + slot) * p.n_kv + head) * p.ctx_alloc * p.d;
+          T* base = p.cache_v + hb;
           for (int c = wave * RPL + lane / ROWS; c < p.d; c += 4 * RPL)
-            base[v_off(pos, c, p.d)] = from_f32<T>(st[r * ld + hh * p.d + c]);
+            base[v_off(pin, c, p.d)] = from_f32<T>(st[r * ld + hh * p.d + c]);
         }
       }
     }

@@ -1841,16 +1841,36 @@ __global__ void synth_target_kernel(int K, int V, const float* draft, float sigm
 
 template <typename T>
 __global__ void copy_cache_kernel(const T* cache_k, const T* cache_v, int layer, int slot, int start, int n,
-                                  int max_batch, int n_kv, int d, int64_t ctx_alloc, T* k_out, T* v_out) {
+                                  int max_batch, int n_kv, int d, int64_t ctx_alloc, KvPages pages, T* k_out,
+                                  T* v_out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)n * n_kv * d;
   if (idx >= total) return;
   const int e = (int)(idx % d);
   const int h = (int)((idx / d) % n_kv);
   const int i = (int)(idx / ((int64_t)d * n_kv));
-  const int64_t head = ((int64_t)layer * max_batch + slot) * n_kv + h;
-  k_out[idx] = cache_k[head * ctx_alloc * d + k_off(start + i, e, d)];
-  v_out[idx] = cache_v[head * ctx_alloc * d + v_off(start + i, e, d)];
+  int64_t base;
+  int pin;
+  if (!kv_locate(pages, ctx_alloc * d, max_batch, n_kv, d, layer, slot, h, start + i, &base, &pin)) {
+    k_out[idx] = (T)0.f;   // unmapped page
+    v_out[idx] = (T)0.f;
+    return;
+  }
+  k_out[idx] = cache_k[base + k_off(pin, e, d)];
+  v_out[idx] = cache_v[base + v_off(pin, e, d)];
+}
+
+// paged cache: every page a request's context occupies must be mapped
+__global__ void page_check_kernel(int n_req, const int32_t* slots, const int32_t* ctx_len, int max_batch,
+                                  KvPages pages, int32_t* err) {
+  const int r = blockIdx.x;
+  const int slot = slots[r];
+  if (slot < 0 || slot >= max_batch || slot >= pages.table_rows) return;
+  const int np = (ctx_len[slot] + pages.page_size - 1) / pages.page_size;
+  for (int p = threadIdx.x; p < np && p < pages.per_slot; p += blockDim.x) {
+    const int pg = pages.table[(int64_t)slot * pages.per_slot + p];
+    if ((unsigned)pg >= (unsigned)pages.n_pages) raise_error(err, ERR_PAGE);
+  }
 }
 
 __global__ void reset_slots_kernel(int n, const int32_t* slots, int32_t* ctx_len, int max_batch, int32_t* err) {
@@ -2153,17 +2173,23 @@ void launch_synth_target(int n_req, int K, int V, const float* draft_logits, flo
   synth_target_kernel<<<grid, 256, 0, s>>>(K, V, draft_logits, sigma, seed, step, out);
 }
 
+void launch_page_check(int n_req, const int32_t* slots, const int32_t* ctx_len, int max_batch, const KvPages& pages,
+                       int32_t* err, hipStream_t s) {
+  if (n_req > 0 && pages.table) page_check_kernel<<<n_req, 64, 0, s>>>(n_req, slots, ctx_len, max_batch, pages, err);
+}
+
 void launch_copy_cache(int dtype, const void* cache_k, const void* cache_v, int layer, int slot, int start, int n,
-                       int max_batch, int n_kv, int d, int64_t ctx_alloc, void* k_out, void* v_out, hipStream_t s) {
+                       int max_batch, int n_kv, int d, int64_t ctx_alloc, const KvPages& pages, void* k_out,
+                       void* v_out, hipStream_t s) {
   const int64_t total = (int64_t)n * n_kv * d;
   if (total <= 0) return;
   if (dtype == DT_BF16)
     copy_cache_kernel<f16_t><<<cdiv(total, 256), 256, 0, s>>>((const f16_t*)cache_k, (const f16_t*)cache_v, layer,
-                                                               slot, start, n, max_batch, n_kv, d, ctx_alloc,
+                                                               slot, start, n, max_batch, n_kv, d, ctx_alloc, pages,
                                                                (f16_t*)k_out, (f16_t*)v_out);
   else
     copy_cache_kernel<float><<<cdiv(total, 256), 256, 0, s>>>((const float*)cache_k, (const float*)cache_v, layer,
-                                                               slot, start, n, max_batch, n_kv, d, ctx_alloc,
+                                                               slot, start, n, max_batch, n_kv, d, ctx_alloc, pages,
                                                                (float*)k_out, (float*)v_out);
 }
 

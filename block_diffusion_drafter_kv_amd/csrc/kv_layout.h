@@ -23,6 +23,34 @@ namespace dfl {
 
 constexpr int KV_BLOCK = 32;   // positions per storage block
 
+// Paged storage (optional): a page holds page_size consecutive positions (a
+// multiple of KV_BLOCK) of one sequence for every layer and kv head, as
+// [layer][kv][page_size * D] with the 32-key blocks above inside; the caller's
+// table maps (slot, position / page_size) to a page id.  Elements per page:
+// n_layers * n_kv * page_size * D.  Contiguous storage is [layer][slot][kv]
+// [ctx_alloc * D].
+struct KvPages {
+  const int32_t* table;   // [table_rows][per_slot] page ids, or null: contiguous
+  int per_slot, page_size, n_pages, table_rows;
+  int64_t page_elems;
+};
+
+// first element of (layer, slot, kv) holding `pos`, and pos's offset from it; false when unmapped
+__device__ __forceinline__ bool kv_locate(const KvPages& pg, int64_t contig_head_elems, int max_slots, int n_kv,
+                                          int D, int layer, int slot, int kv, int pos, int64_t* base,
+                                          int* pos_in) {
+  if (!pg.table) {
+    *base = (((int64_t)layer * max_slots + slot) * n_kv + kv) * contig_head_elems;
+    *pos_in = pos;
+    return true;
+  }
+  const int page = slot < pg.table_rows ? pg.table[(int64_t)slot * pg.per_slot + pos / pg.page_size] : -1;
+  if ((unsigned)page >= (unsigned)pg.n_pages) return false;
+  *base = page * pg.page_elems + ((int64_t)layer * n_kv + kv) * pg.page_size * D;
+  *pos_in = pos % pg.page_size;
+  return true;
+}
+
 __host__ __device__ __forceinline__ int kblk_off(int j, int e, int D) {
   const int t = (j >> 2) & 1, r16 = ((j >> 3) << 2) | (j & 3);
   return (((t * (D >> 5) + (e >> 5)) * 64 + 16 * ((e >> 3) & 3) + r16) << 3) + (e & 7);

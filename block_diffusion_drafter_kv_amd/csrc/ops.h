@@ -133,7 +133,11 @@ void launch_sanitize_slots(int n, const int32_t* in, int32_t* out, int max_batch
 void launch_synth_target(int n_req, int K, int V, const float* draft_logits, float sigma, uint64_t seed,
                          uint64_t step, float* out, hipStream_t s);
 void launch_copy_cache(int dtype, const void* cache_k, const void* cache_v, int layer, int slot, int start, int n,
-                       int max_batch, int n_kv, int d, int64_t ctx_alloc, void* k_out, void* v_out, hipStream_t s);
+                       int max_batch, int n_kv, int d, int64_t ctx_alloc, const KvPages& pages, void* k_out,
+                       void* v_out, hipStream_t s);
+// paged cache: flags ERR_PAGE when a request's context occupies an unmapped page
+void launch_page_check(int n_req, const int32_t* slots, const int32_t* ctx_len, int max_batch, const KvPages& pages,
+                       int32_t* err, hipStream_t s);
 void launch_reset_slots(int n, const int32_t* slots, int32_t* ctx_len, int max_batch, int32_t* err, hipStream_t s);
 // bf16 drafter weights: *out = max over w of the fp32 bit pattern of |w| (atomic max;
 // *out must start at 0), and out = fp16(w * scale)

@@ -14,7 +14,8 @@ from . import (DFLASH_BF16, DFLASH_F32, dflash_config, dflash_copy_cache, dflash
                dflash_destroy, dflash_draft_block, dflash_draft_outputs, dflash_draft_params, dflash_get_error,
                dflash_inject_context, dflash_layer_weights, dflash_profile, dflash_profile_read, dflash_reset_slots,
                dflash_select_from_logits, dflash_verify, dflash_verify_tree, dflash_inject_tree_path,
-               dflash_weights, dflash_select_path, dflash_verify_subset, dflash_set_sampling)
+               dflash_weights, dflash_select_path, dflash_verify_subset, dflash_set_sampling,
+               dflash_set_page_table)
 
 _LAYER_KEYS = ("in_norm", "q_w", "k_w", "v_w", "o_w", "q_norm", "k_norm", "post_norm", "gate_w", "up_w", "down_w")
 _CONV_KEYS = ("attn_conv_base", "attn_conv_proj", "mlp_conv_base", "mlp_conv_proj")
@@ -31,7 +32,8 @@ def _stream():
 
 class Drafter:
     def __init__(self, model, weights: Dict, *, max_batch: int, max_ctx: int, max_k: int, max_inject_rows: int,
-                 max_top_k: int = 0, max_tree: int = 0, output_multiplier: float = 1.0, logit_softcap: float = 0.0):
+                 max_top_k: int = 0, max_tree: int = 0, output_multiplier: float = 1.0, logit_softcap: float = 0.0,
+                 page_size: int = 0, num_pages: int = 0):
         self.model = model
         self.dtype = torch.float32 if model.dtype == "f32" else torch.bfloat16
         self._w = weights                       # keep the borrowed tensors alive
@@ -55,6 +57,9 @@ class Drafter:
         cfg.sel_rank = int(getattr(model, "sel_rank", 0))
         cfg.sel_cands = int(getattr(model, "sel_cands", 16)) if cfg.sel_rank else 0
         cfg.causal_block = 1 if getattr(model, "causal_block", False) else 0
+        cfg.page_size, cfg.num_pages = int(page_size), int(num_pages)
+        self.pages_per_slot = -(-max_ctx // page_size) if page_size else 0
+        self._page_table = None
         self.cfg = cfg
         layers = (dflash_layer_weights * model.n_layers)()
         for l, lw in enumerate(weights["layers"]):
@@ -180,6 +185,15 @@ class Drafter:
                       out["out_tokens"].data_ptr(), out["out_len"].data_ptr(), out["accept_len"].data_ptr(),
                       _ptr(out.get("next_anchor")))
         return out
+
+    def set_page_table(self, table: torch.Tensor):
+        """Paged cache: the device page table [max_batch, pages_per_slot] int32 (borrowed; kept alive here)."""
+        if not table.is_cuda or table.dtype != torch.int32 or not table.is_contiguous() \
+                or tuple(table.shape) != (self.cfg.max_batch, self.pages_per_slot):
+            raise ValueError(f"page table: need a contiguous int32 CUDA tensor [{self.cfg.max_batch}, "
+                             f"{self.pages_per_slot}]")
+        self._page_table = table
+        dflash_set_page_table(self.handle, table.data_ptr())
 
     def set_sampling(self, top_k=0, top_p=1.0):
         """Symmetric top-k / top-p truncation of later sampled drafts and verifications (dflash_set_sampling)."""

@@ -64,7 +64,10 @@ enum dflash_device_error {
   DFLASH_DEV_CAPACITY = 1,   /* an injection would exceed max_ctx: that request's rows were skipped */
   DFLASH_DEV_BAD_SLOT = 2,   /* a slot id outside [0, max_batch): that request was skipped          */
   DFLASH_DEV_ROWS = 4,       /* row counts negative or above rows_upper_bound: rows skipped         */
-  DFLASH_DEV_BAD_TOKEN = 8   /* an anchor id outside [0, vocab): id 0 was embedded instead          */
+  DFLASH_DEV_BAD_TOKEN = 8,  /* an anchor id outside [0, vocab): id 0 was embedded instead          */
+  DFLASH_DEV_PAGE = 16       /* paged cache: a position maps to an unmapped page (table entry outside
+                                [0, num_pages)): injected rows there were skipped; a draft reading
+                                such a page read page 0 instead (its outputs are not meaningful)     */
 };
 
 /* Model shape, numerics and capacity, fixed at create time.
@@ -104,6 +107,10 @@ typedef struct dflash_config {
   int32_t causal_block;       /* 1: block row j attends to the context and to block rows 0..j only
                                  (the pages differ on the block-internal mask [P2 §2.2 vs P4 §5.3]);
                                  0: no mask inside the block (default)                               */
+  /* Paged KV cache (engine integration [P3 §4]); page_size 0 = one contiguous region per slot. */
+  int32_t page_size;          /* positions per page: 0, or a multiple of 32 up to 8192; a page holds
+                                 those positions of one sequence for every layer and kv head        */
+  int32_t num_pages;          /* pages in the handle's pool when page_size > 0 (>= 1)                */
 } dflash_config;
 
 /* Per-layer weights, all [out_features, in_features] row-major, cfg.dtype.
@@ -246,6 +253,18 @@ int dflash_select_from_logits(dflash_handle* h, void* stream, int32_t n_req, con
 int dflash_select_path(dflash_handle* h, void* stream, int32_t n_req, int32_t K, const int32_t* slots,
                        const int32_t* anchor_ids, const float* logits, const float* hidden, float temperature,
                        uint64_t seed, uint64_t step, int32_t* draft_ids, int32_t* cand_ids, float* cand_probs);
+
+/* Paged KV cache [P3 §4: the drafter's cache managed by the serving engine's
+ * pages]: table is a device array [max_batch][pages_per_slot] of int32 page ids
+ * (pages_per_slot = ceil(max_ctx / page_size)); entry (s, p) holds positions
+ * [p * page_size, (p+1) * page_size) of slot s.  Borrowed: the caller owns it,
+ * keeps it alive and may rewrite entries between calls (stream-ordered); -1 or
+ * any id outside [0, num_pages) = unmapped (see DFLASH_DEV_PAGE).  Pages may be
+ * shared between slots only for positions both hold identically (a common
+ * prefix); injecting into a shared page overwrites it for both.  Required
+ * before any call that reads or writes the cache of a paged handle
+ * (DFLASH_E_INVALID otherwise); DFLASH_E_UNSUPPORTED on a contiguous handle. */
+int dflash_set_page_table(dflash_handle* h, const int32_t* table);
 
 /* Symmetric sampling truncation [P2 §3.3]: from this call on, every draw at
  * temperature > 0 uses distributions cut to their top_k ids (probability
