@@ -150,11 +150,11 @@ __device__ __forceinline__ void page_cursor_reset(PageCursor& pc) {
   pc.page = pc.npage = 0;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __device__ __forceinline__ void ctx_group_ptrs(const AttnArgs& a, PageCursor& pc, const T* kc, const T* vc, int slot,
                                                int kv, int g, int ncache, const T** kp, const T** vp) {
   constexpr int BLK = KV_BLOCK * D;
-  if (!a.page_table) {
+  if constexpr (!PAGED) {
     *kp = kc + (int64_t)g * BLK;
     *vp = vc + (int64_t)g * BLK;
     return;
@@ -205,7 +205,7 @@ __device__ __forceinline__ void ctx_group_ptrs(const AttnArgs& a, PageCursor& pc
 //
 // Register budget: three waves per SIMD (<= 168 VGPRs) so that two 5-wave
 // work-groups share a CU.
-template <typename T, int D, int QRT, int S>
+template <typename T, int D, int QRT, int S, bool PAGED>
 __global__ __launch_bounds__(QRT * 64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && QRT == 5 ? 3 : 1)))
 void attn_kernel(const AttnArgs a) {
   constexpr int KS = D / 32, DT = D / 16, ROWS = QRT * 16;
@@ -262,7 +262,7 @@ void attn_kernel(const AttnArgs a) {
       const bool in_cache = is_l < is.ncache;
       const T* kp = is.kb;
       const T* vp = is.vb;
-      if (in_cache) ctx_group_ptrs<T, D>(a, pcur, is.kc, is.vc, is.slot, is.kv, is_l, is.ncache, &kp, &vp);
+      if (in_cache) ctx_group_ptrs<T, D, PAGED>(a, pcur, is.kc, is.vc, is.slot, is.kv, is_l, is.ncache, &kp, &vp);
       kp += lane * EPC;
       vp += lane * EPC;
 #pragma unroll
@@ -459,7 +459,7 @@ void attn_kernel(const AttnArgs a) {
 // fragments in registers across the whole segment.  One barrier per group
 // publishes the group and frees the ring stage of the previous one.  Per group and tile: S^T (32 x 16) = K Q^T, P = exp2(scale*s
 // - m) with the lazy integer reference m (as in attn_kernel), O^T += V^T P^T.
-template <typename T, int D, int QRT, int NW, int NP, int S>
+template <typename T, int D, int QRT, int NW, int NP, int S, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
   constexpr int KS = D / 32, DT = D / 16, ROWS = QRT * 16;
   constexpr int NC = NW - NP;                              // consumer waves
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
     const bool in_cache = is_l < is.ncache;
     const T* kp = is.kb;
     const T* vp = is.vb;
-    if (in_cache) ctx_group_ptrs<T, D>(a, pcur, is.kc, is.vc, is.slot, is.kv, is_l, is.ncache, &kp, &vp);
+    if (in_cache) ctx_group_ptrs<T, D, PAGED>(a, pcur, is.kc, is.vc, is.slot, is.kv, is_l, is.ncache, &kp, &vp);
     kp += lane * EPC;
     vp += lane * EPC;
 #pragma unroll
@@ -744,29 +744,29 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool PG>
 static void launch_attn_t(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
   constexpr int S = (sizeof(T) == 4 && D == 128) ? 4 : 5;  // LDS ring stages (16 or 32 KB each)
   switch (qrt) {
-    case 1: attn_kernel<T, D, 1, S><<<grid, 64, 0, s>>>(a); break;
-    case 2: attn_kernel<T, D, 2, S><<<grid, 128, 0, s>>>(a); break;
-    case 3: attn_kernel<T, D, 3, S><<<grid, 192, 0, s>>>(a); break;
-    case 4: attn_kernel<T, D, 4, S><<<grid, 256, 0, s>>>(a); break;
-    case 5: attn_kernel<T, D, 5, S><<<grid, 320, 0, s>>>(a); break;
+    case 1: attn_kernel<T, D, 1, S, PG><<<grid, 64, 0, s>>>(a); break;
+    case 2: attn_kernel<T, D, 2, S, PG><<<grid, 128, 0, s>>>(a); break;
+    case 3: attn_kernel<T, D, 3, S, PG><<<grid, 192, 0, s>>>(a); break;
+    case 4: attn_kernel<T, D, 4, S, PG><<<grid, 256, 0, s>>>(a); break;
+    case 5: attn_kernel<T, D, 5, S, PG><<<grid, 320, 0, s>>>(a); break;
   }
 }
 
 // 16-bit K/V: one consumer wave per query tile and four producer waves, an
 // 8-stage ring (128 KB at d = 128), one work-group per CU.
-template <int D>
+template <int D, bool PG>
 static void launch_attn_pc(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
   constexpr int NP = 4, S = 8;
   switch (qrt) {
-    case 1: attn_pc_kernel<f16_t, D, 1, 1 + NP, NP, S><<<grid, 64 * (1 + NP), 0, s>>>(a); break;
-    case 2: attn_pc_kernel<f16_t, D, 2, 2 + NP, NP, S><<<grid, 64 * (2 + NP), 0, s>>>(a); break;
-    case 3: attn_pc_kernel<f16_t, D, 3, 3 + NP, NP, S><<<grid, 64 * (3 + NP), 0, s>>>(a); break;
-    case 4: attn_pc_kernel<f16_t, D, 4, 4 + NP, NP, S><<<grid, 64 * (4 + NP), 0, s>>>(a); break;
-    case 5: attn_pc_kernel<f16_t, D, 5, 5 + NP, NP, S><<<grid, 64 * (5 + NP), 0, s>>>(a); break;
+    case 1: attn_pc_kernel<f16_t, D, 1, 1 + NP, NP, S, PG><<<grid, 64 * (1 + NP), 0, s>>>(a); break;
+    case 2: attn_pc_kernel<f16_t, D, 2, 2 + NP, NP, S, PG><<<grid, 64 * (2 + NP), 0, s>>>(a); break;
+    case 3: attn_pc_kernel<f16_t, D, 3, 3 + NP, NP, S, PG><<<grid, 64 * (3 + NP), 0, s>>>(a); break;
+    case 4: attn_pc_kernel<f16_t, D, 4, 4 + NP, NP, S, PG><<<grid, 64 * (4 + NP), 0, s>>>(a); break;
+    case 5: attn_pc_kernel<f16_t, D, 5, 5 + NP, NP, S, PG><<<grid, 64 * (5 + NP), 0, s>>>(a); break;
   }
 }
 
@@ -778,12 +778,14 @@ void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, i
 }
 
 void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStream_t s) {
+  // the paged cache has instantiations of its own: its page cursor stays out of the contiguous kernels
+  const bool pg = a.page_table != nullptr;
   if (dtype == DT_BF16) {
-    if (D == 128) launch_attn_pc<128>(a, qrt, grid, s);
-    else launch_attn_pc<64>(a, qrt, grid, s);
+    if (D == 128) pg ? launch_attn_pc<128, true>(a, qrt, grid, s) : launch_attn_pc<128, false>(a, qrt, grid, s);
+    else pg ? launch_attn_pc<64, true>(a, qrt, grid, s) : launch_attn_pc<64, false>(a, qrt, grid, s);
   } else {
-    if (D == 128) launch_attn_t<float, 128>(a, qrt, grid, s);
-    else launch_attn_t<float, 64>(a, qrt, grid, s);
+    if (D == 128) pg ? launch_attn_t<float, 128, true>(a, qrt, grid, s) : launch_attn_t<float, 128, false>(a, qrt, grid, s);
+    else pg ? launch_attn_t<float, 64, true>(a, qrt, grid, s) : launch_attn_t<float, 64, false>(a, qrt, grid, s);
   }
 }
 
