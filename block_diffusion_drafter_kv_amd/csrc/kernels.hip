@@ -86,15 +86,17 @@ __device__ __forceinline__ float4 load4f(const bf16_t* p) {
 // out[o] = x * rsqrt(mean(x^2) + eps) * gain, x = X row (map_mask ? (o / K) * R + 1 + o % K : o).
 // Rows at or past (*n_valid - valid_base) are skipped when n_valid is given.
 template <typename C>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(int n_rows, int H, const float* X, int map_mask, int K, int R,
+__global__ __launch_bounds__(64) void rmsnorm_kernel(int n_rows, int H, const float* X, int map_mask, int K, int R,
                                                        const typename WeightOf<C>::type* gain, C* h_out, float eps,
                                                        const int32_t* n_valid, int valid_base) {
-  const int o = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // one wave per row; work-groups of one wave spread a few hundred rows over every CU
+  const int o = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (o >= n_rows) return;
   if (n_valid && o >= *n_valid - valid_base) return;
   const int src = map_mask ? (o / K) * R + 1 + (o % K) : o;
   const float* x = X + (int64_t)src * H;
   float ss = 0.f;
+#pragma unroll 4
   for (int c = lane * 4; c < H; c += 256) {
     const float4 v = load4f(x + c);
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
@@ -102,6 +104,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int n_rows, int H, const f
   ss = wave_sum(ss);
   const float rs = rsqrtf(ss / (float)H + eps);
   C* y = h_out + (int64_t)o * H;
+#pragma unroll 4
   for (int c = lane * 4; c < H; c += 256) {
     const float4 v = load4f(x + c), gn = load4f(gain + c);
     store4(y + c, v.x * rs * gn.x, v.y * rs * gn.y, v.z * rs * gn.z, v.w * rs * gn.w);
@@ -1425,12 +1428,12 @@ __global__ __launch_bounds__(64) void rejection_sparse_kernel(int K, int kp, int
 // is rounded to the operand type once.  One work-group per row.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void dyn_conv_kernel(int M, int R, int H, int G, const float* X,
+__global__ __launch_bounds__(64) void dyn_conv_kernel(int M, int R, int H, int G, const float* X,
                                                         const typename WeightOf<T>::type* gain, float eps,
                                                         const float* corr, const typename WeightOf<T>::type* base,
                                                         T* y) {
-  // one wave per row, four rows per work-group (as the RMSNorm kernel)
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // one wave per row (as the RMSNorm kernel), one row per work-group
+  const int m = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (m >= M) return;
   const bool first = m % R == 0;
   const int ng = H / G;
@@ -1935,12 +1938,12 @@ void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int
 void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, int K, int R, const void* gain,
                     void* h_out, float eps, hipStream_t s, const int32_t* n_valid, int valid_base) {
   if (n_rows <= 0) return;
-  const int grid = cdiv(n_rows, 4);
+  const int grid = n_rows;   // one 64-thread work-group per row
   if (dtype == DT_BF16)
-    rmsnorm_kernel<f16_t><<<grid, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, (const bf16_t*)gain, (f16_t*)h_out, eps,
+    rmsnorm_kernel<f16_t><<<grid, 64, 0, s>>>(n_rows, H, X, map_mask, K, R, (const bf16_t*)gain, (f16_t*)h_out, eps,
                                                 n_valid, valid_base);
   else
-    rmsnorm_kernel<float><<<grid, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, (const float*)gain, (float*)h_out, eps,
+    rmsnorm_kernel<float><<<grid, 64, 0, s>>>(n_rows, H, X, map_mask, K, R, (const float*)gain, (float*)h_out, eps,
                                                 n_valid, valid_base);
 }
 
@@ -2084,10 +2087,10 @@ void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, 
 void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const void* gain, float eps,
                      const float* corr, const void* base, void* y, hipStream_t s) {
   if (dtype == DT_BF16)
-    dyn_conv_kernel<f16_t><<<cdiv(M, 4), 256, 0, s>>>(M, R, H, G, X, (const bf16_t*)gain, eps, corr,
+    dyn_conv_kernel<f16_t><<<M, 64, 0, s>>>(M, R, H, G, X, (const bf16_t*)gain, eps, corr,
                                                        (const bf16_t*)base, (f16_t*)y);
   else
-    dyn_conv_kernel<float><<<cdiv(M, 4), 256, 0, s>>>(M, R, H, G, X, (const float*)gain, eps, corr,
+    dyn_conv_kernel<float><<<M, 64, 0, s>>>(M, R, H, G, X, (const float*)gain, eps, corr,
                                                        (const float*)base, (float*)y);
 }
 
