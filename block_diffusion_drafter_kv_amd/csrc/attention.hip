@@ -698,7 +698,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
 
 // One work-group per (request, kv head and q-row part, block of 16 rows): each
 // thread owns one row and D/16 consecutive head dims and merges the segment's
-// chunk records in order (max first, then the rescaled sums).
+// chunk records in order in one pass (running max, earlier sums rescaled).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs a) {
   constexpr int EPT = D / 16;
@@ -712,26 +712,43 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs
   const int cg = attn_chunk_groups(len, a.chunk_min, a.chunk_max);
   const int n = (len + cg - 1) / cg;
   const int64_t p0 = a.chunk_base[seg];
-  float M = -INFINITY;
-  for (int c = 0; c < n; ++c) M = fmaxf(M, a.m_part[(p0 + c) * a.QRT16 + row]);
-  float L = 0.f;
+  // one pass, four chunk records' loads issued together; the running max rescales what came before
+  float M = -INFINITY, L = 0.f;
   float O[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; ++i) O[i] = 0.f;
-  for (int c = 0; c < n; ++c) {
-    const int64_t b = p0 + c;
-    const float m = a.m_part[b * a.QRT16 + row];
-    if (m == -INFINITY) continue;
-    const float wgt = exp2f(m - M);
-    L += a.l_part[b * a.QRT16 + row] * wgt;
-    const float4* op = (const float4*)(a.o_part + (b * a.QRT16 + row) * D + e0);
+  for (int c0 = 0; c0 < n; c0 += 4) {
+    float mc[4], lc[4];
+    float4 oc[4][EPT / 4];
 #pragma unroll
-    for (int i = 0; i < EPT / 4; ++i) {
-      const float4 v = op[i];
-      O[4 * i] += v.x * wgt;
-      O[4 * i + 1] += v.y * wgt;
-      O[4 * i + 2] += v.z * wgt;
-      O[4 * i + 3] += v.w * wgt;
+    for (int u = 0; u < 4; ++u) {
+      const int64_t b = p0 + min(c0 + u, n - 1);
+      mc[u] = c0 + u < n ? a.m_part[b * a.QRT16 + row] : -INFINITY;
+      lc[u] = a.l_part[b * a.QRT16 + row];
+      const float4* op = (const float4*)(a.o_part + (b * a.QRT16 + row) * D + e0);
+#pragma unroll
+      for (int i = 0; i < EPT / 4; ++i) oc[u][i] = op[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float m = mc[u];
+      if (m == -INFINITY) continue;
+      if (m > M) {
+        const float sc = exp2f(M - m);   // 0 while M is -inf
+        L *= sc;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) O[i] *= sc;
+        M = m;
+      }
+      const float wgt = exp2f(m - M);
+      L += lc[u] * wgt;
+#pragma unroll
+      for (int i = 0; i < EPT / 4; ++i) {
+        O[4 * i] += oc[u][i].x * wgt;
+        O[4 * i + 1] += oc[u][i].y * wgt;
+        O[4 * i + 2] += oc[u][i].z * wgt;
+        O[4 * i + 3] += oc[u][i].w * wgt;
+      }
     }
   }
   const float inv = 1.0f / L;
