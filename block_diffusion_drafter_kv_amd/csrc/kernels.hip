@@ -766,16 +766,16 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(int V, const float* x,
   const float* row = x + m * V;
   float best = -INFINITY;
   int arg = 0x7fffffff;
-  if ((V & 3) == 0) {   // 16-byte loads, 4 in flight per thread; ids increase along each thread's walk
+  if ((V & 3) == 0) {   // 16-byte loads, 8 in flight per thread; ids increase along each thread's walk
     const float4* r4 = (const float4*)row;
     const int V4 = V >> 2;
     int c = threadIdx.x;
-    for (; c + 768 < V4; c += 1024) {
-      float4 q[4];
+    for (; c + 1792 < V4; c += 2048) {
+      float4 q[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) q[u] = r4[c + 256 * u];
+      for (int u = 0; u < 8; ++u) q[u] = r4[c + 256 * u];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int b = 4 * (c + 256 * u);
         if (q[u].x > best) { best = q[u].x; arg = b; }
         if (q[u].y > best) { best = q[u].y; arg = b + 1; }
