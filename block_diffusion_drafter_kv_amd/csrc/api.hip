@@ -86,8 +86,7 @@ struct dflash_handle {
   // symmetric sampling truncation (dflash_set_sampling)
   int trunc_k = 0;
   float trunc_p = 1.f;
-  float *vt_max = nullptr, *vt_sum = nullptr, *vrow_max = nullptr, *vrow_lse = nullptr;
-  int32_t* vt_arg = nullptr;
+  float *vt_max = nullptr, *vrow_max = nullptr, *vrow_lse = nullptr;   // tile maxima, row max / log-sum
   int32_t *tr_ids = nullptr, *kp_ids = nullptr;
   float *tr_probs = nullptr, *kp_probs = nullptr;
   // verification
@@ -438,8 +437,6 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     {   // truncation scratch: rows of a verification (K+1 target and K draft rows per request)
       const size_t vrows = (size_t)c.max_batch * (2 * c.max_k + 1);
       if ((rc = alloc_t(h, &h->vt_max, vrows * h->n_vtiles, 4))) break;
-      if ((rc = alloc_t(h, &h->vt_sum, vrows * h->n_vtiles, 4))) break;
-      if ((rc = alloc_t(h, &h->vt_arg, vrows * h->n_vtiles, 4))) break;
       if ((rc = alloc_t(h, &h->vrow_max, vrows, 4))) break;
       if ((rc = alloc_t(h, &h->vrow_lse, vrows, 4))) break;
       if ((rc = alloc_t(h, &h->tr_ids, vrows * 64, 4))) break;

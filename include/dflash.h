@@ -285,7 +285,9 @@ int dflash_set_sampling(dflash_handle* h, int32_t top_k, float top_p);
  * Philox(seed; a+1, slot, step, 2); an exhausted residual (mass < 2^-20)
  * falls back to p.  Outputs (device): out_tokens [n_req, K+1] (unused -1),
  * out_len [n_req] = a+1, accept_len [n_req] = a.  Does not touch the cache:
- * inject the a+1 committed rows next (row_count = out_len on the device). */
+ * inject the a+1 committed rows next (row_count = out_len on the device).
+ * temperature > 0 needs vocab <= 2^21 (DFLASH_E_CAPACITY otherwise: the draw
+ * keeps one float per 256 ids in LDS); draft_logits and slots must be given. */
 int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, const int32_t* slots,
                   const int32_t* draft_ids, const float* draft_logits, const float* target_logits,
                   float temperature, uint64_t seed, uint64_t step, int32_t* out_tokens, int32_t* out_len,
@@ -301,7 +303,7 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
  * first rejection draw from max(0, p - q_full) renormalised (from p when that
  * mass is below 2^-20) with Philox(seed; i, slot, step, 2); after K acceptances
  * the bonus from p_K.  temperature 0: the greedy prefix match of dflash_verify.
- * Outputs as dflash_verify. */
+ * Outputs and the vocabulary limit as dflash_verify. */
 int dflash_verify_subset(dflash_handle* h, void* stream, int32_t n_req, int32_t K, int32_t C, const int32_t* slots,
                          const int32_t* draft_ids, const int32_t* cand_ids, const float* cand_probs,
                          const float* target_logits, float temperature, uint64_t seed, uint64_t step,
@@ -389,7 +391,8 @@ int dflash_ctx_lens(dflash_handle* h, void* stream, int32_t* out_dev);
 
 /* Copy cache positions [start, start+n) of (layer, slot) as K and V, each
  * [n, n_kv_heads, head_dim] in the cache element type (fp32, or fp16 for a
- * bf16 drafter), to device buffers k_out / v_out. */
+ * bf16 drafter), to device buffers k_out / v_out.  Paged cache: positions in
+ * unmapped pages read as 0. */
 int dflash_copy_cache(dflash_handle* h, void* stream, int32_t layer, int32_t slot, int32_t start, int32_t n,
                       void* k_out, void* v_out);
 
