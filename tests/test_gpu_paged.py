@@ -46,7 +46,7 @@ def _shuffled_table(max_batch, per_slot, n_pages, seed):
 
 
 @pytest.mark.parametrize("cfg", [TINY, SMALL_BF16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("page", [32, 64, 160])
+@pytest.mark.parametrize("page", [32, 64, 160, 512])   # 512: one page holds a slot's whole context
 def test_paged_matches_contiguous(gpu_lib, cfg, page):
     mb, max_ctx, K = 3, 400, 8
     per_slot = -(-max_ctx // page)
@@ -98,6 +98,32 @@ def test_paged_logits_match_oracle(gpu_lib, cfg):
     for i, (s, a) in enumerate(zip([1, 0], [9, 44])):
         assert_close_report(z[i], orc.block_logits(s, a, K), atol=TOL[cfg.dtype], what=f"paged logits req {i}")
     assert dp.get_error() == 0
+    dp.close()
+
+
+def test_paged_shared_prefix_page(gpu_lib):
+    """Two slots whose first page is the same physical page (a common prefix, as an engine's
+    prefix cache shares it): both inject the same prefix rows, then their own rows; logits are
+    bit-identical to a contiguous handle holding the two contexts separately."""
+    cfg = SMALL_BF16
+    mb, max_ctx, K, page = 3, 256, 6, 128
+    dc, _, _ = make_pair(cfg, max_batch=mb, max_ctx=max_ctx, max_k=K)
+    dp, _, _ = make_pair(cfg, max_batch=mb, max_ctx=max_ctx, max_k=K, page_size=page, num_pages=6)
+    dp.set_page_table(_dev([[5, 1], [5, 2], [3, 4]]))
+    prefix = gen.hidden_rows(cfg, 0, 0, page, seed=31)
+    own0 = gen.hidden_rows(cfg, 0, page, 72, seed=32)
+    own1 = gen.hidden_rows(cfg, 1, page, 60, seed=33)
+    for d in (dc, dp):
+        rows = torch.cat([prefix, own0, prefix, own1], dim=0).cuda().contiguous()
+        d.inject(_dev([0, 1]), _dev([0, page + 72]), _dev([page + 72, page + 60]), 2 * page + 132, rows)
+    anchors = [11, 11]
+    oc = dc.draft(_dev([0, 1]), _dev(anchors), K, want_logits=True)
+    op = dp.draft(_dev([0, 1]), _dev(anchors), K, want_logits=True)
+    torch.cuda.synchronize()
+    assert torch.equal(oc["logits"], op["logits"])
+    assert not torch.equal(op["logits"][0], op["logits"][1])   # the own rows differ
+    assert dc.get_error() == 0 and dp.get_error() == 0
+    dc.close()
     dp.close()
 
 
