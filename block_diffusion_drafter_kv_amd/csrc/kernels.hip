@@ -32,6 +32,25 @@ __global__ void rope_table_kernel(float2* table, int n_pos, int d, double theta)
   table[idx] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
+// Four values of one row, gain-scaled and stored as one 8- or 16-byte write.
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
+  bf16_t v[4] = {(bf16_t)a, (bf16_t)b, (bf16_t)c, (bf16_t)d};
+  *(uint2*)p = *(const uint2*)v;
+}
+__device__ __forceinline__ void store4(f16_t* p, float a, float b, float c, float d) {
+  f16_t v[4] = {(f16_t)a, (f16_t)b, (f16_t)c, (f16_t)d};
+  *(uint2*)p = *(const uint2*)v;
+}
+__device__ __forceinline__ float4 load4f(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 load4f(const bf16_t* p) {
+  const uint2 u = *(const uint2*)p;
+  const bf16_t* v = (const bf16_t*)&u;
+  return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+
 // ---------------------------------------------------------------------------
 // Block embedding [P2 §2.2; P4 §4]: row r*R + j holds the anchor (j = 0) or the
 // mask token (j >= 1), embedded and scaled; then the first layer's RMSNorm.
@@ -51,36 +70,38 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* a
     id = 0;
   }
   const auto* e = (j > 0 && mask_emb) ? mask_emb : embed + (int64_t)id * H;
+  float* xr = X + (int64_t)m * H;
+  C* hr = h_out + (int64_t)m * H;
+  // four elements per access when the caller's rows allow it (H is a multiple of 128)
+  constexpr uintptr_t A4 = 4 * sizeof(*e) - 1;
+  const bool vec = (((uintptr_t)e | (uintptr_t)gain) & A4) == 0;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < H; c += 256) {
-    const float v = to_f32(e[c]) * scale;
-    X[(int64_t)m * H + c] = v;
-    ss += v * v;
+  if (vec) {
+    for (int c = threadIdx.x * 4; c < H; c += 1024) {
+      const float4 v = load4f(e + c);
+      const float4 x = make_float4(v.x * scale, v.y * scale, v.z * scale, v.w * scale);
+      *(float4*)(xr + c) = x;
+      ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+    }
+  } else {
+    for (int c = threadIdx.x; c < H; c += 256) {
+      const float v = to_f32(e[c]) * scale;
+      xr[c] = v;
+      ss += v * v;
+    }
   }
   ss = block_sum(ss, red);
   const float rs = rsqrtf(ss / (float)H + eps);
-  for (int c = threadIdx.x; c < H; c += 256)
-    h_out[(int64_t)m * H + c] = from_f32<C>(X[(int64_t)m * H + c] * rs * to_f32(gain[c]));
+  if (vec) {
+    for (int c = threadIdx.x * 4; c < H; c += 1024) {
+      const float4 x = *(const float4*)(xr + c), g = load4f(gain + c);
+      store4(hr + c, x.x * rs * g.x, x.y * rs * g.y, x.z * rs * g.z, x.w * rs * g.w);
+    }
+  } else {
+    for (int c = threadIdx.x; c < H; c += 256) hr[c] = from_f32<C>(xr[c] * rs * to_f32(gain[c]));
+  }
 }
 
-// Four values of one row, gain-scaled and stored as one 8- or 16-byte write.
-__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
-  *(float4*)p = make_float4(a, b, c, d);
-}
-__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
-  bf16_t v[4] = {(bf16_t)a, (bf16_t)b, (bf16_t)c, (bf16_t)d};
-  *(uint2*)p = *(const uint2*)v;
-}
-__device__ __forceinline__ void store4(f16_t* p, float a, float b, float c, float d) {
-  f16_t v[4] = {(f16_t)a, (f16_t)b, (f16_t)c, (f16_t)d};
-  *(uint2*)p = *(const uint2*)v;
-}
-__device__ __forceinline__ float4 load4f(const float* p) { return *(const float4*)p; }
-__device__ __forceinline__ float4 load4f(const bf16_t* p) {
-  const uint2 u = *(const uint2*)p;
-  const bf16_t* v = (const bf16_t*)&u;
-  return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
-}
 
 // RMSNorm of fp32 rows, one wave per row (H a multiple of 4):
 // out[o] = x * rsqrt(mean(x^2) + eps) * gain, x = X row (map_mask ? (o / K) * R + 1 + o % K : o).
