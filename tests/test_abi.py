@@ -55,3 +55,15 @@ def test_status_strings_and_host_validation_without_gpu():
                                    None) == -1
     assert dk.load().dflash_profile(None, 1) == -1
     assert dk.load().dflash_draft_block(None, None, 1, None, None, None, None) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The path runs on one GPU (requests shard across GPUs with no exchange): bench.py --gpus 2 exits
+    with status 2 and says so, before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300, env=dict(os.environ, HIP_VISIBLE_DEVICES=""))
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
