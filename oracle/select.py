@@ -116,18 +116,24 @@ def select_block(z: np.ndarray, T: float, top_k: int, seed: int, slot: int, step
     m, lse = row_stats(z, T)
     draft = np.zeros(K, dtype=np.int64)
     margin = np.zeros(K)
+    uniforms = np.full(K, np.nan)
+    weights = []               # the distribution each draw was taken from (truncated if asked)
     for j in range(K):
         if T <= 0:
             draft[j], margin[j] = argmax_with_margin(z[j])
+            weights.append(None)
         else:
             u = float(philox.uniform(seed, slot, step, j + 1, philox.PURPOSE_DRAFT))
+            uniforms[j] = u
             qj = q[j]
             mt = np.inf
             if trunc_k > 0 or trunc_p < 1.0:
                 qj, _, mt = truncate(q[j], trunc_k, trunc_p)
             draft[j], margin[j] = inverse_cdf(qj, u)
             margin[j] = min(margin[j], mt)
-    out = {"draft_ids": draft, "margins": margin, "row_max": m, "row_lse": lse, "probs": q}
+            weights.append(qj)
+    out = {"draft_ids": draft, "margins": margin, "row_max": m, "row_lse": lse, "probs": q,
+           "uniforms": uniforms, "draw_weights": weights}
     if top_k > 0:
         tid = np.stack([topk(z[j], top_k) for j in range(K)])
         out["topk_ids"] = tid

@@ -98,10 +98,13 @@ def verify_rejection(draft_ids, draft_logits, target_logits, T, seed, slot, step
     near = min(mp, mq)
     a = 0
     out = []
+    tests = []                 # (relative margin of accept test i, accepted) for i = 1..
     for i in range(1, K + 1):
         pi, qi = p[i - 1][d[i - 1]], q[i - 1][d[i - 1]]
         u = uniform_fn(i, philox.PURPOSE_ACCEPT)
-        near = min(near, abs(u * qi - pi) / max(pi, qi, 1e-300))
+        m_i = abs(u * qi - pi) / max(pi, qi, 1e-300)
+        near = min(near, m_i)
+        tests.append((m_i, bool(u * qi < pi)))
         if u * qi < pi:
             out.append(int(d[i - 1]))
             a += 1
@@ -116,13 +119,15 @@ def verify_rejection(draft_ids, draft_logits, target_logits, T, seed, slot, step
         near = min(near, m2)
         out.append(c)
         return {"out_tokens": np.array(out, dtype=np.int64), "out_len": a + 1, "accept_len": a,
-                "near_margin": near, "fallback": bool(rs < RESIDUAL_EPS)}
+                "near_margin": near, "fallback": bool(rs < RESIDUAL_EPS), "tests": tests,
+                "draw_weights": w, "draw_u": u2, "draw_margin": m2}
     u2 = uniform_fn(K + 1, philox.PURPOSE_RESAMPLE)
     c, m2 = inverse_cdf(p[K], u2)
     near = min(near, m2)
     out.append(c)
     return {"out_tokens": np.array(out, dtype=np.int64), "out_len": K + 1, "accept_len": K,
-            "near_margin": near, "fallback": False}
+            "near_margin": near, "fallback": False, "tests": tests, "draw_weights": p[K], "draw_u": u2,
+            "draw_margin": m2}
 
 
 def verify_tree_walk(tree_tokens, tree_parents, target_logits, T, seed=0, slot=0, step=0, uniform_fn=None):
@@ -135,7 +140,9 @@ def verify_tree_walk(tree_tokens, tree_parents, target_logits, T, seed=0, slot=0
 
     Returns dict: out_tokens (accepted tokens, then the stopping token),
     path (node indices of the accepted path, root first), out_len = a + 1,
-    accept_len = a, near_margin (smallest decision margin along the walk).
+    accept_len = a, near_margin (smallest decision margin along the walk),
+    steps (per walk step: the node's distribution weights -- logits for greedy,
+    probabilities for T > 0 --, the uniform or None, the pick and its margin).
     """
     if uniform_fn is None:
         def uniform_fn(position, purpose):
@@ -150,12 +157,16 @@ def verify_tree_walk(tree_tokens, tree_parents, target_logits, T, seed=0, slot=0
             children.setdefault(int(par[c]), {})
             assert int(tok[c]) not in children[int(par[c])], "siblings must carry distinct tokens"
             children[int(par[c])][int(tok[c])] = c
-    u_node, depth, out, path, near = 0, 0, [], [0], np.inf
+    u_node, depth, out, path, near, steps = 0, 0, [], [0], np.inf, []
     while True:
         if T <= 0:
             pick, m = argmax_with_margin(t[u_node])
+            steps.append((t[u_node], None, pick, m))
         else:
-            pick, m = inverse_cdf(softmax(t[u_node], T), uniform_fn(depth + 1, philox.PURPOSE_TREE_WALK))
+            w = softmax(t[u_node], T)
+            u = uniform_fn(depth + 1, philox.PURPOSE_TREE_WALK)
+            pick, m = inverse_cdf(w, u)
+            steps.append((w, u, pick, m))
         near = min(near, m)
         out.append(pick)
         nxt = children.get(u_node, {}).get(pick)
@@ -165,7 +176,7 @@ def verify_tree_walk(tree_tokens, tree_parents, target_logits, T, seed=0, slot=0
         path.append(nxt)
     a = len(out) - 1
     return {"out_tokens": np.array(out, dtype=np.int64), "path": np.array(path, dtype=np.int64),
-            "out_len": a + 1, "accept_len": a, "near_margin": near}
+            "out_len": a + 1, "accept_len": a, "near_margin": near, "steps": steps}
 
 
 def subset_to_full(cand_ids, cand_probs, V):

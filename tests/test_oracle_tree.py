@@ -1,4 +1,9 @@
-"""Pins for the best-first prefix tree [P5 §2.1-2.3, §3.3] by brute force on tiny vocabularies."""
+"""Pins for the best-first prefix tree [P5 §2.1-2.3, §3.3] by brute force on tiny vocabularies.
+
+The brute force does not share the heap's arithmetic: a prefix's probability is
+the marginal of the factorised law, summed over every full sequence that starts
+with it, and the top-B are read off a plain sort of every prefix.
+"""
 import itertools
 
 import numpy as np
@@ -29,8 +34,12 @@ def test_heap_equals_brute_force_top_b(L, V, B, seed):
     Kc = min(B, V)
     probs, ids = _candidates(z, q, Kc)
     tok, par, dep, pri = ot.build_tree(probs, ids, B)
-    allp = ot.all_prefix_probs_fp32(probs)
-    order = sorted(allp, key=lambda r: _key(allp[r], r))[:B]
+    allp = ot.all_prefix_probs(q, ids)
+    ranked = sorted(allp, key=lambda r: _key(allp[r], r))
+    vals = np.array([allp[r] for r in ranked[:B + 1]])
+    # no two of the first B + 1 within rounding of each other: the order below is unique
+    assert np.all(vals[:-1] - vals[1:] > 1e-12 * vals[:-1])
+    order = ranked[:B]
     # the heap pops exactly the brute-force order
     paths = {}
     got = []
@@ -65,7 +74,7 @@ def test_prop2_top_b_prefixes_are_prefix_closed(seed):
     L, V = 3, 4
     z, q = _marginals(L, V, seed + 20)
     probs, ids = _candidates(z, q, V)
-    allp = ot.all_prefix_probs_fp32(probs)
+    allp = ot.all_prefix_probs(q, ids)
     ranked = sorted(allp, key=lambda r: _key(allp[r], r))
     for B in range(1, len(ranked) + 1):
         top = set(ranked[:B])
@@ -106,3 +115,35 @@ def test_mask_is_reflexive_transitive_closure_plus_root():
     for i in range(n):
         for j in range(n):
             assert bool((int(bits[i, j // 64]) >> (j % 64)) & 1) == m[i, j]
+
+
+def test_priorities_are_fp64_prefix_probabilities():
+    """Each popped node's priority equals its prefix's marginal probability to fp64
+    rounding (an fp32 product would be off by ~1e-7 relative)."""
+    z, q = _marginals(4, 5, 50, sharp=1.3)
+    probs, ids = _candidates(z, q, 5)
+    tok, par, dep, pri = ot.build_tree(probs, ids, 30)
+    allp = ot.all_prefix_probs(q, ids)
+    rank_of = [{int(t): r + 1 for r, t in enumerate(ids[i])} for i in range(ids.shape[0])]
+    rho = {0: ()}
+    for i in range(1, len(tok)):
+        rho[i] = rho[par[i]] + (rank_of[dep[i] - 1][int(tok[i])],)
+        assert abs(pri[i - 1] - allp[rho[i]]) <= 1e-14 * allp[rho[i]]
+
+
+def test_ties_and_near_ties_are_flagged():
+    """Exact ties follow the stated order (larger P, shallower, smaller rank tuple),
+    and near_ties names the set boundary and the adjacent pops within the margin."""
+    q = np.array([[0.4, 0.4, 0.2], [0.5, 0.3, 0.2]])
+    ids = np.array([[0, 1, 2], [0, 1, 2]])
+    tok, par, dep, pri, front = ot.build_tree(q, ids, 3, with_frontier=True)
+    # (1,) and (2,) tie at 0.4: rank tuple (1,) first; then (1,1) and (2,1) tie at 0.2
+    # with (3,) = 0.2 (shallower, taken third); the frontier is the next 0.2
+    assert list(tok[1:]) == [0, 1, 2] and list(dep[1:]) == [1, 1, 1]
+    assert front == pytest.approx(0.2)
+    set_tie, order = ot.near_ties(pri, front, 1e-9)
+    assert set_tie and order == [1]
+    # well separated priorities: nothing flagged
+    q2 = np.array([[0.7, 0.2, 0.1], [0.6, 0.3, 0.1]])
+    _, _, _, pri2, front2 = ot.build_tree(q2, ids, 3, with_frontier=True)
+    assert ot.near_ties(pri2, front2, 1e-6) == (False, [])
