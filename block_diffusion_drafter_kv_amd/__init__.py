@@ -74,6 +74,8 @@ _SIGS = {
                                    POINTER(dflash_draft_params), POINTER(dflash_draft_outputs)], c_int32),
     "dflash_verify": ([c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
                        c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
+    "dflash_verify_noalloc": ([c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
+                               c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
     "dflash_verify_tree": ([c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_float, c_uint64, c_uint64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p], c_int32),
     "dflash_inject_tree_path": ([c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int64,
@@ -158,6 +160,12 @@ def dflash_verify(h, stream, n_req, K, slots, draft_ids, draft_logits, target_lo
                   out_tokens, out_len, accept_len, next_anchor=None):
     return _call("dflash_verify", h, stream, n_req, K, slots, draft_ids, draft_logits, target_logits, temperature,
                  seed, step, out_tokens, out_len, accept_len, next_anchor)
+
+
+def dflash_verify_noalloc(stream, n_req, K, vocab, slots, draft_ids, draft_logits, target_logits, temperature, seed,
+                          step, out_tokens, out_len, accept_len, next_anchor=None):
+    return _call("dflash_verify_noalloc", stream, n_req, K, vocab, slots, draft_ids, draft_logits, target_logits,
+                 temperature, seed, step, out_tokens, out_len, accept_len, next_anchor)
 
 
 def dflash_verify_tree(h, stream, n_req, K, n_nodes, slots, tree_tokens, tree_parents, target_logits, temperature,

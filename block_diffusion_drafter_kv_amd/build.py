@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash_amd.so")
-SOURCES = ["api.hip", "kernels.hip", "attention.hip", "gemm_bf16.hip", "gemm_f16.hip", "gemm_f32.hip"]
+SOURCES = ["api.hip", "kernels.hip", "attention.hip", "gemm_bf16.hip", "gemm_f16.hip", "gemm_f32.hip",
+           "noalloc.hip"]
 ARCH = os.environ.get("DFLASH_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include")]

@@ -295,6 +295,23 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
 /* next_anchor [n_req] (device, or NULL) receives out_tokens[r][out_len[r]-1]: the
  * token that anchors the next block [P4 §4.2; P1 "核心推理伪代码"]. */
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops or harnesses that forbid hipMalloc): the verification of
+ * dflash_verify without a handle.  Same arguments, outputs, Philox streams and
+ * results as dflash_verify on a handle of this vocabulary, except: the
+ * vocabulary is passed here; no top-k / top-p truncation (as after
+ * dflash_set_sampling(h, 0, 1)); draft ids outside [0, vocab) are rejected
+ * without an error bit (there is no error word).  Its scratch (about 2.3 MB)
+ * is one static array per GPU, resolved on the first call on each device and
+ * kept until the process ends; nothing is allocated.  Limits: n_req <= 256,
+ * 1 <= K <= 31, vocab <= 262144 (DFLASH_E_CAPACITY beyond).  Every call on a
+ * GPU uses that GPU's one array: calls that may overlap on one GPU (different
+ * streams without ordering) race and must not be made. */
+int dflash_verify_noalloc(void* stream, int32_t n_req, int32_t K, int32_t vocab, const int32_t* slots,
+                          const int32_t* draft_ids, const float* draft_logits, const float* target_logits,
+                          float temperature, uint64_t seed, uint64_t step, int32_t* out_tokens, int32_t* out_len,
+                          int32_t* accept_len, int32_t* next_anchor);
+
 /* Rejection verification of a selector draft [P2 §3.1.3, §4.2]: the drafter's
  * distribution at position i is given over C candidates (cand_ids / cand_probs
  * [n_req, K, C], device; C <= 64), projected onto token ids (q_full(v) = summed
