@@ -485,6 +485,197 @@ def tree_verify_measure(reps=20):
             "target_rows_bytes_if_all_read": B * nn * V * 4, **out}
 
 
+def _draft_bytes_flops(cfg, B, K, sum_ctx):
+    """Algorithmic bytes (weights once, context K/V once per layer) and flops of one draft step."""
+    R = K + 1
+    w = phase_work(cfg, B, K, sum_ctx)
+    nbytes = w["_weights_bytes"][1] + w["attn"][1] * cfg.n_layers
+    layer_flops = w["qkv"][1] + w["o"][1] + w["gate_up"][1] + w["down"][1]
+    attn_flops = 4.0 * cfg.n_q_heads * R * cfg.head_dim * (sum_ctx + B * R)
+    flops = cfg.n_layers * (layer_flops + attn_flops) + w["lm_head"][1]
+    return nbytes, flops
+
+
+def _fill_prompts(dr, cfg, ctx, seed, chunk=8192):
+    """Untimed prompt injection of every request (rows N(0,1) drawn on the GPU)."""
+    import numpy as np
+    import torch
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    for r, c in enumerate(ctx):
+        for s0 in range(0, c, chunk):
+            n = min(chunk, c - s0)
+            rows = torch.randn((n, cfg.n_target_layers, cfg.target_hidden), generator=g, device="cuda",
+                               dtype=torch.float32).to(torch.bfloat16)
+            dr.inject(i32([r]), i32([0]), i32([n]), n, rows)
+
+
+def _loop(dr, cfg, B, K, steps, temperature, sigma, seed, pool_seed, warmup=2):
+    """The decode cycle chained on the device, as in main(): inject the out_len committed rows of each
+    request, draft at the next anchor, synthetic target (drafter logits + sigma N(0,1), not timed),
+    verify (greedy, or rejection sampling at `temperature`).  Per-call medians (us), mean out_len."""
+    import numpy as np
+    import torch
+    import ctypes
+    import block_diffusion_drafter_kv_amd as dk
+    R = K + 1
+    V = cfg.vocab
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(pool_seed)
+    pool = torch.randn((B * R, cfg.n_target_layers, cfg.target_hidden), generator=g, device="cuda",
+                       dtype=torch.float32).to(torch.bfloat16)
+    slots, row_start = i32(np.arange(B)), i32(np.arange(B) * R)
+    logits = torch.empty((B, K, V), dtype=torch.float32, device="cuda")
+    target = torch.empty((B, R, V), dtype=torch.float32, device="cuda")
+    vout = {"out_tokens": torch.empty((B, R), dtype=torch.int32, device="cuda"), "out_len": i32(np.ones(B)),
+            "accept_len": torch.empty((B,), dtype=torch.int32, device="cuda"),
+            "next_anchor": i32(np.random.default_rng(3).integers(0, V - 1, B))}
+    stream = torch.cuda.current_stream()
+    cs = ctypes.c_void_p(stream.cuda_stream)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks, lens = [], []
+    for i in range(warmup + steps):
+        e = [ev() for _ in range(6)]
+        e[0].record(stream)
+        dr.inject(slots, row_start, vout["out_len"], B * R, pool)
+        e[1].record(stream)
+        o = dr.draft(slots, vout["next_anchor"], K, temperature=temperature, seed=seed, step=i, want_stats=False,
+                     logits_out=logits)
+        e[2].record(stream)
+        dk.dflash_synth_target_logits(cs, B, K, V, logits.data_ptr(), sigma, seed + 1, i, target.data_ptr())
+        e[3].record(stream)
+        dr.verify(slots, o["draft_ids"], logits if temperature > 0 else None, target, temperature=temperature,
+                  seed=seed, step=i, out=vout)
+        e[4].record(stream)
+        if i >= warmup:
+            marks.append(e)
+            lens.append(vout["out_len"].clone())
+    torch.cuda.synchronize()
+    assert dr.get_error() == 0
+    med = lambda a, b: round(statistics.median(m[a].elapsed_time(m[b]) * 1e3 for m in marks), 1)
+    mean_len = float(torch.stack(lens).float().mean().item())
+    inj, dra, ver = med(0, 1), med(1, 2), med(3, 4)
+    return {"steps": steps, "temperature": temperature, "sigma": sigma, "inject_us": inj, "draft_us": dra,
+            "verify_us": ver, "step_us": round(inj + dra + ver, 1), "mean_committed_per_verify": round(mean_len, 3),
+            "committed_tokens_per_s": round(B * mean_len / ((inj + dra + ver) * 1e-6), 1)}
+
+
+def c2_measure(w, steps=20):
+    """Batch 1, context 2048, K = 16, greedy: the weight-streaming draft step."""
+    import numpy as np
+    import torch
+    import block_diffusion_drafter_kv_amd as dk
+    from synth.configs import get_workload
+    wl = get_workload("b1_ctx2k")
+    cfg, B, K = wl.model, wl.batch, wl.K
+    dr = dk.Drafter(cfg, w, max_batch=B, max_ctx=wl.ctx + (steps + 4) * (K + 1) + 64, max_k=K,
+                    max_inject_rows=8192)
+    _fill_prompts(dr, cfg, [wl.ctx], 2025)
+    res = _loop(dr, cfg, B, K, steps, 0.0, wl.sigma, 11, 31)
+    sum_ctx = dr.ctx_lens()[:B].sum().item()
+    nbytes, flops = _draft_bytes_flops(cfg, B, K, sum_ctx)
+    t = res["draft_us"] * 1e-6
+    res.update({"workload": wl.name, "batch": B, "ctx": wl.ctx, "draft_tokens_per_s": round(B * K / t, 1),
+                "draft_algorithmic_bytes": nbytes, "draft_hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                "draft_mfma_frac": round(flops / t / 1e12 / PEAK_16B_TFLOPS, 4)})
+    dr.close()
+    torch.cuda.empty_cache()
+    return res
+
+
+def c4_measure(w, steps=50):
+    """Batch 4: 32768-row prompts injected in one call (timed), then 50 cycles with T = 1 drafting and
+    rejection-sampling verification (Philox seed 99)."""
+    import numpy as np
+    import torch
+    import block_diffusion_drafter_kv_amd as dk
+    from synth.configs import get_workload
+    wl = get_workload("b4_ctx32k")
+    cfg, B, K, C = wl.model, wl.batch, wl.K, wl.ctx
+    N = B * C
+    dr = dk.Drafter(cfg, w, max_batch=B, max_ctx=C + (steps + 4) * (K + 1) + 64, max_k=K, max_inject_rows=N)
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(78)
+    rows = torch.empty((N, cfg.n_target_layers, cfg.target_hidden), dtype=torch.bfloat16, device="cuda")
+    for s0 in range(0, N, 8192):
+        rows[s0:s0 + 8192] = torch.randn((8192, cfg.n_target_layers, cfg.target_hidden), generator=g,
+                                         device="cuda").to(torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    dr.inject(i32(np.arange(B)), i32(np.arange(B) * C), i32(np.full(B, C)), N, rows)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    inject_ms = e0.elapsed_time(e1)
+    del rows
+    torch.cuda.empty_cache()
+    res = _loop(dr, cfg, B, K, steps, wl.temperature, wl.sigma, wl.philox_seed, 32)
+    sum_ctx = dr.ctx_lens()[:B].sum().item()
+    nbytes, flops = _draft_bytes_flops(cfg, B, K, sum_ctx)
+    t = res["draft_us"] * 1e-6
+    inj_flops = 2.0 * N * cfg.feat_dim * cfg.hidden + 2.0 * N * cfg.hidden * cfg.n_layers * 2 * cfg.kv_dim
+    res.update({"workload": wl.name, "batch": B, "prompt": C, "prompt_inject_ms": round(inject_ms, 3),
+                "prompt_inject_mfma_frac": round(inj_flops / (inject_ms * 1e-3) / 1e12 / PEAK_16B_TFLOPS, 4),
+                "draft_tokens_per_s": round(B * K / t, 1), "draft_algorithmic_bytes": nbytes,
+                "draft_hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                "verify_algorithmic_bytes": B * (2 * K + 1) * cfg.vocab * 4})
+    res["verify_hbm_frac"] = round(res["verify_algorithmic_bytes"] / (res["verify_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    dr.close()
+    torch.cuda.empty_cache()
+    return res
+
+
+def c5_measure(steps=10):
+    """The larger drafter (hidden 5120, 64/8 heads, SwiGLU 17408, fc 25600 -> 5120), batch 64 at
+    context 8192: a T = 1 draft with per-position top-64 and the best-first B = 64 tree + mask."""
+    import numpy as np
+    import torch
+    import block_diffusion_drafter_kv_amd as dk
+    from synth.configs import get_workload
+    wl = get_workload("b64_tree")
+    cfg, B, K, C = wl.model, wl.batch, wl.K, wl.ctx
+    w = gpu_weights(cfg, seed=4321)
+    dr = dk.Drafter(cfg, w, max_batch=B, max_ctx=C + 64, max_k=K, max_inject_rows=32768, max_top_k=wl.top_k,
+                    max_tree=wl.tree_budget)
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(79)
+    per = 32768 // C
+    stream = torch.cuda.current_stream()
+    inj_ms = 0.0
+    for r0 in range(0, B, per):
+        rows = torch.randn((per * C, cfg.n_target_layers, cfg.target_hidden), generator=g, device="cuda",
+                           dtype=torch.float32).to(torch.bfloat16)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dr.inject(i32(np.arange(r0, r0 + per)), i32(np.arange(per) * C), i32(np.full(per, C)), per * C, rows)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        inj_ms += e0.elapsed_time(e1)
+        del rows
+    assert dr.get_error() == 0
+    slots = i32(np.arange(B))
+    anchors = i32(np.random.default_rng(5).integers(0, cfg.vocab - 1, B))
+    us = _timed(lambda: dr.draft(slots, anchors, K, temperature=1.0, seed=1, step=0, top_k=wl.top_k,
+                                 tree_budget=wl.tree_budget, want_stats=False), steps)
+    us_plain = _timed(lambda: dr.draft(slots, anchors, K, temperature=1.0, seed=1, step=0, want_stats=False), steps)
+    assert dr.get_error() == 0
+    nbytes, flops = _draft_bytes_flops(cfg, B, K, B * C)
+    N = B * C
+    inj_flops = 2.0 * N * cfg.feat_dim * cfg.hidden + 2.0 * N * cfg.hidden * cfg.n_layers * 2 * cfg.kv_dim
+    dr.close()
+    del w
+    torch.cuda.empty_cache()
+    t = us * 1e-6
+    return {"workload": wl.name, "batch": B, "ctx": C, "hidden": cfg.hidden, "top_k": wl.top_k,
+            "tree_budget": wl.tree_budget, "steps": steps, "draft_topk_tree_us": round(us, 1),
+            "draft_only_us": round(us_plain, 1), "draft_tokens_per_s": round(B * K / t, 1),
+            "draft_algorithmic_bytes": nbytes, "draft_flops": flops,
+            "draft_hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+            "draft_mfma_frac": round(flops / t / 1e12 / PEAK_16B_TFLOPS, 4),
+            "setup_inject_rows": N, "setup_inject_ms": round(inj_ms, 2),
+            "setup_inject_mfma_frac": round(inj_flops / (inj_ms * 1e-3) / 1e12 / PEAK_16B_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -498,6 +689,8 @@ def main():
     ap.add_argument("--no-dflash2", action="store_true", help="skip the DFlash 2 modules measurement")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the causal-mask / sampled / truncated draft and verify measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (batch 1 / batch 4 long context / larger drafter) and the sigma sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -526,7 +719,9 @@ def main():
     dk.load()
     torch.cuda.set_device(0)
     ctx = wl.ctx_lengths()
-    total_steps = args.warmup + args.steps + 1
+    sweep = [0.5, 1.5, 3.0, 0.1] if not args.no_configs else []
+    sweep_steps = 15
+    total_steps = args.warmup + args.steps + 4 + len(sweep) * (sweep_steps + 2)
     max_ctx = max(ctx) + total_steps * R + 64
     log(f"[bench] workload {wl.name}: B={B} K={K} ctx mean {np.mean(ctx):.0f} (sum {sum(ctx)}), sigma {sigma}")
 
@@ -634,8 +829,18 @@ def main():
                 "algorithmic_per_launch": amount, "avg_launch_ms": round(avg_ms, 4)}
 
     # whole-step HBM roofline of the draft (algorithmic bytes: weights once + context K/V once per layer)
-    draft_bytes = work["_weights_bytes"][1] + work["attn"][1] * cfg.n_layers
+    draft_bytes, draft_flops = _draft_bytes_flops(cfg, B, K, sum_ctx_mid)
     draft_ms = statistics.median(dra)
+    # phase-wise floor: each phase at the larger of its HBM time (bytes / 8 TB/s) and MFMA time (flops / 2.5 PF)
+    pw = phase_work(cfg, B, K, sum_ctx_mid)
+    lw_bytes = cfg.layer_params() * 2
+    gemm_fl = pw["qkv"][1] + pw["o"][1] + pw["gate_up"][1] + pw["down"][1]
+    attn_fl = 4.0 * cfg.n_q_heads * R * cfg.head_dim * (sum_ctx_mid + B * R)
+    phase_floor_us = 1e6 * (cfg.n_layers * (max(lw_bytes / (PEAK_HBM_GBS * 1e9), gemm_fl / (PEAK_16B_TFLOPS * 1e12))
+                                            + max(pw["attn"][1] / (PEAK_HBM_GBS * 1e9),
+                                                  attn_fl / (PEAK_16B_TFLOPS * 1e12)))
+                            + max(cfg.vocab * cfg.hidden * 2 / (PEAK_HBM_GBS * 1e9),
+                                  pw["lm_head"][1] / (PEAK_16B_TFLOPS * 1e12)))
     result = {
         "metric": "draft tokens/s (5-layer, K=16, ctx 4K, B=32)",
         "value": round(B * K / (ms_step * 1e-3), 1),
@@ -656,6 +861,12 @@ def main():
                    "vocab": cfg.vocab, "target_features": f"{cfg.n_target_layers}x{cfg.target_hidden}",
                    "verify": "greedy", "sigma": sigma, "parallelism": "none (1 GPU)"},
         "roofline": roof,
+        "draft_step": {"us_median": round(draft_ms * 1e3, 1),
+                       "hbm_roofline_frac": round(draft_bytes / (draft_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes": draft_bytes, "algorithmic_flops": draft_flops,
+                       "mfma_roofline_frac": round(draft_flops / (draft_ms * 1e-3) / 1e12 / PEAK_16B_TFLOPS, 4),
+                       "phase_floor_us": round(phase_floor_us, 1),
+                       "frac_of_phase_floor": round(phase_floor_us / (draft_ms * 1e3), 4)},
         "draft_us_median": round(draft_ms * 1e3, 1),
         "draft_only_tokens_per_s": round(B * K / (draft_ms * 1e-3), 1),
         "draft_hbm_roofline_frac": round(draft_bytes / (draft_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -666,8 +877,19 @@ def main():
         "mean_committed_per_verify": round(mean_out_len, 3),
         "phase_ms_per_step": {p: round(t, 4) for p, t in sorted(totals.items(), key=lambda x: -x[1])},
     }
+    # the batch-32 workload at the configuration's other noise levels, and at a noise level calibrated so that
+    # a verify commits the pages' 4-6 tokens (random weights accept far less at sigma 1.5)
+    if sweep:
+        log("[bench] sigma sweep on the batch-32 workload ...")
+        result["sigma_sweep"] = [_loop(dr, cfg, B, K, sweep_steps, 0.0, sg, 21 + j, 40 + j)
+                                 for j, sg in enumerate(sweep)]
     dr.close()
     torch.cuda.empty_cache()
+    if not args.no_configs:
+        log("[bench] batch 1, context 2048 ...")
+        result.setdefault("configs", {})["b1_ctx2k"] = c2_measure(w)
+        log("[bench] batch 4, 32768-row prompts in one call, 50 T=1 cycles ...")
+        result["configs"]["b4_ctx32k"] = c4_measure(w)
     if not args.no_inject:
         log("[bench] prompt injection (4 x 32768 rows, one call) ...")
         result["inject_prompt"] = inject_prompt_measure(w)
@@ -681,6 +903,9 @@ def main():
         result["variants"] = variants_measure(w, ctx)
     del w
     torch.cuda.empty_cache()
+    if not args.no_configs:
+        log("[bench] larger drafter, batch 64, context 8192, top-64 + tree ...")
+        result.setdefault("configs", {})["b64_tree"] = c5_measure()
     if not args.no_tree:
         log("[bench] tree verify walk (batch 64, 65-node trees) ...")
         result["tree_verify"] = tree_verify_measure()

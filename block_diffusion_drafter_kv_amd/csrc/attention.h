@@ -65,6 +65,9 @@ struct AttnCombineArgs {
   void* out;               // [n_req*R][q_dim] activations (T)
   int n_kv, group, R, rows_per_split, splits, QRT16, q_dim, D;
   int chunk_min, chunk_max;
+  // wave-range records (16-bit K/V), or null: the plan's per_wg is the groups per wave range;
+  // segment s has one record per wave range it meets, at w + s for those waves w (attn_wave_kernel)
+  const AttnPlan* wave_plan;
 };
 
 // groups per chunk of a segment of `len` groups

@@ -696,6 +696,245 @@ __global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
   }
 }
 
+// Streamed attention, one wave per work-group, no LDS and no barrier (16-bit K/V).
+// The groups of all segments, laid end to end, are cut into equal ranges of
+// a.plan->per_wg groups, one per wave (no snapping: a range may start or end
+// inside a segment).  A wave streams its range straight into registers -- the
+// cache's 32-key blocks are stored in MFMA operand order, so each fragment is
+// one coalesced 1 KB wave load -- with the next group's 16 loads in flight
+// while the current group is computed, and holds every query tile of the
+// segment (Q fragments and O accumulators) itself.  Each (wave, segment) piece
+// of work ends in one partial record (unnormalised O, reference max, sum) at
+// index w + s, which is unique: a wave meets consecutive segments and a segment
+// consecutive waves.  The combine merges a segment's records in wave order.
+// Per group and tile: S^T (32 x 16) = K Q^T, P = exp2(scale*s - m) with the lazy
+// integer reference m, O^T += V^T P^T, exactly as in attn_pc_kernel.
+//
+// Why not an LDS ring shared by query-tile waves: measured on this path's
+// access pattern, copies into LDS published by a work-group barrier per 16 KB
+// group stream at about 2.8 TB/s whatever the ring depth or copy-wave count,
+// while independent waves loading into registers stream at about 5.9 TB/s.
+template <typename T, int D, int QRT, bool PAGED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_wave_kernel(const AttnArgs a) {
+  constexpr int KS = D / 32, DT = D / 16, ROWS = QRT * 16;
+  constexpr int BLK = KV_BLOCK * D;                        // elements of a K (or V) block
+  constexpr int NF = 2 * KS + DT;                          // 16-byte loads per lane per group (K then V)
+  constexpr float TAU = 8.f;
+  static_assert(sizeof(T) == 2, "16-bit K/V");
+  typedef typename Frag<T>::type FragT;
+
+  const int lane = threadIdx.x;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int w = blockIdx.x;
+  const int4 rg = a.wg_range[w];
+  const int g0 = rg.x, g1 = rg.y;
+  if (g0 >= g1) return;
+
+  struct Seg {
+    const T* kc; const T* vc; const T* kb; const T* vb;
+    int start, len, ncache, C, slot, kv;
+    int64_t q0;
+  };
+  auto decode = [&](int s, Seg& d) {
+    const int per_req = a.n_kv * a.splits;
+    const int r = s / per_req, rem = s - r * per_req, kv = rem / a.splits, z = rem - kv * a.splits;
+    const int4 sd = a.seg_desc[s];
+    d.slot = sd.x;
+    d.C = sd.y;
+    d.ncache = (d.C + KV_BLOCK - 1) / KV_BLOCK;
+    d.start = sd.z;
+    d.len = sd.w;
+    d.kv = kv;
+    const int64_t head = (int64_t)d.slot * a.n_kv + kv;
+    d.kc = (const T*)a.cache_k + head * a.ctx_alloc * D;
+    d.vc = (const T*)a.cache_v + head * a.ctx_alloc * D;
+    const int64_t bh = (int64_t)r * a.n_kv + kv;
+    d.kb = (const T*)a.kb + bh * a.Rpad * D;
+    d.vb = (const T*)a.vb + bh * a.Rpad * D;
+    d.q0 = bh * a.QRpad + (int64_t)z * a.rows_per_split;
+  };
+
+  // ---- load cursor: the group after the one being computed
+  int ls_s = rg.z;
+  Seg ls;
+  decode(ls_s, ls);
+  int ls_l = g0 - ls.start;
+  PageCursor pcur;
+  page_cursor_reset(pcur);
+  auto issue = [&](FragT (&kv_next)[NF]) {
+    const T* kp = ls.kb;
+    const T* vp = ls.vb;
+    if (ls_l < ls.ncache) ctx_group_ptrs<T, D, PAGED>(a, pcur, ls.kc, ls.vc, ls.slot, ls.kv, ls_l, ls.ncache, &kp, &vp);
+#pragma unroll
+    for (int f = 0; f < 2 * KS; ++f) *(uint4*)&kv_next[f] = *(const uint4*)(kp + (f * 64 + lane) * 8);
+#pragma unroll
+    for (int f = 0; f < DT; ++f) *(uint4*)&kv_next[2 * KS + f] = *(const uint4*)(vp + (f * 64 + lane) * 8);
+    if (++ls_l == ls.len) {   // the next segment (decoded even when the range ends here: its descriptor exists)
+      if (ls_s + 1 < a.n_seg) {
+        ++ls_s;
+        decode(ls_s, ls);
+      }
+      ls_l = 0;
+      page_cursor_reset(pcur);
+    }
+  };
+
+  // ---- compute cursor; the segment's Q fragments sit in this wave's own LDS (read
+  // per tile and group: registers go to the O accumulators and the K/V double buffer)
+  int cs_s = rg.z;
+  Seg cs;
+  decode(cs_s, cs);
+  int cl = g0 - cs.start;
+  __shared__ uint4 qs[QRT * KS * 64];
+  auto load_q = [&]() {
+#pragma unroll
+    for (int t = 0; t < QRT; ++t) {
+      const int row = t * 16 + r16;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        qs[(t * KS + s) * 64 + lane] = row < a.rows_per_split
+            ? *(const uint4*)((const T*)a.qb + (cs.q0 + row) * D + s * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load_q();
+
+  f32x4 acc[QRT][DT];
+  float m_ref[QRT], l_sum[QRT];
+  const float c = a.scale_log2;
+  auto reset = [&]() {
+#pragma unroll
+    for (int t = 0; t < QRT; ++t) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_ref[t] = -INFINITY;
+      l_sum[t] = 0.f;
+    }
+  };
+  reset();
+
+  // three phases over all tiles, so that each phase's MFMAs and VALU work are
+  // independent across tiles (one wave per SIMD: no other wave hides latency);
+  // kv holds the group's K fragments, then its V fragments
+  auto compute = [&](FragT (&kv)[NF]) {
+    FragT* kf = kv;
+    FragT* vf = kv + 2 * KS;
+    const int nval = cl < cs.ncache ? min(KV_BLOCK, cs.C - KV_BLOCK * cl) : a.R;
+    if (nval < KV_BLOCK) {   // stale cache contents past the end must not turn 0 * x into NaN
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (grp * 8 + e >= nval) vf[dt][e] = (T)0.f;
+    }
+    // S^T = K Q^T for every tile; lane holds keys 8*grp + i (sc[t][0]) and 8*grp + 4 + i (sc[t][1])
+    f32x4 sc[QRT][2];
+#pragma unroll
+    for (int t = 0; t < QRT; ++t) sc[t][0] = sc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int t = 0; t < QRT; ++t) {
+        FragT qf;
+        *(uint4*)&qf = qs[(t * KS + s) * 64 + lane];
+        Frag<T>::mma(sc[t][0], kf[s], qf);
+        Frag<T>::mma(sc[t][1], kf[KS + s], qf);
+      }
+    }
+    // masks, lazy reference, probabilities
+    FragT pf[QRT];
+#pragma unroll
+    for (int t = 0; t < QRT; ++t) {
+      if (nval < KV_BLOCK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (8 * grp + i >= nval) sc[t][0][i] = -INFINITY;
+          if (8 * grp + 4 + i >= nval) sc[t][1][i] = -INFINITY;
+        }
+      }
+      if (a.causal && cl >= cs.ncache) {   // the block's own keys: key j visible to block rows >= j
+        const int jrow = (t * 16 + r16) % a.R;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (8 * grp + i > jrow) sc[t][0][i] = -INFINITY;
+          if (8 * grp + 4 + i > jrow) sc[t][1][i] = -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(sc[t][0][i], sc[t][1][i]));
+      mx *= c;
+      if (__any(mx > m_ref[t] + TAU)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m_ref[t], ceilf(mx));
+        const float alpha = mnew > m_ref[t] ? __builtin_amdgcn_exp2f(m_ref[t] - mnew) : 1.f;   // a power of two
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[t][dt] *= alpha;
+        l_sum[t] *= alpha;
+        m_ref[t] = mnew;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[t][0][i], c, -m_ref[t]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[t][1][i], c, -m_ref[t]));
+        l_sum[t] += p0 + p1;
+        pf[t][i] = (T)p0;
+        pf[t][4 + i] = (T)p1;
+      }
+    }
+    // O^T += V^T P^T for every tile
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int t = 0; t < QRT; ++t) Frag<T>::mma(acc[t][dt], vf[dt], pf[t]);
+  };
+
+  auto flush = [&]() {
+    const int64_t piece = (int64_t)w + cs_s;
+#pragma unroll
+    for (int t = 0; t < QRT; ++t) {
+      float l = l_sum[t];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      const int row = t * 16 + r16;
+      if (row < a.rows_per_split) {
+        float* op = a.o_part + (piece * ROWS + row) * D + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + dt * 16) = acc[t][dt];
+        if (grp == 0) {
+          a.m_part[piece * ROWS + row] = m_ref[t];
+          a.l_part[piece * ROWS + row] = l;
+        }
+      }
+    }
+  };
+
+  auto advance = [&](int gi) {   // bookkeeping after group gi: record at a segment or range end
+    ++cl;
+    const bool seg_end = cl == cs.len;
+    if (seg_end || gi + 1 == g1) {
+      flush();
+      if (seg_end && gi + 1 < g1) {
+        reset();
+        ++cs_s;
+        decode(cs_s, cs);
+        cl = 0;
+        load_q();
+      }
+    }
+  };
+  // group gi + 1 loads into kv_next while group gi is computed from its copy
+  FragT kv_next[NF], kv[NF];
+  issue(kv_next);
+  for (int gi = g0; gi < g1; ++gi) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) kv[f] = kv_next[f];
+    if (gi + 1 < g1) issue(kv_next);
+    compute(kv);
+    advance(gi);
+  }
+}
+
 // One work-group per (request, kv head and q-row part, block of 16 rows): each
 // thread owns one row and D/16 consecutive head dims and merges the segment's
 // chunk records in order in one pass (running max, earlier sums rescaled).
@@ -709,9 +948,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs
   if (row >= a.rows_per_split) return;
   const int seg = (req * a.n_kv + kv) * a.splits + z;
   const int len = a.seg_start[seg + 1] - a.seg_start[seg];
-  const int cg = attn_chunk_groups(len, a.chunk_min, a.chunk_max);
-  const int n = (len + cg - 1) / cg;
-  const int64_t p0 = a.chunk_base[seg];
+  int n;
+  int64_t p0;
+  if (a.wave_plan) {   // one record per wave range the segment meets, at w + seg
+    const int per = a.wave_plan->per_wg;
+    const int w0 = a.seg_start[seg] / per, w1 = (a.seg_start[seg + 1] - 1) / per;
+    n = w1 - w0 + 1;
+    p0 = (int64_t)w0 + seg;
+  } else {
+    const int cg = attn_chunk_groups(len, a.chunk_min, a.chunk_max);
+    n = (len + cg - 1) / cg;
+    p0 = a.chunk_base[seg];
+  }
   // one pass, four chunk records' loads issued together; the running max rescales what came before
   float M = -INFINITY, L = 0.f;
   float O[EPT];
@@ -785,6 +1033,23 @@ static void launch_attn_pc(const AttnArgs& a, int qrt, int grid, hipStream_t s) 
     case 4: attn_pc_kernel<f16_t, D, 4, 4 + NP, NP, S, PG><<<grid, 64 * (4 + NP), 0, s>>>(a); break;
     case 5: attn_pc_kernel<f16_t, D, 5, 5 + NP, NP, S, PG><<<grid, 64 * (5 + NP), 0, s>>>(a); break;
   }
+}
+
+template <int D, bool PG>
+static void launch_attn_wave(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
+  switch (qrt) {
+    case 1: attn_wave_kernel<f16_t, D, 1, PG><<<grid, 64, 0, s>>>(a); break;
+    case 2: attn_wave_kernel<f16_t, D, 2, PG><<<grid, 64, 0, s>>>(a); break;
+    case 3: attn_wave_kernel<f16_t, D, 3, PG><<<grid, 64, 0, s>>>(a); break;
+    case 4: attn_wave_kernel<f16_t, D, 4, PG><<<grid, 64, 0, s>>>(a); break;
+    case 5: attn_wave_kernel<f16_t, D, 5, PG><<<grid, 64, 0, s>>>(a); break;
+  }
+}
+
+void launch_attn_waves(int D, int qrt, const AttnArgs& a, int grid, hipStream_t s) {
+  const bool pg = a.page_table != nullptr;
+  if (D == 128) pg ? launch_attn_wave<128, true>(a, qrt, grid, s) : launch_attn_wave<128, false>(a, qrt, grid, s);
+  else pg ? launch_attn_wave<64, true>(a, qrt, grid, s) : launch_attn_wave<64, false>(a, qrt, grid, s);
 }
 
 void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, int n_kv, int splits, int n_wg_max,

@@ -39,6 +39,8 @@ void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, i
                       int min_per_wg, int chunk_min, int chunk_max, AttnPlan* plan, int32_t* seg_start,
                       int32_t* chunk_base, int4* seg_desc, int4* wg_range, hipStream_t s);
 void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStream_t s);
+// 16-bit K/V: one wave per work-group over equal group ranges (plan built without chunk snapping)
+void launch_attn_waves(int D, int qrt, const AttnArgs& a, int grid, hipStream_t s);
 void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, hipStream_t s);
 
 // ---- elementwise / row kernels (kernels.hip) ----
