@@ -23,13 +23,18 @@ struct dflash_handle {
   const void *embed = nullptr, *lm_head = nullptr, *fc = nullptr, *hidden_norm = nullptr, *final_norm = nullptr;
   std::vector<dflash_layer_weights> layers;
   // matrices as the products read them: the caller's (fp32 drafter) or the
-  // handle's fp16 copies scaled by 2^wscale_log2 (bf16 drafter)
-  struct Mats { const void *q, *k, *v, *o, *gate, *up, *down, *conv_a, *conv_m; };
+  // handle's fp16 copies, each group of them scaled by its own power of two (bf16 drafter)
+  // s_*: 2^-(the copy's scale exponent), multiplied into every product that reads the copy
+  struct Mats {
+    const void *q, *k, *v, *o, *gate, *up, *down, *conv_a, *conv_m;
+    float s_o = 1.f, s_gu = 1.f, s_down = 1.f, s_ca = 1.f, s_cm = 1.f;
+  };
   std::vector<Mats> mats;
   const void* lm = nullptr;
   int op = OP_F32, op_fc = OP_F32;  // operand type of the products / of the fc product
-  int wscale_log2 = 0;
-  float out_scale = 1.f;            // 2^-wscale_log2: undoes the weight scale in every epilogue
+  // scales shared across layers: q | k | v of every layer (the draft reads one layer's q | k | v in
+  // one product, the injection every layer's k | v), the LM head, the selector's W_H
+  float s_qkv = 1.f, s_lm = 1.f, s_selh = 1.f;
   const void** d_k_gains = nullptr;       // device array of per-layer k_norm pointers
   // cache and state
   void* cache_k = nullptr;
@@ -55,6 +60,7 @@ struct dflash_handle {
   int n_rope = 0;
   // draft scratch
   int maxM = 0, Rpad = 0, QRpad = 0, attn_splits = 1, attn_wg = 0, piece_cap = 0, qrt_max = 5;
+  bool attn_waves = false;     // 16-bit K/V: one wave per work-group, attn_wg = 4 per CU
   float* X = nullptr;
   void *hbuf = nullptr, *attn_out = nullptr, *act = nullptr, *qb = nullptr, *kb = nullptr, *vb = nullptr;
   float *o_part = nullptr, *m_part = nullptr, *l_part = nullptr;
@@ -105,6 +111,7 @@ struct dflash_handle {
 namespace {
 
 constexpr int kAttnMinGroups = 8;   // fewest 32-key groups per attention work-group range
+constexpr int kAttnMinGroupsWave = 2;   // ... per single-wave range (16-bit K/V)
 constexpr int kAttnChunkMin = 16;   // chunk of a segment: at least 16 groups (512 keys) ...
 constexpr int kAttnChunkMax = 16;   // ... and at most 16 chunks per segment
 
@@ -239,13 +246,16 @@ void set_b(GemmArgs& g, std::initializer_list<std::pair<const void*, int>> segs,
 inline hipStream_t S(void* s) { return (hipStream_t)s; }
 
 // The matrices every product reads.  fp32 drafter: the caller's.  bf16 drafter:
-// fp16 copies of q/k/v/o/gate/up/down of every layer and of the LM head, all
-// scaled by one power of two 2^s chosen from the largest |w| so that the largest
-// scaled weight lies in [2^14, 2^15).  A bf16 value has 8 significant bits, so
-// w * 2^s is exact in fp16 whenever it is at least 2^-14, which holds for every
-// |w| of at least 2^-28 times the largest; smaller weights round to fp16's
-// subnormal grid (absolute error at most 2^(-25-s)).  The
-// epilogues multiply the products by 2^-s (exact).
+// fp16 copies of q/k/v/o/gate/up/down of every layer, the convolution
+// projections, the LM head and the selector's W_H.  Each group of matrices that
+// one product reads (q|k|v of all layers, since the injection reads every
+// layer's k|v at once; o, gate|up, down and each projection per layer; the LM
+// head; W_H) is scaled by its own power of two 2^s, chosen from the group's
+// largest |w| so that it lies in [2^14, 2^15).  A bf16 value has 8 significant
+// bits, so w * 2^s is exact in fp16 whenever it is at least 2^-14, which holds
+// for every |w| of at least 2^-28 times the group's largest; smaller weights
+// round to fp16's subnormal grid (absolute error at most 2^(-25-s)).  The
+// epilogues multiply each product by its group's 2^-s (exact).
 int prepare_weights(dflash_handle* h) {
   const dflash_config& c = h->cfg;
   h->mats.resize(c.n_layers);
@@ -260,48 +270,59 @@ int prepare_weights(dflash_handle* h) {
   }
   const int64_t H = c.hidden, qdim = (int64_t)c.n_q_heads * c.head_dim, kvdim = (int64_t)c.n_kv_heads * c.head_dim;
   const int64_t F = c.ffn, V = c.vocab;
-  struct Job { const void* src; int64_t n; const void** dst; };
+  // Each group of matrices read by one product gets its own power-of-two scale,
+  // chosen from the group's largest |w|, so one large matrix does not shrink the
+  // exact range of the others.
+  struct Job { const void* src; int64_t n; const void** dst; int group; };
   std::vector<Job> jobs;
+  std::vector<float*> group_scale;           // where each group's 2^-s goes
+  auto group = [&](float* out) { group_scale.push_back(out); return (int)group_scale.size() - 1; };
+  const int g_qkv = group(&h->s_qkv);
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& L = h->layers[l];
     dflash_handle::Mats& m = h->mats[l];
-    jobs.push_back({L.q_w, qdim * H, &m.q});
-    jobs.push_back({L.k_w, kvdim * H, &m.k});
-    jobs.push_back({L.v_w, kvdim * H, &m.v});
-    jobs.push_back({L.o_w, H * qdim, &m.o});
-    jobs.push_back({L.gate_w, F * H, &m.gate});
-    jobs.push_back({L.up_w, F * H, &m.up});
-    jobs.push_back({L.down_w, H * F, &m.down});
+    jobs.push_back({L.q_w, qdim * H, &m.q, g_qkv});
+    jobs.push_back({L.k_w, kvdim * H, &m.k, g_qkv});
+    jobs.push_back({L.v_w, kvdim * H, &m.v, g_qkv});
+    jobs.push_back({L.o_w, H * qdim, &m.o, group(&m.s_o)});
+    const int g_gu = group(&m.s_gu);
+    jobs.push_back({L.gate_w, F * H, &m.gate, g_gu});
+    jobs.push_back({L.up_w, F * H, &m.up, g_gu});
+    jobs.push_back({L.down_w, H * F, &m.down, group(&m.s_down)});
     m.conv_a = m.conv_m = nullptr;
     if (c.conv_group > 0) {
-      jobs.push_back({L.attn_conv_proj, 2 * H / c.conv_group * H, &m.conv_a});
-      jobs.push_back({L.mlp_conv_proj, 2 * H / c.conv_group * H, &m.conv_m});
+      jobs.push_back({L.attn_conv_proj, 2 * H / c.conv_group * H, &m.conv_a, group(&m.s_ca)});
+      jobs.push_back({L.mlp_conv_proj, 2 * H / c.conv_group * H, &m.conv_m, group(&m.s_cm)});
     }
   }
-  jobs.push_back({h->lm_head, V * H, &h->lm});
-  if (c.sel_rank > 0) jobs.push_back({h->sel_hidden_src, (int64_t)c.sel_rank * H, &h->sel_h});
+  jobs.push_back({h->lm_head, V * H, &h->lm, group(&h->s_lm)});
+  if (c.sel_rank > 0) jobs.push_back({h->sel_hidden_src, (int64_t)c.sel_rank * H, &h->sel_h, group(&h->s_selh)});
+  const int ng = (int)group_scale.size();
   uint32_t* d_max = nullptr;
-  int rc = alloc_t(h, &d_max, 1, 4);
+  int rc = alloc_t(h, &d_max, (size_t)ng, 4);
   if (rc) return rc;
-  for (auto& j : jobs) launch_absmax_bf16(j.src, j.n, d_max, nullptr);
-  uint32_t bits = 0;
-  if (hipMemcpy(&bits, d_max, 4, hipMemcpyDeviceToHost) != hipSuccess) return DFLASH_E_HIP;
-  float amax;
-  std::memcpy(&amax, &bits, 4);
-  if (!(amax <= 3.0e38f)) return DFLASH_E_INVALID;   // Inf or NaN among the weights
-  int s = 0;
-  if (amax > 0.f) {
-    int e;
-    std::frexp(amax, &e);     // amax in [2^(e-1), 2^e)
-    s = 15 - e;               // amax * 2^s in [2^14, 2^15)
+  if (hipMemset(d_max, 0, (size_t)ng * 4) != hipSuccess) return DFLASH_E_HIP;
+  for (auto& j : jobs) launch_absmax_bf16(j.src, j.n, d_max + j.group, nullptr);
+  std::vector<uint32_t> bits(ng);
+  if (hipMemcpy(bits.data(), d_max, (size_t)ng * 4, hipMemcpyDeviceToHost) != hipSuccess) return DFLASH_E_HIP;
+  std::vector<float> scale(ng);
+  for (int gi = 0; gi < ng; ++gi) {
+    float amax;
+    std::memcpy(&amax, &bits[gi], 4);
+    if (!(amax <= 3.0e38f)) return DFLASH_E_INVALID;   // Inf or NaN among the weights
+    int s = 0;
+    if (amax > 0.f) {
+      int e;
+      std::frexp(amax, &e);     // amax in [2^(e-1), 2^e)
+      s = 15 - e;               // amax * 2^s in [2^14, 2^15)
+    }
+    *group_scale[gi] = std::ldexp(1.0f, -s);
+    scale[gi] = std::ldexp(1.0f, s);
   }
-  h->wscale_log2 = s;
-  h->out_scale = std::ldexp(1.0f, -s);
-  const float scale = std::ldexp(1.0f, s);
   for (auto& j : jobs) {
     void* dst = nullptr;
     if ((rc = alloc(h, &dst, (size_t)j.n * 2))) return rc;
-    launch_convert_bf16_f16(j.src, j.n, scale, dst, nullptr);
+    launch_convert_bf16_f16(j.src, j.n, scale[j.group], dst, nullptr);
     *j.dst = dst;
   }
   return DFLASH_OK;
@@ -375,11 +396,13 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
   h->Rpad = ((R + 31) / 32) * 32;
   h->QRpad = ((g * R + 15) / 16) * 16 + 80;
   h->ctx_alloc = ((int64_t)(c.max_ctx + 63) / 64) * 64 + 64;
-  // attention work-groups: one producer / consumer work-group per CU for 16-bit
-  // K/V (128 KB LDS ring), two per CU for fp32; at most kAttnChunkMax partial
+  // attention work-groups: for 16-bit K/V one single-wave work-group per SIMD
+  // (equal group ranges, one partial record per (wave, segment) piece); for
+  // fp32 two LDS-ring work-groups per CU with at most kAttnChunkMax partial
   // records (chunks) per segment
-  h->attn_wg = (c.dtype == DFLASH_BF16 ? 1 : 2) * h->num_cus;
-  h->piece_cap = c.max_batch * nkv * splits * kAttnChunkMax;
+  h->attn_waves = c.dtype == DFLASH_BF16;
+  h->attn_wg = (h->attn_waves ? 4 : 2) * h->num_cus;
+  h->piece_cap = h->attn_waves ? h->attn_wg + c.max_batch * nkv * splits : c.max_batch * nkv * splits * kAttnChunkMax;
   h->op = c.dtype == DFLASH_BF16 ? OP_F16 : OP_F32;
   h->op_fc = c.dtype == DFLASH_BF16 ? OP_BF16 : OP_F32;
   h->lm_tile = gemm_bn(h->op);
@@ -566,7 +589,7 @@ int inject_rows(dflash_handle* h, hipStream_t s, int n_req, int64_t rows_upper_b
     for (int l0 = 0; l0 < c.n_layers; l0 += MAX_BSEG / 2) {
       const int nl = std::min(MAX_BSEG / 2, c.n_layers - l0);
       GemmArgs gk = gemm_a1(h->g, H, rows, 2 * kvdim * nl, H);
-      gk.out_scale = h->out_scale;
+      gk.out_scale = h->s_qkv;
       gk.m_valid = h->req_off + n_req;
       gk.m_valid_base = (int)c0;
       for (int i = 0; i < nl; ++i) {
@@ -656,12 +679,13 @@ namespace {
 
 // DFlash 2 [P2 §3.2.3]: hbuf2 = dynamic conv of the block rows in hbuf; the
 // per-row kernel corrections come from one product with the layer's proj.
-void conv_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj, const void* base, const void* gain) {
+void conv_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj, float proj_scale, const void* base,
+                const void* gain) {
   const dflash_config& c = h->cfg;
   const int H = c.hidden, nc = 2 * (H / c.conv_group);
   Phase ph(h, s, DFLASH_PH_CONV);
   GemmArgs ga = gemm_a1(h->hbuf, H, M, nc, H);
-  ga.out_scale = h->out_scale;
+  ga.out_scale = proj_scale;
   set_b(ga, {{proj, nc}}, H);
   EpiStore<float>::Params pc{h->cbuf, nc};
   launch_gemm(h->op, EPI_STORE_F32, ga, &pc, plan_gemm(h->op, M, nc, H, h->num_cus), h->partials, h->partials_elems,
@@ -681,7 +705,7 @@ void selector_stage(dflash_handle* h, hipStream_t s, int n_req, int K, const int
   launch_topk(rows, c.vocab, C, logits, h->tmax, h->n_vtiles, h->lm_tile, T > 0.f ? 1.0f / T : 1.0f, h->row_max,
               h->row_lse, h->sel_cand, h->sel_cprob, s);
   GemmArgs ga = gemm_a1(hidden, H, rows, r, H);
-  ga.out_scale = h->out_scale;
+  ga.out_scale = h->s_selh;
   set_b(ga, {{h->sel_h, r}}, H);
   EpiStore<float>::Params pg{h->sel_gate, r};
   launch_gemm(h->op, EPI_STORE_F32, ga, &pg, plan_gemm(h->op, rows, r, H, h->num_cus), h->partials,
@@ -777,8 +801,12 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   }
   {
     Phase ph(h, s, DFLASH_PH_ATTN_PLAN);
-    launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->attn_wg, kAttnMinGroups, kAttnChunkMin,
-                     kAttnChunkMax, h->plan, h->seg_start, h->chunk_base, h->seg_desc, h->wg_range, s);
+    if (h->attn_waves)   // equal ranges, no snapping to chunk starts
+      launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->attn_wg, kAttnMinGroupsWave, 1, 1 << 30, h->plan,
+                       h->seg_start, h->chunk_base, h->seg_desc, h->wg_range, s);
+    else
+      launch_attn_plan(slots, h->ctx_len, n_req, nkv, splits, h->attn_wg, kAttnMinGroups, kAttnChunkMin,
+                       kAttnChunkMax, h->plan, h->seg_start, h->chunk_base, h->seg_desc, h->wg_range, s);
     launch_page_check(n_req, slots, h->ctx_len, c.max_batch, h->pages(), h->err, s);
   }
   const int64_t layer_cache = (int64_t)(c.max_batch + 1) * nkv * h->ctx_alloc * d * h->esize;
@@ -788,13 +816,13 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     // DFlash 2: dynamic convolution of the attention sub-layer's input
     const void* attn_in = h->hbuf;
     if (c.conv_group > 0) {
-      conv_stage(h, s, M, R, W.conv_a, L.attn_conv_base, L.in_norm);
+      conv_stage(h, s, M, R, W.conv_a, W.s_ca, L.attn_conv_base, L.in_norm);
       attn_in = h->hbuf2;
     }
     // q | k | v with head norm + RoPE into the attention layouts
     {
       GemmArgs ga = gemm_a1(attn_in, H, M, qdim + 2 * kvdim, H);
-      ga.out_scale = h->out_scale;
+      ga.out_scale = h->s_qkv;
       set_b(ga, {{W.q, qdim}, {W.k, kvdim}, {W.v, kvdim}}, H);
       EpiQKV<f16_t>::Params pq;
       pq.qb = (f16_t*)h->qb;
@@ -814,6 +842,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       pq.QRpad = h->QRpad;
       pq.Rpad = h->Rpad;
       pq.eps = c.rms_eps;
+      pq.err = h->err;
       Phase ph(h, s, DFLASH_PH_QKV);
       launch_gemm(h->op, EPI_QKV, ga, &pq, plan_gemm(h->op, M, ga.N, H, h->num_cus), h->partials, h->partials_elems,
                   s);
@@ -858,7 +887,8 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       a.causal = c.causal_block ? 1 : 0;
       {
         Phase ph(h, s, DFLASH_PH_ATTN);
-        launch_attn(dt, d, qrt, a, h->attn_wg, s);
+        if (h->attn_waves) launch_attn_waves(d, qrt, a, h->attn_wg, s);
+        else launch_attn(dt, d, qrt, a, h->attn_wg, s);
       }
       AttnCombineArgs cb;
       cb.o_part = h->o_part;
@@ -877,13 +907,14 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       cb.D = d;
       cb.chunk_min = kAttnChunkMin;
       cb.chunk_max = kAttnChunkMax;
+      cb.wave_plan = h->attn_waves ? h->plan : nullptr;
       Phase ph(h, s, DFLASH_PH_ATTN_COMBINE);
       launch_attn_combine(dt, d, cb, dim3(n_req, nkv * splits, (rows_split + 15) / 16), s);
     }
     // output projection + residual
     {
       GemmArgs ga = gemm_a1(h->attn_out, qdim, M, H, qdim);
-      ga.out_scale = h->out_scale;
+      ga.out_scale = W.s_o;
       set_b(ga, {{W.o, H}}, qdim);
       EpiResidualAdd::Params pr{h->X, H};
       Phase ph(h, s, DFLASH_PH_O);
@@ -897,25 +928,25 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     // DFlash 2: dynamic convolution of the MLP sub-layer's input
     const void* mlp_in = h->hbuf;
     if (c.conv_group > 0) {
-      conv_stage(h, s, M, R, W.conv_m, L.mlp_conv_base, L.post_norm);
+      conv_stage(h, s, M, R, W.conv_m, W.s_cm, L.mlp_conv_base, L.post_norm);
       mlp_in = h->hbuf2;
     }
     // SwiGLU MLP
     {
       GemmArgs ga = gemm_a1(mlp_in, H, M, 2 * F, H);
-      ga.out_scale = h->out_scale;
+      ga.out_scale = W.s_gu;
       ga.b_ptr[0] = W.gate;
       ga.b_ptr[1] = W.up;
       ga.b_interleave = 1;
       ga.b_ld = H;
-      EpiSwiGLU<f16_t>::Params ps{(f16_t*)h->act, F, F};
+      EpiSwiGLU<f16_t>::Params ps{(f16_t*)h->act, F, F, h->err};
       {
         Phase ph(h, s, DFLASH_PH_GATE_UP);
         launch_gemm(h->op, EPI_SWIGLU, ga, &ps, plan_gemm(h->op, M, 2 * F, H, h->num_cus), h->partials,
                     h->partials_elems, s);
       }
       GemmArgs gd = gemm_a1(h->act, F, M, H, F);
-      gd.out_scale = h->out_scale;
+      gd.out_scale = W.s_down;
       set_b(gd, {{W.down, H}}, F);
       EpiResidualAdd::Params pr{h->X, H};
       Phase ph(h, s, DFLASH_PH_DOWN);
@@ -938,7 +969,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   float* logits = o->logits ? o->logits : (need_logits ? h->logits_ws : nullptr);
   {
     GemmArgs ga = gemm_a1(h->hbuf, H, rows, V, H);
-    ga.out_scale = h->out_scale;
+    ga.out_scale = h->s_lm;
     set_b(ga, {{h->lm, V}}, H);
     EpiLMHead::Params pl;
     pl.logits = logits;

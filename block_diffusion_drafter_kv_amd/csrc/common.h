@@ -117,10 +117,31 @@ __device__ __forceinline__ float philox_uniform(uint64_t seed, uint32_t slot, ui
 enum : uint32_t { PURPOSE_DRAFT = 0, PURPOSE_ACCEPT = 1, PURPOSE_RESAMPLE = 2, PURPOSE_NOISE = 3, PURPOSE_TREE_WALK = 4 };
 
 // device error word bits
-enum : int32_t { ERR_CAPACITY = 1, ERR_BAD_SLOT = 2, ERR_ROWS = 4, ERR_BAD_TOKEN = 8, ERR_PAGE = 16 };
+enum : int32_t { ERR_CAPACITY = 1, ERR_BAD_SLOT = 2, ERR_ROWS = 4, ERR_BAD_TOKEN = 8, ERR_PAGE = 16,
+                 ERR_NONFINITE = 32 };
 
 __device__ __forceinline__ void raise_error(int32_t* err, int32_t bit) {
   if (err) atomicOr(err, bit);
+}
+
+// Store conversion of an activation or cache value.  16-bit: a value beyond fp16's
+// largest finite magnitude (or NaN) sets `bad` and is stored saturated (NaN stays
+// NaN), so later kernels see finite values while the caller is told.  fp32: as is.
+template <typename T>
+__device__ __forceinline__ T store_cvt(float x, bool& bad) {
+  if constexpr (sizeof(T) == 2) {
+    if (!(fabsf(x) <= 65504.f)) {
+      bad = true;
+      if (x == x) x = x > 0.f ? 65504.f : -65504.f;
+    }
+  }
+  return from_f32<T>(x);
+}
+
+// After an epilogue pass: one lane of each wave that met an out-of-range value reports it
+// (every lane of the wave must reach this call).
+__device__ __forceinline__ void report_nonfinite(int32_t* err, bool bad, int tid) {
+  if (__any(bad) && (tid & 63) == 0) raise_error(err, ERR_NONFINITE);
 }
 
 }  // namespace dfl

@@ -39,18 +39,20 @@ struct EpiResidualAdd {
 // ---- SwiGLU: tile columns [0, BN/2) are gate, [BN/2, BN) the matching up columns ----
 template <typename OutT>
 struct EpiSwiGLU {
-  struct Params { OutT* out; int64_t ld; int F; };
+  struct Params { OutT* out; int64_t ld; int F; int32_t* err; };
   template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
     constexpr int H = BN / 2;
+    bool bad = false;
     for (int idx = tid; idx < ROWS * H; idx += 256) {
       const int r = idx / H, c = idx % H;
       const int m = m0 + r, f = n0 / 2 + c;
       if (m < M && f < p.F) {
         const float gt = st[r * ld + c], up = st[r * ld + H + c];
-        p.out[(int64_t)m * p.ld + f] = from_f32<OutT>(silu_f(gt) * up);
+        p.out[(int64_t)m * p.ld + f] = store_cvt<OutT>(silu_f(gt) * up, bad);
       }
     }
+    report_nonfinite(p.err, bad, tid);
   }
 };
 
@@ -84,6 +86,7 @@ struct EpiQKV {
     const float2* rope;      // [pos][d/2] (cos, sin)
     int R, group, n_kv, d, q_dim, kv_dim, QRpad, Rpad;
     float eps;
+    int32_t* err;            // device error word (out-of-range 16-bit stores)
   };
   template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
@@ -93,6 +96,7 @@ struct EpiQKV {
     const int sub = lane / half, i = lane % half;
     const int heads = BN / p.d;
     const int items = ROWS * heads;
+    bool bad = false;
     for (int it = wave * per + sub; it < items; it += 4 * per) {
       const int r = it / heads, hh = it % heads;
       const int m = m0 + r;
@@ -108,21 +112,22 @@ struct EpiQKV {
         if (isq) {
           const int qh = nb / p.d, kv = qh / p.group, gi = qh % p.group;
           T* dst = p.qb + ((int64_t)(req * p.n_kv + kv) * p.QRpad + gi * p.R + j) * p.d;
-          dst[i] = from_f32<T>(x1);
-          dst[i + half] = from_f32<T>(x2);
+          dst[i] = store_cvt<T>(x1, bad);
+          dst[i + half] = store_cvt<T>(x2, bad);
         } else {
           const int kh = (nb - p.q_dim) / p.d;
           T* dst = p.kb + (int64_t)(req * p.n_kv + kh) * p.Rpad * p.d;
-          dst[k_off(j, i, p.d)] = from_f32<T>(x1);
-          dst[k_off(j, i + half, p.d)] = from_f32<T>(x2);
+          dst[k_off(j, i, p.d)] = store_cvt<T>(x1, bad);
+          dst[k_off(j, i + half, p.d)] = store_cvt<T>(x2, bad);
         }
       } else {
         const int vh = (nb - p.q_dim - p.kv_dim) / p.d;
         T* dst = p.vb + (int64_t)(req * p.n_kv + vh) * p.Rpad * p.d;
-        dst[v_off(j, i, p.d)] = from_f32<T>(x1);
-        dst[v_off(j, i + half, p.d)] = from_f32<T>(x2);
+        dst[v_off(j, i, p.d)] = store_cvt<T>(x1, bad);
+        dst[v_off(j, i + half, p.d)] = store_cvt<T>(x2, bad);
       }
     }
+    report_nonfinite(p.err, bad, tid);
   }
 };
 
@@ -147,6 +152,7 @@ struct EpiKVInject {
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
     const int lane = tid & 63, wave = tid >> 6;
     const int heads = BN / p.d;
+    bool bad = false;
     for (int hh = 0; hh < heads; ++hh) {
       const int nb = n0 + hh * p.d;
       const int layer = nb / (2 * p.kv_dim);
@@ -172,8 +178,8 @@ struct EpiKVInject {
           float x1 = st[r * ld + hh * p.d + i], x2 = st[r * ld + hh * p.d + i + half];
           norm_rope_pair<W>(x1, x2, i, p.d, p.k_gain[layer], p.eps, p.rope + (int64_t)pos * half);
           T* dst = p.cache_k + hb;
-          dst[k_off(pin, i, p.d)] = from_f32<T>(x1);
-          dst[k_off(pin, i + half, p.d)] = from_f32<T>(x2);
+          dst[k_off(pin, i, p.d)] = store_cvt<T>(x1, bad);
+          dst[k_off(pin, i + half, p.d)] = store_cvt<T>(x2, bad);
         }
       } else {
         // lanes walk rows (consecutive positions -> coalesced stores), waves walk columns
@@ -194,10 +200,11 @@ struct EpiKVInject {
         if (slot >= 0) {
           T* base = p.cache_v + hb;
           for (int c = wave * RPL + lane / ROWS; c < p.d; c += 4 * RPL)
-            base[v_off(pin, c, p.d)] = from_f32<T>(st[r * ld + hh * p.d + c]);
+            base[v_off(pin, c, p.d)] = store_cvt<T>(st[r * ld + hh * p.d + c], bad);
         }
       }
     }
+    report_nonfinite(p.err, bad, tid);
   }
 };
 

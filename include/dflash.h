@@ -32,9 +32,10 @@
  *    activations and KV cache are fp32.  cfg.dtype = DFLASH_BF16: weights and
  *    target hidden states are bf16; every matrix product except the fc takes
  *    fp16 operands with fp32 accumulation, so dflash_create converts q/k/v/o/
- *    gate/up/down of every layer and the LM head once into fp16 copies scaled
- *    by one power of two (exact for every weight of at least 2^-28 times the
- *    largest |w|; the products are scaled back exactly), and the KV cache and
+ *    gate/up/down of every layer and the LM head once into fp16 copies, each
+ *    group of matrices that one product reads scaled by its own power of two
+ *    (exact for every weight of at least 2^-28 times the group's largest |w|;
+ *    the products are scaled back exactly), and the KV cache and
  *    activations are fp16.  The fc product multiplies the given bf16 operands.
  *    The residual stream is fp32 in both.  Logits, probabilities and
  *    statistics are fp32; token ids, lengths and tree indices are int32.
@@ -65,9 +66,14 @@ enum dflash_device_error {
   DFLASH_DEV_BAD_SLOT = 2,   /* a slot id outside [0, max_batch): that request was skipped          */
   DFLASH_DEV_ROWS = 4,       /* row counts negative or above rows_upper_bound: rows skipped         */
   DFLASH_DEV_BAD_TOKEN = 8,  /* an anchor id outside [0, vocab): id 0 was embedded instead          */
-  DFLASH_DEV_PAGE = 16       /* paged cache: a position maps to an unmapped page (table entry outside
+  DFLASH_DEV_PAGE = 16,      /* paged cache: a position maps to an unmapped page (table entry outside
                                 [0, num_pages)): injected rows there were skipped; a draft reading
                                 such a page read page 0 instead (its outputs are not meaningful)     */
+  DFLASH_DEV_NONFINITE = 32  /* bf16 drafter: a value stored in 16 bits (SwiGLU output, q/k/v of the
+                                block, K/V written to the cache) was beyond fp16's largest finite
+                                magnitude 65504, or NaN: it was stored saturated to +-65504 (NaN as
+                                NaN), so later kernels stay finite, and the results that depend on
+                                it are not meaningful                                               */
 };
 
 /* Model shape, numerics and capacity, fixed at create time.
