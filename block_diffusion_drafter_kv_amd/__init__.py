@@ -40,7 +40,8 @@ class dflash_config(ctypes.Structure):
 class dflash_layer_weights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("in_norm", "q_w", "k_w", "v_w", "o_w", "q_norm", "k_norm", "post_norm",
                                         "gate_w", "up_w", "down_w", "attn_conv_base", "attn_conv_proj",
-                                        "mlp_conv_base", "mlp_conv_proj")]
+                                        "mlp_conv_base", "mlp_conv_proj", "attn_conv_post_base",
+                                        "attn_conv_post_proj", "mlp_conv_post_base", "mlp_conv_post_proj")]
 
 
 class dflash_weights(ctypes.Structure):

@@ -27,7 +27,8 @@ struct dflash_handle {
   // s_*: 2^-(the copy's scale exponent), multiplied into every product that reads the copy
   struct Mats {
     const void *q, *k, *v, *o, *gate, *up, *down, *conv_a, *conv_m;
-    float s_o = 1.f, s_gu = 1.f, s_down = 1.f, s_ca = 1.f, s_cm = 1.f;
+    const void *conv_ap = nullptr, *conv_mp = nullptr;   // after-sub-layer convolutions (or null)
+    float s_o = 1.f, s_gu = 1.f, s_down = 1.f, s_ca = 1.f, s_cm = 1.f, s_cap = 1.f, s_cmp = 1.f;
   };
   std::vector<Mats> mats;
   const void* lm = nullptr;
@@ -82,7 +83,8 @@ struct dflash_handle {
   void* g = nullptr;
   int32_t *a_rows = nullptr, *row_slot = nullptr, *row_pos = nullptr, *req_off = nullptr, *req_pos = nullptr;
   // DFlash 2 modules
-  void* hbuf2 = nullptr;                  // convolved sub-layer input
+  void* hbuf2 = nullptr;                  // convolved sub-layer input; operand copy of a sub-layer output
+  float* obuf = nullptr;                  // fp32 sub-layer output ahead of an after-sub-layer convolution
   float* cbuf = nullptr;                  // kernel corrections [maxM, 2H/G]
   const void* sel_h = nullptr;            // W_H (fp16 copy for a bf16 drafter)
   const void *sel_pred = nullptr, *sel_succ = nullptr;
@@ -262,7 +264,8 @@ int prepare_weights(dflash_handle* h) {
   if (c.dtype != DFLASH_BF16) {
     for (int l = 0; l < c.n_layers; ++l) {
       const dflash_layer_weights& L = h->layers[l];
-      h->mats[l] = {L.q_w, L.k_w, L.v_w, L.o_w, L.gate_w, L.up_w, L.down_w, L.attn_conv_proj, L.mlp_conv_proj};
+      h->mats[l] = {L.q_w, L.k_w, L.v_w, L.o_w, L.gate_w, L.up_w, L.down_w, L.attn_conv_proj, L.mlp_conv_proj,
+                    L.attn_conv_post_proj, L.mlp_conv_post_proj};
     }
     h->lm = h->lm_head;
     h->sel_h = h->sel_hidden_src;
@@ -293,6 +296,10 @@ int prepare_weights(dflash_handle* h) {
     if (c.conv_group > 0) {
       jobs.push_back({L.attn_conv_proj, 2 * H / c.conv_group * H, &m.conv_a, group(&m.s_ca)});
       jobs.push_back({L.mlp_conv_proj, 2 * H / c.conv_group * H, &m.conv_m, group(&m.s_cm)});
+      if (L.attn_conv_post_proj)
+        jobs.push_back({L.attn_conv_post_proj, 2 * H / c.conv_group * H, &m.conv_ap, group(&m.s_cap)});
+      if (L.mlp_conv_post_proj)
+        jobs.push_back({L.mlp_conv_post_proj, 2 * H / c.conv_group * H, &m.conv_mp, group(&m.s_cmp)});
     }
   }
   jobs.push_back({h->lm_head, V * H, &h->lm, group(&h->s_lm)});
@@ -359,6 +366,10 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
         !L.gate_w || !L.up_w || !L.down_w)
       return DFLASH_E_INVALID;
     if (c.conv_group > 0 && (!L.attn_conv_base || !L.attn_conv_proj || !L.mlp_conv_base || !L.mlp_conv_proj))
+      return DFLASH_E_INVALID;
+    // an after-sub-layer convolution needs both its pointers
+    if (c.conv_group > 0 && (!L.attn_conv_post_base != !L.attn_conv_post_proj ||
+                             !L.mlp_conv_post_base != !L.mlp_conv_post_proj))
       return DFLASH_E_INVALID;
   }
   if (c.sel_rank > 0 && (!w->sel_pred || !w->sel_succ || !w->sel_hidden)) return DFLASH_E_INVALID;
@@ -470,6 +481,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if (c.conv_group > 0) {
       if ((rc = alloc(h, &h->hbuf2, (size_t)h->maxM * H * es))) break;
       if ((rc = alloc_t(h, &h->cbuf, (size_t)h->maxM * 2 * (H / c.conv_group), 4))) break;
+      if ((rc = alloc_t(h, &h->obuf, (size_t)h->maxM * H, 4))) break;
     }
     if (c.sel_rank > 0) {
       const size_t C = c.sel_cands;
@@ -693,6 +705,46 @@ void conv_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj,
   launch_dyn_conv(c.dtype, M, R, H, c.conv_group, h->X, gain, c.rms_eps, h->cbuf, base, h->hbuf2, s);
 }
 
+// DFlash 2 [P2 §3.2.3]: convolution after a sub-layer.  The sub-layer's output
+// projection is in obuf (fp32) and hbuf2 (operand copy, the correction
+// product's input); X += conv(obuf) over the block rows.
+void conv_post_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj, float proj_scale,
+                     const void* base) {
+  const dflash_config& c = h->cfg;
+  const int H = c.hidden, nc = 2 * (H / c.conv_group);
+  Phase ph(h, s, DFLASH_PH_CONV);
+  GemmArgs ga = gemm_a1(h->hbuf2, H, M, nc, H);
+  ga.out_scale = proj_scale;
+  set_b(ga, {{proj, nc}}, H);
+  EpiStore<float>::Params pc{h->cbuf, nc};
+  launch_gemm(h->op, EPI_STORE_F32, ga, &pc, plan_gemm(h->op, M, nc, H, h->num_cus), h->partials, h->partials_elems,
+              s);
+  launch_dyn_conv_post(c.dtype, M, R, H, c.conv_group, h->obuf, h->cbuf, base, h->X, s);
+}
+
+// Output projection of a sub-layer (A [M, Kd] times B^T [H, Kd]): added to the
+// residual stream, or, when an after-sub-layer convolution follows, stored for it.
+void sublayer_out(dflash_handle* h, hipStream_t s, int M, int R, const void* a, int Kd, const void* b, float b_scale,
+                  const void* post_proj, float post_scale, const void* post_base, int phase) {
+  const int H = h->cfg.hidden;
+  GemmArgs ga = gemm_a1(a, Kd, M, H, Kd);
+  ga.out_scale = b_scale;
+  set_b(ga, {{b, H}}, Kd);
+  const GemmPlan pl = plan_gemm(h->op, M, H, Kd, h->num_cus);
+  if (!post_base) {
+    EpiResidualAdd::Params pr{h->X, H};
+    Phase ph(h, s, phase);
+    launch_gemm(h->op, EPI_RESADD, ga, &pr, pl, h->partials, h->partials_elems, s);
+    return;
+  }
+  {
+    StoreDualParams pd{h->obuf, h->hbuf2, H, h->err};
+    Phase ph(h, s, phase);
+    launch_gemm(h->op, EPI_STORE_DUAL, ga, &pd, pl, h->partials, h->partials_elems, s);
+  }
+  conv_post_stage(h, s, M, R, post_proj, post_scale, post_base);
+}
+
 // DFlash 2 path selector [P2 §3.1.2-3.1.3] over rows n_req*K whose logits and
 // final-normalised hidden rows (operand type, [rows, H]) are given; row
 // statistics (row_max / row_lse) must be current.
@@ -911,16 +963,9 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       Phase ph(h, s, DFLASH_PH_ATTN_COMBINE);
       launch_attn_combine(dt, d, cb, dim3(n_req, nkv * splits, (rows_split + 15) / 16), s);
     }
-    // output projection + residual
-    {
-      GemmArgs ga = gemm_a1(h->attn_out, qdim, M, H, qdim);
-      ga.out_scale = W.s_o;
-      set_b(ga, {{W.o, H}}, qdim);
-      EpiResidualAdd::Params pr{h->X, H};
-      Phase ph(h, s, DFLASH_PH_O);
-      launch_gemm(h->op, EPI_RESADD, ga, &pr, plan_gemm(h->op, M, H, qdim, h->num_cus), h->partials,
-                  h->partials_elems, s);
-    }
+    // output projection (+ DFlash 2 convolution) + residual
+    sublayer_out(h, s, M, R, h->attn_out, qdim, W.o, W.s_o, W.conv_ap, W.s_cap,
+                 c.conv_group > 0 ? L.attn_conv_post_base : nullptr, DFLASH_PH_O);
     {
       Phase ph(h, s, DFLASH_PH_NORM);
       launch_rmsnorm(dt, M, H, h->X, 0, K, R, L.post_norm, h->hbuf, c.rms_eps, s);
@@ -945,13 +990,8 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
         launch_gemm(h->op, EPI_SWIGLU, ga, &ps, plan_gemm(h->op, M, 2 * F, H, h->num_cus), h->partials,
                     h->partials_elems, s);
       }
-      GemmArgs gd = gemm_a1(h->act, F, M, H, F);
-      gd.out_scale = W.s_down;
-      set_b(gd, {{W.down, H}}, F);
-      EpiResidualAdd::Params pr{h->X, H};
-      Phase ph(h, s, DFLASH_PH_DOWN);
-      launch_gemm(h->op, EPI_RESADD, gd, &pr, plan_gemm(h->op, M, H, F, h->num_cus), h->partials,
-                  h->partials_elems, s);
+      sublayer_out(h, s, M, R, h->act, F, W.down, W.s_down, W.conv_mp, W.s_cmp,
+                   c.conv_group > 0 ? L.mlp_conv_post_base : nullptr, DFLASH_PH_DOWN);
     }
     if (l + 1 < c.n_layers) {
       Phase ph(h, s, DFLASH_PH_NORM);

@@ -1486,6 +1486,28 @@ __global__ __launch_bounds__(64) void dyn_conv_kernel(int M, int R, int H, int G
   }
 }
 
+// After-sub-layer convolution [P2 §3.2.3]: X[m] += k_m0 * o[m] + k_m1 * o[m-1]
+// with k_mj = base[j] + corr[m] (group-shared), o[m-1] = 0 on a block's first row.
+// One thread per four channels of one row.
+template <typename W>
+__global__ __launch_bounds__(256) void dyn_conv_post_kernel(int M, int R, int H, int G, const float* o,
+                                                             const float* corr, const W* base, float* X) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int h4 = H / 4;
+  if (i >= (int64_t)M * h4) return;
+  const int m = (int)(i / h4), c = (int)(i % h4) * 4;
+  const int ng = H / G;
+  const float c0 = corr[(int64_t)m * 2 * ng + c / G], c1 = corr[(int64_t)m * 2 * ng + ng + c / G];
+  const float4 v = load4f(o + (int64_t)m * H + c), b0 = load4f(base + c), b1 = load4f(base + H + c);
+  const float4 u = m % R == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : load4f(o + (int64_t)(m - 1) * H + c);
+  float4 x = load4f(X + (int64_t)m * H + c);
+  x.x += (b0.x + c0) * v.x + (b1.x + c1) * u.x;
+  x.y += (b0.y + c0) * v.y + (b1.y + c1) * u.y;
+  x.z += (b0.z + c0) * v.z + (b1.z + c1) * u.z;
+  x.w += (b0.w + c0) * v.w + (b1.w + c1) * u.w;
+  *(float4*)(X + (int64_t)m * H + c) = x;
+}
+
 // ---------------------------------------------------------------------------
 // DFlash 2 path selector [P2 §3.1.2-3.1.3].  Candidates of mask position t are
 // the top-C ids of its logits (top-k order); candidate b following predecessor a
@@ -2113,6 +2135,17 @@ void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, cons
   else
     dyn_conv_kernel<float><<<M, 64, 0, s>>>(M, R, H, G, X, (const float*)gain, eps, corr,
                                                        (const float*)base, (float*)y);
+}
+
+void launch_dyn_conv_post(int dtype, int M, int R, int H, int G, const float* o, const float* corr,
+                          const void* base, float* X, hipStream_t s) {
+  const int64_t n = (int64_t)M * (H / 4);
+  if (n == 0) return;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (dtype == DT_BF16)
+    dyn_conv_post_kernel<bf16_t><<<blocks, 256, 0, s>>>(M, R, H, G, o, corr, (const bf16_t*)base, X);
+  else
+    dyn_conv_post_kernel<float><<<blocks, 256, 0, s>>>(M, R, H, G, o, corr, (const float*)base, X);
 }
 
 void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const int32_t* slots,

@@ -13,7 +13,8 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 enum OpType { OP_F32 = 0, OP_BF16 = 1, OP_F16 = 2 };
 
 // ---- GEMM (gemm_inst.hip) ----
-enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_T, EPI_RESADD, EPI_SWIGLU, EPI_QKV, EPI_KVINJECT, EPI_LMHEAD };
+enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_T, EPI_RESADD, EPI_SWIGLU, EPI_QKV, EPI_KVINJECT, EPI_LMHEAD,
+               EPI_STORE_DUAL };
 
 struct GemmPlan {
   int bm = 128, bn = 128, splits = 1;
@@ -102,6 +103,9 @@ void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, 
 // corrections corr [M, 2H/G]
 void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const void* gain, float eps,
                      const float* corr, const void* base, void* y, hipStream_t s);
+// X[m] += after-sub-layer convolution of o (fp32 [M, H]) with corrections corr [M, 2H/G]
+void launch_dyn_conv_post(int dtype, int M, int R, int H, int G, const float* o, const float* corr,
+                          const void* base, float* X, hipStream_t s);
 // DFlash 2: selector pair-score table (scratch [n_req*K, C, C]) and walk over cand [n_req*K, C] with
 // gate [n_req*K, rank] and codebooks A, B [V, rank]
 void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const int32_t* slots,

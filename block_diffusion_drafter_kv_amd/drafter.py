@@ -19,6 +19,7 @@ from . import (DFLASH_BF16, DFLASH_F32, dflash_config, dflash_copy_cache, dflash
 
 _LAYER_KEYS = ("in_norm", "q_w", "k_w", "v_w", "o_w", "q_norm", "k_norm", "post_norm", "gate_w", "up_w", "down_w")
 _CONV_KEYS = ("attn_conv_base", "attn_conv_proj", "mlp_conv_base", "mlp_conv_proj")
+_CONV_POST_KEYS = ("attn_conv_post_base", "attn_conv_post_proj", "mlp_conv_post_base", "mlp_conv_post_proj")
 _SEL_KEYS = ("sel_pred", "sel_succ", "sel_hidden")
 
 
@@ -63,7 +64,8 @@ class Drafter:
         self.cfg = cfg
         layers = (dflash_layer_weights * model.n_layers)()
         for l, lw in enumerate(weights["layers"]):
-            for k in _LAYER_KEYS + (_CONV_KEYS if cfg.conv_group else ()):
+            post = tuple(k for k in _CONV_POST_KEYS if k in lw) if cfg.conv_group else ()
+            for k in _LAYER_KEYS + (_CONV_KEYS if cfg.conv_group else ()) + post:
                 t = lw[k]
                 if not t.is_cuda or t.dtype != self.dtype or not t.is_contiguous():
                     raise ValueError(f"layer {l} weight {k}: need a contiguous {self.dtype} CUDA tensor")

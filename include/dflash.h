@@ -137,12 +137,21 @@ typedef struct dflash_layer_weights {
   const void* down_w;         /* [H, F]                                           */
   /* DFlash 2 dynamic convolutions (read when cfg.conv_group > 0, else ignored) [P2 §3.2.3]:
    * y_t = k_t0 * x_t + k_t1 * x_{t-1} over the block rows (x_{-1} = 0), with
-   * k_tj[c] = base[j][c] + (x_t . proj^T)[j * H/G + c/G].  attn_* acts on the
-   * RMS-normalised input of q/k/v, mlp_* on that of gate/up. */
+   * k_tj[c] = base[j][c] + (x_t . proj^T)[j * H/G + c/G], x being the
+   * convolution's own input.  One convolution before and one after each
+   * sub-layer: attn_* acts on the RMS-normalised input of q/k/v, mlp_* on that
+   * of gate/up (both required); attn_conv_post_* on the attention output (after
+   * o, before the residual add), mlp_conv_post_* on the MLP output (after down,
+   * before the residual add) -- each post pair optional (both pointers, or
+   * neither). */
   const void* attn_conv_base; /* [2, H]        per-channel kernels of the two taps (current, previous) */
   const void* attn_conv_proj; /* [2*H/G, H]    kernel corrections: rows [0,H/G) tap 0, [H/G,2H/G) tap 1 */
   const void* mlp_conv_base;  /* [2, H]                                           */
   const void* mlp_conv_proj;  /* [2*H/G, H]                                       */
+  const void* attn_conv_post_base;  /* [2, H]      or NULL                        */
+  const void* attn_conv_post_proj;  /* [2*H/G, H]  or NULL                        */
+  const void* mlp_conv_post_base;   /* [2, H]      or NULL                        */
+  const void* mlp_conv_post_proj;   /* [2*H/G, H]  or NULL                        */
 } dflash_layer_weights;
 
 typedef struct dflash_weights {

@@ -28,13 +28,19 @@ layer carries conv weights: a two-tap depthwise convolution over the block's
 rows, y_t = k_{t,0} * x_t + k_{t,1} * x_{t-1}, where each tap's kernel is a
 learned per-channel base plus a correction projected linearly from x_t and
 shared by every group of conv_group channels; the row before the anchor is zero
-(block-local, zero padding).  Readings: the layer holds two convolutions,
-attention_conv and mlp_conv; each acts on its sub-layer's input, i.e. on the
-RMS-normalised rows that feed the q/k/v projections and the gate/up
-projections respectively (the pages place them in the layer's "prepare" and
-"finish" halves); the correction projection has no bias, its output rows
-[0, H/G) correct tap 0 and rows [H/G, 2H/G) tap 1, channel c using group c // G;
-context rows are untouched (their K/V come from the fused target feature).
+(block-local, zero padding).  Readings: the pages put one convolution before
+and one after each of the attention and MLP sub-layers, four per layer, which
+is also what their parameter count needs (+16.5M for the 5-layer drafter at
+hidden 2560 with groups of 16: 20 convolutions of 2*H/16*H + 2*H weights each;
+two per layer would be 8.2M).  A "before" convolution acts on the sub-layer's
+input, the RMS-normalised rows that feed q/k/v or gate/up; an "after" one acts
+on the sub-layer's output (after o, after down) before it is added to the
+residual stream.  Each convolution's correction is projected from its own
+input rows.  Weights: attn_conv_* / mlp_conv_* (before) and attn_conv_post_* /
+mlp_conv_post_* (after); a layer may carry either pair alone.  The correction
+projection has no bias, its output rows [0, H/G) correct tap 0 and rows
+[H/G, 2H/G) tap 1, channel c using group c // G; context rows are untouched
+(their K/V come from the fused target feature).
 
 Variants [P2 §2.2 "注意力" / "输出端"; P4 §5.2]: a causal-in-block flag (block
 row i attends to the context and to block rows j <= i; the pages disagree on the
@@ -212,11 +218,17 @@ class DrafterOracle:
                                              (C, [i]) if causal else None) for i in range(R)], axis=0)
             else:
                 o = attention(q, keys, vals, c.group, (C, list(range(R))) if causal else None)
-            X = X + o.reshape(R, c.q_dim) @ lw["o_w"].T
+            o = o.reshape(R, c.q_dim) @ lw["o_w"].T
+            if "attn_conv_post_base" in lw:      # after the attention sub-layer, before the residual add
+                o = dynamic_conv(o, lw["attn_conv_post_base"], lw["attn_conv_post_proj"], c.conv_group)
+            X = X + o
             h = rms_norm(X, lw["post_norm"], c.rms_eps)
             if "mlp_conv_base" in lw:
                 h = dynamic_conv(h, lw["mlp_conv_base"], lw["mlp_conv_proj"], c.conv_group)
-            X = X + (silu(h @ lw["gate_w"].T) * (h @ lw["up_w"].T)) @ lw["down_w"].T
+            m = (silu(h @ lw["gate_w"].T) * (h @ lw["up_w"].T)) @ lw["down_w"].T
+            if "mlp_conv_post_base" in lw:       # after the MLP sub-layer, before the residual add
+                m = dynamic_conv(m, lw["mlp_conv_post_base"], lw["mlp_conv_post_proj"], c.conv_group)
+            X = X + m
         return X
 
     def block_logits(self, slot: int, anchor: int, K: int, single_query: bool = False) -> np.ndarray:

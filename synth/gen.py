@@ -106,7 +106,7 @@ def weights(cfg: DrafterConfig, seed: int = 1234, gains: str = "ones",
 
 
 def dflash2_weights(cfg: DrafterConfig, seed: int = 4321, conv_base_std: float = 0.3, conv_proj_std: float = 0.002,
-                    codebook_std: float = 0.2, sel_hidden_std: float = 0.02) -> Dict[str, object]:
+                    codebook_std: float = 0.2, sel_hidden_std: float = 0.02, post: bool = True) -> Dict[str, object]:
     """Weights of the DFlash 2 modules, in the model dtype, as CPU tensors.
 
     The pages describe the convolution's kernel as a learned base plus a small
@@ -116,7 +116,8 @@ def dflash2_weights(cfg: DrafterConfig, seed: int = 4321, conv_base_std: float =
 
     Per layer (when cfg.conv_group > 0): attn_conv_base / mlp_conv_base [2, H]
     (tap 0 drawn around 1, tap 1 around 0), attn_conv_proj / mlp_conv_proj
-    [2 * H / conv_group, H].  Shared (when cfg.sel_rank > 0): sel_pred and sel_succ
+    [2 * H / conv_group, H] for the convolutions before the sub-layers and, with
+    post=True, attn_conv_post_* / mlp_conv_post_* for those after them (same recipe).  Shared (when cfg.sel_rank > 0): sel_pred and sel_succ
     [V, rank] codebooks, sel_hidden [rank, H].  Returns {"layers": [...], ...} to
     merge into the dict of `weights`.
     """
@@ -125,13 +126,15 @@ def dflash2_weights(cfg: DrafterConfig, seed: int = 4321, conv_base_std: float =
     out: Dict[str, object] = {"layers": [{} for _ in range(cfg.n_layers)]}
     if cfg.conv_group > 0:
         G = cfg.conv_group
+        names = ("attn", "mlp", "attn_post", "mlp_post") if post else ("attn", "mlp")
         for l in range(cfg.n_layers):
-            for name in ("attn", "mlp"):
+            for name in names:
                 base = normal((2, H), conv_base_std, "f32", seed, l, name, "conv_base")
                 base[0] += 1.0
-                out["layers"][l][f"{name}_conv_base"] = base.to(torch_dtype(dt))
-                out["layers"][l][f"{name}_conv_proj"] = normal((2 * H // G, H), conv_proj_std, dt, seed, l, name,
-                                                               "conv_proj")
+                key = name.replace("_post", "_conv_post") if name.endswith("_post") else f"{name}_conv"
+                out["layers"][l][f"{key}_base"] = base.to(torch_dtype(dt))
+                out["layers"][l][f"{key}_proj"] = normal((2 * H // G, H), conv_proj_std, dt, seed, l, name,
+                                                         "conv_proj")
     if cfg.sel_rank > 0:
         r = cfg.sel_rank
         out["sel_pred"] = normal((V, r), codebook_std, dt, seed, "sel_pred")

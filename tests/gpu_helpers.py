@@ -16,11 +16,15 @@ def to_cuda(w):
 
 
 def make_pair(cfg, *, max_batch, max_ctx, max_k, max_inject_rows=4096, max_top_k=0, max_tree=0, gains="random",
-              seed=1234, lm_head_std=0.02, **kw):
+              seed=1234, lm_head_std=0.02, conv_post=True, **kw):
+    """conv_post: with DFlash 2 convolutions, also those after the sub-layers (True), none of
+    them (False), or a function editing the merged weights (e.g. dropping one layer's pair)."""
     import block_diffusion_drafter_kv_amd as dk
     w = gen.weights(cfg, seed=seed, gains=gains, lm_head_std=lm_head_std)
     if cfg.conv_group or cfg.sel_rank:
-        w = gen.merge_weights(w, gen.dflash2_weights(cfg, seed=seed + 1))
+        w = gen.merge_weights(w, gen.dflash2_weights(cfg, seed=seed + 1, post=conv_post is not False))
+    if callable(conv_post):
+        conv_post(w)
     drafter = dk.Drafter(cfg, to_cuda(w), max_batch=max_batch, max_ctx=max_ctx, max_k=max_k,
                          max_inject_rows=max_inject_rows, max_top_k=max_top_k, max_tree=max_tree, **kw)
     return drafter, od.DrafterOracle(cfg, w), w

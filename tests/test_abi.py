@@ -67,3 +67,30 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=300, env=dict(os.environ, HIP_VISIBLE_DEVICES=""))
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def _header_structs():
+    """{struct name: [field names in order]} of every typedef struct the header defines."""
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for name, body in re.findall(r"typedef struct (\w+) \{(.*?)\}\s*\1\s*;", src, flags=re.S):
+        fields = []
+        for decl in body.split(";"):
+            decl = decl.strip()
+            if not decl:
+                continue
+            # "const void* a" / "int32_t a, b" / "const dflash_layer_weights* layers"
+            head, *rest = decl.split(",")
+            fields.append(re.findall(r"(\w+)\s*$", head)[0])
+            fields += [r.strip().lstrip("*").strip() for r in rest]
+        out[name] = fields
+    return out
+
+
+@pytest.mark.parametrize("name", ["dflash_config", "dflash_layer_weights", "dflash_weights", "dflash_draft_params",
+                                  "dflash_draft_outputs"])
+def test_ctypes_structs_mirror_the_header(name):
+    structs = _header_structs()
+    assert name in structs
+    assert [f for f, _ in getattr(dk, name)._fields_] == structs[name]

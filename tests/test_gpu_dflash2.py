@@ -1,7 +1,7 @@
 """GPU parity of the DFlash 2 modules [P2 §3.1-3.2] against the oracle.
 
-* Dynamic convolutions in every layer: block logits against the exact fp64
-  forward (fp32 drafter 1e-4, bf16 drafter 2e-2), greedy ids where the oracle's
+* Dynamic convolutions in every layer (before and after each sub-layer, only
+  before, or mixed): block logits against the exact fp64 forward (fp32 drafter 1e-4, bf16 drafter 2e-2), greedy ids where the oracle's
   top-2 margin clears the logit tolerance.
 * Path selector inside dflash_draft_block: the candidates, the walk's picks and
   its candidate distribution equal dflash_select_path on the draft's own fp32
@@ -43,9 +43,20 @@ def _np(w):
     return w.float().numpy().astype(np.float64)
 
 
+def _mixed_post(w):
+    """Even layers without the after-attention convolution, odd ones without the after-MLP one."""
+    for l, lw in enumerate(w["layers"]):
+        for k in (("attn_conv_post_base", "attn_conv_post_proj") if l % 2 == 0 else
+                  ("mlp_conv_post_base", "mlp_conv_post_proj")):
+            del lw[k]
+
+
+@pytest.mark.parametrize("post", [True, False, _mixed_post], ids=["four", "two", "mixed"])
 @pytest.mark.parametrize("cfg", [CONV_F32, CONV_BF16], ids=["f32", "bf16"])
-def test_conv_forward_parity(gpu_lib, cfg):
-    dr, orc, _ = make_pair(cfg, max_batch=3, max_ctx=256, max_k=8)
+def test_conv_forward_parity(gpu_lib, cfg, post):
+    """Four convolutions per layer (before and after each sub-layer), only the two before, or
+    a mix across layers."""
+    dr, orc, _ = make_pair(cfg, max_batch=3, max_ctx=256, max_k=8, conv_post=post)
     slots, counts = [0, 2, 1], [37, 90, 5]
     inject_both(dr, orc, cfg, slots, counts, [0, 0, 0])
     K = 6

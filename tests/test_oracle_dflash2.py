@@ -125,9 +125,9 @@ def test_identity_conv_leaves_forward_unchanged():
     orc, w = _df2_oracle()
     H = cfg.hidden
     for lw in w["layers"]:
-        for name in ("attn", "mlp"):
-            lw[f"{name}_conv_base"] = torch.stack([torch.ones(H), torch.zeros(H)])
-            lw[f"{name}_conv_proj"] = torch.zeros_like(lw[f"{name}_conv_proj"])
+        for key in ("attn_conv", "mlp_conv", "attn_conv_post", "mlp_conv_post"):
+            lw[f"{key}_base"] = torch.stack([torch.ones(H), torch.zeros(H)])
+            lw[f"{key}_proj"] = torch.zeros_like(lw[f"{key}_proj"])
     plain = {k: v for k, v in w.items()}
     plain["layers"] = [{k: v for k, v in lw.items() if "conv" not in k} for lw in w["layers"]]
     a, b = od.DrafterOracle(cfg, w), od.DrafterOracle(cfg, plain)
@@ -135,6 +135,66 @@ def test_identity_conv_leaves_forward_unchanged():
     a.inject(0, rows)
     b.inject(0, rows)
     np.testing.assert_array_equal(a.block_logits(0, 7, 4), b.block_logits(0, 7, 4))
+
+
+def test_four_convolutions_per_layer_match_the_pages_parameter_count():
+    """[P2 §3.2.3-3.2.4]: a convolution before and after each attention and MLP sub-layer
+    adds +16.5M parameters to the 5-layer Qwen3-4B-shaped drafter (hidden 2560, groups of
+    16); two per layer would add half of that."""
+    cfg = scaled_model(TINY, n_layers=5, hidden=2560, conv_group=16, sel_rank=0)
+    per_layer = [k for k in gen.dflash2_weights(scaled_model(TINY, conv_group=16), seed=1)["layers"][0]]
+    assert sorted(per_layer) == sorted(["attn_conv_base", "attn_conv_proj", "mlp_conv_base", "mlp_conv_proj",
+                                        "attn_conv_post_base", "attn_conv_post_proj", "mlp_conv_post_base",
+                                        "mlp_conv_post_proj"])
+    H, G = cfg.hidden, cfg.conv_group
+    one = 2 * (H // G) * H + 2 * H                 # correction projection + the two base taps
+    assert abs(cfg.n_layers * 4 * one - 16.5e6) < 0.05e6
+    assert abs(cfg.n_layers * 2 * one - 16.5e6) > 8e6
+
+
+def _single_layer(w, keep_attn: bool, keep_mlp: bool):
+    """One layer's weights with the attention (o) or the MLP (down) output zeroed."""
+    w = dict(w)
+    lw = dict(w["layers"][0])
+    if not keep_attn:
+        lw["o_w"] = torch.zeros_like(lw["o_w"])
+    if not keep_mlp:
+        lw["down_w"] = torch.zeros_like(lw["down_w"])
+    w["layers"] = [lw]
+    return w
+
+
+@pytest.mark.parametrize("which", ["attn", "mlp"])
+def test_after_convolution_acts_on_the_sub_layer_output(which):
+    """With the other sub-layer's output zeroed, the residual after one layer is the
+    embedding plus the sub-layer's output; a pure previous-row kernel in the convolution
+    after that sub-layer shifts exactly that output by one row (zero at the anchor)."""
+    cfg = scaled_model(TINY, n_layers=1, conv_group=16)
+    base_w = gen.merge_weights(gen.weights(cfg, seed=7), gen.dflash2_weights(cfg, seed=8))
+    H = cfg.hidden
+    w = _single_layer(base_w, keep_attn=which == "attn", keep_mlp=which == "mlp")
+    lw = w["layers"][0]
+    for key in ("attn_conv", "mlp_conv"):         # the convolutions before the sub-layers: identity
+        lw[f"{key}_base"] = torch.stack([torch.ones(H), torch.zeros(H)])
+        lw[f"{key}_proj"] = torch.zeros_like(lw[f"{key}_proj"])
+    other = "mlp" if which == "attn" else "attn"
+    lw[f"{other}_conv_post_base"] = torch.stack([torch.ones(H), torch.zeros(H)])
+    lw[f"{other}_conv_post_proj"] = torch.zeros_like(lw[f"{other}_conv_post_proj"])
+    ident = {k: v for k, v in lw.items()}
+    ident[f"{which}_conv_post_base"] = torch.stack([torch.ones(H), torch.zeros(H)])
+    ident[f"{which}_conv_post_proj"] = torch.zeros_like(lw[f"{which}_conv_post_proj"])
+    shift = dict(ident)
+    shift[f"{which}_conv_post_base"] = torch.stack([torch.zeros(H), torch.ones(H)])
+    rows = gen.hidden_rows(cfg, 0, 0, 12)
+    res = {}
+    for name, layer in (("ident", ident), ("shift", shift)):
+        o = od.DrafterOracle(cfg, dict(w, layers=[layer]))
+        o.inject(0, rows)
+        res[name] = o.block_hidden(0, 9, 5)
+    emb = od.DrafterOracle(cfg, w).embed[[9] + [cfg.mask_token_id] * 5] * cfg.input_embedding_scale
+    out = res["ident"] - emb                       # the sub-layer's output
+    want = emb + np.concatenate([np.zeros((1, H)), out[:-1]], axis=0)
+    np.testing.assert_allclose(res["shift"], want, rtol=1e-12, atol=1e-12)
 
 
 def test_conv_forward_invariants():
