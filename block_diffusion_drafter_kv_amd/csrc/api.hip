@@ -453,11 +453,11 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc_t(h, &h->seg_desc, (size_t)c.max_batch * nkv * splits, 16))) break;
     if ((rc = alloc_t(h, &h->wg_range, (size_t)h->attn_wg, 16))) break;
     if ((rc = alloc_t(h, &h->dslots, c.max_batch, 4))) break;
-    // split-K is used only while tiles * splits <= 2 * CUs: bounded by that many output tiles
     // split-K partials: grids of at most 2 * CUs tiles, or a four-way split of the
-    // long-K products over the draft's rows (M x H each)
-    h->partials_elems = std::max((size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(h->op),
-                                 (size_t)4 * ((h->maxM + 127) / 128 * 128) * H);
+    // long-K products over the draft's rows (M x H each, rows padded to 128- or
+    // 192-row tiles); a product needing more runs with fewer splits
+    const size_t mpad = std::max((h->maxM + 127) / 128 * 128, (h->maxM + 191) / 192 * 192);
+    h->partials_elems = std::max((size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(h->op), (size_t)4 * mpad * H);
     if ((rc = alloc_t(h, &h->partials, h->partials_elems, 4))) break;
     const size_t lrows = (size_t)c.max_batch * c.max_k;
     if ((rc = alloc_t(h, &h->logits_ws, lrows * c.vocab, 4))) break;

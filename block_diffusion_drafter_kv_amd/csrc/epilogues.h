@@ -47,14 +47,31 @@ struct EpiStoreDual {
 };
 
 // ---- residual add into the fp32 stream ----
+// Four columns per thread and item; every item's X load is issued before the
+// first add, so the loads' latencies overlap (the stores into X would otherwise
+// order each load after the previous item's store).  N and ld are multiples of 4.
 struct EpiResidualAdd {
   struct Params { float* x; int64_t ld; };
   template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int, int tid) {
-    for (int idx = tid; idx < ROWS * BN; idx += 256) {
-      const int r = idx / BN, c = idx % BN;
+    constexpr int C4 = BN / 4, NV = ROWS * C4 / 256;
+    static_assert(ROWS * C4 % 256 == 0, "whole items per thread");
+    float4 xv[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int idx = tid + j * 256, r = idx / C4, c = 4 * (idx % C4);
       const int m = m0 + r, n = n0 + c;
-      if (m < M && n < N) p.x[(int64_t)m * p.ld + n] += st[r * ld + c];
+      xv[j] = m < M && n < N ? *(const float4*)(p.x + (int64_t)m * p.ld + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int idx = tid + j * 256, r = idx / C4, c = 4 * (idx % C4);
+      const int m = m0 + r, n = n0 + c;
+      if (m < M && n < N) {
+        const float* sr = st + r * ld + c;
+        *(float4*)(p.x + (int64_t)m * p.ld + n) =
+            make_float4(xv[j].x + sr[0], xv[j].y + sr[1], xv[j].z + sr[2], xv[j].w + sr[3]);
+      }
     }
   }
 };
@@ -113,41 +130,75 @@ struct EpiQKV {
   };
   template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
+    if (p.d == 128) run<128, BN, ROWS>(p, st, ld, m0, n0, M, tid);
+    else run<64, BN, ROWS>(p, st, ld, m0, n0, M, tid);
+  }
+  // The items (row, head) of a wave are fixed at compile time, so every global
+  // load they need -- slot, context length, RoPE pair -- is issued for all of
+  // them before the first one is used.
+  template <int D, int BN, int ROWS>
+  __device__ static void run(const Params& p, const float* st, int ld, int m0, int n0, int M, int tid) {
+    constexpr int HALF = D / 2, PER = 64 / HALF, HEADS = BN / D, ITEMS = ROWS * HEADS;
+    constexpr int NIT = ITEMS / (4 * PER);
+    static_assert(BN % D == 0 && ITEMS % (4 * PER) == 0, "whole items per wave");
     const int lane = tid & 63, wave = tid >> 6;
-    const int half = p.d / 2;
-    const int per = 64 / half;  // items per wave iteration
-    const int sub = lane / half, i = lane % half;
-    const int heads = BN / p.d;
-    const int items = ROWS * heads;
+    const int sub = lane / HALF, i = lane % HALF;
+    int m_[NIT], j_[NIT], req_[NIT], nb_[NIT];
+    int pos_[NIT];
+    float2 cs_[NIT];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const int it = (k * 4 + wave) * PER + sub;
+      const int r = it / HEADS, hh = it % HEADS;
+      m_[k] = m0 + r;
+      req_[k] = m_[k] / p.R;
+      j_[k] = m_[k] % p.R;
+      nb_[k] = n0 + hh * D;
+    }
+    // rows past M load request 0's values (never used)
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) pos_[k] = p.slots[m_[k] < M ? req_[k] : 0];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) pos_[k] = p.ctx_len[pos_[k]] + j_[k];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) cs_[k] = p.rope[(int64_t)pos_[k] * HALF + i];
+    const float qg1 = to_f32(p.q_gain[i]), qg2 = to_f32(p.q_gain[i + HALF]);
+    const float kg1 = to_f32(p.k_gain[i]), kg2 = to_f32(p.k_gain[i + HALF]);
     bool bad = false;
-    for (int it = wave * per + sub; it < items; it += 4 * per) {
-      const int r = it / heads, hh = it % heads;
-      const int m = m0 + r;
-      if (m >= M) continue;
-      const int req = m / p.R, j = m % p.R;
-      const int nb = n0 + hh * p.d;
-      float x1 = st[r * ld + hh * p.d + i], x2 = st[r * ld + hh * p.d + i + half];
-      if (nb < p.q_dim + p.kv_dim) {
-        const int slot = p.slots[req];
-        const int pos = p.ctx_len[slot] + j;
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const int it = (k * 4 + wave) * PER + sub;
+      const int r = it / HEADS, hh = it % HEADS;
+      const int m = m_[k], req = req_[k], j = j_[k], nb = nb_[k];
+      float x1 = st[r * ld + hh * D + i], x2 = st[r * ld + hh * D + i + HALF];
+      if (nb < p.q_dim + p.kv_dim) {   // q or k head: RMSNorm + RoPE (every lane of the group reduces)
         const bool isq = nb < p.q_dim;
-        norm_rope_pair<W>(x1, x2, i, p.d, isq ? p.q_gain : p.k_gain, p.eps, p.rope + (int64_t)pos * half);
+        const float ss = group_sum(x1 * x1 + x2 * x2, HALF);
+        const float rs = rsqrtf(ss / (float)D + p.eps);
+        x1 *= rs * (isq ? qg1 : kg1);
+        x2 *= rs * (isq ? qg2 : kg2);
+        const float2 cs = cs_[k];
+        const float y1 = x1 * cs.x - x2 * cs.y, y2 = x2 * cs.x + x1 * cs.y;
+        x1 = y1;
+        x2 = y2;
+        if (m >= M) continue;
         if (isq) {
-          const int qh = nb / p.d, kv = qh / p.group, gi = qh % p.group;
-          T* dst = p.qb + ((int64_t)(req * p.n_kv + kv) * p.QRpad + gi * p.R + j) * p.d;
+          const int qh = nb / D, kv = qh / p.group, gi = qh % p.group;
+          T* dst = p.qb + ((int64_t)(req * p.n_kv + kv) * p.QRpad + gi * p.R + j) * D;
           dst[i] = store_cvt<T>(x1, bad);
-          dst[i + half] = store_cvt<T>(x2, bad);
+          dst[i + HALF] = store_cvt<T>(x2, bad);
         } else {
-          const int kh = (nb - p.q_dim) / p.d;
-          T* dst = p.kb + (int64_t)(req * p.n_kv + kh) * p.Rpad * p.d;
-          dst[k_off(j, i, p.d)] = store_cvt<T>(x1, bad);
-          dst[k_off(j, i + half, p.d)] = store_cvt<T>(x2, bad);
+          const int kh = (nb - p.q_dim) / D;
+          T* dst = p.kb + (int64_t)(req * p.n_kv + kh) * p.Rpad * D;
+          dst[k_off(j, i, D)] = store_cvt<T>(x1, bad);
+          dst[k_off(j, i + HALF, D)] = store_cvt<T>(x2, bad);
         }
       } else {
-        const int vh = (nb - p.q_dim - p.kv_dim) / p.d;
-        T* dst = p.vb + (int64_t)(req * p.n_kv + vh) * p.Rpad * p.d;
-        dst[v_off(j, i, p.d)] = store_cvt<T>(x1, bad);
-        dst[v_off(j, i + half, p.d)] = store_cvt<T>(x2, bad);
+        if (m >= M) continue;
+        const int vh = (nb - p.q_dim - p.kv_dim) / D;
+        T* dst = p.vb + (int64_t)(req * p.n_kv + vh) * p.Rpad * D;
+        dst[v_off(j, i, D)] = store_cvt<T>(x1, bad);
+        dst[v_off(j, i + HALF, D)] = store_cvt<T>(x2, bad);
       }
     }
     report_nonfinite(p.err, bad, tid);

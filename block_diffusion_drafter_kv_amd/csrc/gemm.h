@@ -47,6 +47,15 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row: chunk c of
+// row r is stored at slot c ^ swz(r).  A fragment read takes one chunk from 16
+// consecutive rows per LDS cycle (64 banks of 4 bytes): rows of one parity share
+// banks when they share a slot, so swz must differ across the 8 even and across
+// the 8 odd rows of every aligned group of 16 -- and, for 8-lane phases, across
+// every aligned group of 8 rows.  (row & 7) ^ ((row >> 3) & 1) does both; plain
+// row & 7 leaves rows r and r + 8 in the same banks.
+__host__ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 template <typename T> struct GemmTraits;
 template <> struct GemmTraits<bf16_t> { static constexpr int BK = 64; static constexpr int VEC = 8; };
 template <> struct GemmTraits<f16_t> { static constexpr int BK = 64; static constexpr int VEC = 8; };
@@ -164,12 +173,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g, const typen
 #pragma unroll
     for (int p = 0; p < AL; ++p) {
       const int row = lrow + 32 * p;
-      smem[buf][row * 8 + (lchunk ^ (row & 7))] = *(const uint4*)&ra[p];
+      smem[buf][row * 8 + (lchunk ^ swz(row))] = *(const uint4*)&ra[p];
     }
 #pragma unroll
     for (int p = 0; p < BL; ++p) {
       const int row = lrow + 32 * p;
-      smem[buf][(BM + row) * 8 + (lchunk ^ (row & 7))] = *(const uint4*)&rb[p];
+      smem[buf][(BM + row) * 8 + (lchunk ^ swz(row))] = *(const uint4*)&rb[p];
     }
   };
 
@@ -196,11 +205,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g, const typen
         const int row = wm * WM + fi * 16 + r16;
         if constexpr (VEC == 8) {
           const int c = s * 4 + grp;
-          *(uint4*)&af[fi] = smem[cur][row * 8 + (c ^ (row & 7))];
+          *(uint4*)&af[fi] = smem[cur][row * 8 + (c ^ swz(row))];
         } else {
           const int c = 2 * grp;
-          ((uint4*)&af[fi])[0] = smem[cur][row * 8 + (c ^ (row & 7))];
-          ((uint4*)&af[fi])[1] = smem[cur][row * 8 + ((c + 1) ^ (row & 7))];
+          ((uint4*)&af[fi])[0] = smem[cur][row * 8 + (c ^ swz(row))];
+          ((uint4*)&af[fi])[1] = smem[cur][row * 8 + ((c + 1) ^ swz(row))];
         }
       }
 #pragma unroll
@@ -209,11 +218,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g, const typen
         const int rr = wn * WN + fj * 16 + r16;
         if constexpr (VEC == 8) {
           const int c = s * 4 + grp;
-          *(uint4*)&bfr[fj] = smem[cur][row * 8 + (c ^ (rr & 7))];
+          *(uint4*)&bfr[fj] = smem[cur][row * 8 + (c ^ swz(rr))];
         } else {
           const int c = 2 * grp;
-          ((uint4*)&bfr[fj])[0] = smem[cur][row * 8 + (c ^ (rr & 7))];
-          ((uint4*)&bfr[fj])[1] = smem[cur][row * 8 + ((c + 1) ^ (rr & 7))];
+          ((uint4*)&bfr[fj])[0] = smem[cur][row * 8 + (c ^ swz(rr))];
+          ((uint4*)&bfr[fj])[1] = smem[cur][row * 8 + ((c + 1) ^ swz(rr))];
         }
       }
 #pragma unroll
@@ -264,7 +273,8 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const GemmArgs g, cons
   const int m_base = tm * BM, n_base = tn * BN;
   if (g.m_valid && m_base >= *g.m_valid - g.m_valid_base) return;
   const int m0 = m_base + blockIdx.y * EPI_ROWS;
-  if (m0 >= g.M) return;
+  const int m_lim = min(g.M, m_base + BM);   // rows of this tile (BM need not be a multiple of EPI_ROWS)
+  if (m0 >= m_lim) return;
   // 16-byte loads, two splits in flight at once; sums taken in split order
   constexpr int C4 = BN / 4, NV = EPI_ROWS * C4 / 256;
   static_assert(EPI_ROWS * C4 % 256 == 0, "reduce tiling");
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const GemmArgs g, cons
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int idx = tid + j * 256, r = idx / C4, c4 = idx % C4;
-      v[j] = m0 + r < g.M ? *(const float4*)(g.partials + sp * split_stride + (int64_t)(m0 + r) * g.Npad + n_base + 4 * c4)
+      v[j] = m0 + r < m_lim ? *(const float4*)(g.partials + sp * split_stride + (int64_t)(m0 + r) * g.Npad + n_base + 4 * c4)
                           : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
@@ -312,7 +322,13 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const GemmArgs g, cons
     d[3] = acc[j].w * g.out_scale;
   }
   __syncthreads();
-  Epi::template apply<BN, EPI_ROWS>(ep, stage, BN + 1, m0, n_base, g.M, g.N, tn, tid);
+  Epi::template apply<BN, EPI_ROWS>(ep, stage, BN + 1, m0, n_base, m_lim, g.N, tn, tid);
+}
+
+// grid of the reduction of a BM-row tiling: one block per EPI_ROWS rows of every tile
+template <int BM>
+__host__ __forceinline__ dim3 reduce_grid(const GemmArgs& g) {
+  return dim3(g.tiles_m * g.tiles_n, (BM + EPI_ROWS - 1) / EPI_ROWS);
 }
 
 }  // namespace dfl

@@ -29,18 +29,42 @@ GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide, bool big
     p.sb = 3;
     return p;
   }
+  if (w16 && K >= 8192 && M > 256 && M <= 768) {
+    // long products over a few hundred rows (the MLP down projection): 192 x 128
+    // tiles, K split in four (544 x 4096 x 12288 with a plain store: 84 us,
+    // against 100 us for 128 x 128 tiles with a 3-deep weight ring)
+    p.bm = 192;
+    p.splits = 4;
+    return p;
+  }
   if (w16 && K >= 8192 && M > 64 && M <= 1024) {
-    // long products over few rows (the MLP down projection): 128 x 128, 3-deep
-    // weight ring, K split in four (544 x 4096 x 12288: 101 us, against 120 us
-    // for 64 x 128 tiles without a split)
+    // the same products over fewer or more rows: 128 x 128, 3-deep weight ring,
+    // K split in four (544 x 4096 x 12288: 101 us, against 120 us for 64 x 128
+    // tiles without a split)
     p.sb = 3;
     p.splits = 4;
     return p;
   }
+  if (w16 && M > 256 && M <= 768 && N >= 2048 && N <= 4096 && K <= 4096 && N % 64 == 0) {
+    // square-ish products over a few hundred rows (the attention output
+    // projection): 96 x 64 tiles with 4-deep rings, two or more work-groups
+    // per CU (544 x 4096 x 4096 with a plain store: 41.5 us, against 49 us for
+    // 64 x 128 tiles)
+    p.bm = 96;
+    p.bn = 64;
+    return p;
+  }
+  if (w16 && M > 256 && M <= 768 && N <= 1024 && N % 64 == 0) {
+    // narrow products over a few hundred rows (the DFlash 2 kernel corrections):
+    // 64 x 64 tiles, K split below (544 x 512 x 4096: 17.8 us with a four-way
+    // split, against 20.6 us for 64 x 128 tiles)
+    p.bm = 64;
+    p.bn = 64;
+  }
   // 16-bit: 64-row tiles (3 LDS stages, two work-groups per CU) whenever 128-row
   // tiles would leave fewer than two work-groups per CU (measured on the draft's
   // 544-row products: O 66 -> 45 us, down 175 -> 116 us, QKV 69 -> 56 us)
-  if (w16 && p.bm == 128 && (long)((M + 127) / 128) * ((N + p.bn - 1) / p.bn) < 2L * num_cus)
+  if (w16 && p.bm == 128 && p.bn == 128 && (long)((M + 127) / 128) * ((N + p.bn - 1) / p.bn) < 2L * num_cus)
     p.bm = 64;
   const int bk = w16 ? 64 : 32;
   const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
@@ -58,8 +82,32 @@ GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide, bool big
   return p;
 }
 
-void launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan, float* partials,
+// The tilings gemm_cfg instantiates for an operand type and epilogue; anything
+// else becomes 128 x 128.  The tile counts and split-K partials below are sized
+// from the returned plan, so the kernel that runs always matches them.
+static GemmPlan runnable_plan(int op, EpiKind kind, GemmPlan p) {
+  const bool wide_epi = kind == EPI_QKV || kind == EPI_KVINJECT || kind == EPI_LMHEAD;
+  const bool big_epi = kind == EPI_STORE_F32 || kind == EPI_KVINJECT || kind == EPI_LMHEAD;
+  if (op == OP_F32) {
+    p.bm = p.bm == 64 ? 64 : 128;
+    p.bn = 128;
+    p.sb = 0;
+    return p;
+  }
+  if (p.bm == 256 && p.bn == 256 && big_epi) return p;
+  if (p.bn == 128 && (p.bm == 64 || p.bm == 192 || p.bm == 128)) {
+    if (p.bm != 128) p.sb = 0;
+    return p;
+  }
+  if (p.bn == 64 && (p.bm == 96 || p.bm == 64) && !wide_epi) return p;
+  p.bm = p.bn = 128;
+  p.sb = 0;
+  return p;
+}
+
+void launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan_in, float* partials,
                  size_t partials_elems, hipStream_t s) {
+  const GemmPlan plan = runnable_plan(op, kind, plan_in);
   const int bk = op != OP_F32 ? 64 : 32;
   g.tiles_m = (g.M + plan.bm - 1) / plan.bm;
   g.tiles_n = (g.N + plan.bn - 1) / plan.bn;

@@ -44,12 +44,12 @@ static void gemm2_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (g.a_wide) {
       gemm2_kernel<T, BM, BN, SA, SB, Epi, true><<<grid, 256, 0, s>>>(g, p);
-      if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<dim3(g.tiles_m * g.tiles_n, BM / EPI_ROWS), 256, 0, s>>>(g, p);
+      if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
       return;
     }
   }
   gemm2_kernel<T, BM, BN, SA, SB, Epi><<<grid, 256, 0, s>>>(g, p);
-  if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<dim3(g.tiles_m * g.tiles_n, BM / EPI_ROWS), 256, 0, s>>>(g, p);
+  if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
 }
 
 template <int BM, class Epi>
@@ -57,8 +57,15 @@ static void gemm1_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   const typename Epi::Params& p = *(const typename Epi::Params*)ep;
   dim3 grid(gemm_grid(g.tiles_m * g.tiles_n), g.splits);
   gemm_kernel<float, BM, 128, Epi><<<grid, 256, 0, s>>>(g, p);
-  if (g.splits > 1) gemm_reduce_kernel<BM, 128, Epi><<<dim3(g.tiles_m * g.tiles_n, BM / EPI_ROWS), 256, 0, s>>>(g, p);
+  if (g.splits > 1) gemm_reduce_kernel<BM, 128, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
 }
+
+// Epilogues that work on whole heads or whole 128-column statistics tiles need
+// output tiles at least 128 wide.
+template <class Epi> struct EpiNeedsWide { static constexpr bool value = false; };
+template <typename T> struct EpiNeedsWide<EpiQKV<T>> { static constexpr bool value = true; };
+template <typename T> struct EpiNeedsWide<EpiKVInject<T>> { static constexpr bool value = true; };
+template <> struct EpiNeedsWide<EpiLMHead> { static constexpr bool value = true; };
 
 template <typename T, class Epi>
 static void gemm_cfg(const GemmPlan& pl, const GemmArgs& g, const void* ep, hipStream_t s) {
@@ -69,9 +76,18 @@ static void gemm_cfg(const GemmPlan& pl, const GemmArgs& g, const void* ep, hipS
         return;
       }
     }
-    if (pl.bm == 64) gemm2_go<T, 64, 128, 3, 3, Epi>(g, ep, s);
-    else if (pl.sb == 3) gemm2_go<T, 128, 128, 2, 3, Epi>(g, ep, s);
-    else gemm2_go<T, 128, 128, 2, 2, Epi>(g, ep, s);
+    // the 16-bit tilings (BM x BN, A ring, B ring): exactly the plans that
+    // runnable_plan lets through (anything else arrives as 128 x 128)
+    if (pl.bm == 64 && pl.bn == 128) gemm2_go<T, 64, 128, 3, 3, Epi>(g, ep, s);
+    else if (pl.bm == 192 && pl.bn == 128) gemm2_go<T, 192, 128, 2, 2, Epi>(g, ep, s);
+    else if (pl.bm == 128 && pl.bn == 128 && pl.sb == 3) gemm2_go<T, 128, 128, 2, 3, Epi>(g, ep, s);
+    else if constexpr (!EpiNeedsWide<Epi>::value) {
+      if (pl.bm == 96 && pl.bn == 64) gemm2_go<T, 96, 64, 4, 4, Epi>(g, ep, s);
+      else if (pl.bm == 64 && pl.bn == 64) gemm2_go<T, 64, 64, 4, 4, Epi>(g, ep, s);
+      else gemm2_go<T, 128, 128, 2, 2, Epi>(g, ep, s);
+    } else {
+      gemm2_go<T, 128, 128, 2, 2, Epi>(g, ep, s);
+    }
   } else {
     if (pl.bm == 64) gemm1_go<64, Epi>(g, ep, s);
     else gemm1_go<128, Epi>(g, ep, s);

@@ -18,10 +18,10 @@ enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_T, EPI_RESADD, EPI_SWIGLU, EPI_QKV, 
 
 struct GemmPlan {
   int bm = 128, bn = 128, splits = 1;
-  int sb = 0;   // 16-bit 128-row tiles: B ring depth (2, or 3 with a 2-deep A ring); 0 = 2
+  int sb = 0;   // 16-bit 128 x 128 tiles: B ring depth 3 (with a 2-deep A ring), else 2
 };
-// output tile width of every GEMM, so also the column width of the LM-head
-// statistics tiles
+// output tile width of the products whose epilogue keeps per-tile statistics
+// (the LM head): the column width of its statistics tiles
 inline int gemm_bn(int) { return 128; }
 // Choose tile/split for an M x N x K product (K multiple of the slab); wide = the
 // vocabulary product (widest tiles).

@@ -408,14 +408,15 @@ def test_full_dflash2_qwen_shape(gpu_lib):
     B, K, C, V = 8, 16, cfg.sel_cands, cfg.vocab
     w = gen.merge_weights(gen.weights(cfg, seed=1234), gen.dflash2_weights(cfg, seed=1235))
     import block_diffusion_drafter_kv_amd as dk
-    dr = dk.Drafter(cfg, to_cuda(w), max_batch=B, max_ctx=2048, max_k=K, max_inject_rows=8192)
-    ctx = [1024, 300, 777, 64, 1500, 12, 900, 400]
+    BW = 32                                  # the bench batch: 544 block rows through every product
+    dr = dk.Drafter(cfg, to_cuda(w), max_batch=BW, max_ctx=2048, max_k=K, max_inject_rows=8192)
+    ctx = [1024, 300, 777, 64, 1500, 12, 900, 400] + [40 + 7 * r for r in range(BW - B)]
     rows = []
     for r, c in enumerate(ctx):
         x = gen.hidden_rows(cfg, r, 0, c)
         rows.append(x)
         dr.inject(_dev([r]), _dev([0]), _dev([c]), c, x.cuda().contiguous())
-    anchors = gen.anchor_ids(cfg, B, seed=21)
+    anchors = gen.anchor_ids(cfg, BW, seed=21)
     W_H = w["sel_hidden"].float().numpy().astype(np.float64)
     A = w["sel_pred"].float().numpy().astype(np.float64)
     Bc = w["sel_succ"].float().numpy().astype(np.float64)
@@ -423,9 +424,9 @@ def test_full_dflash2_qwen_shape(gpu_lib):
     zs = gen.logits_like((B, K, V), 2.0, 61, "sel").numpy().astype(np.float32)
     hs = torch.randn((B, K, cfg.hidden), generator=torch.Generator().manual_seed(62)).half().float().numpy()
     for T in (0.0, 1.0):
-        o = dr.draft(_dev(np.arange(B)), _dev(anchors), K, temperature=T, seed=3, step=1, want_logits=True,
+        o = dr.draft(_dev(np.arange(B)), _dev(anchors[:B]), K, temperature=T, seed=3, step=1, want_logits=True,
                      want_hidden=True)
-        sp = dr.select_path(_dev(np.arange(B)), _dev(anchors), o["logits"], o["hidden"], temperature=T, seed=3,
+        sp = dr.select_path(_dev(np.arange(B)), _dev(anchors[:B]), o["logits"], o["hidden"], temperature=T, seed=3,
                             step=1)
         torch.cuda.synchronize()
         assert torch.equal(o["cand_ids"], sp["cand_ids"]) and torch.equal(o["draft_ids"], sp["draft_ids"])
@@ -437,7 +438,13 @@ def test_full_dflash2_qwen_shape(gpu_lib):
             err = assert_close_report(o["logits"][0].cpu().numpy(), zw, atol=2e-2, what="DFlash 2 logits, request 0")
             print(f"[parity] DFlash 2 logits max error {err:.3e}", flush=True)
             del orc
-        sel = dr.select_path(_dev(np.arange(B)), _dev(anchors), torch.tensor(zs, device="cuda"),
+            # the same request inside a batch of 32 (the tilings of 544-row products)
+            ow = dr.draft(_dev(np.arange(BW)), _dev(anchors), K, temperature=0.0, seed=3, step=1, want_logits=True)
+            torch.cuda.synchronize()
+            err = assert_close_report(ow["logits"][0].cpu().numpy(), zw, atol=2e-2,
+                                      what="DFlash 2 logits, request 0 of 32")
+            print(f"[parity] DFlash 2 logits (batch 32) max error {err:.3e}", flush=True)
+        sel = dr.select_path(_dev(np.arange(B)), _dev(anchors[:B]), torch.tensor(zs, device="cuda"),
                              torch.tensor(hs, device="cuda"), temperature=T, seed=3, step=1)
         torch.cuda.synchronize()
         tal = Tally(f"selector walks at T={T}, seeded inputs")
