@@ -262,221 +262,4 @@ __global__ __launch_bounds__(GEMM256_THREADS) void gemm256_kernel(const GemmArgs
   }
 }
 
-// ---------------------------------------------------------------------------
-// The same 256 x 256 tile with one wave per SIMD: 4 waves (2 x 2), each owning
-// 128 x 128 outputs as 4 x 4 blocks of v_mfma_f32_32x32x16.  Per 16-wide k step
-// a wave reads 8 fragments (8 KB) from LDS for 16 MFMAs -- 64 flops per LDS
-// byte against 43 with 8 waves of 128 x 64 -- so the LDS reads of a k step (32
-// KB per CU) take half the time of its MFMAs and the copies into the other
-// stage (16 KB per k step) fit beside them.  The accumulators take 256 of the
-// wave's 512 registers.
-//
-// With no second wave on the SIMD to cover latencies, the instruction order is
-// fixed by hand (scheduling fences between groups): in every k step each of the
-// 16 MFMAs is followed by at most one fragment read for the next k step (in the
-// order the next step consumes them) or one copy of slab kt+1; the copies of
-// slab kt+1 are issued in the first two k steps of slab kt, the barrier that
-// publishes them sits after the first 8 MFMAs of the last k step.  The slab
-// loop has no branch: the last slab is peeled.  A is one buffer (a_nseg == 1).
-// ---------------------------------------------------------------------------
-constexpr int GEMM256Q_THREADS = 256;
-
-template <typename T, class Epi>
-__global__ __launch_bounds__(GEMM256Q_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm256q_kernel(const GemmArgs g, const typename Epi::Params ep) {
-  static_assert(sizeof(T) == 2, "16-bit operands");
-  typedef typename Mfma32<T>::type FragT;
-  constexpr int FM = 4, FN = 4, WGM = 2;
-  constexpr int NT = GEMM256Q_THREADS;
-  constexpr int WM = 32 * FM, WN = 32 * FN;
-  constexpr int BM = GEMM256_TILE, BN = GEMM256_TILE;
-  constexpr int BK = 64;
-  constexpr int RPC = NT / 8;                  // rows per copy round (8 chunks of 16 bytes per row)
-  constexpr int NA = BM / RPC, NB = BN / RPC, NL = NA + NB;
-  static_assert(NL == 16, "16 copies per slab: 8 in each of the first two k steps");
-  constexpr int ER = 32;                       // epilogue rows per pass
-  constexpr int PF_DIST = 3;                   // slab kt+3 is pulled into L2 during slab kt
-  static_assert(ER * (BN + 1) * 4 <= 2 * (BM + BN) * 128, "epilogue slab must fit the stages");
-
-  __shared__ uint4 smem[2 * (BM + BN) * 8];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % WGM, wn = wave / WGM;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  if (logical >= g.tiles_m * g.tiles_n) return;
-  int tm, tn;
-  grouped_tile(logical, g.tiles_m, g.tiles_n, min(GEMM256_GROUP_M, g.tiles_m), tm, tn);
-  const int split = blockIdx.y;
-  const int m_base = tm * BM, n_base = tn * BN;
-  if (g.m_valid && m_base >= *g.m_valid - g.m_valid_base) return;
-  const int k_begin = split * g.k_per_split;
-  const int k_end = min(g.K, k_begin + g.k_per_split);
-  const int nk = max(0, (k_end - k_begin) / BK);
-
-  // copy slots: round i covers rows [i*RPC, (i+1)*RPC); wave w's instruction of a
-  // round fills rows i*RPC + 8w .. +7, lane l -> row +l/8, slot l%8, which holds
-  // logical chunk (l%8) ^ swz(row).
-  const int crow = wave * 8 + (lane >> 3);
-  const int cchunk = (lane & 7) ^ swz(crow);
-  uint32_t a_off[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int m = m_base + i * RPC + crow;
-    int64_t s = 0;                             // rows outside the product read row 0 (discarded)
-    if (m < g.M) {
-      s = g.a_rows ? g.a_rows[m] : m;
-      if (s < 0) s = 0;
-    }
-    a_off[i] = (uint32_t)(s * g.a_ld[0] * (int64_t)sizeof(T) + cchunk * 16);
-  }
-  const char* b_base[NB];
-  uint32_t b_off[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int r0 = n_base + j * RPC + wave * 8;        // first row of this wave's copy (uniform)
-    const T* p0 = b_row_ptr<T, BN>(g, r0);
-    const bool valid = p0 && r0 + (lane >> 3) < g.N;   // 8-row blocks never straddle a segment boundary
-    b_base[j] = (const char*)(p0 ? p0 : (const T*)g.b_ptr[0]) + (int64_t)k_begin * sizeof(T);
-    b_off[j] = (uint32_t)((valid ? (lane >> 3) : 0) * g.b_ld * (int64_t)sizeof(T)) + cchunk * 16;
-  }
-  const char* a_base = (const char*)g.a_ptr[0] + (int64_t)k_begin * sizeof(T);
-  // L2 prefetch lines: thread t touches A row t and B row t of a slab
-  uint32_t pa_off;
-  {
-    const int m = m_base + tid;
-    int64_t s = 0;
-    if (m < g.M) {
-      s = g.a_rows ? g.a_rows[m] : m;
-      if (s < 0) s = 0;
-    }
-    pa_off = (uint32_t)(s * g.a_ld[0] * (int64_t)sizeof(T));
-  }
-  const char* pb_row;
-  {
-    const T* p = b_row_ptr<T, BN>(g, n_base + tid);
-    pb_row = (const char*)(p ? p : (const T*)g.b_ptr[0]) + (int64_t)k_begin * sizeof(T);
-  }
-  __shared__ uint32_t pf_scratch[64];
-  auto prefetch = [&](int kt) {   // slab kt's lines of this tile into L2
-    prefetch4_lds_sv(a_base + (int64_t)kt * BK * sizeof(T), pa_off, pf_scratch);
-    prefetch4_lds(pb_row + (int64_t)kt * BK * sizeof(T), pf_scratch);
-  };
-  // copy q of slab kt into stage st (A copies first)
-  auto copy = [&](int q, int kt, int st) {
-    uint4* dst = smem + st * ((BM + BN) * 8) + (q < NA ? q * RPC * 8 : BM * 8 + (q - NA) * RPC * 8) + wave * 64;
-    if (q < NA) copy16_to_lds_sv_nc(a_base + (int64_t)kt * BK * sizeof(T), a_off[q], dst);
-    else copy16_to_lds_sv_nc(b_base[q - NA] + (int64_t)kt * BK * sizeof(T), b_off[q - NA], dst);
-  };
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  const int r32 = lane & 31, khalf = lane >> 5;
-  FragT af[2][FM], bfr[2][FN];
-  // fragment r of k step s: reads in consumption order A0 B0 B1 B2 B3 A1 A2 A3
-  auto read_frag = [&](int st, int s, int set, int r) {
-    const uint4* buf = smem + st * ((BM + BN) * 8);
-    const int c = s * 2 + khalf;
-    if (r == 0 || r >= 5) {
-      const int fi = r == 0 ? 0 : r - 4;
-      const int row = wm * WM + fi * 32 + r32;
-      *(uint4*)&af[set][fi] = buf[row * 8 + (c ^ swz(row))];
-    } else {
-      const int fj = r - 1;
-      const int row = BM + wn * WN + fj * 32 + r32;
-      *(uint4*)&bfr[set][fj] = buf[row * 8 + (c ^ swz(row))];
-    }
-  };
-  auto mma = [&](int i, int set) { Mfma32<T>::mma(acc[i / FN][i % FN], af[set][i / FN], bfr[set][i % FN]); };
-
-  // one slab: k steps 0..3 of stage st; frags of step 0 are in set 0.  LAST:
-  // no copies, no barrier, no reads past step 3.
-  auto slab = [&](int kt, int st, auto last_tag) {
-    constexpr bool LAST = decltype(last_tag)::value;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int cur = s & 1, nxt = cur ^ 1;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (s == 3 && i == 8 && !LAST) {
-          __builtin_amdgcn_sched_barrier(0);
-          wait_vmcnt<2>();   // slab kt+1 landed; the two newest prefetches may still be in flight
-          wait_lgkmcnt0();
-          lds_barrier();
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        mma(i, cur);
-        if (s < 3 && i < 8) read_frag(st, s + 1, nxt, i);
-        if (s == 3 && i >= 8 && !LAST) read_frag(st ^ 1, 0, 0, i - 8);
-        if (s < 2 && i >= 8 && !LAST) copy(s * 8 + (i - 8), kt + 1, st ^ 1);
-        if (s == 2 && i == 8 && !LAST) prefetch(min(kt + PF_DIST, nk - 1));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  if (nk > 0) {
-#pragma unroll
-    for (int q = 0; q < NL; ++q) copy(q, 0, 0);
-#pragma unroll
-    for (int d = 1; d < PF_DIST; ++d) prefetch(min(d, nk - 1));
-    wait_vmcnt<2 * (PF_DIST - 1)>();
-    lds_barrier();
-#pragma unroll
-    for (int r = 0; r < 8; ++r) read_frag(0, 0, 0, r);
-    for (int kt = 0; kt + 1 < nk; ++kt) slab(kt, kt & 1, std::false_type());
-    slab(nk - 1, (nk - 1) & 1, std::true_type());
-  }
-  wait_vmcnt<0>();
-  wait_lgkmcnt0();
-  lds_barrier();
-
-  if (g.splits > 1) {
-    float* P = g.partials + (int64_t)split * g.Mpad * g.Npad;
-#pragma unroll
-    for (int fi = 0; fi < FM; ++fi)
-#pragma unroll
-      for (int fj = 0; fj < FN; ++fj) {
-        const int col = n_base + wn * WN + fj * 32 + r32;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = m_base + wm * WM + fi * 32 + 8 * (e / 4) + 4 * khalf + (e % 4);
-          P[(int64_t)row * g.Npad + col] = acc[fi][fj][e];
-        }
-      }
-    return;
-  }
-
-  // epilogue: 32 rows per pass staged in LDS; pass p holds block row p % 4 of
-  // the two waves with wm == p / 4
-  float* stage = (float*)smem;
-  constexpr int LD = BN + 1;
-#pragma unroll
-  for (int pass = 0; pass < BM / ER; ++pass) {
-    const int row0 = pass * ER;
-    if (m_base + row0 >= g.M) break;
-    if (wm == pass / FM) {
-      const int fi = pass % FM;
-#pragma unroll
-      for (int fj = 0; fj < FN; ++fj) {
-        const int col = wn * WN + fj * 32 + r32;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = 8 * (e / 4) + 4 * khalf + (e % 4);
-          stage[r * LD + col] = acc[fi][fj][e] * g.out_scale;
-        }
-      }
-    }
-    __syncthreads();
-    Epi::template apply<BN, ER>(ep, stage, LD, m_base + row0, n_base, g.M, g.N, tn, tid);
-    __syncthreads();
-  }
-}
-
 }  // namespace dfl

@@ -63,29 +63,6 @@ __device__ __forceinline__ void copy16_to_lds_sv_nc(const void* sbase, uint32_t 
       : "s"(lds), "v"(voff), "s"(sbase));
 }
 
-// 4-byte global -> LDS copies whose only purpose is to pull a cache line into
-// L2 ahead of its real copy: every lane of the wave lands in the same 256-byte
-// LDS scratch area, which nothing reads.  No register is written, so nothing
-// waits for them except a vmcnt wait that covers them.
-__device__ __forceinline__ void prefetch4_lds(const void* g, void* lds_scratch) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_scratch);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(g));
-}
-__device__ __forceinline__ void prefetch4_lds_sv(const void* sbase, uint32_t voff, void* lds_scratch) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_scratch);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(sbase));
-}
-
 // s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
