@@ -27,8 +27,11 @@ struct dflash_handle {
   // s_*: 2^-(the copy's scale exponent), multiplied into every product that reads the copy
   struct Mats {
     const void *q, *k, *v, *o, *gate, *up, *down, *conv_a, *conv_m;
-    const void *conv_ap = nullptr, *conv_mp = nullptr;   // after-sub-layer convolutions (or null)
-    float s_o = 1.f, s_gu = 1.f, s_down = 1.f, s_ca = 1.f, s_cm = 1.f, s_cap = 1.f, s_cmp = 1.f;
+    // after-sub-layer convolutions (or null): their corrections o . P^T are taken
+    // as A . (P . W)^T, the product's extra output columns, so what is kept is
+    // P . W_o [2H/G, q_dim] and P . W_down [2H/G, ffn] (scaled with o / down)
+    const void *conv_ap = nullptr, *conv_mp = nullptr;
+    float s_o = 1.f, s_gu = 1.f, s_down = 1.f, s_ca = 1.f, s_cm = 1.f;
   };
   std::vector<Mats> mats;
   const void* lm = nullptr;
@@ -83,9 +86,10 @@ struct dflash_handle {
   void* g = nullptr;
   int32_t *a_rows = nullptr, *row_slot = nullptr, *row_pos = nullptr, *req_off = nullptr, *req_pos = nullptr;
   // DFlash 2 modules
-  void* hbuf2 = nullptr;                  // convolved sub-layer input; operand copy of a sub-layer output
+  void* hbuf2 = nullptr;                  // convolved sub-layer input
   float* obuf = nullptr;                  // fp32 sub-layer output ahead of an after-sub-layer convolution
   float* cbuf = nullptr;                  // kernel corrections [maxM, 2H/G]
+  float* rsbuf = nullptr;                 // RMS scales of the rows the last norm pass produced [maxM]
   const void* sel_h = nullptr;            // W_H (fp16 copy for a bf16 drafter)
   const void *sel_pred = nullptr, *sel_succ = nullptr;
   float *sel_gate = nullptr, *sel_cprob = nullptr, *sel_probs_ws = nullptr, *sel_table = nullptr;
@@ -162,6 +166,16 @@ int alloc_t(dflash_handle* h, P** p, size_t count, size_t elem) {
   const int rc = alloc(h, &v, count * elem);
   *p = (P*)v;
   return rc;
+}
+
+// free one allocation of the handle before destroy (create-time temporaries)
+void free_one(dflash_handle* h, void* p) {
+  for (size_t i = 0; i < h->allocs.size(); ++i)
+    if (h->allocs[i] == p) {
+      (void)hipFree(p);
+      h->allocs.erase(h->allocs.begin() + i);
+      return;
+    }
 }
 
 void free_all(dflash_handle* h) {
@@ -258,25 +272,45 @@ inline hipStream_t S(void* s) { return (hipStream_t)s; }
 // for every |w| of at least 2^-28 times the group's largest; smaller weights
 // round to fp16's subnormal grid (absolute error at most 2^(-25-s)).  The
 // epilogues multiply each product by its group's 2^-s (exact).
+//
+// An after-sub-layer convolution's correction o . P^T is computed as A . (P . W)^T,
+// extra output columns of the sub-layer's output product (o = A . W^T), so its
+// P . W (fp32, made here once) joins W's scale group.
 int prepare_weights(dflash_handle* h) {
   const dflash_config& c = h->cfg;
   h->mats.resize(c.n_layers);
+  const int64_t H = c.hidden, qdim = (int64_t)c.n_q_heads * c.head_dim, kvdim = (int64_t)c.n_kv_heads * c.head_dim;
+  const int64_t F = c.ffn, V = c.vocab;
+  const int64_t nc = c.conv_group > 0 ? 2 * H / c.conv_group : 0;
+  // P . W products of the after-sub-layer convolutions, fp32 [nc, q_dim] / [nc, ffn]
+  std::vector<float*> pw_o(c.n_layers, nullptr), pw_d(c.n_layers, nullptr);
+  int rc = DFLASH_OK;
+  for (int l = 0; l < c.n_layers && c.conv_group > 0; ++l) {
+    const dflash_layer_weights& L = h->layers[l];
+    if (L.attn_conv_post_proj) {
+      if ((rc = alloc_t(h, &pw_o[l], (size_t)(nc * qdim), 4))) return rc;
+      launch_matmul_nn(c.dtype, (int)nc, (int)qdim, (int)H, L.attn_conv_post_proj, L.o_w, pw_o[l], nullptr);
+    }
+    if (L.mlp_conv_post_proj) {
+      if ((rc = alloc_t(h, &pw_d[l], (size_t)(nc * F), 4))) return rc;
+      launch_matmul_nn(c.dtype, (int)nc, (int)F, (int)H, L.mlp_conv_post_proj, L.down_w, pw_d[l], nullptr);
+    }
+  }
+  if (hipGetLastError() != hipSuccess) return DFLASH_E_HIP;
   if (c.dtype != DFLASH_BF16) {
     for (int l = 0; l < c.n_layers; ++l) {
       const dflash_layer_weights& L = h->layers[l];
       h->mats[l] = {L.q_w, L.k_w, L.v_w, L.o_w, L.gate_w, L.up_w, L.down_w, L.attn_conv_proj, L.mlp_conv_proj,
-                    L.attn_conv_post_proj, L.mlp_conv_post_proj};
+                    pw_o[l], pw_d[l]};
     }
     h->lm = h->lm_head;
     h->sel_h = h->sel_hidden_src;
     return DFLASH_OK;
   }
-  const int64_t H = c.hidden, qdim = (int64_t)c.n_q_heads * c.head_dim, kvdim = (int64_t)c.n_kv_heads * c.head_dim;
-  const int64_t F = c.ffn, V = c.vocab;
   // Each group of matrices read by one product gets its own power-of-two scale,
   // chosen from the group's largest |w|, so one large matrix does not shrink the
   // exact range of the others.
-  struct Job { const void* src; int64_t n; const void** dst; int group; };
+  struct Job { const void* src; int64_t n; const void** dst; int group; bool f32 = false; };
   std::vector<Job> jobs;
   std::vector<float*> group_scale;           // where each group's 2^-s goes
   auto group = [&](float* out) { group_scale.push_back(out); return (int)group_scale.size() - 1; };
@@ -287,29 +321,31 @@ int prepare_weights(dflash_handle* h) {
     jobs.push_back({L.q_w, qdim * H, &m.q, g_qkv});
     jobs.push_back({L.k_w, kvdim * H, &m.k, g_qkv});
     jobs.push_back({L.v_w, kvdim * H, &m.v, g_qkv});
-    jobs.push_back({L.o_w, H * qdim, &m.o, group(&m.s_o)});
+    const int g_o = group(&m.s_o);
+    jobs.push_back({L.o_w, H * qdim, &m.o, g_o});
+    if (pw_o[l]) jobs.push_back({pw_o[l], nc * qdim, &m.conv_ap, g_o, true});
     const int g_gu = group(&m.s_gu);
     jobs.push_back({L.gate_w, F * H, &m.gate, g_gu});
     jobs.push_back({L.up_w, F * H, &m.up, g_gu});
-    jobs.push_back({L.down_w, H * F, &m.down, group(&m.s_down)});
+    const int g_d = group(&m.s_down);
+    jobs.push_back({L.down_w, H * F, &m.down, g_d});
+    if (pw_d[l]) jobs.push_back({pw_d[l], nc * F, &m.conv_mp, g_d, true});
     m.conv_a = m.conv_m = nullptr;
     if (c.conv_group > 0) {
       jobs.push_back({L.attn_conv_proj, 2 * H / c.conv_group * H, &m.conv_a, group(&m.s_ca)});
       jobs.push_back({L.mlp_conv_proj, 2 * H / c.conv_group * H, &m.conv_m, group(&m.s_cm)});
-      if (L.attn_conv_post_proj)
-        jobs.push_back({L.attn_conv_post_proj, 2 * H / c.conv_group * H, &m.conv_ap, group(&m.s_cap)});
-      if (L.mlp_conv_post_proj)
-        jobs.push_back({L.mlp_conv_post_proj, 2 * H / c.conv_group * H, &m.conv_mp, group(&m.s_cmp)});
     }
   }
   jobs.push_back({h->lm_head, V * H, &h->lm, group(&h->s_lm)});
   if (c.sel_rank > 0) jobs.push_back({h->sel_hidden_src, (int64_t)c.sel_rank * H, &h->sel_h, group(&h->s_selh)});
   const int ng = (int)group_scale.size();
   uint32_t* d_max = nullptr;
-  int rc = alloc_t(h, &d_max, (size_t)ng, 4);
-  if (rc) return rc;
+  if ((rc = alloc_t(h, &d_max, (size_t)ng, 4))) return rc;
   if (hipMemset(d_max, 0, (size_t)ng * 4) != hipSuccess) return DFLASH_E_HIP;
-  for (auto& j : jobs) launch_absmax_bf16(j.src, j.n, d_max + j.group, nullptr);
+  for (auto& j : jobs) {
+    if (j.f32) launch_absmax_f32((const float*)j.src, j.n, d_max + j.group, nullptr);
+    else launch_absmax_bf16(j.src, j.n, d_max + j.group, nullptr);
+  }
   std::vector<uint32_t> bits(ng);
   if (hipMemcpy(bits.data(), d_max, (size_t)ng * 4, hipMemcpyDeviceToHost) != hipSuccess) return DFLASH_E_HIP;
   std::vector<float> scale(ng);
@@ -329,8 +365,13 @@ int prepare_weights(dflash_handle* h) {
   for (auto& j : jobs) {
     void* dst = nullptr;
     if ((rc = alloc(h, &dst, (size_t)j.n * 2))) return rc;
-    launch_convert_bf16_f16(j.src, j.n, scale[j.group], dst, nullptr);
+    if (j.f32) launch_convert_f32_f16((const float*)j.src, j.n, scale[j.group], dst, nullptr);
+    else launch_convert_bf16_f16(j.src, j.n, scale[j.group], dst, nullptr);
     *j.dst = dst;
+  }
+  for (int l = 0; l < c.n_layers; ++l) {   // the fp32 products now live in their fp16 copies
+    if (pw_o[l]) free_one(h, pw_o[l]);
+    if (pw_d[l]) free_one(h, pw_d[l]);
   }
   return DFLASH_OK;
 }
@@ -456,8 +497,10 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     // split-K partials: grids of at most 2 * CUs tiles, or a four-way split of the
     // long-K products over the draft's rows (M x H each, rows padded to 128- or
     // 192-row tiles); a product needing more runs with fewer splits
+    // (H columns, plus the kernel corrections of DFlash 2 after-sub-layer convolutions)
     const size_t mpad = std::max((h->maxM + 127) / 128 * 128, (h->maxM + 191) / 192 * 192);
-    h->partials_elems = std::max((size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(h->op), (size_t)4 * mpad * H);
+    const size_t ncols = H + (c.conv_group > 0 ? 2 * (H / c.conv_group) : 0);
+    h->partials_elems = std::max((size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(h->op), (size_t)4 * mpad * ncols);
     if ((rc = alloc_t(h, &h->partials, h->partials_elems, 4))) break;
     const size_t lrows = (size_t)c.max_batch * c.max_k;
     if ((rc = alloc_t(h, &h->logits_ws, lrows * c.vocab, 4))) break;
@@ -482,6 +525,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
       if ((rc = alloc(h, &h->hbuf2, (size_t)h->maxM * H * es))) break;
       if ((rc = alloc_t(h, &h->cbuf, (size_t)h->maxM * 2 * (H / c.conv_group), 4))) break;
       if ((rc = alloc_t(h, &h->obuf, (size_t)h->maxM * H, 4))) break;
+      if ((rc = alloc_t(h, &h->rsbuf, (size_t)h->maxM, 4))) break;
     }
     if (c.sel_rank > 0) {
       const size_t C = c.sel_cands;
@@ -689,8 +733,9 @@ int dflash_inject_tree_path(dflash_handle* h, void* stream, int32_t n_req, const
 
 namespace {
 
-// DFlash 2 [P2 §3.2.3]: hbuf2 = dynamic conv of the block rows in hbuf; the
-// per-row kernel corrections come from one product with the layer's proj.
+// DFlash 2 [P2 §3.2.3]: hbuf2 = dynamic conv of the block rows of the sub-layer
+// input x = X * rs * gain held in hbuf (rs from the norm pass that wrote hbuf);
+// the per-row kernel corrections come from one product with the layer's proj.
 void conv_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj, float proj_scale, const void* base,
                 const void* gain) {
   const dflash_config& c = h->cfg;
@@ -702,47 +747,49 @@ void conv_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj,
   EpiStore<float>::Params pc{h->cbuf, nc};
   launch_gemm(h->op, EPI_STORE_F32, ga, &pc, plan_gemm(h->op, M, nc, H, h->num_cus), h->partials, h->partials_elems,
               s);
-  launch_dyn_conv(c.dtype, M, R, H, c.conv_group, h->X, gain, c.rms_eps, h->cbuf, base, h->hbuf2, s);
-}
-
-// DFlash 2 [P2 §3.2.3]: convolution after a sub-layer.  The sub-layer's output
-// projection is in obuf (fp32) and hbuf2 (operand copy, the correction
-// product's input); X += conv(obuf) over the block rows.
-void conv_post_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj, float proj_scale,
-                     const void* base) {
-  const dflash_config& c = h->cfg;
-  const int H = c.hidden, nc = 2 * (H / c.conv_group);
-  Phase ph(h, s, DFLASH_PH_CONV);
-  GemmArgs ga = gemm_a1(h->hbuf2, H, M, nc, H);
-  ga.out_scale = proj_scale;
-  set_b(ga, {{proj, nc}}, H);
-  EpiStore<float>::Params pc{h->cbuf, nc};
-  launch_gemm(h->op, EPI_STORE_F32, ga, &pc, plan_gemm(h->op, M, nc, H, h->num_cus), h->partials, h->partials_elems,
-              s);
-  launch_dyn_conv_post(c.dtype, M, R, H, c.conv_group, h->obuf, h->cbuf, base, h->X, s);
+  launch_dyn_conv(c.dtype, M, R, H, c.conv_group, h->X, h->rsbuf, gain, h->cbuf, base, h->hbuf2, s);
 }
 
 // Output projection of a sub-layer (A [M, Kd] times B^T [H, Kd]): added to the
-// residual stream, or, when an after-sub-layer convolution follows, stored for it.
-void sublayer_out(dflash_handle* h, hipStream_t s, int M, int R, const void* a, int Kd, const void* b, float b_scale,
-                  const void* post_proj, float post_scale, const void* post_base, int phase) {
-  const int H = h->cfg.hidden;
-  GemmArgs ga = gemm_a1(a, Kd, M, H, Kd);
+// residual stream; or, when an after-sub-layer convolution follows (post_pw =
+// its P . W [2H/G, Kd]), the output goes to obuf and its kernel corrections,
+// from the same product's extra columns, to cbuf -- norm_stage applies them.
+void sublayer_out(dflash_handle* h, hipStream_t s, int M, const void* a, int Kd, const void* b, float b_scale,
+                  const void* post_pw, int phase) {
+  const dflash_config& c = h->cfg;
+  const int H = c.hidden;
+  const int nc = post_pw ? 2 * (H / c.conv_group) : 0;
+  GemmArgs ga = gemm_a1(a, Kd, M, H + nc, Kd);
   ga.out_scale = b_scale;
-  set_b(ga, {{b, H}}, Kd);
-  const GemmPlan pl = plan_gemm(h->op, M, H, Kd, h->num_cus);
-  if (!post_base) {
+  Phase ph(h, s, phase);
+  if (!post_pw) {
+    set_b(ga, {{b, H}}, Kd);
     EpiResidualAdd::Params pr{h->X, H};
-    Phase ph(h, s, phase);
-    launch_gemm(h->op, EPI_RESADD, ga, &pr, pl, h->partials, h->partials_elems, s);
+    launch_gemm(h->op, EPI_RESADD, ga, &pr, plan_gemm(h->op, M, H, Kd, h->num_cus), h->partials, h->partials_elems,
+                s);
     return;
   }
-  {
-    StoreDualParams pd{h->obuf, h->hbuf2, H, h->err};
-    Phase ph(h, s, phase);
-    launch_gemm(h->op, EPI_STORE_DUAL, ga, &pd, pl, h->partials, h->partials_elems, s);
+  set_b(ga, {{b, H}, {post_pw, nc}}, Kd);
+  StoreSplitParams pd{h->obuf, H, h->cbuf, nc, H};
+  launch_gemm(h->op, EPI_STORE_SPLIT, ga, &pd, plan_gemm(h->op, M, H + nc, Kd, h->num_cus), h->partials,
+              h->partials_elems, s);
+}
+
+// RMSNorm of the rows (map_mask: the mask rows only) into hbuf, after applying
+// the pending after-sub-layer convolution with base post_base (or none); with
+// DFlash 2 convolutions the rows' RMS scales go to rsbuf for the next one.
+void norm_stage(dflash_handle* h, hipStream_t s, int rows, int map_mask, int K, int R, const void* gain,
+                const void* post_base) {
+  const dflash_config& c = h->cfg;
+  float* rs = c.conv_group > 0 ? h->rsbuf : nullptr;
+  if (post_base) {
+    Phase ph(h, s, DFLASH_PH_CONV);
+    launch_conv_post_norm(c.dtype, rows, c.hidden, c.conv_group, h->X, map_mask, K, R, h->obuf, h->cbuf, post_base,
+                          gain, h->hbuf, c.rms_eps, rs, s);
+  } else {
+    Phase ph(h, s, DFLASH_PH_NORM);
+    launch_rmsnorm(c.dtype, rows, c.hidden, h->X, map_mask, K, R, gain, h->hbuf, c.rms_eps, s, nullptr, 0, rs);
   }
-  conv_post_stage(h, s, M, R, post_proj, post_scale, post_base);
 }
 
 // DFlash 2 path selector [P2 §3.1.2-3.1.3] over rows n_req*K whose logits and
@@ -849,7 +896,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   {
     Phase ph(h, s, DFLASH_PH_EMBED);
     launch_embed_norm(dt, M, R, anchor_ids, c.mask_token_id, V, h->embed, h->mask_emb, c.input_embedding_scale, H, h->X,
-                      h->layers[0].in_norm, h->hbuf, c.rms_eps, h->err, s);
+                      h->layers[0].in_norm, h->hbuf, c.rms_eps, h->err, s, c.conv_group > 0 ? h->rsbuf : nullptr);
   }
   {
     Phase ph(h, s, DFLASH_PH_ATTN_PLAN);
@@ -862,6 +909,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     launch_page_check(n_req, slots, h->ctx_len, c.max_batch, h->pages(), h->err, s);
   }
   const int64_t layer_cache = (int64_t)(c.max_batch + 1) * nkv * h->ctx_alloc * d * h->esize;
+  const void* post_m = nullptr;   // the last MLP's pending after-sub-layer convolution
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& L = h->layers[l];
     const dflash_handle::Mats& W = h->mats[l];
@@ -963,13 +1011,10 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       Phase ph(h, s, DFLASH_PH_ATTN_COMBINE);
       launch_attn_combine(dt, d, cb, dim3(n_req, nkv * splits, (rows_split + 15) / 16), s);
     }
-    // output projection (+ DFlash 2 convolution) + residual
-    sublayer_out(h, s, M, R, h->attn_out, qdim, W.o, W.s_o, W.conv_ap, W.s_cap,
-                 c.conv_group > 0 ? L.attn_conv_post_base : nullptr, DFLASH_PH_O);
-    {
-      Phase ph(h, s, DFLASH_PH_NORM);
-      launch_rmsnorm(dt, M, H, h->X, 0, K, R, L.post_norm, h->hbuf, c.rms_eps, s);
-    }
+    // output projection + residual (with a DFlash 2 convolution: applied in the norm pass)
+    const void* post_a = c.conv_group > 0 ? L.attn_conv_post_base : nullptr;
+    sublayer_out(h, s, M, h->attn_out, qdim, W.o, W.s_o, post_a ? W.conv_ap : nullptr, DFLASH_PH_O);
+    norm_stage(h, s, M, 0, K, R, L.post_norm, post_a);
     // DFlash 2: dynamic convolution of the MLP sub-layer's input
     const void* mlp_in = h->hbuf;
     if (c.conv_group > 0) {
@@ -990,20 +1035,14 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
         launch_gemm(h->op, EPI_SWIGLU, ga, &ps, plan_gemm(h->op, M, 2 * F, H, h->num_cus), h->partials,
                     h->partials_elems, s);
       }
-      sublayer_out(h, s, M, R, h->act, F, W.down, W.s_down, W.conv_mp, W.s_cmp,
-                   c.conv_group > 0 ? L.mlp_conv_post_base : nullptr, DFLASH_PH_DOWN);
+      post_m = c.conv_group > 0 ? L.mlp_conv_post_base : nullptr;
+      sublayer_out(h, s, M, h->act, F, W.down, W.s_down, post_m ? W.conv_mp : nullptr, DFLASH_PH_DOWN);
     }
-    if (l + 1 < c.n_layers) {
-      Phase ph(h, s, DFLASH_PH_NORM);
-      launch_rmsnorm(dt, M, H, h->X, 0, K, R, h->layers[l + 1].in_norm, h->hbuf, c.rms_eps, s);
-    }
+    if (l + 1 < c.n_layers) norm_stage(h, s, M, 0, K, R, h->layers[l + 1].in_norm, post_m);
   }
   // final norm on the K mask rows, LM head with streaming statistics
   const int rows = n_req * K;
-  {
-    Phase ph(h, s, DFLASH_PH_NORM);
-    launch_rmsnorm(dt, rows, H, h->X, 1, K, R, h->final_norm, h->hbuf, c.rms_eps, s);
-  }
+  norm_stage(h, s, rows, 1, K, R, h->final_norm, post_m);
   const float T = p->temperature;
   const bool need_logits = o->logits || T > 0.f || p->top_k > 0 || p->tree_budget > 0 || c.sel_rank > 0;
   float* logits = o->logits ? o->logits : (need_logits ? h->logits_ws : nullptr);

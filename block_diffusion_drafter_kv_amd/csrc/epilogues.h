@@ -23,26 +23,20 @@ struct EpiStore {
   }
 };
 
-// ---- the same tile stored twice: fp32, and in the operand type T (the input of
-// a following product); the T copy saturates out-of-range values ----
-struct StoreDualParams { float* out; void* out2; int64_t ld; int32_t* err; };
-template <typename T>
-struct EpiStoreDual {
-  typedef StoreDualParams Params;
+// ---- fp32 store split at a column: columns [0, split) to out, the rest to out2 ----
+struct StoreSplitParams { float* out; int64_t ld; float* out2; int64_t ld2; int split; };
+struct EpiStoreSplit {
+  typedef StoreSplitParams Params;
   template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int, int tid) {
-    T* out2 = (T*)p.out2;
-    bool bad = false;
     for (int idx = tid; idx < ROWS * BN; idx += 256) {
       const int r = idx / BN, c = idx % BN;
       const int m = m0 + r, n = n0 + c;
       if (m < M && n < N) {
-        const float v = st[r * ld + c];
-        p.out[(int64_t)m * p.ld + n] = v;
-        out2[(int64_t)m * p.ld + n] = store_cvt<T>(v, bad);
+        if (n < p.split) p.out[(int64_t)m * p.ld + n] = st[r * ld + c];
+        else p.out2[(int64_t)m * p.ld2 + (n - p.split)] = st[r * ld + c];
       }
     }
-    report_nonfinite(p.err, bad, tid);
   }
 };
 

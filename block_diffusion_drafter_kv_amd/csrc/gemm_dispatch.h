@@ -104,7 +104,7 @@ static void gemm_dispatch_t(EpiKind kind, const GemmPlan& pl, const GemmArgs& g,
     case EPI_QKV: gemm_cfg<T, EpiQKV<T>>(pl, g, ep, s); break;
     case EPI_KVINJECT: gemm_cfg<T, EpiKVInject<T>>(pl, g, ep, s); break;
     case EPI_LMHEAD: gemm_cfg<T, EpiLMHead>(pl, g, ep, s); break;
-    case EPI_STORE_DUAL: gemm_cfg<T, EpiStoreDual<T>>(pl, g, ep, s); break;
+    case EPI_STORE_SPLIT: gemm_cfg<T, EpiStoreSplit>(pl, g, ep, s); break;
   }
 }
 

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* a
                                                           const typename WeightOf<C>::type* embed,
                                                           const typename WeightOf<C>::type* mask_emb, float scale, int H,
                                                           float* X, const typename WeightOf<C>::type* gain, C* h_out,
-                                                          float eps, int32_t* err) {
+                                                          float eps, int32_t* err, float* rs_out) {
   __shared__ float red[4];
   const int m = blockIdx.x;
   const int r = m / R, j = m % R;
@@ -92,6 +92,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* a
   }
   ss = block_sum(ss, red);
   const float rs = rsqrtf(ss / (float)H + eps);
+  if (rs_out && threadIdx.x == 0) rs_out[m] = rs;
   if (vec) {
     for (int c = threadIdx.x * 4; c < H; c += 1024) {
       const float4 x = *(const float4*)(xr + c), g = load4f(gain + c);
@@ -103,31 +104,75 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(int R, const int32_t* a
 }
 
 
-// RMSNorm of fp32 rows, one wave per row (H a multiple of 4):
+// RMSNorm of fp32 rows, one 256-thread work-group per row (H a multiple of 4):
 // out[o] = x * rsqrt(mean(x^2) + eps) * gain, x = X row (map_mask ? (o / K) * R + 1 + o % K : o).
 // Rows at or past (*n_valid - valid_base) are skipped when n_valid is given.
+// rs_out (or null) receives each row's rsqrt(mean(x^2) + eps).
 template <typename C>
-__global__ __launch_bounds__(64) void rmsnorm_kernel(int n_rows, int H, const float* X, int map_mask, int K, int R,
-                                                       const typename WeightOf<C>::type* gain, C* h_out, float eps,
-                                                       const int32_t* n_valid, int valid_base) {
-  // one wave per row; work-groups of one wave spread a few hundred rows over every CU
-  const int o = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int n_rows, int H, const float* X, int map_mask, int K, int R,
+                                                        const typename WeightOf<C>::type* gain, C* h_out, float eps,
+                                                        const int32_t* n_valid, int valid_base, float* rs_out) {
+  __shared__ float red[4];
+  const int o = blockIdx.x;
   if (o >= n_rows) return;
-  if (n_valid && o >= *n_valid - valid_base) return;
+  if (n_valid && o >= *n_valid - valid_base) return;   // uniform over the work-group
   const int src = map_mask ? (o / K) * R + 1 + (o % K) : o;
   const float* x = X + (int64_t)src * H;
   float ss = 0.f;
-#pragma unroll 4
-  for (int c = lane * 4; c < H; c += 256) {
+  for (int c = threadIdx.x * 4; c < H; c += 1024) {
     const float4 v = load4f(x + c);
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
-  ss = wave_sum(ss);
+  ss = block_sum(ss, red);
   const float rs = rsqrtf(ss / (float)H + eps);
+  if (rs_out && threadIdx.x == 0) rs_out[o] = rs;
   C* y = h_out + (int64_t)o * H;
-#pragma unroll 4
-  for (int c = lane * 4; c < H; c += 256) {
+  for (int c = threadIdx.x * 4; c < H; c += 1024) {
     const float4 v = load4f(x + c), gn = load4f(gain + c);
+    store4(y + c, v.x * rs * gn.x, v.y * rs * gn.y, v.z * rs * gn.z, v.w * rs * gn.w);
+  }
+}
+
+// DFlash 2 [P2 §3.2.3], convolution after a sub-layer, fused with the RMSNorm
+// that follows it: the sub-layer output o (fp32 [M, H], before the residual add)
+// is convolved over the block rows, y_m = (base0 + c0_m) * o_m + (base1 + c1_m) *
+// o_{m-1} (o_{m-1} = 0 on a block's first row, corrections corr [M, 2H/G] shared
+// by groups of G channels), added to X, and the updated row normalised as in
+// rmsnorm_kernel (same row mapping; only the mapped rows of X are updated).
+template <typename C>
+__global__ __launch_bounds__(256) void conv_post_norm_kernel(int n_rows, int H, int G, float* X, int map_mask, int K,
+                                                               int R, const float* o, const float* corr,
+                                                               const typename WeightOf<C>::type* base,
+                                                               const typename WeightOf<C>::type* gain, C* h_out,
+                                                               float eps, float* rs_out) {
+  __shared__ float red[4];
+  const int out = blockIdx.x;   // one 256-thread work-group per row
+  if (out >= n_rows) return;
+  const int m = map_mask ? (out / K) * R + 1 + (out % K) : out;
+  const bool first = m % R == 0;
+  const int ng = H / G;
+  float* x = X + (int64_t)m * H;
+  const float* om = o + (int64_t)m * H;
+  const float* cr = corr + (int64_t)m * 2 * ng;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 4; c < H; c += 1024) {   // G is a multiple of 4: the four channels share a group
+    float4 v = load4f(x + c);
+    const float4 a = load4f(om + c), b0 = load4f(base + c), b1 = load4f(base + H + c);
+    const float4 u = first ? make_float4(0.f, 0.f, 0.f, 0.f) : load4f(om - H + c);
+    const float c0 = cr[c / G], c1 = cr[ng + c / G];
+    v.x += (b0.x + c0) * a.x + (b1.x + c1) * u.x;
+    v.y += (b0.y + c0) * a.y + (b1.y + c1) * u.y;
+    v.z += (b0.z + c0) * a.z + (b1.z + c1) * u.z;
+    v.w += (b0.w + c0) * a.w + (b1.w + c1) * u.w;
+    *(float4*)(x + c) = v;
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = block_sum(ss, red);
+  const float rs = rsqrtf(ss / (float)H + eps);
+  if (rs_out && threadIdx.x == 0) rs_out[out] = rs;
+  C* y = h_out + (int64_t)out * H;
+  for (int c = threadIdx.x * 4; c < H; c += 1024) {   // this thread's own stores above
+    const float4 v = *(const float4*)(x + c), gn = load4f(gain + c);
     store4(y + c, v.x * rs * gn.x, v.y * rs * gn.y, v.z * rs * gn.z, v.w * rs * gn.w);
   }
 }
@@ -1449,63 +1494,27 @@ __global__ __launch_bounds__(64) void rejection_sparse_kernel(int K, int kp, int
 // is rounded to the operand type once.  One work-group per row.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(64) void dyn_conv_kernel(int M, int R, int H, int G, const float* X,
-                                                        const typename WeightOf<T>::type* gain, float eps,
-                                                        const float* corr, const typename WeightOf<T>::type* base,
-                                                        T* y) {
-  // one wave per row (as the RMSNorm kernel), one row per work-group
-  const int m = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (m >= M) return;
-  const bool first = m % R == 0;
-  const int ng = H / G;
-  const float* xr = X + (int64_t)m * H;
-  const float* xp = xr - H;
-  float ss = 0.f, sp = 0.f;
-  // unrolled so that several rows' loads are in flight per wave (one wave per row is latency-bound)
-#pragma unroll 8
-  for (int c = lane * 4; c < H; c += 256) {
-    const float4 v = load4f(xr + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    if (!first) {
-      const float4 u = load4f(xp + c);
-      sp += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
-    }
-  }
-  const float rs = rsqrtf(wave_sum(ss) / (float)H + eps);
-  const float rp = first ? 0.f : rsqrtf(wave_sum(sp) / (float)H + eps);
-  const float* cr = corr + (int64_t)m * 2 * ng;
-#pragma unroll 4
-  for (int c = lane * 4; c < H; c += 256) {   // G is a multiple of 4: the four channels share a group
-    const float4 v = load4f(xr + c), g = load4f(gain + c), b0 = load4f(base + c), b1 = load4f(base + H + c);
-    const float4 u = first ? make_float4(0.f, 0.f, 0.f, 0.f) : load4f(xp + c);
-    const float c0 = cr[c / G], c1 = cr[ng + c / G];
-    store4(y + (int64_t)m * H + c, (b0.x + c0) * v.x * rs * g.x + (b1.x + c1) * u.x * rp * g.x,
-           (b0.y + c0) * v.y * rs * g.y + (b1.y + c1) * u.y * rp * g.y,
-           (b0.z + c0) * v.z * rs * g.z + (b1.z + c1) * u.z * rp * g.z,
-           (b0.w + c0) * v.w * rs * g.w + (b1.w + c1) * u.w * rp * g.w);
-  }
-}
-
-// After-sub-layer convolution [P2 §3.2.3]: X[m] += k_m0 * o[m] + k_m1 * o[m-1]
-// with k_mj = base[j] + corr[m] (group-shared), o[m-1] = 0 on a block's first row.
-// One thread per four channels of one row.
-template <typename W>
-__global__ __launch_bounds__(256) void dyn_conv_post_kernel(int M, int R, int H, int G, const float* o,
-                                                             const float* corr, const W* base, float* X) {
+__global__ __launch_bounds__(256) void dyn_conv_kernel(int M, int R, int H, int G, const float* X, const float* rs,
+                                                        const typename WeightOf<T>::type* gain, const float* corr,
+                                                        const typename WeightOf<T>::type* base, T* y) {
+  // elementwise: one thread per four channels of one row; x_m = X_m * rs_m * gain
+  // with the row scales rs written by the RMSNorm pass that produced the
+  // correction product's input
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int h4 = H / 4;
   if (i >= (int64_t)M * h4) return;
   const int m = (int)(i / h4), c = (int)(i % h4) * 4;
+  const bool first = m % R == 0;
   const int ng = H / G;
+  const float4 v = load4f(X + (int64_t)m * H + c), g = load4f(gain + c);
+  const float4 b0 = load4f(base + c), b1 = load4f(base + H + c);
+  const float4 u = first ? make_float4(0.f, 0.f, 0.f, 0.f) : load4f(X + (int64_t)(m - 1) * H + c);
+  const float r0 = rs[m], r1 = first ? 0.f : rs[m - 1];
   const float c0 = corr[(int64_t)m * 2 * ng + c / G], c1 = corr[(int64_t)m * 2 * ng + ng + c / G];
-  const float4 v = load4f(o + (int64_t)m * H + c), b0 = load4f(base + c), b1 = load4f(base + H + c);
-  const float4 u = m % R == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : load4f(o + (int64_t)(m - 1) * H + c);
-  float4 x = load4f(X + (int64_t)m * H + c);
-  x.x += (b0.x + c0) * v.x + (b1.x + c1) * u.x;
-  x.y += (b0.y + c0) * v.y + (b1.y + c1) * u.y;
-  x.z += (b0.z + c0) * v.z + (b1.z + c1) * u.z;
-  x.w += (b0.w + c0) * v.w + (b1.w + c1) * u.w;
-  *(float4*)(X + (int64_t)m * H + c) = x;
+  store4(y + (int64_t)m * H + c, (b0.x + c0) * v.x * r0 * g.x + (b1.x + c1) * u.x * r1 * g.x,
+         (b0.y + c0) * v.y * r0 * g.y + (b1.y + c1) * u.y * r1 * g.y,
+         (b0.z + c0) * v.z * r0 * g.z + (b1.z + c1) * u.z * r1 * g.z,
+         (b0.w + c0) * v.w * r0 * g.w + (b1.w + c1) * u.w * r1 * g.w);
 }
 
 // ---------------------------------------------------------------------------
@@ -1950,6 +1959,60 @@ __global__ void convert_bf16_f16_kernel(const bf16_t* w, int64_t n, float scale,
     out[i] = (f16_t)((float)w[i] * scale);
 }
 
+__global__ void absmax_f32_kernel(const float* w, int64_t n, uint32_t* out) {
+  uint32_t best = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    best = max(best, __float_as_uint(fabsf(w[i])));
+  for (int o = 32; o > 0; o >>= 1) best = max(best, (uint32_t)__shfl_xor((int)best, o, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, best);
+}
+
+__global__ void convert_f32_f16_kernel(const float* w, int64_t n, float scale, f16_t* out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = (f16_t)(w[i] * scale);
+}
+
+// C[r][j] = sum_k A[r][k] * B[k][j] in fp32 (A [R, K] and B [K, J] row-major),
+// for products of weight matrices made once at create time.  64 x 64 output
+// tiles, 16-deep K chunks staged in LDS, 4 x 4 outputs per thread.
+template <typename W>
+__global__ __launch_bounds__(256) void matmul_nn_kernel(int Rn, int J, int Kn, const W* A, const W* B, float* Cm) {
+  __shared__ float as[16][65], bs[16][64];
+  const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
+  const int r0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < Kn; k0 += 16) {
+    for (int e = tid; e < 64 * 16; e += 256) {
+      const int rr = e / 16, kk = e % 16;         // A tile: 64 rows x 16 k
+      as[kk][rr] = (r0 + rr < Rn && k0 + kk < Kn) ? to_f32(A[(int64_t)(r0 + rr) * Kn + k0 + kk]) : 0.f;
+      const int kb = e / 64, jj = e % 64;         // B tile: 16 k x 64 columns
+      bs[kb][jj] = (k0 + kb < Kn && j0 + jj < J) ? to_f32(B[(int64_t)(k0 + kb) * J + j0 + jj]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[q] = as[kk][tr * 4 + q];
+        b[q] = bs[kk][tc * 4 + q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[q][t] += a[q] * b[t];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = r0 + tr * 4 + q, j = j0 + tc * 4 + t;
+      if (r < Rn && j < J) Cm[(int64_t)r * J + j] = acc[q][t];
+    }
+}
+
 __global__ void philox_fill_kernel(int n, uint64_t seed, uint32_t slot, uint64_t step, uint32_t purpose, float* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) out[i] = philox_uniform(seed, slot, step, (uint32_t)i, purpose);
@@ -1967,27 +2030,41 @@ void launch_rope_table(float2* table, int n_pos, int d, double theta, hipStream_
 
 void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int mask_id, int vocab, const void* embed,
                        const void* mask_emb, float scale, int H, float* X, const void* gain, void* h_out, float eps,
-                       int32_t* err, hipStream_t s) {
+                       int32_t* err, hipStream_t s, float* rs_out) {
   if (dtype == DT_BF16)
     embed_norm_kernel<f16_t><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const bf16_t*)embed,
                                                      (const bf16_t*)mask_emb, scale, H, X, (const bf16_t*)gain,
-                                                     (f16_t*)h_out, eps, err);
+                                                     (f16_t*)h_out, eps, err, rs_out);
   else
     embed_norm_kernel<float><<<n_rows, 256, 0, s>>>(R, anchors, mask_id, vocab, (const float*)embed,
                                                      (const float*)mask_emb, scale, H, X, (const float*)gain,
-                                                     (float*)h_out, eps, err);
+                                                     (float*)h_out, eps, err, rs_out);
 }
 
 void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, int K, int R, const void* gain,
-                    void* h_out, float eps, hipStream_t s, const int32_t* n_valid, int valid_base) {
+                    void* h_out, float eps, hipStream_t s, const int32_t* n_valid, int valid_base, float* rs_out) {
   if (n_rows <= 0) return;
-  const int grid = n_rows;   // one 64-thread work-group per row
+  const int grid = n_rows;   // one 256-thread work-group per row
   if (dtype == DT_BF16)
-    rmsnorm_kernel<f16_t><<<grid, 64, 0, s>>>(n_rows, H, X, map_mask, K, R, (const bf16_t*)gain, (f16_t*)h_out, eps,
-                                                n_valid, valid_base);
+    rmsnorm_kernel<f16_t><<<grid, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, (const bf16_t*)gain, (f16_t*)h_out, eps,
+                                                 n_valid, valid_base, rs_out);
   else
-    rmsnorm_kernel<float><<<grid, 64, 0, s>>>(n_rows, H, X, map_mask, K, R, (const float*)gain, (float*)h_out, eps,
-                                                n_valid, valid_base);
+    rmsnorm_kernel<float><<<grid, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, (const float*)gain, (float*)h_out, eps,
+                                                 n_valid, valid_base, rs_out);
+}
+
+void launch_conv_post_norm(int dtype, int n_rows, int H, int G, float* X, int map_mask, int K, int R, const float* o,
+                           const float* corr, const void* base, const void* gain, void* h_out, float eps,
+                           float* rs_out, hipStream_t s) {
+  if (n_rows <= 0) return;
+  if (dtype == DT_BF16)
+    conv_post_norm_kernel<f16_t><<<n_rows, 256, 0, s>>>(n_rows, H, G, X, map_mask, K, R, o, corr,
+                                                        (const bf16_t*)base, (const bf16_t*)gain, (f16_t*)h_out, eps,
+                                                        rs_out);
+  else
+    conv_post_norm_kernel<float><<<n_rows, 256, 0, s>>>(n_rows, H, G, X, map_mask, K, R, o, corr,
+                                                        (const float*)base, (const float*)gain, (float*)h_out, eps,
+                                                        rs_out);
 }
 
 void launch_inject_scan(int n_req, const int32_t* slots, const int32_t* row_start, const int32_t* row_count,
@@ -2127,25 +2204,17 @@ void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, 
                                                            seed, step, out_tokens, out_len, accept_len, next_anchor);
 }
 
-void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const void* gain, float eps,
+void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const float* rs, const void* gain,
                      const float* corr, const void* base, void* y, hipStream_t s) {
-  if (dtype == DT_BF16)
-    dyn_conv_kernel<f16_t><<<M, 64, 0, s>>>(M, R, H, G, X, (const bf16_t*)gain, eps, corr,
-                                                       (const bf16_t*)base, (f16_t*)y);
-  else
-    dyn_conv_kernel<float><<<M, 64, 0, s>>>(M, R, H, G, X, (const float*)gain, eps, corr,
-                                                       (const float*)base, (float*)y);
-}
-
-void launch_dyn_conv_post(int dtype, int M, int R, int H, int G, const float* o, const float* corr,
-                          const void* base, float* X, hipStream_t s) {
   const int64_t n = (int64_t)M * (H / 4);
   if (n == 0) return;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (dtype == DT_BF16)
-    dyn_conv_post_kernel<bf16_t><<<blocks, 256, 0, s>>>(M, R, H, G, o, corr, (const bf16_t*)base, X);
+    dyn_conv_kernel<f16_t><<<blocks, 256, 0, s>>>(M, R, H, G, X, rs, (const bf16_t*)gain, corr, (const bf16_t*)base,
+                                                  (f16_t*)y);
   else
-    dyn_conv_post_kernel<float><<<blocks, 256, 0, s>>>(M, R, H, G, o, corr, (const float*)base, X);
+    dyn_conv_kernel<float><<<blocks, 256, 0, s>>>(M, R, H, G, X, rs, (const float*)gain, corr, (const float*)base,
+                                                  (float*)y);
 }
 
 void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const int32_t* slots,
@@ -2253,6 +2322,25 @@ void launch_copy_cache(int dtype, const void* cache_k, const void* cache_v, int 
 void launch_absmax_bf16(const void* w, int64_t n, uint32_t* out, hipStream_t s) {
   if (n <= 0) return;
   absmax_bf16_kernel<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 4096), 256, 0, s>>>((const bf16_t*)w, n, out);
+}
+
+void launch_absmax_f32(const float* w, int64_t n, uint32_t* out, hipStream_t s) {
+  if (n <= 0) return;
+  absmax_f32_kernel<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 4096), 256, 0, s>>>(w, n, out);
+}
+
+void launch_convert_f32_f16(const float* w, int64_t n, float scale, void* out, hipStream_t s) {
+  if (n <= 0) return;
+  convert_f32_f16_kernel<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 65536), 256, 0, s>>>(w, n, scale, (f16_t*)out);
+}
+
+void launch_matmul_nn(int dtype, int Rn, int J, int Kn, const void* A, const void* B, float* C, hipStream_t s) {
+  if (Rn <= 0 || J <= 0) return;
+  const dim3 grid(cdiv(J, 64), cdiv(Rn, 64));
+  if (dtype == DT_BF16)
+    matmul_nn_kernel<bf16_t><<<grid, 256, 0, s>>>(Rn, J, Kn, (const bf16_t*)A, (const bf16_t*)B, C);
+  else
+    matmul_nn_kernel<float><<<grid, 256, 0, s>>>(Rn, J, Kn, (const float*)A, (const float*)B, C);
 }
 
 void launch_convert_bf16_f16(const void* w, int64_t n, float scale, void* out, hipStream_t s) {

@@ -14,7 +14,7 @@ enum OpType { OP_F32 = 0, OP_BF16 = 1, OP_F16 = 2 };
 
 // ---- GEMM (gemm_inst.hip) ----
 enum EpiKind { EPI_STORE_F32 = 0, EPI_STORE_T, EPI_RESADD, EPI_SWIGLU, EPI_QKV, EPI_KVINJECT, EPI_LMHEAD,
-               EPI_STORE_DUAL };
+               EPI_STORE_SPLIT };
 
 struct GemmPlan {
   int bm = 128, bn = 128, splits = 1;
@@ -48,11 +48,13 @@ void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, 
 void launch_rope_table(float2* table, int n_pos, int d, double theta, hipStream_t s);
 void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int mask_id, int vocab, const void* embed,
                        const void* mask_emb, float scale, int H, float* X, const void* gain, void* h_out, float eps,
-                       int32_t* err, hipStream_t s);
+                       int32_t* err, hipStream_t s, float* rs_out = nullptr);
 // out row o reads X row (map_mask ? (o / K) * R + 1 + o % K : o); rows at or past
-// (*n_valid - valid_base) are skipped when n_valid is given (device-side row count)
+// (*n_valid - valid_base) are skipped when n_valid is given (device-side row count);
+// rs_out (or null) receives each output row's RMS scale rsqrt(mean(x^2) + eps)
 void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, int K, int R, const void* gain,
-                    void* h_out, float eps, hipStream_t s, const int32_t* n_valid = nullptr, int valid_base = 0);
+                    void* h_out, float eps, hipStream_t s, const int32_t* n_valid = nullptr, int valid_base = 0,
+                    float* rs_out = nullptr);
 void launch_inject_scan(int n_req, const int32_t* slots, const int32_t* row_start, const int32_t* row_count,
                         int32_t* ctx_len, int max_ctx, int max_batch, int64_t rows_upper, int32_t* req_off,
                         int32_t* req_pos, int32_t* err, hipStream_t s);
@@ -99,13 +101,15 @@ void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, 
                           uint64_t seed, uint64_t step, float* stats, int32_t* acc, float* chunks,
                           int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
                           int32_t* err, hipStream_t s);
-// DFlash 2: y = dynamic two-tap conv of x = RMSNorm(X; gain) [M, H] (blocks of R rows) with kernel
-// corrections corr [M, 2H/G]
-void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const void* gain, float eps,
+// DFlash 2: y = dynamic two-tap conv of x = X * rs * gain [M, H] (blocks of R rows, rs [M] the
+// rows' RMS scales) with kernel corrections corr [M, 2H/G]
+void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const float* rs, const void* gain,
                      const float* corr, const void* base, void* y, hipStream_t s);
-// X[m] += after-sub-layer convolution of o (fp32 [M, H]) with corrections corr [M, 2H/G]
-void launch_dyn_conv_post(int dtype, int M, int R, int H, int G, const float* o, const float* corr,
-                          const void* base, float* X, hipStream_t s);
+// DFlash 2: X[rows] += two-tap conv of the sub-layer output o (fp32 [M, H]) with corrections corr
+// [M, 2H/G], then RMSNorm of the updated rows into h_out (row mapping as launch_rmsnorm)
+void launch_conv_post_norm(int dtype, int n_rows, int H, int G, float* X, int map_mask, int K, int R, const float* o,
+                           const float* corr, const void* base, const void* gain, void* h_out, float eps,
+                           float* rs_out, hipStream_t s);
 // DFlash 2: selector pair-score table (scratch [n_req*K, C, C]) and walk over cand [n_req*K, C] with
 // gate [n_req*K, rank] and codebooks A, B [V, rank]
 void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const int32_t* slots,
@@ -149,6 +153,10 @@ void launch_reset_slots(int n, const int32_t* slots, int32_t* ctx_len, int max_b
 // *out must start at 0), and out = fp16(w * scale)
 void launch_absmax_bf16(const void* w, int64_t n, uint32_t* out, hipStream_t s);
 void launch_convert_bf16_f16(const void* w, int64_t n, float scale, void* out, hipStream_t s);
+void launch_absmax_f32(const float* w, int64_t n, uint32_t* out, hipStream_t s);
+void launch_convert_f32_f16(const float* w, int64_t n, float scale, void* out, hipStream_t s);
+// C [Rn, J] = A [Rn, Kn] . B [Kn, J] in fp32 (weights in the model dtype; create-time products)
+void launch_matmul_nn(int dtype, int Rn, int J, int Kn, const void* A, const void* B, float* C, hipStream_t s);
 void launch_philox_fill(int n, uint64_t seed, uint32_t slot, uint64_t step, uint32_t purpose, float* out,
                         hipStream_t s);
 
