@@ -98,6 +98,7 @@ struct dflash_handle {
   // symmetric sampling truncation (dflash_set_sampling)
   int trunc_k = 0;
   float trunc_p = 1.f;
+  Nucleus* nuc = nullptr;                 // top-p sets over whole rows (trunc_k 0, trunc_p < 1)
   float *vt_max = nullptr, *vrow_max = nullptr, *vrow_lse = nullptr;   // tile maxima, row max / log-sum
   int32_t *tr_ids = nullptr, *kp_ids = nullptr;
   float *tr_probs = nullptr, *kp_probs = nullptr;
@@ -520,6 +521,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
       if ((rc = alloc_t(h, &h->tr_probs, vrows * 64, 4))) break;
       if ((rc = alloc_t(h, &h->kp_ids, vrows * 64, 4))) break;
       if ((rc = alloc_t(h, &h->kp_probs, vrows * 64, 4))) break;
+      if ((rc = alloc_t(h, &h->nuc, vrows, sizeof(Nucleus)))) break;
     }
     if (c.conv_group > 0) {
       if ((rc = alloc(h, &h->hbuf2, (size_t)h->maxM * H * es))) break;
@@ -844,6 +846,9 @@ void select_stage(dflash_handle* h, hipStream_t s, int n_req, const int32_t* slo
                 h->tr_ids, h->tr_probs, s);
     launch_trunc_rows(rows, h->trunc_k, h->trunc_p, h->tr_ids, h->tr_probs, h->kp_ids, h->kp_probs, s);
     launch_sparse_sample(rows, K, h->trunc_k, slots, p->seed, p->step, h->kp_ids, h->kp_probs, o->draft_ids, s);
+  } else if (T > 0.f && h->trunc_p < 1.f) {   // top-p over whole rows
+    launch_nucleus(rows, V, logits, rows, rows, 0, h->row_max, 1, inv_t, h->trunc_p, h->nuc, s);
+    launch_nucleus_sample(rows, K, V, slots, p->seed, p->step, inv_t, logits, h->row_max, h->nuc, o->draft_ids, s);
   } else if (T > 0.f) {
     launch_sample(rows, K, slots, p->seed, p->step, inv_t, logits, V, h->n_vtiles, h->lm_tile, h->tmax, h->tsum,
                   h->row_max, o->draft_ids, s);
@@ -1156,7 +1161,7 @@ int dflash_set_page_table(dflash_handle* h, const int32_t* table) {
 int dflash_set_sampling(dflash_handle* h, int32_t top_k, float top_p) {
   if (!h) return DFLASH_E_INVALID;
   if (top_k < 0 || top_k > 64 || !(top_p > 0.f && top_p <= 1.f)) return DFLASH_E_INVALID;
-  if (top_k == 0 && top_p < 1.f) return DFLASH_E_UNSUPPORTED;   // top-p is applied within a top-k set
+  if (top_k == 0 && top_p < 1.f && !draw_vocab_ok(h->cfg.vocab)) return DFLASH_E_CAPACITY;
   if (top_k > h->cfg.vocab) return DFLASH_E_CAPACITY;
   h->trunc_k = top_k;
   h->trunc_p = top_p;
@@ -1192,7 +1197,7 @@ int dflash_verify(dflash_handle* h, void* stream, int32_t n_req, int32_t K, cons
   } else {
     launch_verify_rejection(n_req, K, c.vocab, slots, draft_ids, draft_logits, target_logits, 1.0f / temperature,
                             seed, step, h->vstats, h->vacc, h->vchunks, out_tokens, out_len, accept_len,
-                            next_anchor, h->err, s);
+                            next_anchor, h->err, s, h->trunc_p < 1.f ? h->nuc : nullptr, h->trunc_p);
   }
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }
@@ -1278,7 +1283,7 @@ int dflash_verify_subset(dflash_handle* h, void* stream, int32_t n_req, int32_t 
     }
     launch_verify_subset(n_req, K, C, c.vocab, slots, draft_ids, cand_ids, cand_probs, target_logits,
                          1.0f / temperature, seed, step, h->vstats, h->vacc, h->vchunks, out_tokens, out_len,
-                         accept_len, next_anchor, h->err, s);
+                         accept_len, next_anchor, h->err, s, h->trunc_p < 1.f ? h->nuc : nullptr, h->trunc_p);
   }
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;
 }

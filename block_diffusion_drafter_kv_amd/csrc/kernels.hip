@@ -1115,6 +1115,223 @@ __device__ int chunk_draw(int V, float u, WF wf, const float* csum, float* sh, i
   return pick;
 }
 
+// ---------------------------------------------------------------------------
+// Top-p over whole rows [P2 §3.3, with no top-k cut]: the set of ids in
+// probability-descending order (ties: ascending id) up to the one whose
+// cumulative probability reaches top_p.  Probabilities are compared through an
+// order-preserving uint32 key of s = z / T; the threshold key is found by a
+// radix select from the most significant byte, each pass a histogram of the
+// probability mass (exp(s - row max)) of the ids that still match the prefix.
+// Ids at the threshold key have equal probability; the set takes the fewest of
+// them, lowest ids first, that reach top_p.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ bool in_nucleus(float s, int id, const Nucleus& n) {
+  const uint32_t k = order_key(s);
+  return k > n.key || (k == n.key && id <= n.cut);
+}
+
+// The probability law of one row as the rejection kernels use it: exp(s - m) * inv,
+// zero outside the row's top-p set when one is given.
+struct RowLaw {
+  float m, inv;
+  const Nucleus* n;
+  __device__ __forceinline__ float operator()(float s, int id) const {
+    if (n && !in_nucleus(s, id, *n)) return 0.f;
+    return exp_sum_term(s - m) * inv;
+  }
+};
+__device__ __forceinline__ RowLaw row_law(const float* st, const Nucleus* nuc, int j) {
+  RowLaw L;
+  L.m = st[2 * j];
+  L.n = nuc ? nuc + j : nullptr;
+  L.inv = 1.0f / (nuc ? nuc[j].mass : st[2 * j + 1]);
+  return L;
+}
+
+// one 512-thread work-group per row; each wave fills its own histogram with LDS
+// atomics and the waves' histograms are summed in a fixed order
+constexpr int NUC_THREADS = 512, NUC_WAVES = NUC_THREADS / 64;
+__global__ __launch_bounds__(NUC_THREADS) void nucleus_kernel(int V, const float* logits, int per, int nrow, int off,
+                                                               const float* st_max, int st_stride, float inv_temp,
+                                                               float top_p, int vec, Nucleus* out) {
+  __shared__ float hm[NUC_WAVES][256];
+  __shared__ int hc[NUC_WAVES][256];
+  __shared__ uint32_t s_prefix, s_mask;
+  __shared__ float s_above, s_target;
+  __shared__ int s_cnt, s_cut;
+  __shared__ int scan[NUC_WAVES];
+  const int i = blockIdx.x;
+  const int j = (i / per) * nrow + off + i % per;
+  const float* z = logits + (int64_t)i * V;
+  const float mx = st_max[(int64_t)j * st_stride];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool vv = vec != 0;
+  if (tid == 0) {
+    s_prefix = 0;
+    s_mask = 0;
+    s_above = 0.f;
+  }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int b = lane; b < 256; b += 64) {
+      hm[w][b] = 0.f;
+      hc[w][b] = 0;
+    }
+    __syncthreads();
+    const uint32_t prefix = s_prefix, mask = s_mask;
+    for (int c = tid * 4; c < V; c += 4 * NUC_THREADS) {
+      float x[4];
+      load4_row(z, c, V, vv, x);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float sv = x[q] * inv_temp;
+        const uint32_t k = order_key(sv);
+        if (c + q < V && (k & mask) == prefix) {
+          const int b = (int)((k >> shift) & 255u);
+          atomicAdd(&hm[w][b], exp_sum_term(sv - mx));
+          atomicAdd(&hc[w][b], 1);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < 256) {   // 256 buckets, one per thread; waves summed in a fixed order
+      const int b = tid;
+      float sm = hm[0][b];
+      int sc = hc[0][b];
+      for (int q = 1; q < NUC_WAVES; ++q) {
+        sm += hm[q][b];
+        sc += hc[q][b];
+      }
+      hm[0][b] = sm;
+      hc[0][b] = sc;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      if (pass == 0) {   // the row's total, in the same terms as the members' mass
+        float t = 0.f;
+        for (int b = 255; b >= 0; --b) t += hm[0][b];
+        s_target = top_p * t;
+      }
+      const float above = s_above, target = s_target;
+      float cum = 0.f, cum_low = 0.f;
+      int sel = -1, low = -1;
+      for (int b = 255; b >= 0; --b) {
+        if (hc[0][b] == 0) continue;
+        if (above + cum + hm[0][b] >= target) {
+          sel = b;
+          break;
+        }
+        low = b;
+        cum_low = cum;
+        cum += hm[0][b];
+      }
+      if (sel < 0) {   // rounding left the target past the total: every remaining id
+        sel = low < 0 ? 0 : low;
+        cum = cum_low;
+      }
+      s_above = above + cum;
+      s_prefix = prefix | ((uint32_t)sel << shift);
+      s_mask = mask | (255u << shift);
+      s_cnt = hc[0][sel];
+    }
+    __syncthreads();
+  }
+  const uint32_t key = s_prefix;
+  const float above = s_above;
+  const int cnt = s_cnt;
+  const float wk = exp_sum_term(key_value(key) - mx);
+  int kk = cnt;
+  if (wk > 0.f) {
+    const float need = (s_target - above) / wk;
+    kk = need <= 1.f ? 1 : min(cnt, (int)ceilf(need));
+  }
+  if (kk >= cnt) {
+    if (tid == 0) s_cut = 0x7fffffff;   // all ids at the threshold
+  } else {
+    // the kk-th lowest id at the threshold key: ascending 1024-id chunks
+    if (tid == 0) s_cut = -1;
+    int before = 0;
+    for (int c0 = 0; c0 < V; c0 += 4 * NUC_THREADS) {
+      const int c = c0 + tid * 4;
+      float x[4];
+      load4_row(z, c, V, vv, x);
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) n += (c + q < V && order_key(x[q] * inv_temp) == key) ? 1 : 0;
+      // inclusive scan of n over the 256 threads
+      int incl = n;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      __syncthreads();
+      if (lane == 63) scan[w] = incl;
+      __syncthreads();
+      int add = before, chunk_total = 0;
+      for (int q = 0; q < NUC_WAVES; ++q) {
+        if (q < w) add += scan[q];
+        chunk_total += scan[q];
+      }
+      const int ex = add + incl - n;   // ids at the key before this thread's four
+      if (n > 0 && ex < kk && kk <= ex + n) {
+        int seen = ex;
+        for (int q = 0; q < 4; ++q)
+          if (c + q < V && order_key(x[q] * inv_temp) == key && ++seen == kk) s_cut = c + q;
+      }
+      before += chunk_total;
+      __syncthreads();
+      if (before >= kk) break;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    Nucleus nu;
+    nu.key = key;
+    nu.cut = s_cut;
+    nu.mass = above + (float)kk * wk;
+    nu.pad = 0.f;
+    out[j] = nu;
+  }
+}
+
+// draft draw from the top-p set of each row: one 256-thread work-group per row,
+// inverse CDF in ascending id order (Philox(seed; j+1, slot, step, 0))
+__global__ __launch_bounds__(256) void nucleus_sample_kernel(int K, int V, const int32_t* slots, uint64_t seed,
+                                                              uint64_t step, float inv_temp, const float* logits,
+                                                              const float* row_max, const Nucleus* nuc, int vec,
+                                                              int32_t* draft_ids) {
+  extern __shared__ float csum[];
+  __shared__ float sh[4];
+  __shared__ int si[2];
+  const int m = blockIdx.x;
+  const int r = m / K, j = m % K;
+  const float* z = logits + (int64_t)m * V;
+  const float mx = row_max[m];
+  const Nucleus nu = nuc[m];
+  const bool vv = vec != 0;
+  auto wf = [&](int c0, float* e) {
+    float x[4];
+    load4_row(z, c0, V, vv, x);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float sv = x[q] * inv_temp;
+      e[q] = c0 + q < V && in_nucleus(sv, c0 + q, nu) ? exp_sum_term(sv - mx) : 0.f;
+    }
+  };
+  chunk_sums(V, wf, csum);
+  __syncthreads();
+  const float u = philox_uniform(seed, (uint32_t)slots[r], step, (uint32_t)(j + 1), PURPOSE_DRAFT);
+  const int pick = chunk_draw(V, u, wf, csum, sh, si);
+  if (threadIdx.x == 0) draft_ids[m] = pick;
+}
+
 static constexpr float RESIDUAL_EPS = 9.5367431640625e-07f;  // 2^-20
 
 // Rejection verification at temperature T > 0 [P2 §2.3, §4.2; P1 "验证"], in
@@ -1143,7 +1360,7 @@ __global__ __launch_bounds__(64) void verify_accept_kernel(int K, int V, int sub
                                                             const float* target, float inv_temp,
                                                             const float* stats, int C, const int32_t* cand_ids,
                                                             const float* cand_probs, uint64_t seed, uint64_t step,
-                                                            int32_t* acc_out, int32_t* err) {
+                                                            int32_t* acc_out, int32_t* err, const Nucleus* nuc) {
   const int r = blockIdx.x, lane = threadIdx.x;
   const int nrow = subset ? K + 1 : 2 * K + 1;
   const float* ts = stats + (int64_t)r * nrow * 2;
@@ -1154,8 +1371,10 @@ __global__ __launch_bounds__(64) void verify_accept_kernel(int K, int V, int sub
     if (bad) {
       fail = true;
     } else {
-      const float p = expf(target[((int64_t)r * (K + 1) + lane) * V + tok] * inv_temp - ts[2 * lane]) /
-                      ts[2 * lane + 1];
+      const Nucleus* nr = nuc ? nuc + (int64_t)r * nrow : nullptr;
+      const float p = nr ? row_law(ts, nr, lane)(target[((int64_t)r * (K + 1) + lane) * V + tok] * inv_temp, tok)
+                         : expf(target[((int64_t)r * (K + 1) + lane) * V + tok] * inv_temp - ts[2 * lane]) /
+                               ts[2 * lane + 1];
       float q = 0.f;
       if (subset) {
         const int64_t b = ((int64_t)r * K + lane) * C;
@@ -1163,7 +1382,8 @@ __global__ __launch_bounds__(64) void verify_accept_kernel(int K, int V, int sub
           if (cand_ids[b + j] == tok) q += cand_probs[b + j];
       } else {
         const int sr = K + 1 + lane;
-        q = expf(draft_logits[((int64_t)r * K + lane) * V + tok] * inv_temp - ts[2 * sr]) / ts[2 * sr + 1];
+        const float sq = draft_logits[((int64_t)r * K + lane) * V + tok] * inv_temp;
+        q = nr ? row_law(ts, nr, sr)(sq, tok) : expf(sq - ts[2 * sr]) / ts[2 * sr + 1];
       }
       const float u = philox_uniform(seed, (uint32_t)slots[r], step, (uint32_t)(lane + 1), PURPOSE_ACCEPT);
       fail = !(u * q < p);
@@ -1179,7 +1399,7 @@ __global__ __launch_bounds__(64) void verify_accept_kernel(int K, int V, int sub
 __global__ __launch_bounds__(256) void resid_chunks_kernel(int K, int V, int dense, const float* draft_logits,
                                                             const float* target, float inv_temp,
                                                             const float* stats, int vec, const int32_t* acc,
-                                                            int per_wg, float* csp, float* csr) {
+                                                            int per_wg, float* csp, float* csr, const Nucleus* nuc) {
   const int r = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
   const int a = acc[r];
@@ -1188,8 +1408,9 @@ __global__ __launch_bounds__(256) void resid_chunks_kernel(int K, int V, int den
   const float* ts = stats + (int64_t)r * nrow * 2;
   const float* t = target + ((int64_t)r * (K + 1) + a) * V;
   const float* z = draft_logits + ((int64_t)r * K + (resid ? a : 0)) * V;
-  const float pm = ts[2 * a], ips = 1.0f / ts[2 * a + 1];
-  const float qm = resid ? ts[2 * (K + 1 + a)] : 0.f, iqs = resid ? 1.0f / ts[2 * (K + 1 + a) + 1] : 1.f;
+  const Nucleus* nr = nuc ? nuc + (int64_t)r * nrow : nullptr;
+  const RowLaw P = row_law(ts, nr, a);
+  const RowLaw Q = resid ? row_law(ts, nr, K + 1 + a) : P;
   const bool vv = vec != 0;
   const int ch0 = blockIdx.x * per_wg, ch1 = min(nch, ch0 + per_wg);
   float* op = csp + (int64_t)r * nch;
@@ -1208,9 +1429,9 @@ __global__ __launch_bounds__(256) void resid_chunks_kernel(int K, int V, int den
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (cb + q < V) {
-          const float pv = exp_sum_term(x[j][q] * inv_temp - pm) * ips;
+          const float pv = P(x[j][q] * inv_temp, cb + q);
           sp += pv;
-          if (resid) sr += fmaxf(pv - exp_sum_term(y[j][q] * inv_temp - qm) * iqs, 0.f);
+          if (resid) sr += fmaxf(pv - Q(y[j][q] * inv_temp, cb + q), 0.f);
         }
       }
       sp = wave_sum(sp);
@@ -1231,7 +1452,7 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(int K, int V, int subs
                                                            const int32_t* acc, const float* csp, const float* csr,
                                                            uint64_t seed, uint64_t step, int32_t* out_tokens,
                                                            int32_t* out_len, int32_t* accept_len,
-                                                           int32_t* next_anchor) {
+                                                           int32_t* next_anchor, const Nucleus* nuc) {
   extern __shared__ float csum[];
   __shared__ float sh[4];
   __shared__ int si[2];
@@ -1246,9 +1467,9 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(int K, int V, int subs
   const float* ts = stats + (int64_t)r * nrow * 2;
   const float* t = target + ((int64_t)r * (K + 1) + a) * V;
   const float* z = draft_logits ? draft_logits + ((int64_t)r * K + (bonus ? 0 : a)) * V : nullptr;
-  const float pm = ts[2 * a], ips = 1.0f / ts[2 * a + 1];
-  const float qm = !subset && !bonus ? ts[2 * (K + 1 + a)] : 0.f;
-  const float iqs = !subset && !bonus ? 1.0f / ts[2 * (K + 1 + a) + 1] : 1.f;
+  const Nucleus* nr = nuc ? nuc + (int64_t)r * nrow : nullptr;
+  const RowLaw P = row_law(ts, nr, a);
+  const RowLaw Q = !subset && !bonus ? row_law(ts, nr, K + 1 + a) : P;
   const bool vv = vec != 0;
   if (subset && threadIdx.x == 0) {
     // candidates of the rejected position, sorted by id, equal ids merged
@@ -1284,7 +1505,7 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(int K, int V, int subs
     float x[4];
     load4_row(t, c0, V, vv, x);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) e[q] = c0 + q < V ? exp_sum_term(x[q] * inv_temp - pm) * ips : 0.f;
+    for (int q = 0; q < 4; ++q) e[q] = c0 + q < V ? P(x[q] * inv_temp, c0 + q) : 0.f;
   };
   auto wr = [&](int c0, float* e) {   // the residual of ids c0..c0+3
     wp(c0, e);
@@ -1300,7 +1521,7 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(int K, int V, int subs
       load4_row(z, c0, V, vv, y);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (c0 + q < V) e[q] = fmaxf(e[q] - exp_sum_term(y[q] * inv_temp - qm) * iqs, 0.f);
+        if (c0 + q < V) e[q] = fmaxf(e[q] - Q(y[q] * inv_temp, c0 + q), 0.f);
     }
   };
   bool use_resid = !bonus;
@@ -1308,7 +1529,7 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(int K, int V, int subs
     if (subset && threadIdx.x == 0) {   // p - min(p, q) at each candidate, in id order
       for (int k = 0; k < nc; ++k) {
         const int id = sc_id[k];
-        const float pv = exp_sum_term(t[id] * inv_temp - pm) * ips;
+        const float pv = P(t[id] * inv_temp, id);
         const int ch = id / DRAW_CHUNK;
         csum[ch] = fmaxf(csum[ch] - fminf(pv, sc_q[k]), 0.f);
       }
@@ -2168,40 +2389,46 @@ void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, cons
                              const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
                              uint64_t step, float* stats, int32_t* acc, float* chunks, int32_t* out_tokens,
                              int32_t* out_len, int32_t* accept_len, int32_t* next_anchor, int32_t* err,
-                             hipStream_t s) {
+                             hipStream_t s, Nucleus* nuc, float top_p) {
   // stats rows per request: K+1 target rows then K draft rows
   const int vec = rows_vec_ok(V, target) && rows_vec_ok(V, draft_logits);
   const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
   launch_row_stats(n_req * (K + 1), V, target, inv_temp, nullptr, 0, stats, stats + 1, 2, K + 1, 2 * K + 1, 0, 0, s);
   launch_row_stats(n_req * K, V, draft_logits, inv_temp, nullptr, 0, stats, stats + 1, 2, K, 2 * K + 1, K + 1, 0, s);
+  if (nuc) {   // top-p sets of the target rows and of the draft rows, at the statistics' indices
+    launch_nucleus(n_req * (K + 1), V, target, K + 1, 2 * K + 1, 0, stats, 2, inv_temp, top_p, nuc, s);
+    launch_nucleus(n_req * K, V, draft_logits, K, 2 * K + 1, K + 1, stats, 2, inv_temp, top_p, nuc, s);
+  }
   verify_accept_kernel<<<n_req, 64, 0, s>>>(K, V, 0, slots, draft_ids, draft_logits, target, inv_temp, stats, 0,
-                                            nullptr, nullptr, seed, step, acc, err);
+                                            nullptr, nullptr, seed, step, acc, err, nuc);
   const int per_wg = RESID_CHUNKS_PER_WG;
   float* csp = chunks;
   float* csr = chunks + (int64_t)n_req * nch;
   resid_chunks_kernel<<<dim3(cdiv(nch, per_wg), n_req), 256, 0, s>>>(K, V, 1, draft_logits, target, inv_temp, stats,
-                                                                     vec, acc, per_wg, csp, csr);
+                                                                     vec, acc, per_wg, csp, csr, nuc);
   verify_draw_kernel<<<n_req, 256, draw_lds_bytes(V), s>>>(K, V, 0, slots, draft_ids, draft_logits, target, inv_temp,
                                                            stats, vec, 0, nullptr, nullptr, acc, csp, csr, seed, step,
-                                                           out_tokens, out_len, accept_len, next_anchor);
+                                                           out_tokens, out_len, accept_len, next_anchor, nuc);
 }
 
 void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, const int32_t* draft_ids,
                           const int32_t* cand_ids, const float* cand_probs, const float* target, float inv_temp,
                           uint64_t seed, uint64_t step, float* stats, int32_t* acc, float* chunks,
                           int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
-                          int32_t* err, hipStream_t s) {
+                          int32_t* err, hipStream_t s, Nucleus* nuc, float top_p) {
   const int vec = rows_vec_ok(V, target);
   const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
   launch_row_stats(n_req * (K + 1), V, target, inv_temp, nullptr, 0, stats, stats + 1, 2, 1 << 30, 1 << 30, 0, 0, s);
+  if (nuc) launch_nucleus(n_req * (K + 1), V, target, 1 << 30, 1 << 30, 0, stats, 2, inv_temp, top_p, nuc, s);
   verify_accept_kernel<<<n_req, 64, 0, s>>>(K, V, 1, slots, draft_ids, nullptr, target, inv_temp, stats, C, cand_ids,
-                                            cand_probs, seed, step, acc, err);
+                                            cand_probs, seed, step, acc, err, nuc);
   const int per_wg = RESID_CHUNKS_PER_WG;
   resid_chunks_kernel<<<dim3(cdiv(nch, per_wg), n_req), 256, 0, s>>>(K, V, 0, nullptr, target, inv_temp, stats, vec,
-                                                                     acc, per_wg, chunks, chunks);
+                                                                     acc, per_wg, chunks, chunks, nuc);
   verify_draw_kernel<<<n_req, 256, draw_lds_bytes(V), s>>>(K, V, 1, slots, draft_ids, nullptr, target, inv_temp,
                                                            stats, vec, C, cand_ids, cand_probs, acc, chunks, chunks,
-                                                           seed, step, out_tokens, out_len, accept_len, next_anchor);
+                                                           seed, step, out_tokens, out_len, accept_len, next_anchor,
+                                                           nuc);
 }
 
 void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const float* rs, const void* gain,
@@ -2231,6 +2458,21 @@ void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const 
                                                    (const float*)B, table, err);
   sel_walk_kernel<<<n_req, 64, 0, s>>>(K, C, slots, cand, table, temperature > 0.f ? 1.0f / temperature : 0.f, seed,
                                        step, draft_ids, cand_out, probs_out);
+}
+
+void launch_nucleus(int rows, int V, const float* logits, int per, int nrow, int off, const float* st_max,
+                    int st_stride, float inv_temp, float top_p, Nucleus* out, hipStream_t s) {
+  if (rows <= 0) return;
+  nucleus_kernel<<<rows, NUC_THREADS, 0, s>>>(V, logits, per, nrow, off, st_max, st_stride, inv_temp, top_p,
+                                              rows_vec_ok(V, logits), out);
+}
+
+void launch_nucleus_sample(int rows, int K, int V, const int32_t* slots, uint64_t seed, uint64_t step,
+                           float inv_temp, const float* logits, const float* row_max, const Nucleus* nuc,
+                           int32_t* draft_ids, hipStream_t s) {
+  if (rows <= 0) return;
+  nucleus_sample_kernel<<<rows, 256, draw_lds_bytes(V), s>>>(K, V, slots, seed, step, inv_temp, logits, row_max, nuc,
+                                                            rows_vec_ok(V, logits), draft_ids);
 }
 
 void launch_trunc_rows(int rows, int k, float top_p, const int32_t* ids_in, const float* probs_in,

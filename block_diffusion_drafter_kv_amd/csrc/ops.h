@@ -44,6 +44,18 @@ void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStre
 void launch_attn_waves(int D, int qrt, const AttnArgs& a, int grid, hipStream_t s);
 void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, hipStream_t s);
 
+// Top-p set of one row over the whole vocabulary (no top-k): the ids in
+// probability-descending order (ties: ascending id) up to the one whose
+// cumulative probability reaches top_p.  Members: ids whose key(z / T) exceeds
+// key, or equals it with id <= cut (key: order-preserving uint32 image of the
+// float); mass = sum of exp(z / T - row max) over the members.
+struct Nucleus {
+  uint32_t key;
+  int32_t cut;
+  float mass;
+  float pad;
+};
+
 // ---- elementwise / row kernels (kernels.hip) ----
 void launch_rope_table(float2* table, int n_pos, int d, double theta, hipStream_t s);
 void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int mask_id, int vocab, const void* embed,
@@ -100,7 +112,7 @@ void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, 
                           const int32_t* cand_ids, const float* cand_probs, const float* target, float inv_temp,
                           uint64_t seed, uint64_t step, float* stats, int32_t* acc, float* chunks,
                           int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
-                          int32_t* err, hipStream_t s);
+                          int32_t* err, hipStream_t s, Nucleus* nuc = nullptr, float top_p = 1.f);
 // DFlash 2: y = dynamic two-tap conv of x = X * rs * gain [M, H] (blocks of R rows, rs [M] the
 // rows' RMS scales) with kernel corrections corr [M, 2H/G]
 void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const float* rs, const void* gain,
@@ -118,6 +130,15 @@ void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const 
                      int32_t* draft_ids, int32_t* cand_out, float* probs_out, int32_t* err, hipStream_t s);
 // symmetric top-k / top-p truncation: rows of top-k (ids, full-vocabulary probabilities), k <= 64 ->
 // kept ids (-1 elsewhere) and renormalised probabilities
+// top-p sets over whole rows: row i of logits [rows, V] (z / T with T = 1 / inv_temp) with its
+// statistics at index j = (i / per) * nrow + off + i % per of st_max (row max of z / T, stride
+// st_stride); the set goes to out[j]
+void launch_nucleus(int rows, int V, const float* logits, int per, int nrow, int off, const float* st_max,
+                    int st_stride, float inv_temp, float top_p, Nucleus* out, hipStream_t s);
+// draft draws from the top-p sets of rows [rows = n_req * K] (Philox as launch_sample)
+void launch_nucleus_sample(int rows, int K, int V, const int32_t* slots, uint64_t seed, uint64_t step,
+                           float inv_temp, const float* logits, const float* row_max, const Nucleus* nuc,
+                           int32_t* draft_ids, hipStream_t s);
 void launch_trunc_rows(int rows, int k, float top_p, const int32_t* ids_in, const float* probs_in,
                        int32_t* ids_out, float* probs_out, hipStream_t s);
 // draft tokens drawn from truncated rows (row j of request r: Philox(seed; j+1, slot, step, 0))
@@ -137,7 +158,7 @@ void launch_verify_rejection(int n_req, int K, int V, const int32_t* slots, cons
                              const float* draft_logits, const float* target, float inv_temp, uint64_t seed,
                              uint64_t step, float* stats, int32_t* acc, float* chunks, int32_t* out_tokens,
                              int32_t* out_len, int32_t* accept_len, int32_t* next_anchor, int32_t* err,
-                             hipStream_t s);
+                             hipStream_t s, Nucleus* nuc = nullptr, float top_p = 1.f);
 // out[i] = in[i] if in [0, max_batch) else max_batch (a spare empty slot), flagging the error word
 void launch_sanitize_slots(int n, const int32_t* in, int32_t* out, int max_batch, int32_t* err, hipStream_t s);
 void launch_synth_target(int n_req, int K, int V, const float* draft_logits, float sigma, uint64_t seed,

@@ -288,7 +288,11 @@ int dflash_set_page_table(dflash_handle* h, const int32_t* table);
  * renormalised: the draft's sampling (not the selector's walk), and in
  * dflash_verify both p and q, in dflash_verify_subset p.  Truncated draws are
  * inverse CDFs in ascending id order.  top_k 0 = off (the default); 1..64;
- * top_p in (0, 1] (1 = off) needs top_k >= 1 (else DFLASH_E_UNSUPPORTED). */
+ * top_p in (0, 1] (1 = off).  top_p < 1 with top_k 0 cuts the whole row:
+ * the set is the shortest prefix of the full probability-descending order
+ * (ties: ascending id) that reaches top_p, found by a radix select over the
+ * row, and draws and verification run over the full vocabulary with the ids
+ * outside it at probability 0 (needs vocab <= 2^21, else DFLASH_E_CAPACITY). */
 int dflash_set_sampling(dflash_handle* h, int32_t top_k, float top_p);
 
 /* Verification of one drafted block per request [P2 §2.3, §4.2; P1 "验证"].

@@ -250,6 +250,41 @@ def test_full_verify_rejection_b4(gpu_lib):
     dr.close()
 
 
+def test_full_whole_row_top_p_draws(gpu_lib):
+    """Sampled drafts under top-p 0.9 with no top-k cut at full vocabulary (V = 151936; the
+    cut is a radix select over each whole row): draws against the oracle's truncated draw,
+    and always inside the oracle's top-p set unless that row's cut is a near-tie."""
+    wl = get_workload("b4_ctx32k")
+    cfg, K, B, V = wl.model, wl.K, wl.batch, wl.model.vocab
+    import block_diffusion_drafter_kv_amd as dk
+    dr = dk.Drafter(cfg, _idle_weights(cfg), max_batch=B, max_ctx=64, max_k=K, max_inject_rows=64)
+    dr.set_sampling(0, 0.9)
+    # logits N(0, 6^2): sets of a few to ~100 ids, whose cuts sit well clear of fp32 rounding
+    z = gen.logits_like((B, K, V), 6.0, 43, "draft").numpy()
+    tal = Tally("whole-row top-p draws, full vocabulary")
+    for step in range(2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        zd = torch.tensor(z, device="cuda")
+        e0.record()
+        o = dr.select_from_logits(_dev(np.arange(B)), None, zd, temperature=1.0, seed=wl.philox_seed, step=step)
+        e1.record()
+        torch.cuda.synchronize()
+        print(f"[timing] whole-row top-p selection of {B * K} rows: {e0.elapsed_time(e1) * 1e3:.0f} us", flush=True)
+        ids = o["draft_ids"].cpu().numpy()
+        for i in range(B):
+            r = osel.select_block(z[i], 1.0, 0, wl.philox_seed, i, step, trunc_k=0, trunc_p=0.9)
+            for j in range(K):
+                _, keep, cut_margin = osel.truncate(osel.softmax(z[i, j], 1.0), 0, 0.9)
+                assert ids[i, j] in set(keep.tolist()) or cut_margin < 1e-5, f"step {step} req {i} pos {j}"
+                decided = r["margins"][j] > 1e-5
+                tal.add(decided)
+                if decided:
+                    assert ids[i, j] == r["draft_ids"][j], f"step {step} req {i} pos {j}"
+    tal.assert_floor(0.9, min_total=2 * B * K)
+    assert dr.get_error() == 0
+    dr.close()
+
+
 def test_full_topk_tree_b64(gpu_lib):
     """Per-position top-64 and the best-first B = 64 prefix tree at the larger drafter's
     shapes (batch 64, K = 16, V = 151936), from the same fp32 logits on both sides."""

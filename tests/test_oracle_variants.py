@@ -143,3 +143,22 @@ def test_truncated_sampling_and_lossless_rejection():
         oc[v["out_tokens"][0]] += 1
     assert _chi2(dc, qt, n) > 1e-3
     assert _chi2(oc, pt, n) > 1e-3
+
+
+def test_whole_row_top_p_pins():
+    """Top-p with no top-k cut on hand-worked rows: probability-descending order (ties:
+    ascending id), the shortest prefix whose cumulative probability reaches top_p (the id
+    that crosses kept), renormalised."""
+    p = np.array([0.1, 0.4, 0.3, 0.2])
+    t, keep, _ = osel.truncate(p, 0, 0.7)                 # 0.4 + 0.3 reaches 0.7 exactly
+    assert list(keep) == [1, 2] and np.allclose(t, [0, 4 / 7, 3 / 7, 0])
+    t, keep, _ = osel.truncate(p, 0, 0.71)                # needs the third id
+    assert list(keep) == [1, 2, 3] and np.allclose(t, [0, 4 / 9, 3 / 9, 2 / 9])
+    t, keep, _ = osel.truncate(p, 0, 0.35)                # the top id alone crosses
+    assert list(keep) == [1] and np.allclose(t, [0, 1, 0, 0])
+    q = np.full(4, 0.25)                                  # all tied: lowest ids first
+    assert list(osel.truncate(q, 0, 0.5)[1]) == [0, 1]
+    assert list(osel.truncate(q, 0, 0.51)[1]) == [0, 1, 2]
+    r = np.array([0.3, 0.2, 0.3, 0.2])                    # ties at both levels
+    assert list(osel.truncate(r, 0, 0.55)[1]) == [0, 2]   # 0.6 >= 0.55 after two
+    assert list(osel.truncate(r, 0, 0.65)[1]) == [0, 2, 1]
