@@ -22,6 +22,12 @@ GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide, bool big
     p.bm = p.bn = 256;
     return p;
   }
+  if (w16 && wide && M <= 64) {
+    // the vocabulary product over a few rows (weight streaming): 64 x 128 tiles,
+    // 3-deep rings (16 x 151936 x 4096: 231 us, against 240 us for 128 x 128)
+    p.bm = 64;
+    return p;
+  }
   if (w16 && wide) {
     // the vocabulary product: 128 x 128 tiles with a 3-deep weight ring (measured
     // on the 512 x 151936 x 4096 LM head: 743 us, against 1023 us for 128 x 256)
@@ -66,6 +72,11 @@ GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide, bool big
   // 544-row products: O 66 -> 45 us, down 175 -> 116 us, QKV 69 -> 56 us)
   if (w16 && p.bm == 128 && p.bn == 128 && (long)((M + 127) / 128) * ((N + p.bn - 1) / p.bn) < 2L * num_cus)
     p.bm = 64;
+  // up to 64 rows (weight streaming): 64 x 64 tiles with 4-deep rings, K split
+  // below (17 rows: QKV 19.4 -> 17.1 us, O 17.2 -> 14.0, gate/up 36.7 -> 33.9,
+  // down 26.4 -> 24.5, fc 38.6 -> 33.4 against 64 x 128 tiles; epilogues on whole
+  // heads keep 128-wide tiles, see runnable_plan)
+  if (w16 && M <= 64 && p.bn == 128 && N % 64 == 0) p.bn = 64;
   const int bk = w16 ? 64 : 32;
   const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   const int kt = K / bk;
@@ -73,7 +84,7 @@ GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide, bool big
   // Split K for grids far below one work-group per CU (small-M, weight-streaming
   // products), and in two for long products that leave CUs idle; otherwise the
   // partial tiles and their reduction cost more than a partly idle grid (measured).
-  if (tiles * 2 < num_cus) {
+  if (tiles * 2 < num_cus || (M <= 64 && tiles < 2L * num_cus)) {
     while (tiles * sp * 2 <= 2L * num_cus && kt / (sp * 2) >= 8) sp *= 2;
   } else if (tiles < num_cus && kt >= 192) {
     sp = 2;
@@ -99,7 +110,14 @@ static GemmPlan runnable_plan(int op, EpiKind kind, GemmPlan p) {
     if (p.bm != 128) p.sb = 0;
     return p;
   }
-  if (p.bn == 64 && (p.bm == 96 || p.bm == 64) && !wide_epi) return p;
+  if (p.bn == 64 && (p.bm == 96 || p.bm == 64)) {
+    if (!wide_epi) return p;
+    // whole-head / statistics epilogues: the same rows on 128-wide tiles, same K
+    // split (17 x 6144 x 4096 with the q/k/v epilogue: split 4 19.4 us, split 8 21.2)
+    p.bn = 128;
+    if (p.bm == 96) p.bm = 128;
+    return p;
+  }
   p.bm = p.bn = 128;
   p.sb = 0;
   return p;

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(64) void row_finalize_kernel(int n_tiles, const flo
 }
 
 // ---------------------------------------------------------------------------
-// Inverse-CDF draft sampling [P2 §2.2 "采样时按分布抽取"]: the smallest id c
+// Inverse-CDF draft sampling [P2 §2.2]: the smallest id c
 // with sum_{id<=c} exp(z_id/T - M) > u * S, with u = Philox(seed; j+1, slot,
 // step, 0).  The sum runs over the LM-head tile sums (ascending tiles), then
 // inside the selected tile (ascending ids).
