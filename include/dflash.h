@@ -345,7 +345,7 @@ int dflash_verify_subset(dflash_handle* h, void* stream, int32_t n_req, int32_t 
                          const float* target_logits, float temperature, uint64_t seed, uint64_t step,
                          int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor);
 
-/* Verifier walk down a draft tree [P5 §3.5 "验证流程(Verifier Walk)"] (one
+/* Verifier walk down a draft tree [P5 §3.5] (one
  * tree per request, as dflash_draft_block builds it: node 0 = root / anchor,
  * siblings carrying distinct tokens).  From the root, the target's own decoding rule picks the
  * next token from target_logits row u (the target's distribution after the

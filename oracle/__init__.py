@@ -8,8 +8,7 @@ it; the two meet only in the seeded input generators of ``synth/``.
 What it computes, and which passage each part follows:
 
   [P1] "LLM的推理加速-DFlash" (wnma3mz.github.io blog)
-       sections "关键创新：多层特征注入到每层 Attention 的 K/V 上下文" (Steps 1-3),
-       "核心推理伪代码", "验证：沿用投机解码的左到右验证".
+       sections headed "关键创新" (Steps 1-3), "核心推理伪代码" and "验证".
   [P2] "一次前向，白赚 4 个 token：DFlash 2 块扩散投机解码技术详解" (forceinjection.github.io)
        §2.1 (anchor + masks), §2.2 (shared embedding x input_embedding_scale,
        fc + RMSNorm over concatenated target layers, per-position logits),

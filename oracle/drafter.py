@@ -23,7 +23,7 @@ theta^(-2i/d); attention scale 1/sqrt(d); q head h uses kv head h // (n_q/n_kv);
 a final RMSNorm precedes the LM head; the fused feature g is shared by all
 layers (one RMSNorm after fc, no per-layer norm on g).
 
-DFlash 2 dynamic convolution [P2 §3.2.3 "设计：双抽头动态深度卷积"], when the
+DFlash 2 dynamic convolution [P2 §3.2.3], when the
 layer carries conv weights: a two-tap depthwise convolution over the block's
 rows, y_t = k_{t,0} * x_t + k_{t,1} * x_{t-1}, where each tap's kernel is a
 learned per-channel base plus a correction projected linearly from x_t and
@@ -42,7 +42,7 @@ projection has no bias, its output rows [0, H/G) correct tap 0 and rows
 [H/G, 2H/G) tap 1, channel c using group c // G; context rows are untouched
 (their K/V come from the fused target feature).
 
-Variants [P2 §2.2 "注意力" / "输出端"; P4 §5.2]: a causal-in-block flag (block
+Variants [P2 §2.2; P4 §5.2]: a causal-in-block flag (block
 row i attends to the context and to block rows j <= i; the pages disagree on the
 block-internal mask, non-causal is the default); the logits' output multiplier
 and softcap z -> c * tanh(z / c) applied in that order; a mask-embedding

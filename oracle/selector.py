@@ -1,6 +1,6 @@
 """DFlash 2 path selector (oracle side, fp64).  Test infrastructure only.
 
-[P2 §3.1.2 "打分公式：候选间的低秩双线性注意力", §3.1.3 "完全并行：先打分，后游走"]:
+[P2 §3.1.2, §3.1.3]:
 each mask position t keeps the drafter's top-C candidates (C = 16 in the pages);
 a candidate b following predecessor a scores
 

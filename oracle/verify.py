@@ -20,7 +20,7 @@ pages say "exhausted or underflowed" without a threshold); draws are
 inverse-CDF in ascending id order with Philox uniforms (purpose 1 for accept
 tests at position i, purpose 2 for the final draw at position i* or K+1).
 
-Draft-tree verifier walk [P5 §3.5 "验证流程(Verifier Walk)"]: starting at the
+Draft-tree verifier walk [P5 §3.5]: starting at the
 root of a draft tree (the bonus / anchor token, node 0), the target's own
 decoding rule picks the next token from the target's distribution at the
 current node; if one of the node's children carries that token the walk moves
