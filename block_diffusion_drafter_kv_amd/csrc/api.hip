@@ -64,7 +64,7 @@ struct dflash_handle {
   int n_rope = 0;
   // draft scratch
   int maxM = 0, Rpad = 0, QRpad = 0, attn_splits = 1, attn_wg = 0, piece_cap = 0, qrt_max = 5;
-  bool attn_waves = false;     // 16-bit K/V: one wave per work-group, attn_wg = 4 per CU
+  bool attn_waves = false;     // 16-bit K/V: ring work-groups, attn_wg = attn_waves_wg_per_cu() per CU
   float* X = nullptr;
   void *hbuf = nullptr, *attn_out = nullptr, *act = nullptr, *qb = nullptr, *kb = nullptr, *vb = nullptr;
   float *o_part = nullptr, *m_part = nullptr, *l_part = nullptr;
@@ -449,12 +449,12 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
   h->Rpad = ((R + 31) / 32) * 32;
   h->QRpad = ((g * R + 15) / 16) * 16 + 80;
   h->ctx_alloc = ((int64_t)(c.max_ctx + 63) / 64) * 64 + 64;
-  // attention work-groups: for 16-bit K/V one single-wave work-group per SIMD
-  // (equal group ranges, one partial record per (wave, segment) piece); for
-  // fp32 two LDS-ring work-groups per CU with at most kAttnChunkMax partial
-  // records (chunks) per segment
+  // attention work-groups: for 16-bit K/V as many ring work-groups as fit the CUs
+  // at once (equal group ranges, one partial record per (work-group, segment)
+  // piece); for fp32 two LDS-ring work-groups per CU with at most kAttnChunkMax
+  // partial records (chunks) per segment
   h->attn_waves = c.dtype == DFLASH_BF16;
-  h->attn_wg = (h->attn_waves ? 4 : 2) * h->num_cus;
+  h->attn_wg = (h->attn_waves ? attn_waves_wg_per_cu() : 2) * h->num_cus;
   h->piece_cap = h->attn_waves ? h->attn_wg + c.max_batch * nkv * splits : c.max_batch * nkv * splits * kAttnChunkMax;
   h->op = c.dtype == DFLASH_BF16 ? OP_F16 : OP_F32;
   h->op_fc = c.dtype == DFLASH_BF16 ? OP_BF16 : OP_F32;
@@ -993,7 +993,7 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
       {
         Phase ph(h, s, DFLASH_PH_ATTN);
         if (h->attn_waves) launch_attn_waves(d, qrt, a, h->attn_wg, s);
-        else launch_attn(dt, d, qrt, a, h->attn_wg, s);
+        else launch_attn(d, qrt, a, h->attn_wg, s);
       }
       AttnCombineArgs cb;
       cb.o_part = h->o_part;

@@ -448,287 +448,55 @@ void attn_kernel(const AttnArgs a) {
   }
 }
 
-// Streamed attention, producer / consumer.  Work-group w takes the group range
-// wg_range[w] of the plan.  The last NP waves only copy: between them they keep
-// S-1 groups of K/V in flight into the LDS ring, so that the issue of the copies
-// (about 10 bytes per clock per wave at most on gfx950, and stalling while the
-// memory system is saturated) overlaps the arithmetic.  The NW-NP other waves
-// split the segment's QRT query tiles (wave v: tiles [v*TW, min(QRT, (v+1)*TW)),
-// TW = ceil(QRT/(NW-NP))); a consumer keeps
-// the group's K and V fragments in registers across its tiles and its tiles' Q
-// fragments in registers across the whole segment.  One barrier per group
-// publishes the group and frees the ring stage of the previous one.  Per group and tile: S^T (32 x 16) = K Q^T, P = exp2(scale*s
-// - m) with the lazy integer reference m (as in attn_kernel), O^T += V^T P^T.
-template <typename T, int D, int QRT, int NW, int NP, int S, bool PAGED>
-__global__ __launch_bounds__(NW * 64) void attn_pc_kernel(const AttnArgs a) {
+// Streamed attention for 16-bit K/V: NWV waves per work-group share one LDS ring.
+// The groups of all segments, laid end to end, are cut into equal ranges of
+// a.plan->per_wg groups, one per work-group (no snapping: a range may start or
+// end inside a segment).  The work-group streams its range through a ring of S
+// LDS stages, S - 1 groups ahead: each group (K block then V block; the cache's
+// 32-key blocks are stored in MFMA operand order, so each fragment is one
+// coalesced 1 KB wave copy) is copied global -> LDS with 16-byte direct copies,
+// each wave copying its share of the fragments.  Per group: every wave waits
+// for its own copies, then one barrier publishes the group and retires the
+// stage the next copies overwrite.  The segment's query tiles are divided among
+// the waves (Q fragments and O accumulators in registers), so each wave holds
+// at most ceil(QRT / NWV) tiles and two waves fit on a SIMD.  Each (work-group,
+// segment) piece of work ends in one partial record (unnormalised O,
+// reference max, sum) at index w + s, which is unique: a work-group meets
+// consecutive segments and a segment consecutive work-groups.  The combine
+// merges a segment's records in work-group order.
+//
+// Per group and tile: S^T (32 x 16) = K Q^T (MFMA), P = exp2(scale*s - m)
+// rounded to the operand type, O^T += V^T P^T, with l the sum of the unrounded
+// P.  The reference m is an integer in the exp2 domain and moves lazily: only
+// when a scaled score passes it by more than 8 is it raised (to the ceiling of
+// the row max) and O, l rescaled by an exact power of two, so P <= 2^8 and the
+// rounding of P to the operand type does not depend on where the reference
+// sits (a power-of-two shift leaves the significand alone).  Keys past a
+// segment's end are masked out of the scores and their values zeroed (stale
+// cache contents must not turn 0 * x into NaN).
+template <typename T, int D, int QRT, int NWV, int S, bool PAGED>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV, NWV))) void attn_wave_kernel(
+    const AttnArgs a) {
   constexpr int KS = D / 32, DT = D / 16, ROWS = QRT * 16;
-  constexpr int NC = NW - NP;                              // consumer waves
-  constexpr int TW = (QRT + NC - 1) / NC;
-  constexpr int BLK = KV_BLOCK * D;                        // elements of a K (or V) block
-  constexpr int EPC = 16 / (int)sizeof(T);                 // elements per 16-byte copy
-  constexpr int IPG = 2 * BLK / (64 * EPC);                // 1 KB wave copies per group (K, then V)
-  constexpr int PER = IPG / NP;                            // copies per producer wave per group
-  constexpr int VOFF = IPG / 2 * 64;                       // first uint4 of the V block in a stage
-  constexpr int MAXA = (S - 1) * PER < 64 ? S - 1 : 63 / PER;
+  constexpr int NF = 2 * KS + DT;                          // 1 KB fragments per group (K then V)
+  constexpr int CPW = NF / NWV;                            // copies per wave per group
+  constexpr int QA = (QRT + NWV - 1) / NWV;                // tiles per wave (the last wave may hold fewer)
   constexpr float TAU = 8.f;
-  static_assert(sizeof(T) == 2 && NW > NP && IPG % NP == 0 && S >= 2 && S <= 9, "shape");
+  static_assert(sizeof(T) == 2, "16-bit K/V");
+  static_assert(NF % NWV == 0 && (S - 2) * CPW < 64 && S >= 2, "ring");
   typedef typename Frag<T>::type FragT;
-  __shared__ uint4 ring[S][IPG * 64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4, r16 = lane & 15;
-  const bool producer = wave >= NC;
-  const int t0 = wave * TW, nt = producer ? 0 : min(TW, QRT - t0);
-  const int4 rg = a.wg_range[blockIdx.x];
-  const int g0 = rg.x, g1 = rg.y;
-  if (g0 >= g1) return;
-
-  struct Seg {
-    const T* kc; const T* vc; const T* kb; const T* vb;
-    int start, len, ncache, C, cg, slot, kv;
-    int64_t q0;
-  };
-  auto decode = [&](int s, Seg& d) {
-    const int per_req = a.n_kv * a.splits;
-    const int r = s / per_req, rem = s - r * per_req, kv = rem / a.splits, z = rem - kv * a.splits;
-    const int4 sd = a.seg_desc[s];
-    const int slot = sd.x;
-    d.C = sd.y;
-    d.ncache = (d.C + KV_BLOCK - 1) / KV_BLOCK;
-    d.start = sd.z;
-    d.len = sd.w;
-    d.cg = attn_chunk_groups(d.len, a.chunk_min, a.chunk_max);
-    d.slot = slot;
-    d.kv = kv;
-    const int64_t head = (int64_t)slot * a.n_kv + kv;
-    d.kc = (const T*)a.cache_k + head * a.ctx_alloc * D;
-    d.vc = (const T*)a.cache_v + head * a.ctx_alloc * D;
-    const int64_t bh = (int64_t)r * a.n_kv + kv;
-    d.kb = (const T*)a.kb + bh * a.Rpad * D;
-    d.vb = (const T*)a.vb + bh * a.Rpad * D;
-    d.q0 = bh * a.QRpad + (int64_t)z * a.rows_per_split;
-  };
-
-  // ---- copy cursor (producer)
-  const int s0 = rg.z;
-  Seg is;
-  decode(s0, is);
-  int is_s = s0, is_l = g0 - is.start, issued = g0, is_stage = 0;
-  PageCursor pcur;
-  page_cursor_reset(pcur);
-  auto issue = [&]() {
-    const bool in_cache = is_l < is.ncache;
-    const T* kp = is.kb;
-    const T* vp = is.vb;
-    if (in_cache) ctx_group_ptrs<T, D, PAGED>(a, pcur, is.kc, is.vc, is.slot, is.kv, is_l, is.ncache, &kp, &vp);
-    kp += lane * EPC;
-    vp += lane * EPC;
-#pragma unroll
-    for (int c = 0; c < PER; ++c) {
-      const int i = (wave - NC) * PER + c;
-      const T* src = i < IPG / 2 ? kp + i * 64 * EPC : vp + (i - IPG / 2) * 64 * EPC;
-      copy16_to_lds(src, &ring[is_stage][i * 64]);
-    }
-    ++issued;
-    if (++is_stage == S) is_stage = 0;
-    if (++is_l == is.len && issued < g1) {
-      ++is_s;
-      decode(is_s, is);
-      is_l = 0;
-      page_cursor_reset(pcur);
-    }
-  };
-
-  // ---- compute cursor
-  Seg cs = is;
-  int cs_s = s0, cl = g0 - cs.start;
-  FragT qf[TW][KS];
-  auto load_q = [&]() {
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      const int row = (t0 + t) * 16 + r16;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (t < nt && row < a.rows_per_split)
-          *(uint4*)&qf[t][s] = *(const uint4*)((const T*)a.qb + (cs.q0 + row) * D + s * 32 + grp * 8);
-        else
-          *(uint4*)&qf[t][s] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  load_q();
-
-  f32x4 acc[TW][DT];
-  float m_ref[TW], l_sum[TW];
-  const float c = a.scale_log2;
-  auto reset = [&]() {
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m_ref[t] = -INFINITY;
-      l_sum[t] = 0.f;
-    }
-  };
-  reset();
-
-  auto compute = [&](int stage) {
-    const uint4* st = ring[stage];
-    const int nval = cl < cs.ncache ? min(KV_BLOCK, cs.C - KV_BLOCK * cl) : a.R;
-    FragT kf[2 * KS], vf[DT];
-#pragma unroll
-    for (int f = 0; f < 2 * KS; ++f) *(uint4*)&kf[f] = st[f * 64 + lane];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *(uint4*)&vf[dt] = st[VOFF + dt * 64 + lane];
-    if (nval < KV_BLOCK) {   // stale cache contents past the end must not turn 0 * x into NaN
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (grp * 8 + e >= nval) vf[dt][e] = (T)0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (t >= nt) break;
-      f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        Frag<T>::mma(sc0, kf[s], qf[t][s]);
-        Frag<T>::mma(sc1, kf[KS + s], qf[t][s]);
-      }
-      // lane holds keys 8*grp + i (sc0) and 8*grp + 4 + i (sc1), query row r16 of the tile
-      if (nval < KV_BLOCK) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (8 * grp + i >= nval) sc0[i] = -INFINITY;
-          if (8 * grp + 4 + i >= nval) sc1[i] = -INFINITY;
-        }
-      }
-      if (a.causal && cl >= cs.ncache) {   // the block's own keys: key j visible to block rows >= j
-        const int jrow = ((t0 + t) * 16 + r16) % a.R;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (8 * grp + i > jrow) sc0[i] = -INFINITY;
-          if (8 * grp + 4 + i > jrow) sc1[i] = -INFINITY;
-        }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(sc0[i], sc1[i]));
-      mx *= c;
-      if (__any(mx > m_ref[t] + TAU)) {
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m_ref[t], ceilf(mx));
-        const float alpha = mnew > m_ref[t] ? __builtin_amdgcn_exp2f(m_ref[t] - mnew) : 1.f;   // a power of two
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[t][dt] *= alpha;
-        l_sum[t] *= alpha;
-        m_ref[t] = mnew;
-      }
-      FragT pf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc0[i], c, -m_ref[t]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc1[i], c, -m_ref[t]));
-        l_sum[t] += p0 + p1;
-        pf[i] = (T)p0;
-        pf[4 + i] = (T)p1;
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) Frag<T>::mma(acc[t][dt], vf[dt], pf);
-    }
-  };
-
-  auto flush = [&](int ck) {
-    const int64_t piece = a.chunk_base[cs_s] + ck;
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (t >= nt) break;
-      float l = l_sum[t];
-      l += __shfl_xor(l, 16, 64);
-      l += __shfl_xor(l, 32, 64);
-      const int row = (t0 + t) * 16 + r16;
-      if (row < a.rows_per_split) {
-        float* op = a.o_part + (piece * ROWS + row) * D + 4 * grp;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + dt * 16) = acc[t][dt];
-        if (grp == 0) {
-          a.m_part[piece * ROWS + row] = m_ref[t];
-          a.l_part[piece * ROWS + row] = l;
-        }
-      }
-    }
-  };
-
-  if (producer) {
-    while (issued < min(g1, g0 + S - 1)) issue();
-    for (int gi = g0; gi < g1; ++gi) {
-      wait_groups<PER, MAXA>(issued - (gi + 1));   // group gi has landed
-      lds_barrier();                                // publish it; stage (gi-1) % S is free
-      if (issued < g1) issue();                     // group gi + S - 1 into that stage
-    }
-    return;
-  }
-  int stage = 0;                                   // ring stage of group gi
-  int ck = cl / cs.cg;
-  int cend = min(cs.len, (ck + 1) * cs.cg);
-  for (int gi = g0; gi < g1; ++gi) {
-    lds_barrier();
-    compute(stage);
-    if (++stage == S) stage = 0;
-    ++cl;
-    if (cl == cend) {   // ranges end on chunk starts, so a chunk never straddles work-groups
-      flush(ck);
-      reset();
-      ++ck;
-      cend = min(cs.len, cend + cs.cg);
-    }
-    if (cl == cs.len && gi + 1 < g1) {
-      ++cs_s;
-      decode(cs_s, cs);
-      cl = 0;
-      ck = 0;
-      cend = min(cs.len, cs.cg);
-      load_q();
-    }
-  }
-}
-
-// Streamed attention, one wave per work-group, no LDS and no barrier (16-bit K/V).
-// The groups of all segments, laid end to end, are cut into equal ranges of
-// a.plan->per_wg groups, one per wave (no snapping: a range may start or end
-// inside a segment).  A wave streams its range straight into registers -- the
-// cache's 32-key blocks are stored in MFMA operand order, so each fragment is
-// one coalesced 1 KB wave load -- with the next group's 16 loads in flight
-// while the current group is computed, and holds every query tile of the
-// segment (Q fragments and O accumulators) itself.  Each (wave, segment) piece
-// of work ends in one partial record (unnormalised O, reference max, sum) at
-// index w + s, which is unique: a wave meets consecutive segments and a segment
-// consecutive waves.  The combine merges a segment's records in wave order.
-// Per group and tile: S^T (32 x 16) = K Q^T, P = exp2(scale*s - m) with the lazy
-// integer reference m, O^T += V^T P^T, exactly as in attn_pc_kernel.
-//
-// Why not an LDS ring shared by query-tile waves: measured on this path's
-// access pattern, copies into LDS published by a work-group barrier per 16 KB
-// group stream at about 2.8 TB/s whatever the ring depth or copy-wave count,
-// while independent waves loading into registers stream at about 5.9 TB/s.
-template <typename T, int D, int QRT, bool PAGED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_wave_kernel(const AttnArgs a) {
-  constexpr int KS = D / 32, DT = D / 16, ROWS = QRT * 16;
-  constexpr int BLK = KV_BLOCK * D;                        // elements of a K (or V) block
-  constexpr int NF = 2 * KS + DT;                          // 16-byte loads per lane per group (K then V)
-  constexpr float TAU = 8.f;
-  static_assert(sizeof(T) == 2, "16-bit K/V");
-  typedef typename Frag<T>::type FragT;
-
-  const int lane = threadIdx.x;
-  const int grp = lane >> 4, r16 = lane & 15;
+  const int t0 = wave * QA;                                // first tile of this wave
   const int w = blockIdx.x;
   const int4 rg = a.wg_range[w];
   const int g0 = rg.x, g1 = rg.y;
   if (g0 >= g1) return;
+
+  __shared__ uint4 ring[S][NF * 64];
+  const uint32_t ring_lds = lds_addr(&ring[0][0]);
 
   struct Seg {
     const T* kc; const T* vc; const T* kb; const T* vb;
@@ -754,21 +522,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     d.q0 = bh * a.QRpad + (int64_t)z * a.rows_per_split;
   };
 
-  // ---- load cursor: the group after the one being computed
+  // ---- copy cursor: the next group to copy into the ring (stage = its index in the range mod S)
   int ls_s = rg.z;
   Seg ls;
   decode(ls_s, ls);
   int ls_l = g0 - ls.start;
+  int ls_stage = 0;
   PageCursor pcur;
   page_cursor_reset(pcur);
-  auto issue = [&](FragT (&kv_next)[NF]) {
+  auto issue = [&]() {
     const T* kp = ls.kb;
     const T* vp = ls.vb;
     if (ls_l < ls.ncache) ctx_group_ptrs<T, D, PAGED>(a, pcur, ls.kc, ls.vc, ls.slot, ls.kv, ls_l, ls.ncache, &kp, &vp);
 #pragma unroll
-    for (int f = 0; f < 2 * KS; ++f) *(uint4*)&kv_next[f] = *(const uint4*)(kp + (f * 64 + lane) * 8);
-#pragma unroll
-    for (int f = 0; f < DT; ++f) *(uint4*)&kv_next[2 * KS + f] = *(const uint4*)(vp + (f * 64 + lane) * 8);
+    for (int c = 0; c < CPW; ++c) {
+      const int f = wave * CPW + c;
+      const T* src = f < 2 * KS ? kp + (f * 64 + lane) * 8 : vp + ((f - 2 * KS) * 64 + lane) * 8;
+      copy16_to_lds_at(src, ring_lds + (uint32_t)(ls_stage * NF + f) * 1024u);
+    }
+    if (++ls_stage == S) ls_stage = 0;
     if (++ls_l == ls.len) {   // the next segment (decoded even when the range ends here: its descriptor exists)
       if (ls_s + 1 < a.n_seg) {
         ++ls_s;
@@ -779,137 +551,186 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
   };
 
-  // ---- compute cursor; the segment's Q fragments sit in this wave's own LDS (read
-  // per tile and group: registers go to the O accumulators and the K/V double buffer)
+  // ---- compute: this wave's NT tiles (Q fragments and O accumulators in registers)
+  auto run = [&](auto ntc) {
+  constexpr int NT = decltype(ntc)::value;
   int cs_s = rg.z;
   Seg cs;
   decode(cs_s, cs);
   int cl = g0 - cs.start;
-  __shared__ uint4 qs[QRT * KS * 64];
+  FragT qf[NT][KS];
   auto load_q = [&]() {
 #pragma unroll
-    for (int t = 0; t < QRT; ++t) {
-      const int row = t * 16 + r16;
+    for (int i = 0; i < NT; ++i) {
+      const int row = (t0 + i) * 16 + r16;
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        qs[(t * KS + s) * 64 + lane] = row < a.rows_per_split
-            ? *(const uint4*)((const T*)a.qb + (cs.q0 + row) * D + s * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
+      for (int s = 0; s < KS; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < a.rows_per_split) v = *(const uint4*)((const T*)a.qb + (cs.q0 + row) * D + s * 32 + grp * 8);
+        *(uint4*)&qf[i][s] = v;
+      }
     }
   };
   load_q();
 
-  f32x4 acc[QRT][DT];
-  float m_ref[QRT], l_sum[QRT];
+  f32x4 acc[NT][DT];
+  float m_ref[NT], l_sum[NT];
   const float c = a.scale_log2;
   auto reset = [&]() {
 #pragma unroll
-    for (int t = 0; t < QRT; ++t) {
+    for (int i = 0; i < NT; ++i) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m_ref[t] = -INFINITY;
-      l_sum[t] = 0.f;
+      for (int dt = 0; dt < DT; ++dt) acc[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_ref[i] = -INFINITY;
+      l_sum[i] = 0.f;
     }
   };
   reset();
 
-  // three phases over all tiles, so that each phase's MFMAs and VALU work are
-  // independent across tiles (one wave per SIMD: no other wave hides latency);
-  // kv holds the group's K fragments, then its V fragments
-  auto compute = [&](FragT (&kv)[NF]) {
-    FragT* kf = kv;
-    FragT* vf = kv + 2 * KS;
+  // one group from ring stage st; three phases over this wave's tiles, so that
+  // each phase's MFMAs and VALU work are independent across tiles
+  // masked: a group with keys past the segment's end or the block's own keys
+  auto compute = [&](bool masked, int st) {
     const int nval = cl < cs.ncache ? min(KV_BLOCK, cs.C - KV_BLOCK * cl) : a.R;
-    if (nval < KV_BLOCK) {   // stale cache contents past the end must not turn 0 * x into NaN
+    // S^T = K Q^T; lane holds keys 8*grp + i (sc[i][0]) and 8*grp + 4 + i (sc[i][1])
+    f32x4 sc[NT][2];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int i = 0; i < NT; ++i) sc[i][0] = sc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K fragments in two halves of the head dim, each read at once (one LDS latency per half)
+    constexpr int KH = KS / 2;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (grp * 8 + e >= nval) vf[dt][e] = (T)0.f;
-    }
-    // S^T = K Q^T for every tile; lane holds keys 8*grp + i (sc[t][0]) and 8*grp + 4 + i (sc[t][1])
-    f32x4 sc[QRT][2];
+    for (int h = 0; h < 2; ++h) {
+      FragT kf[2 * KH];
 #pragma unroll
-    for (int t = 0; t < QRT; ++t) sc[t][0] = sc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int t = 0; t < QRT; ++t) {
-        FragT qf;
-        *(uint4*)&qf = qs[(t * KS + s) * 64 + lane];
-        Frag<T>::mma(sc[t][0], kf[s], qf);
-        Frag<T>::mma(sc[t][1], kf[KS + s], qf);
+      for (int s = 0; s < KH; ++s) {
+        *(uint4*)&kf[s] = ring[st][(h * KH + s) * 64 + lane];
+        *(uint4*)&kf[KH + s] = ring[st][(KS + h * KH + s) * 64 + lane];
       }
-    }
-    // masks, lazy reference, probabilities
-    FragT pf[QRT];
 #pragma unroll
-    for (int t = 0; t < QRT; ++t) {
-      if (nval < KV_BLOCK) {
+      for (int s = 0; s < KH; ++s) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (8 * grp + i >= nval) sc[t][0][i] = -INFINITY;
-          if (8 * grp + 4 + i >= nval) sc[t][1][i] = -INFINITY;
+        for (int i = 0; i < NT; ++i) {
+          Frag<T>::mma(sc[i][0], kf[s], qf[i][h * KH + s]);
+          Frag<T>::mma(sc[i][1], kf[KH + s], qf[i][h * KH + s]);
         }
       }
-      if (a.causal && cl >= cs.ncache) {   // the block's own keys: key j visible to block rows >= j
-        const int jrow = (t * 16 + r16) % a.R;
+    }
+    // the first half of the V fragments is read before the softmax, whose work
+    // hides the latency; the second half when the products start
+    constexpr int VH = DT / 2;
+    FragT vf[DT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (8 * grp + i > jrow) sc[t][0][i] = -INFINITY;
-          if (8 * grp + 4 + i > jrow) sc[t][1][i] = -INFINITY;
+    for (int dt = 0; dt < VH; ++dt) *(uint4*)&vf[dt] = ring[st][(2 * KS + dt) * 64 + lane];
+    // masks, lazy reference, probabilities
+    FragT pf[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int t = t0 + i;
+      if (masked) {
+        // keys below lim are visible: the valid keys, and for the block's own
+        // keys under the causal mask key j only to block rows >= j
+        int lim = nval;
+        if (a.causal && cl >= cs.ncache) lim = min(lim, (t * 16 + r16) % a.R + 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (8 * grp + j >= lim) sc[i][0][j] = -INFINITY;
+          if (8 * grp + 4 + j >= lim) sc[i][1][j] = -INFINITY;
         }
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(sc[t][0][i], sc[t][1][i]));
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaxf(sc[i][0][j], sc[i][1][j]));
       mx *= c;
-      if (__any(mx > m_ref[t] + TAU)) {
+      if (__any(mx > m_ref[i] + TAU)) {
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m_ref[t], ceilf(mx));
-        const float alpha = mnew > m_ref[t] ? __builtin_amdgcn_exp2f(m_ref[t] - mnew) : 1.f;   // a power of two
+        const float mnew = fmaxf(m_ref[i], ceilf(mx));
+        const float alpha = mnew > m_ref[i] ? __builtin_amdgcn_exp2f(m_ref[i] - mnew) : 1.f;   // a power of two
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[t][dt] *= alpha;
-        l_sum[t] *= alpha;
-        m_ref[t] = mnew;
+        for (int dt = 0; dt < DT; ++dt) acc[i][dt] *= alpha;
+        l_sum[i] *= alpha;
+        m_ref[i] = mnew;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[t][0][i], c, -m_ref[t]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[t][1][i], c, -m_ref[t]));
-        l_sum[t] += p0 + p1;
-        pf[t][i] = (T)p0;
-        pf[t][4 + i] = (T)p1;
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i][0][j], c, -m_ref[i]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i][1][j], c, -m_ref[i]));
+        l_sum[i] += p0 + p1;
+        pf[i][j] = (T)p0;
+        pf[i][4 + j] = (T)p1;
       }
     }
-    // O^T += V^T P^T for every tile
+    // O^T += V^T P^T; values of keys past the end are zeroed (stale cache contents
+    // must not turn 0 * x into NaN): the halves of this lane's eight keys that
+    // hold valid values (all of them in a full group)
+    const int nv = nval - grp * 8;
+    uint32_t mk[4];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int j = 0; j < 4; ++j) mk[j] = (2 * j < nv ? 0xFFFFu : 0u) | (2 * j + 1 < nv ? 0xFFFF0000u : 0u);
 #pragma unroll
-      for (int t = 0; t < QRT; ++t) Frag<T>::mma(acc[t][dt], vf[dt], pf[t]);
+    for (int dt = VH; dt < DT; ++dt) *(uint4*)&vf[dt] = ring[st][(2 * KS + dt) * 64 + lane];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ((uint32_t*)&vf[dt])[j] &= mk[j];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) Frag<T>::mma(acc[i][dt], vf[dt], pf[i]);
+    }
   };
 
   auto flush = [&]() {
     const int64_t piece = (int64_t)w + cs_s;
 #pragma unroll
-    for (int t = 0; t < QRT; ++t) {
-      float l = l_sum[t];
+    for (int i = 0; i < NT; ++i) {
+      float l = l_sum[i];
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
-      const int row = t * 16 + r16;
+      const int row = (t0 + i) * 16 + r16;
       if (row < a.rows_per_split) {
         float* op = a.o_part + (piece * ROWS + row) * D + 4 * grp;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + dt * 16) = acc[t][dt];
+        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + dt * 16) = acc[i][dt];
         if (grp == 0) {
-          a.m_part[piece * ROWS + row] = m_ref[t];
+          a.m_part[piece * ROWS + row] = m_ref[i];
           a.l_part[piece * ROWS + row] = l;
         }
       }
     }
   };
 
-  auto advance = [&](int gi) {   // bookkeeping after group gi: record at a segment or range end
+  // Ring discipline.  Group k of the range lives in stage k mod S.  Only the
+  // ring's copies and, at a segment change, the record stores and Q loads use
+  // the vector-memory counter; loads complete in issue order, so "at most n
+  // operations outstanding" with n the copies of the groups issued after group
+  // k means this wave's copies of group k have landed (extra operations after
+  // them only make the wait stricter).  The barrier then makes every wave's
+  // copies visible, and (each wave having drained its LDS reads first) frees
+  // the stage of group k - 1 for group k + S - 1.
+  int issued = g0;
+  for (; issued < g1 && issued < g0 + S - 1; ++issued) issue();
+  int stage = 0;
+  for (int gi = g0; gi < g1; ++gi) {
+    const int ahead = issued - gi - 1;   // groups issued after this one
+    if constexpr (S >= 4) {
+      if (ahead >= 2) wait_vmcnt<2 * CPW>();
+      else if (ahead == 1) wait_vmcnt<CPW>();
+      else wait_vmcnt<0>();
+    } else if constexpr (S == 3) {
+      if (ahead >= 1) wait_vmcnt<CPW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    wait_lgkmcnt0();
+    lds_barrier();
+    if (issued < g1) {
+      issue();
+      ++issued;
+    }
+    // the cache part's last group may be partial; the block's own group is masked when causal or partial
+    const bool full = cl < cs.ncache ? cs.C - KV_BLOCK * cl >= KV_BLOCK : (a.R >= KV_BLOCK && !a.causal);
+    compute(!full, stage);
+    if (++stage == S) stage = 0;
     ++cl;
     const bool seg_end = cl == cs.len;
     if (seg_end || gi + 1 == g1) {
@@ -922,16 +743,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         load_q();
       }
     }
+  }
   };
-  // group gi + 1 loads into kv_next while group gi is computed from its copy
-  FragT kv_next[NF], kv[NF];
-  issue(kv_next);
-  for (int gi = g0; gi < g1; ++gi) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f) kv[f] = kv_next[f];
-    if (gi + 1 < g1) issue(kv_next);
-    compute(kv);
-    advance(gi);
+  // every wave runs the same group sequence and barriers; only the tile count differs
+  if constexpr (QRT - (NWV - 1) * QA == QA) {
+    run(std::integral_constant<int, QA>{});
+  } else {
+    if (wave == NWV - 1) run(std::integral_constant<int, QRT - (NWV - 1) * QA>{});
+    else run(std::integral_constant<int, QA>{});
   }
 }
 
@@ -1021,28 +840,22 @@ static void launch_attn_t(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
   }
 }
 
-// 16-bit K/V: one consumer wave per query tile and four producer waves, an
-// 8-stage ring (128 KB at d = 128), one work-group per CU.
-template <int D, bool PG>
-static void launch_attn_pc(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
-  constexpr int NP = 4, S = 8;
-  switch (qrt) {
-    case 1: attn_pc_kernel<f16_t, D, 1, 1 + NP, NP, S, PG><<<grid, 64 * (1 + NP), 0, s>>>(a); break;
-    case 2: attn_pc_kernel<f16_t, D, 2, 2 + NP, NP, S, PG><<<grid, 64 * (2 + NP), 0, s>>>(a); break;
-    case 3: attn_pc_kernel<f16_t, D, 3, 3 + NP, NP, S, PG><<<grid, 64 * (3 + NP), 0, s>>>(a); break;
-    case 4: attn_pc_kernel<f16_t, D, 4, 4 + NP, NP, S, PG><<<grid, 64 * (4 + NP), 0, s>>>(a); break;
-    case 5: attn_pc_kernel<f16_t, D, 5, 5 + NP, NP, S, PG><<<grid, 64 * (5 + NP), 0, s>>>(a); break;
-  }
-}
+// Ring depth of the 16-bit streamed attention and its work-groups per CU: two
+// stages of one 16 KB group (head dim 128) per work-group, four work-groups
+// (128 KB of the CU's 160 KB of LDS; two waves per SIMD, at most 256 registers
+// each).  Measured: a third stage with three work-groups per CU is slower.
+static constexpr int kWaveRing = 2, kWaveWgPerCu = 4;
+int attn_waves_wg_per_cu() { return kWaveWgPerCu; }
 
 template <int D, bool PG>
 static void launch_attn_wave(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
+  constexpr int S = kWaveRing;
   switch (qrt) {
-    case 1: attn_wave_kernel<f16_t, D, 1, PG><<<grid, 64, 0, s>>>(a); break;
-    case 2: attn_wave_kernel<f16_t, D, 2, PG><<<grid, 64, 0, s>>>(a); break;
-    case 3: attn_wave_kernel<f16_t, D, 3, PG><<<grid, 64, 0, s>>>(a); break;
-    case 4: attn_wave_kernel<f16_t, D, 4, PG><<<grid, 64, 0, s>>>(a); break;
-    case 5: attn_wave_kernel<f16_t, D, 5, PG><<<grid, 64, 0, s>>>(a); break;
+    case 1: attn_wave_kernel<f16_t, D, 1, 1, S, PG><<<grid, 64, 0, s>>>(a); break;
+    case 2: attn_wave_kernel<f16_t, D, 2, 2, S, PG><<<grid, 128, 0, s>>>(a); break;
+    case 3: attn_wave_kernel<f16_t, D, 3, 2, S, PG><<<grid, 128, 0, s>>>(a); break;
+    case 4: attn_wave_kernel<f16_t, D, 4, 2, S, PG><<<grid, 128, 0, s>>>(a); break;
+    case 5: attn_wave_kernel<f16_t, D, 5, 2, S, PG><<<grid, 128, 0, s>>>(a); break;
   }
 }
 
@@ -1059,16 +872,12 @@ void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, i
                                       plan, seg_start, chunk_base, seg_desc, wg_range);
 }
 
-void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStream_t s) {
-  // the paged cache has instantiations of its own: its page cursor stays out of the contiguous kernels
+void launch_attn(int D, int qrt, const AttnArgs& a, int grid, hipStream_t s) {
+  // fp32 K/V; the paged cache has instantiations of its own: its page cursor stays
+  // out of the contiguous kernels
   const bool pg = a.page_table != nullptr;
-  if (dtype == DT_BF16) {
-    if (D == 128) pg ? launch_attn_pc<128, true>(a, qrt, grid, s) : launch_attn_pc<128, false>(a, qrt, grid, s);
-    else pg ? launch_attn_pc<64, true>(a, qrt, grid, s) : launch_attn_pc<64, false>(a, qrt, grid, s);
-  } else {
-    if (D == 128) pg ? launch_attn_t<float, 128, true>(a, qrt, grid, s) : launch_attn_t<float, 128, false>(a, qrt, grid, s);
-    else pg ? launch_attn_t<float, 64, true>(a, qrt, grid, s) : launch_attn_t<float, 64, false>(a, qrt, grid, s);
-  }
+  if (D == 128) pg ? launch_attn_t<float, 128, true>(a, qrt, grid, s) : launch_attn_t<float, 128, false>(a, qrt, grid, s);
+  else pg ? launch_attn_t<float, 64, true>(a, qrt, grid, s) : launch_attn_t<float, 64, false>(a, qrt, grid, s);
 }
 
 void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, hipStream_t s) {

@@ -63,6 +63,21 @@ __device__ __forceinline__ void copy16_to_lds_sv_nc(const void* sbase, uint32_t 
       : "s"(lds), "v"(voff), "s"(sbase));
 }
 
+// The same copy to an LDS byte address (wave-uniform) given as an integer: a
+// ring addressed through a run-time stage index would otherwise turn the address
+// into a generic pointer that must be cast back.
+__device__ __forceinline__ uint32_t lds_addr(const void* lds_ptr) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_ptr;
+}
+__device__ __forceinline__ void copy16_to_lds_at(const void* g, uint32_t lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_wave_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(g));
+}
+
 // s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -39,9 +39,13 @@ void launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const
 void launch_attn_plan(const int32_t* slots, const int32_t* ctx_len, int n_req, int n_kv, int splits, int n_wg_max,
                       int min_per_wg, int chunk_min, int chunk_max, AttnPlan* plan, int32_t* seg_start,
                       int32_t* chunk_base, int4* seg_desc, int4* wg_range, hipStream_t s);
-void launch_attn(int dtype, int D, int qrt, const AttnArgs& a, int grid, hipStream_t s);
-// 16-bit K/V: one wave per work-group over equal group ranges (plan built without chunk snapping)
+// fp32 K/V: LDS-ring work-groups over chunk-snapped group ranges
+void launch_attn(int D, int qrt, const AttnArgs& a, int grid, hipStream_t s);
+// 16-bit K/V: work-groups of up to two waves sharing an LDS ring, over equal
+// group ranges (plan built without chunk snapping)
 void launch_attn_waves(int D, int qrt, const AttnArgs& a, int grid, hipStream_t s);
+// work-groups of the 16-bit streamed attention that fit one CU at once (its LDS ring and registers)
+int attn_waves_wg_per_cu();
 void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, hipStream_t s);
 
 // Top-p set of one row over the whole vocabulary (no top-k): the ids in
