@@ -474,22 +474,23 @@ void attn_kernel(const AttnArgs a) {
 // sits (a power-of-two shift leaves the significand alone).  Keys past a
 // segment's end are masked out of the scores and their values zeroed (stale
 // cache contents must not turn 0 * x into NaN).
-template <typename T, int D, int QRT, int NWV, int S, bool PAGED>
-__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV, NWV))) void attn_wave_kernel(
+template <typename T, int D, int QRT, int NWV, int S, int WPE, bool PAGED>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_wave_kernel(
     const AttnArgs a) {
   constexpr int KS = D / 32, DT = D / 16, ROWS = QRT * 16;
   constexpr int NF = 2 * KS + DT;                          // 1 KB fragments per group (K then V)
   constexpr int CPW = NF / NWV;                            // copies per wave per group
-  constexpr int QA = (QRT + NWV - 1) / NWV;                // tiles per wave (the last wave may hold fewer)
+  constexpr int QLO = QRT / NWV, QHI = (QRT + NWV - 1) / NWV;   // tiles per wave: wave v holds [vQRT/NWV, (v+1)QRT/NWV)
   constexpr float TAU = 8.f;
   static_assert(sizeof(T) == 2, "16-bit K/V");
   static_assert(NF % NWV == 0 && (S - 2) * CPW < 64 && S >= 2, "ring");
+  static_assert(QLO >= 1, "every wave holds a tile");
   typedef typename Frag<T>::type FragT;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4, r16 = lane & 15;
-  const int t0 = wave * QA;                                // first tile of this wave
+  const int t0 = wave * QRT / NWV;                         // first tile of this wave
   const int w = blockIdx.x;
   const int4 rg = a.wg_range[w];
   const int g0 = rg.x, g1 = rg.y;
@@ -678,22 +679,30 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV, N
     }
   };
 
-  auto flush = [&]() {
-    const int64_t piece = (int64_t)w + cs_s;
+  // The record of a piece holds O / l, the piece's own normalised output, as
+  // fp16 (|O / l| is at most the largest |value|; one more rounding of the same
+  // size as the output's own), in the accumulators' fragment order, so that every
+  // store is one contiguous 512-byte wave write: tile t, 16-column block dt,
+  // lane, 4 values (row 16t + lane % 16, columns 16dt + 4(lane / 16) + i), all 16
+  // rows of a tile (rows past rows_per_split are never read).  Reference max and
+  // sum per row in fp32.
+  auto flush = [&](int64_t piece) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       float l = l_sum[i];
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
-      const int row = (t0 + i) * 16 + r16;
-      if (row < a.rows_per_split) {
-        float* op = a.o_part + (piece * ROWS + row) * D + 4 * grp;
+      const float il = 1.f / l;
+      h4* op = (h4*)a.o_part + ((piece * QRT + t0 + i) * DT) * 64 + lane;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + dt * 16) = acc[i][dt];
-        if (grp == 0) {
-          a.m_part[piece * ROWS + row] = m_ref[i];
-          a.l_part[piece * ROWS + row] = l;
-        }
+      for (int dt = 0; dt < DT; ++dt)
+        op[dt * 64] = h4{(_Float16)(acc[i][dt][0] * il), (_Float16)(acc[i][dt][1] * il),
+                         (_Float16)(acc[i][dt][2] * il), (_Float16)(acc[i][dt][3] * il)};
+      const int row = (t0 + i) * 16 + r16;
+      if (grp == 0) {
+        a.m_part[piece * ROWS + row] = m_ref[i];
+        a.l_part[piece * ROWS + row] = l;
       }
     }
   };
@@ -734,29 +743,103 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV, N
     ++cl;
     const bool seg_end = cl == cs.len;
     if (seg_end || gi + 1 == g1) {
-      flush();
-      if (seg_end && gi + 1 < g1) {
-        reset();
+      const int64_t piece = (int64_t)w + cs_s;
+      if (seg_end && gi + 1 < g1) {   // the next segment's Q loads go out before the record stores
         ++cs_s;
         decode(cs_s, cs);
         cl = 0;
         load_q();
       }
+      flush(piece);
+      if (seg_end && gi + 1 < g1) reset();
     }
   }
   };
   // every wave runs the same group sequence and barriers; only the tile count differs
-  if constexpr (QRT - (NWV - 1) * QA == QA) {
-    run(std::integral_constant<int, QA>{});
+  if constexpr (QLO == QHI) {
+    run(std::integral_constant<int, QLO>{});
   } else {
-    if (wave == NWV - 1) run(std::integral_constant<int, QRT - (NWV - 1) * QA>{});
-    else run(std::integral_constant<int, QA>{});
+    if ((wave + 1) * QRT / NWV - t0 == QHI) run(std::integral_constant<int, QHI>{});
+    else run(std::integral_constant<int, QLO>{});
+  }
+}
+
+// Combine of the 16-bit path's piece records (fp16 O / l in fragment order, see
+// attn_wave_kernel).  One work-group per (request, kv head and q-row part, 16-row
+// tile): thread x owns the 4-value elements x + 256k of the tile's record (all of
+// one row, lane x % 64), so every record load is one contiguous 2 KB block read;
+// the segment's records are merged in work-group order in one pass (running
+// max, earlier sums rescaled), each weighted by its own sum.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_combine_frag_kernel(const AttnCombineArgs a) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  constexpr int DT = D / 16, EPT = DT * 64 / 256;   // elements per thread
+  const int req = blockIdx.x;
+  const int kv = blockIdx.y / a.splits, z = blockIdx.y % a.splits;
+  const int t = blockIdx.z, lane = threadIdx.x & 63;
+  const int row = t * 16 + (lane & 15);
+  if (row >= a.rows_per_split) return;
+  const int seg = (req * a.n_kv + kv) * a.splits + z;
+  // one record per work-group range the segment meets, at w + seg
+  const int per = a.wave_plan->per_wg;
+  const int w0 = a.seg_start[seg] / per, w1 = (a.seg_start[seg + 1] - 1) / per;
+  const int n = w1 - w0 + 1;
+  const int64_t p0 = (int64_t)w0 + seg;
+  const int QRT = a.QRT16 >> 4;
+  float M = -INFINITY, L = 0.f;
+  float O[EPT][4];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) O[k][0] = O[k][1] = O[k][2] = O[k][3] = 0.f;
+  for (int c0 = 0; c0 < n; c0 += 4) {   // four records' loads issued together
+    float mc[4], lc[4];
+    h4 hc[4][EPT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t b = p0 + min(c0 + u, n - 1);
+      mc[u] = c0 + u < n ? a.m_part[b * a.QRT16 + row] : -INFINITY;
+      lc[u] = a.l_part[b * a.QRT16 + row];
+      const h4* hp = (const h4*)a.o_part + (b * QRT + t) * DT * 64 + threadIdx.x;
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) hc[u][k] = hp[256 * k];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float m = mc[u];
+      if (m == -INFINITY) continue;
+      if (m > M) {
+        const float sc = exp2f(M - m);   // 0 while M is -inf
+        L *= sc;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[k][i] *= sc;
+        M = m;
+      }
+      const float wl = lc[u] * exp2f(m - M);   // the record's sum, at the running reference
+      L += wl;
+#pragma unroll
+      for (int k = 0; k < EPT; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[k][i] += (float)hc[u][k][i] * wl;
+    }
+  }
+  const float inv = 1.0f / L;
+  const int gps = a.group / a.splits;
+  const int gi = row / a.R, j = row % a.R;
+  const int qh = kv * a.group + z * gps + gi;
+  T* dst = (T*)a.out + ((int64_t)req * a.R + j) * a.q_dim + qh * D + 4 * (lane >> 4);
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int dt = (threadIdx.x >> 6) + 4 * k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[dt * 16 + i] = from_f32<T>(O[k][i] * inv);
   }
 }
 
 // One work-group per (request, kv head and q-row part, block of 16 rows): each
 // thread owns one row and D/16 consecutive head dims and merges the segment's
 // chunk records in order in one pass (running max, earlier sums rescaled).
+// fp32 K/V path (row-layout fp32 records of chunks).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs a) {
   constexpr int EPT = D / 16;
@@ -769,12 +852,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnCombineArgs
   const int len = a.seg_start[seg + 1] - a.seg_start[seg];
   int n;
   int64_t p0;
-  if (a.wave_plan) {   // one record per wave range the segment meets, at w + seg
-    const int per = a.wave_plan->per_wg;
-    const int w0 = a.seg_start[seg] / per, w1 = (a.seg_start[seg + 1] - 1) / per;
-    n = w1 - w0 + 1;
-    p0 = (int64_t)w0 + seg;
-  } else {
+  {
     const int cg = attn_chunk_groups(len, a.chunk_min, a.chunk_max);
     n = (len + cg - 1) / cg;
     p0 = a.chunk_base[seg];
@@ -840,22 +918,33 @@ static void launch_attn_t(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
   }
 }
 
-// Ring depth of the 16-bit streamed attention and its work-groups per CU: two
-// stages of one 16 KB group (head dim 128) per work-group, four work-groups
-// (128 KB of the CU's 160 KB of LDS; two waves per SIMD, at most 256 registers
-// each).  Measured: a third stage with three work-groups per CU is slower.
-static constexpr int kWaveRing = 2, kWaveWgPerCu = 4;
+// Shape of the 16-bit streamed attention: waves per work-group, ring stages
+// (one 16 KB group at head dim 128 each) and work-groups per CU.  Two waves,
+// two stages, four work-groups: 128 KB of the CU's 160 KB of LDS, two waves per
+// SIMD (at most 256 registers each).
+#ifndef ATTN_WAVE_SHAPE
+#define ATTN_WAVE_SHAPE 2, 2, 4
+#endif
+static constexpr int kWaveShape[3] = {ATTN_WAVE_SHAPE};
+static constexpr int kWaveNW = kWaveShape[0], kWaveRing = kWaveShape[1], kWaveWgPerCu = kWaveShape[2];
 int attn_waves_wg_per_cu() { return kWaveWgPerCu; }
+
+template <int D, int QRT, bool PG>
+static void launch_attn_wave_q(const AttnArgs& a, int grid, hipStream_t s) {
+  // waves per work-group: a power of two (they share a group's fragments) holding at least a tile each
+  constexpr int NWV = QRT >= kWaveNW ? kWaveNW : QRT >= 2 ? 2 : 1;
+  constexpr int WPE = (NWV * kWaveWgPerCu + 3) / 4;
+  attn_wave_kernel<f16_t, D, QRT, NWV, kWaveRing, WPE, PG><<<grid, NWV * 64, 0, s>>>(a);
+}
 
 template <int D, bool PG>
 static void launch_attn_wave(const AttnArgs& a, int qrt, int grid, hipStream_t s) {
-  constexpr int S = kWaveRing;
   switch (qrt) {
-    case 1: attn_wave_kernel<f16_t, D, 1, 1, S, PG><<<grid, 64, 0, s>>>(a); break;
-    case 2: attn_wave_kernel<f16_t, D, 2, 2, S, PG><<<grid, 128, 0, s>>>(a); break;
-    case 3: attn_wave_kernel<f16_t, D, 3, 2, S, PG><<<grid, 128, 0, s>>>(a); break;
-    case 4: attn_wave_kernel<f16_t, D, 4, 2, S, PG><<<grid, 128, 0, s>>>(a); break;
-    case 5: attn_wave_kernel<f16_t, D, 5, 2, S, PG><<<grid, 128, 0, s>>>(a); break;
+    case 1: launch_attn_wave_q<D, 1, PG>(a, grid, s); break;
+    case 2: launch_attn_wave_q<D, 2, PG>(a, grid, s); break;
+    case 3: launch_attn_wave_q<D, 3, PG>(a, grid, s); break;
+    case 4: launch_attn_wave_q<D, 4, PG>(a, grid, s); break;
+    case 5: launch_attn_wave_q<D, 5, PG>(a, grid, s); break;
   }
 }
 
@@ -881,9 +970,9 @@ void launch_attn(int D, int qrt, const AttnArgs& a, int grid, hipStream_t s) {
 }
 
 void launch_attn_combine(int dtype, int D, const AttnCombineArgs& a, dim3 grid, hipStream_t s) {
-  if (dtype == DT_BF16) {
-    if (D == 128) attn_combine_kernel<f16_t, 128><<<grid, 256, 0, s>>>(a);
-    else attn_combine_kernel<f16_t, 64><<<grid, 256, 0, s>>>(a);
+  if (dtype == DT_BF16) {   // records of the 16-bit streamed attention
+    if (D == 128) attn_combine_frag_kernel<f16_t, 128><<<grid, 256, 0, s>>>(a);
+    else attn_combine_frag_kernel<f16_t, 64><<<grid, 256, 0, s>>>(a);
   } else {
     if (D == 128) attn_combine_kernel<float, 128><<<grid, 256, 0, s>>>(a);
     else attn_combine_kernel<float, 64><<<grid, 256, 0, s>>>(a);
