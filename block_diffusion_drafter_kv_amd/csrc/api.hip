@@ -738,6 +738,8 @@ namespace {
 // DFlash 2 [P2 §3.2.3]: hbuf2 = dynamic conv of the block rows of the sub-layer
 // input x = X * rs * gain held in hbuf (rs from the norm pass that wrote hbuf);
 // the per-row kernel corrections come from one product with the layer's proj.
+// A split product leaves its partial tiles to the convolution, which sums them
+// in split order (as the reduction pass would) and applies the weight scale.
 void conv_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj, float proj_scale, const void* base,
                 const void* gain) {
   const dflash_config& c = h->cfg;
@@ -746,10 +748,15 @@ void conv_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj,
   GemmArgs ga = gemm_a1(h->hbuf, H, M, nc, H);
   ga.out_scale = proj_scale;
   set_b(ga, {{proj, nc}}, H);
+  ga.keep_partials = 1;
   EpiStore<float>::Params pc{h->cbuf, nc};
-  launch_gemm(h->op, EPI_STORE_F32, ga, &pc, plan_gemm(h->op, M, nc, H, h->num_cus), h->partials, h->partials_elems,
-              s);
-  launch_dyn_conv(c.dtype, M, R, H, c.conv_group, h->X, h->rsbuf, gain, h->cbuf, base, h->hbuf2, s);
+  const GemmShape gs = launch_gemm(h->op, EPI_STORE_F32, ga, &pc, plan_gemm(h->op, M, nc, H, h->num_cus), h->partials,
+                                   h->partials_elems, s);
+  if (gs.splits > 1)
+    launch_dyn_conv(c.dtype, M, R, H, c.conv_group, h->X, h->rsbuf, gain, h->partials, gs.Npad, gs.splits,
+                    (int64_t)gs.Mpad * gs.Npad, proj_scale, base, h->hbuf2, s);
+  else
+    launch_dyn_conv(c.dtype, M, R, H, c.conv_group, h->X, h->rsbuf, gain, h->cbuf, nc, 1, 0, 1.f, base, h->hbuf2, s);
 }
 
 // Output projection of a sub-layer (A [M, Kd] times B^T [H, Kd]): added to the

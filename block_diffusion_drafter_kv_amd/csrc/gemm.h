@@ -43,6 +43,7 @@ struct GemmArgs {
   int splits;
   int k_per_split;             // multiple of the K slab
   float* partials;             // [splits][Mpad][Npad]
+  int keep_partials;           // 1: a split product leaves its partial tiles to the consumer (no reduce pass)
   int Mpad, Npad;
   int tiles_m, tiles_n;
 };

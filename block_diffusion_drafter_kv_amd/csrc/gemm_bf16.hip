@@ -105,7 +105,10 @@ static GemmPlan runnable_plan(int op, EpiKind kind, GemmPlan p) {
     p.sb = 0;
     return p;
   }
-  if (p.bm == 256 && p.bn == 256 && big_epi) return p;
+  if (p.bm == 256 && p.bn == 256 && big_epi) {   // the 256 x 256 kernel runs unsplit
+    p.splits = 1;
+    return p;
+  }
   if (p.bn == 128 && (p.bm == 64 || p.bm == 192 || p.bm == 128)) {
     if (p.bm != 128) p.sb = 0;
     return p;
@@ -123,8 +126,8 @@ static GemmPlan runnable_plan(int op, EpiKind kind, GemmPlan p) {
   return p;
 }
 
-void launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan_in, float* partials,
-                 size_t partials_elems, hipStream_t s) {
+GemmShape launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan_in,
+                      float* partials, size_t partials_elems, hipStream_t s) {
   const GemmPlan plan = runnable_plan(op, kind, plan_in);
   const int bk = op != OP_F32 ? 64 : 32;
   g.tiles_m = (g.M + plan.bm - 1) / plan.bm;
@@ -140,6 +143,7 @@ void launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const
   if (op == OP_F16) gemm_dispatch_f16(kind, plan, g, epi_params, s);
   else if (op == OP_BF16) gemm_dispatch_bf16(kind, plan, g, epi_params, s);
   else gemm_dispatch_f32(kind, plan, g, epi_params, s);
+  return GemmShape{g.splits, g.Mpad, g.Npad};
 }
 
 }  // namespace dfl

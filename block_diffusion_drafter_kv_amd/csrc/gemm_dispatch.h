@@ -44,12 +44,12 @@ static void gemm2_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (g.a_wide) {
       gemm2_kernel<T, BM, BN, SA, SB, Epi, true><<<grid, 256, 0, s>>>(g, p);
-      if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
+      if (g.splits > 1 && !g.keep_partials) gemm_reduce_kernel<BM, BN, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
       return;
     }
   }
   gemm2_kernel<T, BM, BN, SA, SB, Epi><<<grid, 256, 0, s>>>(g, p);
-  if (g.splits > 1) gemm_reduce_kernel<BM, BN, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
+  if (g.splits > 1 && !g.keep_partials) gemm_reduce_kernel<BM, BN, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
 }
 
 template <int BM, class Epi>
@@ -57,7 +57,7 @@ static void gemm1_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   const typename Epi::Params& p = *(const typename Epi::Params*)ep;
   dim3 grid(gemm_grid(g.tiles_m * g.tiles_n), g.splits);
   gemm_kernel<float, BM, 128, Epi><<<grid, 256, 0, s>>>(g, p);
-  if (g.splits > 1) gemm_reduce_kernel<BM, 128, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
+  if (g.splits > 1 && !g.keep_partials) gemm_reduce_kernel<BM, 128, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
 }
 
 // Epilogues that work on whole heads or whole 128-column statistics tiles need

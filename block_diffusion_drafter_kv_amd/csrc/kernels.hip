@@ -1717,10 +1717,12 @@ __global__ __launch_bounds__(64) void rejection_sparse_kernel(int K, int kp, int
 template <typename T>
 __global__ __launch_bounds__(256) void dyn_conv_kernel(int M, int R, int H, int G, const float* X, const float* rs,
                                                         const typename WeightOf<T>::type* gain, const float* corr,
+                                                        int corr_ld, int splits, int64_t split_stride, float scale,
                                                         const typename WeightOf<T>::type* base, T* y) {
   // elementwise: one thread per four channels of one row; x_m = X_m * rs_m * gain
   // with the row scales rs written by the RMSNorm pass that produced the
-  // correction product's input
+  // correction product's input; the corrections are scale times the sum, in
+  // split order, of the product's split partials (one split: the product itself)
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int h4 = H / 4;
   if (i >= (int64_t)M * h4) return;
@@ -1731,7 +1733,14 @@ __global__ __launch_bounds__(256) void dyn_conv_kernel(int M, int R, int H, int 
   const float4 b0 = load4f(base + c), b1 = load4f(base + H + c);
   const float4 u = first ? make_float4(0.f, 0.f, 0.f, 0.f) : load4f(X + (int64_t)(m - 1) * H + c);
   const float r0 = rs[m], r1 = first ? 0.f : rs[m - 1];
-  const float c0 = corr[(int64_t)m * 2 * ng + c / G], c1 = corr[(int64_t)m * 2 * ng + ng + c / G];
+  const float* cp = corr + (int64_t)m * corr_ld + c / G;
+  float c0 = 0.f, c1 = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    c0 += cp[sp * split_stride];
+    c1 += cp[sp * split_stride + ng];
+  }
+  c0 *= scale;
+  c1 *= scale;
   store4(y + (int64_t)m * H + c, (b0.x + c0) * v.x * r0 * g.x + (b1.x + c1) * u.x * r1 * g.x,
          (b0.y + c0) * v.y * r0 * g.y + (b1.y + c1) * u.y * r1 * g.y,
          (b0.z + c0) * v.z * r0 * g.z + (b1.z + c1) * u.z * r1 * g.z,
@@ -2432,16 +2441,17 @@ void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, 
 }
 
 void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const float* rs, const void* gain,
-                     const float* corr, const void* base, void* y, hipStream_t s) {
+                     const float* corr, int corr_ld, int splits, int64_t split_stride, float scale, const void* base,
+                     void* y, hipStream_t s) {
   const int64_t n = (int64_t)M * (H / 4);
   if (n == 0) return;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (dtype == DT_BF16)
-    dyn_conv_kernel<f16_t><<<blocks, 256, 0, s>>>(M, R, H, G, X, rs, (const bf16_t*)gain, corr, (const bf16_t*)base,
-                                                  (f16_t*)y);
+    dyn_conv_kernel<f16_t><<<blocks, 256, 0, s>>>(M, R, H, G, X, rs, (const bf16_t*)gain, corr, corr_ld, splits,
+                                                  split_stride, scale, (const bf16_t*)base, (f16_t*)y);
   else
-    dyn_conv_kernel<float><<<blocks, 256, 0, s>>>(M, R, H, G, X, rs, (const float*)gain, corr, (const float*)base,
-                                                  (float*)y);
+    dyn_conv_kernel<float><<<blocks, 256, 0, s>>>(M, R, H, G, X, rs, (const float*)gain, corr, corr_ld, splits,
+                                                  split_stride, scale, (const float*)base, (float*)y);
 }
 
 void launch_sel_walk(int dtype, int n_req, int K, int C, int rank, int V, const int32_t* slots,

@@ -28,10 +28,17 @@ inline int gemm_bn(int) { return 128; }
 // big_ok: the product's epilogue has a 256 x 256 instantiation (fc store, K|V
 // injection, LM head).
 GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide = false, bool big_ok = false);
-// Fill tiles/splits/partials fields of g and launch kernel (+ reduce when split).
+// Fill tiles/splits/partials fields of g and launch kernel (+ reduce when split,
+// unless g.keep_partials).  Returns the launched split count and partial-tile
+// shape: with keep_partials and splits > 1 the unscaled partial sums of output
+// (m, n) are partials[s * Mpad * Npad + m * Npad + n], s < splits, and the
+// epilogue did not run.
 // op: operand type; OP_BF16 supports only EPI_STORE_F32 (the fc product).
-void launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan,
-                 float* partials, size_t partials_elems, hipStream_t s);
+struct GemmShape {
+  int splits, Mpad, Npad;
+};
+GemmShape launch_gemm(int op, EpiKind kind, GemmArgs g, const void* epi_params, const GemmPlan& plan,
+                      float* partials, size_t partials_elems, hipStream_t s);
 
 // ---- attention (attention.hip) ----
 // attention work plan: per-segment group starts, equal group ranges for up to
@@ -118,9 +125,11 @@ void launch_verify_subset(int n_req, int K, int C, int V, const int32_t* slots, 
                           int32_t* out_tokens, int32_t* out_len, int32_t* accept_len, int32_t* next_anchor,
                           int32_t* err, hipStream_t s, Nucleus* nuc = nullptr, float top_p = 1.f);
 // DFlash 2: y = dynamic two-tap conv of x = X * rs * gain [M, H] (blocks of R rows, rs [M] the
-// rows' RMS scales) with kernel corrections corr [M, 2H/G]
+// rows' RMS scales) with kernel corrections [M, 2H/G] = scale * sum over s < splits of
+// corr[s * split_stride + m * corr_ld + j] (the split partials of the correction product)
 void launch_dyn_conv(int dtype, int M, int R, int H, int G, const float* X, const float* rs, const void* gain,
-                     const float* corr, const void* base, void* y, hipStream_t s);
+                     const float* corr, int corr_ld, int splits, int64_t split_stride, float scale, const void* base,
+                     void* y, hipStream_t s);
 // DFlash 2: X[rows] += two-tap conv of the sub-layer output o (fp32 [M, H]) with corrections corr
 // [M, 2H/G], then RMSNorm of the updated rows into h_out (row mapping as launch_rmsnorm)
 void launch_conv_post_norm(int dtype, int n_rows, int H, int G, float* X, int map_mask, int K, int R, const float* o,
