@@ -218,59 +218,109 @@ struct EpiKVInject {
   };
   template <int BN, int ROWS>
   __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int, int, int tid) {
+    if (p.d == 128) run<128, BN, ROWS>(p, st, ld, m0, n0, M, tid);
+    else run<64, BN, ROWS>(p, st, ld, m0, n0, M, tid);
+  }
+  // Lane r < ROWS first loads row r's slot and position; every wave then takes
+  // its (row, head) K items, fixed at compile time, CH at a time, reading the
+  // row's slot and position from that lane and issuing the chunk's remaining
+  // global loads (cache location, RoPE pair, gains) before the first is used (a
+  // loop over rows would wait for each row's loads in turn; CH bounds the
+  // registers a chunk holds beside the accumulators).  V heads: lanes walk rows
+  // (consecutive positions -> coalesced stores), waves walk columns.
+  template <int D, int BN, int ROWS>
+  __device__ static void run(const Params& p, const float* st, int ld, int m0, int n0, int M, int tid) {
+    constexpr int HALF = D / 2, PER = 64 / HALF, HEADS = BN / D, ITEMS = ROWS * HEADS;
+    constexpr int NIT = ITEMS / (4 * PER), CH = NIT < 2 ? NIT : 2;
+    static_assert(BN % D == 0 && ITEMS % (4 * PER) == 0 && NIT % CH == 0 && ROWS <= 64, "whole items per wave");
     const int lane = tid & 63, wave = tid >> 6;
-    const int heads = BN / p.d;
+    const int sub = lane / HALF, i = lane % HALF;
     bool bad = false;
-    for (int hh = 0; hh < heads; ++hh) {
-      const int nb = n0 + hh * p.d;
-      const int layer = nb / (2 * p.kv_dim);
+    const int mrow = m0 + lane;
+    const int lslot = lane < ROWS && mrow < M ? p.row_slot[mrow] : -1;
+    const int lpos = lslot >= 0 ? p.row_pos[mrow] : 0;
+    auto head_of = [&](int hh, int& layer, bool& isv, int& head) {
+      const int nb = n0 + hh * D;
+      layer = nb / (2 * p.kv_dim);
       const int within = nb % (2 * p.kv_dim);
-      const bool isv = within >= p.kv_dim;
-      const int head = (within % p.kv_dim) / p.d;
-      if (!isv) {
-        const int half = p.d / 2, per = 64 / half;
-        const int sub = lane / half, i = lane % half;
-        for (int r = wave * per + sub; r < ROWS; r += 4 * per) {
-          const int m = m0 + r;
-          if (m >= M) continue;
-          const int slot = p.row_slot[m];
-          if (slot < 0) continue;
-          const int pos = p.row_pos[m];
-          int64_t hb;
-          int pin;
-          if (!kv_locate(p.pages, p.ctx_alloc * p.d, p.max_batch, p.n_kv, p.d, p.layer0 + layer, slot, head, pos,
-                         &hb, &pin)) {
-            if (i == 0) raise_error(p.err, ERR_PAGE);
-            continue;
+      isv = within >= p.kv_dim;
+      head = (within % p.kv_dim) / D;
+    };
+#pragma unroll 1
+    for (int k0 = 0; k0 < NIT; k0 += CH) {
+      int r_[CH], hh_[CH], slot_[CH], pos_[CH], pin_[CH];
+      int64_t hb_[CH];
+      float2 cs_[CH];
+      float g1_[CH], g2_[CH];
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        const int it = ((k0 + k) * 4 + wave) * PER + sub;
+        r_[k] = it / HEADS;
+        hh_[k] = it % HEADS;
+        int layer, head;
+        bool isv;
+        head_of(hh_[k], layer, isv, head);
+        slot_[k] = __shfl(lslot, r_[k], 64);
+        pos_[k] = __shfl(lpos, r_[k], 64);
+        if (isv) slot_[k] = -1;
+      }
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        int layer, head;
+        bool isv;
+        head_of(hh_[k], layer, isv, head);
+        hb_[k] = 0;
+        pin_[k] = 0;
+        if (slot_[k] >= 0 &&
+            !kv_locate(p.pages, p.ctx_alloc * D, p.max_batch, p.n_kv, D, p.layer0 + layer, slot_[k], head, pos_[k],
+                       &hb_[k], &pin_[k])) {
+          if (i == 0) raise_error(p.err, ERR_PAGE);
+          slot_[k] = -1;
+        }
+        cs_[k] = p.rope[(int64_t)pos_[k] * HALF + i];
+        const W* gain = p.k_gain[layer];
+        g1_[k] = to_f32(gain[i]);
+        g2_[k] = to_f32(gain[i + HALF]);
+      }
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        int layer, head;
+        bool isv;
+        head_of(hh_[k], layer, isv, head);
+        if (!isv) {
+          // every lane of the row's group reduces, valid row or not
+          float x1 = st[r_[k] * ld + hh_[k] * D + i], x2 = st[r_[k] * ld + hh_[k] * D + i + HALF];
+          const float ss = group_sum(x1 * x1 + x2 * x2, HALF);
+          const float rs = rsqrtf(ss / (float)D + p.eps);
+          x1 *= rs * g1_[k];
+          x2 *= rs * g2_[k];
+          const float2 cs = cs_[k];
+          const float y1 = x1 * cs.x - x2 * cs.y, y2 = x2 * cs.x + x1 * cs.y;
+          if (slot_[k] >= 0) {
+            T* dst = p.cache_k + hb_[k];
+            dst[k_off(pin_[k], i, D)] = store_cvt<T>(y1, bad);
+            dst[k_off(pin_[k], i + HALF, D)] = store_cvt<T>(y2, bad);
           }
-          float x1 = st[r * ld + hh * p.d + i], x2 = st[r * ld + hh * p.d + i + half];
-          norm_rope_pair<W>(x1, x2, i, p.d, p.k_gain[layer], p.eps, p.rope + (int64_t)pos * half);
-          T* dst = p.cache_k + hb;
-          dst[k_off(pin, i, p.d)] = store_cvt<T>(x1, bad);
-          dst[k_off(pin, i + half, p.d)] = store_cvt<T>(x2, bad);
-        }
-      } else {
-        // lanes walk rows (consecutive positions -> coalesced stores), waves walk columns
-        constexpr int RPL = 64 / ROWS;   // columns handled at once by one wave
-        const int r = lane % ROWS;
-        const int m = m0 + r;
-        int slot = -1, pos = 0;
-        if (m < M) {
-          slot = p.row_slot[m];
-          pos = p.row_pos[m];
-        }
-        int64_t hb = 0;
-        int pin = 0;
-        if (slot >= 0 &&
-            !kv_locate(p.pages, p.ctx_alloc * p.d, p.max_batch, p.n_kv, p.d, p.layer0 + layer, slot, head, pos, &hb,
-                       &pin))
-          slot = -1;   // unmapped: flagged by the K half
-        if (slot >= 0) {
-          T* base = p.cache_v + hb;
-          for (int c = wave * RPL + lane / ROWS; c < p.d; c += 4 * RPL)
-            base[v_off(pin, c, p.d)] = store_cvt<T>(st[r * ld + hh * p.d + c], bad);
         }
       }
+    }
+    // V heads
+    constexpr int RPL = 64 / ROWS;   // columns handled at once by one wave
+    const int r = lane % ROWS;
+    const int vslot = __shfl(lslot, r, 64), vpos = __shfl(lpos, r, 64);
+#pragma unroll
+    for (int hh = 0; hh < HEADS; ++hh) {
+      int layer, head;
+      bool isv;
+      head_of(hh, layer, isv, head);
+      if (!isv || vslot < 0) continue;
+      int64_t hb = 0;
+      int pin = 0;
+      if (!kv_locate(p.pages, p.ctx_alloc * D, p.max_batch, p.n_kv, D, p.layer0 + layer, vslot, head, vpos, &hb, &pin))
+        continue;   // unmapped: flagged by the K half
+      T* base = p.cache_v + hb;
+      for (int c = wave * RPL + lane / ROWS; c < D; c += 4 * RPL)
+        base[v_off(pin, c, D)] = store_cvt<T>(st[r * ld + hh * D + c], bad);
     }
     report_nonfinite(p.err, bad, tid);
   }
