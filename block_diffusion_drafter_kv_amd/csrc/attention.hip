@@ -36,8 +36,13 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* slots, co
                                                          int4* wg_range) {
   __shared__ int buf[256];
   __shared__ int carry;
+  // the segment starts are searched once per work-group range: an LDS copy when
+  // they fit (a search through global memory waits for each of its loads)
+  constexpr int LDS_SEGS = 8192;
+  __shared__ int ssl[LDS_SEGS + 1];
   const int tid = threadIdx.x;
   const int per_req = n_kv * splits, n_seg = n_req * per_req;
+  const bool in_lds = n_seg <= LDS_SEGS;
   if (tid == 0) carry = 0;
   __syncthreads();
   for (int b = 0; b < n_seg; b += 256) {
@@ -45,24 +50,29 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* slots, co
     int cnt = 0;
     if (s < n_seg) cnt = (ctx_len[slots[s / per_req]] + KV_BLOCK - 1) / KV_BLOCK + 1;
     const int st = block_exclusive_scan(cnt, buf, &carry);
-    if (s < n_seg) seg_start[s] = st;
+    if (s < n_seg) {
+      seg_start[s] = st;
+      if (in_lds) ssl[s] = st;
+    }
   }
   const int total = carry;
   const int per_wg = max(min_per_wg, (total + n_wg_max - 1) / max(n_wg_max, 1));
   __syncthreads();
   if (tid == 0) {
     seg_start[n_seg] = total;
+    if (in_lds) ssl[n_seg] = total;
     plan->total = total;
     plan->per_wg = per_wg;
     plan->n_wg = (total + per_wg - 1) / per_wg;
     carry = 0;
   }
   __syncthreads();
+  const int* ss = in_lds ? ssl : seg_start;
   for (int b = 0; b < n_seg; b += 256) {
     const int s = b + tid;
     int cnt = 0;
     if (s < n_seg) {
-      const int len = seg_start[s + 1] - seg_start[s];
+      const int len = ss[s + 1] - ss[s];
       const int cg = attn_chunk_groups(len, chunk_min, chunk_max);
       cnt = (len + cg - 1) / cg;
     }
@@ -72,12 +82,12 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* slots, co
   // per-segment descriptors and per-work-group ranges, so that an attention
   // work-group starts with two loads instead of dependent searches
   for (int s = tid; s < n_seg; s += 256)
-    seg_desc[s] = make_int4(slots[s / per_req], ctx_len[slots[s / per_req]], seg_start[s], seg_start[s + 1] - seg_start[s]);
+    seg_desc[s] = make_int4(slots[s / per_req], ctx_len[slots[s / per_req]], ss[s], ss[s + 1] - ss[s]);
   auto find_seg = [&](int x) {   // last s with seg_start[s] <= x
     int lo = 0, hi = n_seg - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (seg_start[mid] <= x) lo = mid;
+      if (ss[mid] <= x) lo = mid;
       else hi = mid - 1;
     }
     return lo;
@@ -85,7 +95,7 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* slots, co
   auto chunk_start = [&](int x) {   // first chunk start at or after group x
     if (x >= total) return total;
     const int sg = find_seg(x);
-    const int b = seg_start[sg], e = seg_start[sg + 1];
+    const int b = ss[sg], e = ss[sg + 1];
     const int cg = attn_chunk_groups(e - b, chunk_min, chunk_max);
     return min(e, b + (x - b + cg - 1) / cg * cg);
   };
