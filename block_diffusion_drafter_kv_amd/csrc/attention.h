@@ -6,19 +6,23 @@
 // Work split, decided on the device from the actual context lengths (no host
 // sync).  A segment is one (request, kv head, q-row part); its keys form
 // ceil(C/32) cache groups of 32 keys plus one group holding the block's own
-// R <= 32 keys.  Each segment is cut into chunks of cg = max(chunk_min,
-// ceil(groups / chunk_max)) groups; a chunk's partial result (unnormalised O,
-// running max, sum) depends on that request alone, so results do not depend on
-// the rest of the batch.  The groups of all segments are laid end to end and
-// cut into equal ranges, each snapped forward to a chunk start, one range per
-// work-group, so every work-group streams about the same number of bytes
-// whatever the mix of context lengths.  A combine kernel merges the chunks of
-// each segment in order.
+// R <= 32 keys.  The groups of all segments are laid end to end and cut into
+// equal ranges, one per work-group, so every work-group streams about the same
+// number of bytes whatever the mix of context lengths.
+//   16-bit K/V (attn_wave_kernel): ranges are not snapped, so a range may start
+//   or end inside a segment; each (work-group, segment) piece writes one partial
+//   record (O / l in fp16, fragment order; m and l in fp32) at index w + s.
+//   fp32 K/V (attn_kernel): each segment is cut into chunks of cg = max(chunk_min,
+//   ceil(groups / chunk_max)) groups and the range ends are snapped to chunk
+//   starts, so a chunk's partial record (unnormalised O, m, l in fp32, row
+//   layout) depends on its request alone.
+// A combine kernel merges each segment's records in order.
 //
-// Inside a work-group, one wave per 16-row query tile.  K and V are stored in
-// 32-key blocks in MFMA operand order (kv_layout.h) and copied straight into a
-// ring of LDS stages; scores are computed transposed, S^T = K Q^T, so that the
-// softmax probabilities land in registers as the B operand of O^T = V^T P^T.
+// K and V are stored in 32-key blocks in MFMA operand order (kv_layout.h), so
+// every 64-lane fragment is one contiguous 1 KB span, copied straight into a ring
+// of LDS stages shared by the work-group's waves.  Scores are computed
+// transposed, S^T = K Q^T, so that the softmax probabilities land in registers
+// as the B operand of O^T = V^T P^T.
 #pragma once
 #include "common.h"
 #include "kv_layout.h"
@@ -44,9 +48,9 @@ struct AttnArgs {
   const int32_t* chunk_base;  // [n_seg] first partial-result record (chunk) of each segment
   const int4* seg_desc;       // [n_seg] (slot, context length, first group, group count)
   const int4* wg_range;       // [work-groups] (first group, end group, segment of the first group, -)
-  float* o_part;              // [chunk][QRT*16][D]
-  float* m_part;              // [chunk][QRT*16]   running max (exp2 domain)
-  float* l_part;              // [chunk][QRT*16]   sum of exp2(s - m)
+  float* o_part;              // fp32: [chunk][QRT*16][D]; 16-bit: fp16 O/l [piece][QRT][D/16][64 lanes][4]
+  float* m_part;              // [chunk or piece][QRT*16]   running max (exp2 domain)
+  float* l_part;              // [chunk or piece][QRT*16]   sum of exp2(s - m)
   int n_seg, n_kv, R, Rpad, QRpad, rows_per_split, splits;
   int chunk_min, chunk_max;   // chunk size rule (groups), see above
   int64_t ctx_alloc;
