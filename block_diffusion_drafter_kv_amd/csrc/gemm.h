@@ -48,14 +48,16 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
-// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row: chunk c of
-// row r is stored at slot c ^ swz(r).  A fragment read takes one chunk from 16
-// consecutive rows per LDS cycle (64 banks of 4 bytes): rows of one parity share
-// banks when they share a slot, so swz must differ across the 8 even and across
-// the 8 odd rows of every aligned group of 16 -- and, for 8-lane phases, across
-// every aligned group of 8 rows.  (row & 7) ^ ((row >> 3) & 1) does both; plain
-// row & 7 leaves rows r and r + 8 in the same banks.
+// XOR swizzles of the eight 16-byte chunks of a 128-byte LDS row: chunk c of
+// row r is stored at slot c ^ swz(r).  Which lanes of a 16-byte LDS read share a
+// cycle was measured on gfx950 (bank-conflict counter over a probe of each lane
+// pattern), not assumed.  For the 32 x 32 x 16 fragments of gemm256.h (lane l:
+// row l % 32, chunk l / 32), swz = (row & 7) ^ ((row >> 3) & 1) is conflict-free
+// and plain row & 7 doubles the LDS cycles; for the 16 x 16 x 32 fragments of
+// gemm2.h (row l % 16, chunk l / 16) it is the other way round, so gemm2.h
+// stores with swz16 = row & 7.
 __host__ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__host__ __device__ __forceinline__ int swz16(int row) { return row & 7; }
 
 template <typename T> struct GemmTraits;
 template <> struct GemmTraits<bf16_t> { static constexpr int BK = 64; static constexpr int VEC = 8; };

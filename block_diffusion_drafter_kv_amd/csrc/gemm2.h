@@ -9,7 +9,7 @@
 // __syncthreads, whose release fence would drain every outstanding copy).
 //
 // LDS layout of one buffer: A rows [0, BM) then B rows [0, BN), 8 chunks of 16
-// bytes per row with chunk c of row r stored at slot c ^ swz(r); the copy
+// bytes per row with chunk c of row r stored at slot c ^ swz16(r); the copy
 // unit writes lane l of a wave to slot (wave base + l), so each lane fetches
 // the global chunk that belongs in its slot.
 #pragma once
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
   // it takes a wave-uniform base (SGPRs) plus a per-lane 32-bit byte offset that
   // stays fixed for the whole K loop; only the bases advance per slab.
   const int crow = tid >> 3;
-  const int cchunk = (tid & 7) ^ swz(crow);
+  const int cchunk = (tid & 7) ^ swz16(crow);
   typedef typename std::conditional<A64, int64_t, uint32_t>::type AOff;
   AOff a_off[NA];
 #pragma unroll
@@ -124,12 +124,12 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
 #pragma unroll
       for (int fi = 0; fi < FM; ++fi) {
         const int row = wm * WM + fi * 16 + r16;
-        *(uint4*)&af[fi] = bufA[row * 8 + (c ^ swz(row))];
+        *(uint4*)&af[fi] = bufA[row * 8 + (c ^ swz16(row))];
       }
 #pragma unroll
       for (int fj = 0; fj < FN; ++fj) {
         const int row = wn * WN + fj * 16 + r16;
-        *(uint4*)&bfr[fj] = bufB[row * 8 + (c ^ swz(row))];
+        *(uint4*)&bfr[fj] = bufB[row * 8 + (c ^ swz16(row))];
       }
 #pragma unroll
       for (int fi = 0; fi < FM; ++fi)
