@@ -549,7 +549,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     for (int c = 0; c < CPW; ++c) {
       const int f = wave * CPW + c;
       const T* src = f < 2 * KS ? kp + (f * 64 + lane) * 8 : vp + ((f - 2 * KS) * 64 + lane) * 8;
-      copy16_to_lds_at(src, ring_lds + (uint32_t)(ls_stage * NF + f) * 1024u);
+      copy16_to_lds_m0(src, ring_lds + (uint32_t)(ls_stage * NF + f) * 1024u);
     }
     if (++ls_stage == S) ls_stage = 0;
     if (++ls_l == ls.len) {   // the next segment (decoded even when the range ends here: its descriptor exists)

@@ -44,6 +44,11 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
   __shared__ uint4 smem[(SA * BM + SB * BN) * 8];
   auto smemA = [&](int st) { return smem + st * (BM * 8); };
   auto smemB = [&](int st) { return smem + SA * BM * 8 + st * (BN * 8); };
+  // the same stages as LDS byte addresses for the copies (integers: no generic
+  // pointer round trip per copy)
+  const uint32_t lds0 = lds_addr(smem);
+  auto ldsA = [&](int st) { return lds0 + (uint32_t)(st * BM * 128); };
+  auto ldsB = [&](int st) { return lds0 + (uint32_t)((SA * BM + st * BN) * 128); };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
@@ -87,26 +92,31 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
     b_off[j] = (uint32_t)((valid ? (lane >> 3) : 0) * g.b_ld * (int64_t)sizeof(T)) + cchunk * 16;
   }
 
-  // A-segment cursor of the next slab to issue (A slabs are issued in K order)
+  // A-segment cursor of the next slab to issue (A slabs are issued in K order);
+  // the segment's base pointer is read from the arguments only when the
+  // cursor enters a segment
   int a_seg = k_begin / g.a_segk, a_kk = k_begin - a_seg * g.a_segk;
-  auto issue_a = [&](uint4* dst) {
-    const char* abase = (const char*)g.a_ptr[a_seg] + (int64_t)a_kk * sizeof(T);
+  const char* a_cur = (const char*)g.a_ptr[a_seg < g.a_nseg ? a_seg : 0];
+  auto issue_a = [&](uint32_t dst) {
+    const char* abase = a_cur + (int64_t)a_kk * sizeof(T);
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      if constexpr (A64) copy16_to_lds(abase + a_off[i], dst + i * 256 + wave * 64);
-      else copy16_to_lds_sv(abase, a_off[i], dst + i * 256 + wave * 64);
+      const uint32_t d = dst + (uint32_t)((i * 256 + wave * 64) * 16);
+      if constexpr (A64) copy16_to_lds_m0(abase + a_off[i], d);
+      else copy16_to_lds_sv_m0(abase, a_off[i], d);
     }
     a_kk += BK;
     if (a_kk == g.a_segk) {
       ++a_seg;
       a_kk = 0;
+      if (a_seg < g.a_nseg) a_cur = (const char*)g.a_ptr[a_seg];
     }
   };
-  auto issue_b = [&](int kt, uint4* dst) {
+  auto issue_b = [&](int kt, uint32_t dst) {
     const int k0 = k_begin + kt * BK;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      copy16_to_lds_sv(b_base[j] + (int64_t)k0 * sizeof(T), b_off[j], dst + j * 256 + wave * 64);
+      copy16_to_lds_sv_m0(b_base[j] + (int64_t)k0 * sizeof(T), b_off[j], dst + (uint32_t)((j * 256 + wave * 64) * 16));
   };
 
   f32x4 acc[FM][FN];
@@ -142,8 +152,8 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
   // iteration kt (after its barrier) gives [A(kt+SA-1)][B(kt+SB-1)] when in range.
 #pragma unroll
   for (int p = 0; p < (SA > SB ? SA : SB) - 1; ++p) {
-    if (p < SA - 1 && p < nk) issue_a(smemA(p));
-    if (p < SB - 1 && p < nk) issue_b(p, smemB(p));
+    if (p < SA - 1 && p < nk) issue_a(ldsA(p));
+    if (p < SB - 1 && p < nk) issue_b(p, ldsB(p));
   }
   for (int kt = 0; kt < nk; ++kt) {
     // wait until A(kt) and B(kt) have landed: count the copies issued after them
@@ -166,8 +176,8 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
       else wait_vmcnt<0>();
     }
     lds_barrier();
-    if (kt + SA - 1 < nk) issue_a(smemA((kt + SA - 1) % SA));
-    if (kt + SB - 1 < nk) issue_b(kt + SB - 1, smemB((kt + SB - 1) % SB));
+    if (kt + SA - 1 < nk) issue_a(ldsA((kt + SA - 1) % SA));
+    if (kt + SB - 1 < nk) issue_b(kt + SB - 1, ldsB((kt + SB - 1) % SB));
     compute(smemA(kt % SA), smemB(kt % SB));
   }
   wait_vmcnt<0>();

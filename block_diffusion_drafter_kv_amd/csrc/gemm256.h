@@ -78,6 +78,11 @@ __global__ __launch_bounds__(GEMM256_THREADS) void gemm256_kernel(const GemmArgs
   __shared__ uint4 smem[2 * (BM + BN) * 8];
   auto stA = [&](int st) { return smem + st * ((BM + BN) * 8); };
   auto stB = [&](int st) { return smem + st * ((BM + BN) * 8) + BM * 8; };
+  // the stages as LDS byte addresses for the copies (integers: no generic pointer
+  // round trip per copy)
+  const uint32_t lds0 = lds_addr(smem);
+  auto ldsA = [&](int st) { return lds0 + (uint32_t)(st * (BM + BN) * 128); };
+  auto ldsB = [&](int st) { return lds0 + (uint32_t)((st * (BM + BN) + BM) * 128); };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,12 +133,14 @@ __global__ __launch_bounds__(GEMM256_THREADS) void gemm256_kernel(const GemmArgs
   const char* a_slab = (const char*)g.a_ptr[a_seg] + (int64_t)a_kk * sizeof(T);
   auto copy = [&](int q, int kt, int st) {     // copy q of slab kt into stage st (A copies first)
     if (q < NA) {
-      if constexpr (A64) copy16_to_lds_nc(a_slab + a_off[q], stA(st) + q * RPC * 8 + wave * 64);
-      else copy16_to_lds_sv_nc(a_slab, a_off[q], stA(st) + q * RPC * 8 + wave * 64);
+      const uint32_t d = ldsA(st) + (uint32_t)((q * RPC * 8 + wave * 64) * 16);
+      if constexpr (A64) copy16_to_lds_m0(a_slab + a_off[q], d);
+      else copy16_to_lds_sv_m0(a_slab, a_off[q], d);
     } else {
       const int j = q - NA;
       const int k0 = k_begin + kt * BK;
-      copy16_to_lds_sv_nc(b_base[j] + (int64_t)k0 * sizeof(T), b_off[j], stB(st) + j * RPC * 8 + wave * 64);
+      copy16_to_lds_sv_m0(b_base[j] + (int64_t)k0 * sizeof(T), b_off[j],
+                          ldsB(st) + (uint32_t)((j * RPC * 8 + wave * 64) * 16));
     }
   };
   auto advance_a = [&]() {

@@ -26,56 +26,28 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_wave_base
       : "memory");
 }
 
-// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte
-// offset (global_load_lds with saddr): no per-copy 64-bit address arithmetic.
-__device__ __forceinline__ void copy16_to_lds_sv(const void* sbase, uint32_t voff, void* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(sbase)
-      : "memory");
-}
-
-// The same two copies without a memory clobber, for loops whose barriers
-// (lds_barrier, which clobbers memory) already order every copy against the LDS
-// reads of its stage: the clobber would make the compiler reload kernel
-// arguments after each copy and wait for all outstanding LDS reads first.
-// Volatile asm statements keep their order among themselves.
-__device__ __forceinline__ void copy16_to_lds_nc(const void* g, void* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(g));
-}
-__device__ __forceinline__ void copy16_to_lds_sv_nc(const void* sbase, uint32_t voff, void* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(sbase));
-}
-
-// The same copy to an LDS byte address (wave-uniform) given as an integer: a
-// ring addressed through a run-time stage index would otherwise turn the address
-// into a generic pointer that must be cast back.
+// LDS byte address of a __shared__ object (32-bit, as M0 takes it)
 __device__ __forceinline__ uint32_t lds_addr(const void* lds_ptr) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_ptr;
 }
-__device__ __forceinline__ void copy16_to_lds_at(const void* g, uint32_t lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_wave_base);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(g));
+
+// Copies to an integer LDS byte address (wave-uniform) that declare M0 clobbered
+// instead of saving and restoring it around every copy (the compiler sets M0
+// again wherever it needs it; s_nop 0 is the wait state an M0 write needs
+// before an LDS-DMA instruction reads it), and carry no memory clobber: for ring loops
+// whose explicit waits and barriers order the copies against the LDS reads.
+// sv: wave-uniform 64-bit global base in SGPRs plus a per-lane 32-bit offset.
+__device__ __forceinline__ void copy16_to_lds_sv_m0(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_wave_base), "v"(voff), "s"(sbase)
+               : "m0");
+}
+__device__ __forceinline__ void copy16_to_lds_m0(const void* g, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_wave_base), "v"(g)
+               : "m0");
 }
 
 // s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding)
