@@ -313,6 +313,49 @@ def dflash2_measure(w, ctx, steps=10, warmup=2):
             "phase_ms_per_step": dict(sorted(per_step.items(), key=lambda x: -x[1]))}
 
 
+def dflash2_b1_measure(w, steps=20):
+    """The DFlash 2 modules at the pages' scale: batch 1, context 2048, K = 16, greedy; the plain
+    draft and the draft with both modules (conv group 16, 16 candidates, rank 256) on handles that
+    differ only in the modules, timed alternately on the same device."""
+    import numpy as np
+    import torch
+    import block_diffusion_drafter_kv_amd as dk
+    from synth import gen
+    from synth.configs import get_workload, scaled_model
+    wl = get_workload("b1_ctx2k")
+    cfg, B, K = wl.model, wl.batch, wl.K
+    cfg2 = scaled_model(cfg, conv_group=16, sel_rank=256, sel_cands=16)
+    extra = gen.dflash2_weights(cfg2, seed=77)
+    dev = lambda t: t.cuda()
+    w2 = dict(w)
+    w2["layers"] = [dict(a, **{k: dev(v) for k, v in b.items()}) for a, b in zip(w["layers"], extra["layers"])]
+    for k in ("sel_pred", "sel_succ", "sel_hidden"):
+        w2[k] = dev(extra[k])
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    handles = []
+    for c, ww in ((cfg, w), (cfg2, w2)):
+        dr = dk.Drafter(c, ww, max_batch=B, max_ctx=wl.ctx + 64, max_k=K, max_inject_rows=8192)
+        _fill_prompts(dr, c, [wl.ctx], 2025)
+        handles.append(dr)
+    slots = i32(np.arange(B))
+    anchors = i32(np.random.default_rng(3).integers(0, cfg.vocab - 1, B))
+    logits = torch.empty((B, K, cfg.vocab), dtype=torch.float32, device="cuda")
+    times = []
+    for dr in handles:
+        times.append(_timed(lambda: dr.draft(slots, anchors, K, want_stats=False, logits_out=logits), steps))
+    # a second round in the opposite order, against drift of the clocks
+    for i, dr in reversed(list(enumerate(handles))):
+        times[i] = min(times[i], _timed(lambda: dr.draft(slots, anchors, K, want_stats=False, logits_out=logits),
+                                        steps))
+    for dr in handles:
+        assert dr.get_error() == 0
+        dr.close()
+    del w2, extra
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "batch": B, "ctx": wl.ctx, "steps": steps, "draft_plain_us": round(times[0], 1),
+            "draft_dflash2_us": round(times[1], 1), "overhead_vs_plain_draft": round(times[1] / times[0] - 1.0, 4)}
+
+
 def _timed(fn, steps, warmup=2):
     """Median microseconds of fn() over `steps` calls on torch's current stream (after `warmup`)."""
     import torch
@@ -897,6 +940,8 @@ def main():
         log("[bench] DFlash 2 modules (conv + selector) on the same workload ...")
         d2 = dflash2_measure(w, ctx)
         d2["overhead_vs_plain_draft"] = round(d2["draft_us_median"] / (draft_ms * 1e3) - 1.0, 4)
+        log("[bench] DFlash 2 modules at batch 1 (context 2048) ...")
+        d2["b1_ctx2k"] = dflash2_b1_measure(w)
         result["dflash2"] = d2
     if not args.no_variants:
         log("[bench] sampling and attention variants on the same workload ...")

@@ -502,6 +502,13 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     const size_t mpad = std::max((h->maxM + 127) / 128 * 128, (h->maxM + 191) / 192 * 192);
     const size_t ncols = H + (c.conv_group > 0 ? 2 * (H / c.conv_group) : 0);
     h->partials_elems = std::max((size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(h->op), (size_t)4 * mpad * ncols);
+    // ... and the per-step injection (a row bound of at most 1024 on 64-row tiles,
+    // the true row count on the device): the partial tiles cover every row tile
+    // of the bound, for the fc product's K split in up to eight and the K|V
+    // product's in up to eight (a smaller buffer silently cut both splits)
+    const size_t inj_rows = (size_t)(std::min(c.max_inject_rows, 1024) + 63) / 64 * 64;
+    const size_t kv_cols = (size_t)2 * kvdim * std::min(c.n_layers, MAX_BSEG / 2);
+    h->partials_elems = std::max(h->partials_elems, 8 * inj_rows * std::max((size_t)H, kv_cols));
     if ((rc = alloc_t(h, &h->partials, h->partials_elems, 4))) break;
     const size_t lrows = (size_t)c.max_batch * c.max_k;
     if ((rc = alloc_t(h, &h->logits_ws, lrows * c.vocab, 4))) break;
@@ -606,6 +613,12 @@ int validate_inject(dflash_handle* h, int n_req, const int32_t* slots, const int
   return DFLASH_OK;
 }
 
+// K splits of the per-step injection products (planned for one 64-row tile, the
+// true row count on the device), measured at batch 32: K|V 4 (inject_kv 64 us
+// per step with 2, 50 with 4, 57 with 8), fc 16 (63 us with 8, 61 with 16)
+static constexpr int KV_STEP_SPLITS = 4;
+static constexpr int FC_STEP_SPLITS = 16;
+
 // The products of an injection once its row tables (a_rows, row_slot, row_pos,
 // req_off) are on the device: fc, RMSNorm, per-layer K|V with k-norm + RoPE into the cache.
 int inject_rows(dflash_handle* h, hipStream_t s, int n_req, int64_t rows_upper_bound, const void* const* target_hidden,
@@ -636,8 +649,9 @@ int inject_rows(dflash_handle* h, hipStream_t s, int n_req, int64_t rows_upper_b
     EpiStore<float>::Params pf{h->y, H};
     {
       Phase ph(h, s, DFLASH_PH_INJECT_FC);
-      launch_gemm(h->op_fc, EPI_STORE_F32, ga, &pf, plan_gemm(h->op_fc, plan_rows, H, featK, h->num_cus, false, true),
-                  h->partials, h->partials_elems, s);
+      GemmPlan fp = plan_gemm(h->op_fc, plan_rows, H, featK, h->num_cus, false, true);
+      if (plan_rows <= 64) fp.splits = std::max(fp.splits, FC_STEP_SPLITS);
+      launch_gemm(h->op_fc, EPI_STORE_F32, ga, &pf, fp, h->partials, h->partials_elems, s);
     }
     {
       Phase ph(h, s, DFLASH_PH_INJECT_NORM);
@@ -676,9 +690,10 @@ int inject_rows(dflash_handle* h, hipStream_t s, int n_req, int64_t rows_upper_b
       pk.pages = h->pages();
       pk.err = h->err;
       // the parameter block has the same layout for fp32 (pointers only differ in type)
+      GemmPlan kp = plan_gemm(h->op, plan_rows, gk.N, H, h->num_cus, false, true);
+      if (plan_rows <= 64) kp.splits = std::max(kp.splits, KV_STEP_SPLITS);
       Phase ph(h, s, DFLASH_PH_INJECT_KV);
-      launch_gemm(h->op, EPI_KVINJECT, gk, &pk, plan_gemm(h->op, plan_rows, gk.N, H, h->num_cus, false, true), h->partials,
-                  h->partials_elems, s);
+      launch_gemm(h->op, EPI_KVINJECT, gk, &pk, kp, h->partials, h->partials_elems, s);
     }
   }
   return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_E_HIP;

@@ -276,7 +276,10 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const GemmArgs g, cons
   const int m_base = tm * BM, n_base = tn * BN;
   if (g.m_valid && m_base >= *g.m_valid - g.m_valid_base) return;
   const int m0 = m_base + blockIdx.y * EPI_ROWS;
-  const int m_lim = min(g.M, m_base + BM);   // rows of this tile (BM need not be a multiple of EPI_ROWS)
+  // rows of this tile (BM need not be a multiple of EPI_ROWS), cut at the device
+  // row count when there is one (rows past it are neither summed nor passed on)
+  int m_lim = min(g.M, m_base + BM);
+  if (g.m_valid) m_lim = min(m_lim, *g.m_valid - g.m_valid_base);
   if (m0 >= m_lim) return;
   // 16-byte loads, two splits in flight at once; sums taken in split order
   constexpr int C4 = BN / 4, NV = EPI_ROWS * C4 / 256;
