@@ -28,13 +28,23 @@ static constexpr int GEMM2_EPI_ROWS = 32;   // epilogue slab: 32 rows x (BN+1) f
 // A64: A rows are addressed with per-lane 64-bit byte offsets (one 64-bit add per
 // copy) instead of 32-bit offsets from a wave-uniform base, for A buffers of
 // 4 GiB or more (the injection's caller-provided hidden states).
-template <typename T, int BM, int BN, int SA, int SB, class Epi, bool A64 = false>
-__global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const typename Epi::Params ep) {
+//
+// NT: 256 threads (4 waves, 2 x 2) or 512 (8 waves, 2 x 4, half the columns per
+// wave): two 8-wave work-groups per CU keep four waves on each SIMD, which
+// hides more of each slab's wait (measured on the 544-row products: gate/up
+// 128 x 128 tiles 148 -> 134 us, down 192 x 128 with K split in four 84 -> 79 us;
+// the narrower QKV and O tilings are as fast or faster with 4 waves).
+template <typename T, int BM, int BN, int SA, int SB, class Epi, bool A64 = false, int NT = 256>
+__global__ __launch_bounds__(NT) void gemm2_kernel(const GemmArgs g, const typename Epi::Params ep) {
   static_assert(sizeof(T) == 2, "16-bit operands");
+  static_assert(NT == 256 || NT == 512, "4 or 8 waves");
   typedef typename Frag<T>::type FragT;
   constexpr int BK = 64;
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
-  constexpr int NA = BM * 8 / 256, NB = BN * 8 / 256, NL = NA + NB;
+  constexpr int NW = NT / 64, WGN = NW / 2;                 // waves: 2 along M x WGN along N
+  constexpr int RPC = NT / 8;                               // rows per copy round
+  constexpr int WM = BM / 2, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
+  static_assert(WN % 16 == 0 && BM % RPC == 0 && BN % RPC == 0, "tile shape");
+  constexpr int NA = BM / RPC, NB = BN / RPC, NL = NA + NB;
   constexpr int ER = GEMM2_EPI_ROWS;
   static_assert(SA >= 2 && SB >= 2 && SA <= 4 && SB <= 4 && (SA == SB || SA == 2), "ring depths");
   static_assert((SA - 2) * NL < 64 && NB * (SB - 1) < 64, "vmcnt range");
@@ -67,13 +77,13 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
   // Every copy instruction of a wave covers 8 consecutive rows of one operand, so
   // it takes a wave-uniform base (SGPRs) plus a per-lane 32-bit byte offset that
   // stays fixed for the whole K loop; only the bases advance per slab.
-  const int crow = tid >> 3;
+  const int crow = tid >> 3;   // 0 .. RPC-1
   const int cchunk = (tid & 7) ^ swz16(crow);
   typedef typename std::conditional<A64, int64_t, uint32_t>::type AOff;
   AOff a_off[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int m = m_base + i * 32 + crow;
+    const int m = m_base + i * RPC + crow;
     int64_t s = 0;                      // rows outside the product read row 0 (discarded)
     if (m < g.M) {
       s = g.a_rows ? g.a_rows[m] : m;
@@ -85,7 +95,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
   uint32_t b_off[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int r0 = n_base + j * 32 + wave * 8;          // first row of this wave's block (uniform)
+    const int r0 = n_base + j * RPC + wave * 8;         // first row of this wave's block (uniform)
     const T* p0 = b_row_ptr<T, BN>(g, r0);
     const bool valid = p0 && r0 + (lane >> 3) < g.N;    // blocks never straddle a segment boundary
     b_base[j] = (const char*)(p0 ? p0 : (const T*)g.b_ptr[0]);
@@ -101,7 +111,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
     const char* abase = a_cur + (int64_t)a_kk * sizeof(T);
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const uint32_t d = dst + (uint32_t)((i * 256 + wave * 64) * 16);
+      const uint32_t d = dst + (uint32_t)((i * RPC * 8 + wave * 64) * 16);
       if constexpr (A64) copy16_to_lds_m0(abase + a_off[i], d);
       else copy16_to_lds_sv_m0(abase, a_off[i], d);
     }
@@ -116,7 +126,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
     const int k0 = k_begin + kt * BK;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      copy16_to_lds_sv_m0(b_base[j] + (int64_t)k0 * sizeof(T), b_off[j], dst + (uint32_t)((j * 256 + wave * 64) * 16));
+      copy16_to_lds_sv_m0(b_base[j] + (int64_t)k0 * sizeof(T), b_off[j], dst + (uint32_t)((j * RPC * 8 + wave * 64) * 16));
   };
 
   f32x4 acc[FM][FN];
@@ -199,13 +209,31 @@ __global__ __launch_bounds__(256) void gemm2_kernel(const GemmArgs g, const type
     return;
   }
 
+  // epilogue: NT/256 slabs of ER rows per pass staged as fp32 [ER][BN + 1], one
+  // per 256-thread group (the epilogues are written for 256 threads)
+  constexpr int EG = NT / 256;
+  static_assert(EG * ER * (BN + 1) * 4 <= (SA * BM + SB * BN) * 8 * 16, "epilogue slabs must fit the rings");
+  static_assert(BM % (EG * ER) == 0, "whole epilogue passes");
   float* stage = (float*)smem;
+  const int eg = tid / 256;
 #pragma unroll
-  for (int pass = 0; pass < BM / ER; ++pass) {
-    if (m_base + pass * ER >= g.M) break;
-    stage_acc<BM, BN, ER>(stage, acc, wm, wn, lane, pass, g.out_scale);
+  for (int pass = 0; pass < BM / (EG * ER); ++pass) {
+    if (m_base + pass * EG * ER >= g.M) break;
+#pragma unroll
+    for (int fi = 0; fi < FM; ++fi) {
+      const int row0 = wm * WM + fi * 16;
+      if (row0 < pass * EG * ER || row0 >= (pass + 1) * EG * ER) continue;
+#pragma unroll
+      for (int fj = 0; fj < FN; ++fj) {
+        const int col = wn * WN + fj * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          stage[(row0 - pass * EG * ER + grp * 4 + i) * (BN + 1) + col] = acc[fi][fj][i] * g.out_scale;
+      }
+    }
     __syncthreads();
-    Epi::template apply<BN, ER>(ep, stage, BN + 1, m_base + pass * ER, n_base, g.M, g.N, tn, tid);
+    Epi::template apply<BN, ER>(ep, stage + eg * ER * (BN + 1), BN + 1, m_base + (pass * EG + eg) * ER, n_base, g.M, g.N,
+                                tn, tid & 255);
     __syncthreads();
   }
 }

@@ -2,7 +2,7 @@
 // tile shape).  16-bit products (fp16, or bf16 for the fc) use the pipelined
 // gemm2 kernel; fp32 products use the register-staged kernel of gemm.h.  Tile
 // shapes (measured on MI355X):
-//   16-bit, M > 64 : 128 x 128, 2 LDS stages (64 KB: two work-groups per CU)
+//   16-bit, M > 64 : 128 x 128, 2 LDS stages (64 KB: two 8-wave work-groups per CU)
 //   16-bit, M <= 64: 64 x 128, 3 stages
 //   16-bit LM head and long-K products: 128 x 128, A 2 stages, B 3 stages
 //   fp32           : 128 x 128 or 64 x 128
@@ -35,7 +35,7 @@ static void gemm256_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   gemm256_kernel<T, Epi><<<grid, GEMM256_THREADS, 0, s>>>(g, p);
 }
 
-template <typename T, int BM, int BN, int SA, int SB, class Epi>
+template <typename T, int BM, int BN, int SA, int SB, class Epi, int NT = 256>
 static void gemm2_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   const typename Epi::Params& p = *(const typename Epi::Params*)ep;
   dim3 grid(gemm_grid(g.tiles_m * g.tiles_n), g.splits);
@@ -43,12 +43,12 @@ static void gemm2_go(const GemmArgs& g, const void* ep, hipStream_t s) {
   // fc over the caller's bf16 hidden states)
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (g.a_wide) {
-      gemm2_kernel<T, BM, BN, SA, SB, Epi, true><<<grid, 256, 0, s>>>(g, p);
+      gemm2_kernel<T, BM, BN, SA, SB, Epi, true, NT><<<grid, NT, 0, s>>>(g, p);
       if (g.splits > 1 && !g.keep_partials) gemm_reduce_kernel<BM, BN, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
       return;
     }
   }
-  gemm2_kernel<T, BM, BN, SA, SB, Epi><<<grid, 256, 0, s>>>(g, p);
+  gemm2_kernel<T, BM, BN, SA, SB, Epi, false, NT><<<grid, NT, 0, s>>>(g, p);
   if (g.splits > 1 && !g.keep_partials) gemm_reduce_kernel<BM, BN, Epi><<<reduce_grid<BM>(g), 256, 0, s>>>(g, p);
 }
 
@@ -79,14 +79,14 @@ static void gemm_cfg(const GemmPlan& pl, const GemmArgs& g, const void* ep, hipS
     // the 16-bit tilings (BM x BN, A ring, B ring): exactly the plans that
     // runnable_plan lets through (anything else arrives as 128 x 128)
     if (pl.bm == 64 && pl.bn == 128) gemm2_go<T, 64, 128, 3, 3, Epi>(g, ep, s);
-    else if (pl.bm == 192 && pl.bn == 128) gemm2_go<T, 192, 128, 2, 2, Epi>(g, ep, s);
+    else if (pl.bm == 192 && pl.bn == 128) gemm2_go<T, 192, 128, 2, 2, Epi, 512>(g, ep, s);
     else if (pl.bm == 128 && pl.bn == 128 && pl.sb == 3) gemm2_go<T, 128, 128, 2, 3, Epi>(g, ep, s);
     else if constexpr (!EpiNeedsWide<Epi>::value) {
       if (pl.bm == 96 && pl.bn == 64) gemm2_go<T, 96, 64, 4, 4, Epi>(g, ep, s);
       else if (pl.bm == 64 && pl.bn == 64) gemm2_go<T, 64, 64, 4, 4, Epi>(g, ep, s);
-      else gemm2_go<T, 128, 128, 2, 2, Epi>(g, ep, s);
+      else gemm2_go<T, 128, 128, 2, 2, Epi, 512>(g, ep, s);
     } else {
-      gemm2_go<T, 128, 128, 2, 2, Epi>(g, ep, s);
+      gemm2_go<T, 128, 128, 2, 2, Epi, 512>(g, ep, s);
     }
   } else {
     if (pl.bm == 64) gemm1_go<64, Epi>(g, ep, s);

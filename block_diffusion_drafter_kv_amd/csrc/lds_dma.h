@@ -36,6 +36,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* lds_ptr) {
 // again wherever it needs it; s_nop 0 is the wait state an M0 write needs
 // before an LDS-DMA instruction reads it), and carry no memory clobber: for ring loops
 // whose explicit waits and barriers order the copies against the LDS reads.
+// The compiler keeps no value of its own in M0 on gfx950 unless it emits one of
+// the few instructions that read it (indirect register moves, add-tid LDS
+// operations, messages, GWS, buffer-to-LDS loads), none of which these kernels
+// contain; a device-code test over the built library checks exactly that.
 // sv: wave-uniform 64-bit global base in SGPRs plus a per-lane 32-bit offset.
 __device__ __forceinline__ void copy16_to_lds_sv_m0(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
