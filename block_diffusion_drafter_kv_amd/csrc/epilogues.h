@@ -46,27 +46,45 @@ struct EpiStoreSplit {
 // order each load after the previous item's store).  N and ld are multiples of 4.
 struct EpiResidualAdd {
   struct Params { float* x; int64_t ld; };
+  // The X values of one ROWS-row slab, loadable ahead of the stage (a product
+  // may load them before its main loop: X is written only by this epilogue,
+  // each element by one thread).
   template <int BN, int ROWS>
-  __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int, int tid) {
-    constexpr int C4 = BN / 4, NV = ROWS * C4 / 256;
+  struct Pre {
+    static constexpr int C4 = BN / 4, NV = ROWS * C4 / 256;
     static_assert(ROWS * C4 % 256 == 0, "whole items per thread");
     float4 xv[NV];
+  };
+  template <int BN, int ROWS>
+  __device__ static void load(const Params& p, int m0, int n0, int M, int N, int tid, Pre<BN, ROWS>& pre) {
+    constexpr int C4 = Pre<BN, ROWS>::C4;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
+    for (int j = 0; j < Pre<BN, ROWS>::NV; ++j) {
       const int idx = tid + j * 256, r = idx / C4, c = 4 * (idx % C4);
       const int m = m0 + r, n = n0 + c;
-      xv[j] = m < M && n < N ? *(const float4*)(p.x + (int64_t)m * p.ld + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+      pre.xv[j] = m < M && n < N ? *(const float4*)(p.x + (int64_t)m * p.ld + n) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  }
+  template <int BN, int ROWS>
+  __device__ static void add(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int tid,
+                             const Pre<BN, ROWS>& pre) {
+    constexpr int C4 = Pre<BN, ROWS>::C4;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
+    for (int j = 0; j < Pre<BN, ROWS>::NV; ++j) {
       const int idx = tid + j * 256, r = idx / C4, c = 4 * (idx % C4);
       const int m = m0 + r, n = n0 + c;
       if (m < M && n < N) {
         const float* sr = st + r * ld + c;
         *(float4*)(p.x + (int64_t)m * p.ld + n) =
-            make_float4(xv[j].x + sr[0], xv[j].y + sr[1], xv[j].z + sr[2], xv[j].w + sr[3]);
+            make_float4(pre.xv[j].x + sr[0], pre.xv[j].y + sr[1], pre.xv[j].z + sr[2], pre.xv[j].w + sr[3]);
       }
     }
+  }
+  template <int BN, int ROWS>
+  __device__ static void apply(const Params& p, const float* st, int ld, int m0, int n0, int M, int N, int, int tid) {
+    Pre<BN, ROWS> pre;
+    load<BN, ROWS>(p, m0, n0, M, N, tid, pre);
+    add<BN, ROWS>(p, st, ld, m0, n0, M, N, tid, pre);
   }
 };
 

@@ -14,6 +14,7 @@
 // the global chunk that belongs in its slot.
 #pragma once
 #include <type_traits>
+#include "epilogues.h"
 #include "gemm.h"
 #include "lds_dma.h"
 
@@ -129,6 +130,20 @@ __global__ __launch_bounds__(NT) void gemm2_kernel(const GemmArgs g, const typen
       copy16_to_lds_sv_m0(b_base[j] + (int64_t)k0 * sizeof(T), b_off[j], dst + (uint32_t)((j * RPC * 8 + wave * 64) * 16));
   };
 
+  // 4-wave tiles with the residual add: the epilogue's X rows are loaded before
+  // the main loop, so their latency hides behind it (the product never reads X)
+  constexpr int EG = NT / 256;
+  constexpr bool PRE = std::is_same<Epi, EpiResidualAdd>::value && NT == 256 && BM % GEMM2_EPI_ROWS == 0;
+  constexpr int NPRE = PRE ? BM / GEMM2_EPI_ROWS : 1;
+  typename std::conditional<PRE, EpiResidualAdd::Pre<BN, GEMM2_EPI_ROWS>, int>::type pre[NPRE];
+  if constexpr (PRE) {
+    if (g.splits == 1) {
+#pragma unroll
+      for (int ps = 0; ps < NPRE; ++ps)
+        EpiResidualAdd::load<BN, GEMM2_EPI_ROWS>(ep, m_base + ps * GEMM2_EPI_ROWS, n_base, g.M, g.N, tid, pre[ps]);
+    }
+  }
+
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -211,7 +226,6 @@ __global__ __launch_bounds__(NT) void gemm2_kernel(const GemmArgs g, const typen
 
   // epilogue: NT/256 slabs of ER rows per pass staged as fp32 [ER][BN + 1], one
   // per 256-thread group (the epilogues are written for 256 threads)
-  constexpr int EG = NT / 256;
   static_assert(EG * ER * (BN + 1) * 4 <= (SA * BM + SB * BN) * 8 * 16, "epilogue slabs must fit the rings");
   static_assert(BM % (EG * ER) == 0, "whole epilogue passes");
   float* stage = (float*)smem;
@@ -232,8 +246,11 @@ __global__ __launch_bounds__(NT) void gemm2_kernel(const GemmArgs g, const typen
       }
     }
     __syncthreads();
-    Epi::template apply<BN, ER>(ep, stage + eg * ER * (BN + 1), BN + 1, m_base + (pass * EG + eg) * ER, n_base, g.M, g.N,
-                                tn, tid & 255);
+    if constexpr (PRE)
+      EpiResidualAdd::add<BN, ER>(ep, stage, BN + 1, m_base + pass * ER, n_base, g.M, g.N, tid, pre[pass]);
+    else
+      Epi::template apply<BN, ER>(ep, stage + eg * ER * (BN + 1), BN + 1, m_base + (pass * EG + eg) * ER, n_base, g.M,
+                                  g.N, tn, tid & 255);
     __syncthreads();
   }
 }
