@@ -313,6 +313,35 @@ def dflash2_measure(w, ctx, steps=10, warmup=2):
             "phase_ms_per_step": dict(sorted(per_step.items(), key=lambda x: -x[1]))}
 
 
+def inject_rows_measure(w, reps=10):
+    """Per-step injection on the batch-32 workload at 1, 5 and 17 committed rows per request (5 is
+    the middle of the pages' 4-6 accepted tokens; random weights commit about one): median us per
+    call of dflash_inject_context with the row counts on the device and the same bound (B * (K+1))."""
+    import numpy as np
+    import torch
+    import block_diffusion_drafter_kv_amd as dk
+    from synth.configs import get_workload
+    wl = get_workload("b32_ragged4k")
+    cfg, B, K = wl.model, wl.batch, wl.K
+    R = K + 1
+    ctx0 = 4096
+    dr = dk.Drafter(cfg, w, max_batch=B, max_ctx=ctx0 + 3 * (reps + 2) * R + 64, max_k=K, max_inject_rows=8192)
+    _fill_prompts(dr, cfg, [ctx0] * B, 2026)
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(78)
+    pool = torch.randn((B * R, cfg.n_target_layers, cfg.target_hidden), generator=g, device="cuda",
+                       dtype=torch.float32).to(torch.bfloat16)
+    slots, row_start = i32(np.arange(B)), i32(np.arange(B) * R)
+    out = {}
+    for n in (1, 5, 17):
+        counts = i32(np.full(B, n))
+        out["rows_%d" % n] = round(_timed(lambda: dr.inject(slots, row_start, counts, B * R, pool), reps), 1)
+    assert dr.get_error() == 0
+    dr.close()
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "batch": B, "row_bound": B * R, "reps": reps, "us_per_call": out}
+
+
 def dflash2_b1_measure(w, steps=20):
     """The DFlash 2 modules at the pages' scale: batch 1, context 2048, K = 16, greedy; the plain
     draft and the draft with both modules (conv group 16, 16 candidates, rank 256) on handles that
@@ -936,6 +965,8 @@ def main():
     if not args.no_inject:
         log("[bench] prompt injection (4 x 32768 rows, one call) ...")
         result["inject_prompt"] = inject_prompt_measure(w)
+        log("[bench] per-step injection at 1, 5 and 17 rows per request ...")
+        result["inject_step_rows"] = inject_rows_measure(w)
     if not args.no_dflash2:
         log("[bench] DFlash 2 modules (conv + selector) on the same workload ...")
         d2 = dflash2_measure(w, ctx)
