@@ -778,8 +778,10 @@ void conv_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj,
 // residual stream; or, when an after-sub-layer convolution follows (post_pw =
 // its P . W [2H/G, Kd]), the output goes to obuf and its kernel corrections,
 // from the same product's extra columns, to cbuf -- norm_stage applies them.
-void sublayer_out(dflash_handle* h, hipStream_t s, int M, const void* a, int Kd, const void* b, float b_scale,
-                  const void* post_pw, int phase) {
+// keep_partials (no convolution): a K-split product leaves its partials for the
+// next norm pass to add (launch_partials_add_norm) instead of reducing them here.
+GemmShape sublayer_out(dflash_handle* h, hipStream_t s, int M, const void* a, int Kd, const void* b, float b_scale,
+                       const void* post_pw, int phase, bool keep_partials = false) {
   const dflash_config& c = h->cfg;
   const int H = c.hidden;
   const int nc = post_pw ? 2 * (H / c.conv_group) : 0;
@@ -788,24 +790,33 @@ void sublayer_out(dflash_handle* h, hipStream_t s, int M, const void* a, int Kd,
   Phase ph(h, s, phase);
   if (!post_pw) {
     set_b(ga, {{b, H}}, Kd);
+    ga.keep_partials = keep_partials ? 1 : 0;
     EpiResidualAdd::Params pr{h->X, H};
-    launch_gemm(h->op, EPI_RESADD, ga, &pr, plan_gemm(h->op, M, H, Kd, h->num_cus), h->partials, h->partials_elems,
-                s);
-    return;
+    return launch_gemm(h->op, EPI_RESADD, ga, &pr, plan_gemm(h->op, M, H, Kd, h->num_cus), h->partials,
+                       h->partials_elems, s);
   }
   set_b(ga, {{b, H}, {post_pw, nc}}, Kd);
   StoreSplitParams pd{h->obuf, H, h->cbuf, nc, H};
   launch_gemm(h->op, EPI_STORE_SPLIT, ga, &pd, plan_gemm(h->op, M, H + nc, Kd, h->num_cus), h->partials,
               h->partials_elems, s);
+  return GemmShape{1, 0, 0};
 }
 
 // RMSNorm of the rows (map_mask: the mask rows only) into hbuf, after applying
 // the pending after-sub-layer convolution with base post_base (or none); with
 // DFlash 2 convolutions the rows' RMS scales go to rsbuf for the next one.
+// pend: a product whose split partials still have to be added to X (scale
+// pend_scale) -- added here, fused with the norm.
 void norm_stage(dflash_handle* h, hipStream_t s, int rows, int map_mask, int K, int R, const void* gain,
-                const void* post_base) {
+                const void* post_base, const GemmShape* pend = nullptr, float pend_scale = 1.f) {
   const dflash_config& c = h->cfg;
   float* rs = c.conv_group > 0 ? h->rsbuf : nullptr;
+  if (pend && pend->splits > 1) {
+    Phase ph(h, s, DFLASH_PH_NORM);
+    launch_partials_add_norm(c.dtype, rows, c.hidden, h->X, map_mask, K, R, h->partials, pend->Npad, pend->splits,
+                             (int64_t)pend->Mpad * pend->Npad, pend_scale, gain, h->hbuf, c.rms_eps, s);
+    return;
+  }
   if (post_base) {
     Phase ph(h, s, DFLASH_PH_CONV);
     launch_conv_post_norm(c.dtype, rows, c.hidden, c.conv_group, h->X, map_mask, K, R, h->obuf, h->cbuf, post_base,
@@ -937,6 +948,8 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
   }
   const int64_t layer_cache = (int64_t)(c.max_batch + 1) * nkv * h->ctx_alloc * d * h->esize;
   const void* post_m = nullptr;   // the last MLP's pending after-sub-layer convolution
+  GemmShape down{1, 0, 0};        // the last down product's pending split partials (splits > 1)
+  float down_scale = 1.f;
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& L = h->layers[l];
     const dflash_handle::Mats& W = h->mats[l];
@@ -1063,13 +1076,19 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
                     h->partials_elems, s);
       }
       post_m = c.conv_group > 0 ? L.mlp_conv_post_base : nullptr;
-      sublayer_out(h, s, M, h->act, F, W.down, W.s_down, post_m ? W.conv_mp : nullptr, DFLASH_PH_DOWN);
+      // without DFlash 2 convolutions a K-split down product leaves its partials
+      // to the next norm pass, which adds them to X and normalises in one pass
+      const bool keep = c.conv_group == 0 && H <= 8192;
+      const GemmShape gs = sublayer_out(h, s, M, h->act, F, W.down, W.s_down, post_m ? W.conv_mp : nullptr,
+                                        DFLASH_PH_DOWN, keep);
+      down = keep ? gs : GemmShape{1, 0, 0};   // pending only when the partials were kept
+      down_scale = W.s_down;
     }
-    if (l + 1 < c.n_layers) norm_stage(h, s, M, 0, K, R, h->layers[l + 1].in_norm, post_m);
+    if (l + 1 < c.n_layers) norm_stage(h, s, M, 0, K, R, h->layers[l + 1].in_norm, post_m, &down, down_scale);
   }
   // final norm on the K mask rows, LM head with streaming statistics
   const int rows = n_req * K;
-  norm_stage(h, s, rows, 1, K, R, h->final_norm, post_m);
+  norm_stage(h, s, rows, 1, K, R, h->final_norm, post_m, &down, down_scale);
   const float T = p->temperature;
   const bool need_logits = o->logits || T > 0.f || p->top_k > 0 || p->tree_budget > 0 || c.sel_rank > 0;
   float* logits = o->logits ? o->logits : (need_logits ? h->logits_ws : nullptr);

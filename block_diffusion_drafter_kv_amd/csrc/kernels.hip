@@ -133,6 +133,57 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int n_rows, int H, const f
   }
 }
 
+// The residual add of a product whose K split left its partials in place (fp32
+// [splits][.][ld], summed in split order and scaled, as the split-K reduction
+// does), fused with the RMSNorm that follows it: the row of X is updated and
+// normalised as in rmsnorm_kernel (same row mapping; only the mapped rows of X
+// are updated).  One 256-thread work-group per row; H <= 8192.
+template <typename C>
+__global__ __launch_bounds__(256) void partials_add_norm_kernel(int n_rows, int H, float* X, int map_mask, int K, int R,
+                                                                  const float* P, int ld, int splits,
+                                                                  int64_t split_stride, float scale,
+                                                                  const typename WeightOf<C>::type* gain, C* h_out,
+                                                                  float eps) {
+  __shared__ float red[4];
+  constexpr int MAXV = 8;
+  const int out = blockIdx.x;
+  if (out >= n_rows) return;
+  const int m = map_mask ? (out / K) * R + 1 + (out % K) : out;
+  float* x = X + (int64_t)m * H;
+  const float* p = P + (int64_t)m * ld;
+  float4 v[MAXV];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x * 4 + i * 1024;
+    if (c < H) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int sp = 0; sp < splits; ++sp) {
+        const float4 q = load4f(p + sp * split_stride + c);
+        acc.x += q.x;
+        acc.y += q.y;
+        acc.z += q.z;
+        acc.w += q.w;
+      }
+      const float4 a = load4f(x + c);
+      v[i] = make_float4(a.x + acc.x * scale, a.y + acc.y * scale, a.z + acc.z * scale, a.w + acc.w * scale);
+      *(float4*)(x + c) = v[i];
+      ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    }
+  }
+  ss = block_sum(ss, red);
+  const float rs = rsqrtf(ss / (float)H + eps);
+  C* y = h_out + (int64_t)out * H;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x * 4 + i * 1024;
+    if (c < H) {
+      const float4 gn = load4f(gain + c);
+      store4(y + c, v[i].x * rs * gn.x, v[i].y * rs * gn.y, v[i].z * rs * gn.z, v[i].w * rs * gn.w);
+    }
+  }
+}
+
 // DFlash 2 [P2 §3.2.3], convolution after a sub-layer, fused with the RMSNorm
 // that follows it: the sub-layer output o (fp32 [M, H], before the residual add)
 // is convolved over the block rows, y_m = (base0 + c0_m) * o_m + (base1 + c1_m) *
@@ -2281,6 +2332,18 @@ void launch_rmsnorm(int dtype, int n_rows, int H, const float* X, int map_mask, 
   else
     rmsnorm_kernel<float><<<grid, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, (const float*)gain, (float*)h_out, eps,
                                                  n_valid, valid_base, rs_out);
+}
+
+void launch_partials_add_norm(int dtype, int n_rows, int H, float* X, int map_mask, int K, int R, const float* P, int ld,
+                              int splits, int64_t split_stride, float scale, const void* gain, void* h_out, float eps,
+                              hipStream_t s) {
+  if (n_rows <= 0) return;
+  if (dtype == DT_BF16)
+    partials_add_norm_kernel<f16_t><<<n_rows, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, P, ld, splits, split_stride,
+                                                            scale, (const bf16_t*)gain, (f16_t*)h_out, eps);
+  else
+    partials_add_norm_kernel<float><<<n_rows, 256, 0, s>>>(n_rows, H, X, map_mask, K, R, P, ld, splits, split_stride,
+                                                            scale, (const float*)gain, (float*)h_out, eps);
 }
 
 void launch_conv_post_norm(int dtype, int n_rows, int H, int G, float* X, int map_mask, int K, int R, const float* o,

@@ -67,6 +67,11 @@ struct Nucleus {
   float pad;
 };
 
+// X rows += scale * (sum of a split product's partials, in split order), then
+// RMSNorm of the updated rows into h_out (rmsnorm's row mapping); H <= 8192
+void launch_partials_add_norm(int dtype, int n_rows, int H, float* X, int map_mask, int K, int R, const float* P, int ld,
+                              int splits, int64_t split_stride, float scale, const void* gain, void* h_out, float eps,
+                              hipStream_t s);
 // ---- elementwise / row kernels (kernels.hip) ----
 void launch_rope_table(float2* table, int n_pos, int d, double theta, hipStream_t s);
 void launch_embed_norm(int dtype, int n_rows, int R, const int32_t* anchors, int mask_id, int vocab, const void* embed,
