@@ -781,7 +781,7 @@ void conv_stage(dflash_handle* h, hipStream_t s, int M, int R, const void* proj,
 // keep_partials (no convolution): a K-split product leaves its partials for the
 // next norm pass to add (launch_partials_add_norm) instead of reducing them here.
 GemmShape sublayer_out(dflash_handle* h, hipStream_t s, int M, const void* a, int Kd, const void* b, float b_scale,
-                       const void* post_pw, int phase, bool keep_partials = false) {
+                       const void* post_pw, int phase, bool keep_partials = false, bool balance = false) {
   const dflash_config& c = h->cfg;
   const int H = c.hidden;
   const int nc = post_pw ? 2 * (H / c.conv_group) : 0;
@@ -792,8 +792,14 @@ GemmShape sublayer_out(dflash_handle* h, hipStream_t s, int M, const void* a, in
     set_b(ga, {{b, H}}, Kd);
     ga.keep_partials = keep_partials ? 1 : 0;
     EpiResidualAdd::Params pr{h->X, H};
-    return launch_gemm(h->op, EPI_RESADD, ga, &pr, plan_gemm(h->op, M, H, Kd, h->num_cus), h->partials,
-                       h->partials_elems, s);
+    GemmPlan gp = plan_gemm(h->op, M, H, Kd, h->num_cus);
+    if (keep_partials && balance && gp.splits == 1) {
+      // one round of whole tiles that leaves some CUs one work-group more than
+      // the rest: split K in two (the norm pass adds the partials anyway)
+      const long tiles = (long)((M + gp.bm - 1) / gp.bm) * ((H + gp.bn - 1) / gp.bn);
+      if (tiles < 2L * h->num_cus && tiles % h->num_cus != 0 && Kd / 64 >= 32) gp.splits = 2;
+    }
+    return launch_gemm(h->op, EPI_RESADD, ga, &pr, gp, h->partials, h->partials_elems, s);
   }
   set_b(ga, {{b, H}, {post_pw, nc}}, Kd);
   StoreSplitParams pd{h->obuf, H, h->cbuf, nc, H};
@@ -1053,8 +1059,13 @@ int dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req, const int3
     }
     // output projection + residual (with a DFlash 2 convolution: applied in the norm pass)
     const void* post_a = c.conv_group > 0 ? L.attn_conv_post_base : nullptr;
-    sublayer_out(h, s, M, h->attn_out, qdim, W.o, W.s_o, post_a ? W.conv_ap : nullptr, DFLASH_PH_O);
-    norm_stage(h, s, M, 0, K, R, L.post_norm, post_a);
+    // without DFlash 2 convolutions a K-split output product leaves its partials
+    // to the post-attention norm pass, which adds them to X and normalises in one pass
+    const bool keep_o = !post_a && H <= 8192;
+    const GemmShape og = sublayer_out(h, s, M, h->attn_out, qdim, W.o, W.s_o, post_a ? W.conv_ap : nullptr,
+                                      DFLASH_PH_O, keep_o, /*balance=*/true);
+    const GemmShape o_pend = keep_o ? og : GemmShape{1, 0, 0};
+    norm_stage(h, s, M, 0, K, R, L.post_norm, post_a, &o_pend, W.s_o);
     // DFlash 2: dynamic convolution of the MLP sub-layer's input
     const void* mlp_in = h->hbuf;
     if (c.conv_group > 0) {
