@@ -495,13 +495,13 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_hand
     if ((rc = alloc_t(h, &h->seg_desc, (size_t)c.max_batch * nkv * splits, 16))) break;
     if ((rc = alloc_t(h, &h->wg_range, (size_t)h->attn_wg, 16))) break;
     if ((rc = alloc_t(h, &h->dslots, c.max_batch, 4))) break;
-    // split-K partials: grids of at most 2 * CUs tiles, or a four-way split of the
+    // split-K partials: grids of at most 2 * CUs tiles, or a five-way split of the
     // long-K products over the draft's rows (M x H each, rows padded to 128- or
     // 192-row tiles); a product needing more runs with fewer splits
     // (H columns, plus the kernel corrections of DFlash 2 after-sub-layer convolutions)
     const size_t mpad = std::max((h->maxM + 127) / 128 * 128, (h->maxM + 191) / 192 * 192);
     const size_t ncols = H + (c.conv_group > 0 ? 2 * (H / c.conv_group) : 0);
-    h->partials_elems = std::max((size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(h->op), (size_t)4 * mpad * ncols);
+    h->partials_elems = std::max((size_t)(2 * h->num_cus + 8) * 128 * gemm_bn(h->op), (size_t)5 * mpad * ncols);
     // ... and the per-step injection (a row bound of at most 1024 on 64-row tiles,
     // the true row count on the device): the partial tiles cover every row tile
     // of the bound, for the fc product's K split in up to eight and the K|V

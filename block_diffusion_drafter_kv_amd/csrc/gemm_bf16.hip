@@ -37,10 +37,15 @@ GemmPlan plan_gemm(int op, int M, int N, int K, int num_cus, bool wide, bool big
   }
   if (w16 && K >= 8192 && M > 256 && M <= 768) {
     // long products over a few hundred rows (the MLP down projection): 192 x 128
-    // tiles, K split in four (544 x 4096 x 12288 with a plain store: 84 us,
-    // against 100 us for 128 x 128 tiles with a 3-deep weight ring)
+    // tiles, K split in five (544 x 4096 x 12288 with a plain store: 84 us split
+    // in four, against 100 us for 128 x 128 tiles with a 3-deep weight ring); five
+    // splits make 480 work-groups for the 512 two-per-CU slots where four left
+    // half the CUs with one, and each work-group runs 39 slabs instead of 48;
+    // four where five would spill past those slots (the DFlash 2 product's
+    // extra correction columns: 540 work-groups)
     p.bm = 192;
-    p.splits = 4;
+    const long t192 = (long)((M + 191) / 192) * ((N + 127) / 128);
+    p.splits = t192 * 5 <= 2L * num_cus ? 5 : 4;
     return p;
   }
   if (w16 && K >= 8192 && M > 64 && M <= 1024) {
